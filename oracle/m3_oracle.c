@@ -1,0 +1,409 @@
+/*
+ * Mamba-3 SSM recurrence: plain, slow, fp64 CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path (the HIP library and
+ * its Python binding) may link, load or call this file. Only the tests, the
+ * smoke check and the CPU-baseline leg of the bench use it. It shares no code,
+ * header, table or helper with the GPU path.
+ *
+ * What it computes (the pages' statement of the layer, written out directly):
+ *
+ *   per sequence s, head h (group g = h / (H/G)), token t of that sequence:
+ *     alpha_t = exp(dt_t A_h)                       (discretised decay)
+ *     delta_t = (1 - lam_t) dt_t,  beta_t = delta_t alpha_t,  gamma_t = lam_t dt_t
+ *     angle_t[k] = dt_t theta_t[k]  for k < N/2     (rotation of state pair k)
+ *     h_t = alpha_t R_t h_{t-1} + beta_t R_t B_{t-1} X_{t-1}^T + gamma_t B_t X_t^T
+ *     y_t = H_t^T C_t + D_h X_t                      (P x R output)
+ *   "Mamba-3" paper summary, sections "Exponential-Trapezoidal Discretization"
+ *   (Proposition 1: the three-term update and its alpha, beta, gamma),
+ *   "Complex-Valued State Space Models" (Proposition 2: complex diagonal
+ *   transition = real block-diagonal rotation; Proposition 4: the
+ *   exponential-trapezoidal complex recurrence), "MIMO Formulation"
+ *   (B_t in R^{N x R}, X_t in R^{P x R}, rank-R update B_t X_t^T, output
+ *   y_t = H_t^T C_t in R^{P x R}).
+ *
+ * Three independent forms are provided; the tests pin them against each other
+ * and against closed forms:
+ *   O1  m3o_scan_o1   : complex state in C^{N/2 x P}, physical frame, the
+ *                       transition exp(dt (A + i theta)) applied directly.
+ *   O2  m3o_scan_o2   : Proposition 4 literally - real state in the rotated
+ *                       frame, cumulative rotations from the sequence start
+ *                       absorbed into B and C ("RoPE trick", Proposition 3).
+ *   O3  m3o_scan_o3   : the SSD matrix form Y = (L o C~ B~^T) X with
+ *                       L = L1 L2 materialised (1-semiseparable decay times
+ *                       the 2-band trapezoid matrix), section "Parallel
+ *                       representation under SSD", Figure 1.
+ *
+ * Readings taken where the pages leave a step open:
+ *   - State pair k is rows (2k, 2k+1) of the real state; the complex value is
+ *     h[2k] + i h[2k+1]; B's complex entry is B[2k] + i B[2k+1]; since the real
+ *     form stacks C as [C; -C^], C's complex entry is C[2k] - i C[2k+1].
+ *   - theta is the raw per-token frequency; the applied angle is dt * theta.
+ *   - A sequence start has a zero state and no previous-token term unless a
+ *     state h_in and a previous token (Bprev, xprev) are given (resume).
+ *   - D is a per-head skip term y += D_h X_t (absent from the pages).
+ *   - MIMO: the rotation acts on the N axis identically for every rank column.
+ *
+ * Inputs are read through a dtype tag (f64, f32, bf16 bits) and converted
+ * exactly to double; all arithmetic is in double / double complex.
+ */
+#include <complex.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { M3O_F64 = 0, M3O_F32 = 1, M3O_BF16 = 2 };
+
+typedef struct {
+    int32_t nseq;              /* number of sequences */
+    const int64_t *seq_start;  /* [nseq] first token of each sequence (flat token axis) */
+    const int64_t *seq_len;    /* [nseq] tokens in each sequence */
+    int32_t H, G, P, N, R;     /* heads, B/C groups, head dim, state dim (even), rank */
+    int32_t in_dtype;          /* dtype tag of x, dt, lam, theta, B, C, Bprev, xprev */
+    const void *x;             /* [T, H, P, R] */
+    const void *dt;            /* [T, H] (post-softplus step) */
+    const void *lam;           /* [T, H] (trapezoid weight in [0,1]) */
+    const void *theta;         /* [T, H, N/2] (rotation frequency) */
+    const void *B;             /* [T, G, N, R] */
+    const void *C;             /* [T, G, N, R] */
+    const double *A;           /* [H], negative */
+    const double *D;           /* [H] or NULL */
+    const double *h_in;        /* [nseq, H, N, P] or NULL (zero state) */
+    const void *Bprev;         /* [nseq, G, N, R] or NULL (no previous token) */
+    const void *xprev;         /* [nseq, H, P, R] or NULL */
+} m3o_args;
+
+static inline double ld(const void *p, int dt, int64_t i) {
+    if (dt == M3O_F64) return ((const double *)p)[i];
+    if (dt == M3O_F32) return (double)((const float *)p)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* ---------------------------------------------------------------- O1 ---- */
+/* Complex physical-frame recurrence for one (sequence, head) slab.
+ * y_slab: [len, P, R]; h_slab: [N, P] (may be NULL). */
+static void o1_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_slab) {
+    const int H = a->H, G = a->G, P = a->P, N = a->N, R = a->R, K = N / 2;
+    const int g = h / (H / G);
+    const int dtp = a->in_dtype;
+    const int64_t t0 = a->seq_start[s], len = a->seq_len[s];
+    double complex *hc = calloc((size_t)K * P, sizeof *hc);   /* state   [K][P] */
+    double complex *bp = calloc((size_t)K * R, sizeof *bp);   /* prev b  [K][R] */
+    double *xp = calloc((size_t)P * R, sizeof *xp);           /* prev x  [P][R] */
+    double complex *bc = malloc((size_t)K * R * sizeof *bc);  /* cur b   [K][R] */
+    double complex *cc = malloc((size_t)K * R * sizeof *cc);  /* cur c   [K][R] */
+    double *xc = malloc((size_t)P * R * sizeof *xc);          /* cur x   [P][R] */
+    double complex *z = malloc((size_t)K * sizeof *z);
+    int has_prev = 0;
+
+    if (a->h_in) {
+        const double *hi = a->h_in + ((int64_t)s * H + h) * N * P;
+        for (int k = 0; k < K; k++)
+            for (int p = 0; p < P; p++)
+                hc[k * P + p] = hi[(2 * k) * P + p] + I * hi[(2 * k + 1) * P + p];
+    }
+    if (a->Bprev && a->xprev) {
+        has_prev = 1;
+        int64_t ob = ((int64_t)s * G + g) * N * R, ox = ((int64_t)s * H + h) * P * R;
+        for (int k = 0; k < K; k++)
+            for (int j = 0; j < R; j++)
+                bp[k * R + j] = ld(a->Bprev, dtp, ob + (2 * k) * R + j) +
+                                I * ld(a->Bprev, dtp, ob + (2 * k + 1) * R + j);
+        for (int i = 0; i < P * R; i++) xp[i] = ld(a->xprev, dtp, ox + i);
+    }
+    const double Ah = a->A[h];
+    const double Dh = a->D ? a->D[h] : 0.0;
+
+    for (int64_t tt = 0; tt < len; tt++) {
+        const int64_t t = t0 + tt;
+        const double dt = ld(a->dt, dtp, t * H + h);
+        const double lam = ld(a->lam, dtp, t * H + h);
+        const double delta = (1.0 - lam) * dt, gamma = lam * dt;
+        const double decay = exp(dt * Ah);
+        for (int k = 0; k < K; k++) {
+            double ang = dt * ld(a->theta, dtp, (t * H + h) * K + k);
+            z[k] = decay * (cos(ang) + I * sin(ang));
+        }
+        const int64_t ob = (t * G + g) * N * R, ox = (t * H + h) * P * R;
+        for (int k = 0; k < K; k++)
+            for (int j = 0; j < R; j++) {
+                bc[k * R + j] = ld(a->B, dtp, ob + (2 * k) * R + j) +
+                                I * ld(a->B, dtp, ob + (2 * k + 1) * R + j);
+                cc[k * R + j] = ld(a->C, dtp, ob + (2 * k) * R + j) -
+                                I * ld(a->C, dtp, ob + (2 * k + 1) * R + j);
+            }
+        for (int i = 0; i < P * R; i++) xc[i] = ld(a->x, dtp, ox + i);
+
+        /* h <- z (h + delta b_prev x_prev^T) + gamma b x^T */
+        for (int k = 0; k < K; k++)
+            for (int p = 0; p < P; p++) {
+                double complex prev = 0, cur = 0;
+                for (int j = 0; j < R; j++) {
+                    if (has_prev) prev += bp[k * R + j] * xp[p * R + j];
+                    cur += bc[k * R + j] * xc[p * R + j];
+                }
+                hc[k * P + p] = z[k] * (hc[k * P + p] + delta * prev) + gamma * cur;
+            }
+        /* y[p][i] = Re sum_k c[k][i] h[k][p] + D x[p][i] */
+        double *yt = y_slab + tt * P * R;
+        for (int p = 0; p < P; p++)
+            for (int i = 0; i < R; i++) {
+                double complex acc = 0;
+                for (int k = 0; k < K; k++) acc += cc[k * R + i] * hc[k * P + p];
+                yt[p * R + i] = creal(acc) + Dh * xc[p * R + i];
+            }
+        memcpy(bp, bc, (size_t)K * R * sizeof *bp);
+        memcpy(xp, xc, (size_t)P * R * sizeof *xp);
+        has_prev = 1;
+    }
+    if (h_slab)
+        for (int k = 0; k < K; k++)
+            for (int p = 0; p < P; p++) {
+                h_slab[(2 * k) * P + p] = creal(hc[k * P + p]);
+                h_slab[(2 * k + 1) * P + p] = cimag(hc[k * P + p]);
+            }
+    free(hc); free(bp); free(xp); free(bc); free(cc); free(xc); free(z);
+}
+
+/* ---------------------------------------------------------------- O2 ---- */
+/* Proposition 4 literally: real state h~ in the frame rotated by the
+ * cumulative angle Psi_t = sum_{i<=t} dt_i theta_i (the product of R_i^T over
+ * i = 0..t), B and C rotated by R(-Psi_t), a real scalar transition alpha_t;
+ * the previous-token input carries the previous token's rotation R(-Psi_{t-1}).
+ * The physical state is recovered at the end as h = R(Psi_T) h~. */
+static void rot_vec(double *dst, const double *src, const double *psi, int K, int R, int sign) {
+    /* dst[2k][j], dst[2k+1][j] = R(sign*psi[k]) applied to (src[2k][j], src[2k+1][j]) */
+    for (int k = 0; k < K; k++) {
+        double c = cos(psi[k]), sn = sign * sin(psi[k]);
+        for (int j = 0; j < R; j++) {
+            double u = src[(2 * k) * R + j], v = src[(2 * k + 1) * R + j];
+            dst[(2 * k) * R + j] = c * u - sn * v;
+            dst[(2 * k + 1) * R + j] = sn * u + c * v;
+        }
+    }
+}
+
+static void o2_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_slab) {
+    const int H = a->H, G = a->G, P = a->P, N = a->N, R = a->R, K = N / 2;
+    const int g = h / (H / G);
+    const int dtp = a->in_dtype;
+    const int64_t t0 = a->seq_start[s], len = a->seq_len[s];
+    double *hr = calloc((size_t)N * P, sizeof *hr);      /* rotated-frame state [N][P] */
+    double *psi = calloc((size_t)K, sizeof *psi);        /* cumulative angle */
+    double *braw = malloc((size_t)N * R * sizeof *braw), *craw = malloc((size_t)N * R * sizeof *craw);
+    double *brot = malloc((size_t)N * R * sizeof *brot), *crot = malloc((size_t)N * R * sizeof *crot);
+    double *bprot = calloc((size_t)N * R, sizeof *bprot); /* previous token's rotated B */
+    double *xp = calloc((size_t)P * R, sizeof *xp), *xc = malloc((size_t)P * R * sizeof *xc);
+    int has_prev = 0;
+
+    /* Before the first token the cumulative product is empty: h~ = h_in. */
+    if (a->h_in) memcpy(hr, a->h_in + ((int64_t)s * H + h) * N * P, (size_t)N * P * sizeof *hr);
+    if (a->Bprev && a->xprev) {
+        has_prev = 1;
+        int64_t ob = ((int64_t)s * G + g) * N * R, ox = ((int64_t)s * H + h) * P * R;
+        for (int i = 0; i < N * R; i++) bprot[i] = ld(a->Bprev, dtp, ob + i);
+        for (int i = 0; i < P * R; i++) xp[i] = ld(a->xprev, dtp, ox + i);
+    }
+    const double Ah = a->A[h];
+    const double Dh = a->D ? a->D[h] : 0.0;
+
+    for (int64_t tt = 0; tt < len; tt++) {
+        const int64_t t = t0 + tt;
+        const double dt = ld(a->dt, dtp, t * H + h);
+        const double lam = ld(a->lam, dtp, t * H + h);
+        const double alpha = exp(dt * Ah);
+        const double beta = (1.0 - lam) * dt * alpha, gamma = lam * dt;
+        for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, (t * H + h) * K + k);
+        const int64_t ob = (t * G + g) * N * R, ox = (t * H + h) * P * R;
+        for (int i = 0; i < N * R; i++) {
+            braw[i] = ld(a->B, dtp, ob + i);
+            craw[i] = ld(a->C, dtp, ob + i);
+        }
+        for (int i = 0; i < P * R; i++) xc[i] = ld(a->x, dtp, ox + i);
+        rot_vec(brot, braw, psi, K, R, -1);
+        rot_vec(crot, craw, psi, K, R, -1);
+        for (int n = 0; n < N; n++)
+            for (int p = 0; p < P; p++) {
+                double prev = 0, cur = 0;
+                for (int j = 0; j < R; j++) {
+                    if (has_prev) prev += bprot[n * R + j] * xp[p * R + j];
+                    cur += brot[n * R + j] * xc[p * R + j];
+                }
+                hr[n * P + p] = alpha * hr[n * P + p] + beta * prev + gamma * cur;
+            }
+        double *yt = y_slab + tt * P * R;
+        for (int p = 0; p < P; p++)
+            for (int i = 0; i < R; i++) {
+                double acc = 0;
+                for (int n = 0; n < N; n++) acc += crot[n * R + i] * hr[n * P + p];
+                yt[p * R + i] = acc + Dh * xc[p * R + i];
+            }
+        memcpy(bprot, brot, (size_t)N * R * sizeof *bprot);
+        memcpy(xp, xc, (size_t)P * R * sizeof *xp);
+        has_prev = 1;
+    }
+    if (h_slab) {
+        /* h = R(Psi_T) h~ on every state pair and column */
+        for (int k = 0; k < K; k++) {
+            double c = cos(psi[k]), sn = sin(psi[k]);
+            for (int p = 0; p < P; p++) {
+                double u = hr[(2 * k) * P + p], v = hr[(2 * k + 1) * P + p];
+                h_slab[(2 * k) * P + p] = c * u - sn * v;
+                h_slab[(2 * k + 1) * P + p] = sn * u + c * v;
+            }
+        }
+    }
+    free(hr); free(psi); free(braw); free(craw); free(brot); free(crot);
+    free(bprot); free(xp); free(xc);
+}
+
+/* ---------------------------------------------------------------- O3 ---- */
+/* SSD matrix form for one slab starting from a zero state with no previous
+ * token (the pages unroll from h_0 = gamma_0 B_0 x_0):
+ *   L1[t][s] = prod_{k=s+1..t} alpha_k (s <= t), L2 = diag(gamma) + subdiag(beta)
+ *   L = L1 L2,   Y[t][p][i] = sum_s sum_j L[t][s] (C~_t[:,i] . B~_s[:,j]) X_s[p][j]
+ * with B~, C~ rotated by the cumulative angle of their own token. O(len^2). */
+static void o3_slab(const m3o_args *a, int s, int h, double *y_slab) {
+    const int H = a->H, G = a->G, P = a->P, N = a->N, R = a->R, K = N / 2;
+    const int g = h / (H / G);
+    const int dtp = a->in_dtype;
+    const int64_t t0 = a->seq_start[s], T = a->seq_len[s];
+    double *alpha = malloc(T * sizeof *alpha), *beta = malloc(T * sizeof *beta), *gamma = malloc(T * sizeof *gamma);
+    double *L1 = calloc(T * T, sizeof *L1), *L2 = calloc(T * T, sizeof *L2), *L = calloc(T * T, sizeof *L);
+    double *Bt = malloc(T * N * R * sizeof *Bt), *Ct = malloc(T * N * R * sizeof *Ct);
+    double *X = malloc(T * P * R * sizeof *X);
+    double *psi = calloc(K, sizeof *psi), *tmp = malloc((size_t)N * R * sizeof *tmp);
+    const double Ah = a->A[h], Dh = a->D ? a->D[h] : 0.0;
+
+    for (int64_t t = 0; t < T; t++) {
+        const int64_t tg = t0 + t;
+        double dt = ld(a->dt, dtp, tg * H + h), lam = ld(a->lam, dtp, tg * H + h);
+        alpha[t] = exp(dt * Ah);
+        beta[t] = (1.0 - lam) * dt * alpha[t];
+        gamma[t] = lam * dt;
+        for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, (tg * H + h) * K + k);
+        const int64_t ob = (tg * G + g) * N * R, ox = (tg * H + h) * P * R;
+        for (int i = 0; i < N * R; i++) tmp[i] = ld(a->B, dtp, ob + i);
+        rot_vec(Bt + t * N * R, tmp, psi, K, R, -1);
+        for (int i = 0; i < N * R; i++) tmp[i] = ld(a->C, dtp, ob + i);
+        rot_vec(Ct + t * N * R, tmp, psi, K, R, -1);
+        for (int i = 0; i < P * R; i++) X[t * P * R + i] = ld(a->x, dtp, ox + i);
+    }
+    for (int64_t t = 0; t < T; t++) {
+        double prod = 1.0;
+        for (int64_t s2 = t; s2 >= 0; s2--) {
+            L1[t * T + s2] = prod;
+            prod *= alpha[s2];
+        }
+        L2[t * T + t] = gamma[t];
+        if (t > 0) L2[t * T + t - 1] = beta[t];
+    }
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t s2 = 0; s2 < T; s2++) {
+            double acc = 0;
+            for (int64_t k = 0; k < T; k++) acc += L1[t * T + k] * L2[k * T + s2];
+            L[t * T + s2] = acc;
+        }
+    for (int64_t t = 0; t < T; t++)
+        for (int p = 0; p < P; p++)
+            for (int i = 0; i < R; i++) {
+                double acc = 0;
+                for (int64_t s2 = 0; s2 < T; s2++) {
+                    if (L[t * T + s2] == 0.0) continue;
+                    for (int j = 0; j < R; j++) {
+                        double cb = 0;
+                        for (int n = 0; n < N; n++) cb += Ct[t * N * R + n * R + i] * Bt[s2 * N * R + n * R + j];
+                        acc += L[t * T + s2] * cb * X[s2 * P * R + p * R + j];
+                    }
+                }
+                y_slab[t * P * R + p * R + i] = acc + Dh * X[t * P * R + p * R + i];
+            }
+    free(alpha); free(beta); free(gamma); free(L1); free(L2); free(L);
+    free(Bt); free(Ct); free(X); free(psi); free(tmp);
+}
+
+/* ------------------------------------------------------------ exports ---- */
+static int check(const m3o_args *a) {
+    if (!a || a->nseq < 0 || a->H <= 0 || a->G <= 0 || a->P <= 0 || a->N <= 0 || a->R <= 0) return 1;
+    if (a->N % 2 || a->H % a->G) return 1;
+    if (!a->x || !a->dt || !a->lam || !a->theta || !a->B || !a->C || !a->A) return 1;
+    return 0;
+}
+
+/* Which form: 1 = O1 (complex), 2 = O2 (rotated frame). y: [T, H, P, R] on the
+ * flat token axis, h_out: [nseq, H, N, P] (may be NULL). OpenMP over slabs. */
+int m3o_scan(const m3o_args *a, int form, double *y, double *h_out, int nthreads) {
+    if (check(a) || !y || (form != 1 && form != 2)) return 1;
+    const int H = a->H, P = a->P, N = a->N, R = a->R;
+    const int64_t nslab = (int64_t)a->nseq * H;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t sl = 0; sl < nslab; sl++) {
+        int s = (int)(sl / H), h = (int)(sl % H);
+        int64_t len = a->seq_len[s];
+        double *ys = malloc((size_t)(len > 0 ? len : 1) * P * R * sizeof *ys);
+        double *hs = h_out ? h_out + ((int64_t)s * H + h) * N * P : NULL;
+        if (form == 1) o1_slab(a, s, h, ys, hs); else o2_slab(a, s, h, ys, hs);
+        for (int64_t tt = 0; tt < len; tt++)
+            memcpy(y + ((a->seq_start[s] + tt) * H + h) * P * R, ys + tt * P * R, (size_t)P * R * sizeof *ys);
+        free(ys);
+    }
+    return 0;
+}
+
+/* One (sequence, head) slab. y_slab: [len, P, R]; h_slab: [N, P] or NULL.
+ * form 1 = O1, 2 = O2, 3 = O3 (zero initial state / no previous token only). */
+int m3o_scan_slab(const m3o_args *a, int form, int s, int h, double *y_slab, double *h_slab) {
+    if (check(a) || !y_slab || s < 0 || s >= a->nseq || h < 0 || h >= a->H) return 1;
+    if (form == 1) o1_slab(a, s, h, y_slab, h_slab);
+    else if (form == 2) o2_slab(a, s, h, y_slab, h_slab);
+    else if (form == 3) {
+        if (a->h_in || a->Bprev || a->xprev || h_slab) return 1;
+        o3_slab(a, s, h, y_slab);
+    } else return 1;
+    return 0;
+}
+
+/* One decode step = one token of the O1 recurrence from a given state and
+ * previous token, for every (batch row, head): batch rows are sequences of
+ * length one. h_io: [batch, H, N, P] in/out; y: [batch, H, P, R]. */
+int m3o_decode(const m3o_args *a_in, double *h_io, double *y, int nthreads) {
+    if (check(a_in) || !h_io || !y) return 1;
+    m3o_args a = *a_in;
+    const int H = a.H, P = a.P, N = a.N, R = a.R;
+    double *hcopy = malloc((size_t)a.nseq * H * N * P * sizeof *hcopy);
+    memcpy(hcopy, h_io, (size_t)a.nseq * H * N * P * sizeof *hcopy);
+    a.h_in = hcopy;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t sl = 0; sl < (int64_t)a.nseq * H; sl++) {
+        int s = (int)(sl / H), h = (int)(sl % H);
+        o1_slab(&a, s, h, y + ((int64_t)s * H + h) * P * R, h_io + ((int64_t)s * H + h) * N * P);
+    }
+    free(hcopy);
+    return 0;
+}
+
+int m3o_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

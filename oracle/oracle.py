@@ -1,0 +1,172 @@
+"""ctypes front end of the fp64 CPU oracle (``m3_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``. The product path (the HIP library
+and its binding) never imports, links or calls anything here, and this module
+imports nothing from the product package.
+
+All arrays use the flat token axis (padded batches are flattened to
+``batch*seqlen`` tokens, sequence ``s`` starting at ``s*seqlen``):
+``x [T,H,P,R]``, ``dt, lam [T,H]``, ``theta [T,H,N/2]``, ``B, C [T,G,N,R]``,
+``A, D [H]``, ``h_in [S,H,N,P]``, ``Bprev [S,G,N,R]``, ``xprev [S,H,P,R]``.
+Token inputs may be float64, float32 or uint16 (bf16 bit patterns); they are
+converted exactly to double inside the oracle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "m3_oracle.c")
+_LIB = os.path.join(_HERE, "libm3oracle.so")
+
+F64, F32, BF16 = 0, 1, 2
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, fp64, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+                               "-Wall", "-Wextra", "-Wno-unused-parameter",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Args(ctypes.Structure):
+    _fields_ = [
+        ("nseq", ctypes.c_int32),
+        ("seq_start", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
+        ("H", ctypes.c_int32), ("G", ctypes.c_int32), ("P", ctypes.c_int32),
+        ("N", ctypes.c_int32), ("R", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("dt", ctypes.c_void_p), ("lam", ctypes.c_void_p),
+        ("theta", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+        ("A", ctypes.c_void_p), ("D", ctypes.c_void_p), ("h_in", ctypes.c_void_p),
+        ("Bprev", ctypes.c_void_p), ("xprev", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        l = ctypes.CDLL(_LIB)
+        l.m3o_scan.argtypes = [ctypes.POINTER(_Args), ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        l.m3o_scan_slab.argtypes = [ctypes.POINTER(_Args), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+        l.m3o_decode.argtypes = [ctypes.POINTER(_Args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        l.m3o_max_threads.restype = ctypes.c_int
+        _lib = l
+    return _lib
+
+
+def max_threads() -> int:
+    return lib().m3o_max_threads()
+
+
+def _tag(a: np.ndarray) -> int:
+    if a.dtype == np.float64:
+        return F64
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"unsupported oracle input dtype {a.dtype}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+class _Pack:
+    """Holds contiguous copies alive for the duration of a call."""
+
+    def __init__(self, inp: dict, seq_start, seq_len):
+        keep = {}
+        tok = [inp[k] for k in ("x", "dt", "lam", "theta", "B", "C")]
+        tag = _tag(tok[0])
+        for k in ("x", "dt", "lam", "theta", "B", "C", "Bprev", "xprev"):
+            v = inp.get(k)
+            if v is not None:
+                v = np.ascontiguousarray(v)
+                if _tag(v) != tag:
+                    raise TypeError(f"{k}: all token inputs must share one dtype")
+            keep[k] = v
+        for k in ("A", "D", "h_in"):
+            v = inp.get(k)
+            keep[k] = None if v is None else np.ascontiguousarray(v, dtype=np.float64)
+        x = keep["x"]
+        B = keep["B"]
+        H, P, R = x.shape[-3], x.shape[-2], x.shape[-1]
+        G, N = B.shape[-3], B.shape[-2]
+        keep["seq_start"] = np.ascontiguousarray(seq_start, dtype=np.int64)
+        keep["seq_len"] = np.ascontiguousarray(seq_len, dtype=np.int64)
+        self.keep = keep
+        self.H, self.G, self.P, self.N, self.R = H, G, P, N, R
+        self.nseq = len(keep["seq_len"])
+        self.args = _Args(self.nseq, _ptr(keep["seq_start"]), _ptr(keep["seq_len"]),
+                          H, G, P, N, R, tag,
+                          _ptr(keep["x"]), _ptr(keep["dt"]), _ptr(keep["lam"]), _ptr(keep["theta"]),
+                          _ptr(keep["B"]), _ptr(keep["C"]), _ptr(keep["A"]), _ptr(keep["D"]),
+                          _ptr(keep["h_in"]), _ptr(keep["Bprev"]), _ptr(keep["xprev"]))
+
+
+def flatten(inp: dict) -> tuple[dict, np.ndarray, np.ndarray]:
+    """[batch, L, ...] inputs -> flat token axis + sequence table. Packed
+    inputs (key ``cu_seqlens``, batch 1) take their table from cu_seqlens."""
+    out = dict(inp)
+    b, L = inp["x"].shape[0], inp["x"].shape[1]
+    for k in ("x", "dt", "lam", "theta", "B", "C"):
+        out[k] = inp[k].reshape((b * L,) + inp[k].shape[2:])
+    if inp.get("cu_seqlens") is not None:
+        if b != 1:
+            raise ValueError("packed inputs have batch 1")
+        cu = np.asarray(inp["cu_seqlens"], dtype=np.int64)
+        return out, cu[:-1].copy(), np.diff(cu)
+    return out, np.arange(b, dtype=np.int64) * L, np.full(b, L, dtype=np.int64)
+
+
+def scan(inp: dict, form: int = 1, nthreads: int = 0, want_state: bool = True):
+    """Whole scan. Returns (y [same leading shape as x], h_out [S,H,N,P])."""
+    flat, st, ln = flatten(inp)
+    pk = _Pack(flat, st, ln)
+    T = flat["x"].shape[0]
+    y = np.zeros((T, pk.H, pk.P, pk.R), dtype=np.float64)
+    h = np.zeros((pk.nseq, pk.H, pk.N, pk.P), dtype=np.float64) if want_state else None
+    rc = lib().m3o_scan(ctypes.byref(pk.args), form, y.ctypes.data, _ptr(h), nthreads)
+    if rc:
+        raise ValueError("oracle rejected its arguments")
+    return y.reshape(inp["x"].shape), h
+
+
+def scan_slab(inp: dict, s: int, h: int, form: int = 1, want_state: bool = True):
+    """One (sequence, head) slab. Returns (y [len,P,R], h_out [N,P] or None)."""
+    flat, st, ln = flatten(inp)
+    pk = _Pack(flat, st, ln)
+    y = np.zeros((int(ln[s]), pk.P, pk.R), dtype=np.float64)
+    hs = np.zeros((pk.N, pk.P), dtype=np.float64) if want_state else None
+    rc = lib().m3o_scan_slab(ctypes.byref(pk.args), form, s, h, y.ctypes.data, _ptr(hs))
+    if rc:
+        raise ValueError("oracle rejected its arguments")
+    return y, hs
+
+
+def decode(inp: dict, h: np.ndarray, nthreads: int = 0):
+    """One decode step. inp token arrays have a leading batch axis (no L).
+    Returns (y [batch,H,P,R], h_new [batch,H,N,P]) in float64."""
+    b = inp["x"].shape[0]
+    pk = _Pack(inp, np.arange(b, dtype=np.int64), np.ones(b, dtype=np.int64))
+    hio = np.array(h, dtype=np.float64, copy=True, order="C")
+    y = np.zeros((b, pk.H, pk.P, pk.R), dtype=np.float64)
+    rc = lib().m3o_decode(ctypes.byref(pk.args), hio.ctypes.data, y.ctypes.data, nthreads)
+    if rc:
+        raise ValueError("oracle rejected its arguments")
+    return y, hio

@@ -1,0 +1,50 @@
+"""The oracle's pins have teeth: plant one mistake at a time in a scratch copy
+of the oracle's C source (on the CPU, never on a GPU) and check that the pins
+which do not compare the oracle's two recurrence forms with each other fail.
+
+Mistakes planted: the previous-token term skipping the step's rotation/decay,
+the rotation direction, the sign of C's or B's imaginary part, trapezoid
+weights swapped, rank columns mixed, the D term dropped, and a stale previous
+token."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = {
+    "prev_not_rotated": ("hc[k * P + p] = z[k] * (hc[k * P + p] + delta * prev) + gamma * cur;",
+                         "hc[k * P + p] = z[k] * hc[k * P + p] + delta * prev + gamma * cur;"),
+    "rotation_sign": ("z[k] = decay * (cos(ang) + I * sin(ang));", "z[k] = decay * (cos(ang) - I * sin(ang));"),
+    "c_imag_sign": ("cc[k * R + j] = ld(a->C, dtp, ob + (2 * k) * R + j) -",
+                    "cc[k * R + j] = ld(a->C, dtp, ob + (2 * k) * R + j) +"),
+    "b_imag_sign": ("I * ld(a->B, dtp, ob + (2 * k + 1) * R + j);\n                cc",
+                    "-I * ld(a->B, dtp, ob + (2 * k + 1) * R + j);\n                cc"),
+    "weights_swapped": ("const double delta = (1.0 - lam) * dt, gamma = lam * dt;",
+                        "const double gamma = (1.0 - lam) * dt, delta = lam * dt;"),
+    "rank_mixed": ("cur += bc[k * R + j] * xc[p * R + j];", "cur += bc[k * R + j] * xc[p * R + 0];"),
+    "no_skip_term": ("yt[p * R + i] = creal(acc) + Dh * xc[p * R + i];", "yt[p * R + i] = creal(acc);"),
+    "stale_previous": ("memcpy(bp, bc, (size_t)K * R * sizeof *bp);\n        memcpy(xp, xc, (size_t)P * R * sizeof *xp);\n",
+                       ""),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    src = open(os.path.join(ROOT, "oracle", "m3_oracle.c")).read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) == 1, "mutation anchor moved; update the anchor"
+    work = tmp_path / "tree"
+    os.makedirs(work)
+    shutil.copytree(os.path.join(ROOT, "oracle"), work / "oracle", ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "tests"), work / "tests", ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "state_space_sequence_mamba3_amd"), work / "state_space_sequence_mamba3_amd",
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__", "_build"))
+    (work / "oracle" / "m3_oracle.c").write_text(src.replace(old, new))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_pins.py", "-k", "not rotated_frame"],
+                       cwd=work, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 and " failed" in r.stdout, r.stdout[-2000:]
