@@ -1,0 +1,142 @@
+/*
+ * mamba3.h - C ABI of the Mamba-3 SSM layer recurrence on AMD MI355X (gfx950).
+ *
+ * The operation (per sequence s, head h, B/C group g = h / (H/G), token t):
+ *   alpha_t = exp(dt_t A_h),  delta_t = (1 - lam_t) dt_t,  gamma_t = lam_t dt_t
+ *   R_t     = block-diagonal 2x2 rotations R(dt_t theta_t[k]) on state rows
+ *             (2k, 2k+1), R(a) = [[cos a, -sin a], [sin a, cos a]]
+ *   H_t     = alpha_t R_t (H_{t-1} + delta_t B_{t-1} X_{t-1}^T) + gamma_t B_t X_t^T
+ *   y_t     = H_t^T C_t + D_h X_t
+ * with H_t in R^{N x P} (fp32), B_t, C_t in R^{N x R}, X_t, y_t in R^{P x R}.
+ * This is the exponential-trapezoidal three-term update ("Mamba-3" paper
+ * summary, section "Exponential-Trapezoidal Discretization", Proposition 1:
+ * alpha, beta = delta * alpha, gamma) with the complex-valued transition of
+ * Propositions 2-4 ("Complex-Valued State Space Models": exp(dt(A + i theta))
+ * as a scalar decay times block-diagonal rotations, realised by the RoPE trick
+ * of cumulative rotation angles on B and C) and the rank-R MIMO state update
+ * B_t X_t^T = sum_r B_t^(r) X_t^(r)T ("MIMO Formulation"). The state is kept in
+ * the physical frame (no cumulative angle is carried across calls).
+ *
+ * Layouts (row-major, innermost last; T = tokens):
+ *   x, y        [batch, seqlen, H, P, R]        token inputs / outputs
+ *   dt, lam     [batch, seqlen, H]              step (post-softplus), trapezoid weight in [0,1]
+ *   theta       [batch, seqlen, H, N/2]         rotation frequency; the angle is dt*theta
+ *   B, C        [batch, seqlen, G, N, R]
+ *   A, D        [H] fp32                         decay (A < 0) and skip; D may be NULL (= 0)
+ *   states      [S, H, N, P] fp32                S = batch (padded) or nseq (packed)
+ *   Bprev       [S, G, N, R],  xprev [S, H, P, R]   token before position 0 of each sequence
+ * Token inputs x, dt, lam, theta, B, C, Bprev, xprev and the output y share
+ * one dtype (fp32 or bf16); states, A and D are fp32; arithmetic accumulates
+ * in fp32.
+ *
+ * Conventions:
+ *   - All pointers are device pointers, owned by the caller. The library
+ *     allocates nothing, keeps no pointer after returning, holds no global
+ *     mutable state and is reentrant.
+ *   - Calls enqueue work on the given HIP stream (a hipStream_t passed as
+ *     void*, NULL = default stream) and return without synchronising.
+ *   - Every argument is validated on the host before anything is enqueued: a
+ *     status other than MAMBA3_OK means nothing was launched. Device data
+ *     (values of A, cu_seqlens, ...) is not inspected.
+ *   - A launch failure reported by the HIP runtime returns MAMBA3_EHIP.
+ *   - y must not alias any input. h_out may alias h_in (same slab layout).
+ *   - x, theta, B, C, Bprev, xprev, y and the states must be 16-byte aligned;
+ *     dt and lam need element alignment, A, D and cu_seqlens 4 bytes.
+ */
+#ifndef MAMBA3_H
+#define MAMBA3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MAMBA3_OK = 0,
+    MAMBA3_EINVAL = 1,        /* bad size, NULL required pointer, inconsistent shape */
+    MAMBA3_EUNSUPPORTED = 2,  /* valid but no kernel for this (N, P, R, chunk, dtype) */
+    MAMBA3_EALIGN = 3,        /* a pointer lacks its required alignment */
+    MAMBA3_EHIP = 4,          /* HIP runtime error (no device, launch failure) */
+    MAMBA3_EWORKSPACE = 5     /* workspace missing or too small */
+} mamba3_status;
+
+typedef enum { MAMBA3_F32 = 0, MAMBA3_BF16 = 1 } mamba3_dtype;
+
+/* Whole-sequence chunked scan.
+ *
+ * Padded mode (cu_seqlens == NULL): batch sequences of seqlen tokens each.
+ * Packed mode (cu_seqlens != NULL): batch must be 1; the seqlen tokens hold
+ * nseq sequences back to back, sequence s occupying tokens
+ * [cu_seqlens[s], cu_seqlens[s+1]) (device int32 array of nseq+1 entries,
+ * non-decreasing, cu_seqlens[0] = 0, cu_seqlens[nseq] = seqlen; entries are
+ * clamped to [0, seqlen] on the device). Every sequence start resets the
+ * recurrence: the state is h_in[s] (or zero) and the previous-token term uses
+ * Bprev[s], xprev[s] (or is zero).
+ *
+ * chunk: tokens per chunk of the chunked algorithm (intra-chunk quadratic
+ * form, inter-chunk recurrence: section "Parallel representation under SSD").
+ * The result does not depend on it beyond rounding.
+ *
+ * h_in  NULL: zero initial state.
+ * Bprev/xprev NULL (both): no previous-token term at the sequence start.
+ * h_out NULL: final state not written.
+ */
+typedef struct {
+    int32_t batch, seqlen, nheads, headdim /* P */, dstate /* N, even */, rank /* R */;
+    int32_t ngroups /* G, divides nheads */, chunk /* Q */;
+    int32_t dtype;               /* mamba3_dtype of the token inputs and y */
+    const int32_t *cu_seqlens;   /* packed mode sequence table, or NULL */
+    int32_t nseq;                /* packed mode: number of sequences */
+    const void *x, *dt, *lam, *theta, *B, *C;
+    const float *A, *D;
+    const float *h_in;
+    const void *Bprev, *xprev;
+    void *y;
+    float *h_out;
+    void *workspace;             /* reserved: pass NULL / 0 when the size query returns 0 */
+    size_t workspace_bytes;
+} mamba3_scan_args;
+
+/* Pure host check of every argument (no HIP call). */
+mamba3_status mamba3_scan_validate(const mamba3_scan_args *args);
+
+/* Workspace bytes mamba3_scan_fwd needs for these arguments (currently 0 for
+ * every supported configuration). */
+size_t mamba3_scan_workspace_size(const mamba3_scan_args *args);
+
+/* Enqueue the scan on `stream`. Writes y (every token) and h_out (if given). */
+mamba3_status mamba3_scan_fwd(const mamba3_scan_args *args, void *stream);
+
+/* One decode step for a batch of independent sequences, state updated in
+ * place: h <- alpha R (h + delta Bprev xprev^T) + gamma B x^T, y = h^T C + D x
+ * (the same update as one token of the scan; section "MIMO Formulation" gives
+ * the decode-time form H_t = alpha_t H_{t-1} + dt B_t x_t^T, y_t = H_t^T C_t).
+ * Layouts: x, y [batch, H, P, R]; dt, lam [batch, H]; theta [batch, H, N/2];
+ * B, C [batch, G, N, R]; Bprev [batch, G, N, R] and xprev [batch, H, P, R]
+ * (both NULL = no previous-token term); h [batch, H, N, P] fp32 in/out. */
+typedef struct {
+    int32_t batch, nheads, headdim, dstate, rank, ngroups;
+    int32_t dtype;
+    const void *x, *dt, *lam, *theta, *B, *C;
+    const void *Bprev, *xprev;
+    const float *A, *D;
+    float *h;
+    void *y;
+} mamba3_decode_args;
+
+mamba3_status mamba3_decode_validate(const mamba3_decode_args *args);
+mamba3_status mamba3_decode_step(const mamba3_decode_args *args, void *stream);
+
+/* Static description of a status code. */
+const char *mamba3_status_string(mamba3_status status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int32_t mamba3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA3_H */

@@ -1,0 +1,166 @@
+"""Mamba-3 SSM layer recurrence on AMD MI355X (gfx950).
+
+Thin ctypes binding over the C ABI of ``libmamba3.so`` (declared in
+``include/mamba3.h``). It only marshals arguments: torch tensors provide the
+device memory and the current HIP stream; every step of the computation runs
+in the library's HIP kernels. If the library is missing the binding raises;
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmamba3.so")
+
+MAMBA3_OK, MAMBA3_EINVAL, MAMBA3_EUNSUPPORTED, MAMBA3_EALIGN, MAMBA3_EHIP, MAMBA3_EWORKSPACE = range(6)
+MAMBA3_F32, MAMBA3_BF16 = 0, 1
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+
+
+class ScanArgs(ctypes.Structure):
+    """Mirror of ``mamba3_scan_args``."""
+    _fields_ = [
+        ("batch", _i32), ("seqlen", _i32), ("nheads", _i32), ("headdim", _i32), ("dstate", _i32),
+        ("rank", _i32), ("ngroups", _i32), ("chunk", _i32), ("dtype", _i32),
+        ("cu_seqlens", _vp), ("nseq", _i32),
+        ("x", _vp), ("dt", _vp), ("lam", _vp), ("theta", _vp), ("B", _vp), ("C", _vp),
+        ("A", _vp), ("D", _vp), ("h_in", _vp), ("Bprev", _vp), ("xprev", _vp),
+        ("y", _vp), ("h_out", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of ``mamba3_decode_args``."""
+    _fields_ = [
+        ("batch", _i32), ("nheads", _i32), ("headdim", _i32), ("dstate", _i32), ("rank", _i32),
+        ("ngroups", _i32), ("dtype", _i32),
+        ("x", _vp), ("dt", _vp), ("lam", _vp), ("theta", _vp), ("B", _vp), ("C", _vp),
+        ("Bprev", _vp), ("xprev", _vp), ("A", _vp), ("D", _vp), ("h", _vp), ("y", _vp),
+    ]
+
+
+EXPORTS = ("mamba3_scan_validate", "mamba3_scan_workspace_size", "mamba3_scan_fwd", "mamba3_decode_validate",
+           "mamba3_decode_step", "mamba3_status_string", "mamba3_version")
+
+_lib = None
+
+
+class Mamba3Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def lib():
+    """Loads libmamba3.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m state_space_sequence_mamba3_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        l.mamba3_scan_validate.argtypes = [ctypes.POINTER(ScanArgs)]
+        l.mamba3_scan_validate.restype = ctypes.c_int
+        l.mamba3_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs)]
+        l.mamba3_scan_workspace_size.restype = ctypes.c_size_t
+        l.mamba3_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _vp]
+        l.mamba3_scan_fwd.restype = ctypes.c_int
+        l.mamba3_decode_validate.argtypes = [ctypes.POINTER(DecodeArgs)]
+        l.mamba3_decode_validate.restype = ctypes.c_int
+        l.mamba3_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+        l.mamba3_decode_step.restype = ctypes.c_int
+        l.mamba3_status_string.argtypes = [ctypes.c_int]
+        l.mamba3_status_string.restype = ctypes.c_char_p
+        l.mamba3_version.restype = ctypes.c_int32
+        _lib = l
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mamba3_status_string(status).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return t.data_ptr() if hasattr(t, "data_ptr") else int(t)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MAMBA3_BF16
+    if t.dtype == torch.float32:
+        return MAMBA3_F32
+    raise TypeError(f"token inputs must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def scan_args(x, dt, lam, theta, B, C, A, D=None, *, y, h_in=None, h_out=None, Bprev=None, xprev=None,
+              cu_seqlens=None, chunk=64) -> ScanArgs:
+    """Builds a ScanArgs from tensors in the library's layouts (see mamba3.h)."""
+    b, L, H, P, R = x.shape
+    G, N = B.shape[2], B.shape[3]
+    nseq = int(cu_seqlens.numel()) - 1 if cu_seqlens is not None else 0
+    return ScanArgs(b, L, H, P, N, R, G, chunk, _dtype_code(x), _ptr(cu_seqlens), nseq,
+                    _ptr(x), _ptr(dt), _ptr(lam), _ptr(theta), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
+                    _ptr(h_in), _ptr(Bprev), _ptr(xprev), _ptr(y), _ptr(h_out), None, 0)
+
+
+def mamba3_scan_validate(args: ScanArgs) -> int:
+    return lib().mamba3_scan_validate(ctypes.byref(args))
+
+
+def mamba3_scan_workspace_size(args: ScanArgs) -> int:
+    return lib().mamba3_scan_workspace_size(ctypes.byref(args))
+
+
+def mamba3_scan_fwd(x, dt, lam, theta, B, C, A, D=None, *, y=None, h_in=None, h_out=None, Bprev=None,
+                    xprev=None, cu_seqlens=None, chunk=64, want_state=True, stream=None):
+    """Chunked scan over whole sequences. Tensors are device tensors in the
+    layouts of mamba3.h; y and h_out are allocated when not given. Returns
+    (y, h_out)."""
+    import torch
+    if y is None:
+        y = torch.empty_like(x)
+    if h_out is None and want_state:
+        S = int(cu_seqlens.numel()) - 1 if cu_seqlens is not None else x.shape[0]
+        h_out = torch.empty((S, x.shape[2], B.shape[3], x.shape[3]), dtype=torch.float32, device=x.device)
+    a = scan_args(x, dt, lam, theta, B, C, A, D, y=y, h_in=h_in, h_out=h_out, Bprev=Bprev, xprev=xprev,
+                  cu_seqlens=cu_seqlens, chunk=chunk)
+    st = lib().mamba3_scan_fwd(ctypes.byref(a), _stream(stream))
+    if st != MAMBA3_OK:
+        raise Mamba3Error(st, "mamba3_scan_fwd")
+    return y, h_out
+
+
+def decode_args(x, dt, lam, theta, B, C, A, D=None, *, h, y, Bprev=None, xprev=None) -> DecodeArgs:
+    b, H, P, R = x.shape
+    G, N = B.shape[1], B.shape[2]
+    return DecodeArgs(b, H, P, N, R, G, _dtype_code(x), _ptr(x), _ptr(dt), _ptr(lam), _ptr(theta), _ptr(B),
+                      _ptr(C), _ptr(Bprev), _ptr(xprev), _ptr(A), _ptr(D), _ptr(h), _ptr(y))
+
+
+def mamba3_decode_validate(args: DecodeArgs) -> int:
+    return lib().mamba3_decode_validate(ctypes.byref(args))
+
+
+def mamba3_decode_step(x, dt, lam, theta, B, C, A, D=None, *, h, y=None, Bprev=None, xprev=None, stream=None):
+    """One decode step; h (fp32 [batch,H,N,P]) is updated in place. Returns y."""
+    import torch
+    if y is None:
+        y = torch.empty_like(x)
+    a = decode_args(x, dt, lam, theta, B, C, A, D, h=h, y=y, Bprev=Bprev, xprev=xprev)
+    st = lib().mamba3_decode_step(ctypes.byref(a), _stream(stream))
+    if st != MAMBA3_OK:
+        raise Mamba3Error(st, "mamba3_decode_step")
+    return y

@@ -1,0 +1,44 @@
+// Shared device/host helpers of the HIP library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mamba3.h"
+
+namespace m3 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Token-input element access: fp32 or bf16 (bf16 -> fp32 is exact).
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16>(bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+// gfx950 converts with v_cvt_pk_bf16_f32 (round to nearest even).
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float v) { return (bf16)v; }
+
+// Launch plumbing shared by the kernels' host-side entry points.
+struct ScanPlan {
+    const mamba3_scan_args *a;
+    int64_t nslab;      // sequences * heads
+    int32_t nseq;
+};
+
+mamba3_status launch_scan_f32(const mamba3_scan_args *a, hipStream_t st);
+mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st);
+bool scan_bf16_supported(int N, int P, int R, int Q);
+size_t scan_f32_lds_bytes(int N, int P, int R, int Q);
+mamba3_status launch_decode(const mamba3_decode_args *a, hipStream_t st);
+bool decode_supported(int N, int P, int R, int dtype);
+
+}  // namespace m3

@@ -1,0 +1,217 @@
+// fp32 chunked scan (VALU). One workgroup per (sequence, head) walks the
+// sequence chunk by chunk, keeping the fp32 state in LDS.
+//
+// Chunked form used here (derived from the three-term update of Proposition 4,
+// "Complex-Valued State Space Models", and the SSD matrix form of section
+// "Parallel representation under SSD"): inside a chunk with first token c0,
+// S_t = sum_{c0<=k<=t} dt_k A (log decay), Phi_t[k] = sum_{c0<=j<=t} dt_j theta_j[k]
+// (cumulative angle, restarted at every chunk), B~_s = R(-Phi_s) B_s,
+// C~_t = R(-Phi_t) C_t. With the carried state H' (physical frame) entering
+// the chunk,
+//   y_t = e^{S_t} C~_t^T H' + sum_{s<=t} e^{S_t - S_s} w(t,s) (C~_t . B~_s) X_s + D X_t
+//   w(t,s) = gamma_s + delta_{s+1} [s < t]
+// and the state leaving the chunk (last token e) is
+//   H'_next = R(Phi_e) ( e^{S_e} H' + sum_s e^{S_e - S_s} (gamma_s + delta_{s+1}) B~_s X_s^T ),
+// where delta_{e+1} is the next chunk's first token's (0 at the sequence end),
+// which folds that token's previous-input term into the carried state.
+// At the sequence start H' = h_in + delta_0 Bprev xprev^T.
+#include "m3_common.h"
+
+namespace m3 {
+
+struct ValuParams {
+    const float *x, *dt, *lam, *theta, *B, *C, *Bprev, *xprev;
+    const float *A, *D, *h_in;
+    float *y, *h_out;
+    const int32_t *cu;
+    int32_t nseq, seqlen, H, G, P, N, R, Q;
+};
+
+size_t scan_f32_lds_bytes(int N, int P, int R, int Q) {
+    size_t QR = (size_t)Q * R, K = N / 2;
+    size_t floats = QR * N * 2 + QR * P + QR * QR + (size_t)N * P + (size_t)Q * (7 + K);
+    return floats * sizeof(float);
+}
+
+__global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
+    extern __shared__ float smem[];
+    const int H = p.H, G = p.G, P = p.P, N = p.N, R = p.R, Q = p.Q, K = N / 2, QR = Q * R;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int s = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
+
+    float *Bt = smem;              // [QR][N]
+    float *Ct = Bt + QR * N;       // [QR][N]
+    float *Xs = Ct + QR * N;       // [QR][P]
+    float *M = Xs + QR * P;        // [QR][QR]
+    float *Hs = M + QR * QR;       // [N][P]
+    float *S = Hs + N * P;         // [Q] log decay prefix
+    float *gm = S + Q;             // [Q] gamma
+    float *dl = gm + Q;            // [Q] delta
+    float *g1 = dl + Q;            // [Q] gamma_s + delta_{s+1}
+    float *dts = g1 + Q;           // [Q] dt
+    float *wU = dts + Q;           // [Q] chunk-state weights
+    float *misc = wU + Q;          // [Q] (misc[0] = delta of the token after the chunk)
+    float *phi = misc + Q;         // [Q][K]
+
+    int64_t start, len;
+    if (p.cu) {
+        int64_t a = min(max((int64_t)p.cu[s], (int64_t)0), (int64_t)p.seqlen);
+        int64_t b = min(max((int64_t)p.cu[s + 1], a), (int64_t)p.seqlen);
+        start = a;
+        len = b - a;
+    } else {
+        start = (int64_t)s * p.seqlen;
+        len = p.seqlen;
+    }
+    const float Ah = p.A[h];
+    const float Dh = p.D ? p.D[h] : 0.f;
+    const int64_t st_off = ((int64_t)s * H + h) * N * P;
+
+    for (int e = tid; e < N * P; e += nt) Hs[e] = p.h_in ? p.h_in[st_off + e] : 0.f;
+    __syncthreads();
+
+    for (int64_t c0 = 0; c0 < len; c0 += Q) {
+        const int nq = (int)min((int64_t)Q, len - c0);
+        // per-token scalars
+        for (int t = tid; t < Q; t += nt) {
+            float dtv = 0.f, lv = 0.f;
+            if (t < nq) {
+                int64_t tg = start + c0 + t;
+                dtv = p.dt[tg * H + h];
+                lv = p.lam[tg * H + h];
+            }
+            dts[t] = dtv;
+            gm[t] = lv * dtv;
+            dl[t] = (1.f - lv) * dtv;
+        }
+        if (tid == 0) {
+            float dnext = 0.f;
+            if (c0 + nq < len) {
+                int64_t tg = start + c0 + nq;
+                float dtv = p.dt[tg * H + h], lv = p.lam[tg * H + h];
+                dnext = (1.f - lv) * dtv;
+            }
+            misc[0] = dnext;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float acc = 0.f;
+            for (int t = 0; t < Q; t++) {
+                if (t < nq) acc += dts[t] * Ah;
+                S[t] = acc;
+                float dn = (t + 1 < nq) ? dl[t + 1] : (t + 1 == nq ? misc[0] : 0.f);
+                g1[t] = gm[t] + dn;
+            }
+            for (int t = 0; t < Q; t++) wU[t] = (t < nq) ? expf(S[nq - 1] - S[t]) * g1[t] : 0.f;
+        }
+        for (int k = tid; k < K; k += nt) {
+            float acc = 0.f;
+            for (int t = 0; t < Q; t++) {
+                if (t < nq) acc += dts[t] * p.theta[((start + c0 + t) * H + h) * K + k];
+                phi[t * K + k] = acc;
+            }
+        }
+        // previous-token fold at the sequence start: H' += delta_0 Bprev xprev^T
+        if (c0 == 0 && p.Bprev) {
+            const int64_t ob = ((int64_t)s * G + g) * N * R, ox = ((int64_t)s * H + h) * P * R;
+            const float d0 = dl[0];
+            for (int e = tid; e < N * P; e += nt) {
+                int n = e / P, pp = e % P;
+                float acc = 0.f;
+                for (int j = 0; j < R; j++) acc += p.Bprev[ob + n * R + j] * p.xprev[ox + pp * R + j];
+                Hs[e] += d0 * acc;
+            }
+        }
+        __syncthreads();
+        // rotated B~, C~ and X for the chunk (zero past the sequence end)
+        for (int e = tid; e < Q * K * R; e += nt) {
+            int t = e / (K * R), k = (e / R) % K, j = e % R;
+            float b0 = 0.f, b1 = 0.f, q0 = 0.f, q1 = 0.f, cs = 1.f, sn = 0.f;
+            if (t < nq) {
+                int64_t ob = ((start + c0 + t) * G + g) * N * R;
+                b0 = p.B[ob + (2 * k) * R + j];
+                b1 = p.B[ob + (2 * k + 1) * R + j];
+                q0 = p.C[ob + (2 * k) * R + j];
+                q1 = p.C[ob + (2 * k + 1) * R + j];
+                sincosf(phi[t * K + k], &sn, &cs);
+            }
+            int r = t * R + j;
+            Bt[r * N + 2 * k] = cs * b0 + sn * b1;
+            Bt[r * N + 2 * k + 1] = -sn * b0 + cs * b1;
+            Ct[r * N + 2 * k] = cs * q0 + sn * q1;
+            Ct[r * N + 2 * k + 1] = -sn * q0 + cs * q1;
+        }
+        for (int e = tid; e < Q * P * R; e += nt) {
+            int t = e / (P * R), pp = (e / R) % P, j = e % R;
+            float v = (t < nq) ? p.x[((start + c0 + t) * H + h) * P * R + pp * R + j] : 0.f;
+            Xs[(t * R + j) * P + pp] = v;
+        }
+        __syncthreads();
+        // masked score matrix M[(t,i)][(s,j)]
+        for (int e = tid; e < QR * QR; e += nt) {
+            int r = e / QR, q = e % QR, tt = r / R, ss = q / R;
+            float v = 0.f;
+            if (ss <= tt && tt < nq) {
+                float gdot = 0.f;
+                for (int n = 0; n < N; n++) gdot += Ct[r * N + n] * Bt[q * N + n];
+                float w = (ss < tt) ? g1[ss] : gm[ss];
+                v = expf(S[tt] - S[ss]) * w * gdot;
+            }
+            M[e] = v;
+        }
+        __syncthreads();
+        // outputs
+        for (int e = tid; e < QR * P; e += nt) {
+            int r = e / P, pp = e % P, tt = r / R, i = r % R;
+            if (tt >= nq) continue;
+            float inter = 0.f;
+            for (int n = 0; n < N; n++) inter += Ct[r * N + n] * Hs[n * P + pp];
+            float acc = expf(S[tt]) * inter;
+            for (int q = 0; q < (tt + 1) * R; q++) acc += M[r * QR + q] * Xs[q * P + pp];
+            acc += Dh * Xs[r * P + pp];
+            p.y[((start + c0 + tt) * H + h) * P * R + pp * R + i] = acc;
+        }
+        __syncthreads();
+        // carried state
+        {
+            const float eS = expf(S[nq - 1]);
+            for (int e = tid; e < K * P; e += nt) {
+                int k = e / P, pp = e % P;
+                float u0 = eS * Hs[(2 * k) * P + pp], u1 = eS * Hs[(2 * k + 1) * P + pp];
+                for (int q = 0; q < nq * R; q++) {
+                    float w = wU[q / R] * Xs[q * P + pp];
+                    u0 += w * Bt[q * N + 2 * k];
+                    u1 += w * Bt[q * N + 2 * k + 1];
+                }
+                float sn, cs;
+                sincosf(phi[(nq - 1) * K + k], &sn, &cs);
+                Hs[(2 * k) * P + pp] = cs * u0 - sn * u1;
+                Hs[(2 * k + 1) * P + pp] = sn * u0 + cs * u1;
+            }
+        }
+        __syncthreads();
+    }
+    if (p.h_out)
+        for (int e = tid; e < N * P; e += nt) p.h_out[st_off + e] = Hs[e];
+}
+
+mamba3_status launch_scan_f32(const mamba3_scan_args *a, hipStream_t st) {
+    ValuParams p;
+    p.x = (const float *)a->x; p.dt = (const float *)a->dt; p.lam = (const float *)a->lam;
+    p.theta = (const float *)a->theta; p.B = (const float *)a->B; p.C = (const float *)a->C;
+    p.Bprev = (const float *)a->Bprev; p.xprev = (const float *)a->xprev;
+    p.A = a->A; p.D = a->D; p.h_in = a->h_in; p.y = (float *)a->y; p.h_out = a->h_out;
+    p.cu = a->cu_seqlens;
+    p.nseq = a->cu_seqlens ? a->nseq : a->batch;
+    p.seqlen = a->seqlen; p.H = a->nheads; p.G = a->ngroups; p.P = a->headdim; p.N = a->dstate;
+    p.R = a->rank; p.Q = a->chunk;
+    size_t lds = scan_f32_lds_bytes(p.N, p.P, p.R, p.Q);
+    if (hipFuncSetAttribute((const void *)k_scan_f32, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return MAMBA3_EHIP;
+    int64_t nblk = (int64_t)p.nseq * p.H;
+    if (nblk == 0) return MAMBA3_OK;
+    hipLaunchKernelGGL(k_scan_f32, dim3((unsigned)nblk), dim3(256), lds, st, p);
+    return hipGetLastError() == hipSuccess ? MAMBA3_OK : MAMBA3_EHIP;
+}
+
+}  // namespace m3

@@ -1,0 +1,132 @@
+"""C ABI on the CPU: the library loads, exports every declared symbol, and its
+pure host-side validation returns the documented status codes. No compute
+call is made here (no GPU in this tier)."""
+import os
+import re
+
+import pytest
+
+import state_space_sequence_mamba3_amd as m3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(m3.LIB_PATH):
+        from state_space_sequence_mamba3_amd import build
+        build.build()
+    return m3.lib()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mamba3.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba3_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(m3.EXPORTS)
+
+
+def test_status_strings(lib):
+    assert m3.status_string(m3.MAMBA3_OK) == "ok"
+    for s in range(6):
+        assert m3.status_string(s)
+    assert lib.mamba3_version() == 10000
+
+
+BASE = 0x7F0000000000
+
+
+def fake(i):
+    return BASE + i * 0x100000000
+
+
+def good_scan(**over):
+    a = m3.ScanArgs(batch=2, seqlen=100, nheads=4, headdim=16, dstate=16, rank=1, ngroups=4, chunk=64,
+                    dtype=m3.MAMBA3_F32, cu_seqlens=None, nseq=0, x=fake(1), dt=fake(2), lam=fake(3),
+                    theta=fake(4), B=fake(5), C=fake(6), A=fake(7), D=fake(8), h_in=None, Bprev=None,
+                    xprev=None, y=fake(9), h_out=fake(10), workspace=None, workspace_bytes=0)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_scan_validate_ok(lib):
+    assert m3.mamba3_scan_validate(good_scan()) == m3.MAMBA3_OK
+    assert m3.mamba3_scan_validate(good_scan(h_in=fake(11), Bprev=fake(12), xprev=fake(13))) == m3.MAMBA3_OK
+    # h_out may alias h_in
+    assert m3.mamba3_scan_validate(good_scan(h_in=fake(10))) == m3.MAMBA3_OK
+    assert m3.mamba3_scan_workspace_size(good_scan()) == 0
+    # empty inputs are valid
+    assert m3.mamba3_scan_validate(good_scan(seqlen=0)) == m3.MAMBA3_OK
+    assert m3.mamba3_scan_validate(good_scan(batch=0)) == m3.MAMBA3_OK
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dstate", 15, m3.MAMBA3_EINVAL),
+    ("dstate", 0, m3.MAMBA3_EINVAL),
+    ("ngroups", 3, m3.MAMBA3_EINVAL),
+    ("rank", 0, m3.MAMBA3_EINVAL),
+    ("chunk", 0, m3.MAMBA3_EINVAL),
+    ("headdim", 0, m3.MAMBA3_EINVAL),
+    ("dtype", 7, m3.MAMBA3_EINVAL),
+    ("x", None, m3.MAMBA3_EINVAL),
+    ("A", None, m3.MAMBA3_EINVAL),
+    ("y", None, m3.MAMBA3_EINVAL),
+    ("Bprev", BASE + 0x5000000000, m3.MAMBA3_EINVAL),      # Bprev without xprev
+    ("x", BASE + 0x100000008, m3.MAMBA3_EALIGN),
+    ("theta", BASE + 0x400000004, m3.MAMBA3_EALIGN),
+    ("dt", BASE + 0x200000002, m3.MAMBA3_EALIGN),           # fp32 needs 4-byte alignment
+    ("h_out", BASE + 0xA00000004, m3.MAMBA3_EALIGN),
+    ("y", BASE + 0x100000000, m3.MAMBA3_EINVAL),            # y aliases x
+    ("h_out", BASE + 0x500000000, m3.MAMBA3_EINVAL),        # h_out overlaps B
+    ("workspace_bytes", 64, m3.MAMBA3_EWORKSPACE),
+    ("chunk", 100000, m3.MAMBA3_EUNSUPPORTED),              # fp32 tile does not fit LDS
+])
+def test_scan_validate_errors(lib, field, value, status):
+    assert m3.mamba3_scan_validate(good_scan(**{field: value})) == status
+
+
+def test_scan_validate_packed(lib):
+    a = good_scan(batch=1, seqlen=500, nseq=3)
+    a.cu_seqlens = fake(20)
+    assert m3.mamba3_scan_validate(a) == m3.MAMBA3_OK
+    a.batch = 2
+    assert m3.mamba3_scan_validate(a) == m3.MAMBA3_EINVAL
+    a.batch, a.nseq = 1, 0
+    assert m3.mamba3_scan_validate(a) == m3.MAMBA3_EINVAL
+
+
+def test_scan_validate_null_args(lib):
+    assert lib.mamba3_scan_validate(None) == m3.MAMBA3_EINVAL
+    assert lib.mamba3_decode_validate(None) == m3.MAMBA3_EINVAL
+
+
+def good_decode(**over):
+    a = m3.DecodeArgs(batch=4, nheads=8, headdim=64, dstate=64, rank=4, ngroups=8, dtype=m3.MAMBA3_BF16,
+                      x=fake(1), dt=fake(2), lam=fake(3), theta=fake(4), B=fake(5), C=fake(6), Bprev=fake(7),
+                      xprev=fake(8), A=fake(9), D=fake(10), h=fake(11), y=fake(12))
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_validate(lib):
+    assert m3.mamba3_decode_validate(good_decode()) == m3.MAMBA3_OK
+    assert m3.mamba3_decode_validate(good_decode(Bprev=None, xprev=None)) == m3.MAMBA3_OK
+    assert m3.mamba3_decode_validate(good_decode(Bprev=None)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_decode_validate(good_decode(dstate=63)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_decode_validate(good_decode(h=None)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_decode_validate(good_decode(y=fake(11))) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_decode_validate(good_decode(h=BASE + 0xB00000002)) == m3.MAMBA3_EALIGN
+    assert m3.mamba3_decode_validate(good_decode(dstate=40)) == m3.MAMBA3_EUNSUPPORTED
+    # dt / lam need only element alignment
+    assert m3.mamba3_decode_validate(good_decode(dt=BASE + 0x200000002)) == m3.MAMBA3_OK
+    assert m3.mamba3_decode_validate(good_decode(dt=BASE + 0x200000001)) == m3.MAMBA3_EALIGN
+    assert m3.mamba3_decode_validate(good_decode(batch=0)) == m3.MAMBA3_OK

@@ -1,0 +1,167 @@
+"""GPU parity of the bf16 MFMA chunked scan against the fp64 oracle (max
+relative error 2e-2 per (sequence, head) slab, for y and the final state).
+
+Small cases run the whole oracle; the full-size workloads (8 x 4096 tokens,
+64 heads; the packed 65536-token workload) run the kernel at full size in the
+bench's launch configuration and check sampled (sequence, head) slabs, each
+recomputed by the oracle from that slab's inputs."""
+import numpy as np
+import pytest
+
+import state_space_sequence_mamba3_amd as m3
+from state_space_sequence_mamba3_amd import synth
+from tests.gpu_util import TOL_BF16, device, from_dev, note, slab_relerr, state_relerr, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def run(d, chunk, want_state=True):
+    import torch
+    y, h = m3.mamba3_scan_fwd(d["x"], d["dt"], d["lam"], d["theta"], d["B"], d["C"], d["A"], d.get("D"),
+                              h_in=d.get("h_in"), Bprev=d.get("Bprev"), xprev=d.get("xprev"),
+                              cu_seqlens=d.get("cu_seqlens"), chunk=chunk, want_state=want_state)
+    torch.cuda.synchronize()
+    return y, h
+
+
+def packed_relerr(g, o, cu):
+    worst = 0.0
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b > a:
+            worst = max(worst, slab_relerr(g[:, a:b], o[:, a:b]))
+    return worst
+
+
+SMALL = {
+    "cfg1_siso_n128": dict(cfg=1, batch=2, seqlen=300, nheads=3),
+    "cfg2_mimo_n64": dict(cfg=2, batch=2, seqlen=200, nheads=3),
+    "cfg4_mimo_n128_q128": dict(cfg=4, batch=1, seqlen=333, nheads=2, packed=False),
+    "n64_r1": dict(cfg=1, batch=1, seqlen=150, nheads=2, dstate=64),
+    "n64_r4_q32": dict(cfg=2, batch=1, seqlen=150, nheads=2, chunk=32),
+    "n128_r2": dict(cfg=1, batch=1, seqlen=190, nheads=2, rank=2),
+    "n128_r4_q64": dict(cfg=4, batch=1, seqlen=250, nheads=2, chunk=64, packed=False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+@pytest.mark.parametrize("resume", [False, True])
+def test_small_vs_full_oracle(oracle, name, resume):
+    spec = dict(SMALL[name])
+    cfg = spec.pop("cfg")
+    inp = synth.scan_inputs(cfg, seed=100 + len(name), **spec)
+    if resume:
+        inp = synth.resume_inputs(inp, seed=5)
+    chunk = inp["meta"]["chunk"]
+    note(f"bf16 scan {name} resume={resume} x{inp['x'].shape} chunk={chunk}")
+    y, h = run(upload(inp, device()), chunk)
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    ey, eh = slab_relerr(from_dev(y), yo), state_relerr(from_dev(h), ho)
+    note(f"  y relerr {ey:.2e}  h relerr {eh:.2e}")
+    assert ey < TOL_BF16 and eh < TOL_BF16
+
+
+def test_grouped_bc_and_no_skip(oracle):
+    inp = synth.scan_inputs(dict(synth.CONFIGS[2], ngroups=1), seed=3, batch=1, seqlen=130, nheads=4)
+    inp["D"] = None
+    note("bf16 scan G=1, D=NULL")
+    y, h = run(upload(inp, device()), 64)
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k not in ("meta", "D")})
+    assert slab_relerr(from_dev(y), yo) < TOL_BF16 and state_relerr(from_dev(h), ho) < TOL_BF16
+
+
+def test_packed_ragged_with_empty(oracle):
+    inp = synth.scan_inputs(4, seed=11, seqlen=700, nheads=2)
+    inp["cu_seqlens"] = np.array([0, 1, 1, 129, 130, 400, 700, 700], dtype=np.int32)
+    inp = synth.resume_inputs(inp, seed=12)
+    note("bf16 packed ragged with empty sequences")
+    y, h = run(upload(inp, device()), 128)
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    assert packed_relerr(from_dev(y), yo, inp["cu_seqlens"]) < TOL_BF16
+    assert state_relerr(from_dev(h), ho) < TOL_BF16
+    assert np.array_equal(from_dev(h)[1], inp["h_in"][1].astype(np.float64))
+
+
+def test_chunk_size_invariance():
+    inp = synth.scan_inputs(2, seed=21, batch=1, seqlen=256, nheads=2)
+    note("bf16 chunk invariance 32 vs 64")
+    d = upload(inp, device())
+    y32, h32 = run(d, 32)
+    y64, h64 = run(d, 64)
+    assert slab_relerr(from_dev(y32), from_dev(y64)) < TOL_BF16
+    assert state_relerr(from_dev(h32), from_dev(h64)) < 1e-2
+
+
+def test_deterministic():
+    inp = synth.scan_inputs(1, seed=22, batch=2, seqlen=200, nheads=2)
+    note("bf16 determinism")
+    d = upload(inp, device())
+    y1, h1 = run(d, 64)
+    y2, h2 = run(d, 64)
+    assert from_dev(y1).tobytes() == from_dev(y2).tobytes() and np.array_equal(from_dev(h1), from_dev(h2))
+
+
+def test_split_resume_matches_whole():
+    """scan(0:T) == scan(0:k) -> (h, B_{k-1}, x_{k-1}) -> scan(k:T) on the GPU."""
+    import torch
+    inp = synth.scan_inputs(2, seed=23, batch=2, seqlen=200, nheads=2)
+    note("bf16 split/resume")
+    d = upload(inp, device())
+    yw, hw = run(d, 64)
+    k = 77
+    tok = ("x", "dt", "lam", "theta", "B", "C")
+    a = {kk: (v[:, :k].contiguous() if kk in tok else v) for kk, v in d.items()}
+    b = {kk: (v[:, k:].contiguous() if kk in tok else v) for kk, v in d.items()}
+    y1, h1 = run(a, 64)
+    b["h_in"], b["Bprev"], b["xprev"] = h1, d["B"][:, k - 1].contiguous(), d["x"][:, k - 1].contiguous()
+    y2, h2 = run(b, 64)
+    assert slab_relerr(from_dev(torch.cat([y1, y2], 1)), from_dev(yw)) < TOL_BF16
+    assert state_relerr(from_dev(h2), from_dev(hw)) < TOL_BF16
+
+
+# ---------------------------------------------------------------- full size
+def _slab_inputs(d, s, h, cu=None):
+    """Host copy (bf16 bits) of one (sequence, head) slab of device inputs."""
+    import torch
+    G = d["B"].shape[2]
+    H = d["x"].shape[2]
+    g = h // (H // G)
+    if cu is not None:
+        a, b = int(cu[s]), int(cu[s + 1])
+        sl = (0, slice(a, b))
+    else:
+        sl = (s, slice(None))
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)[None]
+
+    out = dict(x=bits(d["x"][sl][:, h:h + 1]), dt=bits(d["dt"][sl][:, h:h + 1]), lam=bits(d["lam"][sl][:, h:h + 1]),
+               theta=bits(d["theta"][sl][:, h:h + 1]), B=bits(d["B"][sl][:, g:g + 1]), C=bits(d["C"][sl][:, g:g + 1]),
+               A=d["A"][h:h + 1].cpu().numpy(), D=d["D"][h:h + 1].cpu().numpy())
+    return out
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_full_size_sampled_slabs(oracle, cfg):
+    import torch
+    c = synth.CONFIGS[cfg]
+    note(f"full-size bf16 scan config {cfg}: {c['name']}")
+    d = synth.torch_scan_inputs(cfg, device(), seed=cfg)
+    y, h = run(d, c["chunk"])
+    cu = d["cu_seqlens"].cpu().numpy() if "cu_seqlens" in d else None
+    S = (len(cu) - 1) if cu is not None else c["batch"]
+    rng = np.random.default_rng(cfg)
+    picks = [(0, 0), (S - 1, c["nheads"] - 1)] + [(int(rng.integers(S)), int(rng.integers(c["nheads"]))) for _ in range(3)]
+    for s, hh in picks:
+        one = _slab_inputs(d, s, hh, cu)
+        yo, ho = oracle.scan_slab(one, 0, 0)
+        if cu is not None:
+            yg = y[0, int(cu[s]):int(cu[s + 1]), hh]
+        else:
+            yg = y[s, :, hh]
+        ey = float(np.abs(from_dev(yg) - yo).max() / np.abs(yo).max())
+        eh = float(np.abs(from_dev(h[s, hh]) - ho).max() / np.abs(ho).max())
+        note(f"  slab (s={s}, h={hh}) len={yo.shape[0]}: y relerr {ey:.2e}  h relerr {eh:.2e}")
+        assert ey < TOL_BF16 and eh < TOL_BF16
+    del d, y, h
+    torch.cuda.empty_cache()
