@@ -8,11 +8,14 @@
 // Space Models") in the physical frame, with the rank-R update of section
 // "MIMO Formulation".
 //
-// The step is HBM-bound (the state is read and written once: "the state must
-// be read and written at every step"), so the kernel streams the state with
-// 16-byte accesses: a workgroup owns one (b, h) slab; thread tid covers 4
-// consecutive columns p and ROWS consecutive rows (whole rotation pairs); y is
-// reduced over rows through LDS in a fixed order (deterministic).
+// The step is HBM-bound (the state is read and written once per step and
+// dominates the traffic), so the kernel is a streaming kernel: a workgroup
+// owns one (b, h) slab; every thread first issues its 16-byte state loads,
+// then the workgroup stages the slab's small token inputs (x, xprev, B, C,
+// Bprev, theta) through LDS with 16-byte loads, and each thread updates 4
+// consecutive columns of ROWS consecutive rows (whole rotation pairs) and
+// writes them back. y is reduced over rows through LDS in a fixed order
+// (deterministic).
 #include "m3_common.h"
 
 namespace m3 {
@@ -25,12 +28,32 @@ struct DecodeParams {
     int32_t H, G;
 };
 
+// Copy `count` elements of T (count * sizeof(T) a multiple of 16) into LDS as
+// fp32 with 16-byte loads; piece i goes to thread (t0 + i) mod TPB, so arrays
+// staged with different t0 land on different threads.
+template <typename T, int TPB>
+__device__ __forceinline__ void stage_f32(float *dst, const T *src, int count, int tid, int t0) {
+    constexpr int VW = 16 / sizeof(T);
+    for (int i = ((tid - t0) % TPB + TPB) % TPB; i < count / VW; i += TPB) {
+        if constexpr (sizeof(T) == 2) {
+            const bf16x8 v = *(const bf16x8 *)(src + i * VW);
+#pragma unroll
+            for (int e = 0; e < VW; e++) dst[i * VW + e] = (float)v[e];
+        } else {
+            *(f32x4 *)(dst + i * VW) = *(const f32x4 *)(src + i * VW);
+        }
+    }
+}
+
 template <typename T, int N, int P, int R, int TPB>
 __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
     constexpr int PG = P / 4;                 // column groups of 4
     constexpr int NRG = TPB / PG;             // row groups
     constexpr int ROWS = N / NRG;             // rows per thread (even)
+    constexpr int VW = 16 / sizeof(T);
     static_assert(P % 4 == 0 && TPB % PG == 0 && N % NRG == 0 && ROWS % 2 == 0, "decode tiling");
+    static_assert((N * R) % VW == 0 && (P * R) % VW == 0 && (N / 2) % VW == 0, "16-byte staging");
+    __shared__ float sB[N * R], sC[N * R], sBp[N * R], sX[P * R], sXp[P * R], sTh[N / 2];
     __shared__ float red[NRG][P * R];
 
     const int tid = threadIdx.x;
@@ -39,33 +62,38 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
     const int bh = blockIdx.x;
     const int H = pr.H, G = pr.G;
     const int b = bh / H, hh = bh % H, g = hh / (H / G);
-
-    const T *x = (const T *)pr.x + (int64_t)bh * P * R;
-    const T *xp = pr.xprev ? (const T *)pr.xprev + (int64_t)bh * P * R : nullptr;
-    const T *Bv = (const T *)pr.B + ((int64_t)b * G + g) * N * R;
-    const T *Cv = (const T *)pr.C + ((int64_t)b * G + g) * N * R;
-    const T *Bp = pr.Bprev ? (const T *)pr.Bprev + ((int64_t)b * G + g) * N * R : nullptr;
-    const T *th = (const T *)pr.theta + (int64_t)bh * (N / 2);
     float *hs = pr.h + (int64_t)bh * N * P;
 
-    // state tile first: the bulk of the traffic, issued before anything else
+    // state tile first: the bulk of the traffic, in flight while the token inputs are staged
     f32x4 st[ROWS];
 #pragma unroll
-    for (int r = 0; r < ROWS; r++) st[r] = *(const f32x4 *)(hs + (n0 + r) * P + p0);
+    for (int r = 0; r < ROWS; r++) st[r] = __builtin_nontemporal_load((const f32x4 *)(hs + (n0 + r) * P + p0));
 
+    const int64_t obc = ((int64_t)b * G + g) * N * R, ox = (int64_t)bh * P * R;
+    constexpr int CB = N * R / VW, CX = P * R / VW, CT = N / 2 / VW;
+    stage_f32<T, TPB>(sB, (const T *)pr.B + obc, N * R, tid, 0);
+    stage_f32<T, TPB>(sC, (const T *)pr.C + obc, N * R, tid, CB);
+    stage_f32<T, TPB>(sX, (const T *)pr.x + ox, P * R, tid, 2 * CB);
+    stage_f32<T, TPB>(sTh, (const T *)pr.theta + (int64_t)bh * (N / 2), N / 2, tid, 2 * CB + CX);
+    if (pr.Bprev) {
+        stage_f32<T, TPB>(sBp, (const T *)pr.Bprev + obc, N * R, tid, 2 * CB + CX + CT);
+        stage_f32<T, TPB>(sXp, (const T *)pr.xprev + ox, P * R, tid, 3 * CB + CX + CT);
+    }
     const float dt = to_f(((const T *)pr.dt)[bh]);
     const float lam = to_f(((const T *)pr.lam)[bh]);
     const float alpha = expf(dt * pr.A[hh]);
     const float delta = (1.f - lam) * dt, gamma = lam * dt;
     const float Dh = pr.D ? pr.D[hh] : 0.f;
+    const bool has_prev = pr.Bprev != nullptr;
+    __syncthreads();
 
     float xv[4][R], xpv[4][R];
 #pragma unroll
     for (int c = 0; c < 4; c++)
 #pragma unroll
         for (int j = 0; j < R; j++) {
-            xv[c][j] = to_f(x[(p0 + c) * R + j]);
-            xpv[c][j] = xp ? to_f(xp[(p0 + c) * R + j]) : 0.f;
+            xv[c][j] = sX[(p0 + c) * R + j];
+            xpv[c][j] = has_prev ? sXp[(p0 + c) * R + j] : 0.f;
         }
 
     float yp[4][R];
@@ -78,16 +106,16 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
     for (int r = 0; r < ROWS; r += 2) {
         const int n = n0 + r;
         float sn, cs;
-        sincosf(dt * to_f(th[n / 2]), &sn, &cs);
+        sincosf(dt * sTh[n / 2], &sn, &cs);
         float b0[R], b1[R], q0[R], q1[R], bp0[R], bp1[R];
 #pragma unroll
         for (int j = 0; j < R; j++) {
-            b0[j] = to_f(Bv[n * R + j]);
-            b1[j] = to_f(Bv[(n + 1) * R + j]);
-            q0[j] = to_f(Cv[n * R + j]);
-            q1[j] = to_f(Cv[(n + 1) * R + j]);
-            bp0[j] = Bp ? to_f(Bp[n * R + j]) : 0.f;
-            bp1[j] = Bp ? to_f(Bp[(n + 1) * R + j]) : 0.f;
+            b0[j] = sB[n * R + j];
+            b1[j] = sB[(n + 1) * R + j];
+            q0[j] = sC[n * R + j];
+            q1[j] = sC[(n + 1) * R + j];
+            bp0[j] = has_prev ? sBp[n * R + j] : 0.f;
+            bp1[j] = has_prev ? sBp[(n + 1) * R + j] : 0.f;
         }
 #pragma unroll
         for (int c = 0; c < 4; c++) {
@@ -99,10 +127,10 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
                 w0 += b0[j] * xv[c][j];
                 w1 += b1[j] * xv[c][j];
             }
-            float u0 = st[r][c] + delta * v0;
-            float u1 = st[r + 1][c] + delta * v1;
-            float h0 = alpha * (cs * u0 - sn * u1) + gamma * w0;
-            float h1 = alpha * (sn * u0 + cs * u1) + gamma * w1;
+            const float u0 = st[r][c] + delta * v0;
+            const float u1 = st[r + 1][c] + delta * v1;
+            const float h0 = alpha * (cs * u0 - sn * u1) + gamma * w0;
+            const float h1 = alpha * (sn * u0 + cs * u1) + gamma * w1;
             st[r][c] = h0;
             st[r + 1][c] = h1;
 #pragma unroll
@@ -110,7 +138,7 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
         }
     }
 #pragma unroll
-    for (int r = 0; r < ROWS; r++) *(f32x4 *)(hs + (n0 + r) * P + p0) = st[r];
+    for (int r = 0; r < ROWS; r++) __builtin_nontemporal_store(st[r], (f32x4 *)(hs + (n0 + r) * P + p0));
 
 #pragma unroll
     for (int c = 0; c < 4; c++)
@@ -122,7 +150,7 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
         float acc = 0.f;
 #pragma unroll
         for (int q = 0; q < NRG; q++) acc += red[q][e];
-        acc += Dh * to_f(x[e]);
+        acc += Dh * sX[e];
         y[e] = from_f<T>(acc);
     }
 }

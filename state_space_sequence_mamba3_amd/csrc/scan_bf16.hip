@@ -1,4 +1,4 @@
-// bf16 chunked scan on gfx950 MFMA (v_mfma_f32_32x32x16_bf16), fp32 state.
+// bf16 chunked scan on gfx950 MFMA, fp32 state.
 //
 // One workgroup owns one (sequence, head) slab and walks it chunk by chunk;
 // the fp32 state lives in registers across chunks, so every input byte is read
@@ -13,23 +13,27 @@
 // (delta_{e+1} is the next chunk's first token's, 0 at the sequence end: it
 // folds that token's previous-input term into the carried state).
 //
-// Rank-expanded rows: row (tau, j) = tau*R + j of a chunk, so the chunk is a
-// (Q*R) x (Q*R) problem cut into 32-row blocks ("blocks", TOKB = 32/R tokens).
-// Work per chunk:
-//   * every wave owns "tasks" = (t-block, column group of P) and holds the
-//     rotated C~ rows of its t-blocks in registers (MFMA operands) and the
-//     output accumulators Y in registers;
-//   * the chunk is swept over s-blocks: each s-block's rotated B~, weighted
-//     B~^T and X^T are staged through LDS (double buffered, global loads
-//     prefetched one block ahead), then each wave computes its lower-triangle
-//     score tiles G^T = B~ C~^T (MFMA, K = N), applies the decay/trapezoid mask
-//     in registers, converts to bf16 and feeds them straight into the output
-//     MFMA (Y += M X) with the K index permuted to match the accumulator lane
-//     layout - the score tile never touches LDS;
-//   * the state tiles (N x P, fp32, distributed over the waves) accumulate the
-//     chunk's rank-R update B~^T X on MFMA and are rotated by Phi_e at the end.
-// The state enters the next chunk's inter-chunk term e^{S_t} C~_t^T H' as a
-// bf16 copy in LDS.
+// Rank-expanded rows: row (tau, j) = tau*R + j of a chunk, so a chunk is a
+// (Q*R) x (Q*R) problem. Outputs are cut into 16-row t-blocks, the sweep over
+// inputs into 32-row s-blocks.
+//   * Every wave owns t-blocks (balanced pairs along the causal triangle) and
+//     keeps their rotated C~ rows (MFMA operands) and output accumulators in
+//     registers.
+//   * The chunk is swept over s-blocks: each s-block's rotated B~, weighted
+//     B~^T and X^T are staged through LDS; each wave computes its score tiles
+//     G^T = B~ C~^T (v_mfma_f32_16x16x32_bf16, K = N), applies the decay and
+//     trapezoid mask in registers, converts to bf16 and feeds the tile straight
+//     back as the A operand of Y += M X, with the K index permuted to the
+//     accumulator lane layout - score tiles never touch LDS.
+//   * The N x P state is split into tiles over the waves; it accumulates the
+//     chunk's rank-R update B~^T X on MFMA and is rotated by Phi_e at the end.
+//     A bf16 copy in LDS feeds the next chunk's inter-chunk term e^{S_t} C~^T H'.
+//   * Global loads run ahead of use: the raw B and X of the sequence's
+//     s-blocks stream through two register sets two blocks ahead, and the next
+//     chunk's dt, lam, theta and C rows are loaded while the current chunk
+//     computes.
+#include <type_traits>
+
 #include "m3_common.h"
 
 namespace m3 {
@@ -38,6 +42,9 @@ namespace {
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Wait for this wave's outstanding LDS operations (wave-private staging).
@@ -52,6 +59,9 @@ __device__ __forceinline__ float wave_incl_scan(float v, int lane) {
     return v;
 }
 
+// 2^x for x <= 0 (hardware exp2; results below the fp32 normal range flush to 0)
+__device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
+
 struct BfParams {
     const bf16 *x, *dt, *lam, *theta, *B, *C, *Bprev, *xprev;
     const float *A, *D, *h_in;
@@ -61,21 +71,22 @@ struct BfParams {
     int32_t seqlen, H, G;
 };
 
-template <int N_, int P_, int R_, int Q_, int NW_>
+template <int N_, int P_, int R_, int Q_, int NW_, int UT_>
 struct Cfg {
-    static constexpr int N = N_, P = P_, R = R_, Q = Q_, NW = NW_;
-    static constexpr int K = N / 2, QR = Q * R, NB = QR / 32, TOKB = 32 / R;
-    static constexpr int NTHR = NW * 64;
-    static constexpr int PG = (NB >= NW) ? 1 : NW / NB;   // column groups per t-block
-    static constexpr int PT = P / PG, NPT = PT / 32;     // columns / 32-col tiles per task
-    static constexpr int NTASK = NB * PG, TPW = NTASK / NW;
-    static constexpr int NUT = (N / 32) * (P / 32), UPW = NUT / NW;
-    static constexpr int NKK = N / 16;                   // K-steps over N
-    static constexpr int NS = N + 8;                     // padded bf16 row stride of [*][N] tiles
-    static constexpr int RS = 40;                        // padded bf16 row stride of [*][32] tiles
-    static_assert(N % 32 == 0 && P % 32 == 0 && 32 % R == 0 && QR % 32 == 0, "shape");
-    static_assert(NTASK % NW == 0 && NUT % NW == 0 && P % PG == 0 && PT % 32 == 0, "work split");
-    static_assert(TPW == 1 || TPW % 2 == 0, "task pairing");
+    static constexpr int N = N_, P = P_, R = R_, Q = Q_, NW = NW_, UT = UT_;
+    static constexpr int K = N / 2, QR = Q * R;
+    static constexpr int NTB = QR / 16, NSB = QR / 32;      // 16-row t-blocks, 32-row s-blocks
+    static constexpr int TOKT = 16 / R, TOKS = 32 / R;      // tokens per t-block / s-block
+    static constexpr int NTHR = NW * 64, TPW = NTB / NW;
+    static constexpr int NKK = N / 32;                      // K-steps over N (16x16x32)
+    static constexpr int NPT = P / 16;                      // 16-column tiles of P
+    static constexpr int NUT = (N / UT) * (P / UT), UPW = NUT / NW;
+    static constexpr int UR_ = (UT == 32) ? 16 : 4;         // state registers per tile
+    static constexpr int NS = N + 8;                        // padded bf16 row stride of [*][N] tiles
+    static constexpr int RS = 40;                           // padded bf16 row stride of [*][32] tiles
+    static_assert(N % 32 == 0 && P % 32 == 0 && (R == 1 || R == 2 || R == 4) && QR % 32 == 0, "shape");
+    static_assert(NTB % NW == 0 && (TPW == 1 || TPW % 2 == 0), "t-block split");
+    static_assert(NUT % NW == 0 && (UT == 16 || UT == 32), "state tile split");
     static_assert(K % 8 == 0 && Q % NW == 0 && Q <= 128 && Q < NTHR, "prologue");
     // LDS layout (bytes)
     static constexpr int OFF_PHI = 0;                                  // float [Q][K]
@@ -89,22 +100,26 @@ struct Cfg {
     static constexpr int OFF_MISC = OFF_TOT + NW * K * 4;              // float [4]
     static constexpr int OFF_HB = (OFF_MISC + 16 + 15) / 16 * 16;      // bf16 [P][NS] carried state
     static constexpr int OFF_U = OFF_HB + P * NS * 2;                  // union region
-    static constexpr int CST_BYTES = 32 * NS * 2;                      // per-wave C~ staging
+    static constexpr int CST_BYTES = 16 * NS * 2;                      // per-wave C~ staging
     static constexpr int SB_BT = 0, SB_WT = 32 * NS * 2, SB_X = SB_WT + N * RS * 2;
     static constexpr int STAGE = SB_X + P * RS * 2;                    // one s-block stage
     static constexpr int U_BYTES = (NW * CST_BYTES > 2 * STAGE) ? NW * CST_BYTES : 2 * STAGE;
     static constexpr int LDS = OFF_U + U_BYTES;
     static_assert(LDS <= 160 * 1024, "LDS");
-    // global loads per s-block (16 bytes each)
+    // global loads (16 bytes each) per s-block, and next-chunk header prefetch
     static constexpr int BCH = 32 * N / 8, XCH = 32 * P / 8;
     static constexpr int NLB = (BCH + NTHR - 1) / NTHR, NLX = (XCH + NTHR - 1) / NTHR;
+    static constexpr int NTH = (Q * K / 8 + NTHR - 1) / NTHR;
+    static constexpr int CPT = N / 32;                                 // C pieces per lane per t-block
+    static constexpr int NCP = TPW * CPT;
 };
 
 template <class CF>
 __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
-    constexpr int N = CF::N, P = CF::P, R = CF::R, Q = CF::Q, NW = CF::NW, K = CF::K;
-    constexpr int NB = CF::NB, TOKB = CF::TOKB, NTHR = CF::NTHR, PG = CF::PG, PT = CF::PT;
-    constexpr int NPT = CF::NPT, TPW = CF::TPW, UPW = CF::UPW, NKK = CF::NKK, NS = CF::NS, RS = CF::RS;
+    constexpr int N = CF::N, P = CF::P, R = CF::R, Q = CF::Q, NW = CF::NW, K = CF::K, UT = CF::UT;
+    constexpr int TOKT = CF::TOKT, TOKS = CF::TOKS, NTHR = CF::NTHR, TPW = CF::TPW;
+    constexpr int NKK = CF::NKK, NPT = CF::NPT, UPW = CF::UPW, NS = CF::NS, RS = CF::RS, UR_ = CF::UR_;
+    using UAcc = std::conditional_t<UT == 32, f32x16, f32x4>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float *phi = (float *)(smem + CF::OFF_PHI);
     float *S2 = (float *)(smem + CF::OFF_S2);
@@ -119,7 +134,7 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
     char *UR = smem + CF::OFF_U;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hi = lane >> 5;
+    const int l16 = lane & 15, q4 = lane >> 4, l32 = lane & 31, hi = lane >> 5;
     const int H = pr.H, G = pr.G;
     const int s = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
 
@@ -135,38 +150,45 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
     }
     const float A2h = pr.A[h] * kLog2e;
     const float Dh = pr.D ? pr.D[h] : 0.f;
+    // per-(sequence, head) base pointers: add token * stride
+    const bf16 *gB = pr.B + g * (int64_t)N * R;
+    const bf16 *gC = pr.C + g * (int64_t)N * R;
+    const bf16 *gX = pr.x + h * (int64_t)P * R;
+    bf16 *gY = pr.y + h * (int64_t)P * R;
+    const bf16 *gTh = pr.theta + h * (int64_t)K;
+    const int64_t strBC = (int64_t)G * N * R, strX = (int64_t)H * P * R, strTh = (int64_t)H * K;
 
-    // this wave's tasks (t-block, column group) and state tiles
-    int task_tb[TPW], task_p0[TPW];
+    // this wave's t-blocks and state tiles
+    int task_tb[TPW];
 #pragma unroll
-    for (int u = 0; u < TPW; u++) {
-        int task = (TPW == 1) ? wave : (u / 2) * 2 * NW + ((u % 2 == 0) ? wave : 2 * NW - 1 - wave);
-        task_tb[u] = task / PG;
-        task_p0[u] = (task % PG) * PT;
-    }
+    for (int u = 0; u < TPW; u++)
+        task_tb[u] = (TPW == 1) ? wave : (u / 2) * 2 * NW + ((u % 2 == 0) ? wave : 2 * NW - 1 - wave);
     int ut_n0[UPW], ut_p0[UPW];
 #pragma unroll
     for (int v = 0; v < UPW; v++) {
-        int ut = wave * UPW + v;
-        ut_n0[v] = (ut / (P / 32)) * 32;
-        ut_p0[v] = (ut % (P / 32)) * 32;
+        const int ut = wave * UPW + v;
+        ut_n0[v] = (ut / (P / UT)) * UT;
+        ut_p0[v] = (ut % (P / UT)) * UT;
     }
+    // state-tile register r -> (row n, column p) within the tile
+    auto urow = [&](int r) { return (UT == 32) ? 8 * (r / 4) + 4 * hi + (r % 4) : 4 * q4 + r; };
+    const int ucol = (UT == 32) ? l32 : l16;
 
-    // ---- initial state: h_in (+ delta_0 Bprev xprev^T) in the MFMA accumulator layout
-    f32x16 hreg[UPW];
+    // ---- initial state: h_in (+ delta_0 Bprev xprev^T) in the accumulator layout
+    UAcc hreg[UPW];
     {
         const int64_t so = ((int64_t)s * H + h) * N * P;
         float d0 = 0.f;
         if (pr.Bprev && len > 0) {
-            float dt0 = to_f(pr.dt[start * H + h]), l0 = to_f(pr.lam[start * H + h]);
+            const float dt0 = to_f(pr.dt[start * H + h]), l0 = to_f(pr.lam[start * H + h]);
             d0 = (1.f - l0) * dt0;
         }
 #pragma unroll
         for (int v = 0; v < UPW; v++) {
-            const int p = ut_p0[v] + l32;
+            const int p = ut_p0[v] + ucol;
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int n = ut_n0[v] + 8 * (r / 4) + 4 * hi + (r % 4);
+            for (int r = 0; r < UR_; r++) {
+                const int n = ut_n0[v] + urow(r);
                 float val = pr.h_in ? pr.h_in[so + (int64_t)n * P + p] : 0.f;
                 if (pr.Bprev) {
                     const bf16 *bp = pr.Bprev + ((int64_t)s * G + g) * N * R + n * R;
@@ -178,55 +200,122 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
                 }
                 hreg[v][r] = val;
             }
-            // bf16 copy for the first chunk's inter-chunk term
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const int n = ut_n0[v] + 8 * (r / 4) + 4 * hi + (r % 4);
-                bf16x2 pk = {(bf16)hreg[v][r], (bf16)hreg[v][r + 1]};
-                *(bf16x2 *)(HB + p * NS + n) = pk;
+            for (int r = 0; r < UR_; r += 2) {
+                const int n = ut_n0[v] + urow(r);
+                *(bf16x2 *)(HB + p * NS + n) = bf16x2{(bf16)hreg[v][r], (bf16)hreg[v][r + 1]};
             }
         }
     }
+
+    // ---- next-chunk header (dt, lam, theta, own C rows) prefetched into registers
+    float h_dt = 0.f, h_lam = 0.f;
+    bf16x8 h_th[CF::NTH];
+    float h_thdt[CF::NTH];
+    bf16x8 h_c[CF::NCP];
+    auto load_header = [&](int64_t c0h) {
+        const int nqh = (int)min((int64_t)Q, len - c0h);
+        const int64_t t0h = start + c0h;
+        h_dt = 0.f;
+        h_lam = 0.f;
+        if (tid < nqh) {
+            h_dt = to_f(pr.dt[(t0h + tid) * H + h]);
+            h_lam = to_f(pr.lam[(t0h + tid) * H + h]);
+        } else if (tid == Q && c0h + nqh < len) {
+            h_dt = to_f(pr.dt[(t0h + nqh) * H + h]);
+            h_lam = to_f(pr.lam[(t0h + nqh) * H + h]);
+        }
+#pragma unroll
+        for (int i = 0; i < CF::NTH; i++) {
+            const int e = tid + i * NTHR;
+            const int tau = e / (K / 8), k0 = (e % (K / 8)) * 8;
+            h_th[i] = bf16x8{};
+            h_thdt[i] = 0.f;
+            if (e < Q * K / 8 && tau < nqh) {
+                h_thdt[i] = to_f(pr.dt[(t0h + tau) * H + h]);
+                h_th[i] = *(const bf16x8 *)(gTh + (t0h + tau) * strTh + k0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < TPW; u++)
+#pragma unroll
+            for (int i = 0; i < CF::CPT; i++) {
+                const int flat = (lane + i * 64) * 8;
+                const int tau = task_tb[u] * TOKT + flat / (N * R);
+                h_c[u * CF::CPT + i] = bf16x8{};
+                if (tau < nqh) h_c[u * CF::CPT + i] = *(const bf16x8 *)(gC + (t0h + tau) * strBC + (flat % (N * R)));
+            }
+    };
+
+    // ---- s-block stream: block j of the sequence lives in register set j % 2
+    bf16x8 rb0[CF::NLB], rx0[CF::NLX], rb1[CF::NLB], rx1[CF::NLX];
+    auto load_block_into = [&](bf16x8 (&rb)[CF::NLB], bf16x8 (&rx)[CF::NLX], int64_t c0b, int sb) {
+        const int nqb = (int)min((int64_t)Q, len - c0b);
+        const int64_t t0b = start + c0b;
+#pragma unroll
+        for (int i = 0; i < CF::NLB; i++) {
+            const int c = tid + i * NTHR;
+            rb[i] = bf16x8{};
+            if (c < CF::BCH) {
+                const int flat = c * 8, tau = sb * TOKS + flat / (N * R);
+                if (tau < nqb) rb[i] = *(const bf16x8 *)(gB + (t0b + tau) * strBC + (flat % (N * R)));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CF::NLX; i++) {
+            const int c = tid + i * NTHR;
+            rx[i] = bf16x8{};
+            if (c < CF::XCH) {
+                const int flat = c * 8, tau = sb * TOKS + flat / (P * R);
+                if (tau < nqb) rx[i] = *(const bf16x8 *)(gX + (t0b + tau) * strX + (flat % (P * R)));
+            }
+        }
+    };
+    auto advance = [&](int64_t &c0b, int &sb) {
+        if (c0b >= len) return;
+        const int nqb = (int)min((int64_t)Q, len - c0b);
+        if (sb + 1 < (nqb + TOKS - 1) / TOKS) {
+            sb++;
+        } else {
+            c0b += Q;
+            sb = 0;
+        }
+    };
+    int64_t ld_c0 = 0;
+    int ld_sb = 0;
+    if (len > 0) {
+        load_header(0);
+        load_block_into(rb0, rx0, ld_c0, ld_sb);
+        advance(ld_c0, ld_sb);
+        if (ld_c0 < len) load_block_into(rb1, rx1, ld_c0, ld_sb);
+        advance(ld_c0, ld_sb);
+    }
+    int par = 0;   // parity of the next block to stage
     __syncthreads();
 
     for (int64_t c0 = 0; c0 < len; c0 += Q) {
         const int nq = (int)min((int64_t)Q, len - c0);
-        const int64_t tok0 = start + c0;   // flat token index of chunk row 0
+        const int64_t tok0 = start + c0;
 
         // ---- prologue 1: per-token scalars and raw angles dt*theta
         if (tid < Q) {
-            float dtv = 0.f, lv = 0.f;
-            if (tid < nq) {
-                dtv = to_f(pr.dt[(tok0 + tid) * H + h]);
-                lv = to_f(pr.lam[(tok0 + tid) * H + h]);
-            }
-            A2[tid] = dtv * A2h;
-            GM[tid] = lv * dtv;
-            DL[tid] = (1.f - lv) * dtv;
+            A2[tid] = h_dt * A2h;
+            GM[tid] = h_lam * h_dt;
+            DL[tid] = (1.f - h_lam) * h_dt;
         } else if (tid == Q) {
-            float dn = 0.f;
-            if (c0 + nq < len) {
-                const int64_t tn = tok0 + nq;
-                float dtv = to_f(pr.dt[tn * H + h]), lv = to_f(pr.lam[tn * H + h]);
-                dn = (1.f - lv) * dtv;
-            }
-            MISC[0] = dn;
+            MISC[0] = (1.f - h_lam) * h_dt;
         }
-        for (int e = tid; e < Q * K / 8; e += NTHR) {
-            const int tau = e / (K / 8), k0 = (e % (K / 8)) * 8;
-            float v[8];
-            if (tau < nq) {
-                const int64_t tg = tok0 + tau;
-                const float dtv = to_f(pr.dt[tg * H + h]);
-                bf16x8 th = *(const bf16x8 *)(pr.theta + (tg * H + h) * K + k0);
 #pragma unroll
-                for (int i = 0; i < 8; i++) v[i] = dtv * (float)th[i];
-            } else {
+        for (int i = 0; i < CF::NTH; i++) {
+            const int e = tid + i * NTHR;
+            if (e < Q * K / 8) {
+                const int tau = e / (K / 8), k0 = (e % (K / 8)) * 8;
+                float v[8];
 #pragma unroll
-                for (int i = 0; i < 8; i++) v[i] = 0.f;
+                for (int q = 0; q < 8; q++) v[q] = h_thdt[i] * (float)h_th[i][q];
+                *(f32x4 *)(phi + tau * K + k0) = f32x4{v[0], v[1], v[2], v[3]};
+                *(f32x4 *)(phi + tau * K + k0 + 4) = f32x4{v[4], v[5], v[6], v[7]};
             }
-            *(f32x4 *)(phi + tau * K + k0) = f32x4{v[0], v[1], v[2], v[3]};
-            *(f32x4 *)(phi + tau * K + k0 + 4) = f32x4{v[4], v[5], v[6], v[7]};
         }
         __syncthreads();
 
@@ -234,9 +323,10 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
         constexpr int SEG = Q / NW;
         if (lane < K) {
             float acc = 0.f;
-            for (int t = wave * SEG; t < (wave + 1) * SEG; t++) {
-                acc += phi[t * K + lane];
-                phi[t * K + lane] = acc;
+#pragma unroll
+            for (int t = 0; t < SEG; t++) {
+                acc += phi[(wave * SEG + t) * K + lane];
+                phi[(wave * SEG + t) * K + lane] = acc;
             }
             TOT[wave * K + lane] = acc;
         }
@@ -264,56 +354,54 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
             for (int i = 0; i < PER; i++) {
                 const int t = lane * PER + i;
                 if (t < Q) {
-                    float next = (t + 1 < nq) ? DL[t + 1] : ((t + 1 == nq) ? dn : 0.f);
-                    float g1 = GM[t] + next;
+                    const float next = (t + 1 < nq) ? DL[t + 1] : ((t + 1 == nq) ? dn : 0.f);
+                    const float g1 = GM[t] + next;
                     G1[t] = g1;
-                    WU[t] = (t < nq) ? exp2f(S2e - S2[t]) * g1 : 0.f;
+                    WU[t] = (t < nq) ? exp2_neg(S2e - S2[t]) * g1 : 0.f;
                 }
             }
             if (lane == 0) MISC[1] = S2e;
         }
         __syncthreads();
-        // carry the segment sums into later segments
         if (lane < K && wave > 0) {
             float carry = 0.f;
             for (int w = 0; w < wave; w++) carry += TOT[w * K + lane];
-            for (int t = wave * SEG; t < (wave + 1) * SEG; t++) phi[t * K + lane] += carry;
+#pragma unroll
+            for (int t = 0; t < SEG; t++) phi[(wave * SEG + t) * K + lane] += carry;
         }
         __syncthreads();
 
-        // ---- prologue 3: rotated C~ rows of this wave's t-blocks into registers (staged per wave)
+        // ---- prologue 3: rotated C~ rows of this wave's t-blocks into registers (per-wave staging)
         bf16x8 creg[TPW][NKK];
-        f32x16 yacc[TPW][NPT];
+        f32x4 yacc[TPW][NPT];
         {
             bf16 *cst = (bf16 *)(UR + wave * CF::CST_BYTES);
 #pragma unroll
             for (int u = 0; u < TPW; u++) {
                 const int tb = task_tb[u];
-                // raw C of tokens tb*TOKB .. +TOKB: TOKB*N*R bf16 = 32*N, 16-byte pieces over the wave
-                for (int c = lane; c < 32 * N / 8; c += 64) {
-                    const int flat = c * 8;
-                    const int tl = flat / (N * R);               // token within the block
-                    const int n0 = (flat % (N * R)) / R;         // first state row of the piece
-                    const int tau = tb * TOKB + tl;
-                    bf16x8 raw;
-                    if (tau < nq) raw = *(const bf16x8 *)(pr.C + ((tok0 + tau) * G + g) * N * R + n0 * R);
-                    else raw = bf16x8{};
 #pragma unroll
-                    for (int q = 0; q < 4 / R; q++) {            // pairs in the piece
+                for (int i = 0; i < CF::CPT; i++) {
+                    const int flat = (lane + i * 64) * 8;
+                    const int tl = flat / (N * R);               // token within the t-block
+                    const int n0 = (flat % (N * R)) / R;         // first state row of the piece
+                    const int tau = tb * TOKT + tl;
+                    const bf16x8 raw = h_c[u * CF::CPT + i];
+#pragma unroll
+                    for (int q = 0; q < 4 / R; q++) {   // pairs in the piece
                         const int n = n0 + 2 * q;
                         float sn, cs;
                         __sincosf(phi[tau * K + n / 2], &sn, &cs);
 #pragma unroll
                         for (int j = 0; j < R; j++) {
-                            float c0v = (float)raw[(2 * q) * R + j], c1v = (float)raw[(2 * q + 1) * R + j];
-                            bf16x2 pk = {(bf16)(cs * c0v + sn * c1v), (bf16)(-sn * c0v + cs * c1v)};
-                            *(bf16x2 *)(cst + (tl * R + j) * NS + n) = pk;
+                            const float c0v = (float)raw[(2 * q) * R + j], c1v = (float)raw[(2 * q + 1) * R + j];
+                            *(bf16x2 *)(cst + (tl * R + j) * NS + n) =
+                                bf16x2{(bf16)(cs * c0v + sn * c1v), (bf16)(-sn * c0v + cs * c1v)};
                         }
                     }
                 }
                 lds_wait();
 #pragma unroll
-                for (int kk = 0; kk < NKK; kk++) creg[u][kk] = *(const bf16x8 *)(cst + l32 * NS + 16 * kk + 8 * hi);
+                for (int kk = 0; kk < NKK; kk++) creg[u][kk] = *(const bf16x8 *)(cst + l16 * NS + 32 * kk + 8 * q4);
                 lds_wait();
             }
         }
@@ -321,59 +409,36 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
         // ---- inter-chunk term: Y = e^{S_t} C~ H'   (H' bf16 in LDS, [p][n])
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
+            const int tb = task_tb[u];
+            float sc[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) sc[i] = exp2_neg(S2[tb * TOKT + (4 * q4 + i) / R]);
 #pragma unroll
             for (int pt = 0; pt < NPT; pt++) {
-                f32x16 acc = {};
-                const int p = task_p0[u] + pt * 32 + l32;
+                f32x4 acc = {};
+                const int p = pt * 16 + l16;
 #pragma unroll
-                for (int kk = 0; kk < NKK; kk++) {
-                    bf16x8 b = *(const bf16x8 *)(HB + p * NS + 16 * kk + 8 * hi);
-                    acc = mfma32(creg[u][kk], b, acc);
-                }
+                for (int kk = 0; kk < NKK; kk++)
+                    acc = mfma16(creg[u][kk], *(const bf16x8 *)(HB + p * NS + 32 * kk + 8 * q4), acc);
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int tau = task_tb[u] * TOKB + (8 * (r / 4) + 4 * hi + (r % 4)) / R;
-                    acc[r] *= exp2f(S2[tau]);
-                }
+                for (int i = 0; i < 4; i++) acc[i] *= sc[i];
                 yacc[u][pt] = acc;
             }
         }
-        // state decays over the whole chunk before the chunk's update accumulates on it
         {
-            const float eS = exp2f(MISC[1]);
+            const float eS = exp2_neg(MISC[1]);
 #pragma unroll
             for (int v = 0; v < UPW; v++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) hreg[v][r] *= eS;
+                for (int r = 0; r < UR_; r++) hreg[v][r] *= eS;
         }
+        // the header registers are consumed: prefetch the next chunk's header now
+        if (c0 + Q < len) load_header(c0 + Q);
         __syncthreads();   // C~ staging and H' reads done: the union region becomes s-block stages
 
         // ---- s-block sweep
-        const int nbv = (nq + TOKB - 1) / TOKB;   // blocks holding valid tokens
-        bf16x8 rawB[CF::NLB], rawX[CF::NLX];
-        auto load_block = [&](int sb) {
-#pragma unroll
-            for (int i = 0; i < CF::NLB; i++) {
-                const int c = tid + i * NTHR;
-                rawB[i] = bf16x8{};
-                if (c < CF::BCH) {
-                    const int flat = c * 8, tl = flat / (N * R), tau = sb * TOKB + tl;
-                    if (tau < nq)
-                        rawB[i] = *(const bf16x8 *)(pr.B + ((tok0 + tau) * G + g) * N * R + (flat % (N * R)));
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < CF::NLX; i++) {
-                const int c = tid + i * NTHR;
-                rawX[i] = bf16x8{};
-                if (c < CF::XCH) {
-                    const int flat = c * 8, tl = flat / (P * R), tau = sb * TOKB + tl;
-                    if (tau < nq)
-                        rawX[i] = *(const bf16x8 *)(pr.x + ((tok0 + tau) * H + h) * P * R + (flat % (P * R)));
-                }
-            }
-        };
-        auto store_block = [&](int sb, int buf) {
+        const int nbs = (nq + TOKS - 1) / TOKS;   // s-blocks holding valid tokens
+        auto store_block = [&](const bf16x8 (&rawB)[CF::NLB], const bf16x8 (&rawX)[CF::NLX], int sb, int buf) {
             char *stg = UR + buf * CF::STAGE;
             bf16 *bt = (bf16 *)(stg + CF::SB_BT);   // [32 rows][NS]   rotated B~
             bf16 *wt = (bf16 *)(stg + CF::SB_WT);   // [N][RS]         wU * B~, transposed
@@ -383,7 +448,7 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
                 const int c = tid + i * NTHR;
                 if (c < CF::BCH) {
                     const int flat = c * 8, tl = flat / (N * R), n0 = (flat % (N * R)) / R;
-                    const int tau = sb * TOKB + tl;
+                    const int tau = sb * TOKS + tl;
                     const float w = WU[tau];
 #pragma unroll
                     for (int q = 0; q < 4 / R; q++) {
@@ -393,17 +458,16 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
                         float r0[R], r1[R];
 #pragma unroll
                         for (int j = 0; j < R; j++) {
-                            float b0 = (float)rawB[i][(2 * q) * R + j], b1 = (float)rawB[i][(2 * q + 1) * R + j];
+                            const float b0 = (float)rawB[i][(2 * q) * R + j], b1 = (float)rawB[i][(2 * q + 1) * R + j];
                             r0[j] = cs * b0 + sn * b1;
                             r1[j] = -sn * b0 + cs * b1;
-                            bf16x2 pk = {(bf16)r0[j], (bf16)r1[j]};
-                            *(bf16x2 *)(bt + (tl * R + j) * NS + n) = pk;
+                            *(bf16x2 *)(bt + (tl * R + j) * NS + n) = bf16x2{(bf16)r0[j], (bf16)r1[j]};
                         }
                         if constexpr (R == 4) {
-                            bf16x4 w0 = {(bf16)(w * r0[0]), (bf16)(w * r0[1]), (bf16)(w * r0[2]), (bf16)(w * r0[3])};
-                            bf16x4 w1 = {(bf16)(w * r1[0]), (bf16)(w * r1[1]), (bf16)(w * r1[2]), (bf16)(w * r1[3])};
-                            *(bf16x4 *)(wt + n * RS + tl * 4) = w0;
-                            *(bf16x4 *)(wt + (n + 1) * RS + tl * 4) = w1;
+                            *(bf16x4 *)(wt + n * RS + tl * 4) =
+                                bf16x4{(bf16)(w * r0[0]), (bf16)(w * r0[1]), (bf16)(w * r0[2]), (bf16)(w * r0[3])};
+                            *(bf16x4 *)(wt + (n + 1) * RS + tl * 4) =
+                                bf16x4{(bf16)(w * r1[0]), (bf16)(w * r1[1]), (bf16)(w * r1[2]), (bf16)(w * r1[3])};
                         } else {
 #pragma unroll
                             for (int j = 0; j < R; j++) {
@@ -421,10 +485,9 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
                     const int flat = c * 8, tl = flat / (P * R), p0 = (flat % (P * R)) / R;
                     if constexpr (R == 4) {
 #pragma unroll
-                        for (int q = 0; q < 2; q++) {
-                            bf16x4 v = {rawX[i][4 * q], rawX[i][4 * q + 1], rawX[i][4 * q + 2], rawX[i][4 * q + 3]};
-                            *(bf16x4 *)(xt + (p0 + q) * RS + tl * 4) = v;
-                        }
+                        for (int q = 0; q < 2; q++)
+                            *(bf16x4 *)(xt + (p0 + q) * RS + tl * 4) =
+                                bf16x4{rawX[i][4 * q], rawX[i][4 * q + 1], rawX[i][4 * q + 2], rawX[i][4 * q + 3]};
                     } else {
 #pragma unroll
                         for (int e = 0; e < 8; e++) xt[(p0 + e / R) * RS + tl * R + (e % R)] = rawX[i][e];
@@ -432,97 +495,103 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
                 }
             }
         };
-
-        load_block(0);
-        store_block(0, 0);
-        __syncthreads();
-        for (int sb = 0; sb < nbv; sb++) {
-            const int buf = sb & 1;
-            if (sb + 1 < nbv) load_block(sb + 1);
-            const char *stg = UR + buf * CF::STAGE;
+        auto compute_block = [&](int sb) {
+            const char *stg = UR + (sb & 1) * CF::STAGE;
             const bf16 *bt = (const bf16 *)(stg + CF::SB_BT);
             const bf16 *wt = (const bf16 *)(stg + CF::SB_WT);
             const bf16 *xt = (const bf16 *)(stg + CF::SB_X);
-            // scores and outputs for every owned t-block at or after this s-block
 #pragma unroll
             for (int u = 0; u < TPW; u++) {
                 const int tb = task_tb[u];
-                if (tb < sb) continue;
-                f32x16 gt = {};
+                if (2 * sb > tb) continue;                  // t-block lies before this s-block
+                const bool upper = (2 * sb + 1 <= tb);      // second 16-row half of the s-block is causal
+                f32x4 g0 = {}, g1 = {};
 #pragma unroll
                 for (int kk = 0; kk < NKK; kk++) {
-                    bf16x8 a = *(const bf16x8 *)(bt + l32 * NS + 16 * kk + 8 * hi);
-                    gt = mfma32(a, creg[u][kk], gt);
+                    g0 = mfma16(*(const bf16x8 *)(bt + l16 * NS + 32 * kk + 8 * q4), creg[u][kk], g0);
+                    if (upper) g1 = mfma16(*(const bf16x8 *)(bt + (16 + l16) * NS + 32 * kk + 8 * q4), creg[u][kk], g1);
                 }
-                // mask: row (s, j), column (t, i) of this lane
-                const int tcol = tb * TOKB + l32 / R;
-                const float S2t = S2[tcol];
-                bf16x8 mop[2];
+                // decay/trapezoid mask: column (t, i) = lane's t-row, rows (s, j) of the two halves
+                const int tt = tb * TOKT + l16 / R;
+                const float S2t = S2[tt];
+                bf16x8 mop;
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int srow = sb * TOKB + (8 * (r / 4) + 4 * hi + (r % 4)) / R;
+                for (int e = 0; e < 8; e++) {
+                    const int ss = sb * TOKS + (16 * (e / 4) + 4 * q4 + (e % 4)) / R;
                     float coef = 0.f;
-                    if (srow <= tcol) coef = exp2f(S2t - S2[srow]) * ((srow < tcol) ? G1[srow] : GM[srow]);
-                    mop[r / 8][r % 8] = (bf16)(coef * gt[r]);
+                    if (ss <= tt && (e < 4 || upper))
+                        coef = exp2_neg(S2t - S2[ss]) * ((ss < tt) ? G1[ss] : GM[ss]);
+                    mop[e] = (bf16)(coef * ((e < 4) ? g0[e] : g1[e - 4]));
                 }
+                const int dblk = tb - 2 * sb;               // 0/1: t-block is in this s-block's half
 #pragma unroll
                 for (int pt = 0; pt < NPT; pt++) {
-                    const int p = task_p0[u] + pt * 32 + l32;
+                    const int p = pt * 16 + l16;
+                    const bf16x4 lo = *(const bf16x4 *)(xt + p * RS + 4 * q4);
+                    const bf16x4 up = *(const bf16x4 *)(xt + p * RS + 16 + 4 * q4);
+                    yacc[u][pt] = mfma16(mop, bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]},
+                                         yacc[u][pt]);
+                    if (dblk == 0 || dblk == 1) {           // skip term D x_t of the t-block's own rows
+                        const bf16x4 xv = *(const bf16x4 *)(xt + p * RS + 16 * dblk + 4 * q4);
 #pragma unroll
-                    for (int ks = 0; ks < 2; ks++) {
-                        bf16x4 lo = *(const bf16x4 *)(xt + p * RS + 16 * ks + 4 * hi);
-                        bf16x4 up = *(const bf16x4 *)(xt + p * RS + 16 * ks + 8 + 4 * hi);
-                        bf16x8 b = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-                        yacc[u][pt] = mfma32(mop[ks], b, yacc[u][pt]);
-                    }
-                    if (tb == sb) {   // skip term D x_t from the staged X of this block
-#pragma unroll
-                        for (int q = 0; q < 4; q++) {
-                            bf16x4 xv = *(const bf16x4 *)(xt + p * RS + 8 * q + 4 * hi);
-#pragma unroll
-                            for (int e = 0; e < 4; e++) yacc[u][pt][4 * q + e] += Dh * (float)xv[e];
-                        }
+                        for (int i = 0; i < 4; i++) yacc[u][pt][i] += Dh * (float)xv[i];
                     }
                 }
             }
             // chunk-state update on the owned state tiles: H += (wU B~)^T X
 #pragma unroll
             for (int v = 0; v < UPW; v++) {
-                const int n = ut_n0[v] + l32, p = ut_p0[v] + l32;
+                if constexpr (UT == 32) {
+                    const int n = ut_n0[v] + l32, p = ut_p0[v] + l32;
 #pragma unroll
-                for (int ks = 0; ks < 2; ks++) {
-                    bf16x8 a = *(const bf16x8 *)(wt + n * RS + 16 * ks + 8 * hi);
-                    bf16x8 b = *(const bf16x8 *)(xt + p * RS + 16 * ks + 8 * hi);
-                    hreg[v] = mfma32(a, b, hreg[v]);
+                    for (int ks = 0; ks < 2; ks++)
+                        hreg[v] = mfma32(*(const bf16x8 *)(wt + n * RS + 16 * ks + 8 * hi),
+                                         *(const bf16x8 *)(xt + p * RS + 16 * ks + 8 * hi), hreg[v]);
+                } else {
+                    const int n = ut_n0[v] + l16, p = ut_p0[v] + l16;
+                    hreg[v] = mfma16(*(const bf16x8 *)(wt + n * RS + 8 * q4), *(const bf16x8 *)(xt + p * RS + 8 * q4),
+                                     hreg[v]);
                 }
             }
-            if (sb + 1 < nbv) store_block(sb + 1, buf ^ 1);
+        };
+
+        if (par) store_block(rb1, rx1, 0, 0);
+        else store_block(rb0, rx0, 0, 0);
+        __syncthreads();
+        for (int sb = 0; sb < nbs; sb++) {
+            if (par) {
+                if (ld_c0 < len) load_block_into(rb1, rx1, ld_c0, ld_sb);
+                compute_block(sb);
+                if (sb + 1 < nbs) store_block(rb0, rx0, sb + 1, (sb + 1) & 1);
+            } else {
+                if (ld_c0 < len) load_block_into(rb0, rx0, ld_c0, ld_sb);
+                compute_block(sb);
+                if (sb + 1 < nbs) store_block(rb1, rx1, sb + 1, (sb + 1) & 1);
+            }
+            advance(ld_c0, ld_sb);
+            par ^= 1;
             __syncthreads();
         }
 
-        // ---- epilogue: outputs
+        // ---- epilogue: outputs (lane column p, rows 4*q4 + i of each t-block)
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
             const int tb = task_tb[u];
 #pragma unroll
             for (int pt = 0; pt < NPT; pt++) {
-                const int p = task_p0[u] + pt * 32 + l32;
+                const int p = pt * 16 + l16;
+                if constexpr (R == 4) {
+                    const int tau = tb * TOKT + q4;
+                    if (tau < nq)
+                        *(bf16x4 *)(gY + (tok0 + tau) * strX + p * R) =
+                            bf16x4{(bf16)yacc[u][pt][0], (bf16)yacc[u][pt][1], (bf16)yacc[u][pt][2],
+                                   (bf16)yacc[u][pt][3]};
+                } else {
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    if constexpr (R == 4) {
-                        const int tau = tb * TOKB + 2 * q + hi;
-                        if (tau < nq) {
-                            bf16x4 o = {(bf16)yacc[u][pt][4 * q], (bf16)yacc[u][pt][4 * q + 1],
-                                        (bf16)yacc[u][pt][4 * q + 2], (bf16)yacc[u][pt][4 * q + 3]};
-                            *(bf16x4 *)(pr.y + ((tok0 + tau) * H + h) * P * R + p * R) = o;
-                        }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; e++) {
-                            const int row = 8 * q + 4 * hi + e;
-                            const int tau = tb * TOKB + row / R, i = row % R;
-                            if (tau < nq) pr.y[((tok0 + tau) * H + h) * P * R + p * R + i] = (bf16)yacc[u][pt][4 * q + e];
-                        }
+                    for (int i = 0; i < 4; i++) {
+                        const int row = 4 * q4 + i;
+                        const int tau = tb * TOKT + row / R;
+                        if (tau < nq) gY[(tok0 + tau) * strX + p * R + row % R] = (bf16)yacc[u][pt][i];
                     }
                 }
             }
@@ -532,17 +601,16 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
             const float *phe = phi + (nq - 1) * K;
 #pragma unroll
             for (int v = 0; v < UPW; v++) {
-                const int p = ut_p0[v] + l32;
+                const int p = ut_p0[v] + ucol;
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const int n = ut_n0[v] + 8 * (r / 4) + 4 * hi + (r % 4);
+                for (int r = 0; r < UR_; r += 2) {
+                    const int n = ut_n0[v] + urow(r);
                     float sn, cs;
                     __sincosf(phe[n / 2], &sn, &cs);
                     const float u0 = hreg[v][r], u1 = hreg[v][r + 1];
                     hreg[v][r] = cs * u0 - sn * u1;
                     hreg[v][r + 1] = sn * u0 + cs * u1;
-                    bf16x2 pk = {(bf16)hreg[v][r], (bf16)hreg[v][r + 1]};
-                    *(bf16x2 *)(HB + p * NS + n) = pk;
+                    *(bf16x2 *)(HB + p * NS + n) = bf16x2{(bf16)hreg[v][r], (bf16)hreg[v][r + 1]};
                 }
             }
         }
@@ -553,12 +621,9 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
         const int64_t so = ((int64_t)s * H + h) * N * P;
 #pragma unroll
         for (int v = 0; v < UPW; v++) {
-            const int p = ut_p0[v] + l32;
+            const int p = ut_p0[v] + ucol;
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int n = ut_n0[v] + 8 * (r / 4) + 4 * hi + (r % 4);
-                pr.h_out[so + (int64_t)n * P + p] = hreg[v][r];
-            }
+            for (int r = 0; r < UR_; r++) pr.h_out[so + (int64_t)(ut_n0[v] + urow(r)) * P + p] = hreg[v][r];
         }
     }
 }
@@ -583,18 +648,18 @@ mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st) {
 
 }  // namespace
 
-// (N, P, R, Q) -> waves per workgroup
-#define M3_BF16_SHAPES(X) \
-    X(128, 64, 1, 64, 4)  \
-    X(64, 64, 4, 64, 4)   \
-    X(128, 64, 4, 128, 8) \
-    X(64, 64, 1, 64, 4)   \
-    X(64, 64, 4, 32, 4)   \
-    X(128, 64, 2, 64, 4)  \
-    X(128, 64, 4, 64, 8)
+// (N, P, R, Q) -> waves per workgroup, state tile size
+#define M3_BF16_SHAPES(X)      \
+    X(128, 64, 1, 64, 4, 32)   \
+    X(64, 64, 4, 64, 8, 16)    \
+    X(128, 64, 4, 128, 16, 16) \
+    X(64, 64, 1, 64, 4, 32)    \
+    X(64, 64, 4, 32, 8, 16)    \
+    X(128, 64, 2, 64, 8, 32)   \
+    X(128, 64, 4, 64, 8, 32)
 
 bool scan_bf16_supported(int N, int P, int R, int Q) {
-#define X(n, p, r, q, w) if (N == n && P == p && R == r && Q == q) return true;
+#define X(n, p, r, q, w, ut) if (N == n && P == p && R == r && Q == q) return true;
     M3_BF16_SHAPES(X)
 #undef X
     return false;
@@ -602,8 +667,8 @@ bool scan_bf16_supported(int N, int P, int R, int Q) {
 
 mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st) {
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
-#define X(n, p, r, q, w) \
-    if (N == n && P == p && R == r && Q == q) return launch_cfg<Cfg<n, p, r, q, w>>(a, st);
+#define X(n, p, r, q, w, ut) \
+    if (N == n && P == p && R == r && Q == q) return launch_cfg<Cfg<n, p, r, q, w, ut>>(a, st);
     M3_BF16_SHAPES(X)
 #undef X
     return MAMBA3_EUNSUPPORTED;
