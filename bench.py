@@ -118,16 +118,16 @@ def bench_decode(steps_per_rep, reps, dev):
         return torch.randn(shape, generator=g, device=dev) * std + mean
 
     import math
-    x = nrm((ring, b, H, P, R)).bfloat16()
+    x = nrm((ring, b, H, R, P)).bfloat16()
     dt = torch.nn.functional.softplus(nrm((ring, b, H), -2.0, 0.5)).bfloat16()
     lam = torch.sigmoid(nrm((ring, b, H))).bfloat16()
     th = ((torch.rand((ring, b, H, N // 2), generator=g, device=dev) * 2 - 1) * math.pi).bfloat16()
-    B = nrm((ring, b, H, N, R), 0, 1 / math.sqrt(N)).bfloat16()
-    C = nrm((ring, b, H, N, R), 0, 1 / math.sqrt(N)).bfloat16()
+    B = nrm((ring, b, H, R, N), 0, 1 / math.sqrt(N)).bfloat16()
+    C = nrm((ring, b, H, R, N), 0, 1 / math.sqrt(N)).bfloat16()
     A = -torch.exp(nrm((H,), 0, 0.5))
     D = nrm((H,))
     h = nrm((b, H, N, P))
-    ys = torch.empty((ring, b, H, P, R), dtype=torch.bfloat16, device=dev)
+    ys = torch.empty((ring, b, H, R, P), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     state = {"k": 0}

@@ -17,14 +17,16 @@
  * B_t X_t^T = sum_r B_t^(r) X_t^(r)T ("MIMO Formulation"). The state is kept in
  * the physical frame (no cumulative angle is carried across calls).
  *
- * Layouts (row-major, innermost last; T = tokens):
- *   x, y        [batch, seqlen, H, P, R]        token inputs / outputs
+ * Layouts (row-major, innermost last; T = tokens). Rank-major: the R columns
+ * of B_t, C_t (length N) and of X_t, y_t (length P) are stored one after
+ * another, i.e. B_t^T, C_t^T, X_t^T, y_t^T row-major.
+ *   x, y        [batch, seqlen, H, R, P]        token inputs / outputs
  *   dt, lam     [batch, seqlen, H]              step (post-softplus), trapezoid weight in [0,1]
  *   theta       [batch, seqlen, H, N/2]         rotation frequency; the angle is dt*theta
- *   B, C        [batch, seqlen, G, N, R]
+ *   B, C        [batch, seqlen, G, R, N]
  *   A, D        [H] fp32                         decay (A < 0) and skip; D may be NULL (= 0)
  *   states      [S, H, N, P] fp32                S = batch (padded) or nseq (packed)
- *   Bprev       [S, G, N, R],  xprev [S, H, P, R]   token before position 0 of each sequence
+ *   Bprev       [S, G, R, N],  xprev [S, H, R, P]   token before position 0 of each sequence
  * Token inputs x, dt, lam, theta, B, C, Bprev, xprev and the output y share
  * one dtype (fp32 or bf16); states, A and D are fp32; arithmetic accumulates
  * in fp32.
@@ -113,8 +115,8 @@ mamba3_status mamba3_scan_fwd(const mamba3_scan_args *args, void *stream);
  * place: h <- alpha R (h + delta Bprev xprev^T) + gamma B x^T, y = h^T C + D x
  * (the same update as one token of the scan; section "MIMO Formulation" gives
  * the decode-time form H_t = alpha_t H_{t-1} + dt B_t x_t^T, y_t = H_t^T C_t).
- * Layouts: x, y [batch, H, P, R]; dt, lam [batch, H]; theta [batch, H, N/2];
- * B, C [batch, G, N, R]; Bprev [batch, G, N, R] and xprev [batch, H, P, R]
+ * Layouts: x, y [batch, H, R, P]; dt, lam [batch, H]; theta [batch, H, N/2];
+ * B, C [batch, G, R, N]; Bprev [batch, G, R, N] and xprev [batch, H, R, P]
  * (both NULL = no previous-token term); h [batch, H, N, P] fp32 in/out. */
 typedef struct {
     int32_t batch, nheads, headdim, dstate, rank, ngroups;

@@ -65,17 +65,17 @@ typedef struct {
     const int64_t *seq_len;    /* [nseq] tokens in each sequence */
     int32_t H, G, P, N, R;     /* heads, B/C groups, head dim, state dim (even), rank */
     int32_t in_dtype;          /* dtype tag of x, dt, lam, theta, B, C, Bprev, xprev */
-    const void *x;             /* [T, H, P, R] */
+    const void *x;             /* [T, H, R, P] */
     const void *dt;            /* [T, H] (post-softplus step) */
     const void *lam;           /* [T, H] (trapezoid weight in [0,1]) */
     const void *theta;         /* [T, H, N/2] (rotation frequency) */
-    const void *B;             /* [T, G, N, R] */
-    const void *C;             /* [T, G, N, R] */
+    const void *B;             /* [T, G, R, N] */
+    const void *C;             /* [T, G, R, N] */
     const double *A;           /* [H], negative */
     const double *D;           /* [H] or NULL */
     const double *h_in;        /* [nseq, H, N, P] or NULL (zero state) */
-    const void *Bprev;         /* [nseq, G, N, R] or NULL (no previous token) */
-    const void *xprev;         /* [nseq, H, P, R] or NULL */
+    const void *Bprev;         /* [nseq, G, R, N] or NULL (no previous token) */
+    const void *xprev;         /* [nseq, H, R, P] or NULL */
 } m3o_args;
 
 static inline double ld(const void *p, int dt, int64_t i) {
@@ -89,7 +89,7 @@ static inline double ld(const void *p, int dt, int64_t i) {
 
 /* ---------------------------------------------------------------- O1 ---- */
 /* Complex physical-frame recurrence for one (sequence, head) slab.
- * y_slab: [len, P, R]; h_slab: [N, P] (may be NULL). */
+ * y_slab: [len, R, P]; h_slab: [N, P] (may be NULL). */
 static void o1_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_slab) {
     const int H = a->H, G = a->G, P = a->P, N = a->N, R = a->R, K = N / 2;
     const int g = h / (H / G);
@@ -115,9 +115,10 @@ static void o1_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
         int64_t ob = ((int64_t)s * G + g) * N * R, ox = ((int64_t)s * H + h) * P * R;
         for (int k = 0; k < K; k++)
             for (int j = 0; j < R; j++)
-                bp[k * R + j] = ld(a->Bprev, dtp, ob + (2 * k) * R + j) +
-                                I * ld(a->Bprev, dtp, ob + (2 * k + 1) * R + j);
-        for (int i = 0; i < P * R; i++) xp[i] = ld(a->xprev, dtp, ox + i);
+                bp[k * R + j] = ld(a->Bprev, dtp, ob + j * N + 2 * k) +
+                                I * ld(a->Bprev, dtp, ob + j * N + 2 * k + 1);
+        for (int p = 0; p < P; p++)
+            for (int j = 0; j < R; j++) xp[p * R + j] = ld(a->xprev, dtp, ox + j * P + p);
     }
     const double Ah = a->A[h];
     const double Dh = a->D ? a->D[h] : 0.0;
@@ -135,12 +136,13 @@ static void o1_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
         const int64_t ob = (t * G + g) * N * R, ox = (t * H + h) * P * R;
         for (int k = 0; k < K; k++)
             for (int j = 0; j < R; j++) {
-                bc[k * R + j] = ld(a->B, dtp, ob + (2 * k) * R + j) +
-                                I * ld(a->B, dtp, ob + (2 * k + 1) * R + j);
-                cc[k * R + j] = ld(a->C, dtp, ob + (2 * k) * R + j) -
-                                I * ld(a->C, dtp, ob + (2 * k + 1) * R + j);
+                bc[k * R + j] = ld(a->B, dtp, ob + j * N + 2 * k) +
+                                I * ld(a->B, dtp, ob + j * N + 2 * k + 1);
+                cc[k * R + j] = ld(a->C, dtp, ob + j * N + 2 * k) -
+                                I * ld(a->C, dtp, ob + j * N + 2 * k + 1);
             }
-        for (int i = 0; i < P * R; i++) xc[i] = ld(a->x, dtp, ox + i);
+        for (int p = 0; p < P; p++)
+            for (int j = 0; j < R; j++) xc[p * R + j] = ld(a->x, dtp, ox + j * P + p);
 
         /* h <- z (h + delta b_prev x_prev^T) + gamma b x^T */
         for (int k = 0; k < K; k++)
@@ -152,13 +154,13 @@ static void o1_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
                 }
                 hc[k * P + p] = z[k] * (hc[k * P + p] + delta * prev) + gamma * cur;
             }
-        /* y[p][i] = Re sum_k c[k][i] h[k][p] + D x[p][i] */
+        /* y[i][p] = Re sum_k c[k][i] h[k][p] + D x[p][i] */
         double *yt = y_slab + tt * P * R;
         for (int p = 0; p < P; p++)
             for (int i = 0; i < R; i++) {
                 double complex acc = 0;
                 for (int k = 0; k < K; k++) acc += cc[k * R + i] * hc[k * P + p];
-                yt[p * R + i] = creal(acc) + Dh * xc[p * R + i];
+                yt[i * P + p] = creal(acc) + Dh * xc[p * R + i];
             }
         memcpy(bp, bc, (size_t)K * R * sizeof *bp);
         memcpy(xp, xc, (size_t)P * R * sizeof *xp);
@@ -209,8 +211,10 @@ static void o2_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
     if (a->Bprev && a->xprev) {
         has_prev = 1;
         int64_t ob = ((int64_t)s * G + g) * N * R, ox = ((int64_t)s * H + h) * P * R;
-        for (int i = 0; i < N * R; i++) bprot[i] = ld(a->Bprev, dtp, ob + i);
-        for (int i = 0; i < P * R; i++) xp[i] = ld(a->xprev, dtp, ox + i);
+        for (int n = 0; n < N; n++)
+            for (int j = 0; j < R; j++) bprot[n * R + j] = ld(a->Bprev, dtp, ob + j * N + n);
+        for (int p = 0; p < P; p++)
+            for (int j = 0; j < R; j++) xp[p * R + j] = ld(a->xprev, dtp, ox + j * P + p);
     }
     const double Ah = a->A[h];
     const double Dh = a->D ? a->D[h] : 0.0;
@@ -223,11 +227,13 @@ static void o2_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
         const double beta = (1.0 - lam) * dt * alpha, gamma = lam * dt;
         for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, (t * H + h) * K + k);
         const int64_t ob = (t * G + g) * N * R, ox = (t * H + h) * P * R;
-        for (int i = 0; i < N * R; i++) {
-            braw[i] = ld(a->B, dtp, ob + i);
-            craw[i] = ld(a->C, dtp, ob + i);
-        }
-        for (int i = 0; i < P * R; i++) xc[i] = ld(a->x, dtp, ox + i);
+        for (int n = 0; n < N; n++)
+            for (int j = 0; j < R; j++) {
+                braw[n * R + j] = ld(a->B, dtp, ob + j * N + n);
+                craw[n * R + j] = ld(a->C, dtp, ob + j * N + n);
+            }
+        for (int p = 0; p < P; p++)
+            for (int j = 0; j < R; j++) xc[p * R + j] = ld(a->x, dtp, ox + j * P + p);
         rot_vec(brot, braw, psi, K, R, -1);
         rot_vec(crot, craw, psi, K, R, -1);
         for (int n = 0; n < N; n++)
@@ -244,7 +250,7 @@ static void o2_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
             for (int i = 0; i < R; i++) {
                 double acc = 0;
                 for (int n = 0; n < N; n++) acc += crot[n * R + i] * hr[n * P + p];
-                yt[p * R + i] = acc + Dh * xc[p * R + i];
+                yt[i * P + p] = acc + Dh * xc[p * R + i];
             }
         memcpy(bprot, brot, (size_t)N * R * sizeof *bprot);
         memcpy(xp, xc, (size_t)P * R * sizeof *xp);
@@ -291,11 +297,14 @@ static void o3_slab(const m3o_args *a, int s, int h, double *y_slab) {
         gamma[t] = lam * dt;
         for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, (tg * H + h) * K + k);
         const int64_t ob = (tg * G + g) * N * R, ox = (tg * H + h) * P * R;
-        for (int i = 0; i < N * R; i++) tmp[i] = ld(a->B, dtp, ob + i);
+        for (int n = 0; n < N; n++)
+            for (int j = 0; j < R; j++) tmp[n * R + j] = ld(a->B, dtp, ob + j * N + n);
         rot_vec(Bt + t * N * R, tmp, psi, K, R, -1);
-        for (int i = 0; i < N * R; i++) tmp[i] = ld(a->C, dtp, ob + i);
+        for (int n = 0; n < N; n++)
+            for (int j = 0; j < R; j++) tmp[n * R + j] = ld(a->C, dtp, ob + j * N + n);
         rot_vec(Ct + t * N * R, tmp, psi, K, R, -1);
-        for (int i = 0; i < P * R; i++) X[t * P * R + i] = ld(a->x, dtp, ox + i);
+        for (int p = 0; p < P; p++)
+            for (int j = 0; j < R; j++) X[t * P * R + p * R + j] = ld(a->x, dtp, ox + j * P + p);
     }
     for (int64_t t = 0; t < T; t++) {
         double prod = 1.0;
@@ -324,7 +333,7 @@ static void o3_slab(const m3o_args *a, int s, int h, double *y_slab) {
                         acc += L[t * T + s2] * cb * X[s2 * P * R + p * R + j];
                     }
                 }
-                y_slab[t * P * R + p * R + i] = acc + Dh * X[t * P * R + p * R + i];
+                y_slab[t * P * R + i * P + p] = acc + Dh * X[t * P * R + p * R + i];
             }
     free(alpha); free(beta); free(gamma); free(L1); free(L2); free(L);
     free(Bt); free(Ct); free(X); free(psi); free(tmp);
@@ -338,7 +347,7 @@ static int check(const m3o_args *a) {
     return 0;
 }
 
-/* Which form: 1 = O1 (complex), 2 = O2 (rotated frame). y: [T, H, P, R] on the
+/* Which form: 1 = O1 (complex), 2 = O2 (rotated frame). y: [T, H, R, P] on the
  * flat token axis, h_out: [nseq, H, N, P] (may be NULL). OpenMP over slabs. */
 int m3o_scan(const m3o_args *a, int form, double *y, double *h_out, int nthreads) {
     if (check(a) || !y || (form != 1 && form != 2)) return 1;
@@ -363,7 +372,7 @@ int m3o_scan(const m3o_args *a, int form, double *y, double *h_out, int nthreads
     return 0;
 }
 
-/* One (sequence, head) slab. y_slab: [len, P, R]; h_slab: [N, P] or NULL.
+/* One (sequence, head) slab. y_slab: [len, R, P]; h_slab: [N, P] or NULL.
  * form 1 = O1, 2 = O2, 3 = O3 (zero initial state / no previous token only). */
 int m3o_scan_slab(const m3o_args *a, int form, int s, int h, double *y_slab, double *h_slab) {
     if (check(a) || !y_slab || s < 0 || s >= a->nseq || h < 0 || h >= a->H) return 1;
@@ -378,7 +387,7 @@ int m3o_scan_slab(const m3o_args *a, int form, int s, int h, double *y_slab, dou
 
 /* One decode step = one token of the O1 recurrence from a given state and
  * previous token, for every (batch row, head): batch rows are sequences of
- * length one. h_io: [batch, H, N, P] in/out; y: [batch, H, P, R]. */
+ * length one. h_io: [batch, H, N, P] in/out; y: [batch, H, R, P]. */
 int m3o_decode(const m3o_args *a_in, double *h_io, double *y, int nthreads) {
     if (check(a_in) || !h_io || !y) return 1;
     m3o_args a = *a_in;

@@ -7,8 +7,9 @@ imports nothing from the product package.
 
 All arrays use the flat token axis (padded batches are flattened to
 ``batch*seqlen`` tokens, sequence ``s`` starting at ``s*seqlen``):
-``x [T,H,P,R]``, ``dt, lam [T,H]``, ``theta [T,H,N/2]``, ``B, C [T,G,N,R]``,
-``A, D [H]``, ``h_in [S,H,N,P]``, ``Bprev [S,G,N,R]``, ``xprev [S,H,P,R]``.
+``x [T,H,R,P]``, ``dt, lam [T,H]``, ``theta [T,H,N/2]``, ``B, C [T,G,R,N]``,
+``A, D [H]``, ``h_in [S,H,N,P]``, ``Bprev [S,G,R,N]``, ``xprev [S,H,R,P]``
+(rank-major: the R columns of B_t, X_t are stored one after another).
 Token inputs may be float64, float32 or uint16 (bf16 bit patterns); they are
 converted exactly to double inside the oracle.
 """
@@ -105,8 +106,8 @@ class _Pack:
             keep[k] = None if v is None else np.ascontiguousarray(v, dtype=np.float64)
         x = keep["x"]
         B = keep["B"]
-        H, P, R = x.shape[-3], x.shape[-2], x.shape[-1]
-        G, N = B.shape[-3], B.shape[-2]
+        H, R, P = x.shape[-3], x.shape[-2], x.shape[-1]
+        G, N = B.shape[-3], B.shape[-1]
         keep["seq_start"] = np.ascontiguousarray(seq_start, dtype=np.int64)
         keep["seq_len"] = np.ascontiguousarray(seq_len, dtype=np.int64)
         self.keep = keep
@@ -139,7 +140,7 @@ def scan(inp: dict, form: int = 1, nthreads: int = 0, want_state: bool = True):
     flat, st, ln = flatten(inp)
     pk = _Pack(flat, st, ln)
     T = flat["x"].shape[0]
-    y = np.zeros((T, pk.H, pk.P, pk.R), dtype=np.float64)
+    y = np.zeros((T, pk.H, pk.R, pk.P), dtype=np.float64)
     h = np.zeros((pk.nseq, pk.H, pk.N, pk.P), dtype=np.float64) if want_state else None
     rc = lib().m3o_scan(ctypes.byref(pk.args), form, y.ctypes.data, _ptr(h), nthreads)
     if rc:
@@ -148,10 +149,10 @@ def scan(inp: dict, form: int = 1, nthreads: int = 0, want_state: bool = True):
 
 
 def scan_slab(inp: dict, s: int, h: int, form: int = 1, want_state: bool = True):
-    """One (sequence, head) slab. Returns (y [len,P,R], h_out [N,P] or None)."""
+    """One (sequence, head) slab. Returns (y [len,R,P], h_out [N,P] or None)."""
     flat, st, ln = flatten(inp)
     pk = _Pack(flat, st, ln)
-    y = np.zeros((int(ln[s]), pk.P, pk.R), dtype=np.float64)
+    y = np.zeros((int(ln[s]), pk.R, pk.P), dtype=np.float64)
     hs = np.zeros((pk.N, pk.P), dtype=np.float64) if want_state else None
     rc = lib().m3o_scan_slab(ctypes.byref(pk.args), form, s, h, y.ctypes.data, _ptr(hs))
     if rc:
@@ -161,11 +162,11 @@ def scan_slab(inp: dict, s: int, h: int, form: int = 1, want_state: bool = True)
 
 def decode(inp: dict, h: np.ndarray, nthreads: int = 0):
     """One decode step. inp token arrays have a leading batch axis (no L).
-    Returns (y [batch,H,P,R], h_new [batch,H,N,P]) in float64."""
+    Returns (y [batch,H,R,P], h_new [batch,H,N,P]) in float64."""
     b = inp["x"].shape[0]
     pk = _Pack(inp, np.arange(b, dtype=np.int64), np.ones(b, dtype=np.int64))
     hio = np.array(h, dtype=np.float64, copy=True, order="C")
-    y = np.zeros((b, pk.H, pk.P, pk.R), dtype=np.float64)
+    y = np.zeros((b, pk.H, pk.R, pk.P), dtype=np.float64)
     rc = lib().m3o_decode(ctypes.byref(pk.args), hio.ctypes.data, y.ctypes.data, nthreads)
     if rc:
         raise ValueError("oracle rejected its arguments")

@@ -108,8 +108,8 @@ def _stream(stream):
 def scan_args(x, dt, lam, theta, B, C, A, D=None, *, y, h_in=None, h_out=None, Bprev=None, xprev=None,
               cu_seqlens=None, chunk=64) -> ScanArgs:
     """Builds a ScanArgs from tensors in the library's layouts (see mamba3.h)."""
-    b, L, H, P, R = x.shape
-    G, N = B.shape[2], B.shape[3]
+    b, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
     nseq = int(cu_seqlens.numel()) - 1 if cu_seqlens is not None else 0
     return ScanArgs(b, L, H, P, N, R, G, chunk, _dtype_code(x), _ptr(cu_seqlens), nseq,
                     _ptr(x), _ptr(dt), _ptr(lam), _ptr(theta), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
@@ -134,7 +134,7 @@ def mamba3_scan_fwd(x, dt, lam, theta, B, C, A, D=None, *, y=None, h_in=None, h_
         y = torch.empty_like(x)
     if h_out is None and want_state:
         S = int(cu_seqlens.numel()) - 1 if cu_seqlens is not None else x.shape[0]
-        h_out = torch.empty((S, x.shape[2], B.shape[3], x.shape[3]), dtype=torch.float32, device=x.device)
+        h_out = torch.empty((S, x.shape[2], B.shape[4], x.shape[4]), dtype=torch.float32, device=x.device)
     a = scan_args(x, dt, lam, theta, B, C, A, D, y=y, h_in=h_in, h_out=h_out, Bprev=Bprev, xprev=xprev,
                   cu_seqlens=cu_seqlens, chunk=chunk)
     st = lib().mamba3_scan_fwd(ctypes.byref(a), _stream(stream))
@@ -144,8 +144,8 @@ def mamba3_scan_fwd(x, dt, lam, theta, B, C, A, D=None, *, y=None, h_in=None, h_
 
 
 def decode_args(x, dt, lam, theta, B, C, A, D=None, *, h, y, Bprev=None, xprev=None) -> DecodeArgs:
-    b, H, P, R = x.shape
-    G, N = B.shape[1], B.shape[2]
+    b, H, R, P = x.shape
+    G, N = B.shape[1], B.shape[3]
     return DecodeArgs(b, H, P, N, R, G, _dtype_code(x), _ptr(x), _ptr(dt), _ptr(lam), _ptr(theta), _ptr(B),
                       _ptr(C), _ptr(Bprev), _ptr(xprev), _ptr(A), _ptr(D), _ptr(h), _ptr(y))
 

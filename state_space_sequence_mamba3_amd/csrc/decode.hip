@@ -15,7 +15,7 @@
 // Bprev, theta) through LDS with 16-byte loads, and each thread updates 4
 // consecutive columns of ROWS consecutive rows (whole rotation pairs) and
 // writes them back. y is reduced over rows through LDS in a fixed order
-// (deterministic).
+// (deterministic). Token layouts are rank-major (B [R][N], x and y [R][P]).
 #include "m3_common.h"
 
 namespace m3 {
@@ -92,8 +92,8 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
     for (int c = 0; c < 4; c++)
 #pragma unroll
         for (int j = 0; j < R; j++) {
-            xv[c][j] = sX[(p0 + c) * R + j];
-            xpv[c][j] = has_prev ? sXp[(p0 + c) * R + j] : 0.f;
+            xv[c][j] = sX[j * P + p0 + c];
+            xpv[c][j] = has_prev ? sXp[j * P + p0 + c] : 0.f;
         }
 
     float yp[4][R];
@@ -110,12 +110,12 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
         float b0[R], b1[R], q0[R], q1[R], bp0[R], bp1[R];
 #pragma unroll
         for (int j = 0; j < R; j++) {
-            b0[j] = sB[n * R + j];
-            b1[j] = sB[(n + 1) * R + j];
-            q0[j] = sC[n * R + j];
-            q1[j] = sC[(n + 1) * R + j];
-            bp0[j] = has_prev ? sBp[n * R + j] : 0.f;
-            bp1[j] = has_prev ? sBp[(n + 1) * R + j] : 0.f;
+            b0[j] = sB[j * N + n];
+            b1[j] = sB[j * N + n + 1];
+            q0[j] = sC[j * N + n];
+            q1[j] = sC[j * N + n + 1];
+            bp0[j] = has_prev ? sBp[j * N + n] : 0.f;
+            bp1[j] = has_prev ? sBp[j * N + n + 1] : 0.f;
         }
 #pragma unroll
         for (int c = 0; c < 4; c++) {
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
 #pragma unroll
     for (int c = 0; c < 4; c++)
 #pragma unroll
-        for (int i = 0; i < R; i++) red[rg][(p0 + c) * R + i] = yp[c][i];
+        for (int i = 0; i < R; i++) red[rg][i * P + p0 + c] = yp[c][i];
     __syncthreads();
     T *y = (T *)pr.y + (int64_t)bh * P * R;
     for (int e = tid; e < P * R; e += TPB) {

@@ -13,25 +13,32 @@
 // (delta_{e+1} is the next chunk's first token's, 0 at the sequence end: it
 // folds that token's previous-input term into the carried state).
 //
-// Rank-expanded rows: row (tau, j) = tau*R + j of a chunk, so a chunk is a
-// (Q*R) x (Q*R) problem. Outputs are cut into 16-row t-blocks, the sweep over
+// Rank-expanded rows: row (tau, j) = tau*R + j of a chunk; with the rank-major
+// layouts every such row of B, C, x and y is contiguous in memory. A chunk is
+// a (Q*R) x (Q*R) problem: outputs are cut into 16-row t-blocks, the sweep over
 // inputs into 32-row s-blocks.
-//   * Every wave owns t-blocks (balanced pairs along the causal triangle) and
-//     keeps their rotated C~ rows (MFMA operands) and output accumulators in
-//     registers.
-//   * The chunk is swept over s-blocks: each s-block's rotated B~, weighted
-//     B~^T and X^T are staged through LDS; each wave computes its score tiles
+//   * Once per chunk the cumulative angles become an fp16 (cos, sin) table in
+//     LDS; every rotation of B, C reads it (one sincos per angle and chunk).
+//   * Every wave owns t-blocks (balanced pairs along the causal triangle); it
+//     loads their C rows straight from memory in MFMA operand layout, rotates
+//     them in registers and keeps them, with the output accumulators, in
+//     registers for the whole chunk.
+//   * Each s-block's rotated B~ rows, X rows and weighted X rows are staged in
+//     LDS as plain row copies. Each wave computes its score tiles
 //     G^T = B~ C~^T (v_mfma_f32_16x16x32_bf16, K = N), applies the decay and
-//     trapezoid mask in registers, converts to bf16 and feeds the tile straight
-//     back as the A operand of Y += M X, with the K index permuted to the
-//     accumulator lane layout - score tiles never touch LDS.
+//     trapezoid mask in registers and feeds the bf16 tile straight back as the
+//     A operand of Y += M X, with the K index permuted to the accumulator lane
+//     layout; score tiles never touch LDS. Operands that need the token axis
+//     as the K index (X for the outputs, B~ and weighted X for the state
+//     update) are read with the LDS transpose read ds_read_b64_tr_b16.
 //   * The N x P state is split into tiles over the waves; it accumulates the
-//     chunk's rank-R update B~^T X on MFMA and is rotated by Phi_e at the end.
-//     A bf16 copy in LDS feeds the next chunk's inter-chunk term e^{S_t} C~^T H'.
-//   * Global loads run ahead of use: the raw B and X of the sequence's
-//     s-blocks stream through two register sets two blocks ahead, and the next
-//     chunk's dt, lam, theta and C rows are loaded while the current chunk
-//     computes.
+//     chunk's rank-R update B~^T (w X) on MFMA and is rotated by the chunk's
+//     total angle at the end (fp32). A bf16 copy in LDS feeds the next chunk's
+//     inter-chunk term e^{S_t} C~^T H'.
+//   * Global loads run ahead of use: raw B and X of the sequence's s-blocks
+//     stream through two register sets two blocks ahead, and the next chunk's
+//     dt, lam, theta and C rows are loaded while the current chunk computes.
+//   * Outputs leave through a per-wave LDS transpose as 16-byte row stores.
 #include <type_traits>
 
 #include "m3_common.h"
@@ -40,11 +47,31 @@ namespace m3 {
 
 namespace {
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read (16-bit elements): within each group of 16 lanes, lane i
+// receives element i % 4 of the 4 elements read by lanes i/4 + 4k, k = 0..3.
+// With lane i of the group pointing at &M[r0 + i/4][c0 + 4*(i%4)] of a
+// row-major bf16 matrix M, lane i receives M[r0 + k][c0 + i] for k = 0..3.
+__device__ __forceinline__ bf16x4 ds_read_tr(const bf16 *p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+// 8 K-values (rows r0 .. r0+3 and r1 .. r1+3) of column c0 + (lane % 16) of a
+// row-major [rows][ld] bf16 matrix, as an MFMA operand.
+__device__ __forceinline__ bf16x8 tr_operand(const bf16 *m, int ld, int r0, int r1, int c0, int l16) {
+    const bf16x4 a = ds_read_tr(m + (r0 + l16 / 4) * ld + c0 + 4 * (l16 % 4));
+    const bf16x4 b = ds_read_tr(m + (r1 + l16 / 4) * ld + c0 + 4 * (l16 % 4));
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 // Wait for this wave's outstanding LDS operations (wave-private staging).
@@ -62,6 +89,21 @@ __device__ __forceinline__ float wave_incl_scan(float v, int lane) {
 // 2^x for x <= 0 (hardware exp2; results below the fp32 normal range flush to 0)
 __device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Rotate the 4 pairs of an 8-element row piece by -Phi: (u, v) -> (c u + s v, -s u + c v),
+// with (cos, sin) of the 4 pairs packed as fp16 in cs.
+__device__ __forceinline__ void rot_piece(const bf16x8 raw, const f16x8 cs, float (&o)[8]) {
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const float c = (float)cs[2 * m], sn = (float)cs[2 * m + 1];
+        const float u = (float)raw[2 * m], v = (float)raw[2 * m + 1];
+        o[2 * m] = c * u + sn * v;
+        o[2 * m + 1] = c * v - sn * u;
+    }
+}
+__device__ __forceinline__ bf16x8 pack8(const float (&o)[8]) {
+    return bf16x8{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3], (bf16)o[4], (bf16)o[5], (bf16)o[6], (bf16)o[7]};
+}
+
 struct BfParams {
     const bf16 *x, *dt, *lam, *theta, *B, *C, *Bprev, *xprev;
     const float *A, *D, *h_in;
@@ -75,22 +117,22 @@ template <int N_, int P_, int R_, int Q_, int NW_, int UT_>
 struct Cfg {
     static constexpr int N = N_, P = P_, R = R_, Q = Q_, NW = NW_, UT = UT_;
     static constexpr int K = N / 2, QR = Q * R;
-    static constexpr int NTB = QR / 16, NSB = QR / 32;      // 16-row t-blocks, 32-row s-blocks
+    static constexpr int NTB = QR / 16;                     // 16-row t-blocks
     static constexpr int TOKT = 16 / R, TOKS = 32 / R;      // tokens per t-block / s-block
     static constexpr int NTHR = NW * 64, TPW = NTB / NW;
     static constexpr int NKK = N / 32;                      // K-steps over N (16x16x32)
     static constexpr int NPT = P / 16;                      // 16-column tiles of P
     static constexpr int NUT = (N / UT) * (P / UT), UPW = NUT / NW;
     static constexpr int UR_ = (UT == 32) ? 16 : 4;         // state registers per tile
-    static constexpr int NS = N + 8;                        // padded bf16 row stride of [*][N] tiles
-    static constexpr int RS = 40;                           // padded bf16 row stride of [*][32] tiles
+    static constexpr int NS = N + 8, PS = P + 8;            // padded bf16 row strides
     static_assert(N % 32 == 0 && P % 32 == 0 && (R == 1 || R == 2 || R == 4) && QR % 32 == 0, "shape");
     static_assert(NTB % NW == 0 && (TPW == 1 || TPW % 2 == 0), "t-block split");
     static_assert(NUT % NW == 0 && (UT == 16 || UT == 32), "state tile split");
     static_assert(K % 8 == 0 && Q % NW == 0 && Q <= 128 && Q < NTHR, "prologue");
     // LDS layout (bytes)
-    static constexpr int OFF_PHI = 0;                                  // float [Q][K]
-    static constexpr int OFF_S2 = OFF_PHI + Q * K * 4;                 // float [Q] log2 decay prefix
+    static constexpr int OFF_PHI = 0;                                  // float [Q][K] -> f16x2 (cos, sin)
+    static constexpr int OFF_PHE = OFF_PHI + Q * K * 4;                // float [K] chunk's total angle
+    static constexpr int OFF_S2 = OFF_PHE + K * 4;                     // float [Q] log2 decay prefix
     static constexpr int OFF_A2 = OFF_S2 + Q * 4;                      // float [Q] per-token log2 decay
     static constexpr int OFF_GM = OFF_A2 + Q * 4;                      // float [Q] gamma
     static constexpr int OFF_DL = OFF_GM + Q * 4;                      // float [Q] delta
@@ -99,29 +141,29 @@ struct Cfg {
     static constexpr int OFF_TOT = OFF_WU + Q * 4;                     // float [NW][K] angle segment sums
     static constexpr int OFF_MISC = OFF_TOT + NW * K * 4;              // float [4]
     static constexpr int OFF_HB = (OFF_MISC + 16 + 15) / 16 * 16;      // bf16 [P][NS] carried state
-    static constexpr int OFF_U = OFF_HB + P * NS * 2;                  // union region
-    static constexpr int CST_BYTES = 16 * NS * 2;                      // per-wave C~ staging
-    static constexpr int SB_BT = 0, SB_WT = 32 * NS * 2, SB_X = SB_WT + N * RS * 2;
-    static constexpr int STAGE = SB_X + P * RS * 2;                    // one s-block stage
-    static constexpr int U_BYTES = (NW * CST_BYTES > 2 * STAGE) ? NW * CST_BYTES : 2 * STAGE;
+    static constexpr int OFF_U = OFF_HB + P * NS * 2;                  // stage buffers / output staging
+    static constexpr int SB_BT = 0, SB_X = 32 * NS * 2, SB_WX = SB_X + 32 * PS * 2;
+    static constexpr int STAGE = SB_WX + 32 * PS * 2;                  // one s-block stage
+    static constexpr int YST = 16 * PS * 2;                            // per-wave output staging
+    static constexpr int U_BYTES = (NW * YST > 2 * STAGE) ? NW * YST : 2 * STAGE;
     static constexpr int LDS = OFF_U + U_BYTES;
     static_assert(LDS <= 160 * 1024, "LDS");
     // global loads (16 bytes each) per s-block, and next-chunk header prefetch
     static constexpr int BCH = 32 * N / 8, XCH = 32 * P / 8;
     static constexpr int NLB = (BCH + NTHR - 1) / NTHR, NLX = (XCH + NTHR - 1) / NTHR;
     static constexpr int NTH = (Q * K / 8 + NTHR - 1) / NTHR;
-    static constexpr int CPT = N / 32;                                 // C pieces per lane per t-block
-    static constexpr int NCP = TPW * CPT;
 };
 
 template <class CF>
 __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
     constexpr int N = CF::N, P = CF::P, R = CF::R, Q = CF::Q, NW = CF::NW, K = CF::K, UT = CF::UT;
     constexpr int TOKT = CF::TOKT, TOKS = CF::TOKS, NTHR = CF::NTHR, TPW = CF::TPW;
-    constexpr int NKK = CF::NKK, NPT = CF::NPT, UPW = CF::UPW, NS = CF::NS, RS = CF::RS, UR_ = CF::UR_;
+    constexpr int NKK = CF::NKK, NPT = CF::NPT, UPW = CF::UPW, NS = CF::NS, PS = CF::PS, UR_ = CF::UR_;
     using UAcc = std::conditional_t<UT == 32, f32x16, f32x4>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float *phi = (float *)(smem + CF::OFF_PHI);
+    const f16x2 *cst = (const f16x2 *)(smem + CF::OFF_PHI);   // after the prologue: (cos, sin) table
+    float *PHE = (float *)(smem + CF::OFF_PHE);
     float *S2 = (float *)(smem + CF::OFF_S2);
     float *A2 = (float *)(smem + CF::OFF_A2);
     float *GM = (float *)(smem + CF::OFF_GM);
@@ -150,13 +192,13 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
     }
     const float A2h = pr.A[h] * kLog2e;
     const float Dh = pr.D ? pr.D[h] : 0.f;
-    // per-(sequence, head) base pointers: add token * stride
-    const bf16 *gB = pr.B + g * (int64_t)N * R;
-    const bf16 *gC = pr.C + g * (int64_t)N * R;
-    const bf16 *gX = pr.x + h * (int64_t)P * R;
-    bf16 *gY = pr.y + h * (int64_t)P * R;
+    // per-(sequence, head) base pointers: add token * stride (+ rank * N or P)
+    const bf16 *gB = pr.B + g * (int64_t)R * N;
+    const bf16 *gC = pr.C + g * (int64_t)R * N;
+    const bf16 *gX = pr.x + h * (int64_t)R * P;
+    bf16 *gY = pr.y + h * (int64_t)R * P;
     const bf16 *gTh = pr.theta + h * (int64_t)K;
-    const int64_t strBC = (int64_t)G * N * R, strX = (int64_t)H * P * R, strTh = (int64_t)H * K;
+    const int64_t strBC = (int64_t)G * R * N, strX = (int64_t)H * R * P, strTh = (int64_t)H * K;
 
     // this wave's t-blocks and state tiles
     int task_tb[TPW];
@@ -170,7 +212,7 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
         ut_n0[v] = (ut / (P / UT)) * UT;
         ut_p0[v] = (ut % (P / UT)) * UT;
     }
-    // state-tile register r -> (row n, column p) within the tile
+    // state-tile register r -> row n within the tile; column = ucol
     auto urow = [&](int r) { return (UT == 32) ? 8 * (r / 4) + 4 * hi + (r % 4) : 4 * q4 + r; };
     const int ucol = (UT == 32) ? l32 : l16;
 
@@ -191,11 +233,11 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
                 const int n = ut_n0[v] + urow(r);
                 float val = pr.h_in ? pr.h_in[so + (int64_t)n * P + p] : 0.f;
                 if (pr.Bprev) {
-                    const bf16 *bp = pr.Bprev + ((int64_t)s * G + g) * N * R + n * R;
-                    const bf16 *xp = pr.xprev + ((int64_t)s * H + h) * P * R + p * R;
+                    const bf16 *bp = pr.Bprev + ((int64_t)s * G + g) * R * N + n;
+                    const bf16 *xp = pr.xprev + ((int64_t)s * H + h) * R * P + p;
                     float acc = 0.f;
 #pragma unroll
-                    for (int j = 0; j < R; j++) acc += to_f(bp[j]) * to_f(xp[j]);
+                    for (int j = 0; j < R; j++) acc += to_f(bp[j * N]) * to_f(xp[j * P]);
                     val += d0 * acc;
                 }
                 hreg[v][r] = val;
@@ -212,7 +254,7 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
     float h_dt = 0.f, h_lam = 0.f;
     bf16x8 h_th[CF::NTH];
     float h_thdt[CF::NTH];
-    bf16x8 h_c[CF::NCP];
+    bf16x8 h_c[TPW][NKK];
     auto load_header = [&](int64_t c0h) {
         const int nqh = (int)min((int64_t)Q, len - c0h);
         const int64_t t0h = start + c0h;
@@ -236,15 +278,17 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
                 h_th[i] = *(const bf16x8 *)(gTh + (t0h + tau) * strTh + k0);
             }
         }
+        // C rows of the own t-blocks in operand layout: row 16 tb + l16, columns 32 kk + 8 q4 ..
 #pragma unroll
-        for (int u = 0; u < TPW; u++)
+        for (int u = 0; u < TPW; u++) {
+            const int row = task_tb[u] * 16 + l16;
+            const int tau = row / R, j = row % R;
 #pragma unroll
-            for (int i = 0; i < CF::CPT; i++) {
-                const int flat = (lane + i * 64) * 8;
-                const int tau = task_tb[u] * TOKT + flat / (N * R);
-                h_c[u * CF::CPT + i] = bf16x8{};
-                if (tau < nqh) h_c[u * CF::CPT + i] = *(const bf16x8 *)(gC + (t0h + tau) * strBC + (flat % (N * R)));
+            for (int kk = 0; kk < NKK; kk++) {
+                h_c[u][kk] = bf16x8{};
+                if (tau < nqh) h_c[u][kk] = *(const bf16x8 *)(gC + (t0h + tau) * strBC + j * N + 32 * kk + 8 * q4);
             }
+        }
     };
 
     // ---- s-block stream: block j of the sequence lives in register set j % 2
@@ -257,8 +301,9 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
             const int c = tid + i * NTHR;
             rb[i] = bf16x8{};
             if (c < CF::BCH) {
-                const int flat = c * 8, tau = sb * TOKS + flat / (N * R);
-                if (tau < nqb) rb[i] = *(const bf16x8 *)(gB + (t0b + tau) * strBC + (flat % (N * R)));
+                const int row = c / (N / 8), col = (c % (N / 8)) * 8;
+                const int tau = sb * TOKS + row / R;
+                if (tau < nqb) rb[i] = *(const bf16x8 *)(gB + (t0b + tau) * strBC + (row % R) * N + col);
             }
         }
 #pragma unroll
@@ -266,8 +311,9 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
             const int c = tid + i * NTHR;
             rx[i] = bf16x8{};
             if (c < CF::XCH) {
-                const int flat = c * 8, tau = sb * TOKS + flat / (P * R);
-                if (tau < nqb) rx[i] = *(const bf16x8 *)(gX + (t0b + tau) * strX + (flat % (P * R)));
+                const int row = c / (P / 8), col = (c % (P / 8)) * 8;
+                const int tau = sb * TOKS + row / R;
+                if (tau < nqb) rx[i] = *(const bf16x8 *)(gX + (t0b + tau) * strX + (row % R) * P + col);
             }
         }
     };
@@ -363,46 +409,34 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
             if (lane == 0) MISC[1] = S2e;
         }
         __syncthreads();
-        if (lane < K && wave > 0) {
+        // ---- prologue 3: carry the segment sums, keep the total angle, turn angles into (cos, sin)
+        if (lane < K) {
             float carry = 0.f;
             for (int w = 0; w < wave; w++) carry += TOT[w * K + lane];
 #pragma unroll
-            for (int t = 0; t < SEG; t++) phi[(wave * SEG + t) * K + lane] += carry;
+            for (int t = 0; t < SEG; t++) {
+                const int tau = wave * SEG + t;
+                const float a = phi[tau * K + lane] + carry;
+                if (tau == Q - 1) PHE[lane] = a;   // angles past the end are zero: Phi[Q-1] = Phi[nq-1]
+                float sn, cs;
+                __sincosf(a, &sn, &cs);
+                ((f16x2 *)phi)[tau * K + lane] = f16x2{(_Float16)cs, (_Float16)sn};
+            }
         }
         __syncthreads();
 
-        // ---- prologue 3: rotated C~ rows of this wave's t-blocks into registers (per-wave staging)
+        // ---- rotated C~ rows of this wave's t-blocks, straight from the header registers
         bf16x8 creg[TPW][NKK];
         f32x4 yacc[TPW][NPT];
-        {
-            bf16 *cst = (bf16 *)(UR + wave * CF::CST_BYTES);
 #pragma unroll
-            for (int u = 0; u < TPW; u++) {
-                const int tb = task_tb[u];
+        for (int u = 0; u < TPW; u++) {
+            const int tau = (task_tb[u] * 16 + l16) / R;
 #pragma unroll
-                for (int i = 0; i < CF::CPT; i++) {
-                    const int flat = (lane + i * 64) * 8;
-                    const int tl = flat / (N * R);               // token within the t-block
-                    const int n0 = (flat % (N * R)) / R;         // first state row of the piece
-                    const int tau = tb * TOKT + tl;
-                    const bf16x8 raw = h_c[u * CF::CPT + i];
-#pragma unroll
-                    for (int q = 0; q < 4 / R; q++) {   // pairs in the piece
-                        const int n = n0 + 2 * q;
-                        float sn, cs;
-                        __sincosf(phi[tau * K + n / 2], &sn, &cs);
-#pragma unroll
-                        for (int j = 0; j < R; j++) {
-                            const float c0v = (float)raw[(2 * q) * R + j], c1v = (float)raw[(2 * q + 1) * R + j];
-                            *(bf16x2 *)(cst + (tl * R + j) * NS + n) =
-                                bf16x2{(bf16)(cs * c0v + sn * c1v), (bf16)(-sn * c0v + cs * c1v)};
-                        }
-                    }
-                }
-                lds_wait();
-#pragma unroll
-                for (int kk = 0; kk < NKK; kk++) creg[u][kk] = *(const bf16x8 *)(cst + l16 * NS + 32 * kk + 8 * q4);
-                lds_wait();
+            for (int kk = 0; kk < NKK; kk++) {
+                const f16x8 cs = *(const f16x8 *)(cst + tau * K + 16 * kk + 4 * q4);
+                float o[8];
+                rot_piece(h_c[u][kk], cs, o);
+                creg[u][kk] = pack8(o);
             }
         }
 
@@ -412,7 +446,7 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
             const int tb = task_tb[u];
             float sc[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++) sc[i] = exp2_neg(S2[tb * TOKT + (4 * q4 + i) / R]);
+            for (int i = 0; i < 4; i++) sc[i] = exp2_neg(S2[(tb * 16 + 4 * q4 + i) / R]);
 #pragma unroll
             for (int pt = 0; pt < NPT; pt++) {
                 f32x4 acc = {};
@@ -434,72 +468,44 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
         }
         // the header registers are consumed: prefetch the next chunk's header now
         if (c0 + Q < len) load_header(c0 + Q);
-        __syncthreads();   // C~ staging and H' reads done: the union region becomes s-block stages
 
         // ---- s-block sweep
         const int nbs = (nq + TOKS - 1) / TOKS;   // s-blocks holding valid tokens
         auto store_block = [&](const bf16x8 (&rawB)[CF::NLB], const bf16x8 (&rawX)[CF::NLX], int sb, int buf) {
             char *stg = UR + buf * CF::STAGE;
-            bf16 *bt = (bf16 *)(stg + CF::SB_BT);   // [32 rows][NS]   rotated B~
-            bf16 *wt = (bf16 *)(stg + CF::SB_WT);   // [N][RS]         wU * B~, transposed
-            bf16 *xt = (bf16 *)(stg + CF::SB_X);    // [P][RS]         X, transposed
+            bf16 *bt = (bf16 *)(stg + CF::SB_BT);   // [32 rows][NS]  rotated B~
+            bf16 *xs = (bf16 *)(stg + CF::SB_X);    // [32 rows][PS]  X
+            bf16 *wx = (bf16 *)(stg + CF::SB_WX);   // [32 rows][PS]  wU * X
 #pragma unroll
             for (int i = 0; i < CF::NLB; i++) {
                 const int c = tid + i * NTHR;
                 if (c < CF::BCH) {
-                    const int flat = c * 8, tl = flat / (N * R), n0 = (flat % (N * R)) / R;
-                    const int tau = sb * TOKS + tl;
-                    const float w = WU[tau];
-#pragma unroll
-                    for (int q = 0; q < 4 / R; q++) {
-                        const int n = n0 + 2 * q;
-                        float sn, cs;
-                        __sincosf(phi[tau * K + n / 2], &sn, &cs);
-                        float r0[R], r1[R];
-#pragma unroll
-                        for (int j = 0; j < R; j++) {
-                            const float b0 = (float)rawB[i][(2 * q) * R + j], b1 = (float)rawB[i][(2 * q + 1) * R + j];
-                            r0[j] = cs * b0 + sn * b1;
-                            r1[j] = -sn * b0 + cs * b1;
-                            *(bf16x2 *)(bt + (tl * R + j) * NS + n) = bf16x2{(bf16)r0[j], (bf16)r1[j]};
-                        }
-                        if constexpr (R == 4) {
-                            *(bf16x4 *)(wt + n * RS + tl * 4) =
-                                bf16x4{(bf16)(w * r0[0]), (bf16)(w * r0[1]), (bf16)(w * r0[2]), (bf16)(w * r0[3])};
-                            *(bf16x4 *)(wt + (n + 1) * RS + tl * 4) =
-                                bf16x4{(bf16)(w * r1[0]), (bf16)(w * r1[1]), (bf16)(w * r1[2]), (bf16)(w * r1[3])};
-                        } else {
-#pragma unroll
-                            for (int j = 0; j < R; j++) {
-                                wt[n * RS + tl * R + j] = (bf16)(w * r0[j]);
-                                wt[(n + 1) * RS + tl * R + j] = (bf16)(w * r1[j]);
-                            }
-                        }
-                    }
+                    const int row = c / (N / 8), col = (c % (N / 8)) * 8;
+                    const int tau = sb * TOKS + row / R;
+                    float o[8];
+                    rot_piece(rawB[i], *(const f16x8 *)(cst + tau * K + col / 2), o);
+                    *(bf16x8 *)(bt + row * NS + col) = pack8(o);
                 }
             }
 #pragma unroll
             for (int i = 0; i < CF::NLX; i++) {
                 const int c = tid + i * NTHR;
                 if (c < CF::XCH) {
-                    const int flat = c * 8, tl = flat / (P * R), p0 = (flat % (P * R)) / R;
-                    if constexpr (R == 4) {
+                    const int row = c / (P / 8), col = (c % (P / 8)) * 8;
+                    const float w = WU[sb * TOKS + row / R];
+                    *(bf16x8 *)(xs + row * PS + col) = rawX[i];
+                    float o[8];
 #pragma unroll
-                        for (int q = 0; q < 2; q++)
-                            *(bf16x4 *)(xt + (p0 + q) * RS + tl * 4) =
-                                bf16x4{rawX[i][4 * q], rawX[i][4 * q + 1], rawX[i][4 * q + 2], rawX[i][4 * q + 3]};
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; e++) xt[(p0 + e / R) * RS + tl * R + (e % R)] = rawX[i][e];
-                    }
+                    for (int e = 0; e < 8; e++) o[e] = w * (float)rawX[i][e];
+                    *(bf16x8 *)(wx + row * PS + col) = pack8(o);
                 }
             }
         };
         auto compute_block = [&](int sb) {
             const char *stg = UR + (sb & 1) * CF::STAGE;
             const bf16 *bt = (const bf16 *)(stg + CF::SB_BT);
-            const bf16 *wt = (const bf16 *)(stg + CF::SB_WT);
-            const bf16 *xt = (const bf16 *)(stg + CF::SB_X);
+            const bf16 *xs = (const bf16 *)(stg + CF::SB_X);
+            const bf16 *wx = (const bf16 *)(stg + CF::SB_WX);
 #pragma unroll
             for (int u = 0; u < TPW; u++) {
                 const int tb = task_tb[u];
@@ -512,45 +518,45 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
                     if (upper) g1 = mfma16(*(const bf16x8 *)(bt + (16 + l16) * NS + 32 * kk + 8 * q4), creg[u][kk], g1);
                 }
                 // decay/trapezoid mask: column (t, i) = lane's t-row, rows (s, j) of the two halves
-                const int tt = tb * TOKT + l16 / R;
+                const int tt = (tb * 16 + l16) / R;
                 const float S2t = S2[tt];
                 bf16x8 mop;
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
-                    const int ss = sb * TOKS + (16 * (e / 4) + 4 * q4 + (e % 4)) / R;
+                    const int ss = (sb * 32 + 16 * (e / 4) + 4 * q4 + (e % 4)) / R;
                     float coef = 0.f;
                     if (ss <= tt && (e < 4 || upper))
                         coef = exp2_neg(S2t - S2[ss]) * ((ss < tt) ? G1[ss] : GM[ss]);
                     mop[e] = (bf16)(coef * ((e < 4) ? g0[e] : g1[e - 4]));
                 }
-                const int dblk = tb - 2 * sb;               // 0/1: t-block is in this s-block's half
+                const int dblk = tb - 2 * sb;               // 0/1: the t-block's rows are in this s-block
 #pragma unroll
                 for (int pt = 0; pt < NPT; pt++) {
-                    const int p = pt * 16 + l16;
-                    const bf16x4 lo = *(const bf16x4 *)(xt + p * RS + 4 * q4);
-                    const bf16x4 up = *(const bf16x4 *)(xt + p * RS + 16 + 4 * q4);
-                    yacc[u][pt] = mfma16(mop, bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]},
-                                         yacc[u][pt]);
+                    // X rows 4 q4 .. and 16 + 4 q4 .. of column 16 pt + l16 (K permuted like mop)
+                    yacc[u][pt] = mfma16(mop, tr_operand(xs, PS, 4 * q4, 16 + 4 * q4, pt * 16, l16), yacc[u][pt]);
                     if (dblk == 0 || dblk == 1) {           // skip term D x_t of the t-block's own rows
-                        const bf16x4 xv = *(const bf16x4 *)(xt + p * RS + 16 * dblk + 4 * q4);
+                        const bf16x4 xv = ds_read_tr(xs + (16 * dblk + 4 * q4 + l16 / 4) * PS + pt * 16 + 4 * (l16 % 4));
 #pragma unroll
                         for (int i = 0; i < 4; i++) yacc[u][pt][i] += Dh * (float)xv[i];
                     }
                 }
             }
-            // chunk-state update on the owned state tiles: H += (wU B~)^T X
+            // chunk-state update on the owned state tiles: H += B~^T (wU X), K = the s-block's rows
 #pragma unroll
             for (int v = 0; v < UPW; v++) {
                 if constexpr (UT == 32) {
-                    const int n = ut_n0[v] + l32, p = ut_p0[v] + l32;
+                    // lane groups: column half c0 = 16 (group % 2), K rows 8 (group / 2) ..
+                    const int grp = lane >> 4;
+                    const int cn = ut_n0[v] + 16 * (grp & 1), cp = ut_p0[v] + 16 * (grp & 1);
 #pragma unroll
-                    for (int ks = 0; ks < 2; ks++)
-                        hreg[v] = mfma32(*(const bf16x8 *)(wt + n * RS + 16 * ks + 8 * hi),
-                                         *(const bf16x8 *)(xt + p * RS + 16 * ks + 8 * hi), hreg[v]);
+                    for (int ks = 0; ks < 2; ks++) {
+                        const int r0 = 16 * ks + 8 * (grp >> 1);
+                        hreg[v] = mfma32(tr_operand(bt, NS, r0, r0 + 4, cn, l16), tr_operand(wx, PS, r0, r0 + 4, cp, l16),
+                                         hreg[v]);
+                    }
                 } else {
-                    const int n = ut_n0[v] + l16, p = ut_p0[v] + l16;
-                    hreg[v] = mfma16(*(const bf16x8 *)(wt + n * RS + 8 * q4), *(const bf16x8 *)(xt + p * RS + 8 * q4),
-                                     hreg[v]);
+                    hreg[v] = mfma16(tr_operand(bt, NS, 8 * q4, 8 * q4 + 4, ut_n0[v], l16),
+                                     tr_operand(wx, PS, 8 * q4, 8 * q4 + 4, ut_p0[v], l16), hreg[v]);
                 }
             }
         };
@@ -573,45 +579,40 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
             __syncthreads();
         }
 
-        // ---- epilogue: outputs (lane column p, rows 4*q4 + i of each t-block)
+        // ---- epilogue: outputs through a per-wave LDS transpose, 16-byte row stores
+        {
+            bf16 *ys = (bf16 *)(UR + wave * CF::YST);   // [16 rows][PS]
 #pragma unroll
-        for (int u = 0; u < TPW; u++) {
-            const int tb = task_tb[u];
+            for (int u = 0; u < TPW; u++) {
+                const int tb = task_tb[u];
 #pragma unroll
-            for (int pt = 0; pt < NPT; pt++) {
-                const int p = pt * 16 + l16;
-                if constexpr (R == 4) {
-                    const int tau = tb * TOKT + q4;
-                    if (tau < nq)
-                        *(bf16x4 *)(gY + (tok0 + tau) * strX + p * R) =
-                            bf16x4{(bf16)yacc[u][pt][0], (bf16)yacc[u][pt][1], (bf16)yacc[u][pt][2],
-                                   (bf16)yacc[u][pt][3]};
-                } else {
+                for (int pt = 0; pt < NPT; pt++)
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const int row = 4 * q4 + i;
-                        const int tau = tb * TOKT + row / R;
-                        if (tau < nq) gY[(tok0 + tau) * strX + p * R + row % R] = (bf16)yacc[u][pt][i];
-                    }
+                    for (int i = 0; i < 4; i++) ys[(4 * q4 + i) * PS + pt * 16 + l16] = (bf16)yacc[u][pt][i];
+                lds_wait();
+#pragma unroll
+                for (int c = lane; c < 16 * P / 8; c += 64) {
+                    const int row = c / (P / 8), col = (c % (P / 8)) * 8;
+                    const int rr = tb * 16 + row, tau = rr / R;
+                    if (tau < nq) *(bf16x8 *)(gY + (tok0 + tau) * strX + (rr % R) * P + col) =
+                        *(const bf16x8 *)(ys + row * PS + col);
                 }
+                lds_wait();
             }
         }
         // ---- epilogue: rotate the state by the chunk's total angle; bf16 copy for the next chunk
-        {
-            const float *phe = phi + (nq - 1) * K;
 #pragma unroll
-            for (int v = 0; v < UPW; v++) {
-                const int p = ut_p0[v] + ucol;
+        for (int v = 0; v < UPW; v++) {
+            const int p = ut_p0[v] + ucol;
 #pragma unroll
-                for (int r = 0; r < UR_; r += 2) {
-                    const int n = ut_n0[v] + urow(r);
-                    float sn, cs;
-                    __sincosf(phe[n / 2], &sn, &cs);
-                    const float u0 = hreg[v][r], u1 = hreg[v][r + 1];
-                    hreg[v][r] = cs * u0 - sn * u1;
-                    hreg[v][r + 1] = sn * u0 + cs * u1;
-                    *(bf16x2 *)(HB + p * NS + n) = bf16x2{(bf16)hreg[v][r], (bf16)hreg[v][r + 1]};
-                }
+            for (int r = 0; r < UR_; r += 2) {
+                const int n = ut_n0[v] + urow(r);
+                float sn, cs;
+                __sincosf(PHE[n / 2], &sn, &cs);
+                const float u0 = hreg[v][r], u1 = hreg[v][r + 1];
+                hreg[v][r] = cs * u0 - sn * u1;
+                hreg[v][r + 1] = sn * u0 + cs * u1;
+                *(bf16x2 *)(HB + p * NS + n) = bf16x2{(bf16)hreg[v][r], (bf16)hreg[v][r + 1]};
             }
         }
         __syncthreads();

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
             for (int e = tid; e < N * P; e += nt) {
                 int n = e / P, pp = e % P;
                 float acc = 0.f;
-                for (int j = 0; j < R; j++) acc += p.Bprev[ob + n * R + j] * p.xprev[ox + pp * R + j];
+                for (int j = 0; j < R; j++) acc += p.Bprev[ob + j * N + n] * p.xprev[ox + j * P + pp];
                 Hs[e] += d0 * acc;
             }
         }
@@ -129,10 +129,10 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
             float b0 = 0.f, b1 = 0.f, q0 = 0.f, q1 = 0.f, cs = 1.f, sn = 0.f;
             if (t < nq) {
                 int64_t ob = ((start + c0 + t) * G + g) * N * R;
-                b0 = p.B[ob + (2 * k) * R + j];
-                b1 = p.B[ob + (2 * k + 1) * R + j];
-                q0 = p.C[ob + (2 * k) * R + j];
-                q1 = p.C[ob + (2 * k + 1) * R + j];
+                b0 = p.B[ob + j * N + 2 * k];
+                b1 = p.B[ob + j * N + 2 * k + 1];
+                q0 = p.C[ob + j * N + 2 * k];
+                q1 = p.C[ob + j * N + 2 * k + 1];
                 sincosf(phi[t * K + k], &sn, &cs);
             }
             int r = t * R + j;
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
         }
         for (int e = tid; e < Q * P * R; e += nt) {
             int t = e / (P * R), pp = (e / R) % P, j = e % R;
-            float v = (t < nq) ? p.x[((start + c0 + t) * H + h) * P * R + pp * R + j] : 0.f;
+            float v = (t < nq) ? p.x[((start + c0 + t) * H + h) * P * R + j * P + pp] : 0.f;
             Xs[(t * R + j) * P + pp] = v;
         }
         __syncthreads();
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
             float acc = expf(S[tt]) * inter;
             for (int q = 0; q < (tt + 1) * R; q++) acc += M[r * QR + q] * Xs[q * P + pp];
             acc += Dh * Xs[r * P + pp];
-            p.y[((start + c0 + tt) * H + h) * P * R + pp * R + i] = acc;
+            p.y[((start + c0 + tt) * H + h) * P * R + i * P + pp] = acc;
         }
         __syncthreads();
         // carried state

@@ -6,14 +6,15 @@ exactly the arrays made here (bf16 values travel as their uint16 bit patterns),
 and the bench uses the device-side twin ``torch_scan_inputs``.
 
 Distributions (one head dim P, state dim N, rank R, B/C groups G):
-  x ~ N(0, 1)                       [b, L, H, P, R]
+  x ~ N(0, 1)                       [b, L, H, R, P]
   dt = softplus(N(-2, 0.5))         [b, L, H]        (step, post-activation)
   lam = sigmoid(N(0, 1))            [b, L, H]        (trapezoid weight)
   theta ~ U(-pi, pi)                [b, L, H, N/2]   (frequency; angle = dt*theta)
-  B, C ~ N(0, 1/N)                  [b, L, G, N, R]
+  B, C ~ N(0, 1/N)                  [b, L, G, R, N]
   A = -exp(N(0, 0.5))               [H]  fp32
   D ~ N(0, 1)                       [H]  fp32
-N(m, s) names mean and standard deviation. Arrays are drawn whole, in the
+N(m, s) names mean and standard deviation. Layouts are rank-major: the R
+columns of B_t, C_t (length N) and X_t (length P) are stored one after another. Arrays are drawn whole, in the
 order A, D, x, dt, lam, theta, B, C, then (decode only) state, Bprev, xprev,
 from numpy's PCG64 seeded with 1000 + config index unless a seed is given.
 Token inputs are rounded to bf16 (round to nearest even, via fp32) for the bf16
@@ -103,12 +104,12 @@ def scan_inputs(cfg: int | dict, seed: int | None = None, **over) -> dict:
     A = (-np.exp(_normal(rng, (H,), 0.0, 0.5).astype(np.float64))).astype(np.float32)
     D = _normal(rng, (H,)).astype(np.float32)
     out = dict(A=A, D=D)
-    out["x"] = _tok(_normal(rng, (b, L, H, P, R)), dt_)
+    out["x"] = _tok(_normal(rng, (b, L, H, R, P)), dt_)
     out["dt"] = _tok(_softplus(_normal(rng, (b, L, H), -2.0, 0.5)), dt_)
     out["lam"] = _tok(_sigmoid(_normal(rng, (b, L, H))), dt_)
     out["theta"] = _tok(rng.uniform(-math.pi, math.pi, size=(b, L, H, N // 2)).astype(np.float32), dt_)
-    out["B"] = _tok(_normal(rng, (b, L, G, N, R), 0.0, 1.0 / math.sqrt(N)), dt_)
-    out["C"] = _tok(_normal(rng, (b, L, G, N, R), 0.0, 1.0 / math.sqrt(N)), dt_)
+    out["B"] = _tok(_normal(rng, (b, L, G, R, N), 0.0, 1.0 / math.sqrt(N)), dt_)
+    out["C"] = _tok(_normal(rng, (b, L, G, R, N), 0.0, 1.0 / math.sqrt(N)), dt_)
     if c.get("packed"):
         if b != 1:
             raise ValueError("packed workloads have batch 1")
@@ -120,23 +121,23 @@ def scan_inputs(cfg: int | dict, seed: int | None = None, **over) -> dict:
 
 def resume_inputs(inp: dict, seed: int) -> dict:
     """Adds a state h_in [S,H,N,P] ~ N(0,1) fp32 and a previous token
-    (Bprev [S,G,N,R], xprev [S,H,P,R]) drawn like a token, for resume tests."""
+    (Bprev [S,G,R,N], xprev [S,H,R,P]) drawn like a token, for resume tests."""
     m = inp["meta"]
     rng = np.random.Generator(np.random.PCG64(seed))
     S = len(inp["cu_seqlens"]) - 1 if inp.get("cu_seqlens") is not None else m["batch"]
     H, P, N, R, G = m["nheads"], m["headdim"], m["dstate"], m["rank"], m["ngroups"]
     out = dict(inp)
     out["h_in"] = _normal(rng, (S, H, N, P)).astype(np.float32)
-    out["Bprev"] = _tok(_normal(rng, (S, G, N, R), 0.0, 1.0 / math.sqrt(N)), m["dtype"])
-    out["xprev"] = _tok(_normal(rng, (S, H, P, R)), m["dtype"])
+    out["Bprev"] = _tok(_normal(rng, (S, G, R, N), 0.0, 1.0 / math.sqrt(N)), m["dtype"])
+    out["xprev"] = _tok(_normal(rng, (S, H, R, P)), m["dtype"])
     return out
 
 
 def decode_inputs(cfg: int | dict = 3, seed: int | None = None, ring: int = 1, **over) -> dict:
     """Decode workload: ``ring`` token-input sets (each like one token of a
     scan, leading axis ring), a previous token, and an fp32 state ~ N(0,1).
-    Returns x [ring,b,H,P,R], dt/lam [ring,b,H], theta [ring,b,H,N/2],
-    B/C [ring,b,G,N,R], A, D, h [b,H,N,P], Bprev [b,G,N,R], xprev [b,H,P,R]."""
+    Returns x [ring,b,H,R,P], dt/lam [ring,b,H], theta [ring,b,H,N/2],
+    B/C [ring,b,G,R,N], A, D, h [b,H,N,P], Bprev [b,G,R,N], xprev [b,H,R,P]."""
     c = dict(CONFIGS[cfg]) if isinstance(cfg, int) else dict(cfg)
     c.update(over)
     if seed is None:
@@ -148,15 +149,15 @@ def decode_inputs(cfg: int | dict = 3, seed: int | None = None, ring: int = 1, *
     A = (-np.exp(_normal(rng, (H,), 0.0, 0.5).astype(np.float64))).astype(np.float32)
     D = _normal(rng, (H,)).astype(np.float32)
     out = dict(A=A, D=D)
-    out["x"] = _tok(_normal(rng, (ring, b, H, P, R)), dt_)
+    out["x"] = _tok(_normal(rng, (ring, b, H, R, P)), dt_)
     out["dt"] = _tok(_softplus(_normal(rng, (ring, b, H), -2.0, 0.5)), dt_)
     out["lam"] = _tok(_sigmoid(_normal(rng, (ring, b, H))), dt_)
     out["theta"] = _tok(rng.uniform(-math.pi, math.pi, size=(ring, b, H, N // 2)).astype(np.float32), dt_)
-    out["B"] = _tok(_normal(rng, (ring, b, G, N, R), 0.0, 1.0 / math.sqrt(N)), dt_)
-    out["C"] = _tok(_normal(rng, (ring, b, G, N, R), 0.0, 1.0 / math.sqrt(N)), dt_)
+    out["B"] = _tok(_normal(rng, (ring, b, G, R, N), 0.0, 1.0 / math.sqrt(N)), dt_)
+    out["C"] = _tok(_normal(rng, (ring, b, G, R, N), 0.0, 1.0 / math.sqrt(N)), dt_)
     out["h"] = _normal(rng, (b, H, N, P)).astype(np.float32)
-    out["Bprev"] = _tok(_normal(rng, (b, G, N, R), 0.0, 1.0 / math.sqrt(N)), dt_)
-    out["xprev"] = _tok(_normal(rng, (b, H, P, R)), dt_)
+    out["Bprev"] = _tok(_normal(rng, (b, G, R, N), 0.0, 1.0 / math.sqrt(N)), dt_)
+    out["xprev"] = _tok(_normal(rng, (b, H, R, P)), dt_)
     out["meta"] = dict(c, ngroups=G, seed=seed)
     return out
 
@@ -178,12 +179,12 @@ def torch_scan_inputs(cfg: int | dict, device, seed: int = 0, **over) -> dict:
         return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std + mean
 
     out = dict(A=-torch.exp(nrm((H,), 0.0, 0.5)), D=nrm((H,)))
-    out["x"] = nrm((b, L, H, P, R)).to(td)
+    out["x"] = nrm((b, L, H, R, P)).to(td)
     out["dt"] = torch.nn.functional.softplus(nrm((b, L, H), -2.0, 0.5)).to(td)
     out["lam"] = torch.sigmoid(nrm((b, L, H))).to(td)
     out["theta"] = ((torch.rand((b, L, H, N // 2), generator=g, device=device) * 2 - 1) * math.pi).to(td)
-    out["B"] = nrm((b, L, G, N, R), 0.0, 1.0 / math.sqrt(N)).to(td)
-    out["C"] = nrm((b, L, G, N, R), 0.0, 1.0 / math.sqrt(N)).to(td)
+    out["B"] = nrm((b, L, G, R, N), 0.0, 1.0 / math.sqrt(N)).to(td)
+    out["C"] = nrm((b, L, G, R, N), 0.0, 1.0 / math.sqrt(N)).to(td)
     if c.get("packed"):
         rng = np.random.Generator(np.random.PCG64(1000 + seed))
         ln = packed_lengths(rng, c["nseq"], L, c["len_lo"], c["len_hi"])

@@ -19,14 +19,14 @@ MUTATIONS = {
     "prev_not_rotated": ("hc[k * P + p] = z[k] * (hc[k * P + p] + delta * prev) + gamma * cur;",
                          "hc[k * P + p] = z[k] * hc[k * P + p] + delta * prev + gamma * cur;"),
     "rotation_sign": ("z[k] = decay * (cos(ang) + I * sin(ang));", "z[k] = decay * (cos(ang) - I * sin(ang));"),
-    "c_imag_sign": ("cc[k * R + j] = ld(a->C, dtp, ob + (2 * k) * R + j) -",
-                    "cc[k * R + j] = ld(a->C, dtp, ob + (2 * k) * R + j) +"),
-    "b_imag_sign": ("I * ld(a->B, dtp, ob + (2 * k + 1) * R + j);\n                cc",
-                    "-I * ld(a->B, dtp, ob + (2 * k + 1) * R + j);\n                cc"),
+    "c_imag_sign": ("cc[k * R + j] = ld(a->C, dtp, ob + j * N + 2 * k) -",
+                    "cc[k * R + j] = ld(a->C, dtp, ob + j * N + 2 * k) +"),
+    "b_imag_sign": ("I * ld(a->B, dtp, ob + j * N + 2 * k + 1);\n                cc",
+                    "-I * ld(a->B, dtp, ob + j * N + 2 * k + 1);\n                cc"),
     "weights_swapped": ("const double delta = (1.0 - lam) * dt, gamma = lam * dt;",
                         "const double gamma = (1.0 - lam) * dt, delta = lam * dt;"),
     "rank_mixed": ("cur += bc[k * R + j] * xc[p * R + j];", "cur += bc[k * R + j] * xc[p * R + 0];"),
-    "no_skip_term": ("yt[p * R + i] = creal(acc) + Dh * xc[p * R + i];", "yt[p * R + i] = creal(acc);"),
+    "no_skip_term": ("yt[i * P + p] = creal(acc) + Dh * xc[p * R + i];", "yt[i * P + p] = creal(acc);"),
     "stale_previous": ("memcpy(bp, bc, (size_t)K * R * sizeof *bp);\n        memcpy(xp, xc, (size_t)P * R * sizeof *xp);\n",
                        ""),
 }

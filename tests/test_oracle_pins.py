@@ -19,20 +19,20 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 def rand_inputs(rng, b=2, L=17, H=4, G=2, P=3, N=6, R=2, state=False, prev=False, scale_theta=1.0):
     """Generic float64 inputs (wider ranges than the workloads on purpose)."""
     inp = dict(
-        x=rng.standard_normal((b, L, H, P, R)),
+        x=rng.standard_normal((b, L, H, R, P)),
         dt=np.log1p(np.exp(rng.normal(-1.5, 0.6, (b, L, H)))),
         lam=1 / (1 + np.exp(-rng.standard_normal((b, L, H)))),
         theta=rng.uniform(-math.pi, math.pi, (b, L, H, N // 2)) * scale_theta,
-        B=rng.standard_normal((b, L, G, N, R)) / math.sqrt(N),
-        C=rng.standard_normal((b, L, G, N, R)) / math.sqrt(N),
+        B=rng.standard_normal((b, L, G, R, N)) / math.sqrt(N),
+        C=rng.standard_normal((b, L, G, R, N)) / math.sqrt(N),
         A=-np.exp(rng.normal(0, 0.5, H)),
         D=rng.standard_normal(H),
     )
     if state:
         inp["h_in"] = rng.standard_normal((b, H, N, P))
     if prev:
-        inp["Bprev"] = rng.standard_normal((b, G, N, R)) / math.sqrt(N)
-        inp["xprev"] = rng.standard_normal((b, H, P, R))
+        inp["Bprev"] = rng.standard_normal((b, G, R, N)) / math.sqrt(N)
+        inp["xprev"] = rng.standard_normal((b, H, R, P))
     return inp
 
 
@@ -78,8 +78,8 @@ def _real_trapezoid(inp, use_rotation):
     rotation matrices on the state pairs (Proposition 2's block-diagonal R_t),
     written with numpy matrices rather than complex numbers."""
     x, dt, lam, th, B, C, A, D = (inp[k] for k in ("x", "dt", "lam", "theta", "B", "C", "A", "D"))
-    b, L, H, P, R = x.shape
-    G, N = B.shape[2], B.shape[3]
+    b, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
     y = np.zeros_like(x)
     for s in range(b):
         for h in range(H):
@@ -94,10 +94,10 @@ def _real_trapezoid(inp, use_rotation):
                 for k in range(N // 2):
                     a = dt[s, t, h] * th[s, t, h, k] if use_rotation else 0.0
                     Rt[2 * k:2 * k + 2, 2 * k:2 * k + 2] = [[math.cos(a), -math.sin(a)], [math.sin(a), math.cos(a)]]
-                cur = B[s, t, g] @ x[s, t, h].T
+                cur = B[s, t, g].T @ x[s, t, h]                     # sum_r B^(r) x^(r)T
                 st = alpha * (Rt @ st) + beta * (Rt @ prev) + gamma * cur
                 prev = cur
-                y[s, t, h] = st.T @ C[s, t, g] + D[h] * x[s, t, h]
+                y[s, t, h] = C[s, t, g] @ st + D[h] * x[s, t, h]    # [R, P] = (H^T C)^T
     return y
 
 
@@ -136,11 +136,11 @@ def test_lambda_one_is_exponential_euler(oracle):
     h = inp["h_in"][0, 0, 0::2] + 1j * inp["h_in"][0, 0, 1::2]          # [K,P]
     for t in range(x.shape[1]):
         z = np.exp(dt[0, t, 0] * (A[0] + 1j * th[0, t, 0]))               # [K]
-        b = B[0, t, 0, 0::2, 0] + 1j * B[0, t, 0, 1::2, 0]
-        c = C[0, t, 0, 0::2, 0] - 1j * C[0, t, 0, 1::2, 0]
-        h = z[:, None] * h + dt[0, t, 0] * np.outer(b, x[0, t, 0, :, 0])
-        yt = (c @ h).real + D[0] * x[0, t, 0, :, 0]
-        assert np.allclose(y1[0, t, 0, :, 0], yt, rtol=1e-12, atol=1e-13)
+        b = B[0, t, 0, 0, 0::2] + 1j * B[0, t, 0, 0, 1::2]
+        c = C[0, t, 0, 0, 0::2] - 1j * C[0, t, 0, 0, 1::2]
+        h = z[:, None] * h + dt[0, t, 0] * np.outer(b, x[0, t, 0, 0, :])
+        yt = (c @ h).real + D[0] * x[0, t, 0, 0, :]
+        assert np.allclose(y1[0, t, 0, 0, :], yt, rtol=1e-12, atol=1e-13)
     hr = np.empty((4, 2))
     hr[0::2], hr[1::2] = h.real, h.imag
     assert relerr(h1[0, 0], hr) < 1e-12
@@ -169,11 +169,11 @@ def _discrete_lti(oracle, lam_val, n, Ac, bc, cc, h0, omega, T):
         dt=np.full((1, n, 1), dt),
         lam=np.full((1, n, 1), lam_val),
         theta=np.full((1, n, 1, 1), th),
-        B=np.tile(np.array([bc.real, bc.imag]).reshape(1, 1, 1, 2, 1), (1, n, 1, 1, 1)),
-        C=np.tile(np.array([cc.real, -cc.imag]).reshape(1, 1, 1, 2, 1), (1, n, 1, 1, 1)),
+        B=np.tile(np.array([bc.real, bc.imag]).reshape(1, 1, 1, 1, 2), (1, n, 1, 1, 1)),
+        C=np.tile(np.array([cc.real, -cc.imag]).reshape(1, 1, 1, 1, 2), (1, n, 1, 1, 1)),
         A=np.array([A]), D=np.zeros(1),
         h_in=np.array([h0.real, h0.imag]).reshape(1, 1, 2, 1),
-        Bprev=np.array([bc.real, bc.imag]).reshape(1, 1, 2, 1),
+        Bprev=np.array([bc.real, bc.imag]).reshape(1, 1, 1, 2),
         xprev=np.ones((1, 1, 1, 1)),
     )
     y, h = oracle.scan(inp, form=1)
@@ -214,7 +214,7 @@ def test_parity_worked_example(oracle):
     inp = dict(
         x=np.ones((1, n, 1, 1, 1)), dt=np.ones((1, n, 1)), lam=np.full((1, n, 1), 0.5),
         theta=(math.pi * bits).reshape(1, n, 1, 1),
-        B=np.zeros((1, n, 1, 2, 1)), C=np.tile(np.array([1.0, 0.0]).reshape(1, 1, 1, 2, 1), (1, n, 1, 1, 1)),
+        B=np.zeros((1, n, 1, 1, 2)), C=np.tile(np.array([1.0, 0.0]).reshape(1, 1, 1, 1, 2), (1, n, 1, 1, 1)),
         A=np.zeros(1), D=np.zeros(1), h_in=np.array([1.0, 0.0]).reshape(1, 1, 2, 1),
     )
     y, _ = oracle.scan(inp, form=1)
@@ -237,14 +237,14 @@ def test_mimo_is_sum_of_siso(oracle):
     for j in range(R):
         for i in range(R):
             siso = dict(inp)
-            siso["x"] = inp["x"][..., j:j + 1]
-            siso["B"] = inp["B"][..., j:j + 1]
-            siso["C"] = inp["C"][..., i:i + 1]
-            siso["Bprev"] = inp["Bprev"][..., j:j + 1]
-            siso["xprev"] = inp["xprev"][..., j:j + 1]
+            siso["x"] = inp["x"][..., j:j + 1, :]
+            siso["B"] = inp["B"][..., j:j + 1, :]
+            siso["C"] = inp["C"][..., i:i + 1, :]
+            siso["Bprev"] = inp["Bprev"][..., j:j + 1, :]
+            siso["xprev"] = inp["xprev"][..., j:j + 1, :]
             siso["h_in"] = inp["h_in"] if j == 0 else np.zeros_like(inp["h_in"])
             ys, hs = oracle.scan(siso, form=1)
-            ysum[..., i] += ys[..., 0]
+            ysum[..., i, :] += ys[..., 0, :]
             if i == 0:
                 hsum += hs
     assert relerr(ysum, y) < 1e-12
@@ -259,13 +259,13 @@ def test_constant_inputs_closed_form(oracle):
     P, N, R = 2, 4, 2
     dt, lam, A, D = 0.3, 0.35, -0.8, 0.7
     th = rng.uniform(-3, 3, N // 2)
-    Bv = rng.standard_normal((N, R))
-    Cv = rng.standard_normal((N, R))
-    xv = rng.standard_normal((P, R))
-    b = Bv[0::2] + 1j * Bv[1::2]
-    c = Cv[0::2] - 1j * Cv[1::2]
+    Bv = rng.standard_normal((R, N))                                        # rank-major columns
+    Cv = rng.standard_normal((R, N))
+    xv = rng.standard_normal((R, P))
+    b = (Bv[:, 0::2] + 1j * Bv[:, 1::2]).T                                  # [K,R]
+    c = (Cv[:, 0::2] - 1j * Cv[:, 1::2]).T
     z = np.exp(dt * (A + 1j * th))
-    v = b @ xv.T                                                            # [K,P]
+    v = b @ xv                                                              # [K,P]
     delta, gamma = (1 - lam) * dt, lam * dt
     hstar = ((delta * z + gamma)[:, None] * v) / (1 - z)[:, None]
     for L in (1, 2, 5, 37):
@@ -276,7 +276,7 @@ def test_constant_inputs_closed_form(oracle):
         ht = hstar + (z ** (L - 1))[:, None] * (gamma * v - hstar)
         hc = h[0, 0, 0::2] + 1j * h[0, 0, 1::2]
         assert np.allclose(hc, ht, rtol=1e-12, atol=1e-12)
-        yt = (c.T @ ht).real.T + D * xv                                     # [P,R]
+        yt = (c.T @ ht).real + D * xv                                       # [R,P]
         assert np.allclose(y[0, -1, 0], yt, rtol=1e-12, atol=1e-12)
 
 

@@ -23,8 +23,8 @@ def test_determinism_and_shapes():
     b = synth.scan_inputs(2, batch=1, seqlen=16, nheads=2)
     for k in ("x", "dt", "lam", "theta", "B", "C", "A", "D"):
         assert np.array_equal(a[k], b[k])
-    assert a["x"].shape == (1, 16, 2, 64, 4) and a["x"].dtype == np.uint16
-    assert a["B"].shape == (1, 16, 2, 64, 4)
+    assert a["x"].shape == (1, 16, 2, 4, 64) and a["x"].dtype == np.uint16
+    assert a["B"].shape == (1, 16, 2, 4, 64)
     assert a["theta"].shape == (1, 16, 2, 32)
     c = synth.scan_inputs(2, seed=7, batch=1, seqlen=16, nheads=2)
     assert not np.array_equal(a["x"], c["x"])
