@@ -117,7 +117,7 @@ template <int N_, int P_, int R_, int Q_, int NW_, int UT_>
 struct Cfg {
     static constexpr int N = N_, P = P_, R = R_, Q = Q_, NW = NW_, UT = UT_;
     static constexpr int K = N / 2, QR = Q * R;
-    static constexpr int NTB = QR / 16;                     // 16-row t-blocks
+    static constexpr int NTB = QR / 16, NSB = QR / 32;      // 16-row t-blocks, 32-row s-blocks
     static constexpr int TOKT = 16 / R, TOKS = 32 / R;      // tokens per t-block / s-block
     static constexpr int NTHR = NW * 64, TPW = NTB / NW;
     static constexpr int NKK = N / 32;                      // K-steps over N (16x16x32)
@@ -129,6 +129,7 @@ struct Cfg {
     static_assert(NTB % NW == 0 && (TPW == 1 || TPW % 2 == 0), "t-block split");
     static_assert(NUT % NW == 0 && (UT == 16 || UT == 32), "state tile split");
     static_assert(K % 8 == 0 && Q % NW == 0 && Q <= 128 && Q < NTHR, "prologue");
+    static_assert(NSB % 2 == 0, "full chunks alternate the two prefetch register sets");
     // LDS layout (bytes)
     static constexpr int OFF_PHI = 0;                                  // float [Q][K] -> f16x2 (cos, sin)
     static constexpr int OFF_PHE = OFF_PHI + Q * K * 4;                // float [K] chunk's total angle
@@ -255,38 +256,44 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
     bf16x8 h_th[CF::NTH];
     float h_thdt[CF::NTH];
     bf16x8 h_c[TPW][NKK];
-    auto load_header = [&](int64_t c0h) {
-        const int nqh = (int)min((int64_t)Q, len - c0h);
-        const int64_t t0h = start + c0h;
-        h_dt = 0.f;
-        h_lam = 0.f;
-        if (tid < nqh) {
-            h_dt = to_f(pr.dt[(t0h + tid) * H + h]);
-            h_lam = to_f(pr.lam[(t0h + tid) * H + h]);
-        } else if (tid == Q && c0h + nqh < len) {
-            h_dt = to_f(pr.dt[(t0h + nqh) * H + h]);
-            h_lam = to_f(pr.lam[(t0h + nqh) * H + h]);
+    // All prefetch loads are unconditional (clamped to a valid token, invalid
+    // results replaced by zero) so the compiler sees a fixed sequence of memory
+    // operations and waits only for the loads each use needs.
+    auto load_header = [&](int64_t c0h) {   // c0h >= len: dummy loads, zero results
+        const bool any = c0h < len;
+        const int64_t c0c = any ? c0h : 0;
+        const int nqh = (int)min((int64_t)Q, len - c0c);
+        const int64_t t0h = start + c0c, last = len - c0c - 1;
+        {
+            const int idx = (tid < Q) ? tid : nqh;                 // thread Q: the token after the chunk
+            const bool valid = any && ((tid < nqh) || (tid == Q && c0h + nqh < len));
+            const int64_t tk = t0h + min((int64_t)idx, last);
+            const float dv = to_f(pr.dt[tk * H + h]), lv = to_f(pr.lam[tk * H + h]);
+            h_dt = valid ? dv : 0.f;
+            h_lam = valid ? lv : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < CF::NTH; i++) {
-            const int e = tid + i * NTHR;
+            const int e = min(tid + i * NTHR, Q * K / 8 - 1);
             const int tau = e / (K / 8), k0 = (e % (K / 8)) * 8;
-            h_th[i] = bf16x8{};
-            h_thdt[i] = 0.f;
-            if (e < Q * K / 8 && tau < nqh) {
-                h_thdt[i] = to_f(pr.dt[(t0h + tau) * H + h]);
-                h_th[i] = *(const bf16x8 *)(gTh + (t0h + tau) * strTh + k0);
-            }
+            const bool valid = any && tau < nqh && tid + i * NTHR < Q * K / 8;
+            const int64_t tk = t0h + min((int64_t)tau, last);
+            const float dv = to_f(pr.dt[tk * H + h]);
+            const bf16x8 th = *(const bf16x8 *)(gTh + tk * strTh + k0);
+            h_thdt[i] = valid ? dv : 0.f;
+            h_th[i] = valid ? th : bf16x8{};
         }
         // C rows of the own t-blocks in operand layout: row 16 tb + l16, columns 32 kk + 8 q4 ..
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
             const int row = task_tb[u] * 16 + l16;
             const int tau = row / R, j = row % R;
+            const bool valid = any && tau < nqh;
+            const int64_t tk = t0h + min((int64_t)tau, last);
 #pragma unroll
             for (int kk = 0; kk < NKK; kk++) {
-                h_c[u][kk] = bf16x8{};
-                if (tau < nqh) h_c[u][kk] = *(const bf16x8 *)(gC + (t0h + tau) * strBC + j * N + 32 * kk + 8 * q4);
+                const bf16x8 v = *(const bf16x8 *)(gC + tk * strBC + j * N + 32 * kk + 8 * q4);
+                h_c[u][kk] = valid ? v : bf16x8{};
             }
         }
     };
@@ -294,27 +301,27 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
     // ---- s-block stream: block j of the sequence lives in register set j % 2
     bf16x8 rb0[CF::NLB], rx0[CF::NLX], rb1[CF::NLB], rx1[CF::NLX];
     auto load_block_into = [&](bf16x8 (&rb)[CF::NLB], bf16x8 (&rx)[CF::NLX], int64_t c0b, int sb) {
-        const int nqb = (int)min((int64_t)Q, len - c0b);
-        const int64_t t0b = start + c0b;
+        const bool any = c0b < len;                                // past the end: dummy loads
+        const int64_t c0c = any ? c0b : 0;
+        const int nqb = (int)min((int64_t)Q, len - c0c);
+        const int64_t t0b = start + c0c, last = len - c0c - 1;
 #pragma unroll
         for (int i = 0; i < CF::NLB; i++) {
-            const int c = tid + i * NTHR;
-            rb[i] = bf16x8{};
-            if (c < CF::BCH) {
-                const int row = c / (N / 8), col = (c % (N / 8)) * 8;
-                const int tau = sb * TOKS + row / R;
-                if (tau < nqb) rb[i] = *(const bf16x8 *)(gB + (t0b + tau) * strBC + (row % R) * N + col);
-            }
+            const int c = (tid + i * NTHR) % CF::BCH;
+            const int row = c / (N / 8), col = (c % (N / 8)) * 8;
+            const int tau = sb * TOKS + row / R;
+            const int64_t tk = t0b + min((int64_t)tau, last);
+            const bf16x8 v = *(const bf16x8 *)(gB + tk * strBC + (row % R) * N + col);
+            rb[i] = (any && tau < nqb) ? v : bf16x8{};
         }
 #pragma unroll
         for (int i = 0; i < CF::NLX; i++) {
-            const int c = tid + i * NTHR;
-            rx[i] = bf16x8{};
-            if (c < CF::XCH) {
-                const int row = c / (P / 8), col = (c % (P / 8)) * 8;
-                const int tau = sb * TOKS + row / R;
-                if (tau < nqb) rx[i] = *(const bf16x8 *)(gX + (t0b + tau) * strX + (row % R) * P + col);
-            }
+            const int c = (tid + i * NTHR) % CF::XCH;
+            const int row = c / (P / 8), col = (c % (P / 8)) * 8;
+            const int tau = sb * TOKS + row / R;
+            const int64_t tk = t0b + min((int64_t)tau, last);
+            const bf16x8 v = *(const bf16x8 *)(gX + tk * strX + (row % R) * P + col);
+            rx[i] = (any && tau < nqb) ? v : bf16x8{};
         }
     };
     auto advance = [&](int64_t &c0b, int &sb) {
@@ -333,14 +340,18 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
         load_header(0);
         load_block_into(rb0, rx0, ld_c0, ld_sb);
         advance(ld_c0, ld_sb);
-        if (ld_c0 < len) load_block_into(rb1, rx1, ld_c0, ld_sb);
+        load_block_into(rb1, rx1, ld_c0, ld_sb);
         advance(ld_c0, ld_sb);
     }
-    int par = 0;   // parity of the next block to stage
     __syncthreads();
 
-    for (int64_t c0 = 0; c0 < len; c0 += Q) {
-        const int nq = (int)min((int64_t)Q, len - c0);
+    // One chunk. Full chunks (Q tokens) have a compile-time number of s-blocks
+    // (NSB, even), so block j of the sequence always sits in register set j % 2
+    // and the sweep is fully unrolled; the final partial chunk runs the same
+    // steps under a runtime bound.
+    auto chunk_body = [&](auto FULLC, int64_t c0) {
+        constexpr bool FULL = decltype(FULLC)::value;
+        const int nq = FULL ? Q : (int)(len - c0);
         const int64_t tok0 = start + c0;
 
         // ---- prologue 1: per-token scalars and raw angles dt*theta
@@ -467,10 +478,10 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
                 for (int r = 0; r < UR_; r++) hreg[v][r] *= eS;
         }
         // the header registers are consumed: prefetch the next chunk's header now
-        if (c0 + Q < len) load_header(c0 + Q);
+        load_header(c0 + Q);
 
         // ---- s-block sweep
-        const int nbs = (nq + TOKS - 1) / TOKS;   // s-blocks holding valid tokens
+        const int nbs = FULL ? CF::NSB : (nq + TOKS - 1) / TOKS;   // s-blocks holding valid tokens
         auto store_block = [&](const bf16x8 (&rawB)[CF::NLB], const bf16x8 (&rawX)[CF::NLX], int sb, int buf) {
             char *stg = UR + buf * CF::STAGE;
             bf16 *bt = (bf16 *)(stg + CF::SB_BT);   // [32 rows][NS]  rotated B~
@@ -561,22 +572,33 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
             }
         };
 
-        if (par) store_block(rb1, rx1, 0, 0);
-        else store_block(rb0, rx0, 0, 0);
-        __syncthreads();
-        for (int sb = 0; sb < nbs; sb++) {
-            if (par) {
-                if (ld_c0 < len) load_block_into(rb1, rx1, ld_c0, ld_sb);
-                compute_block(sb);
-                if (sb + 1 < nbs) store_block(rb0, rx0, sb + 1, (sb + 1) & 1);
-            } else {
-                if (ld_c0 < len) load_block_into(rb0, rx0, ld_c0, ld_sb);
-                compute_block(sb);
-                if (sb + 1 < nbs) store_block(rb1, rx1, sb + 1, (sb + 1) & 1);
-            }
+        // block sb of this chunk: set sb % 2 receives block sb + 2 of the stream, then the
+        // block is computed and block sb + 1 is staged from the other set
+        auto step = [&](auto SETC, int sb) {
+            constexpr int ST = decltype(SETC)::value;
+            if constexpr (ST == 0) load_block_into(rb0, rx0, ld_c0, ld_sb);
+            else load_block_into(rb1, rx1, ld_c0, ld_sb);
             advance(ld_c0, ld_sb);
-            par ^= 1;
+            compute_block(sb);
+            if (sb + 1 < nbs) {
+                if constexpr (ST == 0) store_block(rb1, rx1, sb + 1, (sb + 1) & 1);
+                else store_block(rb0, rx0, sb + 1, (sb + 1) & 1);
+            }
             __syncthreads();
+        };
+        store_block(rb0, rx0, 0, 0);
+        __syncthreads();
+        if constexpr (FULL) {
+#pragma unroll
+            for (int sb = 0; sb < CF::NSB; sb += 2) {
+                step(std::integral_constant<int, 0>{}, sb);
+                step(std::integral_constant<int, 1>{}, sb + 1);
+            }
+        } else {
+            for (int sb = 0; sb < nbs; sb += 2) {
+                step(std::integral_constant<int, 0>{}, sb);
+                if (sb + 1 < nbs) step(std::integral_constant<int, 1>{}, sb + 1);
+            }
         }
 
         // ---- epilogue: outputs through a per-wave LDS transpose, 16-byte row stores
@@ -594,7 +616,7 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
                 for (int c = lane; c < 16 * P / 8; c += 64) {
                     const int row = c / (P / 8), col = (c % (P / 8)) * 8;
                     const int rr = tb * 16 + row, tau = rr / R;
-                    if (tau < nq) *(bf16x8 *)(gY + (tok0 + tau) * strX + (rr % R) * P + col) =
+                    if (FULL || tau < nq) *(bf16x8 *)(gY + (tok0 + tau) * strX + (rr % R) * P + col) =
                         *(const bf16x8 *)(ys + row * PS + col);
                 }
                 lds_wait();
@@ -616,7 +638,11 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
             }
         }
         __syncthreads();
-    }
+    };
+
+    int64_t c0 = 0;
+    for (; c0 + Q <= len; c0 += Q) chunk_body(std::true_type{}, c0);
+    if (c0 < len) chunk_body(std::false_type{}, c0);
 
     if (pr.h_out) {
         const int64_t so = ((int64_t)s * H + h) * N * P;
