@@ -125,6 +125,7 @@ struct Cfg {
     static constexpr int NUT = (N / UT) * (P / UT), UPW = NUT / NW;
     static constexpr int UR_ = (UT == 32) ? 16 : 4;         // state registers per tile
     static constexpr int NS = N + 8, PS = P + 8;            // padded bf16 row strides
+    static constexpr bool PFC = TPW <= 2;                   // prefetch the next chunk's C rows
     static_assert(N % 32 == 0 && P % 32 == 0 && (R == 1 || R == 2 || R == 4) && QR % 32 == 0, "shape");
     static_assert(NTB % NW == 0 && (TPW == 1 || TPW % 2 == 0), "t-block split");
     static_assert(NUT % NW == 0 && (UT == 16 || UT == 32), "state tile split");
@@ -132,14 +133,16 @@ struct Cfg {
     static_assert(NSB % 2 == 0, "full chunks alternate the two prefetch register sets");
     // LDS layout (bytes)
     static constexpr int OFF_PHI = 0;                                  // float [Q][K] -> f16x2 (cos, sin)
-    static constexpr int OFF_PHE = OFF_PHI + Q * K * 4;                // float [K] chunk's total angle
-    static constexpr int OFF_S2 = OFF_PHE + K * 4;                     // float [Q] log2 decay prefix
+    static constexpr int OFF_PHC = OFF_PHI + Q * K * 4;                // float2 [K] (cos, sin) of the chunk's total angle
+    static constexpr int OFF_S2 = OFF_PHC + K * 8;                     // float [Q] log2 decay prefix
     static constexpr int OFF_A2 = OFF_S2 + Q * 4;                      // float [Q] per-token log2 decay
     static constexpr int OFF_GM = OFF_A2 + Q * 4;                      // float [Q] gamma
     static constexpr int OFF_DL = OFF_GM + Q * 4;                      // float [Q] delta
     static constexpr int OFF_G1 = OFF_DL + Q * 4;                      // float [Q] gamma_s + delta_{s+1}
     static constexpr int OFF_WU = OFF_G1 + Q * 4;                      // float [Q] chunk-state weights
-    static constexpr int OFF_TOT = OFF_WU + Q * 4;                     // float [NW][K] angle segment sums
+    static constexpr int OFF_F1 = OFF_WU + Q * 4;                      // float [Q] column mask factors, s < t
+    static constexpr int OFF_F0 = OFF_F1 + Q * 4;                      // float [Q] column mask factors, s = t
+    static constexpr int OFF_TOT = OFF_F0 + Q * 4;                     // float [NW][K] angle segment sums
     static constexpr int OFF_MISC = OFF_TOT + NW * K * 4;              // float [4]
     static constexpr int OFF_HB = (OFF_MISC + 16 + 15) / 16 * 16;      // bf16 [P][NS] carried state
     static constexpr int OFF_U = OFF_HB + P * NS * 2;                  // stage buffers / output staging
@@ -156,7 +159,7 @@ struct Cfg {
 };
 
 template <class CF>
-__global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
+__global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) void k_scan_bf16(BfParams pr) {
     constexpr int N = CF::N, P = CF::P, R = CF::R, Q = CF::Q, NW = CF::NW, K = CF::K, UT = CF::UT;
     constexpr int TOKT = CF::TOKT, TOKS = CF::TOKS, NTHR = CF::NTHR, TPW = CF::TPW;
     constexpr int NKK = CF::NKK, NPT = CF::NPT, UPW = CF::UPW, NS = CF::NS, PS = CF::PS, UR_ = CF::UR_;
@@ -164,19 +167,22 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float *phi = (float *)(smem + CF::OFF_PHI);
     const f16x2 *cst = (const f16x2 *)(smem + CF::OFF_PHI);   // after the prologue: (cos, sin) table
-    float *PHE = (float *)(smem + CF::OFF_PHE);
+    float2 *PHC = (float2 *)(smem + CF::OFF_PHC);
     float *S2 = (float *)(smem + CF::OFF_S2);
     float *A2 = (float *)(smem + CF::OFF_A2);
     float *GM = (float *)(smem + CF::OFF_GM);
     float *DL = (float *)(smem + CF::OFF_DL);
     float *G1 = (float *)(smem + CF::OFF_G1);
     float *WU = (float *)(smem + CF::OFF_WU);
+    float *F1 = (float *)(smem + CF::OFF_F1);
+    float *F0 = (float *)(smem + CF::OFF_F0);
     float *TOT = (float *)(smem + CF::OFF_TOT);
     float *MISC = (float *)(smem + CF::OFF_MISC);
     bf16 *HB = (bf16 *)(smem + CF::OFF_HB);
     char *UR = smem + CF::OFF_U;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps per-wave branches scalar
     const int l16 = lane & 15, q4 = lane >> 4, l32 = lane & 31, hi = lane >> 5;
     const int H = pr.H, G = pr.G;
     const int s = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
@@ -259,6 +265,25 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
     // All prefetch loads are unconditional (clamped to a valid token, invalid
     // results replaced by zero) so the compiler sees a fixed sequence of memory
     // operations and waits only for the loads each use needs.
+    // C rows of the own t-blocks in operand layout: row 16 tb + l16, columns 32 kk + 8 q4 ..
+    auto load_crows = [&](int64_t c0h) {
+        const bool any = c0h < len;
+        const int64_t c0c = any ? c0h : 0;
+        const int nqh = (int)min((int64_t)Q, len - c0c);
+        const int64_t t0h = start + c0c, last = len - c0c - 1;
+#pragma unroll
+        for (int u = 0; u < TPW; u++) {
+            const int row = task_tb[u] * 16 + l16;
+            const int tau = row / R, j = row % R;
+            const bool valid = any && tau < nqh;
+            const int64_t tk = t0h + min((int64_t)tau, last);
+#pragma unroll
+            for (int kk = 0; kk < NKK; kk++) {
+                const bf16x8 v = *(const bf16x8 *)(gC + tk * strBC + j * N + 32 * kk + 8 * q4);
+                h_c[u][kk] = valid ? v : bf16x8{};
+            }
+        }
+    };
     auto load_header = [&](int64_t c0h) {   // c0h >= len: dummy loads, zero results
         const bool any = c0h < len;
         const int64_t c0c = any ? c0h : 0;
@@ -283,19 +308,7 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
             h_thdt[i] = valid ? dv : 0.f;
             h_th[i] = valid ? th : bf16x8{};
         }
-        // C rows of the own t-blocks in operand layout: row 16 tb + l16, columns 32 kk + 8 q4 ..
-#pragma unroll
-        for (int u = 0; u < TPW; u++) {
-            const int row = task_tb[u] * 16 + l16;
-            const int tau = row / R, j = row % R;
-            const bool valid = any && tau < nqh;
-            const int64_t tk = t0h + min((int64_t)tau, last);
-#pragma unroll
-            for (int kk = 0; kk < NKK; kk++) {
-                const bf16x8 v = *(const bf16x8 *)(gC + tk * strBC + j * N + 32 * kk + 8 * q4);
-                h_c[u][kk] = valid ? v : bf16x8{};
-            }
-        }
+        if constexpr (CF::PFC) load_crows(c0h);
     };
 
     // ---- s-block stream: block j of the sequence lives in register set j % 2
@@ -415,9 +428,17 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
                     const float g1 = GM[t] + next;
                     G1[t] = g1;
                     WU[t] = (t < nq) ? exp2_neg(S2e - S2[t]) * g1 : 0.f;
+                    // mask factor relative to the first token of the t's s-block (>= 1)
+                    const float f = __builtin_amdgcn_exp2f(S2[(t / TOKS) * TOKS] - S2[t]);
+                    F1[t] = f * g1;
+                    F0[t] = f * GM[t];
                 }
             }
-            if (lane == 0) MISC[1] = S2e;
+            if (lane == 0) {
+                MISC[1] = S2e;
+                // the factored mask is used when every factor stays far inside the fp32 range
+                MISC[2] = (S2[0] - S2[Q - 1] <= 120.f) ? 1.f : 0.f;
+            }
         }
         __syncthreads();
         // ---- prologue 3: carry the segment sums, keep the total angle, turn angles into (cos, sin)
@@ -428,7 +449,11 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
             for (int t = 0; t < SEG; t++) {
                 const int tau = wave * SEG + t;
                 const float a = phi[tau * K + lane] + carry;
-                if (tau == Q - 1) PHE[lane] = a;   // angles past the end are zero: Phi[Q-1] = Phi[nq-1]
+                if (tau == Q - 1) {                // angles past the end are zero: Phi[Q-1] = Phi[nq-1]
+                    float sn, cs;
+                    sincosf(a, &sn, &cs);
+                    PHC[lane] = float2{cs, sn};
+                }
                 float sn, cs;
                 __sincosf(a, &sn, &cs);
                 ((f16x2 *)phi)[tau * K + lane] = f16x2{(_Float16)cs, (_Float16)sn};
@@ -436,7 +461,8 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
         }
         __syncthreads();
 
-        // ---- rotated C~ rows of this wave's t-blocks, straight from the header registers
+        // ---- rotated C~ rows of this wave's t-blocks, from the prefetched (or just loaded) raw rows
+        if constexpr (!CF::PFC) load_crows(c0);
         bf16x8 creg[TPW][NKK];
         f32x4 yacc[TPW][NPT];
 #pragma unroll
@@ -481,6 +507,14 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
         load_header(c0 + Q);
 
         // ---- s-block sweep
+        // lane coordinates made opaque per chunk: the mask indices derived from them are
+        // recomputed in every chunk instead of being hoisted out of the chunk loop (and spilled)
+        int l16c = l16, q4c = q4;
+        if constexpr (CF::NSB <= 8) asm volatile("" : "+v"(l16c), "+v"(q4c));   // fully unrolled sweeps
+        const bool fastmask = __builtin_amdgcn_readfirstlane(__float_as_int(MISC[2])) != 0;
+        float S2t[TPW];
+#pragma unroll
+        for (int u = 0; u < TPW; u++) S2t[u] = S2[(task_tb[u] * 16 + l16) / R];
         const int nbs = FULL ? CF::NSB : (nq + TOKS - 1) / TOKS;   // s-blocks holding valid tokens
         auto store_block = [&](const bf16x8 (&rawB)[CF::NLB], const bf16x8 (&rawX)[CF::NLX], int sb, int buf) {
             char *stg = UR + buf * CF::STAGE;
@@ -529,16 +563,48 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
                     if (upper) g1 = mfma16(*(const bf16x8 *)(bt + (16 + l16) * NS + 32 * kk + 8 * q4), creg[u][kk], g1);
                 }
                 // decay/trapezoid mask: column (t, i) = lane's t-row, rows (s, j) of the two halves
-                const int tt = (tb * 16 + l16) / R;
-                const float S2t = S2[tt];
+                const int tt = (tb * 16 + l16c) / R;
+                auto sidx = [&](int e) { return (sb * 32 + 16 * (e / 4) + 4 * q4c + (e % 4)) / R; };
                 bf16x8 mop;
+                if (fastmask) {
+                    // e^{S_t - S_s} w_s = 2^{S2_t - S2_ref} * (2^{S2_ref - S2_s} w_s), ref = first token
+                    // of the s-block; the second factor is tabulated per chunk
+                    const float rf = exp2_neg(S2t[u] - S2[sb * TOKS]);
+                    float fc[8];
+                    if constexpr (R == 1) {
+                        const f32x4 a = *(const f32x4 *)(F1 + sb * 32 + 4 * q4);
+                        const f32x4 b = *(const f32x4 *)(F1 + sb * 32 + 16 + 4 * q4);
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const int ss = (sb * 32 + 16 * (e / 4) + 4 * q4 + (e % 4)) / R;
-                    float coef = 0.f;
-                    if (ss <= tt && (e < 4 || upper))
-                        coef = exp2_neg(S2t - S2[ss]) * ((ss < tt) ? G1[ss] : GM[ss]);
-                    mop[e] = (bf16)(coef * ((e < 4) ? g0[e] : g1[e - 4]));
+                        for (int e = 0; e < 4; e++) { fc[e] = a[e]; fc[e + 4] = b[e]; }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; e++) fc[e] = F1[sidx(e)];
+                    }
+                    if (tb >= 2 * sb + 2) {                 // every s of the tile precedes every t
+#pragma unroll
+                        for (int e = 0; e < 8; e++) mop[e] = (bf16)(rf * fc[e] * ((e < 4) ? g0[e] : g1[e - 4]));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; e++) {
+                            // masks as 0/1 factors rather than selects of loaded values, which
+                            // the compiler would turn into branches around the loads
+                            const int ss = sidx(e);
+                            const float m1 = (ss < tt) ? 1.f : 0.f, m0 = (ss == tt) ? 1.f : 0.f;
+                            float coef = fc[e] * m1 + F0[ss] * m0;
+                            if (!(e < 4 || upper)) coef = 0.f;
+                            mop[e] = (bf16)(rf * coef * ((e < 4) ? g0[e] : g1[e - 4]));
+                        }
+                    }
+                } else {
+                    const float S2tt = S2[tt];
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        const int ss = sidx(e);
+                        const float m1 = (ss < tt) ? 1.f : 0.f, m0 = (ss == tt) ? 1.f : 0.f;
+                        float coef = exp2_neg(fminf(S2tt - S2[ss], 0.f)) * (G1[ss] * m1 + GM[ss] * m0);
+                        if (!(e < 4 || upper)) coef = 0.f;
+                        mop[e] = (bf16)(coef * ((e < 4) ? g0[e] : g1[e - 4]));
+                    }
                 }
                 const int dblk = tb - 2 * sb;               // 0/1: the t-block's rows are in this s-block
 #pragma unroll
@@ -588,8 +654,14 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
         };
         store_block(rb0, rx0, 0, 0);
         __syncthreads();
-        if constexpr (FULL) {
+        if constexpr (FULL && CF::NSB <= 8) {
 #pragma unroll
+            for (int sb = 0; sb < CF::NSB; sb += 2) {
+                step(std::integral_constant<int, 0>{}, sb);
+                step(std::integral_constant<int, 1>{}, sb + 1);
+            }
+        } else if constexpr (FULL) {
+#pragma nounroll
             for (int sb = 0; sb < CF::NSB; sb += 2) {
                 step(std::integral_constant<int, 0>{}, sb);
                 step(std::integral_constant<int, 1>{}, sb + 1);
@@ -629,8 +701,8 @@ __global__ __launch_bounds__(CF::NTHR) void k_scan_bf16(BfParams pr) {
 #pragma unroll
             for (int r = 0; r < UR_; r += 2) {
                 const int n = ut_n0[v] + urow(r);
-                float sn, cs;
-                __sincosf(PHE[n / 2], &sn, &cs);
+                const float2 rot = PHC[n / 2];
+                const float cs = rot.x, sn = rot.y;
                 const float u0 = hreg[v][r], u1 = hreg[v][r + 1];
                 hreg[v][r] = cs * u0 - sn * u1;
                 hreg[v][r + 1] = sn * u0 + cs * u1;
@@ -679,7 +751,7 @@ mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st) {
 #define M3_BF16_SHAPES(X)      \
     X(128, 64, 1, 64, 4, 32)   \
     X(64, 64, 4, 64, 8, 16)    \
-    X(128, 64, 4, 128, 16, 16) \
+    X(128, 64, 4, 128, 8, 16)  \
     X(64, 64, 1, 64, 4, 32)    \
     X(64, 64, 4, 32, 8, 16)    \
     X(128, 64, 2, 64, 8, 32)   \
