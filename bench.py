@@ -24,6 +24,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "Mamba-3 SSM prefill tokens/s + decode step \u00b5s at 1 GPU; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, published
 
@@ -78,12 +79,12 @@ def timed(fn, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps, wall
 
 
-def bench_scan(cfg, steps, warmup, dev):
+def bench_scan(cfg, steps, warmup, dev, **over):
     import torch
     import state_space_sequence_mamba3_amd as m3
     from state_space_sequence_mamba3_amd import synth
-    c = synth.CONFIGS[cfg]
-    d = synth.torch_scan_inputs(cfg, dev, seed=cfg)
+    c = dict(synth.CONFIGS[cfg], **over)
+    d = synth.torch_scan_inputs(cfg, dev, seed=cfg, **over)
     y = torch.empty_like(d["x"])
     S = int(d["cu_seqlens"].numel()) - 1 if "cu_seqlens" in d else c["batch"]
     h = torch.empty((S, c["nheads"], c["dstate"], c["headdim"]), dtype=torch.float32, device=dev)
@@ -97,7 +98,8 @@ def bench_scan(cfg, steps, warmup, dev):
     ms, wall = timed(step, steps, warmup, stream)
     tokens = c["batch"] * c["seqlen"]
     nbytes, flops = scan_bytes(c), scan_flops(c)
-    out = dict(workload=c["name"], ms=ms, tokens_per_s=tokens / (ms * 1e-3), bytes=nbytes, flops=flops,
+    name = c["name"] + (f" (B, C shared: G={c['ngroups']})" if "ngroups" in over else "")
+    out = dict(workload=name, ms=ms, tokens_per_s=tokens / (ms * 1e-3), bytes=nbytes, flops=flops,
                hbm_gbs=nbytes / (ms * 1e-3) / 1e9, mfma_tfs=flops / (ms * 1e-3) / 1e12, wall_s=wall)
     del d, y, h
     torch.cuda.empty_cache()
@@ -142,8 +144,44 @@ def bench_decode(steps_per_rep, reps, dev):
     ms, wall = timed(step, steps_per_rep, 10, stream)
     nbytes = decode_bytes(c)
     us = ms * 1e3
-    return dict(workload=c["name"], us_per_step=us, steps=steps_per_rep, bytes_per_step=nbytes,
-                hbm_gbs=nbytes / (us * 1e-6) / 1e9, wall_s=wall)
+    # per-step event pairs (outside the timed region) for the median
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps_per_rep)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    median = per[len(per) // 2]
+    # the same steps replayed from a HIP graph (one ring period captured), wall time per step
+    graph_us = None
+    try:
+        gr = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            state["k"] = 0
+            gstream = torch.cuda.current_stream()
+            with torch.cuda.graph(gr, stream=gstream):
+                for _ in range(ring):
+                    k = state["k"]
+                    i, j = k % ring, (k - 1) % ring
+                    m3.mamba3_decode_step(x[i], dt[i], lam[i], th[i], B[i], C[i], A, D, h=h, y=ys[i], Bprev=B[j],
+                                          xprev=x[j], stream=torch.cuda.current_stream())
+                    state["k"] = k + 1
+        torch.cuda.synchronize()
+        reps = max(1, steps_per_rep // ring)
+        gr.replay()
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for _ in range(reps):
+            gr.replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - w0) / (reps * ring) * 1e6
+    except Exception as exc:  # graph capture unavailable: report the eager figures only
+        print(f"# decode graph replay skipped: {exc}", file=sys.stderr)
+    return dict(workload=c["name"], us_per_step=us, median_us=median, graph_wall_us=graph_us, steps=steps_per_rep,
+                bytes_per_step=nbytes, hbm_gbs=nbytes / (us * 1e-6) / 1e9, wall_s=wall)
 
 
 def cpu_baseline(target_s=12.0):
@@ -187,7 +225,98 @@ def traffic_record(kernel):
     return rec.get("bytes_per_launch")
 
 
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    """Kernel name without the argument list and namespaces."""
+    n = name[5:] if name.startswith("void ") else name
+    n = n.replace("m3::(anonymous namespace)::", "").replace("at::native::(anonymous namespace)::", "at::native::")
+    depth = 0
+    for i, ch in enumerate(n):   # cut the argument list: the first '(' outside template brackets
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            return n[:i]
+    return n
+
+
+def summarize_stats(stats_dir, out_md, command):
+    """Writes a short text summary of a rocprofv3 --kernel-trace --stats run."""
+    rows = _csv_rows(os.path.join(stats_dir, "run_kernel_stats.csv"))
+    lines = ["# rocprofv3 kernel statistics", "", "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+             "```", command, "```", "", "| kernel | calls | average us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['TotalDurationNs']) / 1e6:.3f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print(f"wrote {out_md}")
+
+
+def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 30):
+    """Turns two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) of `bench.py --copy-calibration` into HBM bytes per launch of the
+    scan and decode kernels, each counter scaled by its reading on the plain
+    1 GiB device copy. Writes traffic_<kernel>.json records (read by the bench
+    while the kernel source is unchanged) and a text summary."""
+    import hashlib
+    from collections import defaultdict
+
+    def per_dispatch(d, counter):
+        agg, names = defaultdict(float), {}
+        for r in _csv_rows(os.path.join(d, "run_counter_collection.csv")):
+            if r["Counter_Name"] == counter:
+                agg[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        by = defaultdict(list)
+        for k, v in agg.items():
+            by[names[k]].append(v * 1024.0)
+        return by
+
+    fetch, write = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
+    # the calibration copies: the device-to-device copy kernel's dispatches of about 1 GiB
+    copy_f = [v for n, vs in fetch.items() if "copyBuffer" in n for v in vs if v > copy_bytes / 2]
+    copy_w = [v for n, vs in write.items() if "copyBuffer" in n for v in vs if v > copy_bytes / 2]
+    if not copy_f or not copy_w:
+        raise SystemExit("no copy kernel found in the counter runs (run bench.py with --copy-calibration)")
+    kf, kw = copy_bytes / (sum(copy_f) / len(copy_f)), copy_bytes / (sum(copy_w) / len(copy_w))
+    kernels = {"scan_bf16": ("scan_bf16.hip", "Cfg<128, 64, 1, 64,"), "decode": ("decode.hip", "k_decode")}
+    md = ["# HBM traffic per launch from rocprofv3 counters", "", "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):",
+          "", "```", *commands, "```", "",
+          f"Calibration: a plain 1 GiB device copy reads {sum(copy_f) / len(copy_f) / 2**30:.4f} GiB by FETCH_SIZE and writes "
+          f"{sum(copy_w) / len(copy_w) / 2**30:.4f} GiB by WRITE_SIZE; scale factors {kf:.4f} (fetch), {kw:.4f} (write).", "",
+          "| kernel | dispatches | fetch MB | write MB | traffic MB per launch |", "|---|---|---|---|---|"]
+    for key, (src, pat) in kernels.items():
+        fs = [v for n, vs in fetch.items() if pat in n for v in vs]
+        ws = [v for n, vs in write.items() if pat in n for v in vs]
+        if not fs or not ws:
+            continue
+        fb, wb = kf * sum(fs) / len(fs), kw * sum(ws) / len(ws)
+        name = next(n for n in fetch if pat in n)
+        srcp = os.path.join(ROOT, "state_space_sequence_mamba3_amd", "csrc", src)
+        rec = {"kernel": _short(name), "source": src,
+               "source_sha256": hashlib.sha256(open(srcp, "rb").read()).hexdigest(),
+               "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb, "dispatches": len(fs),
+               "copy_scale_fetch": kf, "copy_scale_write": kw}
+        json.dump(rec, open(os.path.join(out_dir, f"traffic_{key}.json"), "w"), indent=1)
+        md.append(f"| `{_short(name)}` | {len(fs)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} |")
+    out_md = os.path.join(out_dir, "traffic_scan_bf16_siso_8x4096_and_decode_b256.md")
+    open(out_md, "w").write("\n".join(md) + "\n")
+    print(f"wrote {out_md}")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-stats":
+        # bench.py --summarize-stats STATS_DIR OUT_MD COMMAND
+        summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-traffic":
+        # bench.py --summarize-traffic FETCH_DIR WRITE_DIR OUT_DIR COMMAND...
+        summarize_traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -225,6 +354,11 @@ def main():
         print(f"# mimo scan {res['mimo']['ms']:.3f} ms", file=sys.stderr, flush=True)
         res["packed"] = bench_scan(4, max(2, args.steps // 2), max(1, args.warmup // 2), dev)
         print(f"# packed scan {res['packed']['ms']:.3f} ms", file=sys.stderr, flush=True)
+        # B and C shared by all heads (one group), as the MIMO layer can be configured
+        res["mimo_g1"] = bench_scan(2, args.steps, args.warmup, dev, ngroups=1)
+        print(f"# mimo scan G=1 {res['mimo_g1']['ms']:.3f} ms", file=sys.stderr, flush=True)
+        res["packed_g1"] = bench_scan(4, max(2, args.steps // 2), max(1, args.warmup // 2), dev, ngroups=1)
+        print(f"# packed scan G=1 {res['packed_g1']['ms']:.3f} ms", file=sys.stderr, flush=True)
     if args.only in ("decode", "all"):
         res["decode"] = bench_decode(1000, 1, dev)
         print(f"# decode {res['decode']['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
@@ -237,7 +371,7 @@ def main():
         s = res["siso"]
         tr = traffic_record("scan_bf16")
         line = {
-            "metric": "Mamba-3 SSM prefill tokens/s (SISO scan) + decode step us; % of HBM/MFMA roofline",
+            "metric": METRIC,
             "value": s["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": s["ms"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, device-generated)",
@@ -251,18 +385,25 @@ def main():
             "cpu_baseline": cpu,
         }
     else:
-        line = {"metric": "Mamba-3 SSM decode step us", "value": None}
+        line = {"metric": METRIC, "value": None}
     sec = {}
-    for k in ("mimo", "packed"):
+    for k in ("mimo", "packed", "mimo_g1", "packed_g1"):
         if k in res:
             r = res[k]
-            sec[k] = {"workload": r["workload"], "ms": r["ms"], "tokens_per_s": r["tokens_per_s"],
-                      "roofline": {"bound": "hbm", "achieved": r["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": r["hbm_gbs"] / HBM_PEAK_GBS, "mfma_tflops": r["mfma_tfs"],
-                                   "mfma_frac": r["mfma_tfs"] / MFMA_BF16_PEAK_TFS}}
+            # the binding roofline: whichever of HBM bytes and MFMA flops needs more time at peak
+            mfma_bound = r["flops"] / (MFMA_BF16_PEAK_TFS * 1e12) > r["bytes"] / (HBM_PEAK_GBS * 1e9)
+            roof = ({"bound": "mfma", "achieved": r["mfma_tfs"], "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": r["mfma_tfs"] / MFMA_BF16_PEAK_TFS, "hbm_gbs": r["hbm_gbs"],
+                     "hbm_frac": r["hbm_gbs"] / HBM_PEAK_GBS} if mfma_bound else
+                    {"bound": "hbm", "achieved": r["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["hbm_gbs"] / HBM_PEAK_GBS, "mfma_tflops": r["mfma_tfs"],
+                     "mfma_frac": r["mfma_tfs"] / MFMA_BF16_PEAK_TFS})
+            roof.update(bytes_per_launch=r["bytes"], flops_per_launch=r["flops"])
+            sec[k] = {"workload": r["workload"], "ms": r["ms"], "tokens_per_s": r["tokens_per_s"], "roofline": roof}
     if "decode" in res:
         r = res["decode"]
-        sec["decode"] = {"workload": r["workload"], "us_per_step": r["us_per_step"], "steps": r["steps"],
+        sec["decode"] = {"workload": r["workload"], "us_per_step": r["us_per_step"], "median_us": r["median_us"],
+                         "graph_wall_us": r["graph_wall_us"], "steps": r["steps"],
                          "roofline": {"bound": "hbm", "achieved": r["hbm_gbs"], "peak": HBM_PEAK_GBS,
                                       "unit": "GB/s", "frac": r["hbm_gbs"] / HBM_PEAK_GBS,
                                       "bytes_per_launch": r["bytes_per_step"],
