@@ -208,10 +208,12 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     const int64_t strBC = (int64_t)G * R * N, strX = (int64_t)H * R * P, strTh = (int64_t)H * K;
 
     // this wave's t-blocks and state tiles
-    int task_tb[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; u++)
-        task_tb[u] = (TPW == 1) ? wave : (u / 2) * 2 * NW + ((u % 2 == 0) ? wave : 2 * NW - 1 - wave);
+    // t-block u of this wave in the chunk starting at c0x: balanced pairs along the causal
+    // triangle, rotated by the chunk index so the heavy blocks move across the SIMDs
+    auto tb_of = [&](int u, int64_t c0x) {
+        const int w = (wave + (int)(c0x / Q)) % NW;
+        return (TPW == 1) ? w : (u / 2) * 2 * NW + ((u % 2 == 0) ? w : 2 * NW - 1 - w);
+    };
     int ut_n0[UPW], ut_p0[UPW];
 #pragma unroll
     for (int v = 0; v < UPW; v++) {
@@ -258,55 +260,46 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 
     // ---- next-chunk header (dt, lam, theta, own C rows) prefetched into registers
-    float h_dt = 0.f, h_lam = 0.f;
+    // All prefetch loads are unconditional: a token past the end of the
+    // sequence is clamped to the last valid one (or to the sequence start when
+    // the whole chunk lies past the end), so the compiler sees a fixed sequence
+    // of memory operations. Loaded values stay raw until their use, where
+    // tokens past the end are masked; no select or conversion sits next to a
+    // load, so nothing waits for a prefetch before its consumer needs it.
+    bf16 h_dt = {}, h_lam = {};
     bf16x8 h_th[CF::NTH];
-    float h_thdt[CF::NTH];
+    bf16 h_thdt[CF::NTH];
     bf16x8 h_c[TPW][NKK];
-    // All prefetch loads are unconditional (clamped to a valid token, invalid
-    // results replaced by zero) so the compiler sees a fixed sequence of memory
-    // operations and waits only for the loads each use needs.
     // C rows of the own t-blocks in operand layout: row 16 tb + l16, columns 32 kk + 8 q4 ..
     auto load_crows = [&](int64_t c0h) {
-        const bool any = c0h < len;
-        const int64_t c0c = any ? c0h : 0;
-        const int nqh = (int)min((int64_t)Q, len - c0c);
+        const int64_t c0c = c0h < len ? c0h : 0;
         const int64_t t0h = start + c0c, last = len - c0c - 1;
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
-            const int row = task_tb[u] * 16 + l16;
+            const int row = tb_of(u, c0h) * 16 + l16;
             const int tau = row / R, j = row % R;
-            const bool valid = any && tau < nqh;
             const int64_t tk = t0h + min((int64_t)tau, last);
 #pragma unroll
-            for (int kk = 0; kk < NKK; kk++) {
-                const bf16x8 v = *(const bf16x8 *)(gC + tk * strBC + j * N + 32 * kk + 8 * q4);
-                h_c[u][kk] = valid ? v : bf16x8{};
-            }
+            for (int kk = 0; kk < NKK; kk++) h_c[u][kk] = *(const bf16x8 *)(gC + tk * strBC + j * N + 32 * kk + 8 * q4);
         }
     };
-    auto load_header = [&](int64_t c0h) {   // c0h >= len: dummy loads, zero results
-        const bool any = c0h < len;
-        const int64_t c0c = any ? c0h : 0;
+    auto load_header = [&](int64_t c0h) {
+        const int64_t c0c = c0h < len ? c0h : 0;
         const int nqh = (int)min((int64_t)Q, len - c0c);
         const int64_t t0h = start + c0c, last = len - c0c - 1;
         {
             const int idx = (tid < Q) ? tid : nqh;                 // thread Q: the token after the chunk
-            const bool valid = any && ((tid < nqh) || (tid == Q && c0h + nqh < len));
             const int64_t tk = t0h + min((int64_t)idx, last);
-            const float dv = to_f(pr.dt[tk * H + h]), lv = to_f(pr.lam[tk * H + h]);
-            h_dt = valid ? dv : 0.f;
-            h_lam = valid ? lv : 0.f;
+            h_dt = pr.dt[tk * H + h];
+            h_lam = pr.lam[tk * H + h];
         }
 #pragma unroll
         for (int i = 0; i < CF::NTH; i++) {
             const int e = min(tid + i * NTHR, Q * K / 8 - 1);
             const int tau = e / (K / 8), k0 = (e % (K / 8)) * 8;
-            const bool valid = any && tau < nqh && tid + i * NTHR < Q * K / 8;
             const int64_t tk = t0h + min((int64_t)tau, last);
-            const float dv = to_f(pr.dt[tk * H + h]);
-            const bf16x8 th = *(const bf16x8 *)(gTh + tk * strTh + k0);
-            h_thdt[i] = valid ? dv : 0.f;
-            h_th[i] = valid ? th : bf16x8{};
+            h_thdt[i] = pr.dt[tk * H + h];
+            h_th[i] = *(const bf16x8 *)(gTh + tk * strTh + k0);
         }
         if constexpr (CF::PFC) load_crows(c0h);
     };
@@ -314,9 +307,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     // ---- s-block stream: block j of the sequence lives in register set j % 2
     bf16x8 rb0[CF::NLB], rx0[CF::NLX], rb1[CF::NLB], rx1[CF::NLX];
     auto load_block_into = [&](bf16x8 (&rb)[CF::NLB], bf16x8 (&rx)[CF::NLX], int64_t c0b, int sb) {
-        const bool any = c0b < len;                                // past the end: dummy loads
-        const int64_t c0c = any ? c0b : 0;
-        const int nqb = (int)min((int64_t)Q, len - c0c);
+        const int64_t c0c = c0b < len ? c0b : 0;                   // past the end: dummy loads, never used
         const int64_t t0b = start + c0c, last = len - c0c - 1;
 #pragma unroll
         for (int i = 0; i < CF::NLB; i++) {
@@ -324,8 +315,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             const int row = c / (N / 8), col = (c % (N / 8)) * 8;
             const int tau = sb * TOKS + row / R;
             const int64_t tk = t0b + min((int64_t)tau, last);
-            const bf16x8 v = *(const bf16x8 *)(gB + tk * strBC + (row % R) * N + col);
-            rb[i] = (any && tau < nqb) ? v : bf16x8{};
+            rb[i] = *(const bf16x8 *)(gB + tk * strBC + (row % R) * N + col);
         }
 #pragma unroll
         for (int i = 0; i < CF::NLX; i++) {
@@ -333,8 +323,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             const int row = c / (P / 8), col = (c % (P / 8)) * 8;
             const int tau = sb * TOKS + row / R;
             const int64_t tk = t0b + min((int64_t)tau, last);
-            const bf16x8 v = *(const bf16x8 *)(gX + tk * strX + (row % R) * P + col);
-            rx[i] = (any && tau < nqb) ? v : bf16x8{};
+            rx[i] = *(const bf16x8 *)(gX + tk * strX + (row % R) * P + col);
         }
     };
     auto advance = [&](int64_t &c0b, int &sb) {
@@ -366,23 +355,32 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         constexpr bool FULL = decltype(FULLC)::value;
         const int nq = FULL ? Q : (int)(len - c0);
         const int64_t tok0 = start + c0;
+        int task_tb[TPW];
+#pragma unroll
+        for (int u = 0; u < TPW; u++) task_tb[u] = tb_of(u, c0);
 
         // ---- prologue 1: per-token scalars and raw angles dt*theta
-        if (tid < Q) {
-            A2[tid] = h_dt * A2h;
-            GM[tid] = h_lam * h_dt;
-            DL[tid] = (1.f - h_lam) * h_dt;
-        } else if (tid == Q) {
-            MISC[0] = (1.f - h_lam) * h_dt;
+        {
+            const float dt = to_f(h_dt), lm = to_f(h_lam);
+            if (tid < Q) {
+                const bool ok = FULL || tid < nq;
+                A2[tid] = ok ? dt * A2h : 0.f;
+                GM[tid] = ok ? lm * dt : 0.f;
+                DL[tid] = ok ? (1.f - lm) * dt : 0.f;
+            } else if (tid == Q) {
+                MISC[0] = (c0 + nq < len) ? (1.f - lm) * dt : 0.f;   // delta of the token after the chunk
+            }
         }
 #pragma unroll
         for (int i = 0; i < CF::NTH; i++) {
             const int e = tid + i * NTHR;
             if (e < Q * K / 8) {
                 const int tau = e / (K / 8), k0 = (e % (K / 8)) * 8;
+                const bool ok = FULL || tau < nq;
+                const float dt = to_f(h_thdt[i]);
                 float v[8];
 #pragma unroll
-                for (int q = 0; q < 8; q++) v[q] = h_thdt[i] * (float)h_th[i][q];
+                for (int q = 0; q < 8; q++) v[q] = ok ? dt * (float)h_th[i][q] : 0.f;
                 *(f32x4 *)(phi + tau * K + k0) = f32x4{v[0], v[1], v[2], v[3]};
                 *(f32x4 *)(phi + tau * K + k0 + 4) = f32x4{v[4], v[5], v[6], v[7]};
             }
@@ -473,7 +471,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 const f16x8 cs = *(const f16x8 *)(cst + tau * K + 16 * kk + 4 * q4);
                 float o[8];
                 rot_piece(h_c[u][kk], cs, o);
-                creg[u][kk] = pack8(o);
+                creg[u][kk] = (FULL || tau < nq) ? pack8(o) : bf16x8{};
             }
         }
 
@@ -521,6 +519,20 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             bf16 *bt = (bf16 *)(stg + CF::SB_BT);   // [32 rows][NS]  rotated B~
             bf16 *xs = (bf16 *)(stg + CF::SB_X);    // [32 rows][PS]  X
             bf16 *wx = (bf16 *)(stg + CF::SB_WX);   // [32 rows][PS]  wU * X
+            // every LDS read of the block first, then the arithmetic and the stores: a read
+            // issued after a store would also wait for that store
+            f16x8 csb[CF::NLB];
+            float wxv[CF::NLX];
+#pragma unroll
+            for (int i = 0; i < CF::NLB; i++) {
+                const int c = min(tid + i * NTHR, CF::BCH - 1);
+                csb[i] = *(const f16x8 *)(cst + (sb * TOKS + (c / (N / 8)) / R) * K + (c % (N / 8)) * 4);
+            }
+#pragma unroll
+            for (int i = 0; i < CF::NLX; i++) {
+                const int c = min(tid + i * NTHR, CF::XCH - 1);
+                wxv[i] = WU[sb * TOKS + (c / (P / 8)) / R];
+            }
 #pragma unroll
             for (int i = 0; i < CF::NLB; i++) {
                 const int c = tid + i * NTHR;
@@ -528,8 +540,8 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                     const int row = c / (N / 8), col = (c % (N / 8)) * 8;
                     const int tau = sb * TOKS + row / R;
                     float o[8];
-                    rot_piece(rawB[i], *(const f16x8 *)(cst + tau * K + col / 2), o);
-                    *(bf16x8 *)(bt + row * NS + col) = pack8(o);
+                    rot_piece(rawB[i], csb[i], o);
+                    *(bf16x8 *)(bt + row * NS + col) = (FULL || tau < nq) ? pack8(o) : bf16x8{};
                 }
             }
 #pragma unroll
@@ -537,12 +549,13 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 const int c = tid + i * NTHR;
                 if (c < CF::XCH) {
                     const int row = c / (P / 8), col = (c % (P / 8)) * 8;
-                    const float w = WU[sb * TOKS + row / R];
-                    *(bf16x8 *)(xs + row * PS + col) = rawX[i];
+                    const int tau = sb * TOKS + row / R;
+                    const bool ok = FULL || tau < nq;
+                    *(bf16x8 *)(xs + row * PS + col) = ok ? rawX[i] : bf16x8{};
                     float o[8];
 #pragma unroll
-                    for (int e = 0; e < 8; e++) o[e] = w * (float)rawX[i][e];
-                    *(bf16x8 *)(wx + row * PS + col) = pack8(o);
+                    for (int e = 0; e < 8; e++) o[e] = wxv[i] * (float)rawX[i][e];
+                    *(bf16x8 *)(wx + row * PS + col) = ok ? pack8(o) : bf16x8{};
                 }
             }
         };
@@ -695,14 +708,20 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
         // ---- epilogue: rotate the state by the chunk's total angle; bf16 copy for the next chunk
+        // (cos, sin) of the pairs of rows urow(4q) .. urow(4q) + 3: two pairs per 16-byte read,
+        // all read before the first store
+        f32x4 rot4[UPW][UR_ / 4];
+#pragma unroll
+        for (int v = 0; v < UPW; v++)
+#pragma unroll
+            for (int q = 0; q < UR_ / 4; q++) rot4[v][q] = *(const f32x4 *)(PHC + (ut_n0[v] + urow(4 * q)) / 2);
 #pragma unroll
         for (int v = 0; v < UPW; v++) {
             const int p = ut_p0[v] + ucol;
 #pragma unroll
             for (int r = 0; r < UR_; r += 2) {
                 const int n = ut_n0[v] + urow(r);
-                const float2 rot = PHC[n / 2];
-                const float cs = rot.x, sn = rot.y;
+                const float cs = rot4[v][r / 4][r % 4], sn = rot4[v][r / 4][r % 4 + 1];
                 const float u0 = hreg[v][r], u1 = hreg[v][r + 1];
                 hreg[v][r] = cs * u0 - sn * u1;
                 hreg[v][r + 1] = sn * u0 + cs * u1;
