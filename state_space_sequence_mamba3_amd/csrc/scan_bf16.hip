@@ -49,6 +49,7 @@ namespace {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -113,12 +114,15 @@ struct BfParams {
     int32_t seqlen, H, G;
 };
 
-template <int N_, int P_, int R_, int Q_, int NW_, int UT_>
+template <int N_, int P_, int R_, int Q_, int NW_, int UT_, int SBR_>
 struct Cfg {
-    static constexpr int N = N_, P = P_, R = R_, Q = Q_, NW = NW_, UT = UT_;
+    static constexpr int N = N_, P = P_, R = R_, Q = Q_, NW = NW_, UT = UT_, SBR = SBR_;
     static constexpr int K = N / 2, QR = Q * R;
-    static constexpr int NTB = QR / 16, NSB = QR / 32;      // 16-row t-blocks, 32-row s-blocks
-    static constexpr int TOKT = 16 / R, TOKS = 32 / R;      // tokens per t-block / s-block
+    static constexpr int NTB = QR / 16, NSB = QR / SBR;     // 16-row t-blocks, SBR-row s-blocks
+    static constexpr int NSUB = SBR / 32;                    // 32-row score tiles per s-block
+    static constexpr int NST = (NSB == 1) ? 1 : 2;           // LDS stages of s-blocks
+    static constexpr int TOKT = 16 / R, TOKS = SBR / R;     // tokens per t-block / s-block
+    static constexpr int TOKS32 = 32 / R;                   // tokens per 32-row tile
     static constexpr int NTHR = NW * 64, TPW = NTB / NW;
     static constexpr int NKK = N / 32;                      // K-steps over N (16x16x32)
     static constexpr int NPT = P / 16;                      // 16-column tiles of P
@@ -126,13 +130,17 @@ struct Cfg {
     static constexpr int UR_ = (UT == 32) ? 16 : 4;         // state registers per tile
     static constexpr int NS = N + 8, PS = P + 8;            // padded bf16 row strides
     static constexpr bool PFC = TPW <= 2;                   // prefetch the next chunk's C rows
+    // angle prefix: wave w owns angles [w KW, (w+1) KW); lane = (angle pair, token group)
+    static constexpr int KW = K / NW, KP = KW / 2, TG = 64 / KP, TPL = Q / TG;
+    static_assert(K % NW == 0 && KW % 2 == 0 && 64 % KP == 0 && Q % TG == 0, "angle prefix split");
     static_assert(N % 32 == 0 && P % 32 == 0 && (R == 1 || R == 2 || R == 4) && QR % 32 == 0, "shape");
     static_assert(NTB % NW == 0 && (TPW == 1 || TPW % 2 == 0), "t-block split");
     static_assert(NUT % NW == 0 && (UT == 16 || UT == 32), "state tile split");
     static_assert(K % 8 == 0 && Q % NW == 0 && Q <= 128 && Q < NTHR, "prologue");
-    static_assert(NSB % 2 == 0, "full chunks alternate the two prefetch register sets");
+    static_assert(SBR % 32 == 0 && QR % SBR == 0, "s-block size");
+    static_assert(NSB == 1 || NSB % 2 == 0, "full chunks alternate the two prefetch register sets");
     // LDS layout (bytes)
-    static constexpr int OFF_PHI = 0;                                  // float [Q][K] -> f16x2 (cos, sin)
+    static constexpr int OFF_PHI = 0;                                  // f16x2 [Q][K] (cos, sin) of Phi
     static constexpr int OFF_PHC = OFF_PHI + Q * K * 4;                // float2 [K] (cos, sin) of the chunk's total angle
     static constexpr int OFF_S2 = OFF_PHC + K * 8;                     // float [Q] log2 decay prefix
     static constexpr int OFF_A2 = OFF_S2 + Q * 4;                      // float [Q] per-token log2 decay
@@ -142,31 +150,30 @@ struct Cfg {
     static constexpr int OFF_WU = OFF_G1 + Q * 4;                      // float [Q] chunk-state weights
     static constexpr int OFF_F1 = OFF_WU + Q * 4;                      // float [Q] column mask factors, s < t
     static constexpr int OFF_F0 = OFF_F1 + Q * 4;                      // float [Q] column mask factors, s = t
-    static constexpr int OFF_TOT = OFF_F0 + Q * 4;                     // float [NW][K] angle segment sums
-    static constexpr int OFF_MISC = OFF_TOT + NW * K * 4;              // float [4]
+    static constexpr int OFF_DT = OFF_F0 + Q * 4;                      // float [Q] dt (0 past the end)
+    static constexpr int OFF_MISC = OFF_DT + Q * 4;                    // float [4]
     static constexpr int OFF_HB = (OFF_MISC + 16 + 15) / 16 * 16;      // bf16 [P][NS] carried state
     static constexpr int OFF_U = OFF_HB + P * NS * 2;                  // stage buffers / output staging
-    static constexpr int SB_BT = 0, SB_X = 32 * NS * 2, SB_WX = SB_X + 32 * PS * 2;
-    static constexpr int STAGE = SB_WX + 32 * PS * 2;                  // one s-block stage
+    static constexpr int SB_BT = 0, SB_X = SBR * NS * 2, SB_WX = SB_X + SBR * PS * 2;
+    static constexpr int STAGE = SB_WX + SBR * PS * 2;                 // one s-block stage
     static constexpr int YST = 16 * PS * 2;                            // per-wave output staging
-    static constexpr int U_BYTES = (NW * YST > 2 * STAGE) ? NW * YST : 2 * STAGE;
-    static constexpr int LDS = OFF_U + U_BYTES;
+    static constexpr int OFF_Y = OFF_U + NST * STAGE;
+    static constexpr int LDS = OFF_Y + NW * YST;
     static_assert(LDS <= 160 * 1024, "LDS");
     // global loads (16 bytes each) per s-block, and next-chunk header prefetch
-    static constexpr int BCH = 32 * N / 8, XCH = 32 * P / 8;
+    static constexpr int BCH = SBR * N / 8, XCH = SBR * P / 8;
     static constexpr int NLB = (BCH + NTHR - 1) / NTHR, NLX = (XCH + NTHR - 1) / NTHR;
-    static constexpr int NTH = (Q * K / 8 + NTHR - 1) / NTHR;
 };
 
 template <class CF>
 __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) void k_scan_bf16(BfParams pr) {
     constexpr int N = CF::N, P = CF::P, R = CF::R, Q = CF::Q, NW = CF::NW, K = CF::K, UT = CF::UT;
-    constexpr int TOKT = CF::TOKT, TOKS = CF::TOKS, NTHR = CF::NTHR, TPW = CF::TPW;
+    constexpr int TOKT = CF::TOKT, TOKS = CF::TOKS, TOKS32 = CF::TOKS32, NTHR = CF::NTHR, TPW = CF::TPW;
     constexpr int NKK = CF::NKK, NPT = CF::NPT, UPW = CF::UPW, NS = CF::NS, PS = CF::PS, UR_ = CF::UR_;
     using UAcc = std::conditional_t<UT == 32, f32x16, f32x4>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    float *phi = (float *)(smem + CF::OFF_PHI);
-    const f16x2 *cst = (const f16x2 *)(smem + CF::OFF_PHI);   // after the prologue: (cos, sin) table
+    f16x2 *cstw = (f16x2 *)(smem + CF::OFF_PHI);
+    const f16x2 *cst = cstw;                                   // (cos, sin) table of the chunk's angles
     float2 *PHC = (float2 *)(smem + CF::OFF_PHC);
     float *S2 = (float *)(smem + CF::OFF_S2);
     float *A2 = (float *)(smem + CF::OFF_A2);
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     float *WU = (float *)(smem + CF::OFF_WU);
     float *F1 = (float *)(smem + CF::OFF_F1);
     float *F0 = (float *)(smem + CF::OFF_F0);
-    float *TOT = (float *)(smem + CF::OFF_TOT);
+    float *DT = (float *)(smem + CF::OFF_DT);
     float *MISC = (float *)(smem + CF::OFF_MISC);
     bf16 *HB = (bf16 *)(smem + CF::OFF_HB);
     char *UR = smem + CF::OFF_U;
@@ -266,9 +273,9 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     // of memory operations. Loaded values stay raw until their use, where
     // tokens past the end are masked; no select or conversion sits next to a
     // load, so nothing waits for a prefetch before its consumer needs it.
-    bf16 h_dt = {}, h_lam = {};
-    bf16x8 h_th[CF::NTH];
-    bf16 h_thdt[CF::NTH];
+    bf16 h_dt = {}, h_lam = {};     // token tid of the chunk (tid < Q)
+    bf16 h_dtn = {}, h_lamn = {};   // the token after the chunk (same for every thread)
+    bf16x2 h_th2[CF::TPL];          // theta of the lane's angle pair for its TPL tokens
     bf16x8 h_c[TPW][NKK];
     // C rows of the own t-blocks in operand layout: row 16 tb + l16, columns 32 kk + 8 q4 ..
     auto load_crows = [&](int64_t c0h) {
@@ -288,18 +295,20 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         const int nqh = (int)min((int64_t)Q, len - c0c);
         const int64_t t0h = start + c0c, last = len - c0c - 1;
         {
-            const int idx = (tid < Q) ? tid : nqh;                 // thread Q: the token after the chunk
-            const int64_t tk = t0h + min((int64_t)idx, last);
+            const int64_t tk = t0h + min((int64_t)min(tid, Q - 1), last);
             h_dt = pr.dt[tk * H + h];
             h_lam = pr.lam[tk * H + h];
+            const int64_t tn = t0h + min((int64_t)nqh, last);
+            h_dtn = pr.dt[tn * H + h];
+            h_lamn = pr.lam[tn * H + h];
         }
+        {
+            const int k = wave * CF::KW + 2 * (lane % CF::KP), g0 = (lane / CF::KP) * CF::TPL;
 #pragma unroll
-        for (int i = 0; i < CF::NTH; i++) {
-            const int e = min(tid + i * NTHR, Q * K / 8 - 1);
-            const int tau = e / (K / 8), k0 = (e % (K / 8)) * 8;
-            const int64_t tk = t0h + min((int64_t)tau, last);
-            h_thdt[i] = pr.dt[tk * H + h];
-            h_th[i] = *(const bf16x8 *)(gTh + tk * strTh + k0);
+            for (int j = 0; j < CF::TPL; j++) {
+                const int64_t tk = t0h + min((int64_t)(g0 + j), last);
+                h_th2[j] = *(const bf16x2 *)(gTh + tk * strTh + k);
+            }
         }
         if constexpr (CF::PFC) load_crows(c0h);
     };
@@ -342,8 +351,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         load_header(0);
         load_block_into(rb0, rx0, ld_c0, ld_sb);
         advance(ld_c0, ld_sb);
-        load_block_into(rb1, rx1, ld_c0, ld_sb);
-        advance(ld_c0, ld_sb);
+        if constexpr (CF::NST == 2) {
+            load_block_into(rb1, rx1, ld_c0, ld_sb);
+            advance(ld_c0, ld_sb);
+        }
     }
     __syncthreads();
 
@@ -359,102 +370,130 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int u = 0; u < TPW; u++) task_tb[u] = tb_of(u, c0);
 
-        // ---- prologue 1: per-token scalars and raw angles dt*theta
-        {
-            const float dt = to_f(h_dt), lm = to_f(h_lam);
+        // ---- prologue 1: per-token scalars. With Q <= 64 wave 0 holds every token of the chunk
+        // and builds the log2-decay prefix and the weight tables in registers.
+        if constexpr (Q <= 64) {
+            if (wave == 0) {
+                const int t = lane;
+                const bool ok = (FULL || t < nq) && t < Q;
+                const float dt = ok ? to_f(h_dt) : 0.f, lm = ok ? to_f(h_lam) : 0.f;
+                const float gm = lm * dt, dl = (1.f - lm) * dt;
+                const float s2 = wave_incl_scan(dt * A2h, lane);
+                const float s2e = __shfl(s2, nq - 1, 64);
+                const float dn = (c0 + nq < len) ? (1.f - to_f(h_lamn)) * to_f(h_dtn) : 0.f;
+                const float dl1 = __shfl_down(dl, 1, 64);
+                const float g1 = gm + ((t + 1 < nq) ? dl1 : ((t + 1 == nq) ? dn : 0.f));
+                // mask factor relative to the first token of t's 32-row tile (>= 1)
+                const float f = __builtin_amdgcn_exp2f(__shfl(s2, (t / TOKS32) * TOKS32, 64) - s2);
+                const float s2first = __shfl(s2, 0, 64), s2last = __shfl(s2, Q - 1, 64);
+                if (t < Q) {
+                    DT[t] = dt;
+                    S2[t] = s2;
+                    GM[t] = gm;
+                    G1[t] = g1;
+                    WU[t] = (t < nq) ? exp2_neg(s2e - s2) * g1 : 0.f;
+                    F1[t] = f * g1;
+                    F0[t] = f * gm;
+                }
+                if (lane == 0) {
+                    MISC[1] = s2e;
+                    // the factored mask is used when every factor stays far inside the fp32 range
+                    MISC[2] = (s2first - s2last <= 120.f) ? 1.f : 0.f;
+                }
+            }
+        } else {
             if (tid < Q) {
                 const bool ok = FULL || tid < nq;
-                A2[tid] = ok ? dt * A2h : 0.f;
-                GM[tid] = ok ? lm * dt : 0.f;
-                DL[tid] = ok ? (1.f - lm) * dt : 0.f;
-            } else if (tid == Q) {
-                MISC[0] = (c0 + nq < len) ? (1.f - lm) * dt : 0.f;   // delta of the token after the chunk
+                const float dt = ok ? to_f(h_dt) : 0.f, lm = ok ? to_f(h_lam) : 0.f;
+                DT[tid] = dt;
+                A2[tid] = dt * A2h;
+                GM[tid] = lm * dt;
+                DL[tid] = (1.f - lm) * dt;
             }
-        }
-#pragma unroll
-        for (int i = 0; i < CF::NTH; i++) {
-            const int e = tid + i * NTHR;
-            if (e < Q * K / 8) {
-                const int tau = e / (K / 8), k0 = (e % (K / 8)) * 8;
-                const bool ok = FULL || tau < nq;
-                const float dt = to_f(h_thdt[i]);
-                float v[8];
-#pragma unroll
-                for (int q = 0; q < 8; q++) v[q] = ok ? dt * (float)h_th[i][q] : 0.f;
-                *(f32x4 *)(phi + tau * K + k0) = f32x4{v[0], v[1], v[2], v[3]};
-                *(f32x4 *)(phi + tau * K + k0 + 4) = f32x4{v[4], v[5], v[6], v[7]};
-            }
+            if (tid == 0) MISC[0] = (c0 + nq < len) ? (1.f - to_f(h_lamn)) * to_f(h_dtn) : 0.f;
         }
         __syncthreads();
 
-        // ---- prologue 2: angle prefix within each wave's token segment; log-decay prefix (wave 0)
-        constexpr int SEG = Q / NW;
-        if (lane < K) {
-            float acc = 0.f;
+        // ---- prologue 2: cumulative angles of the wave's angle pairs over the chunk, as a
+        // (cos, sin) table; with Q > 64 wave 0 also builds the log2-decay prefix here
+        if constexpr (Q > 64) {
+            if (wave == 0) {
+                constexpr int PER = (Q + 63) / 64;
+                float loc[PER];
+                float run = 0.f;
 #pragma unroll
-            for (int t = 0; t < SEG; t++) {
-                acc += phi[(wave * SEG + t) * K + lane];
-                phi[(wave * SEG + t) * K + lane] = acc;
-            }
-            TOT[wave * K + lane] = acc;
-        }
-        if (wave == 0) {
-            constexpr int PER = (Q + 63) / 64;
-            float loc[PER];
-            float run = 0.f;
+                for (int i = 0; i < PER; i++) {
+                    const int t = lane * PER + i;
+                    run += (t < Q) ? A2[t] : 0.f;
+                    loc[i] = run;
+                }
+                const float incl = wave_incl_scan(run, lane);
+                const float excl = incl - run;
 #pragma unroll
-            for (int i = 0; i < PER; i++) {
-                const int t = lane * PER + i;
-                run += (t < Q) ? A2[t] : 0.f;
-                loc[i] = run;
-            }
-            const float incl = wave_incl_scan(run, lane);
-            const float excl = incl - run;
+                for (int i = 0; i < PER; i++) {
+                    const int t = lane * PER + i;
+                    if (t < Q) S2[t] = excl + loc[i];
+                }
+                lds_wait();
+                const float S2e = S2[nq - 1];
+                const float dn = MISC[0];
 #pragma unroll
-            for (int i = 0; i < PER; i++) {
-                const int t = lane * PER + i;
-                if (t < Q) S2[t] = excl + loc[i];
-            }
-            lds_wait();
-            const float S2e = S2[nq - 1];
-            const float dn = MISC[0];
-#pragma unroll
-            for (int i = 0; i < PER; i++) {
-                const int t = lane * PER + i;
-                if (t < Q) {
-                    const float next = (t + 1 < nq) ? DL[t + 1] : ((t + 1 == nq) ? dn : 0.f);
-                    const float g1 = GM[t] + next;
-                    G1[t] = g1;
-                    WU[t] = (t < nq) ? exp2_neg(S2e - S2[t]) * g1 : 0.f;
-                    // mask factor relative to the first token of the t's s-block (>= 1)
-                    const float f = __builtin_amdgcn_exp2f(S2[(t / TOKS) * TOKS] - S2[t]);
-                    F1[t] = f * g1;
-                    F0[t] = f * GM[t];
+                for (int i = 0; i < PER; i++) {
+                    const int t = lane * PER + i;
+                    if (t < Q) {
+                        const float next = (t + 1 < nq) ? DL[t + 1] : ((t + 1 == nq) ? dn : 0.f);
+                        const float g1 = GM[t] + next;
+                        G1[t] = g1;
+                        WU[t] = (t < nq) ? exp2_neg(S2e - S2[t]) * g1 : 0.f;
+                        const float f = __builtin_amdgcn_exp2f(S2[(t / TOKS32) * TOKS32] - S2[t]);
+                        F1[t] = f * g1;
+                        F0[t] = f * GM[t];
+                    }
+                }
+                if (lane == 0) {
+                    MISC[1] = S2e;
+                    MISC[2] = (S2[0] - S2[Q - 1] <= 120.f) ? 1.f : 0.f;
                 }
             }
-            if (lane == 0) {
-                MISC[1] = S2e;
-                // the factored mask is used when every factor stays far inside the fp32 range
-                MISC[2] = (S2[0] - S2[Q - 1] <= 120.f) ? 1.f : 0.f;
-            }
         }
-        __syncthreads();
-        // ---- prologue 3: carry the segment sums, keep the total angle, turn angles into (cos, sin)
-        if (lane < K) {
-            float carry = 0.f;
-            for (int w = 0; w < wave; w++) carry += TOT[w * K + lane];
+        {
+            constexpr int KP = CF::KP, TPL = CF::TPL;
+            const int k = wave * CF::KW + 2 * (lane % KP), g0 = (lane / KP) * TPL;
+            float a0[TPL], a1[TPL];
+            float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-            for (int t = 0; t < SEG; t++) {
-                const int tau = wave * SEG + t;
-                const float a = phi[tau * K + lane] + carry;
-                if (tau == Q - 1) {                // angles past the end are zero: Phi[Q-1] = Phi[nq-1]
-                    float sn, cs;
-                    sincosf(a, &sn, &cs);
-                    PHC[lane] = float2{cs, sn};
+            for (int j = 0; j < TPL; j++) {
+                const float dt = DT[g0 + j];   // 0 past the end: the angle stays put
+                r0 += dt * (float)h_th2[j][0];
+                r1 += dt * (float)h_th2[j][1];
+                a0[j] = r0;
+                a1[j] = r1;
+            }
+            // exclusive prefix of the token groups' sums across the lanes holding the same pair
+            float e0 = r0, e1 = r1;
+#pragma unroll
+            for (int off = KP; off < 64; off <<= 1) {
+                const float o0 = __shfl_up(e0, off, 64), o1 = __shfl_up(e1, off, 64);
+                if (lane >= off) {
+                    e0 += o0;
+                    e1 += o1;
                 }
-                float sn, cs;
-                __sincosf(a, &sn, &cs);
-                ((f16x2 *)phi)[tau * K + lane] = f16x2{(_Float16)cs, (_Float16)sn};
+            }
+            e0 -= r0;
+            e1 -= r1;
+#pragma unroll
+            for (int j = 0; j < TPL; j++) {
+                const int tau = g0 + j;
+                const float x0 = a0[j] + e0, x1 = a1[j] + e1;
+                float s0, c0v, s1, c1v;
+                __sincosf(x0, &s0, &c0v);
+                __sincosf(x1, &s1, &c1v);
+                *(f16x4 *)(cstw + tau * K + k) = f16x4{(_Float16)c0v, (_Float16)s0, (_Float16)c1v, (_Float16)s1};
+                if (tau == Q - 1) {   // angles past the end are zero: Phi[Q-1] = Phi[nq-1]
+                    sincosf(x0, &s0, &c0v);
+                    sincosf(x1, &s1, &c1v);
+                    *(f32x4 *)(PHC + k) = f32x4{c0v, s0, c1v, s1};
+                }
             }
         }
         __syncthreads();
@@ -507,7 +546,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         // ---- s-block sweep
         // lane coordinates made opaque per chunk: the mask indices derived from them are
         // recomputed in every chunk instead of being hoisted out of the chunk loop (and spilled)
-        int l16c = l16, q4c = q4;
+        unsigned l16c = l16, q4c = q4;
         if constexpr (CF::NSB <= 8) asm volatile("" : "+v"(l16c), "+v"(q4c));   // fully unrolled sweeps
         const bool fastmask = __builtin_amdgcn_readfirstlane(__float_as_int(MISC[2])) != 0;
         float S2t[TPW];
@@ -560,93 +599,118 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         };
         auto compute_block = [&](int sb) {
-            const char *stg = UR + (sb & 1) * CF::STAGE;
+            const char *stg = UR + ((CF::NST == 1) ? 0 : (sb & 1)) * CF::STAGE;
             const bf16 *bt = (const bf16 *)(stg + CF::SB_BT);
             const bf16 *xs = (const bf16 *)(stg + CF::SB_X);
             const bf16 *wx = (const bf16 *)(stg + CF::SB_WX);
 #pragma unroll
             for (int u = 0; u < TPW; u++) {
                 const int tb = task_tb[u];
-                if (2 * sb > tb) continue;                  // t-block lies before this s-block
-                const bool upper = (2 * sb + 1 <= tb);      // second 16-row half of the s-block is causal
-                f32x4 g0 = {}, g1 = {};
+                const int tt = (int)((unsigned)(tb * 16) + l16c) / R;
 #pragma unroll
-                for (int kk = 0; kk < NKK; kk++) {
-                    g0 = mfma16(*(const bf16x8 *)(bt + l16 * NS + 32 * kk + 8 * q4), creg[u][kk], g0);
-                    if (upper) g1 = mfma16(*(const bf16x8 *)(bt + (16 + l16) * NS + 32 * kk + 8 * q4), creg[u][kk], g1);
-                }
-                // decay/trapezoid mask: column (t, i) = lane's t-row, rows (s, j) of the two halves
-                const int tt = (tb * 16 + l16c) / R;
-                auto sidx = [&](int e) { return (sb * 32 + 16 * (e / 4) + 4 * q4c + (e % 4)) / R; };
-                bf16x8 mop;
-                if (fastmask) {
-                    // e^{S_t - S_s} w_s = 2^{S2_t - S2_ref} * (2^{S2_ref - S2_s} w_s), ref = first token
-                    // of the s-block; the second factor is tabulated per chunk
-                    const float rf = exp2_neg(S2t[u] - S2[sb * TOKS]);
-                    float fc[8];
-                    if constexpr (R == 1) {
-                        const f32x4 a = *(const f32x4 *)(F1 + sb * 32 + 4 * q4);
-                        const f32x4 b = *(const f32x4 *)(F1 + sb * 32 + 16 + 4 * q4);
+                for (int j = 0; j < CF::NSUB; j++) {
+                    const int sbj = sb * CF::NSUB + j;          // 32-row tile of the chunk
+                    if (2 * sbj > tb) continue;                 // t-block lies before this tile
+                    if (!FULL && 32 * sbj >= nq * R) continue;  // tile past the end of the sequence
+                    const bool upper = (2 * sbj + 1 <= tb);     // second 16-row half of the tile is causal
+                    const int rb = 32 * j;                      // first row of the tile in the stage
+                    f32x4 g0 = {}, g1 = {};
 #pragma unroll
-                        for (int e = 0; e < 4; e++) { fc[e] = a[e]; fc[e + 4] = b[e]; }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; e++) fc[e] = F1[sidx(e)];
+                    for (int kk = 0; kk < NKK; kk++) {
+                        g0 = mfma16(*(const bf16x8 *)(bt + (rb + l16) * NS + 32 * kk + 8 * q4), creg[u][kk], g0);
+                        if (upper)
+                            g1 = mfma16(*(const bf16x8 *)(bt + (rb + 16 + l16) * NS + 32 * kk + 8 * q4), creg[u][kk], g1);
                     }
-                    if (tb >= 2 * sb + 2) {                 // every s of the tile precedes every t
+                    // decay/trapezoid mask: column (t, i) = lane's t-row, rows (s, j) of the two halves.
+                    // Row 16 h + 4 q4 + i of the tile (e = 4 h + i) is token tok_h + i / R.
+                    const unsigned tok0 = ((unsigned)(sbj * 32) + 4 * q4c) / R, tok1 = tok0 + 16 / R;
+                    auto sidx = [&](int e) { return (int)(((e < 4) ? tok0 : tok1) + (unsigned)(e % 4) / R); };
+                    // the distinct per-token values of a tabulated column array for the 8 rows
+                    auto col8 = [&](const float *tab, float (&o)[8]) {
+                        if constexpr (R == 1) {
+                            const f32x4 a = *(const f32x4 *)(tab + tok0), b = *(const f32x4 *)(tab + tok1);
 #pragma unroll
-                        for (int e = 0; e < 8; e++) mop[e] = (bf16)(rf * fc[e] * ((e < 4) ? g0[e] : g1[e - 4]));
+                            for (int e = 0; e < 4; e++) { o[e] = a[e]; o[e + 4] = b[e]; }
+                        } else if constexpr (R == 2) {
+                            const float2 a = *(const float2 *)(tab + tok0), b = *(const float2 *)(tab + tok1);
+                            o[0] = o[1] = a.x; o[2] = o[3] = a.y; o[4] = o[5] = b.x; o[6] = o[7] = b.y;
+                        } else {
+                            const float a = tab[tok0], b = tab[tok1];
+#pragma unroll
+                            for (int e = 0; e < 4; e++) { o[e] = a; o[e + 4] = b; }
+                        }
+                    };
+                    bf16x8 mop;
+                    if (fastmask) {
+                        // e^{S_t - S_s} w_s = 2^{S2_t - S2_ref} * (2^{S2_ref - S2_s} w_s), ref = first
+                        // token of the tile; the second factor is tabulated per chunk
+                        const float rf = exp2_neg(S2t[u] - S2[sbj * TOKS32]);
+                        float fc[8];
+                        col8(F1, fc);
+                        if (tb >= 2 * sbj + 2) {                // every s of the tile precedes every t
+#pragma unroll
+                            for (int e = 0; e < 8; e++) mop[e] = (bf16)(rf * fc[e] * ((e < 4) ? g0[e] : g1[e - 4]));
+                        } else {
+                            float f0[8];
+                            col8(F0, f0);
+#pragma unroll
+                            for (int e = 0; e < 8; e++) {
+                                // masks as 0/1 factors rather than selects of loaded values, which
+                                // the compiler would turn into branches around the loads
+                                const int ss = sidx(e);
+                                const float m1 = (ss < tt) ? 1.f : 0.f, m0 = (ss == tt) ? 1.f : 0.f;
+                                float coef = fc[e] * m1 + f0[e] * m0;
+                                if (!(e < 4 || upper)) coef = 0.f;
+                                mop[e] = (bf16)(rf * coef * ((e < 4) ? g0[e] : g1[e - 4]));
+                            }
+                        }
                     } else {
+                        const float S2tt = S2[tt];
 #pragma unroll
                         for (int e = 0; e < 8; e++) {
-                            // masks as 0/1 factors rather than selects of loaded values, which
-                            // the compiler would turn into branches around the loads
                             const int ss = sidx(e);
                             const float m1 = (ss < tt) ? 1.f : 0.f, m0 = (ss == tt) ? 1.f : 0.f;
-                            float coef = fc[e] * m1 + F0[ss] * m0;
+                            float coef = exp2_neg(fminf(S2tt - S2[ss], 0.f)) * (G1[ss] * m1 + GM[ss] * m0);
                             if (!(e < 4 || upper)) coef = 0.f;
-                            mop[e] = (bf16)(rf * coef * ((e < 4) ? g0[e] : g1[e - 4]));
+                            mop[e] = (bf16)(coef * ((e < 4) ? g0[e] : g1[e - 4]));
                         }
                     }
-                } else {
-                    const float S2tt = S2[tt];
+                    const int dblk = tb - 2 * sbj;              // 0/1: the t-block's rows are in this tile
 #pragma unroll
-                    for (int e = 0; e < 8; e++) {
-                        const int ss = sidx(e);
-                        const float m1 = (ss < tt) ? 1.f : 0.f, m0 = (ss == tt) ? 1.f : 0.f;
-                        float coef = exp2_neg(fminf(S2tt - S2[ss], 0.f)) * (G1[ss] * m1 + GM[ss] * m0);
-                        if (!(e < 4 || upper)) coef = 0.f;
-                        mop[e] = (bf16)(coef * ((e < 4) ? g0[e] : g1[e - 4]));
-                    }
-                }
-                const int dblk = tb - 2 * sb;               // 0/1: the t-block's rows are in this s-block
+                    for (int pt = 0; pt < NPT; pt++) {
+                        // X rows 4 q4 .. and 16 + 4 q4 .. of column 16 pt + l16 (K permuted like mop)
+                        yacc[u][pt] = mfma16(mop, tr_operand(xs, PS, rb + 4 * q4, rb + 16 + 4 * q4, pt * 16, l16),
+                                             yacc[u][pt]);
+                        if (dblk == 0 || dblk == 1) {           // skip term D x_t of the t-block's own rows
+                            const bf16x4 xv =
+                                ds_read_tr(xs + (rb + 16 * dblk + 4 * q4 + l16 / 4) * PS + pt * 16 + 4 * (l16 % 4));
 #pragma unroll
-                for (int pt = 0; pt < NPT; pt++) {
-                    // X rows 4 q4 .. and 16 + 4 q4 .. of column 16 pt + l16 (K permuted like mop)
-                    yacc[u][pt] = mfma16(mop, tr_operand(xs, PS, 4 * q4, 16 + 4 * q4, pt * 16, l16), yacc[u][pt]);
-                    if (dblk == 0 || dblk == 1) {           // skip term D x_t of the t-block's own rows
-                        const bf16x4 xv = ds_read_tr(xs + (16 * dblk + 4 * q4 + l16 / 4) * PS + pt * 16 + 4 * (l16 % 4));
-#pragma unroll
-                        for (int i = 0; i < 4; i++) yacc[u][pt][i] += Dh * (float)xv[i];
+                            for (int i = 0; i < 4; i++) yacc[u][pt][i] += Dh * (float)xv[i];
+                        }
                     }
                 }
             }
             // chunk-state update on the owned state tiles: H += B~^T (wU X), K = the s-block's rows
 #pragma unroll
-            for (int v = 0; v < UPW; v++) {
-                if constexpr (UT == 32) {
-                    // lane groups: column half c0 = 16 (group % 2), K rows 8 (group / 2) ..
-                    const int grp = lane >> 4;
-                    const int cn = ut_n0[v] + 16 * (grp & 1), cp = ut_p0[v] + 16 * (grp & 1);
+            for (int j = 0; j < CF::NSUB; j++) {
+                if (!FULL && 32 * (sb * CF::NSUB + j) >= nq * R) continue;
+                const int rb = 32 * j;
 #pragma unroll
-                    for (int ks = 0; ks < 2; ks++) {
-                        const int r0 = 16 * ks + 8 * (grp >> 1);
-                        hreg[v] = mfma32(tr_operand(bt, NS, r0, r0 + 4, cn, l16), tr_operand(wx, PS, r0, r0 + 4, cp, l16),
-                                         hreg[v]);
+                for (int v = 0; v < UPW; v++) {
+                    if constexpr (UT == 32) {
+                        // lane groups: column half c0 = 16 (group % 2), K rows 8 (group / 2) ..
+                        const int grp = lane >> 4;
+                        const int cn = ut_n0[v] + 16 * (grp & 1), cp = ut_p0[v] + 16 * (grp & 1);
+#pragma unroll
+                        for (int ks = 0; ks < 2; ks++) {
+                            const int r0 = rb + 16 * ks + 8 * (grp >> 1);
+                            hreg[v] = mfma32(tr_operand(bt, NS, r0, r0 + 4, cn, l16),
+                                             tr_operand(wx, PS, r0, r0 + 4, cp, l16), hreg[v]);
+                        }
+                    } else {
+                        hreg[v] = mfma16(tr_operand(bt, NS, rb + 8 * q4, rb + 8 * q4 + 4, ut_n0[v], l16),
+                                         tr_operand(wx, PS, rb + 8 * q4, rb + 8 * q4 + 4, ut_p0[v], l16), hreg[v]);
                     }
-                } else {
-                    hreg[v] = mfma16(tr_operand(bt, NS, 8 * q4, 8 * q4 + 4, ut_n0[v], l16),
-                                     tr_operand(wx, PS, 8 * q4, 8 * q4 + 4, ut_p0[v], l16), hreg[v]);
                 }
             }
         };
@@ -665,21 +729,33 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             }
             __syncthreads();
         };
-        store_block(rb0, rx0, 0, 0);
-        __syncthreads();
-        if constexpr (FULL && CF::NSB <= 8) {
+        if constexpr (CF::NST == 1) {
+            // the whole chunk is one s-block: stage it, then reuse the register set for the
+            // next chunk's block while this one is computed
+            store_block(rb0, rx0, 0, 0);
+            load_block_into(rb0, rx0, ld_c0, ld_sb);
+            advance(ld_c0, ld_sb);
+            __syncthreads();
+            compute_block(0);
+        } else if constexpr (FULL && CF::NSB <= 8) {
+            store_block(rb0, rx0, 0, 0);
+            __syncthreads();
 #pragma unroll
             for (int sb = 0; sb < CF::NSB; sb += 2) {
                 step(std::integral_constant<int, 0>{}, sb);
                 step(std::integral_constant<int, 1>{}, sb + 1);
             }
         } else if constexpr (FULL) {
+            store_block(rb0, rx0, 0, 0);
+            __syncthreads();
 #pragma nounroll
             for (int sb = 0; sb < CF::NSB; sb += 2) {
                 step(std::integral_constant<int, 0>{}, sb);
                 step(std::integral_constant<int, 1>{}, sb + 1);
             }
         } else {
+            store_block(rb0, rx0, 0, 0);
+            __syncthreads();
             for (int sb = 0; sb < nbs; sb += 2) {
                 step(std::integral_constant<int, 0>{}, sb);
                 if (sb + 1 < nbs) step(std::integral_constant<int, 1>{}, sb + 1);
@@ -688,7 +764,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 
         // ---- epilogue: outputs through a per-wave LDS transpose, 16-byte row stores
         {
-            bf16 *ys = (bf16 *)(UR + wave * CF::YST);   // [16 rows][PS]
+            bf16 *ys = (bf16 *)(smem + CF::OFF_Y + wave * CF::YST);   // [16 rows][PS], own region
 #pragma unroll
             for (int u = 0; u < TPW; u++) {
                 const int tb = task_tb[u];
@@ -766,18 +842,18 @@ mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st) {
 
 }  // namespace
 
-// (N, P, R, Q) -> waves per workgroup, state tile size
-#define M3_BF16_SHAPES(X)      \
-    X(128, 64, 1, 64, 4, 32)   \
-    X(64, 64, 4, 64, 8, 16)    \
-    X(128, 64, 4, 128, 8, 16)  \
-    X(64, 64, 1, 64, 4, 32)    \
-    X(64, 64, 4, 32, 8, 16)    \
-    X(128, 64, 2, 64, 8, 32)   \
-    X(128, 64, 4, 64, 8, 32)
+// (N, P, R, Q) -> waves per workgroup, state tile size, rows per s-block
+#define M3_BF16_SHAPES(X)          \
+    X(128, 64, 1, 64, 4, 32, 64)   \
+    X(64, 64, 4, 64, 8, 16, 256)   \
+    X(128, 64, 4, 128, 8, 16, 64)  \
+    X(64, 64, 1, 64, 4, 32, 64)    \
+    X(64, 64, 4, 32, 8, 16, 128)   \
+    X(128, 64, 2, 64, 8, 32, 128)  \
+    X(128, 64, 4, 64, 8, 32, 64)
 
 bool scan_bf16_supported(int N, int P, int R, int Q) {
-#define X(n, p, r, q, w, ut) if (N == n && P == p && R == r && Q == q) return true;
+#define X(n, p, r, q, w, ut, sbr) if (N == n && P == p && R == r && Q == q) return true;
     M3_BF16_SHAPES(X)
 #undef X
     return false;
@@ -785,8 +861,8 @@ bool scan_bf16_supported(int N, int P, int R, int Q) {
 
 mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st) {
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
-#define X(n, p, r, q, w, ut) \
-    if (N == n && P == p && R == r && Q == q) return launch_cfg<Cfg<n, p, r, q, w, ut>>(a, st);
+#define X(n, p, r, q, w, ut, sbr) \
+    if (N == n && P == p && R == r && Q == q) return launch_cfg<Cfg<n, p, r, q, w, ut, sbr>>(a, st);
     M3_BF16_SHAPES(X)
 #undef X
     return MAMBA3_EUNSUPPORTED;
