@@ -111,7 +111,7 @@ struct BfParams {
     bf16 *y;
     float *h_out;
     const int32_t *cu;
-    int32_t seqlen, H, G;
+    int32_t seqlen, H, G, nseq;
 };
 
 template <int N_, int P_, int R_, int Q_, int NW_, int UT_, int SBR_>
@@ -192,7 +192,27 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps per-wave branches scalar
     const int l16 = lane & 15, q4 = lane >> 4, l32 = lane & 31, hi = lane >> 5;
     const int H = pr.H, G = pr.G;
-    const int s = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
+    const int h = blockIdx.x % H, g = h / (H / G);
+    // Packed batches of at most 64 sequences run longest first: workgroup rank r = blockIdx / H
+    // takes the sequence of rank r by length (ties by index), so the longest sequences start in
+    // the first wave of workgroups and the short ones fill in behind them. Every wave ranks the
+    // lengths itself (one lane per sequence).
+    int s = blockIdx.x / H;
+    if (pr.cu && pr.nseq <= 64) {
+        const int ns = pr.nseq, i = lane;
+        int li = -1;
+        if (i < ns) {
+            const int a0 = min(max(pr.cu[i], 0), pr.seqlen), a1 = min(max(pr.cu[i + 1], a0), pr.seqlen);
+            li = a1 - a0;
+        }
+        int rank = 0;
+        for (int j = 0; j < ns; j++) {
+            const int lj = __builtin_amdgcn_readlane(li, j);
+            rank += (lj > li || (lj == li && j < i)) ? 1 : 0;
+        }
+        const unsigned long long hit = __ballot(i < ns && rank == s);
+        s = __builtin_amdgcn_readfirstlane((int)__ffsll((long long)hit) - 1);
+    }
 
     int64_t start, len;
     if (pr.cu) {
@@ -830,6 +850,7 @@ mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st) {
     p.Bprev = (const bf16 *)a->Bprev; p.xprev = (const bf16 *)a->xprev;
     p.A = a->A; p.D = a->D; p.h_in = a->h_in; p.y = (bf16 *)a->y; p.h_out = a->h_out;
     p.cu = a->cu_seqlens; p.seqlen = a->seqlen; p.H = a->nheads; p.G = a->ngroups;
+    p.nseq = a->cu_seqlens ? a->nseq : a->batch;
     const int64_t nseq = a->cu_seqlens ? a->nseq : a->batch;
     const int64_t nblk = nseq * a->nheads;
     if (nblk == 0) return MAMBA3_OK;
@@ -846,7 +867,7 @@ mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st) {
 #define M3_BF16_SHAPES(X)          \
     X(128, 64, 1, 64, 4, 32, 64)   \
     X(64, 64, 4, 64, 8, 16, 256)   \
-    X(128, 64, 4, 128, 8, 16, 64)  \
+    X(128, 64, 4, 128, 8, 16, 32)  \
     X(64, 64, 1, 64, 4, 32, 64)    \
     X(64, 64, 4, 32, 8, 16, 128)   \
     X(128, 64, 2, 64, 8, 32, 128)  \
