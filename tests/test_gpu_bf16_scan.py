@@ -82,6 +82,24 @@ def test_packed_ragged_with_empty(oracle):
     assert np.array_equal(from_dev(h)[1], inp["h_in"][1].astype(np.float64))
 
 
+@pytest.mark.parametrize("lengths", [
+    [100, 300, 100, 300, 0, 300],                     # ties in length: ranked by index
+    list(np.random.default_rng(31).integers(0, 41, size=70)),   # more than 64 sequences: launch order
+])
+def test_packed_sequence_order(oracle, lengths):
+    """Packed batches run their sequences in an order of the kernel's choosing (longest
+    first for up to 64 sequences); every sequence still gets its own state and outputs."""
+    total = int(sum(lengths))
+    inp = synth.scan_inputs(2, seed=33, seqlen=total, nheads=2, batch=1)
+    inp["cu_seqlens"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    inp = synth.resume_inputs(inp, seed=34)
+    note(f"bf16 packed order, {len(lengths)} sequences")
+    y, h = run(upload(inp, device()), 64)
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    assert packed_relerr(from_dev(y), yo, inp["cu_seqlens"]) < TOL_BF16
+    assert state_relerr(from_dev(h), ho) < TOL_BF16
+
+
 def test_chunk_size_invariance():
     inp = synth.scan_inputs(2, seed=21, batch=1, seqlen=256, nheads=2)
     note("bf16 chunk invariance 32 vs 64")
