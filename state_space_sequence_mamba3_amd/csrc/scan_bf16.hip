@@ -535,23 +535,28 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         }
 
         // ---- inter-chunk term: Y = e^{S_t} C~ H'   (H' bf16 in LDS, [p][n])
+        // each H' operand is read once and used for every t-block of the wave
+#pragma unroll
+        for (int pt = 0; pt < NPT; pt++) {
+            const int p = pt * 16 + l16;
+#pragma unroll
+            for (int u = 0; u < TPW; u++) yacc[u][pt] = f32x4{};
+#pragma unroll
+            for (int kk = 0; kk < NKK; kk++) {
+                const bf16x8 hop = *(const bf16x8 *)(HB + p * NS + 32 * kk + 8 * q4);
+#pragma unroll
+                for (int u = 0; u < TPW; u++) yacc[u][pt] = mfma16(creg[u][kk], hop, yacc[u][pt]);
+            }
+        }
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
-            const int tb = task_tb[u];
             float sc[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++) sc[i] = exp2_neg(S2[(tb * 16 + 4 * q4 + i) / R]);
+            for (int i = 0; i < 4; i++) sc[i] = exp2_neg(S2[(task_tb[u] * 16 + 4 * q4 + i) / R]);
 #pragma unroll
-            for (int pt = 0; pt < NPT; pt++) {
-                f32x4 acc = {};
-                const int p = pt * 16 + l16;
+            for (int pt = 0; pt < NPT; pt++)
 #pragma unroll
-                for (int kk = 0; kk < NKK; kk++)
-                    acc = mfma16(creg[u][kk], *(const bf16x8 *)(HB + p * NS + 32 * kk + 8 * q4), acc);
-#pragma unroll
-                for (int i = 0; i < 4; i++) acc[i] *= sc[i];
-                yacc[u][pt] = acc;
-            }
+                for (int i = 0; i < 4; i++) yacc[u][pt][i] *= sc[i];
         }
         {
             const float eS = exp2_neg(MISC[1]);
@@ -701,7 +706,8 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                         // X rows 4 q4 .. and 16 + 4 q4 .. of column 16 pt + l16 (K permuted like mop)
                         yacc[u][pt] = mfma16(mop, tr_operand(xs, PS, rb + 4 * q4, rb + 16 + 4 * q4, pt * 16, l16),
                                              yacc[u][pt]);
-                        if (dblk == 0 || dblk == 1) {           // skip term D x_t of the t-block's own rows
+                        // skip term D x_t of the t-block's own rows (one-stage shapes add it after the sweep)
+                        if (CF::NST == 2 && (dblk == 0 || dblk == 1)) {
                             const bf16x4 xv =
                                 ds_read_tr(xs + (rb + 16 * dblk + 4 * q4 + l16 / 4) * PS + pt * 16 + 4 * (l16 % 4));
 #pragma unroll
@@ -757,6 +763,16 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             advance(ld_c0, ld_sb);
             __syncthreads();
             compute_block(0);
+            // skip term D x_t, off the MFMA chains: the stage still holds the chunk's X rows
+            const bf16 *xs = (const bf16 *)(UR + CF::SB_X);
+#pragma unroll
+            for (int u = 0; u < TPW; u++)
+#pragma unroll
+                for (int pt = 0; pt < NPT; pt++) {
+                    const bf16x4 xv = ds_read_tr(xs + (task_tb[u] * 16 + 4 * q4 + l16 / 4) * PS + pt * 16 + 4 * (l16 % 4));
+#pragma unroll
+                    for (int i = 0; i < 4; i++) yacc[u][pt][i] += Dh * (float)xv[i];
+                }
         } else if constexpr (FULL && CF::NSB <= 8) {
             store_block(rb0, rx0, 0, 0);
             __syncthreads();
