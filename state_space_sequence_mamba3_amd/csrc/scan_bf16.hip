@@ -628,56 +628,82 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             const bf16 *bt = (const bf16 *)(stg + CF::SB_BT);
             const bf16 *xs = (const bf16 *)(stg + CF::SB_X);
             const bf16 *wx = (const bf16 *)(stg + CF::SB_WX);
+            // Per 32-row tile, t-blocks in groups of (up to) two: the group's t-blocks that reach
+            // the tile share its B~ and X operands; the score MFMAs of both are issued before their
+            // masks, and the masks before the output MFMAs, so their dependent chains overlap.
+            constexpr int UG = TPW < 2 ? TPW : 2;
 #pragma unroll
-            for (int u = 0; u < TPW; u++) {
-                const int tb = task_tb[u];
-                const int tt = (int)((unsigned)(tb * 16) + l16c) / R;
+            for (int ug = 0; ug < TPW; ug += UG)
 #pragma unroll
-                for (int j = 0; j < CF::NSUB; j++) {
-                    const int sbj = sb * CF::NSUB + j;          // 32-row tile of the chunk
-                    if (2 * sbj > tb) continue;                 // t-block lies before this tile
-                    if (!FULL && 32 * sbj >= nq * R) continue;  // tile past the end of the sequence
-                    const bool upper = (2 * sbj + 1 <= tb);     // second 16-row half of the tile is causal
-                    const int rb = 32 * j;                      // first row of the tile in the stage
-                    f32x4 g0 = {}, g1 = {};
+            for (int j = 0; j < CF::NSUB; j++) {
+                const int sbj = sb * CF::NSUB + j;              // 32-row tile of the chunk
+                if (!FULL && 32 * sbj >= nq * R) continue;      // tile past the end of the sequence
+                bool act[UG], up[UG];
+                bool any = false, anyup = false, anydiag = false;
 #pragma unroll
-                    for (int kk = 0; kk < NKK; kk++) {
-                        g0 = mfma16(*(const bf16x8 *)(bt + (rb + l16) * NS + 32 * kk + 8 * q4), creg[u][kk], g0);
-                        if (upper)
-                            g1 = mfma16(*(const bf16x8 *)(bt + (rb + 16 + l16) * NS + 32 * kk + 8 * q4), creg[u][kk], g1);
+                for (int u = 0; u < UG; u++) {
+                    act[u] = 2 * sbj <= task_tb[ug + u];        // t-block reaches this tile
+                    up[u] = 2 * sbj + 1 <= task_tb[ug + u];     // second 16-row half of the tile is causal
+                    any |= act[u];
+                    anyup |= up[u];
+                    anydiag |= act[u] && task_tb[ug + u] < 2 * sbj + 2;
+                }
+                if (!any) continue;
+                const int rb = 32 * j;                          // first row of the tile in the stage
+                f32x4 g0[UG], g1[UG];
+#pragma unroll
+                for (int u = 0; u < UG; u++) g0[u] = g1[u] = f32x4{};
+#pragma unroll
+                for (int kk = 0; kk < NKK; kk++) {
+                    const bf16x8 b0 = *(const bf16x8 *)(bt + (rb + l16) * NS + 32 * kk + 8 * q4);
+#pragma unroll
+                    for (int u = 0; u < UG; u++)
+                        if (act[u]) g0[u] = mfma16(b0, creg[ug + u][kk], g0[u]);
+                    if (anyup) {
+                        const bf16x8 b1 = *(const bf16x8 *)(bt + (rb + 16 + l16) * NS + 32 * kk + 8 * q4);
+#pragma unroll
+                        for (int u = 0; u < UG; u++)
+                            if (up[u]) g1[u] = mfma16(b1, creg[ug + u][kk], g1[u]);
                     }
-                    // decay/trapezoid mask: column (t, i) = lane's t-row, rows (s, j) of the two halves.
-                    // Row 16 h + 4 q4 + i of the tile (e = 4 h + i) is token tok_h + i / R.
-                    const unsigned tok0 = ((unsigned)(sbj * 32) + 4 * q4c) / R, tok1 = tok0 + 16 / R;
-                    auto sidx = [&](int e) { return (int)(((e < 4) ? tok0 : tok1) + (unsigned)(e % 4) / R); };
-                    // the distinct per-token values of a tabulated column array for the 8 rows
-                    auto col8 = [&](const float *tab, float (&o)[8]) {
-                        if constexpr (R == 1) {
-                            const f32x4 a = *(const f32x4 *)(tab + tok0), b = *(const f32x4 *)(tab + tok1);
+                }
+                // decay/trapezoid mask: column (t, i) = lane's t-row, rows (s, j) of the two halves.
+                // Row 16 h + 4 q4 + i of the tile (e = 4 h + i) is token tok_h + i / R.
+                const unsigned tok0 = ((unsigned)(sbj * 32) + 4 * q4c) / R, tok1 = tok0 + 16 / R;
+                auto sidx = [&](int e) { return (int)(((e < 4) ? tok0 : tok1) + (unsigned)(e % 4) / R); };
+                // the distinct per-token values of a tabulated column array for the 8 rows
+                auto col8 = [&](const float *tab, float (&o)[8]) {
+                    if constexpr (R == 1) {
+                        const f32x4 a = *(const f32x4 *)(tab + tok0), b = *(const f32x4 *)(tab + tok1);
 #pragma unroll
-                            for (int e = 0; e < 4; e++) { o[e] = a[e]; o[e + 4] = b[e]; }
-                        } else if constexpr (R == 2) {
-                            const float2 a = *(const float2 *)(tab + tok0), b = *(const float2 *)(tab + tok1);
-                            o[0] = o[1] = a.x; o[2] = o[3] = a.y; o[4] = o[5] = b.x; o[6] = o[7] = b.y;
-                        } else {
-                            const float a = tab[tok0], b = tab[tok1];
+                        for (int e = 0; e < 4; e++) { o[e] = a[e]; o[e + 4] = b[e]; }
+                    } else if constexpr (R == 2) {
+                        const float2 a = *(const float2 *)(tab + tok0), b = *(const float2 *)(tab + tok1);
+                        o[0] = o[1] = a.x; o[2] = o[3] = a.y; o[4] = o[5] = b.x; o[6] = o[7] = b.y;
+                    } else {
+                        const float a = tab[tok0], b = tab[tok1];
 #pragma unroll
-                            for (int e = 0; e < 4; e++) { o[e] = a; o[e + 4] = b; }
-                        }
-                    };
-                    bf16x8 mop;
-                    if (fastmask) {
-                        // e^{S_t - S_s} w_s = 2^{S2_t - S2_ref} * (2^{S2_ref - S2_s} w_s), ref = first
-                        // token of the tile; the second factor is tabulated per chunk
-                        const float rf = exp2_neg(S2t[u] - S2[sbj * TOKS32]);
-                        float fc[8];
-                        col8(F1, fc);
+                        for (int e = 0; e < 4; e++) { o[e] = a; o[e + 4] = b; }
+                    }
+                };
+                bf16x8 mop[UG];
+                if (fastmask) {
+                    // e^{S_t - S_s} w_s = 2^{S2_t - S2_ref} * (2^{S2_ref - S2_s} w_s), ref = first
+                    // token of the tile; the second factor is tabulated per chunk
+                    const float s2ref = S2[sbj * TOKS32];
+                    float fc[8], f0[8];
+                    col8(F1, fc);
+                    if (anydiag) col8(F0, f0);
+#pragma unroll
+                    for (int u = 0; u < UG; u++) {
+                        if (!act[u]) continue;
+                        const int tb = task_tb[ug + u];
+                        const float rf = exp2_neg(S2t[ug + u] - s2ref);
                         if (tb >= 2 * sbj + 2) {                // every s of the tile precedes every t
 #pragma unroll
-                            for (int e = 0; e < 8; e++) mop[e] = (bf16)(rf * fc[e] * ((e < 4) ? g0[e] : g1[e - 4]));
+                            for (int e = 0; e < 8; e++)
+                                mop[u][e] = (bf16)(rf * fc[e] * ((e < 4) ? g0[u][e] : g1[u][e - 4]));
                         } else {
-                            float f0[8];
-                            col8(F0, f0);
+                            const int tt = (int)((unsigned)(tb * 16) + l16c) / R;
 #pragma unroll
                             for (int e = 0; e < 8; e++) {
                                 // masks as 0/1 factors rather than selects of loaded values, which
@@ -685,33 +711,47 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                                 const int ss = sidx(e);
                                 const float m1 = (ss < tt) ? 1.f : 0.f, m0 = (ss == tt) ? 1.f : 0.f;
                                 float coef = fc[e] * m1 + f0[e] * m0;
-                                if (!(e < 4 || upper)) coef = 0.f;
-                                mop[e] = (bf16)(rf * coef * ((e < 4) ? g0[e] : g1[e - 4]));
+                                if (!(e < 4 || up[u])) coef = 0.f;
+                                mop[u][e] = (bf16)(rf * coef * ((e < 4) ? g0[u][e] : g1[u][e - 4]));
                             }
                         }
-                    } else {
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < UG; u++) {
+                        if (!act[u]) continue;
+                        const int tt = (int)((unsigned)(task_tb[ug + u] * 16) + l16c) / R;
                         const float S2tt = S2[tt];
 #pragma unroll
                         for (int e = 0; e < 8; e++) {
                             const int ss = sidx(e);
                             const float m1 = (ss < tt) ? 1.f : 0.f, m0 = (ss == tt) ? 1.f : 0.f;
                             float coef = exp2_neg(fminf(S2tt - S2[ss], 0.f)) * (G1[ss] * m1 + GM[ss] * m0);
-                            if (!(e < 4 || upper)) coef = 0.f;
-                            mop[e] = (bf16)(coef * ((e < 4) ? g0[e] : g1[e - 4]));
+                            if (!(e < 4 || up[u])) coef = 0.f;
+                            mop[u][e] = (bf16)(coef * ((e < 4) ? g0[u][e] : g1[u][e - 4]));
                         }
                     }
-                    const int dblk = tb - 2 * sbj;              // 0/1: the t-block's rows are in this tile
+                }
 #pragma unroll
-                    for (int pt = 0; pt < NPT; pt++) {
-                        // X rows 4 q4 .. and 16 + 4 q4 .. of column 16 pt + l16 (K permuted like mop)
-                        yacc[u][pt] = mfma16(mop, tr_operand(xs, PS, rb + 4 * q4, rb + 16 + 4 * q4, pt * 16, l16),
-                                             yacc[u][pt]);
-                        // skip term D x_t of the t-block's own rows (one-stage shapes add it after the sweep)
-                        if (CF::NST == 2 && (dblk == 0 || dblk == 1)) {
+                for (int pt = 0; pt < NPT; pt++) {
+                    // X rows 4 q4 .. and 16 + 4 q4 .. of column 16 pt + l16 (K permuted like mop)
+                    const bf16x8 xop = tr_operand(xs, PS, rb + 4 * q4, rb + 16 + 4 * q4, pt * 16, l16);
+#pragma unroll
+                    for (int u = 0; u < UG; u++)
+                        if (act[u]) yacc[ug + u][pt] = mfma16(mop[u], xop, yacc[ug + u][pt]);
+                }
+                // skip term D x_t of the t-block's own rows (one-stage shapes add it after the sweep)
+                if constexpr (CF::NST == 2) {
+#pragma unroll
+                    for (int u = 0; u < UG; u++) {
+                        const int dblk = task_tb[ug + u] - 2 * sbj;   // 0/1: the t-block's rows are in this tile
+                        if (dblk != 0 && dblk != 1) continue;
+#pragma unroll
+                        for (int pt = 0; pt < NPT; pt++) {
                             const bf16x4 xv =
                                 ds_read_tr(xs + (rb + 16 * dblk + 4 * q4 + l16 / 4) * PS + pt * 16 + 4 * (l16 % 4));
 #pragma unroll
-                            for (int i = 0; i < 4; i++) yacc[u][pt][i] += Dh * (float)xv[i];
+                            for (int i = 0; i < 4; i++) yacc[ug + u][pt][i] += Dh * (float)xv[i];
                         }
                     }
                 }
