@@ -61,6 +61,22 @@ def test_small_vs_full_oracle(oracle, name, resume):
     assert ey < TOL_BF16 and eh < TOL_BF16
 
 
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_strong_decay(oracle, cfg):
+    """Heads whose decay over a chunk spans from a few to hundreds of binary orders of
+    magnitude: chunks beyond the factored mask's range take the per-element form, chunks
+    near the threshold switch between the two."""
+    inp = synth.scan_inputs(cfg, seed=41, batch=2, seqlen=400, nheads=4)
+    inp["A"] = np.array([-0.5, -9.0, -10.0, -40.0], dtype=np.float32)
+    inp = synth.resume_inputs(inp, seed=42)
+    note(f"bf16 strong decay cfg{cfg}")
+    y, h = run(upload(inp, device()), inp["meta"]["chunk"])
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    ey, eh = slab_relerr(from_dev(y), yo), state_relerr(from_dev(h), ho)
+    note(f"  y relerr {ey:.2e}  h relerr {eh:.2e}")
+    assert ey < TOL_BF16 and eh < TOL_BF16
+
+
 def test_grouped_bc_and_no_skip(oracle):
     inp = synth.scan_inputs(dict(synth.CONFIGS[2], ngroups=1), seed=3, batch=1, seqlen=130, nheads=4)
     inp["D"] = None
