@@ -54,7 +54,8 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
     static_assert(P % 4 == 0 && TPB % PG == 0 && N % NRG == 0 && ROWS % 2 == 0, "decode tiling");
     static_assert((N * R) % VW == 0 && (P * R) % VW == 0 && (N / 2) % VW == 0, "16-byte staging");
     __shared__ float sB[N * R], sC[N * R], sBp[N * R], sX[P * R], sXp[P * R], sTh[N / 2];
-    __shared__ float red[NRG][P * R];
+    constexpr int WL = TPB < 64 ? TPB : 64, NWV = (TPB + 63) / 64;   // lanes per wave, waves
+    __shared__ float red[NWV][P * R];
 
     const int tid = threadIdx.x;
     const int pg = tid % PG, rg = tid / PG;
@@ -81,7 +82,9 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
     }
     const float dt = to_f(((const T *)pr.dt)[bh]);
     const float lam = to_f(((const T *)pr.lam)[bh]);
-    const float alpha = expf(dt * pr.A[hh]);
+    // fp32 inputs take the precise exp and sincos, bf16 inputs the hardware approximations
+    constexpr bool FAST = sizeof(T) == 2;
+    const float alpha = FAST ? __expf(dt * pr.A[hh]) : expf(dt * pr.A[hh]);
     const float delta = (1.f - lam) * dt, gamma = lam * dt;
     const float Dh = pr.D ? pr.D[hh] : 0.f;
     const bool has_prev = pr.Bprev != nullptr;
@@ -106,7 +109,8 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
     for (int r = 0; r < ROWS; r += 2) {
         const int n = n0 + r;
         float sn, cs;
-        sincosf(dt * sTh[n / 2], &sn, &cs);
+        if constexpr (FAST) __sincosf(dt * sTh[n / 2], &sn, &cs);
+        else sincosf(dt * sTh[n / 2], &sn, &cs);
         float b0[R], b1[R], q0[R], q1[R], bp0[R], bp1[R];
 #pragma unroll
         for (int j = 0; j < R; j++) {
@@ -140,16 +144,26 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
 #pragma unroll
     for (int r = 0; r < ROWS; r++) __builtin_nontemporal_store(st[r], (f32x4 *)(hs + (n0 + r) * P + p0));
 
+    // y = H^T C: sum the row groups' partials, first across the lanes of a wave (the row groups
+    // of one wave are PG lanes apart), then across the waves through LDS
 #pragma unroll
-    for (int c = 0; c < 4; c++)
+    for (int off = PG; off < WL; off <<= 1)
 #pragma unroll
-        for (int i = 0; i < R; i++) red[rg][i * P + p0 + c] = yp[c][i];
+        for (int c = 0; c < 4; c++)
+#pragma unroll
+            for (int i = 0; i < R; i++) yp[c][i] += __shfl_xor(yp[c][i], off, 64);
+    if ((tid & 63) < PG) {
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+#pragma unroll
+            for (int i = 0; i < R; i++) red[tid >> 6][i * P + p0 + c] = yp[c][i];
+    }
     __syncthreads();
     T *y = (T *)pr.y + (int64_t)bh * P * R;
     for (int e = tid; e < P * R; e += TPB) {
         float acc = 0.f;
 #pragma unroll
-        for (int q = 0; q < NRG; q++) acc += red[q][e];
+        for (int q = 0; q < NWV; q++) acc += red[q][e];
         acc += Dh * sX[e];
         y[e] = from_f<T>(acc);
     }
