@@ -9,13 +9,11 @@
 // "MIMO Formulation".
 //
 // The step is HBM-bound (the state is read and written once per step and
-// dominates the traffic), so the kernel is a streaming kernel: a workgroup
-// owns one (b, h) slab; every thread first issues its 16-byte state loads,
-// then the workgroup stages the slab's small token inputs (x, xprev, B, C,
-// Bprev, theta) through LDS with 16-byte loads, and each thread updates 4
-// consecutive columns of ROWS consecutive rows (whole rotation pairs) and
-// writes them back. y is reduced over rows through LDS in a fixed order
-// (deterministic). Token layouts are rank-major (B [R][N], x and y [R][P]).
+// dominates the traffic), so both kernels are streaming kernels with one
+// workgroup per (b, h) slab. Head dim 64 uses the column kernel (one lane per
+// state column); other head dims use the tile kernel (4 columns x ROWS rows per
+// thread). y is reduced over rows in a fixed order (deterministic). Token
+// layouts are rank-major (B [R][N], x and y [R][P]).
 #include "m3_common.h"
 
 namespace m3 {
@@ -169,6 +167,140 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
     }
 }
 
+// Head dim 64: one lane per state column, so a wave's loads and stores of a state row are one
+// coalesced 256-byte access and every y partial is the lane's own column. Wave w updates rows
+// [16 w, 16 w + 16). The update is applied term by term (previous-token term, rotation and
+// decay, current-token term, readout), each a pass over the lane's 16 rows, so few values are
+// live at once and eight waves per SIMD stay resident.
+template <typename T, int N, int R>
+__global__ __launch_bounds__(N / 16 * 64) __attribute__((amdgpu_waves_per_eu(8))) void k_decode_col(DecodeParams pr) {
+    constexpr int P = 64, ROWS = 16, NW = N / ROWS, TPB = NW * 64;
+    static_assert(N % ROWS == 0 && (N * R) % (16 / sizeof(T)) == 0, "decode column tiling");
+    __shared__ __attribute__((aligned(16))) float sB[R * N], sC[R * N], sBp[R * N];
+    __shared__ __attribute__((aligned(16))) float2 sCS[N / 2];
+    __shared__ float red[NW][R * P];
+
+    const int tid = threadIdx.x, p = tid & 63, w = tid >> 6, n0 = w * ROWS;
+    const int bh = blockIdx.x;
+    const int H = pr.H, G = pr.G;
+    const int b = bh / H, hh = bh % H, g = hh / (H / G);
+    float *hs = pr.h + (int64_t)bh * N * P;
+
+    const int64_t obc = ((int64_t)b * G + g) * N * R, ox = (int64_t)bh * P * R;
+    const bool has_prev = pr.Bprev != nullptr;
+    const T *xp_src = has_prev ? (const T *)pr.xprev : (const T *)pr.x;   // (no previous token: unused)
+    // All token loads are unconditional and issued before the state loads, and each thread
+    // waits only for its own: loads complete in order, so the staging below does not wait for
+    // the state. Thread t loads 16-byte piece t % PCS of B (t < PCS), C or Bprev.
+    constexpr int VW = 16 / sizeof(T), PCS = N * R / VW;
+    static_assert(3 * PCS <= TPB, "decode staging");
+    const int arr = tid / PCS, pc = tid % PCS;
+    const T *src = (arr == 1) ? (const T *)pr.C : (arr == 2 && has_prev) ? (const T *)pr.Bprev : (const T *)pr.B;
+    typedef T vec_t __attribute__((ext_vector_type(VW)));
+    const vec_t piece = *(const vec_t *)(src + obc + pc * VW);
+    T xr[R], xpr[R];
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+        xr[j] = ((const T *)pr.x)[ox + j * P + p];
+        xpr[j] = xp_src[ox + j * P + p];
+    }
+    const T thr = ((const T *)pr.theta)[(int64_t)bh * (N / 2) + min(tid, N / 2 - 1)];
+    const float dt = to_f(((const T *)pr.dt)[bh]);
+    const float lam = to_f(((const T *)pr.lam)[bh]);
+    const float Ah = pr.A[hh];
+    const float Dh = pr.D ? pr.D[hh] : 0.f;
+
+    float st[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; r++) st[r] = __builtin_nontemporal_load(hs + (n0 + r) * P + p);
+
+    if (arr < 2 || (arr == 2 && has_prev)) {
+        float *dst = (arr == 0) ? sB : (arr == 1) ? sC : sBp;
+#pragma unroll
+        for (int e = 0; e < VW; e++) dst[pc * VW + e] = (float)piece[e];
+    }
+    float xv[R], xpv[R];
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+        xv[j] = to_f(xr[j]);
+        xpv[j] = has_prev ? to_f(xpr[j]) : 0.f;
+    }
+    // fp32 inputs take the precise exp and sincos, bf16 inputs the hardware approximations
+    constexpr bool FAST = sizeof(T) == 2;
+    if (tid < N / 2) {   // one sincos per state pair, shared through LDS
+        const float a = dt * to_f(thr);
+        float sn, cs;
+        if constexpr (FAST) __sincosf(a, &sn, &cs);
+        else sincosf(a, &sn, &cs);
+        sCS[tid] = float2{cs, sn};
+    }
+    const float alpha = FAST ? __expf(dt * Ah) : expf(dt * Ah);
+    const float delta = (1.f - lam) * dt, gamma = lam * dt;
+    __syncthreads();
+
+    // H + delta Bprev xprev^T
+    if (has_prev) {
+#pragma unroll
+        for (int j = 0; j < R; j++) {
+            const float dx = delta * xpv[j];
+#pragma unroll
+            for (int q = 0; q < ROWS / 4; q++) {
+                const f32x4 bq = *(const f32x4 *)(sBp + j * N + n0 + 4 * q);
+#pragma unroll
+                for (int e = 0; e < 4; e++) st[4 * q + e] += bq[e] * dx;
+            }
+        }
+    }
+    // alpha R(phi) (.)
+#pragma unroll
+    for (int q = 0; q < ROWS / 4; q++) {
+        const f32x4 cs2 = *(const f32x4 *)(sCS + (n0 + 4 * q) / 2);   // two pairs
+#pragma unroll
+        for (int m = 0; m < 2; m++) {
+            const float c = alpha * cs2[2 * m], sn = alpha * cs2[2 * m + 1];
+            const float u0 = st[4 * q + 2 * m], u1 = st[4 * q + 2 * m + 1];
+            st[4 * q + 2 * m] = c * u0 - sn * u1;
+            st[4 * q + 2 * m + 1] = sn * u0 + c * u1;
+        }
+    }
+    // + gamma B x^T
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+        const float gx = gamma * xv[j];
+#pragma unroll
+        for (int q = 0; q < ROWS / 4; q++) {
+            const f32x4 bq = *(const f32x4 *)(sB + j * N + n0 + 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; e++) st[4 * q + e] += bq[e] * gx;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; r++) __builtin_nontemporal_store(st[r], hs + (n0 + r) * P + p);
+    // y partial of the lane's column over the wave's rows
+    float yp[R];
+#pragma unroll
+    for (int i = 0; i < R; i++) {
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < ROWS / 4; q++) {
+            const f32x4 cq = *(const f32x4 *)(sC + i * N + n0 + 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc += cq[e] * st[4 * q + e];
+        }
+        yp[i] = acc;
+    }
+#pragma unroll
+    for (int i = 0; i < R; i++) red[w][i * P + p] = yp[i];
+    __syncthreads();
+    T *y = (T *)pr.y + (int64_t)bh * P * R;
+    for (int e = tid; e < P * R; e += TPB) {
+        float acc = Dh * to_f(((const T *)pr.x)[ox + e]);
+#pragma unroll
+        for (int q = 0; q < NW; q++) acc += red[q][e];
+        y[e] = from_f<T>(acc);
+    }
+}
+
 template <typename T, int N, int P, int R>
 static mamba3_status launch_one(const mamba3_decode_args *a, hipStream_t st) {
     constexpr int TPB = (N * P / 8 >= 256) ? 256 : N * P / 8;
@@ -176,7 +308,10 @@ static mamba3_status launch_one(const mamba3_decode_args *a, hipStream_t st) {
                    a->nheads, a->ngroups};
     int64_t nblk = (int64_t)a->batch * a->nheads;
     if (nblk == 0) return MAMBA3_OK;
-    hipLaunchKernelGGL((k_decode<T, N, P, R, TPB>), dim3((unsigned)nblk), dim3(TPB), 0, st, p);
+    if constexpr (P == 64)
+        hipLaunchKernelGGL((k_decode_col<T, N, R>), dim3((unsigned)nblk), dim3(N / 16 * 64), 0, st, p);
+    else
+        hipLaunchKernelGGL((k_decode<T, N, P, R, TPB>), dim3((unsigned)nblk), dim3(TPB), 0, st, p);
     return hipGetLastError() == hipSuccess ? MAMBA3_OK : MAMBA3_EHIP;
 }
 
