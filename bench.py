@@ -205,10 +205,18 @@ def cpu_baseline(target_s=12.0):
         done += nslab
     tokens = c["batch"] * c["seqlen"]
     whole_job_s = spent * total_slabs / done
+    # the same oracle on one thread, on a few slabs
+    one = {k: (v[:, :, :2] if k in ("x", "dt", "lam", "theta", "B", "C") else (v[:2] if k in ("A", "D") else v))
+           for k, v in inp.items()}
+    t0 = time.perf_counter()
+    o.scan(one, form=1, nthreads=1)
+    one_s = (time.perf_counter() - t0) * total_slabs / 2
     return dict(value=tokens / whole_job_s, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{done} (sequence, head) slabs of the 8x4096 SISO workload ({nslab} distinct, "
                        f"4096 tokens each; the batch has {total_slabs}) in {spent:.1f} s; rate scaled to the "
-                       f"whole batch")
+                       f"whole batch",
+                single_thread_value=tokens / one_s,
+                single_thread_sample="2 slabs on 1 thread, rate scaled to the whole batch")
 
 
 def traffic_record(kernel):
