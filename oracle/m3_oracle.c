@@ -44,6 +44,14 @@
  *   - D is a per-head skip term y += D_h X_t (absent from the pages).
  *   - MIMO: the rotation acts on the N axis identically for every rank column.
  *
+ * Optional block prologue and epilogue (section "Architectural Integration"):
+ * every B and C column (N values of one token, group and rank) may be scaled
+ * to unit root-mean-square and then get its head's per-channel bias added,
+ * before the rotation, for the current and the previous token alike; the
+ * output may be gated, y <- y * SiLU(z). Readings: the norm has no gain and
+ * normalizes each rank column of B_t, C_t separately; the bias is [H, N],
+ * shared by the rank columns; the skip term D x is added before the gate.
+ *
  * Inputs are read through a dtype tag (f64, f32, bf16 bits) and converted
  * exactly to double; all arithmetic is in double / double complex.
  */
@@ -76,6 +84,13 @@ typedef struct {
     const double *h_in;        /* [nseq, H, N, P] or NULL (zero state) */
     const void *Bprev;         /* [nseq, G, R, N] or NULL (no previous token) */
     const void *xprev;         /* [nseq, H, R, P] or NULL */
+    /* Block prologue and epilogue around the recurrence (section "Architectural
+     * Integration": BC normalization, BC biases, output gating): */
+    const double *B_bias;      /* [H, N] per-head bias added to B after the norm, or NULL */
+    const double *C_bias;      /* [H, N] per-head bias added to C after the norm, or NULL */
+    const void *z;             /* [T, H, R, P] gate (dtype in_dtype), or NULL: y <- y * SiLU(z) */
+    int32_t bc_norm;           /* 1: every B and C column (N values) is scaled to unit RMS */
+    double bc_eps;             /* added to the mean square under the root */
 } m3o_args;
 
 static inline double ld(const void *p, int dt, int64_t i) {
@@ -85,6 +100,33 @@ static inline double ld(const void *p, int dt, int64_t i) {
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/* One N-vector of B or C as the recurrence sees it: the raw column at src[off ..
+ * off + N), scaled to unit root-mean-square when bc_norm is set (RMSNorm without a
+ * gain), then the head's bias added (section "Architectural Integration": BC
+ * normalization after the projection, then learned per-head, per-channel biases). */
+static void bc_row(const m3o_args *a, const void *src, int64_t off, int h, const double *bias, double *out) {
+    const int N = a->N;
+    double ss = 0.0;
+    for (int n = 0; n < N; n++) {
+        out[n] = ld(src, a->in_dtype, off + n);
+        ss += out[n] * out[n];
+    }
+    if (a->bc_norm) {
+        const double inv = 1.0 / sqrt(ss / N + a->bc_eps);
+        for (int n = 0; n < N; n++) out[n] *= inv;
+    }
+    if (bias)
+        for (int n = 0; n < N; n++) out[n] += bias[(int64_t)h * N + n];
+}
+
+/* Output gating: y * SiLU(z) with SiLU(v) = v / (1 + e^{-v}) (section
+ * "Architectural Integration", output gating); y itself when there is no gate. */
+static inline double gate(const m3o_args *a, double y, int64_t zi) {
+    if (!a->z) return y;
+    const double v = ld(a->z, a->in_dtype, zi);
+    return y * v / (1.0 + exp(-v));
 }
 
 /* ---------------------------------------------------------------- O1 ---- */
@@ -102,6 +144,7 @@ static void o1_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
     double complex *cc = malloc((size_t)K * R * sizeof *cc);  /* cur c   [K][R] */
     double *xc = malloc((size_t)P * R * sizeof *xc);          /* cur x   [P][R] */
     double complex *z = malloc((size_t)K * sizeof *z);
+    double *row = malloc((size_t)N * sizeof *row), *row2 = malloc((size_t)N * sizeof *row2);
     int has_prev = 0;
 
     if (a->h_in) {
@@ -113,10 +156,10 @@ static void o1_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
     if (a->Bprev && a->xprev) {
         has_prev = 1;
         int64_t ob = ((int64_t)s * G + g) * N * R, ox = ((int64_t)s * H + h) * P * R;
-        for (int k = 0; k < K; k++)
-            for (int j = 0; j < R; j++)
-                bp[k * R + j] = ld(a->Bprev, dtp, ob + j * N + 2 * k) +
-                                I * ld(a->Bprev, dtp, ob + j * N + 2 * k + 1);
+        for (int j = 0; j < R; j++) {
+            bc_row(a, a->Bprev, ob + j * N, h, a->B_bias, row);
+            for (int k = 0; k < K; k++) bp[k * R + j] = row[2 * k] + I * row[2 * k + 1];
+        }
         for (int p = 0; p < P; p++)
             for (int j = 0; j < R; j++) xp[p * R + j] = ld(a->xprev, dtp, ox + j * P + p);
     }
@@ -134,13 +177,14 @@ static void o1_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
             z[k] = decay * (cos(ang) + I * sin(ang));
         }
         const int64_t ob = (t * G + g) * N * R, ox = (t * H + h) * P * R;
-        for (int k = 0; k < K; k++)
-            for (int j = 0; j < R; j++) {
-                bc[k * R + j] = ld(a->B, dtp, ob + j * N + 2 * k) +
-                                I * ld(a->B, dtp, ob + j * N + 2 * k + 1);
-                cc[k * R + j] = ld(a->C, dtp, ob + j * N + 2 * k) -
-                                I * ld(a->C, dtp, ob + j * N + 2 * k + 1);
+        for (int j = 0; j < R; j++) {
+            bc_row(a, a->B, ob + j * N, h, a->B_bias, row);
+            bc_row(a, a->C, ob + j * N, h, a->C_bias, row2);
+            for (int k = 0; k < K; k++) {
+                bc[k * R + j] = row[2 * k] + I * row[2 * k + 1];
+                cc[k * R + j] = row2[2 * k] - I * row2[2 * k + 1];
             }
+        }
         for (int p = 0; p < P; p++)
             for (int j = 0; j < R; j++) xc[p * R + j] = ld(a->x, dtp, ox + j * P + p);
 
@@ -160,7 +204,7 @@ static void o1_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
             for (int i = 0; i < R; i++) {
                 double complex acc = 0;
                 for (int k = 0; k < K; k++) acc += cc[k * R + i] * hc[k * P + p];
-                yt[i * P + p] = creal(acc) + Dh * xc[p * R + i];
+                yt[i * P + p] = gate(a, creal(acc) + Dh * xc[p * R + i], ox + i * P + p);
             }
         memcpy(bp, bc, (size_t)K * R * sizeof *bp);
         memcpy(xp, xc, (size_t)P * R * sizeof *xp);
@@ -172,7 +216,7 @@ static void o1_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
                 h_slab[(2 * k) * P + p] = creal(hc[k * P + p]);
                 h_slab[(2 * k + 1) * P + p] = cimag(hc[k * P + p]);
             }
-    free(hc); free(bp); free(xp); free(bc); free(cc); free(xc); free(z);
+    free(hc); free(bp); free(xp); free(bc); free(cc); free(xc); free(z); free(row); free(row2);
 }
 
 /* ---------------------------------------------------------------- O2 ---- */
@@ -204,6 +248,7 @@ static void o2_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
     double *brot = malloc((size_t)N * R * sizeof *brot), *crot = malloc((size_t)N * R * sizeof *crot);
     double *bprot = calloc((size_t)N * R, sizeof *bprot); /* previous token's rotated B */
     double *xp = calloc((size_t)P * R, sizeof *xp), *xc = malloc((size_t)P * R * sizeof *xc);
+    double *rowb = malloc((size_t)N * sizeof *rowb), *rowc = malloc((size_t)N * sizeof *rowc);
     int has_prev = 0;
 
     /* Before the first token the cumulative product is empty: h~ = h_in. */
@@ -211,8 +256,12 @@ static void o2_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
     if (a->Bprev && a->xprev) {
         has_prev = 1;
         int64_t ob = ((int64_t)s * G + g) * N * R, ox = ((int64_t)s * H + h) * P * R;
-        for (int n = 0; n < N; n++)
-            for (int j = 0; j < R; j++) bprot[n * R + j] = ld(a->Bprev, dtp, ob + j * N + n);
+        double *row = malloc((size_t)N * sizeof *row);
+        for (int j = 0; j < R; j++) {
+            bc_row(a, a->Bprev, ob + j * N, h, a->B_bias, row);
+            for (int n = 0; n < N; n++) bprot[n * R + j] = row[n];
+        }
+        free(row);
         for (int p = 0; p < P; p++)
             for (int j = 0; j < R; j++) xp[p * R + j] = ld(a->xprev, dtp, ox + j * P + p);
     }
@@ -227,11 +276,14 @@ static void o2_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
         const double beta = (1.0 - lam) * dt * alpha, gamma = lam * dt;
         for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, (t * H + h) * K + k);
         const int64_t ob = (t * G + g) * N * R, ox = (t * H + h) * P * R;
-        for (int n = 0; n < N; n++)
-            for (int j = 0; j < R; j++) {
-                braw[n * R + j] = ld(a->B, dtp, ob + j * N + n);
-                craw[n * R + j] = ld(a->C, dtp, ob + j * N + n);
+        for (int j = 0; j < R; j++) {
+            bc_row(a, a->B, ob + j * N, h, a->B_bias, rowb);
+            bc_row(a, a->C, ob + j * N, h, a->C_bias, rowc);
+            for (int n = 0; n < N; n++) {
+                braw[n * R + j] = rowb[n];
+                craw[n * R + j] = rowc[n];
             }
+        }
         for (int p = 0; p < P; p++)
             for (int j = 0; j < R; j++) xc[p * R + j] = ld(a->x, dtp, ox + j * P + p);
         rot_vec(brot, braw, psi, K, R, -1);
@@ -250,7 +302,7 @@ static void o2_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
             for (int i = 0; i < R; i++) {
                 double acc = 0;
                 for (int n = 0; n < N; n++) acc += crot[n * R + i] * hr[n * P + p];
-                yt[i * P + p] = acc + Dh * xc[p * R + i];
+                yt[i * P + p] = gate(a, acc + Dh * xc[p * R + i], ox + i * P + p);
             }
         memcpy(bprot, brot, (size_t)N * R * sizeof *bprot);
         memcpy(xp, xc, (size_t)P * R * sizeof *xp);
@@ -267,7 +319,7 @@ static void o2_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
             }
         }
     }
-    free(hr); free(psi); free(braw); free(craw); free(brot); free(crot);
+    free(hr); free(psi); free(braw); free(craw); free(brot); free(crot); free(rowb); free(rowc);
     free(bprot); free(xp); free(xc);
 }
 
@@ -287,6 +339,7 @@ static void o3_slab(const m3o_args *a, int s, int h, double *y_slab) {
     double *Bt = malloc(T * N * R * sizeof *Bt), *Ct = malloc(T * N * R * sizeof *Ct);
     double *X = malloc(T * P * R * sizeof *X);
     double *psi = calloc(K, sizeof *psi), *tmp = malloc((size_t)N * R * sizeof *tmp);
+    double *row = malloc((size_t)N * sizeof *row);
     const double Ah = a->A[h], Dh = a->D ? a->D[h] : 0.0;
 
     for (int64_t t = 0; t < T; t++) {
@@ -297,11 +350,15 @@ static void o3_slab(const m3o_args *a, int s, int h, double *y_slab) {
         gamma[t] = lam * dt;
         for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, (tg * H + h) * K + k);
         const int64_t ob = (tg * G + g) * N * R, ox = (tg * H + h) * P * R;
-        for (int n = 0; n < N; n++)
-            for (int j = 0; j < R; j++) tmp[n * R + j] = ld(a->B, dtp, ob + j * N + n);
+        for (int j = 0; j < R; j++) {
+            bc_row(a, a->B, ob + j * N, h, a->B_bias, row);
+            for (int n = 0; n < N; n++) tmp[n * R + j] = row[n];
+        }
         rot_vec(Bt + t * N * R, tmp, psi, K, R, -1);
-        for (int n = 0; n < N; n++)
-            for (int j = 0; j < R; j++) tmp[n * R + j] = ld(a->C, dtp, ob + j * N + n);
+        for (int j = 0; j < R; j++) {
+            bc_row(a, a->C, ob + j * N, h, a->C_bias, row);
+            for (int n = 0; n < N; n++) tmp[n * R + j] = row[n];
+        }
         rot_vec(Ct + t * N * R, tmp, psi, K, R, -1);
         for (int p = 0; p < P; p++)
             for (int j = 0; j < R; j++) X[t * P * R + p * R + j] = ld(a->x, dtp, ox + j * P + p);
@@ -333,10 +390,11 @@ static void o3_slab(const m3o_args *a, int s, int h, double *y_slab) {
                         acc += L[t * T + s2] * cb * X[s2 * P * R + p * R + j];
                     }
                 }
-                y_slab[t * P * R + i * P + p] = acc + Dh * X[t * P * R + p * R + i];
+                y_slab[t * P * R + i * P + p] =
+                    gate(a, acc + Dh * X[t * P * R + p * R + i], ((t0 + t) * H + h) * P * R + i * P + p);
             }
     free(alpha); free(beta); free(gamma); free(L1); free(L2); free(L);
-    free(Bt); free(Ct); free(X); free(psi); free(tmp);
+    free(Bt); free(Ct); free(X); free(psi); free(tmp); free(row);
 }
 
 /* ------------------------------------------------------------ exports ---- */
@@ -344,6 +402,7 @@ static int check(const m3o_args *a) {
     if (!a || a->nseq < 0 || a->H <= 0 || a->G <= 0 || a->P <= 0 || a->N <= 0 || a->R <= 0) return 1;
     if (a->N % 2 || a->H % a->G) return 1;
     if (!a->x || !a->dt || !a->lam || !a->theta || !a->B || !a->C || !a->A) return 1;
+    if (a->bc_norm && !(a->bc_eps >= 0.0)) return 1;
     return 0;
 }
 

@@ -9,7 +9,9 @@ All arrays use the flat token axis (padded batches are flattened to
 ``batch*seqlen`` tokens, sequence ``s`` starting at ``s*seqlen``):
 ``x [T,H,R,P]``, ``dt, lam [T,H]``, ``theta [T,H,N/2]``, ``B, C [T,G,R,N]``,
 ``A, D [H]``, ``h_in [S,H,N,P]``, ``Bprev [S,G,R,N]``, ``xprev [S,H,R,P]``
-(rank-major: the R columns of B_t, X_t are stored one after another).
+(rank-major: the R columns of B_t, X_t are stored one after another), and the
+optional block prologue/epilogue: ``B_bias, C_bias [H,N]``, ``z`` (like x),
+``bc_norm`` (bool) and ``bc_eps``.
 Token inputs may be float64, float32 or uint16 (bf16 bit patterns); they are
 converted exactly to double inside the oracle.
 """
@@ -49,6 +51,8 @@ class _Args(ctypes.Structure):
         ("theta", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
         ("A", ctypes.c_void_p), ("D", ctypes.c_void_p), ("h_in", ctypes.c_void_p),
         ("Bprev", ctypes.c_void_p), ("xprev", ctypes.c_void_p),
+        ("B_bias", ctypes.c_void_p), ("C_bias", ctypes.c_void_p), ("z", ctypes.c_void_p),
+        ("bc_norm", ctypes.c_int32), ("bc_eps", ctypes.c_double),
     ]
 
 
@@ -94,14 +98,14 @@ class _Pack:
         keep = {}
         tok = [inp[k] for k in ("x", "dt", "lam", "theta", "B", "C")]
         tag = _tag(tok[0])
-        for k in ("x", "dt", "lam", "theta", "B", "C", "Bprev", "xprev"):
+        for k in ("x", "dt", "lam", "theta", "B", "C", "Bprev", "xprev", "z"):
             v = inp.get(k)
             if v is not None:
                 v = np.ascontiguousarray(v)
                 if _tag(v) != tag:
                     raise TypeError(f"{k}: all token inputs must share one dtype")
             keep[k] = v
-        for k in ("A", "D", "h_in"):
+        for k in ("A", "D", "h_in", "B_bias", "C_bias"):
             v = inp.get(k)
             keep[k] = None if v is None else np.ascontiguousarray(v, dtype=np.float64)
         x = keep["x"]
@@ -117,7 +121,9 @@ class _Pack:
                           H, G, P, N, R, tag,
                           _ptr(keep["x"]), _ptr(keep["dt"]), _ptr(keep["lam"]), _ptr(keep["theta"]),
                           _ptr(keep["B"]), _ptr(keep["C"]), _ptr(keep["A"]), _ptr(keep["D"]),
-                          _ptr(keep["h_in"]), _ptr(keep["Bprev"]), _ptr(keep["xprev"]))
+                          _ptr(keep["h_in"]), _ptr(keep["Bprev"]), _ptr(keep["xprev"]),
+                          _ptr(keep["B_bias"]), _ptr(keep["C_bias"]), _ptr(keep["z"]),
+                          1 if inp.get("bc_norm") else 0, float(inp.get("bc_eps", 0.0)))
 
 
 def flatten(inp: dict) -> tuple[dict, np.ndarray, np.ndarray]:
@@ -125,8 +131,9 @@ def flatten(inp: dict) -> tuple[dict, np.ndarray, np.ndarray]:
     inputs (key ``cu_seqlens``, batch 1) take their table from cu_seqlens."""
     out = dict(inp)
     b, L = inp["x"].shape[0], inp["x"].shape[1]
-    for k in ("x", "dt", "lam", "theta", "B", "C"):
-        out[k] = inp[k].reshape((b * L,) + inp[k].shape[2:])
+    for k in ("x", "dt", "lam", "theta", "B", "C", "z"):
+        if inp.get(k) is not None:
+            out[k] = inp[k].reshape((b * L,) + inp[k].shape[2:])
     if inp.get("cu_seqlens") is not None:
         if b != 1:
             raise ValueError("packed inputs have batch 1")

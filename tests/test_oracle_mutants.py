@@ -4,8 +4,9 @@ which do not compare the oracle's two recurrence forms with each other fail.
 
 Mistakes planted: the previous-token term skipping the step's rotation/decay,
 the rotation direction, the sign of C's or B's imaginary part, trapezoid
-weights swapped, rank columns mixed, the D term dropped, and a stale previous
-token."""
+weights swapped, rank columns mixed, the D term dropped, a stale previous
+token, a sigmoid instead of a SiLU gate, an L2 instead of an RMS norm, and
+every head taking head 0's bias."""
 import os
 import shutil
 import subprocess
@@ -19,14 +20,18 @@ MUTATIONS = {
     "prev_not_rotated": ("hc[k * P + p] = z[k] * (hc[k * P + p] + delta * prev) + gamma * cur;",
                          "hc[k * P + p] = z[k] * hc[k * P + p] + delta * prev + gamma * cur;"),
     "rotation_sign": ("z[k] = decay * (cos(ang) + I * sin(ang));", "z[k] = decay * (cos(ang) - I * sin(ang));"),
-    "c_imag_sign": ("cc[k * R + j] = ld(a->C, dtp, ob + j * N + 2 * k) -",
-                    "cc[k * R + j] = ld(a->C, dtp, ob + j * N + 2 * k) +"),
-    "b_imag_sign": ("I * ld(a->B, dtp, ob + j * N + 2 * k + 1);\n                cc",
-                    "-I * ld(a->B, dtp, ob + j * N + 2 * k + 1);\n                cc"),
+    "c_imag_sign": ("cc[k * R + j] = row2[2 * k] - I * row2[2 * k + 1];",
+                    "cc[k * R + j] = row2[2 * k] + I * row2[2 * k + 1];"),
+    "b_imag_sign": ("bc[k * R + j] = row[2 * k] + I * row[2 * k + 1];",
+                    "bc[k * R + j] = row[2 * k] - I * row[2 * k + 1];"),
     "weights_swapped": ("const double delta = (1.0 - lam) * dt, gamma = lam * dt;",
                         "const double gamma = (1.0 - lam) * dt, delta = lam * dt;"),
     "rank_mixed": ("cur += bc[k * R + j] * xc[p * R + j];", "cur += bc[k * R + j] * xc[p * R + 0];"),
-    "no_skip_term": ("yt[i * P + p] = creal(acc) + Dh * xc[p * R + i];", "yt[i * P + p] = creal(acc);"),
+    "no_skip_term": ("yt[i * P + p] = gate(a, creal(acc) + Dh * xc[p * R + i], ox + i * P + p);",
+                     "yt[i * P + p] = gate(a, creal(acc), ox + i * P + p);"),
+    "gate_sigmoid_only": ("return y * v / (1.0 + exp(-v));", "return y / (1.0 + exp(-v));"),
+    "norm_without_mean": ("1.0 / sqrt(ss / N + a->bc_eps)", "1.0 / sqrt(ss + a->bc_eps)"),
+    "bias_of_head_zero": ("out[n] += bias[(int64_t)h * N + n];", "out[n] += bias[n];"),
     "stale_previous": ("memcpy(bp, bc, (size_t)K * R * sizeof *bp);\n        memcpy(xp, xc, (size_t)P * R * sizeof *xp);\n",
                        ""),
 }

@@ -349,3 +349,86 @@ def test_input_dtype_tags_are_exact(oracle):
     yc, _ = oracle.scan({k: v for k, v in as64.items() if k != "meta"}, form=1)
     assert np.array_equal(ya, yb) and np.array_equal(ya, yc)
     assert inp["x"].dtype == np.float32
+
+
+# --------------------------------------------------------------------------
+# Block prologue and epilogue ("Architectural Integration": BC normalization,
+# BC biases, output gating).
+@pytest.mark.parametrize("form", [1, 2])
+def test_bc_norm_is_scale_invariant_per_column(oracle, form):
+    """RMS-normalizing each B and C column makes the layer blind to a positive
+    rescaling of any single (token, group, rank) column of B or C, including the
+    previous token's; biases added after the norm keep that property."""
+    rng = np.random.default_rng(71)
+    inp = rand_inputs(rng, G=4, state=True, prev=True)
+    inp.update(bc_norm=True, bc_eps=0.0, B_bias=rng.uniform(0, 1, (4, 6)), C_bias=rng.uniform(0, 1, (4, 6)))
+    y0, h0 = oracle.scan(inp, form=form)
+    scaled = dict(inp)
+    for k in ("B", "C", "Bprev"):
+        shape = inp[k].shape[:-1] + (1,)
+        scaled[k] = inp[k] * rng.uniform(0.2, 5.0, shape)
+    y1, h1 = oracle.scan(scaled, form=form)
+    assert relerr(y1, y0) < 1e-12 and relerr(h1, h0) < 1e-12
+
+
+def test_bc_norm_fixes_unit_rms_columns(oracle):
+    """A column that already has unit RMS passes the norm unchanged: with every
+    column scaled to unit RMS beforehand, the normed layer equals the plain one.
+    With the scale invariance above this pins the norm to v / rms(v)."""
+    rng = np.random.default_rng(72)
+    inp = rand_inputs(rng, state=True, prev=True)
+    for k in ("B", "C", "Bprev"):
+        v = inp[k]
+        inp[k] = v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True))
+    y0, h0 = oracle.scan(inp)
+    y1, h1 = oracle.scan(dict(inp, bc_norm=True, bc_eps=0.0))
+    assert relerr(y1, y0) < 1e-13 and relerr(h1, h0) < 1e-13
+
+
+def test_bc_bias_is_a_per_head_column_offset(oracle):
+    """Zero B and C data plus per-head biases equals the plain layer fed, for
+    every token and rank column, B and C equal to that head's bias vectors
+    (one group per head)."""
+    rng = np.random.default_rng(73)
+    H, N, R = 4, 6, 2
+    inp = rand_inputs(rng, H=H, G=H, N=N, R=R, state=True, prev=True)
+    bb, cb = rng.standard_normal((H, N)), rng.standard_normal((H, N))
+    plain = dict(inp)
+    plain["B"] = np.broadcast_to(bb[None, None, :, None, :], inp["B"].shape).copy()
+    plain["C"] = np.broadcast_to(cb[None, None, :, None, :], inp["C"].shape).copy()
+    plain["Bprev"] = np.broadcast_to(bb[None, :, None, :], inp["Bprev"].shape).copy()
+    biased = dict(inp, B=np.zeros_like(inp["B"]), C=np.zeros_like(inp["C"]), Bprev=np.zeros_like(inp["Bprev"]),
+                  B_bias=bb, C_bias=cb)
+    y0, h0 = oracle.scan(plain)
+    y1, h1 = oracle.scan(biased)
+    assert relerr(y1, y0) < 1e-13 and relerr(h1, h0) < 1e-13
+
+
+def test_output_gate(oracle):
+    """y <- y * SiLU(z): SiLU(0) = 0, SiLU(1) is the logistic function at 1
+    (0.7310585786300049), SiLU(v) -> v for large v; the state is not gated."""
+    rng = np.random.default_rng(74)
+    inp = rand_inputs(rng, state=True, prev=True)
+    y, h = oracle.scan(inp)
+    for zval, factor in ((0.0, 0.0), (1.0, 0.7310585786300049), (40.0, 40.0)):
+        yg, hg = oracle.scan(dict(inp, z=np.full_like(inp["x"], zval)))
+        assert np.allclose(yg, factor * y, rtol=1e-14, atol=1e-300)
+        assert np.array_equal(hg, h)
+
+
+def test_prologue_and_gate_in_decode(oracle):
+    """The decode step applies the same prologue and gate as the scan."""
+    rng = np.random.default_rng(75)
+    inp = rand_inputs(rng, b=3, L=6, state=True, prev=True)
+    inp.update(bc_norm=True, bc_eps=1e-6, B_bias=rng.uniform(0, 1, (4, 6)), C_bias=rng.uniform(0, 1, (4, 6)),
+               z=rng.standard_normal(inp["x"].shape))
+    y_all, h_all = oracle.scan(inp)
+    h = inp["h_in"]
+    for t in range(inp["x"].shape[1]):
+        step = {k: inp[k][:, t] for k in ("x", "dt", "lam", "theta", "B", "C", "z")}
+        step.update(A=inp["A"], D=inp["D"], B_bias=inp["B_bias"], C_bias=inp["C_bias"], bc_norm=True, bc_eps=1e-6)
+        step["Bprev"] = inp["Bprev"] if t == 0 else inp["B"][:, t - 1]
+        step["xprev"] = inp["xprev"] if t == 0 else inp["x"][:, t - 1]
+        y, h = oracle.decode(step, h)
+        assert relerr(y, y_all[:, t]) < 1e-12
+    assert relerr(h, h_all) < 1e-12
