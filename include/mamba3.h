@@ -44,6 +44,30 @@
  *   - y must not alias any input. h_out may alias h_in (same slab layout).
  *   - x, theta, B, C, Bprev, xprev, y and the states must be 16-byte aligned;
  *     dt and lam need element alignment, A, D and cu_seqlens 4 bytes.
+ *   - Callers zero-initialise the argument structs, so that fields added in a
+ *     later minor version (all of which default to "off" at zero) stay off.
+ *
+ * Block prologue and epilogue (ABI 1.1, fields B_bias, C_bias, z, bc_norm,
+ * bc_eps of both argument structs; all zero = off). The paper summary's
+ * section "Architectural Integration" places a normalization on B and C right
+ * after their projection, adds learned per-head, per-channel biases to B and
+ * C after it, and gates the layer output. The library fuses these steps into
+ * the scan and the decode step:
+ *   bc_norm = 1  every column of B and C (the N values of one token, group and
+ *                rank column; Bprev's columns too) is divided by
+ *                sqrt(mean of its squares + bc_eps): an RMS norm without a
+ *                gain. bc_norm must be 0 or 1; with bc_norm = 1, bc_eps must be
+ *                finite and >= 0.
+ *   B_bias, C_bias  [H, N] fp32 (16-byte aligned) or NULL: row h is added to
+ *                every (normalised) column of B, C (and Bprev) that head h
+ *                reads, for every rank column. With G < H the heads of a group
+ *                then see different B and C.
+ *   z            gate in the token dtype with the layout of x (16-byte
+ *                aligned) or NULL: y <- y * SiLU(z), SiLU(v) = v / (1 + e^-v),
+ *                applied after the D x term.
+ * The normalisation and biases act before the rotation; the recurrence is
+ * otherwise unchanged. y must not alias z or a bias; the states must not
+ * alias them either.
  */
 #ifndef MAMBA3_H
 #define MAMBA3_H
@@ -99,6 +123,11 @@ typedef struct {
     float *h_out;
     void *workspace;             /* reserved: pass NULL / 0 when the size query returns 0 */
     size_t workspace_bytes;
+    /* Block prologue and epilogue fused into the scan (ABI 1.1; see below). */
+    const float *B_bias, *C_bias;
+    const void *z;
+    int32_t bc_norm;
+    float bc_eps;
 } mamba3_scan_args;
 
 /* Pure host check of every argument (no HIP call). */
@@ -126,6 +155,11 @@ typedef struct {
     const float *A, *D;
     float *h;
     void *y;
+    /* Block prologue and epilogue (ABI 1.1; see below). */
+    const float *B_bias, *C_bias;
+    const void *z;
+    int32_t bc_norm;
+    float bc_eps;
 } mamba3_decode_args;
 
 mamba3_status mamba3_decode_validate(const mamba3_decode_args *args);

@@ -30,6 +30,7 @@ class ScanArgs(ctypes.Structure):
         ("x", _vp), ("dt", _vp), ("lam", _vp), ("theta", _vp), ("B", _vp), ("C", _vp),
         ("A", _vp), ("D", _vp), ("h_in", _vp), ("Bprev", _vp), ("xprev", _vp),
         ("y", _vp), ("h_out", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("B_bias", _vp), ("C_bias", _vp), ("z", _vp), ("bc_norm", _i32), ("bc_eps", ctypes.c_float),
     ]
 
 
@@ -40,6 +41,7 @@ class DecodeArgs(ctypes.Structure):
         ("ngroups", _i32), ("dtype", _i32),
         ("x", _vp), ("dt", _vp), ("lam", _vp), ("theta", _vp), ("B", _vp), ("C", _vp),
         ("Bprev", _vp), ("xprev", _vp), ("A", _vp), ("D", _vp), ("h", _vp), ("y", _vp),
+        ("B_bias", _vp), ("C_bias", _vp), ("z", _vp), ("bc_norm", _i32), ("bc_eps", ctypes.c_float),
     ]
 
 
@@ -106,14 +108,16 @@ def _stream(stream):
 
 
 def scan_args(x, dt, lam, theta, B, C, A, D=None, *, y, h_in=None, h_out=None, Bprev=None, xprev=None,
-              cu_seqlens=None, chunk=64) -> ScanArgs:
+              cu_seqlens=None, chunk=64, B_bias=None, C_bias=None, z=None, bc_norm=False,
+              bc_eps=1e-5) -> ScanArgs:
     """Builds a ScanArgs from tensors in the library's layouts (see mamba3.h)."""
     b, L, H, R, P = x.shape
     G, N = B.shape[2], B.shape[4]
     nseq = int(cu_seqlens.numel()) - 1 if cu_seqlens is not None else 0
     return ScanArgs(b, L, H, P, N, R, G, chunk, _dtype_code(x), _ptr(cu_seqlens), nseq,
                     _ptr(x), _ptr(dt), _ptr(lam), _ptr(theta), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
-                    _ptr(h_in), _ptr(Bprev), _ptr(xprev), _ptr(y), _ptr(h_out), None, 0)
+                    _ptr(h_in), _ptr(Bprev), _ptr(xprev), _ptr(y), _ptr(h_out), None, 0,
+                    _ptr(B_bias), _ptr(C_bias), _ptr(z), int(bool(bc_norm)), float(bc_eps))
 
 
 def mamba3_scan_validate(args: ScanArgs) -> int:
@@ -125,10 +129,12 @@ def mamba3_scan_workspace_size(args: ScanArgs) -> int:
 
 
 def mamba3_scan_fwd(x, dt, lam, theta, B, C, A, D=None, *, y=None, h_in=None, h_out=None, Bprev=None,
-                    xprev=None, cu_seqlens=None, chunk=64, want_state=True, stream=None):
+                    xprev=None, cu_seqlens=None, chunk=64, want_state=True, stream=None, B_bias=None,
+                    C_bias=None, z=None, bc_norm=False, bc_eps=1e-5):
     """Chunked scan over whole sequences. Tensors are device tensors in the
     layouts of mamba3.h; y and h_out are allocated when not given. Returns
-    (y, h_out)."""
+    (y, h_out). B_bias, C_bias ([H, N] fp32), z (layout of x) and bc_norm /
+    bc_eps switch on the fused B/C normalisation, B/C biases and output gate."""
     import torch
     if y is None:
         y = torch.empty_like(x)
@@ -136,30 +142,36 @@ def mamba3_scan_fwd(x, dt, lam, theta, B, C, A, D=None, *, y=None, h_in=None, h_
         S = int(cu_seqlens.numel()) - 1 if cu_seqlens is not None else x.shape[0]
         h_out = torch.empty((S, x.shape[2], B.shape[4], x.shape[4]), dtype=torch.float32, device=x.device)
     a = scan_args(x, dt, lam, theta, B, C, A, D, y=y, h_in=h_in, h_out=h_out, Bprev=Bprev, xprev=xprev,
-                  cu_seqlens=cu_seqlens, chunk=chunk)
+                  cu_seqlens=cu_seqlens, chunk=chunk, B_bias=B_bias, C_bias=C_bias, z=z, bc_norm=bc_norm,
+                  bc_eps=bc_eps)
     st = lib().mamba3_scan_fwd(ctypes.byref(a), _stream(stream))
     if st != MAMBA3_OK:
         raise Mamba3Error(st, "mamba3_scan_fwd")
     return y, h_out
 
 
-def decode_args(x, dt, lam, theta, B, C, A, D=None, *, h, y, Bprev=None, xprev=None) -> DecodeArgs:
+def decode_args(x, dt, lam, theta, B, C, A, D=None, *, h, y, Bprev=None, xprev=None, B_bias=None, C_bias=None,
+                z=None, bc_norm=False, bc_eps=1e-5) -> DecodeArgs:
     b, H, R, P = x.shape
     G, N = B.shape[1], B.shape[3]
     return DecodeArgs(b, H, P, N, R, G, _dtype_code(x), _ptr(x), _ptr(dt), _ptr(lam), _ptr(theta), _ptr(B),
-                      _ptr(C), _ptr(Bprev), _ptr(xprev), _ptr(A), _ptr(D), _ptr(h), _ptr(y))
+                      _ptr(C), _ptr(Bprev), _ptr(xprev), _ptr(A), _ptr(D), _ptr(h), _ptr(y),
+                      _ptr(B_bias), _ptr(C_bias), _ptr(z), int(bool(bc_norm)), float(bc_eps))
 
 
 def mamba3_decode_validate(args: DecodeArgs) -> int:
     return lib().mamba3_decode_validate(ctypes.byref(args))
 
 
-def mamba3_decode_step(x, dt, lam, theta, B, C, A, D=None, *, h, y=None, Bprev=None, xprev=None, stream=None):
-    """One decode step; h (fp32 [batch,H,N,P]) is updated in place. Returns y."""
+def mamba3_decode_step(x, dt, lam, theta, B, C, A, D=None, *, h, y=None, Bprev=None, xprev=None, stream=None,
+                       B_bias=None, C_bias=None, z=None, bc_norm=False, bc_eps=1e-5):
+    """One decode step; h (fp32 [batch,H,N,P]) is updated in place. Returns y.
+    The prologue / epilogue keywords are those of mamba3_scan_fwd."""
     import torch
     if y is None:
         y = torch.empty_like(x)
-    a = decode_args(x, dt, lam, theta, B, C, A, D, h=h, y=y, Bprev=Bprev, xprev=xprev)
+    a = decode_args(x, dt, lam, theta, B, C, A, D, h=h, y=y, Bprev=Bprev, xprev=xprev, B_bias=B_bias,
+                    C_bias=C_bias, z=z, bc_norm=bc_norm, bc_eps=bc_eps)
     st = lib().mamba3_decode_step(ctypes.byref(a), _stream(stream))
     if st != MAMBA3_OK:
         raise Mamba3Error(st, "mamba3_decode_step")

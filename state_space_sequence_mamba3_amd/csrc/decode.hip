@@ -14,6 +14,11 @@
 // state column); other head dims use the tile kernel (4 columns x ROWS rows per
 // thread). y is reduced over rows in a fixed order (deterministic). Token
 // layouts are rank-major (B [R][N], x and y [R][P]).
+//
+// The EPI instantiations add the block prologue and epilogue (section
+// "Architectural Integration"): each staged B, C and Bprev column is scaled to
+// unit RMS and gets the head's bias before the update, and y is multiplied by
+// SiLU(z) after the D term.
 #include "m3_common.h"
 
 namespace m3 {
@@ -24,7 +29,17 @@ struct DecodeParams {
     float *h;
     void *y;
     int32_t H, G;
+    const float *Bb, *Cb;   // prologue biases [H, N], or NULL
+    const void *z;          // output gate (token dtype), or NULL
+    int32_t norm;           // 1: B, C, Bprev columns scaled to unit RMS
+    float eps;
 };
+
+// Stand-in for an absent bias row or gate (read-only zeros), so that prologue loads are
+// unconditional.
+__constant__ float kZeroRow[256];
+
+__device__ __forceinline__ float silu(float v, bool fast) { return v / (1.f + (fast ? __expf(-v) : expf(-v))); }
 
 // Copy `count` elements of T (count * sizeof(T) a multiple of 16) into LDS as
 // fp32 with 16-byte loads; piece i goes to thread (t0 + i) mod TPB, so arrays
@@ -43,7 +58,7 @@ __device__ __forceinline__ void stage_f32(float *dst, const T *src, int count, i
     }
 }
 
-template <typename T, int N, int P, int R, int TPB>
+template <typename T, int N, int P, int R, int TPB, bool EPI>
 __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
     constexpr int PG = P / 4;                 // column groups of 4
     constexpr int NRG = TPB / PG;             // row groups
@@ -87,6 +102,22 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
     const float Dh = pr.D ? pr.D[hh] : 0.f;
     const bool has_prev = pr.Bprev != nullptr;
     __syncthreads();
+    if constexpr (EPI) {   // prologue: one thread per staged column of B, C, Bprev
+        static_assert(3 * R <= TPB, "decode prologue");
+        const int arr = tid / R, j = tid % R;
+        if (tid < 3 * R && (arr < 2 || has_prev)) {
+            float *col = (arr == 0 ? sB : arr == 1 ? sC : sBp) + j * N;
+            const float *bias = arr == 1 ? pr.Cb : pr.Bb;
+            float inv = 1.f;
+            if (pr.norm) {
+                float ss = 0.f;
+                for (int n = 0; n < N; n++) ss += col[n] * col[n];
+                inv = 1.f / sqrtf(ss * (1.f / N) + pr.eps);
+            }
+            for (int n = 0; n < N; n++) col[n] = col[n] * inv + (bias ? bias[hh * N + n] : 0.f);
+        }
+        __syncthreads();
+    }
 
     float xv[4][R], xpv[4][R];
 #pragma unroll
@@ -163,6 +194,8 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
 #pragma unroll
         for (int q = 0; q < NWV; q++) acc += red[q][e];
         acc += Dh * sX[e];
+        if constexpr (EPI)
+            if (pr.z) acc *= silu(to_f(((const T *)pr.z)[(int64_t)bh * P * R + e]), FAST);
         y[e] = from_f<T>(acc);
     }
 }
@@ -172,10 +205,15 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
 // [16 w, 16 w + 16). The update is applied term by term (previous-token term, rotation and
 // decay, current-token term, readout), each a pass over the lane's 16 rows, so few values are
 // live at once and eight waves per SIMD stay resident.
-template <typename T, int N, int R>
+//
+// With EPI the prologue is fused into the staging: the 16-byte pieces of one column sit in
+// N / VW consecutive lanes of one wave, so each column's sum of squares is a butterfly of wave
+// shuffles, and every thread scales its own piece and adds its slice of the bias row.
+template <typename T, int N, int R, bool EPI>
 __global__ __launch_bounds__(N / 16 * 64) __attribute__((amdgpu_waves_per_eu(8))) void k_decode_col(DecodeParams pr) {
     constexpr int P = 64, ROWS = 16, NW = N / ROWS, TPB = NW * 64;
     static_assert(N % ROWS == 0 && (N * R) % (16 / sizeof(T)) == 0, "decode column tiling");
+    static_assert(P * R <= TPB && N <= 256 && P * R * sizeof(T) <= sizeof(kZeroRow), "decode column epilogue");
     __shared__ __attribute__((aligned(16))) float sB[R * N], sC[R * N], sBp[R * N];
     __shared__ __attribute__((aligned(16))) float2 sCS[N / 2];
     __shared__ float red[NW][R * P];
@@ -192,12 +230,21 @@ __global__ __launch_bounds__(N / 16 * 64) __attribute__((amdgpu_waves_per_eu(8))
     // All token loads are unconditional and issued before the state loads, and each thread
     // waits only for its own: loads complete in order, so the staging below does not wait for
     // the state. Thread t loads 16-byte piece t % PCS of B (t < PCS), C or Bprev.
-    constexpr int VW = 16 / sizeof(T), PCS = N * R / VW;
-    static_assert(3 * PCS <= TPB, "decode staging");
+    constexpr int VW = 16 / sizeof(T), PCS = N * R / VW, CPC = N / VW;   // pieces per array, per column
+    static_assert(3 * PCS <= TPB && CPC <= 64 && (CPC & (CPC - 1)) == 0, "decode staging");
     const int arr = tid / PCS, pc = tid % PCS;
     const T *src = (arr == 1) ? (const T *)pr.C : (arr == 2 && has_prev) ? (const T *)pr.Bprev : (const T *)pr.B;
     typedef T vec_t __attribute__((ext_vector_type(VW)));
     const vec_t piece = *(const vec_t *)(src + obc + pc * VW);
+    f32x4 bias4[VW / 4];
+    T zr{};
+    if constexpr (EPI) {
+        const float *Bb = pr.Bb ? pr.Bb + hh * N : kZeroRow, *Cb = pr.Cb ? pr.Cb + hh * N : kZeroRow;
+        const float *bsrc = ((arr == 1) ? Cb : Bb) + (pc % CPC) * VW;
+#pragma unroll
+        for (int q = 0; q < VW / 4; q++) bias4[q] = *(const f32x4 *)(bsrc + 4 * q);
+        zr = *(pr.z ? (const T *)pr.z + ox + min(tid, P * R - 1) : (const T *)kZeroRow);
+    }
     T xr[R], xpr[R];
 #pragma unroll
     for (int j = 0; j < R; j++) {
@@ -214,10 +261,29 @@ __global__ __launch_bounds__(N / 16 * 64) __attribute__((amdgpu_waves_per_eu(8))
 #pragma unroll
     for (int r = 0; r < ROWS; r++) st[r] = __builtin_nontemporal_load(hs + (n0 + r) * P + p);
 
+    // fp32 inputs take the precise exp, sincos and root, bf16 inputs the hardware approximations
+    constexpr bool FAST = sizeof(T) == 2;
+    float pv[VW];
+#pragma unroll
+    for (int e = 0; e < VW; e++) pv[e] = (float)piece[e];
+    if constexpr (EPI) {
+        float inv = 1.f;
+        if (pr.norm) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < VW; e++) ss += pv[e] * pv[e];
+#pragma unroll
+            for (int off = 1; off < CPC; off <<= 1) ss += __shfl_xor(ss, off, 64);
+            const float ms = ss * (1.f / N) + pr.eps;
+            inv = FAST ? rsqrtf(ms) : 1.f / sqrtf(ms);
+        }
+#pragma unroll
+        for (int e = 0; e < VW; e++) pv[e] = pv[e] * inv + bias4[e / 4][e % 4];
+    }
     if (arr < 2 || (arr == 2 && has_prev)) {
         float *dst = (arr == 0) ? sB : (arr == 1) ? sC : sBp;
 #pragma unroll
-        for (int e = 0; e < VW; e++) dst[pc * VW + e] = (float)piece[e];
+        for (int e = 0; e < VW; e++) dst[pc * VW + e] = pv[e];
     }
     float xv[R], xpv[R];
 #pragma unroll
@@ -225,8 +291,6 @@ __global__ __launch_bounds__(N / 16 * 64) __attribute__((amdgpu_waves_per_eu(8))
         xv[j] = to_f(xr[j]);
         xpv[j] = has_prev ? to_f(xpr[j]) : 0.f;
     }
-    // fp32 inputs take the precise exp and sincos, bf16 inputs the hardware approximations
-    constexpr bool FAST = sizeof(T) == 2;
     if (tid < N / 2) {   // one sincos per state pair, shared through LDS
         const float a = dt * to_f(thr);
         float sn, cs;
@@ -293,25 +357,35 @@ __global__ __launch_bounds__(N / 16 * 64) __attribute__((amdgpu_waves_per_eu(8))
     for (int i = 0; i < R; i++) red[w][i * P + p] = yp[i];
     __syncthreads();
     T *y = (T *)pr.y + (int64_t)bh * P * R;
-    for (int e = tid; e < P * R; e += TPB) {
-        float acc = Dh * to_f(((const T *)pr.x)[ox + e]);
+    if (tid < P * R) {
+        float acc = Dh * to_f(((const T *)pr.x)[ox + tid]);
 #pragma unroll
-        for (int q = 0; q < NW; q++) acc += red[q][e];
-        y[e] = from_f<T>(acc);
+        for (int q = 0; q < NW; q++) acc += red[q][tid];
+        if constexpr (EPI)
+            if (pr.z) acc *= silu(to_f(zr), FAST);
+        y[tid] = from_f<T>(acc);
     }
+}
+
+template <typename T, int N, int P, int R, bool EPI>
+static void launch_kernel(const DecodeParams &p, int64_t nblk, hipStream_t st) {
+    constexpr int TPB = (N * P / 8 >= 256) ? 256 : N * P / 8;
+    if constexpr (P == 64)
+        hipLaunchKernelGGL((k_decode_col<T, N, R, EPI>), dim3((unsigned)nblk), dim3(N / 16 * 64), 0, st, p);
+    else
+        hipLaunchKernelGGL((k_decode<T, N, P, R, TPB, EPI>), dim3((unsigned)nblk), dim3(TPB), 0, st, p);
 }
 
 template <typename T, int N, int P, int R>
 static mamba3_status launch_one(const mamba3_decode_args *a, hipStream_t st) {
-    constexpr int TPB = (N * P / 8 >= 256) ? 256 : N * P / 8;
     DecodeParams p{a->x, a->dt, a->lam, a->theta, a->B, a->C, a->Bprev, a->xprev, a->A, a->D, a->h, a->y,
-                   a->nheads, a->ngroups};
+                   a->nheads, a->ngroups, a->B_bias, a->C_bias, a->z, a->bc_norm, a->bc_eps};
     int64_t nblk = (int64_t)a->batch * a->nheads;
     if (nblk == 0) return MAMBA3_OK;
-    if constexpr (P == 64)
-        hipLaunchKernelGGL((k_decode_col<T, N, R>), dim3((unsigned)nblk), dim3(N / 16 * 64), 0, st, p);
+    if (a->bc_norm || a->B_bias || a->C_bias || a->z)
+        launch_kernel<T, N, P, R, true>(p, nblk, st);
     else
-        hipLaunchKernelGGL((k_decode<T, N, P, R, TPB>), dim3((unsigned)nblk), dim3(TPB), 0, st, p);
+        launch_kernel<T, N, P, R, false>(p, nblk, st);
     return hipGetLastError() == hipSuccess ? MAMBA3_OK : MAMBA3_EHIP;
 }
 

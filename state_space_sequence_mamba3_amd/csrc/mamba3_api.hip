@@ -2,6 +2,8 @@
 // before any HIP call, so an error status means nothing was enqueued.
 #include <string.h>
 
+#include <cmath>
+
 #include "m3_common.h"
 
 namespace {
@@ -23,6 +25,17 @@ Range span(const void *p, int64_t elems, int64_t esize) {
     return {(const char *)p, (const char *)p + elems * esize};
 }
 
+// The fused block prologue / epilogue fields shared by both argument structs.
+mamba3_status check_prologue(int32_t bc_norm, float bc_eps, const float *B_bias, const float *C_bias,
+                             const void *z) {
+    if (bc_norm != 0 && bc_norm != 1) return MAMBA3_EINVAL;
+    if (bc_norm && !(bc_eps >= 0.f && std::isfinite(bc_eps))) return MAMBA3_EINVAL;   // NaN fails >= 0
+    const void *al16[] = {B_bias, C_bias, z};
+    for (const void *p : al16)
+        if (p && !aligned16(p)) return MAMBA3_EALIGN;
+    return MAMBA3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -39,7 +52,7 @@ const char *mamba3_status_string(mamba3_status s) {
     return "unknown status";
 }
 
-int32_t mamba3_version(void) { return 10000; }
+int32_t mamba3_version(void) { return 10100; }
 
 mamba3_status mamba3_scan_validate(const mamba3_scan_args *a) {
     if (!a) return MAMBA3_EINVAL;
@@ -63,6 +76,8 @@ mamba3_status mamba3_scan_validate(const mamba3_scan_args *a) {
     if (!aligned_elem(a->dt, a->dtype) || !aligned_elem(a->lam, a->dtype)) return MAMBA3_EALIGN;
     if (!aligned4(a->A) || (a->D && !aligned4(a->D)) || (a->cu_seqlens && !aligned4(a->cu_seqlens)))
         return MAMBA3_EALIGN;
+    mamba3_status pst = check_prologue(a->bc_norm, a->bc_eps, a->B_bias, a->C_bias, a->z);
+    if (pst != MAMBA3_OK) return pst;
     // y must not overlap any input
     const int64_t es = a->dtype == MAMBA3_BF16 ? 2 : 4;
     const int64_t H = a->nheads, G = a->ngroups, P = a->headdim, N = a->dstate, R = a->rank;
@@ -71,12 +86,13 @@ mamba3_status mamba3_scan_validate(const mamba3_scan_args *a) {
                    span(a->theta, T * H * (N / 2), es), span(a->B, T * G * N * R, es),
                    span(a->C, T * G * N * R, es), span(a->h_in, S * H * N * P, 4),
                    span(a->Bprev, S * G * N * R, es), span(a->xprev, S * H * P * R, es),
-                   span(a->h_out, S * H * N * P, 4)};
+                   span(a->h_out, S * H * N * P, 4), span(a->B_bias, H * N, 4), span(a->C_bias, H * N, 4),
+                   span(a->z, T * H * P * R, es)};
     for (Range r : ins)
         if (overlaps(y, r)) return MAMBA3_EINVAL;
     // h_out may be h_in exactly, but no other overlap with an input
     Range ho = span(a->h_out, S * H * N * P, 4);
-    Range ins2[] = {ins[0], ins[1], ins[2], ins[3], ins[4], ins[5], ins[7], ins[8]};
+    Range ins2[] = {ins[0], ins[1], ins[2], ins[3], ins[4], ins[5], ins[7], ins[8], ins[10], ins[11], ins[12]};
     for (Range r : ins2)
         if (overlaps(ho, r)) return MAMBA3_EINVAL;
     if (a->h_in && a->h_out && a->h_in != a->h_out && overlaps(ins[6], ho)) return MAMBA3_EINVAL;
@@ -119,6 +135,8 @@ mamba3_status mamba3_decode_validate(const mamba3_decode_args *a) {
         if (p && !aligned16(p)) return MAMBA3_EALIGN;
     if (!aligned_elem(a->dt, a->dtype) || !aligned_elem(a->lam, a->dtype)) return MAMBA3_EALIGN;
     if ((a->A && !aligned4(a->A)) || (a->D && !aligned4(a->D))) return MAMBA3_EALIGN;
+    mamba3_status pst = check_prologue(a->bc_norm, a->bc_eps, a->B_bias, a->C_bias, a->z);
+    if (pst != MAMBA3_OK) return pst;
     const int64_t es = a->dtype == MAMBA3_BF16 ? 2 : 4;
     const int64_t b = a->batch, H = a->nheads, G = a->ngroups, P = a->headdim, N = a->dstate, R = a->rank;
     Range y = span(a->y, b * H * P * R, es);
@@ -126,10 +144,11 @@ mamba3_status mamba3_decode_validate(const mamba3_decode_args *a) {
     Range ins[] = {span(a->x, b * H * P * R, es), span(a->dt, b * H, es), span(a->lam, b * H, es),
                    span(a->theta, b * H * (N / 2), es), span(a->B, b * G * N * R, es),
                    span(a->C, b * G * N * R, es), span(a->Bprev, b * G * N * R, es),
-                   span(a->xprev, b * H * P * R, es), hh};
+                   span(a->xprev, b * H * P * R, es), span(a->B_bias, H * N, 4), span(a->C_bias, H * N, 4),
+                   span(a->z, b * H * P * R, es), hh};
     for (Range r : ins)
         if (overlaps(y, r)) return MAMBA3_EINVAL;
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < 11; i++)
         if (overlaps(hh, ins[i])) return MAMBA3_EINVAL;
     if (!m3::decode_supported(a->dstate, a->headdim, a->rank, a->dtype)) return MAMBA3_EUNSUPPORTED;
     return MAMBA3_OK;

@@ -39,6 +39,16 @@
 //     stream through two register sets two blocks ahead, and the next chunk's
 //     dt, lam, theta and C rows are loaded while the current chunk computes.
 //   * Outputs leave through a per-wave LDS transpose as 16-byte row stores.
+//     The transpose buffers share LDS with the angle table, which is dead
+//     from the end of the sweep until the next chunk rebuilds it.
+//
+// The EPI instantiations fuse the block prologue and epilogue (section
+// "Architectural Integration"): every B, C and Bprev column is scaled to unit
+// RMS and gets the head's bias (rows kept in LDS) before its rotation, and y
+// is multiplied by SiLU(z) after the D term, in fp32 before the single bf16
+// rounding. The RMS of a column is a butterfly of wave shuffles over the lanes
+// that hold its pieces: the 4 operand lanes of a C row, the N/8 consecutive
+// loading lanes of a staged B row.
 #include <type_traits>
 
 #include "m3_common.h"
@@ -92,14 +102,33 @@ __device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp
 
 // Rotate the 4 pairs of an 8-element row piece by -Phi: (u, v) -> (c u + s v, -s u + c v),
 // with (cos, sin) of the 4 pairs packed as fp16 in cs.
-__device__ __forceinline__ void rot_piece(const bf16x8 raw, const f16x8 cs, float (&o)[8]) {
+__device__ __forceinline__ void rot_piece_f(const float (&in)[8], const f16x8 cs, float (&o)[8]) {
 #pragma unroll
     for (int m = 0; m < 4; m++) {
         const float c = (float)cs[2 * m], sn = (float)cs[2 * m + 1];
-        const float u = (float)raw[2 * m], v = (float)raw[2 * m + 1];
+        const float u = in[2 * m], v = in[2 * m + 1];
         o[2 * m] = c * u + sn * v;
         o[2 * m + 1] = c * v - sn * u;
     }
+}
+__device__ __forceinline__ void rot_piece(const bf16x8 raw, const f16x8 cs, float (&o)[8]) {
+    float in[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) in[e] = (float)raw[e];
+    rot_piece_f(in, cs, o);
+}
+// Prologue of one 8-element piece of a B or C column: scale by inv (the column's inverse RMS,
+// or 1) and add the bias slice b (8 fp32 values in LDS).
+__device__ __forceinline__ void prologue_piece(const bf16x8 raw, float inv, const float *b, float (&o)[8]) {
+    const f32x4 b0 = *(const f32x4 *)b, b1 = *(const f32x4 *)(b + 4);
+#pragma unroll
+    for (int e = 0; e < 8; e++) o[e] = (float)raw[e] * inv + ((e < 4) ? b0[e] : b1[e - 4]);
+}
+__device__ __forceinline__ float sumsq8(const bf16x8 v) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) ss += (float)v[e] * (float)v[e];
+    return ss;
 }
 __device__ __forceinline__ bf16x8 pack8(const float (&o)[8]) {
     return bf16x8{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3], (bf16)o[4], (bf16)o[5], (bf16)o[6], (bf16)o[7]};
@@ -112,11 +141,16 @@ struct BfParams {
     float *h_out;
     const int32_t *cu;
     int32_t seqlen, H, G, nseq;
+    const float *Bb, *Cb;   // prologue biases [H, N], or NULL
+    const bf16 *z;          // output gate, or NULL
+    int32_t norm;           // 1: B, C, Bprev columns scaled to unit RMS
+    float eps;
 };
 
-template <int N_, int P_, int R_, int Q_, int NW_, int UT_, int SBR_>
+template <int N_, int P_, int R_, int Q_, int NW_, int UT_, int SBR_, bool EPI_>
 struct Cfg {
     static constexpr int N = N_, P = P_, R = R_, Q = Q_, NW = NW_, UT = UT_, SBR = SBR_;
+    static constexpr bool EPI = EPI_;                        // fused block prologue / epilogue
     static constexpr int K = N / 2, QR = Q * R;
     static constexpr int NTB = QR / 16, NSB = QR / SBR;     // 16-row t-blocks, SBR-row s-blocks
     static constexpr int NSUB = SBR / 32;                    // 32-row score tiles per s-block
@@ -139,9 +173,14 @@ struct Cfg {
     static_assert(K % 8 == 0 && Q % NW == 0 && Q <= 128 && Q < NTHR, "prologue");
     static_assert(SBR % 32 == 0 && QR % SBR == 0, "s-block size");
     static_assert(NSB == 1 || NSB % 2 == 0, "full chunks alternate the two prefetch register sets");
+    static_assert(NTHR % (N / 8) == 0 && N / 8 <= 64, "a staged B row is N/8 consecutive lanes of one wave");
     // LDS layout (bytes)
+    static constexpr int YPS = EPI ? P + 4 : PS;                       // output staging row stride (elements)
+    static constexpr int YST = 16 * YPS * (EPI ? 4 : 2);               // per-wave output staging (fp32 with EPI)
+    static constexpr int REG0 = (Q * K * 4 > NW * YST) ? Q * K * 4 : NW * YST;
     static constexpr int OFF_PHI = 0;                                  // f16x2 [Q][K] (cos, sin) of Phi
-    static constexpr int OFF_PHC = OFF_PHI + Q * K * 4;                // float2 [K] (cos, sin) of the chunk's total angle
+    static constexpr int OFF_Y = 0;                                    // output staging, shares the table's bytes
+    static constexpr int OFF_PHC = REG0;                               // float2 [K] (cos, sin) of the chunk's total angle
     static constexpr int OFF_S2 = OFF_PHC + K * 8;                     // float [Q] log2 decay prefix
     static constexpr int OFF_A2 = OFF_S2 + Q * 4;                      // float [Q] per-token log2 decay
     static constexpr int OFF_GM = OFF_A2 + Q * 4;                      // float [Q] gamma
@@ -152,13 +191,12 @@ struct Cfg {
     static constexpr int OFF_F0 = OFF_F1 + Q * 4;                      // float [Q] column mask factors, s = t
     static constexpr int OFF_DT = OFF_F0 + Q * 4;                      // float [Q] dt (0 past the end)
     static constexpr int OFF_MISC = OFF_DT + Q * 4;                    // float [4]
-    static constexpr int OFF_HB = (OFF_MISC + 16 + 15) / 16 * 16;      // bf16 [P][NS] carried state
+    static constexpr int OFF_BIA = (OFF_MISC + 16 + 15) / 16 * 16;     // float [2][N] B, C bias rows (EPI)
+    static constexpr int OFF_HB = OFF_BIA + (EPI ? 2 * N * 4 : 0);     // bf16 [P][NS] carried state
     static constexpr int OFF_U = OFF_HB + P * NS * 2;                  // stage buffers / output staging
     static constexpr int SB_BT = 0, SB_X = SBR * NS * 2, SB_WX = SB_X + SBR * PS * 2;
     static constexpr int STAGE = SB_WX + SBR * PS * 2;                 // one s-block stage
-    static constexpr int YST = 16 * PS * 2;                            // per-wave output staging
-    static constexpr int OFF_Y = OFF_U + NST * STAGE;
-    static constexpr int LDS = OFF_Y + NW * YST;
+    static constexpr int LDS = OFF_U + NST * STAGE;
     static_assert(LDS <= 160 * 1024, "LDS");
     // global loads (16 bytes each) per s-block, and next-chunk header prefetch
     static constexpr int BCH = SBR * N / 8, XCH = SBR * P / 8;
@@ -233,6 +271,14 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     bf16 *gY = pr.y + h * (int64_t)R * P;
     const bf16 *gTh = pr.theta + h * (int64_t)K;
     const int64_t strBC = (int64_t)G * R * N, strX = (int64_t)H * R * P, strTh = (int64_t)H * K;
+    // prologue bias rows of the head (zeros for an absent bias): [0, N) for B, [N, 2N) for C
+    float *BIA = (float *)(smem + CF::OFF_BIA);
+    if constexpr (CF::EPI) {
+        for (int e = tid; e < 2 * N; e += NTHR) {
+            const float *src = (e < N) ? pr.Bb : pr.Cb;
+            BIA[e] = src ? src[(int64_t)h * N + e % N] : 0.f;
+        }
+    }
 
     // this wave's t-blocks and state tiles
     // t-block u of this wave in the chunk starting at c0x: balanced pairs along the causal
@@ -261,6 +307,23 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             const float dt0 = to_f(pr.dt[start * H + h]), l0 = to_f(pr.lam[start * H + h]);
             d0 = (1.f - l0) * dt0;
         }
+        // prologue of Bprev's columns: inverse RMS per column (every wave computes its own)
+        float invp[R];
+#pragma unroll
+        for (int j = 0; j < R; j++) invp[j] = 1.f;
+        if constexpr (CF::EPI) {
+            if (pr.Bprev && pr.norm) {
+                const bf16 *bp0 = pr.Bprev + ((int64_t)s * G + g) * R * N;
+#pragma unroll
+                for (int j = 0; j < R; j++) {
+                    float ss = 0.f;
+                    for (int n = lane; n < N; n += 64) ss += to_f(bp0[j * N + n]) * to_f(bp0[j * N + n]);
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                    invp[j] = rsqrtf(ss * (1.f / N) + pr.eps);
+                }
+            }
+        }
 #pragma unroll
         for (int v = 0; v < UPW; v++) {
             const int p = ut_p0[v] + ucol;
@@ -271,9 +334,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 if (pr.Bprev) {
                     const bf16 *bp = pr.Bprev + ((int64_t)s * G + g) * R * N + n;
                     const bf16 *xp = pr.xprev + ((int64_t)s * H + h) * R * P + p;
+                    const float bb = (CF::EPI && pr.Bb) ? pr.Bb[(int64_t)h * N + n] : 0.f;
                     float acc = 0.f;
 #pragma unroll
-                    for (int j = 0; j < R; j++) acc += to_f(bp[j * N]) * to_f(xp[j * P]);
+                    for (int j = 0; j < R; j++) acc += (to_f(bp[j * N]) * invp[j] + bb) * to_f(xp[j * P]);
                     val += d0 * acc;
                 }
                 hreg[v][r] = val;
@@ -525,11 +589,29 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
             const int tau = (task_tb[u] * 16 + l16) / R;
+            // prologue: the row's N values sit in lanes l16 + 16 q4, NKK pieces each
+            float cinv = 1.f;
+            if constexpr (CF::EPI) {
+                if (pr.norm) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int kk = 0; kk < NKK; kk++) ss += sumsq8(h_c[u][kk]);
+                    ss += __shfl_xor(ss, 16, 64);
+                    ss += __shfl_xor(ss, 32, 64);
+                    cinv = rsqrtf(ss * (1.f / N) + pr.eps);
+                }
+            }
 #pragma unroll
             for (int kk = 0; kk < NKK; kk++) {
                 const f16x8 cs = *(const f16x8 *)(cst + tau * K + 16 * kk + 4 * q4);
                 float o[8];
-                rot_piece(h_c[u][kk], cs, o);
+                if constexpr (CF::EPI) {
+                    float in[8];
+                    prologue_piece(h_c[u][kk], cinv, BIA + N + 32 * kk + 8 * q4, in);
+                    rot_piece_f(in, cs, o);
+                } else {
+                    rot_piece(h_c[u][kk], cs, o);
+                }
                 creg[u][kk] = (FULL || tau < nq) ? pack8(o) : bf16x8{};
             }
         }
@@ -597,6 +679,23 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 const int c = min(tid + i * NTHR, CF::XCH - 1);
                 wxv[i] = WU[sb * TOKS + (c / (P / 8)) / R];
             }
+            // prologue: a row's pieces are N/8 consecutive lanes, and every piece of this thread
+            // covers the same columns (NTHR is a multiple of N/8), so one bias slice serves all
+            float binv[CF::NLB];
+            const float *bslice = BIA + (tid % (N / 8)) * 8;
+#pragma unroll
+            for (int i = 0; i < CF::NLB; i++) binv[i] = 1.f;
+            if constexpr (CF::EPI) {
+                if (pr.norm) {
+#pragma unroll
+                    for (int i = 0; i < CF::NLB; i++) {
+                        float ss = sumsq8(rawB[i]);
+#pragma unroll
+                        for (int off = 1; off < N / 8; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                        binv[i] = rsqrtf(ss * (1.f / N) + pr.eps);
+                    }
+                }
+            }
 #pragma unroll
             for (int i = 0; i < CF::NLB; i++) {
                 const int c = tid + i * NTHR;
@@ -604,7 +703,13 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                     const int row = c / (N / 8), col = (c % (N / 8)) * 8;
                     const int tau = sb * TOKS + row / R;
                     float o[8];
-                    rot_piece(rawB[i], csb[i], o);
+                    if constexpr (CF::EPI) {
+                        float in[8];
+                        prologue_piece(rawB[i], binv[i], bslice, in);
+                        rot_piece_f(in, csb[i], o);
+                    } else {
+                        rot_piece(rawB[i], csb[i], o);
+                    }
                     *(bf16x8 *)(bt + row * NS + col) = (FULL || tau < nq) ? pack8(o) : bf16x8{};
                 }
             }
@@ -839,7 +944,51 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         }
 
         // ---- epilogue: outputs through a per-wave LDS transpose, 16-byte row stores
-        {
+        if constexpr (CF::EPI) {
+            // fp32 transpose, then y * SiLU(z) in fp32 and one rounding to bf16
+            constexpr int NPC = 16 * P / 8 / 64;   // 16-byte pieces per lane and t-block
+            static_assert((16 * P / 8) % 64 == 0, "output pieces");
+            float *ysf = (float *)(smem + CF::OFF_Y + wave * CF::YST);   // [16 rows][YPS], own region
+            const bool has_z = pr.z != nullptr;
+            const bf16 *gZ = (has_z ? pr.z : pr.x) + h * (int64_t)R * P;
+#pragma unroll
+            for (int u = 0; u < TPW; u++) {
+                const int tb = task_tb[u];
+                bf16x8 zr[NPC];
+                if (has_z) {
+#pragma unroll
+                    for (int k = 0; k < NPC; k++) {
+                        const int c = lane + 64 * k, row = c / (P / 8), col = (c % (P / 8)) * 8;
+                        const int rr = tb * 16 + row, tau = min(rr / R, nq - 1);   // in bounds; unused past the end
+                        zr[k] = *(const bf16x8 *)(gZ + (tok0 + tau) * strX + (rr % R) * P + col);
+                    }
+                }
+#pragma unroll
+                for (int pt = 0; pt < NPT; pt++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) ysf[(4 * q4 + i) * CF::YPS + pt * 16 + l16] = yacc[u][pt][i];
+                lds_wait();
+#pragma unroll
+                for (int k = 0; k < NPC; k++) {
+                    const int c = lane + 64 * k, row = c / (P / 8), col = (c % (P / 8)) * 8;
+                    const int rr = tb * 16 + row, tau = rr / R;
+                    const f32x4 a = *(const f32x4 *)(ysf + row * CF::YPS + col);
+                    const f32x4 b = *(const f32x4 *)(ysf + row * CF::YPS + col + 4);
+                    float o[8];
+#pragma unroll
+                    for (int e = 0; e < 8; e++) o[e] = (e < 4) ? a[e] : b[e - 4];
+                    if (has_z) {
+#pragma unroll
+                        for (int e = 0; e < 8; e++) {
+                            const float v = (float)zr[k][e];
+                            o[e] *= v / (1.f + __expf(-v));
+                        }
+                    }
+                    if (FULL || tau < nq) *(bf16x8 *)(gY + (tok0 + tau) * strX + (rr % R) * P + col) = pack8(o);
+                }
+                lds_wait();
+            }
+        } else {
             bf16 *ys = (bf16 *)(smem + CF::OFF_Y + wave * CF::YST);   // [16 rows][PS], own region
 #pragma unroll
             for (int u = 0; u < TPW; u++) {
@@ -907,6 +1056,7 @@ mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st) {
     p.A = a->A; p.D = a->D; p.h_in = a->h_in; p.y = (bf16 *)a->y; p.h_out = a->h_out;
     p.cu = a->cu_seqlens; p.seqlen = a->seqlen; p.H = a->nheads; p.G = a->ngroups;
     p.nseq = a->cu_seqlens ? a->nseq : a->batch;
+    p.Bb = a->B_bias; p.Cb = a->C_bias; p.z = (const bf16 *)a->z; p.norm = a->bc_norm; p.eps = a->bc_eps;
     const int64_t nseq = a->cu_seqlens ? a->nseq : a->batch;
     const int64_t nblk = nseq * a->nheads;
     if (nblk == 0) return MAMBA3_OK;
@@ -938,8 +1088,11 @@ bool scan_bf16_supported(int N, int P, int R, int Q) {
 
 mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st) {
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
-#define X(n, p, r, q, w, ut, sbr) \
-    if (N == n && P == p && R == r && Q == q) return launch_cfg<Cfg<n, p, r, q, w, ut, sbr>>(a, st);
+    const bool epi = a->bc_norm || a->B_bias || a->C_bias || a->z;
+#define X(n, p, r, q, w, ut, sbr)                                                       \
+    if (N == n && P == p && R == r && Q == q)                                           \
+        return epi ? launch_cfg<Cfg<n, p, r, q, w, ut, sbr, true>>(a, st)               \
+                   : launch_cfg<Cfg<n, p, r, q, w, ut, sbr, false>>(a, st);
     M3_BF16_SHAPES(X)
 #undef X
     return MAMBA3_EUNSUPPORTED;

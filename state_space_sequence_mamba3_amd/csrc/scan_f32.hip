@@ -15,6 +15,10 @@
 // where delta_{e+1} is the next chunk's first token's (0 at the sequence end),
 // which folds that token's previous-input term into the carried state.
 // At the sequence start H' = h_in + delta_0 Bprev xprev^T.
+//
+// Optional block prologue and epilogue (section "Architectural Integration"):
+// each B and C column is scaled to unit RMS and gets its head's bias before
+// the rotation, and y is multiplied by SiLU(z) after the D term.
 #include "m3_common.h"
 
 namespace m3 {
@@ -24,8 +28,27 @@ struct ValuParams {
     const float *A, *D, *h_in;
     float *y, *h_out;
     const int32_t *cu;
+    const float *Bb, *Cb, *z;   // prologue biases [H, N] and output gate, or NULL
     int32_t nseq, seqlen, H, G, P, N, R, Q;
+    int32_t norm;               // 1: B and C columns scaled to unit RMS
+    float eps;
 };
+
+// Block prologue on `nrows` LDS rows of N values: scale each row to unit RMS
+// (norm) and add the head's bias row (bias may be NULL). One thread per row.
+__device__ void bc_prologue_rows(float *rows, int nrows, int N, const float *bias, int norm, float eps, int tid,
+                                 int nt) {
+    for (int r = tid; r < nrows; r += nt) {
+        float *v = rows + (int64_t)r * N;
+        float inv = 1.f;
+        if (norm) {
+            float ss = 0.f;
+            for (int n = 0; n < N; n++) ss += v[n] * v[n];
+            inv = 1.f / sqrtf(ss / (float)N + eps);
+        }
+        for (int n = 0; n < N; n++) v[n] = v[n] * inv + (bias ? bias[n] : 0.f);
+    }
+}
 
 size_t scan_f32_lds_bytes(int N, int P, int R, int Q) {
     size_t QR = (size_t)Q * R, K = N / 2;
@@ -65,6 +88,9 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
     }
     const float Ah = p.A[h];
     const float Dh = p.D ? p.D[h] : 0.f;
+    const bool pro = p.norm || p.Bb || p.Cb;
+    const float *Bbh = p.Bb ? p.Bb + (int64_t)h * N : nullptr;
+    const float *Cbh = p.Cb ? p.Cb + (int64_t)h * N : nullptr;
     const int64_t st_off = ((int64_t)s * H + h) * N * P;
 
     for (int e = tid; e < N * P; e += nt) Hs[e] = p.h_in ? p.h_in[st_off + e] : 0.f;
@@ -111,31 +137,51 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
                 phi[t * K + k] = acc;
             }
         }
-        // previous-token fold at the sequence start: H' += delta_0 Bprev xprev^T
+        // previous-token fold at the sequence start: H' += delta_0 Bprev xprev^T (Bprev's
+        // columns staged in Bt, through the prologue)
         if (c0 == 0 && p.Bprev) {
             const int64_t ob = ((int64_t)s * G + g) * N * R, ox = ((int64_t)s * H + h) * P * R;
+            for (int e = tid; e < R * N; e += nt) Bt[e] = p.Bprev[ob + e];
+            __syncthreads();
+            if (pro) {
+                bc_prologue_rows(Bt, R, N, Bbh, p.norm, p.eps, tid, nt);
+                __syncthreads();
+            }
             const float d0 = dl[0];
             for (int e = tid; e < N * P; e += nt) {
                 int n = e / P, pp = e % P;
                 float acc = 0.f;
-                for (int j = 0; j < R; j++) acc += p.Bprev[ob + j * N + n] * p.xprev[ox + j * P + pp];
+                for (int j = 0; j < R; j++) acc += Bt[j * N + n] * p.xprev[ox + j * P + pp];
                 Hs[e] += d0 * acc;
             }
         }
         __syncthreads();
-        // rotated B~, C~ and X for the chunk (zero past the sequence end)
-        for (int e = tid; e < Q * K * R; e += nt) {
-            int t = e / (K * R), k = (e / R) % K, j = e % R;
-            float b0 = 0.f, b1 = 0.f, q0 = 0.f, q1 = 0.f, cs = 1.f, sn = 0.f;
+        // B and C columns of the chunk (zero past the sequence end), through the prologue
+        for (int e = tid; e < QR * N; e += nt) {
+            int r = e / N, n = e % N, t = r / R, j = r % R;
+            float bv = 0.f, cv = 0.f;
             if (t < nq) {
-                int64_t ob = ((start + c0 + t) * G + g) * N * R;
-                b0 = p.B[ob + j * N + 2 * k];
-                b1 = p.B[ob + j * N + 2 * k + 1];
-                q0 = p.C[ob + j * N + 2 * k];
-                q1 = p.C[ob + j * N + 2 * k + 1];
-                sincosf(phi[t * K + k], &sn, &cs);
+                int64_t ob = ((start + c0 + t) * G + g) * N * R + j * N + n;
+                bv = p.B[ob];
+                cv = p.C[ob];
             }
+            Bt[e] = bv;
+            Ct[e] = cv;
+        }
+        if (pro) {
+            __syncthreads();
+            bc_prologue_rows(Bt, nq * R, N, Bbh, p.norm, p.eps, tid, nt);
+            bc_prologue_rows(Ct, nq * R, N, Cbh, p.norm, p.eps, tid, nt);
+        }
+        __syncthreads();
+        // rotated B~, C~ in place
+        for (int e = tid; e < nq * K * R; e += nt) {
+            int t = e / (K * R), k = (e / R) % K, j = e % R;
+            float cs, sn;
+            sincosf(phi[t * K + k], &sn, &cs);
             int r = t * R + j;
+            const float b0 = Bt[r * N + 2 * k], b1 = Bt[r * N + 2 * k + 1];
+            const float q0 = Ct[r * N + 2 * k], q1 = Ct[r * N + 2 * k + 1];
             Bt[r * N + 2 * k] = cs * b0 + sn * b1;
             Bt[r * N + 2 * k + 1] = -sn * b0 + cs * b1;
             Ct[r * N + 2 * k] = cs * q0 + sn * q1;
@@ -169,7 +215,12 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
             float acc = expf(S[tt]) * inter;
             for (int q = 0; q < (tt + 1) * R; q++) acc += M[r * QR + q] * Xs[q * P + pp];
             acc += Dh * Xs[r * P + pp];
-            p.y[((start + c0 + tt) * H + h) * P * R + i * P + pp] = acc;
+            const int64_t oy = ((start + c0 + tt) * H + h) * P * R + i * P + pp;
+            if (p.z) {
+                const float v = p.z[oy];
+                acc *= v / (1.f + expf(-v));
+            }
+            p.y[oy] = acc;
         }
         __syncthreads();
         // carried state
@@ -205,6 +256,8 @@ mamba3_status launch_scan_f32(const mamba3_scan_args *a, hipStream_t st) {
     p.nseq = a->cu_seqlens ? a->nseq : a->batch;
     p.seqlen = a->seqlen; p.H = a->nheads; p.G = a->ngroups; p.P = a->headdim; p.N = a->dstate;
     p.R = a->rank; p.Q = a->chunk;
+    p.Bb = a->B_bias; p.Cb = a->C_bias; p.z = (const float *)a->z;
+    p.norm = a->bc_norm; p.eps = a->bc_eps;
     size_t lds = scan_f32_lds_bytes(p.N, p.P, p.R, p.Q);
     if (hipFuncSetAttribute((const void *)k_scan_f32, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return MAMBA3_EHIP;

@@ -19,6 +19,10 @@ order A, D, x, dt, lam, theta, B, C, then (decode only) state, Bprev, xprev,
 from numpy's PCG64 seeded with 1000 + config index unless a seed is given.
 Token inputs are rounded to bf16 (round to nearest even, via fp32) for the bf16
 configurations; A, D and states are fp32.
+
+The block prologue / epilogue inputs (``block_inputs``) come from a generator
+of their own: B and C biases ~ U(0.5, 1.5) [H, N] fp32 (positive, around the
+all-ones initialisation of the biases), then a gate z ~ N(0, 1) shaped like x.
 """
 from __future__ import annotations
 
@@ -133,6 +137,26 @@ def resume_inputs(inp: dict, seed: int) -> dict:
     return out
 
 
+def block_inputs(inp: dict, seed: int, norm: bool = True, B_bias: bool = True, C_bias: bool = True,
+                 gate: bool = True, eps: float = 1e-5) -> dict:
+    """Adds the inputs of the fused block prologue / epilogue to a scan or
+    decode input set: the B/C RMS-norm switch and its eps, per-head B and C
+    biases [H, N] fp32 ~ U[0.5, 1.5] (positive, around the all-ones
+    initialisation), and a gate z shaped like x (~N(0, 1), token dtype)."""
+    m = inp["meta"]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    H, N = m["nheads"], m["dstate"]
+    out = dict(inp)
+    out["bc_norm"], out["bc_eps"] = bool(norm), float(eps)
+    if B_bias:
+        out["B_bias"] = rng.uniform(0.5, 1.5, size=(H, N)).astype(np.float32)
+    if C_bias:
+        out["C_bias"] = rng.uniform(0.5, 1.5, size=(H, N)).astype(np.float32)
+    if gate:
+        out["z"] = _tok(_normal(rng, inp["x"].shape), m["dtype"])
+    return out
+
+
 def decode_inputs(cfg: int | dict = 3, seed: int | None = None, ring: int = 1, **over) -> dict:
     """Decode workload: ``ring`` token-input sets (each like one token of a
     scan, leading axis ring), a previous token, and an fp32 state ~ N(0,1).
@@ -190,4 +214,19 @@ def torch_scan_inputs(cfg: int | dict, device, seed: int = 0, **over) -> dict:
         ln = packed_lengths(rng, c["nseq"], L, c["len_lo"], c["len_hi"])
         out["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(ln)]), dtype=torch.int32, device=device)
     out["meta"] = dict(c, ngroups=G, seed=seed)
+    return out
+
+
+def torch_block_inputs(d: dict, device, seed: int = 0) -> dict:
+    """Device-side twin of ``block_inputs`` (norm on, both biases, gate)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    H, N = d["A"].shape[0], d["B"].shape[-1]
+    out = dict(d)
+    out["bc_norm"], out["bc_eps"] = True, 1e-5
+    out["B_bias"] = torch.rand((H, N), generator=g, device=device) + 0.5
+    out["C_bias"] = torch.rand((H, N), generator=g, device=device) + 0.5
+    out["z"] = torch.randn(d["x"].shape, generator=g, device=device, dtype=torch.float32).to(d["x"].dtype)
     return out

@@ -37,7 +37,7 @@ def test_status_strings(lib):
     assert m3.status_string(m3.MAMBA3_OK) == "ok"
     for s in range(6):
         assert m3.status_string(s)
-    assert lib.mamba3_version() == 10000
+    assert lib.mamba3_version() == 10100
 
 
 BASE = 0x7F0000000000
@@ -91,6 +91,37 @@ def test_scan_validate_ok(lib):
 ])
 def test_scan_validate_errors(lib, field, value, status):
     assert m3.mamba3_scan_validate(good_scan(**{field: value})) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(bc_norm=1, bc_eps=1e-5), m3.MAMBA3_OK),
+    (dict(bc_norm=1, bc_eps=0.0), m3.MAMBA3_OK),
+    (dict(B_bias=fake(14), C_bias=fake(15), z=fake(16)), m3.MAMBA3_OK),
+    (dict(bc_norm=2), m3.MAMBA3_EINVAL),
+    (dict(bc_norm=-1), m3.MAMBA3_EINVAL),
+    (dict(bc_norm=1, bc_eps=-1e-6), m3.MAMBA3_EINVAL),
+    (dict(bc_norm=1, bc_eps=float("nan")), m3.MAMBA3_EINVAL),
+    (dict(bc_norm=1, bc_eps=float("inf")), m3.MAMBA3_EINVAL),
+    (dict(bc_norm=0, bc_eps=float("nan")), m3.MAMBA3_OK),       # eps unused without the norm
+    (dict(z=fake(16) + 8), m3.MAMBA3_EALIGN),
+    (dict(B_bias=fake(14) + 4), m3.MAMBA3_EALIGN),
+    (dict(C_bias=fake(15) + 12), m3.MAMBA3_EALIGN),
+    (dict(z=fake(9)), m3.MAMBA3_EINVAL),                        # y aliases z
+    (dict(B_bias=fake(9) + 64), m3.MAMBA3_EINVAL),              # bias inside y
+    (dict(C_bias=fake(10)), m3.MAMBA3_EINVAL),                  # h_out aliases a bias
+])
+def test_scan_validate_prologue(lib, over, status):
+    assert m3.mamba3_scan_validate(good_scan(**over)) == status
+
+
+def test_decode_validate_prologue(lib):
+    ok = dict(B_bias=fake(14), C_bias=fake(15), z=fake(16), bc_norm=1, bc_eps=1e-6)
+    assert m3.mamba3_decode_validate(good_decode(**ok)) == m3.MAMBA3_OK
+    assert m3.mamba3_decode_validate(good_decode(bc_norm=3)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_decode_validate(good_decode(bc_norm=1, bc_eps=-0.5)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_decode_validate(good_decode(z=fake(16) + 2)) == m3.MAMBA3_EALIGN
+    assert m3.mamba3_decode_validate(good_decode(z=fake(12))) == m3.MAMBA3_EINVAL       # y aliases z
+    assert m3.mamba3_decode_validate(good_decode(B_bias=fake(11))) == m3.MAMBA3_EINVAL  # h aliases a bias
 
 
 def test_scan_validate_packed(lib):

@@ -1,5 +1,7 @@
 """GPU parity of the bf16 MFMA chunked scan against the fp64 oracle (max
-relative error 2e-2 per (sequence, head) slab, for y and the final state).
+relative error 2e-2 per (sequence, head) slab, for y and the final state),
+without and with the fused block prologue / epilogue (B/C RMS norm, per-head
+B/C biases, SiLU(z) output gate).
 
 Small cases run the whole oracle; the full-size workloads (8 x 4096 tokens,
 64 heads; the packed 65536-token workload) run the kernel at full size in the
@@ -19,7 +21,9 @@ def run(d, chunk, want_state=True):
     import torch
     y, h = m3.mamba3_scan_fwd(d["x"], d["dt"], d["lam"], d["theta"], d["B"], d["C"], d["A"], d.get("D"),
                               h_in=d.get("h_in"), Bprev=d.get("Bprev"), xprev=d.get("xprev"),
-                              cu_seqlens=d.get("cu_seqlens"), chunk=chunk, want_state=want_state)
+                              cu_seqlens=d.get("cu_seqlens"), chunk=chunk, want_state=want_state,
+                              B_bias=d.get("B_bias"), C_bias=d.get("C_bias"), z=d.get("z"),
+                              bc_norm=d.get("bc_norm", False), bc_eps=d.get("bc_eps", 1e-5))
     torch.cuda.synchronize()
     return y, h
 
@@ -59,6 +63,57 @@ def test_small_vs_full_oracle(oracle, name, resume):
     ey, eh = slab_relerr(from_dev(y), yo), state_relerr(from_dev(h), ho)
     note(f"  y relerr {ey:.2e}  h relerr {eh:.2e}")
     assert ey < TOL_BF16 and eh < TOL_BF16
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_block_prologue_epilogue(oracle, name):
+    """Fused B/C RMS norm, per-head B/C biases and SiLU(z) gate, with a resumed state and a
+    previous token (whose B column goes through the prologue too)."""
+    spec = dict(SMALL[name])
+    cfg = spec.pop("cfg")
+    inp = synth.resume_inputs(synth.scan_inputs(cfg, seed=200 + len(name), **spec), seed=6)
+    inp = synth.block_inputs(inp, seed=7)
+    chunk = inp["meta"]["chunk"]
+    note(f"bf16 scan block prologue/epilogue {name} x{inp['x'].shape} chunk={chunk}")
+    y, h = run(upload(inp, device()), chunk)
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    ey, eh = slab_relerr(from_dev(y), yo), state_relerr(from_dev(h), ho)
+    note(f"  y relerr {ey:.2e}  h relerr {eh:.2e}")
+    assert ey < TOL_BF16 and eh < TOL_BF16
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("features", [
+    dict(norm=True, B_bias=False, C_bias=False, gate=False),
+    dict(norm=False, B_bias=True, C_bias=False, gate=False),
+    dict(norm=False, B_bias=False, C_bias=True, gate=False),
+    dict(norm=False, B_bias=False, C_bias=False, gate=True),
+    dict(norm=True, B_bias=True, C_bias=True, gate=True, eps=0.0),
+])
+def test_block_feature_subsets(oracle, cfg, features):
+    """Each prologue / epilogue feature alone (each switches the fused kernel on), and all of
+    them with eps = 0."""
+    inp = synth.resume_inputs(synth.scan_inputs(cfg, seed=51, batch=2, seqlen=150, nheads=2), seed=52)
+    inp = synth.block_inputs(inp, seed=53, **features)
+    note(f"bf16 scan block features cfg{cfg} {features}")
+    y, h = run(upload(inp, device()), inp["meta"]["chunk"])
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    ey, eh = slab_relerr(from_dev(y), yo), state_relerr(from_dev(h), ho)
+    note(f"  y relerr {ey:.2e}  h relerr {eh:.2e}")
+    assert ey < TOL_BF16 and eh < TOL_BF16
+
+
+def test_block_packed_grouped(oracle):
+    """Prologue / epilogue on a packed ragged batch with G = 1 (every head adds its own bias to
+    the shared B and C) and empty sequences."""
+    inp = synth.scan_inputs(dict(synth.CONFIGS[4], ngroups=1), seed=61, seqlen=600, nheads=2)
+    inp["cu_seqlens"] = np.array([0, 1, 1, 200, 333, 600, 600], dtype=np.int32)
+    inp = synth.block_inputs(synth.resume_inputs(inp, seed=62), seed=63)
+    note("bf16 packed block prologue/epilogue, G=1")
+    y, h = run(upload(inp, device()), 128)
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    assert packed_relerr(from_dev(y), yo, inp["cu_seqlens"]) < TOL_BF16
+    assert state_relerr(from_dev(h), ho) < TOL_BF16
 
 
 @pytest.mark.parametrize("cfg", [1, 2])
@@ -172,15 +227,24 @@ def _slab_inputs(d, s, h, cu=None):
     out = dict(x=bits(d["x"][sl][:, h:h + 1]), dt=bits(d["dt"][sl][:, h:h + 1]), lam=bits(d["lam"][sl][:, h:h + 1]),
                theta=bits(d["theta"][sl][:, h:h + 1]), B=bits(d["B"][sl][:, g:g + 1]), C=bits(d["C"][sl][:, g:g + 1]),
                A=d["A"][h:h + 1].cpu().numpy(), D=d["D"][h:h + 1].cpu().numpy())
+    if d.get("z") is not None:
+        out["z"] = bits(d["z"][sl][:, h:h + 1])
+    for k in ("B_bias", "C_bias"):
+        if d.get(k) is not None:
+            out[k] = d[k][h:h + 1].cpu().numpy()
+    if "bc_norm" in d:
+        out["bc_norm"], out["bc_eps"] = d["bc_norm"], d["bc_eps"]
     return out
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 4])
-def test_full_size_sampled_slabs(oracle, cfg):
+@pytest.mark.parametrize("cfg,block", [(1, False), (2, False), (4, False), (1, True), (2, True)])
+def test_full_size_sampled_slabs(oracle, cfg, block):
     import torch
     c = synth.CONFIGS[cfg]
-    note(f"full-size bf16 scan config {cfg}: {c['name']}")
+    note(f"full-size bf16 scan config {cfg}: {c['name']} block prologue/epilogue={block}")
     d = synth.torch_scan_inputs(cfg, device(), seed=cfg)
+    if block:
+        d = synth.torch_block_inputs(d, device(), seed=cfg)
     y, h = run(d, c["chunk"])
     cu = d["cu_seqlens"].cpu().numpy() if "cu_seqlens" in d else None
     S = (len(cu) - 1) if cu is not None else c["batch"]

@@ -17,7 +17,9 @@ def run_scan(inp, chunk, want_state=True):
     d = upload(inp, dev)
     y, h = m3.mamba3_scan_fwd(d["x"], d["dt"], d["lam"], d["theta"], d["B"], d["C"], d["A"], d.get("D"),
                               h_in=d.get("h_in"), Bprev=d.get("Bprev"), xprev=d.get("xprev"),
-                              cu_seqlens=d.get("cu_seqlens"), chunk=chunk, want_state=want_state)
+                              cu_seqlens=d.get("cu_seqlens"), chunk=chunk, want_state=want_state,
+                              B_bias=d.get("B_bias"), C_bias=d.get("C_bias"), z=d.get("z"),
+                              bc_norm=d.get("bc_norm", False), bc_eps=d.get("bc_eps", 1e-5))
     torch.cuda.synchronize()
     return from_dev(y), (from_dev(h) if h is not None else None)
 
@@ -77,6 +79,41 @@ def test_scan_fp32_packed_with_empty_sequences(oracle):
     assert np.array_equal(h[1], inp["h_in"][1].astype(np.float64))
 
 
+@pytest.mark.parametrize("shape", [
+    dict(batch=2, seqlen=200, nheads=4, headdim=16, dstate=16, rank=1, chunk=64),
+    dict(batch=1, seqlen=130, nheads=2, headdim=16, dstate=32, rank=4, chunk=16),
+    dict(batch=2, seqlen=65, nheads=4, headdim=8, dstate=8, rank=2, chunk=32, ngroups=2),
+])
+@pytest.mark.parametrize("features", [
+    dict(),
+    dict(norm=False),
+    dict(gate=False, B_bias=False),
+    dict(norm=True, B_bias=False, C_bias=False, gate=False, eps=0.0),
+])
+def test_scan_fp32_block_prologue_epilogue(oracle, shape, features):
+    cfg = dict(synth.CONFIGS[0], **shape)
+    inp = synth.resume_inputs(synth.scan_inputs(cfg, seed=17), seed=18)
+    inp = synth.block_inputs(inp, seed=19, **features)
+    note(f"scan f32 block {shape} {features}")
+    y, h = run_scan(inp, chunk=shape["chunk"])
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    ey, eh = slab_relerr(y, yo), state_relerr(h, ho)
+    note(f"  y relerr {ey:.2e}  h relerr {eh:.2e}")
+    assert ey < TOL_F32 and eh < TOL_F32
+
+
+def test_scan_fp32_block_packed(oracle):
+    cfg = dict(synth.CONFIGS[0], batch=1, seqlen=300, nheads=2, headdim=16, dstate=16, rank=2, chunk=32)
+    inp = synth.scan_inputs(cfg, seed=29)
+    inp["cu_seqlens"] = np.array([0, 50, 50, 51, 180, 300, 300], dtype=np.int32)
+    inp = synth.block_inputs(synth.resume_inputs(inp, seed=30), seed=31)
+    note("scan f32 packed block prologue/epilogue")
+    y, h = run_scan(inp, chunk=32)
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    assert packed_relerr(y, yo, inp["cu_seqlens"]) < TOL_F32
+    assert state_relerr(h, ho) < TOL_F32
+
+
 def test_scan_fp32_chunk_size_invariance():
     cfg = dict(synth.CONFIGS[0], batch=1, seqlen=192, nheads=2, rank=2)
     inp = synth.scan_inputs(cfg, seed=12)
@@ -105,7 +142,9 @@ def run_decode(inp, steps, ring_index=None):
     for k in range(steps):
         i = k % d["x"].shape[0]
         y = m3.mamba3_decode_step(d["x"][i], d["dt"][i], d["lam"][i], d["theta"][i], d["B"][i], d["C"][i],
-                                  d["A"], d["D"], h=h, Bprev=Bprev, xprev=xprev)
+                                  d["A"], d["D"], h=h, Bprev=Bprev, xprev=xprev, B_bias=d.get("B_bias"),
+                                  C_bias=d.get("C_bias"), z=d["z"][i] if d.get("z") is not None else None,
+                                  bc_norm=d.get("bc_norm", False), bc_eps=d.get("bc_eps", 1e-5))
         ys.append(y)
         Bprev, xprev = d["B"][i], d["x"][i]
     torch.cuda.synchronize()
@@ -120,6 +159,11 @@ def oracle_decode(oracle, inp, steps):
         i = k % inp["x"].shape[0]
         tok = {kk: inp[kk][i] for kk in ("x", "dt", "lam", "theta", "B", "C")}
         tok.update(A=inp["A"], D=inp["D"], Bprev=Bprev, xprev=xprev)
+        for kk in ("B_bias", "C_bias", "bc_norm", "bc_eps"):
+            if kk in inp:
+                tok[kk] = inp[kk]
+        if inp.get("z") is not None:
+            tok["z"] = inp["z"][i]
         y, h = oracle.decode(tok, h)
         ys.append(y)
         Bprev, xprev = inp["B"][i], inp["x"][i]
@@ -144,6 +188,48 @@ def test_decode_steps(oracle, dtype, tol, shape):
         den = np.abs(b).max(axis=(2, 3))
         assert float(np.max(num / den)) < tol
     assert state_relerr(hg, ho) < (tol if dtype == "f32" else 1e-5)
+
+
+@pytest.mark.parametrize("dtype,tol", [("bf16", TOL_BF16), ("f32", TOL_F32)])
+@pytest.mark.parametrize("shape", [
+    dict(batch=8, nheads=4, headdim=64, dstate=64, rank=4),
+    dict(batch=4, nheads=4, headdim=64, dstate=128, rank=4),
+    dict(batch=4, nheads=2, headdim=64, dstate=128, rank=1),
+    dict(batch=4, nheads=4, headdim=64, dstate=64, rank=2, ngroups=1),
+    dict(batch=5, nheads=4, headdim=16, dstate=16, rank=4, ngroups=2),
+    dict(batch=3, nheads=2, headdim=32, dstate=32, rank=2),
+])
+def test_decode_block_prologue_epilogue(oracle, dtype, tol, shape):
+    """Fused B/C RMS norm (Bprev's columns included), per-head biases and SiLU(z) gate over
+    several steps; the state is fp32 whatever the token dtype."""
+    cfg = dict(synth.CONFIGS[3], dtype=dtype, **shape)
+    inp = synth.block_inputs(synth.decode_inputs(cfg, seed=22, ring=3), seed=23)
+    note(f"decode block prologue/epilogue {dtype} {shape}")
+    yg, hg = run_decode(inp, steps=4)
+    yo, ho = oracle_decode(oracle, inp, steps=4)
+    for a, b in zip(yg, yo):
+        num = np.abs(a - b).max(axis=(2, 3))
+        den = np.abs(b).max(axis=(2, 3))
+        assert float(np.max(num / den)) < tol
+    assert state_relerr(hg, ho) < (tol if dtype == "f32" else 1e-5)
+
+
+@pytest.mark.parametrize("features", [
+    dict(norm=True, B_bias=False, C_bias=False, gate=False),
+    dict(norm=False, B_bias=True, C_bias=False, gate=False),
+    dict(norm=False, B_bias=False, C_bias=True, gate=False),
+    dict(norm=False, B_bias=False, C_bias=False, gate=True),
+])
+def test_decode_block_feature_subsets(oracle, features):
+    cfg = dict(synth.CONFIGS[3], batch=6, nheads=4)
+    inp = synth.block_inputs(synth.decode_inputs(cfg, seed=24, ring=2), seed=25, **features)
+    note(f"decode block features {features}")
+    yg, hg = run_decode(inp, steps=3)
+    yo, ho = oracle_decode(oracle, inp, steps=3)
+    for a, b in zip(yg, yo):
+        num = np.abs(a - b).max(axis=(2, 3))
+        assert float(np.max(num / np.abs(b).max(axis=(2, 3)))) < TOL_BF16
+    assert state_relerr(hg, ho) < 1e-5
 
 
 def test_decode_config3_full_batch(oracle):
