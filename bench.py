@@ -9,7 +9,9 @@ update, outputs). Inputs are synthetic (seeded, device-generated) and resident
 in HBM before timing starts. The same JSON line also carries the decode step
 (batch 256, 64 heads, N=64, R=4, fp32 state updated in place, 1000
 consecutive steps over a ring of 64 token-input sets) and the MIMO and packed
-MIMO scans as secondary figures, each with its roofline.
+MIMO scans as secondary figures, each with its roofline, and the SISO, MIMO
+and decode workloads again with the fused block prologue / epilogue (B/C RMS
+norm, per-head B/C biases, SiLU(z) output gate).
 
 Timing: HIP events recorded on the stream the kernels are launched on (torch's
 current stream, which the binding passes to the library), W untimed warmup
@@ -29,19 +31,21 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, published
 
 
-def scan_bytes(c):
+def scan_bytes(c, block=False):
     """Algorithmic HBM bytes of one scan: every input read once, y and the
-    final state written once (token inputs bf16, A/D/state fp32)."""
+    final state written once (token inputs bf16, A/D/state fp32); with the
+    block prologue / epilogue also the gate z and the two [H, N] fp32 bias
+    tables."""
     b, L, H, P, N, R = c["batch"], c["seqlen"], c["nheads"], c["headdim"], c["dstate"], c["rank"]
     G = c.get("ngroups", H)
     T = b * L
     S = c.get("nseq", b) if c.get("packed") else b
     es = 2
-    tok = T * (H * P * R * es * 2          # x, y
-               + H * es * 2                # dt, lam
-               + H * (N // 2) * es         # theta
-               + 2 * G * N * R * es)       # B, C
-    return tok + S * H * N * P * 4 + 2 * H * 4
+    tok = T * (H * P * R * es * (3 if block else 2)   # x, y (, z)
+               + H * es * 2                          # dt, lam
+               + H * (N // 2) * es                   # theta
+               + 2 * G * N * R * es)                 # B, C
+    return tok + S * H * N * P * 4 + 2 * H * 4 + (2 * H * N * 4 if block else 0)
 
 
 def scan_flops(c):
@@ -52,14 +56,15 @@ def scan_flops(c):
     return c["batch"] * L * H * (R * R * (N + P) * (Q + 1) + 4 * R * N * P)
 
 
-def decode_bytes(c):
+def decode_bytes(c, block=False):
     b, H, P, N, R = c["batch"], c["nheads"], c["headdim"], c["dstate"], c["rank"]
     G = c.get("ngroups", H)
     es = 2
     return (b * H * N * P * 4 * 2                       # state read + write
-            + b * H * P * R * es * 3                    # x, xprev, y
+            + b * H * P * R * es * (4 if block else 3)  # x, xprev, y (, z)
             + b * G * N * R * es * 3                    # B, C, Bprev
-            + b * H * (N // 2) * es + b * H * es * 2)   # theta, dt, lam
+            + b * H * (N // 2) * es + b * H * es * 2    # theta, dt, lam
+            + (2 * H * N * 4 if block else 0))          # bias tables
 
 
 def timed(fn, steps, warmup, stream):
@@ -79,12 +84,14 @@ def timed(fn, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps, wall
 
 
-def bench_scan(cfg, steps, warmup, dev, **over):
+def bench_scan(cfg, steps, warmup, dev, block=False, **over):
     import torch
     import state_space_sequence_mamba3_amd as m3
     from state_space_sequence_mamba3_amd import synth
     c = dict(synth.CONFIGS[cfg], **over)
     d = synth.torch_scan_inputs(cfg, dev, seed=cfg, **over)
+    if block:
+        d = synth.torch_block_inputs(d, dev, seed=cfg)
     y = torch.empty_like(d["x"])
     S = int(d["cu_seqlens"].numel()) - 1 if "cu_seqlens" in d else c["batch"]
     h = torch.empty((S, c["nheads"], c["dstate"], c["headdim"]), dtype=torch.float32, device=dev)
@@ -93,12 +100,15 @@ def bench_scan(cfg, steps, warmup, dev, **over):
 
     def step():
         m3.mamba3_scan_fwd(d["x"], d["dt"], d["lam"], d["theta"], d["B"], d["C"], d["A"], d["D"], y=y, h_out=h,
-                           cu_seqlens=d.get("cu_seqlens"), chunk=c["chunk"], stream=stream)
+                           cu_seqlens=d.get("cu_seqlens"), chunk=c["chunk"], stream=stream,
+                           B_bias=d.get("B_bias"), C_bias=d.get("C_bias"), z=d.get("z"),
+                           bc_norm=d.get("bc_norm", False), bc_eps=d.get("bc_eps", 1e-5))
 
     ms, wall = timed(step, steps, warmup, stream)
     tokens = c["batch"] * c["seqlen"]
-    nbytes, flops = scan_bytes(c), scan_flops(c)
+    nbytes, flops = scan_bytes(c, block), scan_flops(c)
     name = c["name"] + (f" (B, C shared: G={c['ngroups']})" if "ngroups" in over else "")
+    name += " + BC norm, BC biases, SiLU gate" if block else ""
     out = dict(workload=name, ms=ms, tokens_per_s=tokens / (ms * 1e-3), bytes=nbytes, flops=flops,
                hbm_gbs=nbytes / (ms * 1e-3) / 1e9, mfma_tfs=flops / (ms * 1e-3) / 1e12, wall_s=wall)
     del d, y, h
@@ -106,7 +116,7 @@ def bench_scan(cfg, steps, warmup, dev, **over):
     return out
 
 
-def bench_decode(steps_per_rep, reps, dev):
+def bench_decode(steps_per_rep, reps, dev, block=False):
     import torch
     import state_space_sequence_mamba3_amd as m3
     from state_space_sequence_mamba3_amd import synth
@@ -130,19 +140,27 @@ def bench_decode(steps_per_rep, reps, dev):
     D = nrm((H,))
     h = nrm((b, H, N, P))
     ys = torch.empty((ring, b, H, R, P), dtype=torch.bfloat16, device=dev)
+    blk = {}
+    if block:   # fused prologue / epilogue: BC norm, per-head biases ~ U(0.5, 1.5), gate z ~ N(0, 1)
+        z = nrm((ring, b, H, R, P)).bfloat16()
+        blk = dict(B_bias=torch.rand((H, N), generator=g, device=dev) + 0.5,
+                   C_bias=torch.rand((H, N), generator=g, device=dev) + 0.5, bc_norm=True, bc_eps=1e-5)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     state = {"k": 0}
+
+    def zarg(i):
+        return dict(blk, z=z[i]) if block else {}
 
     def step():
         k = state["k"]
         i, j = k % ring, (k - 1) % ring
         m3.mamba3_decode_step(x[i], dt[i], lam[i], th[i], B[i], C[i], A, D, h=h, y=ys[i], Bprev=B[j], xprev=x[j],
-                              stream=stream)
+                              stream=stream, **zarg(i))
         state["k"] = k + 1
 
     ms, wall = timed(step, steps_per_rep, 10, stream)
-    nbytes = decode_bytes(c)
+    nbytes = decode_bytes(c, block)
     us = ms * 1e3
     # per-step event pairs (outside the timed region) for the median
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps_per_rep)]
@@ -167,7 +185,7 @@ def bench_decode(steps_per_rep, reps, dev):
                     k = state["k"]
                     i, j = k % ring, (k - 1) % ring
                     m3.mamba3_decode_step(x[i], dt[i], lam[i], th[i], B[i], C[i], A, D, h=h, y=ys[i], Bprev=B[j],
-                                          xprev=x[j], stream=torch.cuda.current_stream())
+                                          xprev=x[j], stream=torch.cuda.current_stream(), **zarg(i))
                     state["k"] = k + 1
         torch.cuda.synchronize()
         reps = max(1, steps_per_rep // ring)
@@ -180,7 +198,7 @@ def bench_decode(steps_per_rep, reps, dev):
         graph_us = (time.perf_counter() - w0) / (reps * ring) * 1e6
     except Exception as exc:  # graph capture unavailable: report the eager figures only
         print(f"# decode graph replay skipped: {exc}", file=sys.stderr)
-    return dict(workload=c["name"], us_per_step=us, median_us=median, graph_wall_us=graph_us, steps=steps_per_rep,
+    return dict(workload=c["name"] + (" + BC norm, BC biases, SiLU gate" if block else ""), us_per_step=us, median_us=median, graph_wall_us=graph_us, steps=steps_per_rep,
                 bytes_per_step=nbytes, hbm_gbs=nbytes / (us * 1e-6) / 1e9, wall_s=wall)
 
 
@@ -257,9 +275,15 @@ def summarize_stats(stats_dir, out_md, command):
     rows = _csv_rows(os.path.join(stats_dir, "run_kernel_stats.csv"))
     lines = ["# rocprofv3 kernel statistics", "", "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
              "```", command, "```", "", "| kernel | calls | average us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+    other, other_ms = 0, 0.0
     for r in rows:
+        if "k_scan" not in r["Name"] and "k_decode" not in r["Name"]:
+            other += 1
+            other_ms += float(r["TotalDurationNs"]) / 1e6
+            continue
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['TotalDurationNs']) / 1e6:.3f} |")
+    lines += ["", f"Not listed: {other} other kernels (torch's input generation and copies), {other_ms:.3f} ms in total."]
     open(out_md, "w").write("\n".join(lines) + "\n")
     print(f"wrote {out_md}")
 
@@ -291,19 +315,25 @@ def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 3
     if not copy_f or not copy_w:
         raise SystemExit("no copy kernel found in the counter runs (run bench.py with --copy-calibration)")
     kf, kw = copy_bytes / (sum(copy_f) / len(copy_f)), copy_bytes / (sum(copy_w) / len(copy_w))
-    kernels = {"scan_bf16": ("scan_bf16.hip", "Cfg<128, 64, 1, 64,"), "decode": ("decode.hip", "k_decode")}
+    # the headline SISO scan, the decode step, and both again with the fused block prologue / epilogue
+    # (demangled or mangled names, as rocprofv3 prints them)
+    kernels = {"scan_bf16": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, false>",)),
+               "scan_bf16_block": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, true>",)),
+               "decode": ("decode.hip", ("k_decode_colIDF16bLi64ELi4ELb0E", "k_decode_col<__bf16, 64, 4, false>")),
+               "decode_block": ("decode.hip", ("k_decode_colIDF16bLi64ELi4ELb1E", "k_decode_col<__bf16, 64, 4, true>"))}
     md = ["# HBM traffic per launch from rocprofv3 counters", "", "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):",
           "", "```", *commands, "```", "",
           f"Calibration: a plain 1 GiB device copy reads {sum(copy_f) / len(copy_f) / 2**30:.4f} GiB by FETCH_SIZE and writes "
           f"{sum(copy_w) / len(copy_w) / 2**30:.4f} GiB by WRITE_SIZE; scale factors {kf:.4f} (fetch), {kw:.4f} (write).", "",
           "| kernel | dispatches | fetch MB | write MB | traffic MB per launch |", "|---|---|---|---|---|"]
-    for key, (src, pat) in kernels.items():
-        fs = [v for n, vs in fetch.items() if pat in n for v in vs]
-        ws = [v for n, vs in write.items() if pat in n for v in vs]
+    for key, (src, pats) in kernels.items():
+        hit = lambda n: any(p in n for p in pats)
+        fs = [v for n, vs in fetch.items() if hit(n) for v in vs]
+        ws = [v for n, vs in write.items() if hit(n) for v in vs]
         if not fs or not ws:
             continue
         fb, wb = kf * sum(fs) / len(fs), kw * sum(ws) / len(ws)
-        name = next(n for n in fetch if pat in n)
+        name = next(n for n in fetch if hit(n))
         srcp = os.path.join(ROOT, "state_space_sequence_mamba3_amd", "csrc", src)
         rec = {"kernel": _short(name), "source": src,
                "source_sha256": hashlib.sha256(open(srcp, "rb").read()).hexdigest(),
@@ -367,9 +397,17 @@ def main():
         print(f"# mimo scan G=1 {res['mimo_g1']['ms']:.3f} ms", file=sys.stderr, flush=True)
         res["packed_g1"] = bench_scan(4, max(2, args.steps // 2), max(1, args.warmup // 2), dev, ngroups=1)
         print(f"# packed scan G=1 {res['packed_g1']['ms']:.3f} ms", file=sys.stderr, flush=True)
+        # the fused block prologue / epilogue on
+        res["siso_block"] = bench_scan(1, args.steps, args.warmup, dev, block=True)
+        print(f"# siso scan + block {res['siso_block']['ms']:.3f} ms", file=sys.stderr, flush=True)
+        res["mimo_block"] = bench_scan(2, args.steps, args.warmup, dev, block=True)
+        print(f"# mimo scan + block {res['mimo_block']['ms']:.3f} ms", file=sys.stderr, flush=True)
     if args.only in ("decode", "all"):
         res["decode"] = bench_decode(1000, 1, dev)
         print(f"# decode {res['decode']['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
+    if args.only == "all":
+        res["decode_block"] = bench_decode(1000, 1, dev, block=True)
+        print(f"# decode + block {res['decode_block']['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline and args.only in ("scan", "all"):
@@ -395,7 +433,7 @@ def main():
     else:
         line = {"metric": METRIC, "value": None}
     sec = {}
-    for k in ("mimo", "packed", "mimo_g1", "packed_g1"):
+    for k in ("mimo", "packed", "mimo_g1", "packed_g1", "siso_block", "mimo_block"):
         if k in res:
             r = res[k]
             # the binding roofline: whichever of HBM bytes and MFMA flops needs more time at peak
@@ -407,15 +445,18 @@ def main():
                      "frac": r["hbm_gbs"] / HBM_PEAK_GBS, "mfma_tflops": r["mfma_tfs"],
                      "mfma_frac": r["mfma_tfs"] / MFMA_BF16_PEAK_TFS})
             roof.update(bytes_per_launch=r["bytes"], flops_per_launch=r["flops"])
+            if k == "siso_block":
+                roof["traffic"] = traffic_record("scan_bf16_block")
             sec[k] = {"workload": r["workload"], "ms": r["ms"], "tokens_per_s": r["tokens_per_s"], "roofline": roof}
-    if "decode" in res:
-        r = res["decode"]
-        sec["decode"] = {"workload": r["workload"], "us_per_step": r["us_per_step"], "median_us": r["median_us"],
-                         "graph_wall_us": r["graph_wall_us"], "steps": r["steps"],
-                         "roofline": {"bound": "hbm", "achieved": r["hbm_gbs"], "peak": HBM_PEAK_GBS,
-                                      "unit": "GB/s", "frac": r["hbm_gbs"] / HBM_PEAK_GBS,
-                                      "bytes_per_launch": r["bytes_per_step"],
-                                      "traffic": traffic_record("decode")}}
+    for k in ("decode", "decode_block"):
+        if k in res:
+            r = res[k]
+            sec[k] = {"workload": r["workload"], "us_per_step": r["us_per_step"], "median_us": r["median_us"],
+                      "graph_wall_us": r["graph_wall_us"], "steps": r["steps"],
+                      "roofline": {"bound": "hbm", "achieved": r["hbm_gbs"], "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": r["hbm_gbs"] / HBM_PEAK_GBS,
+                                   "bytes_per_launch": r["bytes_per_step"],
+                                   "traffic": traffic_record(k)}}
     line["secondary"] = sec
     print(json.dumps(line), flush=True)
 

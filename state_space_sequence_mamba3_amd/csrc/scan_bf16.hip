@@ -85,6 +85,14 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16 *m, int ld, int r0, int 
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// The value, made opaque to the compiler when ON: address math derived from it is then
+// recomputed where it is used instead of being hoisted out of the chunk loop (and spilled).
+template <bool ON>
+__device__ __forceinline__ int opaque(int v) {
+    if constexpr (ON) asm volatile("" : "+v"(v));
+    return v;
+}
+
 // Wait for this wave's outstanding LDS operations (wave-private staging).
 __device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
@@ -177,9 +185,10 @@ struct Cfg {
     // LDS layout (bytes)
     static constexpr int YPS = EPI ? P + 4 : PS;                       // output staging row stride (elements)
     static constexpr int YST = 16 * YPS * (EPI ? 4 : 2);               // per-wave output staging (fp32 with EPI)
-    static constexpr int REG0 = (Q * K * 4 > NW * YST) ? Q * K * 4 : NW * YST;
+    // with EPI the output staging shares the angle table's bytes (the table is dead from the end of
+    // the sweep to the next chunk's prologue); otherwise it has a region of its own
+    static constexpr int REG0 = EPI ? ((Q * K * 4 > NW * YST) ? Q * K * 4 : NW * YST) : Q * K * 4;
     static constexpr int OFF_PHI = 0;                                  // f16x2 [Q][K] (cos, sin) of Phi
-    static constexpr int OFF_Y = 0;                                    // output staging, shares the table's bytes
     static constexpr int OFF_PHC = REG0;                               // float2 [K] (cos, sin) of the chunk's total angle
     static constexpr int OFF_S2 = OFF_PHC + K * 8;                     // float [Q] log2 decay prefix
     static constexpr int OFF_A2 = OFF_S2 + Q * 4;                      // float [Q] per-token log2 decay
@@ -196,7 +205,8 @@ struct Cfg {
     static constexpr int OFF_U = OFF_HB + P * NS * 2;                  // stage buffers / output staging
     static constexpr int SB_BT = 0, SB_X = SBR * NS * 2, SB_WX = SB_X + SBR * PS * 2;
     static constexpr int STAGE = SB_WX + SBR * PS * 2;                 // one s-block stage
-    static constexpr int LDS = OFF_U + NST * STAGE;
+    static constexpr int OFF_Y = EPI ? 0 : OFF_U + NST * STAGE;        // per-wave output staging
+    static constexpr int LDS = EPI ? OFF_U + NST * STAGE : OFF_Y + NW * YST;
     static_assert(LDS <= 160 * 1024, "LDS");
     // global loads (16 bytes each) per s-block, and next-chunk header prefetch
     static constexpr int BCH = SBR * N / 8, XCH = SBR * P / 8;
@@ -362,24 +372,26 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     bf16x2 h_th2[CF::TPL];          // theta of the lane's angle pair for its TPL tokens
     bf16x8 h_c[TPW][NKK];
     // C rows of the own t-blocks in operand layout: row 16 tb + l16, columns 32 kk + 8 q4 ..
-    auto load_crows = [&](int64_t c0h) {
+    // tq: the thread index the address math uses (tid, or an opaque copy inside the chunk loop)
+    auto load_crows = [&](int64_t c0h, int tq) {
         const int64_t c0c = c0h < len ? c0h : 0;
         const int64_t t0h = start + c0c, last = len - c0c - 1;
+        const int l16q = tq & 15, q4q = (tq & 63) >> 4;
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
-            const int row = tb_of(u, c0h) * 16 + l16;
+            const int row = tb_of(u, c0h) * 16 + l16q;
             const int tau = row / R, j = row % R;
             const int64_t tk = t0h + min((int64_t)tau, last);
 #pragma unroll
-            for (int kk = 0; kk < NKK; kk++) h_c[u][kk] = *(const bf16x8 *)(gC + tk * strBC + j * N + 32 * kk + 8 * q4);
+            for (int kk = 0; kk < NKK; kk++) h_c[u][kk] = *(const bf16x8 *)(gC + tk * strBC + j * N + 32 * kk + 8 * q4q);
         }
     };
-    auto load_header = [&](int64_t c0h) {
+    auto load_header = [&](int64_t c0h, int tq) {
         const int64_t c0c = c0h < len ? c0h : 0;
         const int nqh = (int)min((int64_t)Q, len - c0c);
         const int64_t t0h = start + c0c, last = len - c0c - 1;
         {
-            const int64_t tk = t0h + min((int64_t)min(tid, Q - 1), last);
+            const int64_t tk = t0h + min((int64_t)min(tq, Q - 1), last);
             h_dt = pr.dt[tk * H + h];
             h_lam = pr.lam[tk * H + h];
             const int64_t tn = t0h + min((int64_t)nqh, last);
@@ -387,24 +399,25 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             h_lamn = pr.lam[tn * H + h];
         }
         {
-            const int k = wave * CF::KW + 2 * (lane % CF::KP), g0 = (lane / CF::KP) * CF::TPL;
+            const int lq = tq & 63;
+            const int k = wave * CF::KW + 2 * (lq % CF::KP), g0 = (lq / CF::KP) * CF::TPL;
 #pragma unroll
             for (int j = 0; j < CF::TPL; j++) {
                 const int64_t tk = t0h + min((int64_t)(g0 + j), last);
                 h_th2[j] = *(const bf16x2 *)(gTh + tk * strTh + k);
             }
         }
-        if constexpr (CF::PFC) load_crows(c0h);
+        if constexpr (CF::PFC) load_crows(c0h, tq);
     };
 
     // ---- s-block stream: block j of the sequence lives in register set j % 2
     bf16x8 rb0[CF::NLB], rx0[CF::NLX], rb1[CF::NLB], rx1[CF::NLX];
-    auto load_block_into = [&](bf16x8 (&rb)[CF::NLB], bf16x8 (&rx)[CF::NLX], int64_t c0b, int sb) {
+    auto load_block_into = [&](bf16x8 (&rb)[CF::NLB], bf16x8 (&rx)[CF::NLX], int64_t c0b, int sb, int tq) {
         const int64_t c0c = c0b < len ? c0b : 0;                   // past the end: dummy loads, never used
         const int64_t t0b = start + c0c, last = len - c0c - 1;
 #pragma unroll
         for (int i = 0; i < CF::NLB; i++) {
-            const int c = (tid + i * NTHR) % CF::BCH;
+            const int c = (tq + i * NTHR) % CF::BCH;
             const int row = c / (N / 8), col = (c % (N / 8)) * 8;
             const int tau = sb * TOKS + row / R;
             const int64_t tk = t0b + min((int64_t)tau, last);
@@ -412,7 +425,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         }
 #pragma unroll
         for (int i = 0; i < CF::NLX; i++) {
-            const int c = (tid + i * NTHR) % CF::XCH;
+            const int c = (tq + i * NTHR) % CF::XCH;
             const int row = c / (P / 8), col = (c % (P / 8)) * 8;
             const int tau = sb * TOKS + row / R;
             const int64_t tk = t0b + min((int64_t)tau, last);
@@ -432,11 +445,11 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     int64_t ld_c0 = 0;
     int ld_sb = 0;
     if (len > 0) {
-        load_header(0);
-        load_block_into(rb0, rx0, ld_c0, ld_sb);
+        load_header(0, tid);
+        load_block_into(rb0, rx0, ld_c0, ld_sb, tid);
         advance(ld_c0, ld_sb);
         if constexpr (CF::NST == 2) {
-            load_block_into(rb1, rx1, ld_c0, ld_sb);
+            load_block_into(rb1, rx1, ld_c0, ld_sb, tid);
             advance(ld_c0, ld_sb);
         }
     }
@@ -449,6 +462,9 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     auto chunk_body = [&](auto FULLC, int64_t c0) {
         constexpr bool FULL = decltype(FULLC)::value;
         const int nq = FULL ? Q : (int)(len - c0);
+        // with the fused prologue / epilogue the registers run short: the lane-derived address
+        // math of the prefetch, staging and output code is recomputed in every chunk
+        const int tq = opaque<CF::EPI>(tid);
         const int64_t tok0 = start + c0;
         int task_tb[TPW];
 #pragma unroll
@@ -583,7 +599,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         __syncthreads();
 
         // ---- rotated C~ rows of this wave's t-blocks, from the prefetched (or just loaded) raw rows
-        if constexpr (!CF::PFC) load_crows(c0);
+        if constexpr (!CF::PFC) load_crows(c0, tq);
         bf16x8 creg[TPW][NKK];
         f32x4 yacc[TPW][NPT];
 #pragma unroll
@@ -648,7 +664,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 for (int r = 0; r < UR_; r++) hreg[v][r] *= eS;
         }
         // the header registers are consumed: prefetch the next chunk's header now
-        load_header(c0 + Q);
+        load_header(c0 + Q, tq);
 
         // ---- s-block sweep
         // lane coordinates made opaque per chunk: the mask indices derived from them are
@@ -671,18 +687,18 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             float wxv[CF::NLX];
 #pragma unroll
             for (int i = 0; i < CF::NLB; i++) {
-                const int c = min(tid + i * NTHR, CF::BCH - 1);
+                const int c = min(tq + i * NTHR, CF::BCH - 1);
                 csb[i] = *(const f16x8 *)(cst + (sb * TOKS + (c / (N / 8)) / R) * K + (c % (N / 8)) * 4);
             }
 #pragma unroll
             for (int i = 0; i < CF::NLX; i++) {
-                const int c = min(tid + i * NTHR, CF::XCH - 1);
+                const int c = min(tq + i * NTHR, CF::XCH - 1);
                 wxv[i] = WU[sb * TOKS + (c / (P / 8)) / R];
             }
             // prologue: a row's pieces are N/8 consecutive lanes, and every piece of this thread
             // covers the same columns (NTHR is a multiple of N/8), so one bias slice serves all
             float binv[CF::NLB];
-            const float *bslice = BIA + (tid % (N / 8)) * 8;
+            const float *bslice = BIA + (tq % (N / 8)) * 8;
 #pragma unroll
             for (int i = 0; i < CF::NLB; i++) binv[i] = 1.f;
             if constexpr (CF::EPI) {
@@ -698,7 +714,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             }
 #pragma unroll
             for (int i = 0; i < CF::NLB; i++) {
-                const int c = tid + i * NTHR;
+                const int c = tq + i * NTHR;
                 if (c < CF::BCH) {
                     const int row = c / (N / 8), col = (c % (N / 8)) * 8;
                     const int tau = sb * TOKS + row / R;
@@ -715,7 +731,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             }
 #pragma unroll
             for (int i = 0; i < CF::NLX; i++) {
-                const int c = tid + i * NTHR;
+                const int c = tq + i * NTHR;
                 if (c < CF::XCH) {
                     const int row = c / (P / 8), col = (c % (P / 8)) * 8;
                     const int tau = sb * TOKS + row / R;
@@ -890,8 +906,8 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         // block is computed and block sb + 1 is staged from the other set
         auto step = [&](auto SETC, int sb) {
             constexpr int ST = decltype(SETC)::value;
-            if constexpr (ST == 0) load_block_into(rb0, rx0, ld_c0, ld_sb);
-            else load_block_into(rb1, rx1, ld_c0, ld_sb);
+            if constexpr (ST == 0) load_block_into(rb0, rx0, ld_c0, ld_sb, tq);
+            else load_block_into(rb1, rx1, ld_c0, ld_sb, tq);
             advance(ld_c0, ld_sb);
             compute_block(sb);
             if (sb + 1 < nbs) {
@@ -904,7 +920,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             // the whole chunk is one s-block: stage it, then reuse the register set for the
             // next chunk's block while this one is computed
             store_block(rb0, rx0, 0, 0);
-            load_block_into(rb0, rx0, ld_c0, ld_sb);
+            load_block_into(rb0, rx0, ld_c0, ld_sb, tq);
             advance(ld_c0, ld_sb);
             __syncthreads();
             compute_block(0);
@@ -958,7 +974,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 if (has_z) {
 #pragma unroll
                     for (int k = 0; k < NPC; k++) {
-                        const int c = lane + 64 * k, row = c / (P / 8), col = (c % (P / 8)) * 8;
+                        const int c = (tq & 63) + 64 * k, row = c / (P / 8), col = (c % (P / 8)) * 8;
                         const int rr = tb * 16 + row, tau = min(rr / R, nq - 1);   // in bounds; unused past the end
                         zr[k] = *(const bf16x8 *)(gZ + (tok0 + tau) * strX + (rr % R) * P + col);
                     }
@@ -970,7 +986,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 lds_wait();
 #pragma unroll
                 for (int k = 0; k < NPC; k++) {
-                    const int c = lane + 64 * k, row = c / (P / 8), col = (c % (P / 8)) * 8;
+                    const int c = (tq & 63) + 64 * k, row = c / (P / 8), col = (c % (P / 8)) * 8;
                     const int rr = tb * 16 + row, tau = rr / R;
                     const f32x4 a = *(const f32x4 *)(ysf + row * CF::YPS + col);
                     const f32x4 b = *(const f32x4 *)(ysf + row * CF::YPS + col + 4);

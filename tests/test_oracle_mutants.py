@@ -5,8 +5,8 @@ which do not compare the oracle's two recurrence forms with each other fail.
 Mistakes planted: the previous-token term skipping the step's rotation/decay,
 the rotation direction, the sign of C's or B's imaginary part, trapezoid
 weights swapped, rank columns mixed, the D term dropped, a stale previous
-token, a sigmoid instead of a SiLU gate, an L2 instead of an RMS norm, and
-every head taking head 0's bias."""
+token, a sigmoid instead of a SiLU gate, an L2 instead of an RMS norm, the
+norm's eps added outside the root, and every head taking head 0's bias."""
 import os
 import shutil
 import subprocess
@@ -31,6 +31,7 @@ MUTATIONS = {
                      "yt[i * P + p] = gate(a, creal(acc), ox + i * P + p);"),
     "gate_sigmoid_only": ("return y * v / (1.0 + exp(-v));", "return y / (1.0 + exp(-v));"),
     "norm_without_mean": ("1.0 / sqrt(ss / N + a->bc_eps)", "1.0 / sqrt(ss + a->bc_eps)"),
+    "eps_outside_root": ("1.0 / sqrt(ss / N + a->bc_eps)", "1.0 / (sqrt(ss / N) + a->bc_eps)"),
     "bias_of_head_zero": ("out[n] += bias[(int64_t)h * N + n];", "out[n] += bias[n];"),
     "stale_previous": ("memcpy(bp, bc, (size_t)K * R * sizeof *bp);\n        memcpy(xp, xc, (size_t)P * R * sizeof *xp);\n",
                        ""),

@@ -385,6 +385,32 @@ def test_bc_norm_fixes_unit_rms_columns(oracle):
     assert relerr(y1, y0) < 1e-13 and relerr(h1, h0) < 1e-13
 
 
+@pytest.mark.parametrize("form", [1, 2, 3])
+def test_bc_norm_eps_closed_form(oracle, form):
+    """First token of a sequence (zero state, no previous token): H_0 = gamma_0 B x^T and
+    y_0 = gamma_0 x (B.C) + D x. With constant columns B = b, C = c and the norm on, each
+    column becomes b / sqrt(b^2 + eps), so y_0 = gamma_0 x N b c / sqrt((b^2+eps)(c^2+eps))
+    + D x: this fixes where eps enters."""
+    rng = np.random.default_rng(76)
+    H, N, P, eps = 2, 6, 3, 0.37
+    inp = rand_inputs(rng, b=1, L=1, H=H, G=H, P=P, N=N, R=1)
+    bv, cv = np.array([0.8, -1.7]), np.array([-0.6, 2.2])   # per head
+    inp["B"] = np.broadcast_to(bv[None, None, :, None, None], inp["B"].shape).copy()
+    inp["C"] = np.broadcast_to(cv[None, None, :, None, None], inp["C"].shape).copy()
+    if form == 3:
+        y, _ = oracle.scan_slab(dict(inp, bc_norm=True, bc_eps=eps), 0, 0, form=3, want_state=False)
+        heads = [0]
+        y = y[None, :, None]
+    else:
+        y, _ = oracle.scan(dict(inp, bc_norm=True, bc_eps=eps), form=form)
+        heads = range(H)
+    for h in heads:
+        gamma = inp["lam"][0, 0, h] * inp["dt"][0, 0, h]
+        x = inp["x"][0, 0, h, 0]
+        want = gamma * x * N * bv[h] * cv[h] / math.sqrt((bv[h] ** 2 + eps) * (cv[h] ** 2 + eps)) + inp["D"][h] * x
+        assert relerr(y[0, 0, h, 0], want) < 1e-13
+
+
 def test_bc_bias_is_a_per_head_column_offset(oracle):
     """Zero B and C data plus per-head biases equals the plain layer fed, for
     every token and rank column, B and C equal to that head's bias vectors
