@@ -366,7 +366,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the scan and decode shard over (sequence, head) with no communication, see DESIGN.md", file=sys.stderr)
+              "the scan and decode shard over (sequence, head) with no communication", file=sys.stderr)
         sys.exit(2)
 
     import torch
