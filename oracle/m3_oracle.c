@@ -397,6 +397,243 @@ static void o3_slab(const m3o_args *a, int s, int h, double *y_slab) {
     free(Bt); free(Ct); free(X); free(psi); free(tmp); free(row);
 }
 
+/* ---------------------------------------------------------------- OB ---- */
+/* Gradient of the layer (reverse mode), one (sequence, head) slab at a time.
+ *
+ * Given dL/dy for every output and dL/dh_out for the final state, it returns
+ * dL/d(every input). It is the chain rule taken backwards through the plain
+ * real-form recurrence of the physical frame (the statement in the header):
+ *   U_t = H_{t-1} + delta_t Bp_t Xp_t^T      (Bp, Xp: the previous token, or Bprev, xprev)
+ *   H_t = alpha_t R(dt_t theta_t) U_t + gamma_t B_t X_t^T
+ *   y_t = gate(H_t^T C_t + D X_t, z_t)
+ * Backwards, with G = dL/dH_t carried from the future (dh_out at the end):
+ *   G      += C_t dy0_t^T                   (dy0: dy through the gate)
+ *   dC_t    = H_t dy0_t,   dX_t += D dy0_t + gamma_t G^T B_t,   dB_t += gamma_t G X_t
+ *   dgamma  = <G, B_t X_t^T>,  dalpha = <G, R U_t>,  dphi_k = alpha <G_k, R'(phi_k) U_k>
+ *   V       = alpha R^T G                   (= dL/dU_t)
+ *   ddelta  = <V, Bp Xp^T>,  dBp += delta V Xp,  dXp += delta V^T Bp,  and G <- V
+ * then alpha = e^{dt A}, delta = (1 - lam) dt, gamma = lam dt, phi = dt theta
+ * give dA, ddt, dlam, dtheta; the prologue's norm and bias and the gate are
+ * differentiated as written in bc_row and gate. No chunking, no reordering.
+ * (The pins compare every gradient with central differences of O1.) */
+typedef struct {
+    const double *dy;      /* [T, H, R, P] */
+    const double *dh_out;  /* [nseq, H, N, P] or NULL */
+    /* outputs, accumulated into caller-zeroed arrays (NULL: not wanted) */
+    double *dx;            /* [T, H, R, P] */
+    double *ddt, *dlam;    /* [T, H] */
+    double *dtheta;        /* [T, H, N/2] */
+    double *dB, *dC;       /* [T, G, R, N] */
+    double *dA, *dD;       /* [H] */
+    double *dh_in;         /* [nseq, H, N, P] */
+    double *dBprev;        /* [nseq, G, R, N] */
+    double *dxprev;        /* [nseq, H, R, P] */
+    double *dB_bias, *dC_bias;   /* [H, N] */
+    double *dz;            /* [T, H, R, P] */
+} m3o_grads;
+
+/* Backward of bc_row: gout = dL/d(out) for the N outputs; adds dL/d(raw column)
+ * to graw and dL/d(bias) to gbias (if not NULL). out = v inv + bias with
+ * inv = (mean(v^2) + eps)^(-1/2) when the norm is on (else inv = 1), so
+ * d out_n / d v_m = inv [n = m] - v_n v_m inv^3 / N. */
+static void bc_row_bwd(const m3o_args *a, const void *src, int64_t off, const double *gout, double *graw,
+                       double *gbias) {
+    const int N = a->N;
+    double *v = malloc((size_t)N * sizeof *v);
+    double ss = 0.0, dot = 0.0;
+    for (int n = 0; n < N; n++) {
+        v[n] = ld(src, a->in_dtype, off + n);
+        ss += v[n] * v[n];
+        dot += gout[n] * v[n];
+    }
+    if (gbias)
+        for (int n = 0; n < N; n++) gbias[n] += gout[n];
+    if (a->bc_norm) {
+        const double inv = 1.0 / sqrt(ss / N + a->bc_eps);
+        for (int m = 0; m < N; m++) graw[m] += gout[m] * inv - dot * inv * inv * inv * v[m] / N;
+    } else {
+        for (int m = 0; m < N; m++) graw[m] += gout[m];
+    }
+    free(v);
+}
+
+static void ob_slab(const m3o_args *a, const m3o_grads *gr, int s, int h, double *dA_h, double *dD_h,
+                    double *dBb_h, double *dCb_h) {
+    const int H = a->H, G = a->G, P = a->P, N = a->N, R = a->R, K = N / 2;
+    const int g = h / (H / G);
+    const int dtp = a->in_dtype;
+    const int64_t t0 = a->seq_start[s], L = a->seq_len[s];
+    const size_t NP = (size_t)N * P, RN = (size_t)R * N, RP = (size_t)R * P;
+    const double Ah = a->A[h], Dh = a->D ? a->D[h] : 0.0;
+    const int has_prev = a->Bprev && a->xprev;
+    const int64_t Lm = L > 0 ? L : 1;
+
+    /* the recurrence's B, C (after the prologue) and x, rank-major [R][N] / [R][P] per token */
+    double *Be = malloc(Lm * RN * sizeof *Be), *Ce = malloc(Lm * RN * sizeof *Ce);
+    double *X = malloc(Lm * RP * sizeof *X), *Bpe = calloc(RN, sizeof *Bpe), *Xp0 = calloc(RP, sizeof *Xp0);
+    for (int64_t t = 0; t < L; t++) {
+        const int64_t ob = ((t0 + t) * G + g) * RN, ox = ((t0 + t) * H + h) * RP;
+        for (int j = 0; j < R; j++) {
+            bc_row(a, a->B, ob + j * N, h, a->B_bias, Be + t * RN + j * N);
+            bc_row(a, a->C, ob + j * N, h, a->C_bias, Ce + t * RN + j * N);
+        }
+        for (size_t e = 0; e < RP; e++) X[t * RP + e] = ld(a->x, dtp, ox + e);
+    }
+    if (has_prev) {
+        for (int j = 0; j < R; j++) bc_row(a, a->Bprev, ((int64_t)s * G + g) * RN + j * N, h, a->B_bias, Bpe + j * N);
+        for (size_t e = 0; e < RP; e++) Xp0[e] = ld(a->xprev, dtp, ((int64_t)s * H + h) * RP + e);
+    }
+    /* forward: every state H_t kept ([L][N][P]), plus the initial one */
+    double *Hall = malloc((Lm + 1) * NP * sizeof *Hall);   /* Hall[0] = H_{-1}, Hall[t+1] = H_t */
+    for (size_t e = 0; e < NP; e++) Hall[e] = a->h_in ? a->h_in[((int64_t)s * H + h) * NP + e] : 0.0;
+    double *U = malloc(NP * sizeof *U);
+    for (int64_t t = 0; t < L; t++) {
+        const int64_t tg = t0 + t;
+        const double dt = ld(a->dt, dtp, tg * H + h), lam = ld(a->lam, dtp, tg * H + h);
+        const double alpha = exp(dt * Ah), delta = (1.0 - lam) * dt, gamma = lam * dt;
+        const double *Hp = Hall + t * NP;
+        double *Hn = Hall + (t + 1) * NP;
+        const double *Bp = t > 0 ? Be + (t - 1) * RN : Bpe, *Xp = t > 0 ? X + (t - 1) * RP : Xp0;
+        const int prev = t > 0 || has_prev;
+        for (int n = 0; n < N; n++)
+            for (int p = 0; p < P; p++) {
+                double v = 0.0;
+                if (prev)
+                    for (int j = 0; j < R; j++) v += Bp[j * N + n] * Xp[j * P + p];
+                U[n * P + p] = Hp[n * P + p] + delta * v;
+            }
+        for (int k = 0; k < K; k++) {
+            const double ang = dt * ld(a->theta, dtp, tg * H * K + (int64_t)h * K + k);
+            const double c = cos(ang), sn = sin(ang);
+            for (int p = 0; p < P; p++) {
+                const double u0 = U[(2 * k) * P + p], u1 = U[(2 * k + 1) * P + p];
+                double w0 = 0.0, w1 = 0.0;
+                for (int j = 0; j < R; j++) {
+                    w0 += Be[t * RN + j * N + 2 * k] * X[t * RP + j * P + p];
+                    w1 += Be[t * RN + j * N + 2 * k + 1] * X[t * RP + j * P + p];
+                }
+                Hn[(2 * k) * P + p] = alpha * (c * u0 - sn * u1) + gamma * w0;
+                Hn[(2 * k + 1) * P + p] = alpha * (sn * u0 + c * u1) + gamma * w1;
+            }
+        }
+    }
+    /* reverse */
+    double *Gm = calloc(NP, sizeof *Gm), *V = malloc(NP * sizeof *V);
+    double *dBe = calloc(Lm * RN, sizeof *dBe), *dCe = calloc(Lm * RN, sizeof *dCe);
+    double *dX = calloc(Lm * RP, sizeof *dX), *dBpe = calloc(RN, sizeof *dBpe), *dXp0 = calloc(RP, sizeof *dXp0);
+    double *dy0 = malloc(RP * sizeof *dy0), *dphi = malloc((size_t)K * sizeof *dphi);
+    if (gr->dh_out)
+        for (size_t e = 0; e < NP; e++) Gm[e] = gr->dh_out[((int64_t)s * H + h) * NP + e];
+    for (int64_t t = L - 1; t >= 0; t--) {
+        const int64_t tg = t0 + t;
+        const double dt = ld(a->dt, dtp, tg * H + h), lam = ld(a->lam, dtp, tg * H + h);
+        const double alpha = exp(dt * Ah), delta = (1.0 - lam) * dt, gamma = lam * dt;
+        const double *Ht = Hall + (t + 1) * NP, *Hp = Hall + t * NP;
+        const double *Bt = Be + t * RN, *Ct = Ce + t * RN, *Xt = X + t * RP;
+        const int64_t oy = (tg * H + h) * RP;
+        /* output and gate */
+        for (int i = 0; i < R; i++)
+            for (int p = 0; p < P; p++) {
+                double y0 = Dh * Xt[i * P + p];
+                for (int n = 0; n < N; n++) y0 += Ht[n * P + p] * Ct[i * N + n];
+                const double d = gr->dy[oy + i * P + p];
+                if (a->z) {
+                    const double v = ld(a->z, dtp, oy + i * P + p), sg = 1.0 / (1.0 + exp(-v));
+                    dy0[i * P + p] = d * v * sg;
+                    if (gr->dz) gr->dz[oy + i * P + p] += d * y0 * (sg + v * sg * (1.0 - sg));
+                } else {
+                    dy0[i * P + p] = d;
+                }
+                dX[t * RP + i * P + p] += Dh * dy0[i * P + p];
+                *dD_h += dy0[i * P + p] * Xt[i * P + p];
+            }
+        for (int i = 0; i < R; i++)
+            for (int n = 0; n < N; n++) {
+                double acc = 0.0;
+                for (int p = 0; p < P; p++) acc += Ht[n * P + p] * dy0[i * P + p];
+                dCe[t * RN + i * N + n] += acc;
+            }
+        for (int n = 0; n < N; n++)
+            for (int p = 0; p < P; p++)
+                for (int i = 0; i < R; i++) Gm[n * P + p] += Ct[i * N + n] * dy0[i * P + p];
+        /* H_t = alpha R U + gamma B X^T */
+        double dgamma = 0.0, dalpha = 0.0, ddelta = 0.0;
+        for (int n = 0; n < N; n++)
+            for (int p = 0; p < P; p++)
+                for (int j = 0; j < R; j++) {
+                    dgamma += Gm[n * P + p] * Bt[j * N + n] * Xt[j * P + p];
+                    dBe[t * RN + j * N + n] += gamma * Gm[n * P + p] * Xt[j * P + p];
+                    dX[t * RP + j * P + p] += gamma * Gm[n * P + p] * Bt[j * N + n];
+                }
+        const double *Bp = t > 0 ? Be + (t - 1) * RN : Bpe, *Xp = t > 0 ? X + (t - 1) * RP : Xp0;
+        const int prev = t > 0 || has_prev;
+        for (int n = 0; n < N; n++)
+            for (int p = 0; p < P; p++) {
+                double v = 0.0;
+                if (prev)
+                    for (int j = 0; j < R; j++) v += Bp[j * N + n] * Xp[j * P + p];
+                U[n * P + p] = Hp[n * P + p] + delta * v;
+            }
+        for (int k = 0; k < K; k++) {
+            const double ang = dt * ld(a->theta, dtp, tg * H * K + (int64_t)h * K + k);
+            const double c = cos(ang), sn = sin(ang);
+            double acc = 0.0;
+            for (int p = 0; p < P; p++) {
+                const double u0 = U[(2 * k) * P + p], u1 = U[(2 * k + 1) * P + p];
+                const double g0 = Gm[(2 * k) * P + p], g1 = Gm[(2 * k + 1) * P + p];
+                dalpha += g0 * (c * u0 - sn * u1) + g1 * (sn * u0 + c * u1);
+                acc += g0 * (-sn * u0 - c * u1) + g1 * (c * u0 - sn * u1);
+                V[(2 * k) * P + p] = alpha * (c * g0 + sn * g1);
+                V[(2 * k + 1) * P + p] = alpha * (-sn * g0 + c * g1);
+            }
+            dphi[k] = alpha * acc;
+        }
+        /* U = H_{t-1} + delta Bp Xp^T */
+        if (prev) {
+            double *dBp = t > 0 ? dBe + (t - 1) * RN : dBpe, *dXp = t > 0 ? dX + (t - 1) * RP : dXp0;
+            for (int n = 0; n < N; n++)
+                for (int p = 0; p < P; p++)
+                    for (int j = 0; j < R; j++) {
+                        ddelta += V[n * P + p] * Bp[j * N + n] * Xp[j * P + p];
+                        dBp[j * N + n] += delta * V[n * P + p] * Xp[j * P + p];
+                        dXp[j * P + p] += delta * V[n * P + p] * Bp[j * N + n];
+                    }
+        }
+        memcpy(Gm, V, NP * sizeof *Gm);
+        /* scalars: alpha = e^{dt A}, delta = (1 - lam) dt, gamma = lam dt, phi_k = dt theta_k */
+        double ddt = Ah * alpha * dalpha + (1.0 - lam) * ddelta + lam * dgamma;
+        for (int k = 0; k < K; k++) {
+            const double th = ld(a->theta, dtp, tg * H * K + (int64_t)h * K + k);
+            ddt += th * dphi[k];
+            if (gr->dtheta) gr->dtheta[(tg * H + h) * K + k] += dt * dphi[k];
+        }
+        if (gr->ddt) gr->ddt[tg * H + h] += ddt;
+        if (gr->dlam) gr->dlam[tg * H + h] += dt * (dgamma - ddelta);
+        *dA_h += dt * alpha * dalpha;
+    }
+    if (gr->dh_in)
+        for (size_t e = 0; e < NP; e++) gr->dh_in[((int64_t)s * H + h) * NP + e] += Gm[e];
+    /* back through the prologue to the raw B, C columns (shared by the heads of a group) */
+    for (int64_t t = 0; t < L; t++) {
+        const int64_t ob = ((t0 + t) * G + g) * RN, ox = ((t0 + t) * H + h) * RP;
+        for (int j = 0; j < R; j++) {
+            if (gr->dB) bc_row_bwd(a, a->B, ob + j * N, dBe + t * RN + j * N, gr->dB + ob + j * N, a->B_bias ? dBb_h : NULL);
+            if (gr->dC) bc_row_bwd(a, a->C, ob + j * N, dCe + t * RN + j * N, gr->dC + ob + j * N, a->C_bias ? dCb_h : NULL);
+        }
+        if (gr->dx)
+            for (size_t e = 0; e < RP; e++) gr->dx[ox + e] += dX[t * RP + e];
+    }
+    if (has_prev) {
+        const int64_t ob = ((int64_t)s * G + g) * RN, ox = ((int64_t)s * H + h) * RP;
+        for (int j = 0; j < R; j++)
+            if (gr->dBprev) bc_row_bwd(a, a->Bprev, ob + j * N, dBpe + j * N, gr->dBprev + ob + j * N, a->B_bias ? dBb_h : NULL);
+        if (gr->dxprev)
+            for (size_t e = 0; e < RP; e++) gr->dxprev[ox + e] += dXp0[e];
+    }
+    free(Be); free(Ce); free(X); free(Bpe); free(Xp0); free(Hall); free(U); free(Gm); free(V);
+    free(dBe); free(dCe); free(dX); free(dBpe); free(dXp0); free(dy0); free(dphi);
+}
+
 /* ------------------------------------------------------------ exports ---- */
 static int check(const m3o_args *a) {
     if (!a || a->nseq < 0 || a->H <= 0 || a->G <= 0 || a->P <= 0 || a->N <= 0 || a->R <= 0) return 1;
@@ -465,6 +702,40 @@ int m3o_decode(const m3o_args *a_in, double *h_io, double *y, int nthreads) {
         o1_slab(&a, s, h, y + ((int64_t)s * H + h) * P * R, h_io + ((int64_t)s * H + h) * N * P);
     }
     free(hcopy);
+    return 0;
+}
+
+/* Gradient of the whole scan (OB). Sequences run in parallel; the heads of a
+ * sequence run in order, so the heads of a group add into dB, dC, dBprev one
+ * after another. The per-head sums dA, dD and the bias gradients are added
+ * in sequence order. */
+int m3o_scan_bwd(const m3o_args *a, const m3o_grads *gr, int nthreads) {
+    if (check(a) || !gr || !gr->dy) return 1;
+    const int H = a->H, N = a->N;
+    double *pA = calloc((size_t)a->nseq * H + 1, sizeof *pA), *pD = calloc((size_t)a->nseq * H + 1, sizeof *pD);
+    double *pBb = calloc((size_t)a->nseq * H * N + 1, sizeof *pBb), *pCb = calloc((size_t)a->nseq * H * N + 1, sizeof *pCb);
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int s = 0; s < a->nseq; s++)
+        for (int h = 0; h < H; h++) {
+            const int64_t sh = (int64_t)s * H + h;
+            ob_slab(a, gr, s, h, pA + sh, pD + sh, pBb + sh * N, pCb + sh * N);
+        }
+    for (int s = 0; s < a->nseq; s++)
+        for (int h = 0; h < H; h++) {
+            const int64_t sh = (int64_t)s * H + h;
+            if (gr->dA) gr->dA[h] += pA[sh];
+            if (gr->dD) gr->dD[h] += pD[sh];
+            for (int n = 0; n < N; n++) {
+                if (gr->dB_bias) gr->dB_bias[h * N + n] += pBb[sh * N + n];
+                if (gr->dC_bias) gr->dC_bias[h * N + n] += pCb[sh * N + n];
+            }
+        }
+    free(pA); free(pD); free(pBb); free(pCb);
     return 0;
 }
 

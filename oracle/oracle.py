@@ -56,6 +56,12 @@ class _Args(ctypes.Structure):
     ]
 
 
+class _Grads(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in (
+        "dy", "dh_out", "dx", "ddt", "dlam", "dtheta", "dB", "dC", "dA", "dD", "dh_in", "dBprev", "dxprev",
+        "dB_bias", "dC_bias", "dz")]
+
+
 _lib = None
 
 
@@ -69,6 +75,7 @@ def lib():
                                     ctypes.c_void_p, ctypes.c_void_p]
         l.m3o_decode.argtypes = [ctypes.POINTER(_Args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         l.m3o_max_threads.restype = ctypes.c_int
+        l.m3o_scan_bwd.argtypes = [ctypes.POINTER(_Args), ctypes.POINTER(_Grads), ctypes.c_int]
         _lib = l
     return _lib
 
@@ -178,3 +185,39 @@ def decode(inp: dict, h: np.ndarray, nthreads: int = 0):
     if rc:
         raise ValueError("oracle rejected its arguments")
     return y, hio
+
+
+def scan_bwd(inp: dict, dy: np.ndarray, dh_out: np.ndarray | None = None, nthreads: int = 0) -> dict:
+    """Gradient of the whole scan (OB, reverse mode in fp64): given dL/dy
+    (shaped like x) and dL/dh_out ([S,H,N,P] or None), returns float64 arrays
+    dx, ddt, dlam, dtheta, dB, dC (shaped like the inputs), dA, dD [H], dh_in
+    [S,H,N,P], and, where the inputs have them, dBprev, dxprev, dB_bias,
+    dC_bias, dz."""
+    flat, st, ln = flatten(inp)
+    pk = _Pack(flat, st, ln)
+    T = flat["x"].shape[0]
+    H, G, P, N, R, S = pk.H, pk.G, pk.P, pk.N, pk.R, pk.nseq
+    dyf = np.ascontiguousarray(np.asarray(dy, dtype=np.float64).reshape(T, H, R, P))
+    dho = None if dh_out is None else np.ascontiguousarray(dh_out, dtype=np.float64)
+    out = dict(dx=np.zeros((T, H, R, P)), ddt=np.zeros((T, H)), dlam=np.zeros((T, H)), dtheta=np.zeros((T, H, N // 2)),
+               dB=np.zeros((T, G, R, N)), dC=np.zeros((T, G, R, N)), dA=np.zeros(H), dD=np.zeros(H),
+               dh_in=np.zeros((S, H, N, P)))
+    if inp.get("Bprev") is not None:
+        out["dBprev"], out["dxprev"] = np.zeros((S, G, R, N)), np.zeros((S, H, R, P))
+    if inp.get("B_bias") is not None:
+        out["dB_bias"] = np.zeros((H, N))
+    if inp.get("C_bias") is not None:
+        out["dC_bias"] = np.zeros((H, N))
+    if inp.get("z") is not None:
+        out["dz"] = np.zeros((T, H, R, P))
+    g = _Grads(dyf.ctypes.data, _ptr(dho), *[_ptr(out.get(k)) for k in (
+        "dx", "ddt", "dlam", "dtheta", "dB", "dC", "dA", "dD", "dh_in", "dBprev", "dxprev", "dB_bias", "dC_bias", "dz")])
+    if lib().m3o_scan_bwd(ctypes.byref(pk.args), ctypes.byref(g), nthreads):
+        raise ValueError("oracle rejected its arguments")
+    shp = {k: inp[k].shape for k in ("x", "dt", "lam", "theta", "B", "C")}
+    for k, src in (("dx", "x"), ("ddt", "dt"), ("dlam", "lam"), ("dtheta", "theta"), ("dB", "B"), ("dC", "C")):
+        out[k] = out[k].reshape(shp[src])
+    if "dz" in out:
+        out["dz"] = out["dz"].reshape(inp["z"].shape)
+    return out
+

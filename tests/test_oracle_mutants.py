@@ -6,7 +6,11 @@ Mistakes planted: the previous-token term skipping the step's rotation/decay,
 the rotation direction, the sign of C's or B's imaginary part, trapezoid
 weights swapped, rank columns mixed, the D term dropped, a stale previous
 token, a sigmoid instead of a SiLU gate, an L2 instead of an RMS norm, the
-norm's eps added outside the root, and every head taking head 0's bias."""
+norm's eps added outside the root, every head taking head 0's bias; and in
+the gradient: the rotation's transpose taken the wrong way, the angle
+derivative's sign, the previous-token weight dropped from its gradient, the
+norm's Jacobian reduced to its diagonal, the gate's derivative without its
+input factor, and the decay's share of the step's gradient dropped."""
 import os
 import shutil
 import subprocess
@@ -30,9 +34,22 @@ MUTATIONS = {
     "no_skip_term": ("yt[i * P + p] = gate(a, creal(acc) + Dh * xc[p * R + i], ox + i * P + p);",
                      "yt[i * P + p] = gate(a, creal(acc), ox + i * P + p);"),
     "gate_sigmoid_only": ("return y * v / (1.0 + exp(-v));", "return y / (1.0 + exp(-v));"),
-    "norm_without_mean": ("1.0 / sqrt(ss / N + a->bc_eps)", "1.0 / sqrt(ss + a->bc_eps)"),
-    "eps_outside_root": ("1.0 / sqrt(ss / N + a->bc_eps)", "1.0 / (sqrt(ss / N) + a->bc_eps)"),
+    "norm_without_mean": ("1.0 / sqrt(ss / N + a->bc_eps);\n        for (int n = 0; n < N; n++) out[n] *= inv;",
+                          "1.0 / sqrt(ss + a->bc_eps);\n        for (int n = 0; n < N; n++) out[n] *= inv;"),
+    "eps_outside_root": ("1.0 / sqrt(ss / N + a->bc_eps);\n        for (int n = 0; n < N; n++) out[n] *= inv;",
+                         "1.0 / (sqrt(ss / N) + a->bc_eps);\n        for (int n = 0; n < N; n++) out[n] *= inv;"),
     "bias_of_head_zero": ("out[n] += bias[(int64_t)h * N + n];", "out[n] += bias[n];"),
+    "grad_rotation_transposed": ("V[(2 * k) * P + p] = alpha * (c * g0 + sn * g1);",
+                                 "V[(2 * k) * P + p] = alpha * (c * g0 - sn * g1);"),
+    "grad_angle_sign": ("acc += g0 * (-sn * u0 - c * u1) + g1 * (c * u0 - sn * u1);",
+                        "acc += g0 * (sn * u0 - c * u1) + g1 * (c * u0 - sn * u1);"),
+    "grad_prev_weight_dropped": ("dBp[j * N + n] += delta * V[n * P + p] * Xp[j * P + p];",
+                                 "dBp[j * N + n] += V[n * P + p] * Xp[j * P + p];"),
+    "grad_norm_jacobian_dropped": ("graw[m] += gout[m] * inv - dot * inv * inv * inv * v[m] / N;",
+                                   "graw[m] += gout[m] * inv;"),
+    "grad_gate_without_input": ("dy0[i * P + p] = d * v * sg;", "dy0[i * P + p] = d * sg;"),
+    "grad_decay_chain_dropped": ("double ddt = Ah * alpha * dalpha + (1.0 - lam) * ddelta + lam * dgamma;",
+                                 "double ddt = (1.0 - lam) * ddelta + lam * dgamma;"),
     "stale_previous": ("memcpy(bp, bc, (size_t)K * R * sizeof *bp);\n        memcpy(xp, xc, (size_t)P * R * sizeof *xp);\n",
                        ""),
 }

@@ -458,3 +458,77 @@ def test_prologue_and_gate_in_decode(oracle):
         y, h = oracle.decode(step, h)
         assert relerr(y, y_all[:, t]) < 1e-12
     assert relerr(h, h_all) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Gradient of the layer (OB): every input's gradient against central
+# differences of the forward form O1 (an independent implementation), for the
+# loss L = sum(dy * y) + sum(dh * h_out).
+GRAD_KEYS = (("x", "dx"), ("dt", "ddt"), ("lam", "dlam"), ("theta", "dtheta"), ("B", "dB"), ("C", "dC"),
+             ("A", "dA"), ("D", "dD"), ("h_in", "dh_in"), ("Bprev", "dBprev"), ("xprev", "dxprev"),
+             ("B_bias", "dB_bias"), ("C_bias", "dC_bias"), ("z", "dz"))
+
+
+def fd_check(oracle, inp, rng, with_dh=True, tol=2e-7):
+    dy = rng.standard_normal(inp["x"].shape)
+    S = len(inp["cu_seqlens"]) - 1 if inp.get("cu_seqlens") is not None else inp["x"].shape[0]
+    H, N, P = inp["x"].shape[2], inp["B"].shape[-1], inp["x"].shape[-1]
+    dh = rng.standard_normal((S, H, N, P)) if with_dh else None
+
+    def loss(d):
+        y, h = oracle.scan(d)
+        return float((y * dy).sum() + ((h * dh).sum() if with_dh else 0.0))
+
+    gr = oracle.scan_bwd(inp, dy, dh)
+    checked = 0
+    for k, gk in GRAD_KEYS:
+        if inp.get(k) is None:
+            continue
+        a = inp[k]
+        fd = np.zeros_like(a)
+        for idx in np.ndindex(a.shape):
+            e = 1e-6 * max(1.0, abs(a[idx]))
+            ap = a.copy()
+            ap[idx] += e
+            lp = loss(dict(inp, **{k: ap}))
+            ap[idx] -= 2 * e
+            lm = loss(dict(inp, **{k: ap}))
+            fd[idx] = (lp - lm) / (2 * e)
+        assert relerr(gr[gk], fd) < tol, (k, relerr(gr[gk], fd))
+        checked += 1
+    return checked
+
+
+def test_gradient_all_features(oracle):
+    """State, previous token, grouped B/C (G < H), rank 2, BC norm, biases and gate."""
+    rng = np.random.default_rng(81)
+    inp = rand_inputs(rng, b=2, L=5, H=2, G=1, P=3, N=4, R=2, state=True, prev=True)
+    inp.update(bc_norm=True, bc_eps=0.1, B_bias=rng.uniform(0, 1, (2, 4)), C_bias=rng.uniform(0, 1, (2, 4)),
+               z=rng.standard_normal(inp["x"].shape))
+    assert fd_check(oracle, inp, rng) == 14
+
+
+def test_gradient_plain_siso(oracle):
+    """Zero initial state, no previous token, rank 1, no prologue; only dL/dy."""
+    rng = np.random.default_rng(82)
+    inp = rand_inputs(rng, b=1, L=9, H=2, G=2, P=2, N=6, R=1)
+    assert fd_check(oracle, inp, rng, with_dh=False) == 8
+
+
+def test_gradient_packed(oracle):
+    """Packed sequences (one empty, one of a single token) with resume inputs per sequence."""
+    rng = np.random.default_rng(83)
+    inp = rand_inputs(rng, b=1, L=9, H=2, G=2, P=2, N=4, R=2)
+    inp["cu_seqlens"] = np.array([0, 4, 4, 5, 9], dtype=np.int32)
+    inp["h_in"] = rng.standard_normal((4, 2, 4, 2))
+    inp["Bprev"] = rng.standard_normal((4, 2, 2, 4))
+    inp["xprev"] = rng.standard_normal((4, 2, 2, 2))
+    assert fd_check(oracle, inp, rng) == 11
+
+
+def test_gradient_norm_eps_zero(oracle):
+    """The BC norm with eps = 0 and biases but no gate, grouped B/C."""
+    rng = np.random.default_rng(84)
+    inp = rand_inputs(rng, b=1, L=6, H=4, G=2, P=2, N=4, R=1, prev=True)
+    inp.update(bc_norm=True, bc_eps=0.0, B_bias=rng.uniform(0, 1, (4, 4)), C_bias=rng.uniform(0, 1, (4, 4)))
+    assert fd_check(oracle, inp, rng) == 12
