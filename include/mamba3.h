@@ -140,6 +140,50 @@ size_t mamba3_scan_workspace_size(const mamba3_scan_args *args);
 /* Enqueue the scan on `stream`. Writes y (every token) and h_out (if given). */
 mamba3_status mamba3_scan_fwd(const mamba3_scan_args *args, void *stream);
 
+/* Backward of the scan: the gradient of a loss L with respect to every input
+ * of mamba3_scan_fwd, given dL/dy and dL/dh_out: the chain rule taken
+ * backwards through the recurrence above, in the same chunked form. Training
+ * runs the layer chunk-parallel (sections "Parallel representation under SSD"
+ * and "MIMO Formulation") and needs this gradient.
+ *
+ * fwd       the forward call's arguments, unchanged (its y, h_out and
+ *           workspace fields are ignored). Every input the forward read is
+ *           read again; nothing of the forward pass needs to be kept.
+ * dy        dL/dy, layout and dtype of x (required when there are tokens).
+ * dh_out    [S, H, N, P] fp32 dL/dh_out, or NULL (zero).
+ * Outputs, overwritten, in the layout and dtype of the matching input:
+ *   dx, ddt, dlam, dtheta, dB, dC (required when there are tokens);
+ *   dA [H] fp32 (required); dD [H] fp32 or NULL;
+ *   dh_in [S, H, N, P] fp32 or NULL;
+ *   dBprev, dxprev: both or neither, and only with Bprev/xprev;
+ *   dB_bias, dC_bias [H, N] fp32, each only with its bias (or NULL);
+ *   dz: only with z (or NULL).
+ * No output may overlap any input or another output. Alignment as for the
+ * matching inputs. The fused prologue / epilogue settings of fwd apply.
+ *
+ * workspace: device memory of at least mamba3_scan_bwd_workspace_size(args)
+ * bytes, owned by the caller, 256-byte aligned. It holds the state entering
+ * every chunk (the backward walks the chunks in reverse) and per-(sequence,
+ * head) partial sums, so that every sum is formed in a fixed order: the
+ * results are bitwise reproducible. Its contents are scratch on return. */
+typedef struct {
+    mamba3_scan_args fwd;
+    const void *dy;
+    const float *dh_out;
+    void *dx, *ddt, *dlam, *dtheta, *dB, *dC;
+    float *dA, *dD;
+    float *dh_in;
+    void *dBprev, *dxprev;
+    float *dB_bias, *dC_bias;
+    void *dz;
+    void *workspace;
+    size_t workspace_bytes;
+} mamba3_scan_bwd_args;
+
+mamba3_status mamba3_scan_bwd_validate(const mamba3_scan_bwd_args *args);
+size_t mamba3_scan_bwd_workspace_size(const mamba3_scan_bwd_args *args);
+mamba3_status mamba3_scan_bwd(const mamba3_scan_bwd_args *args, void *stream);
+
 /* One decode step for a batch of independent sequences, state updated in
  * place: h <- alpha R (h + delta Bprev xprev^T) + gamma B x^T, y = h^T C + D x
  * (the same update as one token of the scan; section "MIMO Formulation" gives

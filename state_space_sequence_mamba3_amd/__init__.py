@@ -45,7 +45,18 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
-EXPORTS = ("mamba3_scan_validate", "mamba3_scan_workspace_size", "mamba3_scan_fwd", "mamba3_decode_validate",
+class ScanBwdArgs(ctypes.Structure):
+    """Mirror of ``mamba3_scan_bwd_args``."""
+    _fields_ = [
+        ("fwd", ScanArgs), ("dy", _vp), ("dh_out", _vp),
+        ("dx", _vp), ("ddt", _vp), ("dlam", _vp), ("dtheta", _vp), ("dB", _vp), ("dC", _vp),
+        ("dA", _vp), ("dD", _vp), ("dh_in", _vp), ("dBprev", _vp), ("dxprev", _vp),
+        ("dB_bias", _vp), ("dC_bias", _vp), ("dz", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+EXPORTS = ("mamba3_scan_validate", "mamba3_scan_workspace_size", "mamba3_scan_fwd", "mamba3_scan_bwd_validate",
+           "mamba3_scan_bwd_workspace_size", "mamba3_scan_bwd", "mamba3_decode_validate",
            "mamba3_decode_step", "mamba3_status_string", "mamba3_version")
 
 _lib = None
@@ -70,6 +81,12 @@ def lib():
         l.mamba3_scan_workspace_size.restype = ctypes.c_size_t
         l.mamba3_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _vp]
         l.mamba3_scan_fwd.restype = ctypes.c_int
+        l.mamba3_scan_bwd_validate.argtypes = [ctypes.POINTER(ScanBwdArgs)]
+        l.mamba3_scan_bwd_validate.restype = ctypes.c_int
+        l.mamba3_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanBwdArgs)]
+        l.mamba3_scan_bwd_workspace_size.restype = ctypes.c_size_t
+        l.mamba3_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdArgs), _vp]
+        l.mamba3_scan_bwd.restype = ctypes.c_int
         l.mamba3_decode_validate.argtypes = [ctypes.POINTER(DecodeArgs)]
         l.mamba3_decode_validate.restype = ctypes.c_int
         l.mamba3_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
@@ -148,6 +165,57 @@ def mamba3_scan_fwd(x, dt, lam, theta, B, C, A, D=None, *, y=None, h_in=None, h_
     if st != MAMBA3_OK:
         raise Mamba3Error(st, "mamba3_scan_fwd")
     return y, h_out
+
+
+def mamba3_scan_bwd_validate(args: ScanBwdArgs) -> int:
+    return lib().mamba3_scan_bwd_validate(ctypes.byref(args))
+
+
+def mamba3_scan_bwd_workspace_size(args: ScanBwdArgs) -> int:
+    return lib().mamba3_scan_bwd_workspace_size(ctypes.byref(args))
+
+
+def mamba3_scan_bwd(x, dt, lam, theta, B, C, A, D=None, *, dy, dh_out=None, h_in=None, Bprev=None, xprev=None,
+                    cu_seqlens=None, chunk=64, B_bias=None, C_bias=None, z=None, bc_norm=False, bc_eps=1e-5,
+                    want_dD=True, want_dh_in=True, workspace=None, stream=None):
+    """Gradients of the scan. Takes the forward's inputs plus dy (layout of
+    x) and dh_out ([S,H,N,P] fp32 or None); returns a dict of gradients shaped
+    like the inputs (dx, ddt, dlam, dtheta, dB, dC; dA, dD fp32 [H]; dh_in;
+    dBprev, dxprev, dB_bias, dC_bias, dz where the input exists). The
+    workspace is allocated unless given (a uint8 device tensor)."""
+    import torch
+    fwd = scan_args(x, dt, lam, theta, B, C, A, D, y=None, h_in=h_in, h_out=None, Bprev=Bprev, xprev=xprev,
+                    cu_seqlens=cu_seqlens, chunk=chunk, B_bias=B_bias, C_bias=C_bias, z=z, bc_norm=bc_norm,
+                    bc_eps=bc_eps)
+    S = int(cu_seqlens.numel()) - 1 if cu_seqlens is not None else x.shape[0]
+    H, N, P = x.shape[2], B.shape[4], x.shape[4]
+    f32 = dict(dtype=torch.float32, device=x.device)
+    g = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt), dlam=torch.empty_like(lam),
+             dtheta=torch.empty_like(theta), dB=torch.empty_like(B), dC=torch.empty_like(C),
+             dA=torch.empty((H,), **f32))
+    if want_dD:
+        g["dD"] = torch.empty((H,), **f32)
+    if want_dh_in:
+        g["dh_in"] = torch.empty((S, H, N, P), **f32)
+    if Bprev is not None:
+        g["dBprev"], g["dxprev"] = torch.empty_like(Bprev), torch.empty_like(xprev)
+    if B_bias is not None:
+        g["dB_bias"] = torch.empty_like(B_bias)
+    if C_bias is not None:
+        g["dC_bias"] = torch.empty_like(C_bias)
+    if z is not None:
+        g["dz"] = torch.empty_like(z)
+    a = ScanBwdArgs(fwd, _ptr(dy), _ptr(dh_out), *[_ptr(g.get(k)) for k in (
+        "dx", "ddt", "dlam", "dtheta", "dB", "dC", "dA", "dD", "dh_in", "dBprev", "dxprev", "dB_bias", "dC_bias",
+        "dz")], None, 0)
+    need = lib().mamba3_scan_bwd_workspace_size(ctypes.byref(a))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    st = lib().mamba3_scan_bwd(ctypes.byref(a), _stream(stream))
+    if st != MAMBA3_OK:
+        raise Mamba3Error(st, "mamba3_scan_bwd")
+    return g
 
 
 def decode_args(x, dt, lam, theta, B, C, A, D=None, *, h, y, Bprev=None, xprev=None, B_bias=None, C_bias=None,

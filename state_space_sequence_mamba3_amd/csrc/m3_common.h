@@ -39,6 +39,9 @@ mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st);
 bool scan_bf16_supported(int N, int P, int R, int Q);
 size_t scan_f32_lds_bytes(int N, int P, int R, int Q);
 mamba3_status launch_decode(const mamba3_decode_args *a, hipStream_t st);
+mamba3_status launch_scan_bwd(const mamba3_scan_bwd_args *b, hipStream_t st);
+size_t scan_bwd_workspace_bytes(const mamba3_scan_bwd_args *b);
+int scan_bwd_chunk(int N, int P, int R);
 bool decode_supported(int N, int P, int R, int dtype);
 
 }  // namespace m3

@@ -52,9 +52,10 @@ const char *mamba3_status_string(mamba3_status s) {
     return "unknown status";
 }
 
-int32_t mamba3_version(void) { return 10100; }
+int32_t mamba3_version(void) { return 10200; }
 
-mamba3_status mamba3_scan_validate(const mamba3_scan_args *a) {
+// Every check of the scan arguments except the availability of a forward kernel.
+static mamba3_status scan_args_check(const mamba3_scan_args *a) {
     if (!a) return MAMBA3_EINVAL;
     if (a->dtype != MAMBA3_F32 && a->dtype != MAMBA3_BF16) return MAMBA3_EINVAL;
     if (a->batch < 0 || a->seqlen < 0 || a->nheads < 1 || a->headdim < 1 || a->dstate < 2 ||
@@ -96,6 +97,12 @@ mamba3_status mamba3_scan_validate(const mamba3_scan_args *a) {
     for (Range r : ins2)
         if (overlaps(ho, r)) return MAMBA3_EINVAL;
     if (a->h_in && a->h_out && a->h_in != a->h_out && overlaps(ins[6], ho)) return MAMBA3_EINVAL;
+    return MAMBA3_OK;
+}
+
+mamba3_status mamba3_scan_validate(const mamba3_scan_args *a) {
+    const mamba3_status st = scan_args_check(a);
+    if (st != MAMBA3_OK) return st;
     // kernel availability
     if (a->dtype == MAMBA3_F32) {
         if (m3::scan_f32_lds_bytes(a->dstate, a->headdim, a->rank, a->chunk) > kMaxLds) return MAMBA3_EUNSUPPORTED;
@@ -118,6 +125,76 @@ mamba3_status mamba3_scan_fwd(const mamba3_scan_args *a, void *stream) {
     if ((int64_t)a->batch * a->seqlen == 0 && !a->h_out) return MAMBA3_OK;
     hipStream_t hs = (hipStream_t)stream;
     return a->dtype == MAMBA3_F32 ? m3::launch_scan_f32(a, hs) : m3::launch_scan_bf16(a, hs);
+}
+
+mamba3_status mamba3_scan_bwd_validate(const mamba3_scan_bwd_args *b) {
+    if (!b) return MAMBA3_EINVAL;
+    // the forward arguments, with dy in the place of y (same layout, must not overlap an input)
+    mamba3_scan_args f = b->fwd;
+    f.y = (void *)b->dy;
+    f.h_out = nullptr;
+    f.workspace = nullptr;
+    f.workspace_bytes = 0;
+    mamba3_status st = scan_args_check(&f);
+    if (st != MAMBA3_OK) return st;
+    const mamba3_scan_args *a = &b->fwd;
+    const int64_t S = a->cu_seqlens ? a->nseq : a->batch, T = (int64_t)a->batch * a->seqlen;
+    const int64_t H = a->nheads, G = a->ngroups, P = a->headdim, N = a->dstate, R = a->rank;
+    if (T > 0 && (!b->dx || !b->ddt || !b->dlam || !b->dtheta || !b->dB || !b->dC)) return MAMBA3_EINVAL;
+    if (!b->dA) return MAMBA3_EINVAL;
+    if ((b->dBprev == nullptr) != (b->dxprev == nullptr)) return MAMBA3_EINVAL;
+    if (b->dBprev && !a->Bprev) return MAMBA3_EINVAL;
+    if ((b->dB_bias && !a->B_bias) || (b->dC_bias && !a->C_bias) || (b->dz && !a->z)) return MAMBA3_EINVAL;
+    const void *al16[] = {b->dx, b->dtheta, b->dB, b->dC, b->dBprev, b->dxprev, b->dz, b->dh_in, b->dh_out,
+                          b->dB_bias, b->dC_bias};
+    for (const void *q : al16)
+        if (q && !aligned16(q)) return MAMBA3_EALIGN;
+    if ((b->ddt && !aligned_elem(b->ddt, a->dtype)) || (b->dlam && !aligned_elem(b->dlam, a->dtype)) ||
+        !aligned4(b->dA) || (b->dD && !aligned4(b->dD)))
+        return MAMBA3_EALIGN;
+    const int64_t es = a->dtype == MAMBA3_BF16 ? 2 : 4;
+    // every output against every input and every other output
+    Range outs[] = {span(b->dx, T * H * P * R, es), span(b->ddt, T * H, es), span(b->dlam, T * H, es),
+                    span(b->dtheta, T * H * (N / 2), es), span(b->dB, T * G * N * R, es),
+                    span(b->dC, T * G * N * R, es), span(b->dA, H, 4), span(b->dD, H, 4),
+                    span(b->dh_in, S * H * N * P, 4), span(b->dBprev, S * G * N * R, es),
+                    span(b->dxprev, S * H * P * R, es), span(b->dB_bias, H * N, 4), span(b->dC_bias, H * N, 4),
+                    span(b->dz, T * H * P * R, es)};
+    Range ins[] = {span(a->x, T * H * P * R, es), span(a->dt, T * H, es), span(a->lam, T * H, es),
+                   span(a->theta, T * H * (N / 2), es), span(a->B, T * G * N * R, es),
+                   span(a->C, T * G * N * R, es), span(a->h_in, S * H * N * P, 4),
+                   span(a->Bprev, S * G * N * R, es), span(a->xprev, S * H * P * R, es), span(a->A, H, 4),
+                   span(a->D, H, 4), span(a->B_bias, H * N, 4), span(a->C_bias, H * N, 4),
+                   span(a->z, T * H * P * R, es), span(a->cu_seqlens, a->cu_seqlens ? a->nseq + 1 : 0, 4),
+                   span(b->dy, T * H * P * R, es), span(b->dh_out, S * H * N * P, 4)};
+    const int nout = sizeof outs / sizeof outs[0];
+    for (int i = 0; i < nout; i++) {
+        for (Range r : ins)
+            if (overlaps(outs[i], r)) return MAMBA3_EINVAL;
+        for (int j = i + 1; j < nout; j++)
+            if (overlaps(outs[i], outs[j])) return MAMBA3_EINVAL;
+    }
+    if (!m3::scan_bwd_chunk(a->dstate, a->headdim, a->rank)) return MAMBA3_EUNSUPPORTED;
+    const size_t need = m3::scan_bwd_workspace_bytes(b);
+    if (b->workspace_bytes < need || (need > 0 && !b->workspace)) return MAMBA3_EWORKSPACE;
+    if (b->workspace && ((uintptr_t)b->workspace & 255u)) return MAMBA3_EALIGN;
+    const Range wsr = span(b->workspace, (int64_t)b->workspace_bytes, 1);
+    for (Range r : ins)
+        if (overlaps(wsr, r)) return MAMBA3_EINVAL;
+    for (Range r : outs)
+        if (overlaps(wsr, r)) return MAMBA3_EINVAL;
+    return MAMBA3_OK;
+}
+
+size_t mamba3_scan_bwd_workspace_size(const mamba3_scan_bwd_args *b) {
+    if (!b || !m3::scan_bwd_chunk(b->fwd.dstate, b->fwd.headdim, b->fwd.rank)) return 0;
+    return m3::scan_bwd_workspace_bytes(b);
+}
+
+mamba3_status mamba3_scan_bwd(const mamba3_scan_bwd_args *b, void *stream) {
+    const mamba3_status st = mamba3_scan_bwd_validate(b);
+    if (st != MAMBA3_OK) return st;
+    return m3::launch_scan_bwd(b, (hipStream_t)stream);
 }
 
 mamba3_status mamba3_decode_validate(const mamba3_decode_args *a) {

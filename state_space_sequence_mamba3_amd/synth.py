@@ -157,6 +157,18 @@ def block_inputs(inp: dict, seed: int, norm: bool = True, B_bias: bool = True, C
     return out
 
 
+def grad_inputs(inp: dict, seed: int, dh_out: bool = True) -> dict:
+    """Output gradients for a backward test: dy ~ N(0, 1) shaped like x (token
+    dtype) and, if asked, dh_out ~ N(0, 1) [S, H, N, P] fp32."""
+    m = inp["meta"]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    S = len(inp["cu_seqlens"]) - 1 if inp.get("cu_seqlens") is not None else m["batch"]
+    out = dict(dy=_tok(_normal(rng, inp["x"].shape), m["dtype"]))
+    if dh_out:
+        out["dh_out"] = _normal(rng, (S, m["nheads"], m["dstate"], m["headdim"])).astype(np.float32)
+    return out
+
+
 def decode_inputs(cfg: int | dict = 3, seed: int | None = None, ring: int = 1, **over) -> dict:
     """Decode workload: ``ring`` token-input sets (each like one token of a
     scan, leading axis ring), a previous token, and an fp32 state ~ N(0,1).

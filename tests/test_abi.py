@@ -37,7 +37,7 @@ def test_status_strings(lib):
     assert m3.status_string(m3.MAMBA3_OK) == "ok"
     for s in range(6):
         assert m3.status_string(s)
-    assert lib.mamba3_version() == 10100
+    assert lib.mamba3_version() == 10200
 
 
 BASE = 0x7F0000000000
@@ -122,6 +122,64 @@ def test_decode_validate_prologue(lib):
     assert m3.mamba3_decode_validate(good_decode(z=fake(16) + 2)) == m3.MAMBA3_EALIGN
     assert m3.mamba3_decode_validate(good_decode(z=fake(12))) == m3.MAMBA3_EINVAL       # y aliases z
     assert m3.mamba3_decode_validate(good_decode(B_bias=fake(11))) == m3.MAMBA3_EINVAL  # h aliases a bias
+
+
+def good_bwd(**over):
+    fwd = good_scan(y=None, h_out=None, h_in=fake(11), Bprev=fake(12), xprev=fake(13))
+    b = m3.ScanBwdArgs(fwd=fwd, dy=fake(20), dh_out=fake(21), dx=fake(22), ddt=fake(23), dlam=fake(24),
+                       dtheta=fake(25), dB=fake(26), dC=fake(27), dA=fake(28), dD=fake(29), dh_in=fake(30),
+                       dBprev=fake(31), dxprev=fake(32), dB_bias=None, dC_bias=None, dz=None,
+                       workspace=fake(40), workspace_bytes=1 << 40)
+    for k, v in over.items():
+        setattr(b, k, v)
+    return b
+
+
+def test_scan_bwd_validate(lib):
+    b = good_bwd()
+    need = m3.mamba3_scan_bwd_workspace_size(b)
+    assert 0 < need < 1 << 40
+    assert m3.mamba3_scan_bwd_validate(b) == m3.MAMBA3_OK
+    b.workspace_bytes = need
+    assert m3.mamba3_scan_bwd_validate(b) == m3.MAMBA3_OK
+    b.workspace_bytes = need - 1
+    assert m3.mamba3_scan_bwd_validate(b) == m3.MAMBA3_EWORKSPACE
+    assert m3.mamba3_scan_bwd_validate(good_bwd(workspace=None)) == m3.MAMBA3_EWORKSPACE
+    assert m3.mamba3_scan_bwd_validate(good_bwd(workspace=fake(40) + 128)) == m3.MAMBA3_EALIGN
+    # optional outputs may be left out
+    assert m3.mamba3_scan_bwd_validate(good_bwd(dD=None, dh_in=None, dh_out=None, dBprev=None, dxprev=None)) == m3.MAMBA3_OK
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dy", None, m3.MAMBA3_EINVAL),
+    ("dA", None, m3.MAMBA3_EINVAL),
+    ("dx", None, m3.MAMBA3_EINVAL),
+    ("dBprev", None, m3.MAMBA3_EINVAL),                     # dxprev without dBprev
+    ("dz", BASE + 0x3300000000, m3.MAMBA3_EINVAL),          # no gate in the forward
+    ("dB_bias", BASE + 0x3400000000, m3.MAMBA3_EINVAL),     # no bias in the forward
+    ("dx", BASE + 0x100000000, m3.MAMBA3_EINVAL),           # dx aliases x
+    ("dB", BASE + 0x1900000000, m3.MAMBA3_EINVAL),          # dB aliases dtheta
+    ("dA", BASE + 0x1500000000, m3.MAMBA3_EINVAL),          # dA aliases dh_out
+    ("dx", BASE + 0x1600000008, m3.MAMBA3_EALIGN),
+    ("dA", BASE + 0x1C00000002, m3.MAMBA3_EALIGN),
+    ("workspace", BASE + 0x700000000, m3.MAMBA3_EINVAL),    # workspace overlaps A
+])
+def test_scan_bwd_validate_errors(lib, field, value, status):
+    assert m3.mamba3_scan_bwd_validate(good_bwd(**{field: value})) == status
+
+
+def test_scan_bwd_validate_shapes(lib):
+    b = good_bwd()
+    b.fwd.dstate, b.fwd.headdim = 1024, 512       # the state and its gradient do not fit in LDS
+    assert m3.mamba3_scan_bwd_validate(b) == m3.MAMBA3_EUNSUPPORTED
+    assert m3.mamba3_scan_bwd_workspace_size(b) == 0
+    b = good_bwd()
+    b.fwd.dtype = m3.MAMBA3_BF16                  # bf16 shapes without a forward kernel are fine here
+    b.fwd.dstate, b.fwd.headdim = 24, 40
+    assert m3.mamba3_scan_bwd_validate(b) == m3.MAMBA3_OK
+    b.fwd.dstate = 23
+    assert m3.mamba3_scan_bwd_validate(b) == m3.MAMBA3_EINVAL
+    assert lib.mamba3_scan_bwd_validate(None) == m3.MAMBA3_EINVAL
 
 
 def test_scan_validate_packed(lib):
