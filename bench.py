@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Mamba-3 SSM prefill tokens/s + decode step \u00b5s at 1 GPU; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+VALU_F32_PEAK_TFS = 157.3      # MI355X fp32 vector, published
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, published
 
 
@@ -54,6 +55,41 @@ def scan_flops(c):
     update): R^2 (N + P)(Q + 1) + 4 R N P."""
     L, H, P, N, R, Q = c["seqlen"], c["nheads"], c["headdim"], c["dstate"], c["rank"], c["chunk"]
     return c["batch"] * L * H * (R * R * (N + P) * (Q + 1) + 4 * R * N * P)
+
+
+def bwd_chunk(c):
+    """Chunk length the backward kernel picks (largest power of two <= 64 whose
+    LDS layout fits 160 KB; mirrors the library's choice)."""
+    N, P, R = c["dstate"], c["headdim"], c["rank"]
+    for q in (64, 32, 16, 8, 4, 2, 1):
+        QR, K = q * R, N // 2
+        wk = max(max(QR, K) * (P + 1), 512)
+        o = 3 * q * K + 11 * q + q * q + 7 * QR
+        o = (o + 3) & ~3
+        o += 4 * QR * (N + 1) + 2 * QR * (P + 1) + 2 * N * (P + 1) + 2 * QR * (QR + 1) + 2 * wk
+        o += 4 * R * N + 3 * R * P + R + 2 * N + 16
+        if o * 4 <= 160 * 1024:
+            return q
+    return 0
+
+
+def bwd_bytes(c):
+    """Algorithmic HBM bytes of the backward: the forward's token inputs and dy
+    read once, their gradients written once (bf16), A read and dA, dD written."""
+    b, L, H, P, N, R = c["batch"], c["seqlen"], c["nheads"], c["headdim"], c["dstate"], c["rank"]
+    G = c.get("ngroups", H)
+    T = b * L
+    es = 2
+    return T * (H * P * R * es * 3 + H * es * 4 + H * (N // 2) * es * 2 + 4 * G * N * R * es) + 3 * H * 4
+
+
+def bwd_flops(c, q):
+    """Flops of the chunked backward at chunk q per token-head: the six causal
+    chunk contractions (scores, intra outputs, dP, dX, dC, dB: R^2 q/2 (3N + 3P)
+    multiply-adds) and seven N x P x R ones (state update, inter output, dX and
+    dB state terms, dC inter term, the rotated state, dH)."""
+    L, H, P, N, R = c["seqlen"], c["nheads"], c["headdim"], c["dstate"], c["rank"]
+    return 2 * c["batch"] * L * H * (R * R * q / 2 * (3 * N + 3 * P) + 7 * R * N * P)
 
 
 def decode_bytes(c, block=False):
@@ -112,6 +148,42 @@ def bench_scan(cfg, steps, warmup, dev, block=False, **over):
     out = dict(workload=name, ms=ms, tokens_per_s=tokens / (ms * 1e-3), bytes=nbytes, flops=flops,
                hbm_gbs=nbytes / (ms * 1e-3) / 1e9, mfma_tfs=flops / (ms * 1e-3) / 1e12, wall_s=wall)
     del d, y, h
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_bwd(cfg, steps, warmup, dev):
+    import torch
+    import state_space_sequence_mamba3_amd as m3
+    from state_space_sequence_mamba3_amd import synth
+    c = dict(synth.CONFIGS[cfg])
+    d = synth.torch_scan_inputs(cfg, dev, seed=cfg)
+    g = torch.Generator(device=dev)
+    g.manual_seed(100 + cfg)
+    dy = torch.randn(d["x"].shape, generator=g, device=dev, dtype=torch.float32).to(d["x"].dtype)
+    ws = None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        nonlocal ws
+        out = m3.mamba3_scan_bwd(d["x"], d["dt"], d["lam"], d["theta"], d["B"], d["C"], d["A"], d["D"], dy=dy,
+                                 cu_seqlens=d.get("cu_seqlens"), workspace=ws, stream=stream)
+        return out
+
+    # the workspace is allocated once (chunk states and partial sums), outside the timed region
+    import ctypes
+    fwd = m3.scan_args(d["x"], d["dt"], d["lam"], d["theta"], d["B"], d["C"], d["A"], d["D"], y=None)
+    a = m3.ScanBwdArgs(fwd=fwd)   # the size depends on the forward's shapes only
+    need = m3.lib().mamba3_scan_bwd_workspace_size(ctypes.byref(a))
+    ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ms, wall = timed(step, steps, warmup, stream)
+    q = bwd_chunk(c)
+    nbytes, flops = bwd_bytes(c), bwd_flops(c, q)
+    tokens = c["batch"] * c["seqlen"]
+    out = dict(workload=c["name"] + " backward", ms=ms, tokens_per_s=tokens / (ms * 1e-3), bytes=nbytes, flops=flops,
+               chunk=q, workspace_bytes=need, hbm_gbs=nbytes / (ms * 1e-3) / 1e9,
+               alu_tfs=flops / (ms * 1e-3) / 1e12, wall_s=wall)
+    del d, dy, ws
     torch.cuda.empty_cache()
     return out
 
@@ -360,7 +432,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["scan", "decode", "all"], default="all")
+    ap.add_argument("--only", choices=["scan", "decode", "bwd", "all"], default="all")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -402,6 +474,12 @@ def main():
         print(f"# siso scan + block {res['siso_block']['ms']:.3f} ms", file=sys.stderr, flush=True)
         res["mimo_block"] = bench_scan(2, args.steps, args.warmup, dev, block=True)
         print(f"# mimo scan + block {res['mimo_block']['ms']:.3f} ms", file=sys.stderr, flush=True)
+    if args.only in ("bwd", "all"):
+        # the backward (fp32 VALU kernel): a few steps, each is a whole backward of the batch
+        res["siso_bwd"] = bench_bwd(1, 3, 1, dev)
+        print(f"# siso backward {res['siso_bwd']['ms']:.2f} ms", file=sys.stderr, flush=True)
+        res["mimo_bwd"] = bench_bwd(2, 3, 1, dev)
+        print(f"# mimo backward {res['mimo_bwd']['ms']:.2f} ms", file=sys.stderr, flush=True)
     if args.only in ("decode", "all"):
         res["decode"] = bench_decode(1000, 1, dev)
         print(f"# decode {res['decode']['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
@@ -448,6 +526,18 @@ def main():
             if k == "siso_block":
                 roof["traffic"] = traffic_record("scan_bf16_block")
             sec[k] = {"workload": r["workload"], "ms": r["ms"], "tokens_per_s": r["tokens_per_s"], "roofline": roof}
+    for k in ("siso_bwd", "mimo_bwd"):
+        if k in res:
+            r = res[k]
+            # binding roofline: fp32 vector arithmetic (the kernel computes on VALU) or HBM bytes
+            alu_bound = r["flops"] / (VALU_F32_PEAK_TFS * 1e12) > r["bytes"] / (HBM_PEAK_GBS * 1e9)
+            roof = ({"bound": "alu", "achieved": r["alu_tfs"], "peak": VALU_F32_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": r["alu_tfs"] / VALU_F32_PEAK_TFS, "hbm_gbs": r["hbm_gbs"]} if alu_bound else
+                    {"bound": "hbm", "achieved": r["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["hbm_gbs"] / HBM_PEAK_GBS, "alu_tflops": r["alu_tfs"]})
+            roof.update(bytes_per_launch=r["bytes"], flops_per_launch=r["flops"], chunk=r["chunk"])
+            sec[k] = {"workload": r["workload"], "ms": r["ms"], "tokens_per_s": r["tokens_per_s"],
+                      "workspace_bytes": r["workspace_bytes"], "roofline": roof}
     for k in ("decode", "decode_block"):
         if k in res:
             r = res[k]

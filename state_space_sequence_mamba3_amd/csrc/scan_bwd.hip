@@ -27,6 +27,7 @@
 // of dA, dD and the bias gradients, and (with G < H) per-head dB, dC, dBprev,
 // go to the workspace and a second kernel adds them up.
 #include <algorithm>
+#include <type_traits>
 
 #include "m3_common.h"
 
@@ -49,9 +50,11 @@ struct BwdParams {
     float eps;
 };
 
+constexpr int kBwdThreads = 512;
+
 // LDS layout of the backward (offsets in floats)
 struct BwdLayout {
-    int cs, sn, dphi, dts, lms, gms, dls, S, g1, dS, dgm, ddl, scal_end;
+    int cs, sn, dphi, dts, lms, gms, dls, S, g1, dS, dgm, ddl, es, cu, em, scal_end;
     int invB, invC, rowA, rowB, colS, colG, colD, rows_end;
     int Bt, Ct, dBt, dCt, Xs, dY, Hs, dH, Sc, dPm, Wk, Wk2;
     int Bp, BpRaw, Xp, dBc_in, dXc_in, dBc_out, dXc_out, invBp, bba, cba, misc, total;
@@ -60,7 +63,8 @@ struct BwdLayout {
 __host__ __device__ inline BwdLayout bwd_layout(int N, int P, int R, int Q) {
     BwdLayout L;
     const int K = N / 2, QR = Q * R;
-    const int WK0 = (QR > K ? QR : K) * P, WK = WK0 > 256 ? WK0 : 256;   // >= one float per thread
+    const int NS = N + 1, PS = P + 1, QS = QR + 1;   // padded row strides
+    const int WK0 = (QR > K ? QR : K) * PS, WK = WK0 > kBwdThreads ? WK0 : kBwdThreads;   // >= one float per thread
     int o = 0;
     L.cs = o; o += Q * K;
     L.sn = o; o += Q * K;
@@ -74,6 +78,9 @@ __host__ __device__ inline BwdLayout bwd_layout(int N, int P, int R, int Q) {
     L.dS = o; o += Q;
     L.dgm = o; o += Q;
     L.ddl = o; o += Q;
+    L.es = o; o += Q;
+    L.cu = o; o += Q;
+    L.em = o; o += Q * Q;
     L.scal_end = o;
     L.invB = o; o += QR;
     L.invC = o; o += QR;
@@ -84,16 +91,16 @@ __host__ __device__ inline BwdLayout bwd_layout(int N, int P, int R, int Q) {
     L.colD = o; o += QR;
     L.rows_end = o;
     o = (o + 3) & ~3;
-    L.Bt = o; o += QR * N;
-    L.Ct = o; o += QR * N;
-    L.dBt = o; o += QR * N;
-    L.dCt = o; o += QR * N;
-    L.Xs = o; o += QR * P;
-    L.dY = o; o += QR * P;
-    L.Hs = o; o += N * P;
-    L.dH = o; o += N * P;
-    L.Sc = o; o += QR * QR;
-    L.dPm = o; o += QR * QR;
+    L.Bt = o; o += QR * NS;
+    L.Ct = o; o += QR * NS;
+    L.dBt = o; o += QR * NS;
+    L.dCt = o; o += QR * NS;
+    L.Xs = o; o += QR * PS;
+    L.dY = o; o += QR * PS;
+    L.Hs = o; o += N * PS;
+    L.dH = o; o += N * PS;
+    L.Sc = o; o += QR * QS;
+    L.dPm = o; o += QR * QS;
     L.Wk = o; o += WK;
     L.Wk2 = o; o += WK;
     L.Bp = o; o += R * N;
@@ -122,16 +129,33 @@ __device__ __forceinline__ void stt(void *p, int64_t i, float v) {
     ((T *)p)[i] = from_f<T>(v);
 }
 
+// Sum of one value per thread over the workgroup in a fixed order (wave butterflies, then the
+// wave sums in order); every thread gets the total. red: one float of LDS per wave. Must be
+// reached by every thread.
+__device__ float block_sum(float v, float *red) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+    __syncthreads();   // red is free
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int w = 0; w < (int)(blockDim.x >> 6); w++) t += red[w];
+    return t;
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads) void k_scan_bwd(BwdParams p) {
     extern __shared__ float sm[];
     const int H = p.H, G = p.G, P = p.P, N = p.N, R = p.R, Q = p.Q, K = N / 2, QR = Q * R;
+    // LDS row strides padded by one element: column walks across lanes hit distinct banks
+    const int NS = N + 1, PS = P + 1, QS = QR + 1;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int s = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
     const BwdLayout L = bwd_layout(N, P, R, Q);
     float *CS = sm + L.cs, *SN = sm + L.sn, *DPHI = sm + L.dphi;
     float *DT = sm + L.dts, *LM = sm + L.lms, *GM = sm + L.gms, *DL = sm + L.dls, *S = sm + L.S, *G1 = sm + L.g1;
     float *DS = sm + L.dS, *DGM = sm + L.dgm, *DDL = sm + L.ddl;
+    float *ES = sm + L.es, *CU = sm + L.cu, *EM = sm + L.em;   // e^{S_t}, c_t, e^{S_t - S_u}
     float *INVB = sm + L.invB, *INVC = sm + L.invC, *ROWA = sm + L.rowA, *ROWB = sm + L.rowB;
     float *COLS = sm + L.colS, *COLG = sm + L.colG, *COLD = sm + L.colD;
     float *Bt = sm + L.Bt, *Ct = sm + L.Ct, *dBt = sm + L.dBt, *dCt = sm + L.dCt;
@@ -176,9 +200,9 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
 
     // Prologue of `nrows` LDS rows (one thread per row): scale to unit RMS (inv kept in invs) and
     // add the bias row. Rows hold the raw values on entry.
-    auto prologue_rows = [&](float *rows, int nrows, const float *bias, float *invs) {
+    auto prologue_rows = [&](float *rows, int nrows, int stride, const float *bias, float *invs) {
         for (int r = tid; r < nrows; r += nt) {
-            float *v = rows + (int64_t)r * N;
+            float *v = rows + (int64_t)r * stride;
             float inv = 1.f;
             if (p.norm) {
                 float ss = 0.f;
@@ -223,6 +247,15 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
             }
         }
         __syncthreads();
+        for (int e = tid; e < Q * Q; e += nt) {
+            const int t = e / Q, u = e % Q;
+            EM[e] = (u <= t) ? expf(S[t] - S[u]) : 0.f;
+        }
+        for (int t = tid; t < Q; t += nt) {
+            ES[t] = expf(S[t]);
+            CU[t] = (t < nq) ? expf(S[nq - 1] - S[t]) * G1[t] : 0.f;
+        }
+        __syncthreads();
     };
     // the previous token of the chunk at c0 (its B after the prologue, raw B, x): token c0 - 1 of
     // the sequence, or Bprev / xprev at the start; MISC[0] = 1 if it exists
@@ -243,7 +276,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
         }
         if (tid == 0) MISC[0] = ex ? 1.f : 0.f;
         __syncthreads();
-        if (ex) prologue_rows(Bp, R, Bbh, INVBP);
+        if (ex) prologue_rows(Bp, R, N, Bbh, INVBP);
         __syncthreads();
     };
     // B~ (and C~ when withC) and X of the chunk: raw rows, prologue, rotation by -Phi
@@ -256,34 +289,34 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
                 bv = ldt<T>(p.B, o);
                 if (withC) cv = ldt<T>(p.C, o);
             }
-            Bt[e] = bv;
-            if (withC) Ct[e] = cv;
+            Bt[r * NS + n] = bv;
+            if (withC) Ct[r * NS + n] = cv;
         }
         for (int e = tid; e < QR * P; e += nt) {
             const int r = e / P, pp = e % P, t = r / R, j = r % R;
-            Xs[e] = (t < nq) ? ldt<T>(p.x, tokX(c0 + t) + j * P + pp) : 0.f;
+            Xs[r * PS + pp] = (t < nq) ? ldt<T>(p.x, tokX(c0 + t) + j * P + pp) : 0.f;
         }
         __syncthreads();
-        prologue_rows(Bt, nq * R, Bbh, INVB);
-        if (withC) prologue_rows(Ct, nq * R, Cbh, INVC);
+        prologue_rows(Bt, nq * R, NS, Bbh, INVB);
+        if (withC) prologue_rows(Ct, nq * R, NS, Cbh, INVC);
         __syncthreads();
         for (int e = tid; e < nq * K * R; e += nt) {
             const int t = e / (K * R), k = (e / R) % K, j = e % R, r = t * R + j;
             const float cs = CS[t * K + k], sn = SN[t * K + k];
-            const float b0 = Bt[r * N + 2 * k], b1 = Bt[r * N + 2 * k + 1];
-            Bt[r * N + 2 * k] = cs * b0 + sn * b1;
-            Bt[r * N + 2 * k + 1] = -sn * b0 + cs * b1;
+            const float b0 = Bt[r * NS + 2 * k], b1 = Bt[r * NS + 2 * k + 1];
+            Bt[r * NS + 2 * k] = cs * b0 + sn * b1;
+            Bt[r * NS + 2 * k + 1] = -sn * b0 + cs * b1;
             if (withC) {
-                const float q0 = Ct[r * N + 2 * k], q1 = Ct[r * N + 2 * k + 1];
-                Ct[r * N + 2 * k] = cs * q0 + sn * q1;
-                Ct[r * N + 2 * k + 1] = -sn * q0 + cs * q1;
+                const float q0 = Ct[r * NS + 2 * k], q1 = Ct[r * NS + 2 * k + 1];
+                Ct[r * NS + 2 * k] = cs * q0 + sn * q1;
+                Ct[r * NS + 2 * k + 1] = -sn * q0 + cs * q1;
             }
         }
         __syncthreads();
     };
 
     // ------------------------------------------------------------ forward: chunk states
-    for (int e = tid; e < N * P; e += nt) Hs[e] = p.h_in ? p.h_in[sh * N * P + e] : 0.f;
+    for (int e = tid; e < N * P; e += nt) Hs[(e / P) * PS + e % P] = p.h_in ? p.h_in[sh * N * P + e] : 0.f;
     __syncthreads();
     for (int64_t c = 0; c < nch; c++) {
         const int64_t c0 = c * Q;
@@ -296,30 +329,30 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
             const int n = e / P, pp = e % P;
             float acc = 0.f;
             for (int j = 0; j < R; j++) acc += Bp[j * N + n] * Xp[j * P + pp];
-            const float v = Hs[e] + d0 * acc;
-            Hs[e] = v;
+            const float v = Hs[n * PS + pp] + d0 * acc;
+            Hs[n * PS + pp] = v;
             ws[e] = v;
         }
         load_chunk(c0, nq, false);   // its first barrier also orders the state writes above
-        const float eSe = expf(S[nq - 1]);
+        const float eSe = ES[nq - 1];
         for (int e = tid; e < K * P; e += nt) {
             const int k = e / P, pp = e % P;
-            float u0 = eSe * Hs[(2 * k) * P + pp], u1 = eSe * Hs[(2 * k + 1) * P + pp];
+            float u0 = eSe * Hs[(2 * k) * PS + pp], u1 = eSe * Hs[(2 * k + 1) * PS + pp];
             for (int q = 0; q < nq * R; q++) {
                 const int t = q / R;
-                const float w = expf(S[nq - 1] - S[t]) * G1[t] * Xs[q * P + pp];
-                u0 += w * Bt[q * N + 2 * k];
-                u1 += w * Bt[q * N + 2 * k + 1];
+                const float w = CU[t] * Xs[q * PS + pp];
+                u0 += w * Bt[q * NS + 2 * k];
+                u1 += w * Bt[q * NS + 2 * k + 1];
             }
             const float cs = CS[(nq - 1) * K + k], sn = SN[(nq - 1) * K + k];
-            Hs[(2 * k) * P + pp] = cs * u0 - sn * u1;
-            Hs[(2 * k + 1) * P + pp] = sn * u0 + cs * u1;
+            Hs[(2 * k) * PS + pp] = cs * u0 - sn * u1;
+            Hs[(2 * k + 1) * PS + pp] = sn * u0 + cs * u1;
         }
         __syncthreads();
     }
 
     // ------------------------------------------------------------ reverse
-    for (int e = tid; e < N * P; e += nt) dH[e] = p.dh_out ? p.dh_out[sh * N * P + e] : 0.f;
+    for (int e = tid; e < N * P; e += nt) dH[(e / P) * PS + e % P] = p.dh_out ? p.dh_out[sh * N * P + e] : 0.f;
     for (int e = tid; e < R * N; e += nt) dBcIn[e] = 0.f;
     for (int e = tid; e < R * P; e += nt) dXcIn[e] = 0.f;
     for (int e = tid; e < N; e += nt) BBA[e] = CBA[e] = 0.f;
@@ -334,29 +367,29 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
         load_prev(c0);
         load_chunk(c0, nq, true);
         const float *ws = wsS(c);
-        for (int e = tid; e < N * P; e += nt) Hs[e] = ws[e];
+        for (int e = tid; e < N * P; e += nt) Hs[(e / P) * PS + e % P] = ws[e];
         for (int e = tid; e < QR * P; e += nt) {
             const int r = e / P, pp = e % P, t = r / R, j = r % R;
-            dY[e] = (t < nq) ? ldt<T>(p.dy, tokX(c0 + t) + j * P + pp) : 0.f;
+            dY[r * PS + pp] = (t < nq) ? ldt<T>(p.dy, tokX(c0 + t) + j * P + pp) : 0.f;
         }
-        for (int e = tid; e < QR * N; e += nt) dBt[e] = dCt[e] = 0.f;
+        for (int e = tid; e < QR * NS; e += nt) dBt[e] = dCt[e] = 0.f;
         for (int e = tid; e < Q * K; e += nt) DPHI[e] = 0.f;
         for (int t = tid; t < Q; t += nt) DS[t] = DGM[t] = DDL[t] = 0.f;
         // G^ = R(-Phi_e) dH_n, in place
         for (int e = tid; e < K * P; e += nt) {
             const int k = e / P, pp = e % P;
             const float cs = CS[e_ * K + k], sn = SN[e_ * K + k];
-            const float g0 = dH[(2 * k) * P + pp], g1 = dH[(2 * k + 1) * P + pp];
-            dH[(2 * k) * P + pp] = cs * g0 + sn * g1;
-            dH[(2 * k + 1) * P + pp] = -sn * g0 + cs * g1;
+            const float g0 = dH[(2 * k) * PS + pp], g1 = dH[(2 * k + 1) * PS + pp];
+            dH[(2 * k) * PS + pp] = cs * g0 + sn * g1;
+            dH[(2 * k + 1) * PS + pp] = -sn * g0 + cs * g1;
         }
         // scores C~_r . B~_q over the causal part (zero elsewhere)
         for (int e = tid; e < QR * QR; e += nt) {
             const int r = e / QR, q = e % QR, t = r / R, u = q / R;
             float v = 0.f;
             if (u <= t && t < nq)
-                for (int n = 0; n < N; n++) v += Ct[r * N + n] * Bt[q * N + n];
-            Sc[e] = v;
+                for (int n = 0; n < N; n++) v += Ct[r * NS + n] * Bt[q * NS + n];
+            Sc[r * QS + q] = v;
         }
         __syncthreads();
         // outputs before the gate, the gate's gradient, dy0 = dL/d(pre-gate y); Wk = dy0 * inter term
@@ -365,16 +398,16 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
             float dy0 = 0.f, prod = 0.f;
             if (t < nq) {
                 float yin = 0.f;
-                for (int n = 0; n < N; n++) yin += Ct[r * N + n] * Hs[n * P + pp];
-                yin *= expf(S[t]);
+                for (int n = 0; n < N; n++) yin += Ct[r * NS + n] * Hs[n * PS + pp];
+                yin *= ES[t];
                 float yintra = 0.f;
                 for (int q = 0; q < (t + 1) * R; q++) {
                     const int u = q / R;
-                    const float mw = expf(S[t] - S[u]) * ((u < t) ? G1[u] : GM[u]);
-                    yintra += mw * Sc[r * QR + q] * Xs[q * P + pp];
+                    const float mw = EM[t * Q + u] * ((u < t) ? G1[u] : GM[u]);
+                    yintra += mw * Sc[r * QS + q] * Xs[q * PS + pp];
                 }
-                const float y0 = yin + yintra + Dh * Xs[e];
-                const float d = dY[e];
+                const float y0 = yin + yintra + Dh * Xs[r * PS + pp];
+                const float d = dY[r * PS + pp];
                 if (p.z) {
                     const int64_t oz = tokX(c0 + t) + j * P + pp;
                     const float v = ldt<T>(p.z, oz), sg = 1.f / (1.f + expf(-v));
@@ -385,16 +418,16 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
                 }
                 prod = dy0 * yin;
             }
-            dY[e] = dy0;
-            Wk[e] = prod;
+            dY[r * PS + pp] = dy0;
+            Wk[r * PS + pp] = prod;
         }
         __syncthreads();
         // row sums: inter-term share of dS (ROWA), D's gradient; dP over the causal part
         for (int r = tid; r < QR; r += nt) {
             float a = 0.f, d = 0.f;
             for (int pp = 0; pp < P; pp++) {
-                a += Wk[r * P + pp];
-                d += dY[r * P + pp] * Xs[r * P + pp];
+                a += Wk[r * PS + pp];
+                d += dY[r * PS + pp] * Xs[r * PS + pp];
             }
             ROWA[r] = a;
             dD_acc += d;
@@ -403,8 +436,8 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
             const int r = e / QR, q = e % QR, t = r / R, u = q / R;
             float v = 0.f;
             if (u <= t && t < nq)
-                for (int pp = 0; pp < P; pp++) v += dY[r * P + pp] * Xs[q * P + pp];
-            dPm[e] = v;
+                for (int pp = 0; pp < P; pp++) v += dY[r * PS + pp] * Xs[q * PS + pp];
+            dPm[r * QS + q] = v;
         }
         __syncthreads();
         // d(mask): dMw = Sc * dP. Row sums of dMw * Mw (dS_t), column sums of the same (-dS_s) and of
@@ -414,8 +447,8 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
             float a = 0.f;
             for (int q = 0; q <= (t + 1) * R - 1 && t < nq; q++) {
                 const int u = q / R;
-                const float mw = expf(S[t] - S[u]) * ((u < t) ? G1[u] : GM[u]);
-                a += Sc[r * QR + q] * dPm[r * QR + q] * mw;
+                const float mw = EM[t * Q + u] * ((u < t) ? G1[u] : GM[u]);
+                a += Sc[r * QS + q] * dPm[r * QS + q] * mw;
             }
             ROWB[r] = a;
         }
@@ -424,8 +457,8 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
             float cs_ = 0.f, cg = 0.f, cd = 0.f;
             for (int r = u * R; r < nq * R; r++) {
                 const int t = r / R;
-                const float E = expf(S[t] - S[u]);
-                const float dm = Sc[r * QR + q] * dPm[r * QR + q];
+                const float E = EM[t * Q + u];
+                const float dm = Sc[r * QS + q] * dPm[r * QS + q];
                 const float mw = E * ((u < t) ? G1[u] : GM[u]);
                 cs_ += dm * mw;
                 cg += dm * E;
@@ -440,9 +473,9 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
         for (int e = tid; e < QR * QR; e += nt) {
             const int r = e / QR, q = e % QR, t = r / R, u = q / R;
             float mw = 0.f;
-            if (u <= t && t < nq) mw = expf(S[t] - S[u]) * ((u < t) ? G1[u] : GM[u]);
-            dPm[e] *= mw;
-            Sc[e] *= mw;
+            if (u <= t && t < nq) mw = EM[t * Q + u] * ((u < t) ? G1[u] : GM[u]);
+            dPm[r * QS + q] *= mw;
+            Sc[r * QS + q] *= mw;
         }
         __syncthreads();
         // dX, and Wk = (G^^T B~_q)[p] X_q[p] (for dc); dC~; dB~
@@ -451,74 +484,70 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
             float prod = 0.f;
             if (u < nq) {
                 float gb = 0.f;
-                for (int n = 0; n < N; n++) gb += dH[n * P + pp] * Bt[q * N + n];
-                const float cq = expf(S[e_] - S[u]) * G1[u];
-                float dx = cq * gb + Dh * dY[e];
-                for (int r = u * R; r < nq * R; r++) dx += Sc[r * QR + q] * dY[r * P + pp];
+                for (int n = 0; n < N; n++) gb += dH[n * PS + pp] * Bt[q * NS + n];
+                const float cq = CU[u];
+                float dx = cq * gb + Dh * dY[q * PS + pp];
+                for (int r = u * R; r < nq * R; r++) dx += Sc[r * QS + q] * dY[r * PS + pp];
                 if (u == e_) dx += dXcIn[j * P + pp];
                 stt<T>(p.dx, tokX(c0 + u) + j * P + pp, dx);
-                prod = gb * Xs[e];
+                prod = gb * Xs[q * PS + pp];
             }
-            Wk[e] = prod;
+            Wk[q * PS + pp] = prod;
         }
         for (int e = tid; e < QR * N; e += nt) {
             const int r = e / N, n = e % N, t = r / R;
             if (t >= nq) continue;
             float a = 0.f;
-            for (int q = 0; q < (t + 1) * R; q++) a += dPm[r * QR + q] * Bt[q * N + n];
+            for (int q = 0; q < (t + 1) * R; q++) a += dPm[r * QS + q] * Bt[q * NS + n];
             float b = 0.f;
-            for (int pp = 0; pp < P; pp++) b += Hs[n * P + pp] * dY[r * P + pp];
-            dCt[e] = a + expf(S[t]) * b;
+            for (int pp = 0; pp < P; pp++) b += Hs[n * PS + pp] * dY[r * PS + pp];
+            dCt[r * NS + n] = a + ES[t] * b;
         }
         for (int e = tid; e < QR * N; e += nt) {
             const int q = e / N, n = e % N, u = q / R;
             if (u >= nq) continue;
             float a = 0.f;
-            for (int r = u * R; r < nq * R; r++) a += dPm[r * QR + q] * Ct[r * N + n];
+            for (int r = u * R; r < nq * R; r++) a += dPm[r * QS + q] * Ct[r * NS + n];
             float b = 0.f;
-            for (int pp = 0; pp < P; pp++) b += dH[n * P + pp] * Xs[q * P + pp];
-            dBt[e] = a + expf(S[e_] - S[u]) * G1[u] * b;
+            for (int pp = 0; pp < P; pp++) b += dH[n * PS + pp] * Xs[q * PS + pp];
+            dBt[q * NS + n] = a + CU[u] * b;
         }
+        float gh_acc = 0.f;   // <G^, H'>, this thread's terms
         // dPhi_e: Wk2[k][p] = G^1 Inner0 - G^0 Inner1 with Inner = e^{S_e} H' + sum_q c_q B~_q X_q^T;
-        // its state-decay share e^{S_e} <G^, H'> per (k, p) in the second half of Wk2's rows
+        // and <G^, H'> (the state decay's share of dS_e)
         for (int e = tid; e < K * P; e += nt) {
             const int k = e / P, pp = e % P;
-            const float eSe = expf(S[e_]);
-            float i0 = eSe * Hs[(2 * k) * P + pp], i1 = eSe * Hs[(2 * k + 1) * P + pp];
+            const float eSe = ES[e_];
+            float i0 = eSe * Hs[(2 * k) * PS + pp], i1 = eSe * Hs[(2 * k + 1) * PS + pp];
             for (int q = 0; q < nq * R; q++) {
                 const int u = q / R;
-                const float w = expf(S[e_] - S[u]) * G1[u] * Xs[q * P + pp];
-                i0 += w * Bt[q * N + 2 * k];
-                i1 += w * Bt[q * N + 2 * k + 1];
+                const float w = CU[u] * Xs[q * PS + pp];
+                i0 += w * Bt[q * NS + 2 * k];
+                i1 += w * Bt[q * NS + 2 * k + 1];
             }
-            const float g0 = dH[(2 * k) * P + pp], g1 = dH[(2 * k + 1) * P + pp];
-            Wk2[e] = g1 * i0 - g0 * i1;
+            const float g0 = dH[(2 * k) * PS + pp], g1 = dH[(2 * k + 1) * PS + pp];
+            Wk2[k * PS + pp] = g1 * i0 - g0 * i1;
+            gh_acc += g0 * Hs[(2 * k) * PS + pp] + g1 * Hs[(2 * k + 1) * PS + pp];
         }
-        __syncthreads();
-        // reductions: dc per token row (ROWA += ... kept separate in COLS? no: use rows of Wk)
+        const float gh = block_sum(gh_acc, MISC + 4);   // <G^, H'> (also the barrier of this phase)
+        // dc per row q: the sum of Wk's row, kept in the row's first element
         for (int q = tid; q < QR; q += nt) {
             float a = 0.f;
-            for (int pp = 0; pp < P; pp++) a += Wk[q * P + pp];
-            Wk[q * P] = a;   // dc share of row q (first element of the row; read after the barrier)
-        }
-        if (tid == 0) {
-            float a = 0.f;   // e^{S_e} <G^, H'>
-            const float eSe = expf(S[e_]);
-            for (int e = 0; e < N * P; e++) a += dH[e] * Hs[e];
-            MISC[1] = eSe * a;
+            for (int pp = 0; pp < P; pp++) a += Wk[q * PS + pp];
+            Wk[q * PS] = a;   // dc share of row q (first element of the row; read after the barrier)
         }
         for (int k = tid; k < K; k += nt) {
             float a = 0.f;
-            for (int pp = 0; pp < P; pp++) a += Wk2[k * P + pp];
+            for (int pp = 0; pp < P; pp++) a += Wk2[k * PS + pp];
             DPHI[e_ * K + k] += a;
         }
         __syncthreads();
         // dH' = e^{S_e} G^ + sum_r e^{S_t} C~_r dy_r^T (in place: every read of G^ is done)
         for (int e = tid; e < N * P; e += nt) {
             const int n = e / P, pp = e % P;
-            float v = expf(S[e_]) * dH[e];
-            for (int r = 0; r < nq * R; r++) v += expf(S[r / R]) * Ct[r * N + n] * dY[r * P + pp];
-            dH[e] = v;
+            float v = ES[e_] * dH[n * PS + pp];
+            for (int r = 0; r < nq * R; r++) v += ES[r / R] * Ct[r * NS + n] * dY[r * PS + pp];
+            dH[n * PS + pp] = v;
         }
         // dPhi_t from C~ and B~ (thread per (t, k))
         for (int e = tid; e < nq * K; e += nt) {
@@ -526,15 +555,15 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
             float a = 0.f;
             for (int j = 0; j < R; j++) {
                 const int r = t * R + j;
-                a += dCt[r * N + 2 * k] * Ct[r * N + 2 * k + 1] - dCt[r * N + 2 * k + 1] * Ct[r * N + 2 * k];
-                a += dBt[r * N + 2 * k] * Bt[r * N + 2 * k + 1] - dBt[r * N + 2 * k + 1] * Bt[r * N + 2 * k];
+                a += dCt[r * NS + 2 * k] * Ct[r * NS + 2 * k + 1] - dCt[r * NS + 2 * k + 1] * Ct[r * NS + 2 * k];
+                a += dBt[r * NS + 2 * k] * Bt[r * NS + 2 * k + 1] - dBt[r * NS + 2 * k + 1] * Bt[r * NS + 2 * k];
             }
             DPHI[t * K + k] += a;
         }
         __syncthreads();
         // per-token scalar gradients: dS (inter rows, mask rows/columns, state), d gamma, d delta
         if (tid == 0) {
-            float dSe = MISC[1];
+            float dSe = ES[e_] * gh;
             for (int u = 0; u < nq; u++) {
                 float rowA = 0.f, rowB = 0.f, colS = 0.f, colG = 0.f, colD = 0.f, dc = 0.f;
                 for (int j = 0; j < R; j++) {
@@ -544,10 +573,10 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
                     colS += COLS[q];
                     colG += COLG[q];
                     colD += COLD[q];
-                    dc += Wk[q * P];
+                    dc += Wk[q * PS];
                 }
-                const float E = expf(S[e_] - S[u]);
-                const float cu = E * G1[u];
+                const float E = EM[e_ * Q + u];
+                const float cu = CU[u];
                 DS[u] += rowA + rowB - colS - dc * cu;
                 dSe += dc * cu;
                 DGM[u] += colG + dc * E;
@@ -556,34 +585,27 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
             DS[e_] += dSe;
         }
         // the fold at the chunk start: d delta_0 = <dH', Bp Xp^T>, carries for the previous token
+        float fold_acc = 0.f;   // <dH', Bp Xp^T>, this thread's terms
         if (MISC[0] != 0.f) {
             for (int e = tid; e < R * N; e += nt) {
                 const int j = e / N, n = e % N;
                 float a = 0.f;
-                for (int pp = 0; pp < P; pp++) a += dH[n * P + pp] * Xp[j * P + pp];
+                for (int pp = 0; pp < P; pp++) a += dH[n * PS + pp] * Xp[j * P + pp];
                 dBcOut[e] = DL[0] * a;
+                fold_acc += Bp[e] * a;
             }
             for (int e = tid; e < R * P; e += nt) {
                 const int j = e / P, pp = e % P;
                 float a = 0.f;
-                for (int n = 0; n < N; n++) a += dH[n * P + pp] * Bp[j * N + n];
+                for (int n = 0; n < N; n++) a += dH[n * PS + pp] * Bp[j * N + n];
                 dXcOut[e] = DL[0] * a;
             }
         } else {
             for (int e = tid; e < R * N; e += nt) dBcOut[e] = 0.f;
             for (int e = tid; e < R * P; e += nt) dXcOut[e] = 0.f;
         }
-        __syncthreads();
-        if (tid == 0 && MISC[0] != 0.f) {
-            float a = 0.f;   // <dH', Bp Xp^T> = sum_j <dXcOut_j / delta_0 ... computed directly for accuracy
-            for (int n = 0; n < N; n++)
-                for (int pp = 0; pp < P; pp++) {
-                    float bx = 0.f;
-                    for (int j = 0; j < R; j++) bx += Bp[j * N + n] * Xp[j * P + pp];
-                    a += dH[n * P + pp] * bx;
-                }
-            DDL[0] += a;
-        }
+        const float fold = block_sum(fold_acc, MISC + 4);
+        if (tid == 0) DDL[0] += fold;
         __syncthreads();
         // reverse prefix sums over the chunk: dphi (per angle pair) and d(dt A)
         for (int k = tid; k < K; k += nt) {
@@ -617,25 +639,25 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
         for (int e = tid; e < nq * K * R; e += nt) {
             const int t = e / (K * R), k = (e / R) % K, j = e % R, r = t * R + j;
             const float cs = CS[t * K + k], sn = SN[t * K + k];
-            float d0 = dBt[r * N + 2 * k], d1 = dBt[r * N + 2 * k + 1];
+            float d0 = dBt[r * NS + 2 * k], d1 = dBt[r * NS + 2 * k + 1];
             float b0 = cs * d0 - sn * d1, b1 = sn * d0 + cs * d1;
             if (t == e_) {
                 b0 += dBcIn[j * N + 2 * k];
                 b1 += dBcIn[j * N + 2 * k + 1];
             }
-            dBt[r * N + 2 * k] = b0;
-            dBt[r * N + 2 * k + 1] = b1;
-            d0 = dCt[r * N + 2 * k];
-            d1 = dCt[r * N + 2 * k + 1];
-            dCt[r * N + 2 * k] = cs * d0 - sn * d1;
-            dCt[r * N + 2 * k + 1] = sn * d0 + cs * d1;
+            dBt[r * NS + 2 * k] = b0;
+            dBt[r * NS + 2 * k + 1] = b1;
+            d0 = dCt[r * NS + 2 * k];
+            d1 = dCt[r * NS + 2 * k + 1];
+            dCt[r * NS + 2 * k] = cs * d0 - sn * d1;
+            dCt[r * NS + 2 * k + 1] = sn * d0 + cs * d1;
         }
         __syncthreads();
         for (int n = tid; n < N; n += nt) {
             float a = 0.f, b = 0.f;
             for (int r = 0; r < nq * R; r++) {
-                a += dBt[r * N + n];
-                b += dCt[r * N + n];
+                a += dBt[r * NS + n];
+                b += dCt[r * NS + n];
             }
             BBA[n] += a;
             CBA[n] += b;
@@ -643,7 +665,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
         for (int r = tid; r < 2 * nq * R; r += nt) {
             const bool isC = r >= nq * R;
             const int rr = isC ? r - nq * R : r, t = rr / R, j = rr % R;
-            const float *gout = (isC ? dCt : dBt) + rr * N;
+            const float *gout = (isC ? dCt : dBt) + rr * NS;
             const float inv = (isC ? INVC : INVB)[rr];
             const void *src = isC ? p.C : p.B;
             const int64_t o = tokB(c0 + t) + j * N;
@@ -666,7 +688,7 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
 
     // ------------------------------------------------------------ slab results
     if (p.dh_in)
-        for (int e = tid; e < N * P; e += nt) p.dh_in[sh * N * P + e] = dH[e];
+        for (int e = tid; e < N * P; e += nt) p.dh_in[sh * N * P + e] = dH[(e / P) * PS + e % P];
     if (has_prev) {
         // dBprev: the carry of the first chunk's fold (zero for an empty sequence), through the prologue
         for (int j = tid; j < R; j += nt) {
@@ -706,6 +728,764 @@ __global__ __launch_bounds__(256) void k_scan_bwd(BwdParams p) {
         p.p_dBb[sh * N + n] = BBA[n];
         p.p_dCb[sh * N + n] = CBA[n];
     }
+}
+
+// ---------------------------------------------------------------- MFMA path (bf16 token inputs)
+// The same chunked backward with every chunk contraction on v_mfma_f32_16x16x32_bf16: bf16
+// operands staged in LDS, fp32 accumulation. The state entering each chunk (forward pass) and
+// the carried gradient dH (reverse pass) live in fp32 accumulator registers; each wave owns
+// N x P tiles of both. Per chunk: scores S = C~ B~^T and dP = dY X^T on the causal tiles
+// (masked into A = M o S and dS' = M o dP), then dX = A^T dY + c o (B~ G^), dC~ = dS' B~ +
+// e^{S} o (dY H'^T), dB~ = dS'^T C~ + c o (X G^^T), dH' = e^{S_e} G^ + C~^T (e^{S} o dY) and the
+// rotated state Inner = e^{S_e} H' + B~^T (c o X). Row and column sums that the scalar
+// gradients need are formed per tile (wave shuffles) and added in a fixed order.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Operands of the 16x16x32 product, lane l: i = l % 16 is the A operand's row / the B operand's
+// column, g = l / 16 picks its 8 K-values of the 32-wide K block. Two K orders occur, and the
+// two operands of one product always use the same one:
+//   natural: K = 8g .. 8g + 7                                  (op_nat)
+//   split:   K = 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3         (op_split, op_tr)
+// op_nat and op_split read a row of a K-contiguous matrix ([row][K]); op_tr reads column c0 + i
+// of a matrix stored with K as its row index ([K][col]) through the LDS transpose read.
+__device__ __forceinline__ bf16x8 op_nat(const bf16 *m, int ld, int row, int k0, int g) {
+    return *(const bf16x8 *)(m + row * ld + k0 + 8 * g);
+}
+__device__ __forceinline__ bf16x8 op_split(const bf16 *m, int ld, int row, int k0, int g) {
+    const bf16x4 a = *(const bf16x4 *)(m + row * ld + k0 + 4 * g);
+    const bf16x4 b = *(const bf16x4 *)(m + row * ld + k0 + 16 + 4 * g);
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+// LDS transpose read (16-bit elements): within a group of 16 lanes, lane i receives element
+// i % 4 of the 4 elements read by lanes i / 4 + 4k, k = 0..3; pointed at &M[r0 + i/4][c0 + 4(i%4)],
+// lane i receives M[r0 + k][c0 + i], k = 0..3.
+__device__ __forceinline__ bf16x4 ds_tr4(const bf16 *q) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(q));
+    return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x8 op_tr(const bf16 *m, int ld, int k0, int c0, int i, int g) {
+    const bf16x4 a = ds_tr4(m + (k0 + 4 * g + i / 4) * ld + c0 + 4 * (i % 4));
+    const bf16x4 b = ds_tr4(m + (k0 + 16 + 4 * g + i / 4) * ld + c0 + 4 * (i % 4));
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+// sum over the 16 lanes of a lane group (i = l % 16), and over the 4 groups (g = l / 16)
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+__device__ __forceinline__ float sum_groups(float v) {
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+template <int N_, int P_, int R_, int Q_, int NW_>
+struct BCfg {
+    static constexpr int N = N_, P = P_, R = R_, Q = Q_, NW = NW_;
+    static constexpr int QR = Q * R, K2 = N / 2, NT = NW * 64;
+    static constexpr int NS = N + 8, PS = P + 8, QS = QR + 8, NF = N + 1, SF = QR + 1;
+    static constexpr int TQ = QR / 16, TN = N / 16, TP = P / 16, NPT = TN * TP, UPW = NPT / NW;
+    static_assert(QR % 32 == 0 && N % 32 == 0 && P % 32 == 0 && NPT % NW == 0, "MFMA backward tiling");
+    static_assert(R == 1 || R == 2 || R == 4, "rank");
+    // LDS layout (bytes; every region 16-byte aligned)
+    static constexpr int al(int b) { return (b + 15) / 16 * 16; }
+    static constexpr int O_CS = 0, O_SN = O_CS + al(Q * K2 * 4), O_DPHI = O_SN + al(Q * K2 * 4);
+    static constexpr int O_SC = O_DPHI + al(Q * K2 * 4);            // 11 float [Q] tables
+    static constexpr int O_EM = O_SC + al(11 * Q * 4);              // float [Q][Q]
+    static constexpr int O_INV = O_EM + al(Q * Q * 4);              // float [2][QR]
+    static constexpr int O_RPM = O_INV + al(2 * QR * 4);            // float [QR][TQ] row partials of dM M
+    static constexpr int O_CPM = O_RPM + al(QR * TQ * 4);           // float [3][QR][TQ] column partials
+    static constexpr int O_RPI = O_CPM + al(3 * QR * TQ * 4);       // float [QR][TN] dS inter partials
+    static constexpr int O_RPC = O_RPI + al(QR * TN * 4);           // float [QR][TP] dc partials
+    static constexpr int O_PHE = O_RPC + al(QR * TP * 4);           // float [K2][TP] dPhi_e partials
+    static constexpr int O_SMALL = O_PHE + al(K2 * TP * 4);         // previous token, carries, biases
+    static constexpr int SMALL = 6 * R * N + 4 * R * P + R + 2 * N + 16 + 64;
+    static constexpr int O_DCF = O_SMALL + al(SMALL * 4);           // float [QR][NF] dC~ (raw C staging)
+    static constexpr int O_DBF = O_DCF + al(QR * NF * 4);           // float [QR][NF] dB~ (raw B staging)
+    static constexpr int O_SF = O_DBF + al(QR * NF * 4);            // float [QR][SF] scores
+    static constexpr int O_CT = O_SF + al(QR * SF * 4);             // bf16 [QR][NS] C~
+    static constexpr int O_BT = O_CT + al(QR * NS * 2);             // bf16 [QR][NS] B~
+    static constexpr int O_XB = O_BT + al(QR * NS * 2);             // bf16 [QR][PS] X
+    static constexpr int O_XC = O_XB + al(QR * PS * 2);             // bf16 [QR][PS] c o X
+    static constexpr int O_DY = O_XC + al(QR * PS * 2);             // bf16 [QR][PS] dy0
+    static constexpr int O_EDY = O_DY + al(QR * PS * 2);            // bf16 [QR][PS] e^{S} o dy0
+    static constexpr int O_HB = O_EDY + al(QR * PS * 2);            // bf16 [N][PS] H'
+    static constexpr int O_GB = O_HB + al(N * PS * 2);              // bf16 [N][PS] G^ (then dH')
+    static constexpr int O_AB = O_GB + al(N * PS * 2);              // bf16 [QR][QS] A = M o S
+    static constexpr int O_DSB = O_AB + al(QR * QS * 2);            // bf16 [QR][QS] dS' = M o dP
+    static constexpr int LDS = O_DSB + al(QR * QS * 2);
+    static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <class CF>
+__global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
+    constexpr int N = CF::N, P = CF::P, R = CF::R, Q = CF::Q, NW = CF::NW, QR = CF::QR, K = CF::K2, NT = CF::NT;
+    constexpr int NS = CF::NS, PS = CF::PS, QS = CF::QS, NF = CF::NF, SF = CF::SF;
+    constexpr int TQ = CF::TQ, TN = CF::TN, TP = CF::TP, UPW = CF::UPW;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    float *CS = (float *)(smem + CF::O_CS), *SN = (float *)(smem + CF::O_SN), *DPHI = (float *)(smem + CF::O_DPHI);
+    float *SC = (float *)(smem + CF::O_SC);
+    float *DT = SC, *LM = SC + Q, *GM = SC + 2 * Q, *DL = SC + 3 * Q, *S = SC + 4 * Q, *G1 = SC + 5 * Q;
+    float *ES = SC + 6 * Q, *CU = SC + 7 * Q, *DS = SC + 8 * Q, *DGM = SC + 9 * Q, *DDL = SC + 10 * Q;
+    float *EM = (float *)(smem + CF::O_EM);
+    float *INVB = (float *)(smem + CF::O_INV), *INVC = INVB + QR;
+    float *RPM = (float *)(smem + CF::O_RPM), *CPM = (float *)(smem + CF::O_CPM);
+    float *CPG = CPM + QR * TQ, *CPD = CPG + QR * TQ;
+    float *RPI = (float *)(smem + CF::O_RPI), *RPC = (float *)(smem + CF::O_RPC), *PHE = (float *)(smem + CF::O_PHE);
+    float *SMALLp = (float *)(smem + CF::O_SMALL);
+    float *Bp = SMALLp, *BpRaw = Bp + R * N, *Xp = BpRaw + R * N, *dBcIn = Xp + R * P, *dBcOut = dBcIn + R * N;
+    float *dXcIn = dBcOut + R * N, *dXcOut = dXcIn + R * P, *INVBP = dXcOut + R * P, *BBA = INVBP + R;
+    float *CBA = BBA + N, *MISC = CBA + N, *RED = MISC + 16;
+    float *dCf = (float *)(smem + CF::O_DCF), *dBf = (float *)(smem + CF::O_DBF), *Sf = (float *)(smem + CF::O_SF);
+    bf16 *Ct = (bf16 *)(smem + CF::O_CT), *Bt = (bf16 *)(smem + CF::O_BT), *Xb = (bf16 *)(smem + CF::O_XB);
+    bf16 *XcB = (bf16 *)(smem + CF::O_XC), *dYb = (bf16 *)(smem + CF::O_DY), *EdYb = (bf16 *)(smem + CF::O_EDY);
+    bf16 *Hb = (bf16 *)(smem + CF::O_HB), *Gb = (bf16 *)(smem + CF::O_GB), *Ab = (bf16 *)(smem + CF::O_AB);
+    bf16 *dSb = (bf16 *)(smem + CF::O_DSB);
+
+    const int H = p.H, G = p.G;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, lg = lane >> 4;
+    const int s = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
+    const bf16 *gx = (const bf16 *)p.x, *gB = (const bf16 *)p.B, *gC = (const bf16 *)p.C, *gdy = (const bf16 *)p.dy;
+
+    int64_t start, len, cbase;
+    if (p.cu) {
+        const int64_t a = min(max((int64_t)p.cu[s], (int64_t)0), (int64_t)p.seqlen);
+        const int64_t b = min(max((int64_t)p.cu[s + 1], a), (int64_t)p.seqlen);
+        start = a;
+        len = b - a;
+        cbase = 0;
+        for (int j = 0; j < s; j++) {
+            const int64_t a0 = min(max((int64_t)p.cu[j], (int64_t)0), (int64_t)p.seqlen);
+            const int64_t b0 = min(max((int64_t)p.cu[j + 1], a0), (int64_t)p.seqlen);
+            cbase += (b0 - a0 + Q - 1) / Q;
+        }
+    } else {
+        start = (int64_t)s * p.seqlen;
+        len = p.seqlen;
+        cbase = (int64_t)s * ((p.seqlen + Q - 1) / Q);
+    }
+    const int64_t nch = (len + Q - 1) / Q;
+    if (cbase + nch > p.ws_chunks) return;   // a sequence table that breaks its contract
+    const float Ah = p.A[h];
+    const float Dh = p.D ? p.D[h] : 0.f;
+    const bool pro = p.norm || p.Bb || p.Cb;
+    const bool has_prev = p.Bprev != nullptr;
+    const int64_t sh = (int64_t)s * H + h;
+    const float *Bbh = p.Bb ? p.Bb + (int64_t)h * N : nullptr;
+    const float *Cbh = p.Cb ? p.Cb + (int64_t)h * N : nullptr;
+    auto wsS = [&](int64_t c) { return p.ws_state + ((cbase + c) * H + h) * (int64_t)N * P; };
+    auto tokB = [&](int64_t t) { return ((start + t) * G + g) * (int64_t)R * N; };
+    auto tokX = [&](int64_t t) { return ((start + t) * H + h) * (int64_t)R * P; };
+    // this wave's N x P tiles: tile v covers rows n0 .. n0 + 15, columns p0 .. p0 + 15; the lane
+    // holds rows n0 + 4 lg + i (i = 0..3) of column p0 + li
+    auto tile_n0 = [&](int v) { return ((wave * UPW + v) / TP) * 16; };
+    auto tile_p0 = [&](int v) { return ((wave * UPW + v) % TP) * 16; };
+
+    auto prologue_rows = [&](float *rows, int nrows, int stride, const float *bias, float *invs) {
+        for (int r = tid; r < nrows; r += NT) {
+            float *v = rows + (int64_t)r * stride;
+            float inv = 1.f;
+            if (p.norm) {
+                float ss = 0.f;
+                for (int n = 0; n < N; n++) ss += v[n] * v[n];
+                inv = 1.f / sqrtf(ss / (float)N + p.eps);
+            }
+            invs[r] = inv;
+            if (pro)
+                for (int n = 0; n < N; n++) v[n] = v[n] * inv + (bias ? bias[n] : 0.f);
+        }
+    };
+    auto load_scalars = [&](int64_t c0, int nq) {
+        for (int t = tid; t < Q; t += NT) {
+            float dtv = 0.f, lv = 0.f;
+            if (t < nq) {
+                dtv = ldt<bf16>(p.dt, (start + c0 + t) * H + h);
+                lv = ldt<bf16>(p.lam, (start + c0 + t) * H + h);
+            }
+            DT[t] = dtv;
+            LM[t] = lv;
+            GM[t] = lv * dtv;
+            DL[t] = (1.f - lv) * dtv;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float acc = 0.f;
+            for (int t = 0; t < Q; t++) {
+                acc += DT[t] * Ah;
+                S[t] = acc;
+                G1[t] = GM[t] + ((t + 1 < nq) ? DL[t + 1] : 0.f);
+            }
+        }
+        for (int k = tid; k < K; k += NT) {
+            float acc = 0.f;
+            for (int t = 0; t < Q; t++) {
+                if (t < nq) acc += DT[t] * ldt<bf16>(p.theta, ((start + c0 + t) * H + h) * K + k);
+                float sn, cs;
+                sincosf(acc, &sn, &cs);
+                CS[t * K + k] = cs;
+                SN[t * K + k] = sn;
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < Q * Q; e += NT) {
+            const int t = e / Q, u = e % Q;
+            EM[e] = (u <= t) ? expf(S[t] - S[u]) : 0.f;
+        }
+        for (int t = tid; t < Q; t += NT) {
+            ES[t] = expf(S[t]);
+            CU[t] = (t < nq) ? expf(S[nq - 1] - S[t]) * G1[t] : 0.f;
+        }
+        __syncthreads();
+    };
+    auto load_prev = [&](int64_t c0) {
+        const bool ex = c0 > 0 || has_prev;
+        for (int e = tid; e < R * N; e += NT) {
+            float v = 0.f;
+            if (c0 > 0) v = ldt<bf16>(p.B, tokB(c0 - 1) + e);
+            else if (has_prev) v = ldt<bf16>(p.Bprev, ((int64_t)s * G + g) * R * N + e);
+            Bp[e] = v;
+            BpRaw[e] = v;
+        }
+        for (int e = tid; e < R * P; e += NT) {
+            float v = 0.f;
+            if (c0 > 0) v = ldt<bf16>(p.x, tokX(c0 - 1) + e);
+            else if (has_prev) v = ldt<bf16>(p.xprev, ((int64_t)s * H + h) * R * P + e);
+            Xp[e] = v;
+        }
+        if (tid == 0) MISC[0] = ex ? 1.f : 0.f;
+        __syncthreads();
+        if (ex) prologue_rows(Bp, R, N, Bbh, INVBP);
+        __syncthreads();
+    };
+    // B~ (and C~, dy in the reverse pass) and X, c o X of the chunk in bf16; raw B and C rows go
+    // through fp32 staging (dBf, dCf) for the prologue and the rotation
+    auto stage_chunk = [&](int64_t c0, int nq, bool rev) {
+        for (int e = tid; e < QR * N; e += NT) {
+            const int r = e / N, n = e % N, t = r / R, j = r % R;
+            float bv = 0.f, cv = 0.f;
+            if (t < nq) {
+                const int64_t o = tokB(c0 + t) + j * N + n;
+                bv = (float)gB[o];
+                if (rev) cv = (float)gC[o];
+            }
+            dBf[r * NF + n] = bv;
+            if (rev) dCf[r * NF + n] = cv;
+        }
+        for (int e = tid; e < QR * P; e += NT) {
+            const int r = e / P, pp = e % P, t = r / R, j = r % R;
+            float xv = 0.f, dv = 0.f;
+            if (t < nq) {
+                xv = (float)gx[tokX(c0 + t) + j * P + pp];
+                if (rev) dv = (float)gdy[tokX(c0 + t) + j * P + pp];
+            }
+            Xb[r * PS + pp] = (bf16)xv;
+            XcB[r * PS + pp] = (bf16)(CU[t] * xv);
+            if (rev) dYb[r * PS + pp] = (bf16)dv;
+        }
+        __syncthreads();
+        prologue_rows(dBf, nq * R, NF, Bbh, INVB);
+        if (rev) prologue_rows(dCf, nq * R, NF, Cbh, INVC);
+        __syncthreads();
+        for (int e = tid; e < QR * K; e += NT) {
+            const int r = e / K, k = e % K, t = r / R;
+            float b0 = 0.f, b1 = 0.f, q0 = 0.f, q1 = 0.f;
+            if (t < nq) {
+                const float cs = CS[t * K + k], sn = SN[t * K + k];
+                const float u0 = dBf[r * NF + 2 * k], u1 = dBf[r * NF + 2 * k + 1];
+                b0 = cs * u0 + sn * u1;
+                b1 = -sn * u0 + cs * u1;
+                if (rev) {
+                    const float v0 = dCf[r * NF + 2 * k], v1 = dCf[r * NF + 2 * k + 1];
+                    q0 = cs * v0 + sn * v1;
+                    q1 = -sn * v0 + cs * v1;
+                }
+            }
+            *(bf16x2 *)(Bt + r * NS + 2 * k) = bf16x2{(bf16)b0, (bf16)b1};
+            if (rev) *(bf16x2 *)(Ct + r * NS + 2 * k) = bf16x2{(bf16)q0, (bf16)q1};
+        }
+        __syncthreads();
+    };
+
+    // ------------------------------------------------------------ forward: chunk states
+    f32x4 hacc[UPW];
+#pragma unroll
+    for (int v = 0; v < UPW; v++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int n = tile_n0(v) + 4 * lg + i, pp = tile_p0(v) + li;
+            hacc[v][i] = p.h_in ? p.h_in[sh * N * P + n * P + pp] : 0.f;
+        }
+    for (int64_t c = 0; c < nch; c++) {
+        const int64_t c0 = c * Q;
+        const int nq = (int)min((int64_t)Q, len - c0), e_ = nq - 1;
+        load_scalars(c0, nq);
+        load_prev(c0);
+        float *ws = wsS(c);
+#pragma unroll
+        for (int v = 0; v < UPW; v++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int n = tile_n0(v) + 4 * lg + i, pp = tile_p0(v) + li;
+                float acc = 0.f;
+                for (int j = 0; j < R; j++) acc += Bp[j * N + n] * Xp[j * P + pp];
+                hacc[v][i] += DL[0] * acc;
+                ws[n * P + pp] = hacc[v][i];
+            }
+        stage_chunk(c0, nq, false);
+#pragma unroll
+        for (int v = 0; v < UPW; v++) {
+            const int n0 = tile_n0(v), p0 = tile_p0(v);
+            f32x4 acc = {};
+#pragma unroll
+            for (int k0 = 0; k0 < QR; k0 += 32)
+                acc = mfma16(op_tr(Bt, NS, k0, n0, li, lg), op_tr(XcB, PS, k0, p0, li, lg), acc);
+#pragma unroll
+            for (int m = 0; m < 2; m++) {   // pairs (rows 4 lg + 2m, + 1)
+                const int k = (n0 + 4 * lg) / 2 + m;
+                const float cs = CS[e_ * K + k], sn = SN[e_ * K + k];
+                const float u0 = ES[e_] * hacc[v][2 * m] + acc[2 * m];
+                const float u1 = ES[e_] * hacc[v][2 * m + 1] + acc[2 * m + 1];
+                hacc[v][2 * m] = cs * u0 - sn * u1;
+                hacc[v][2 * m + 1] = sn * u0 + cs * u1;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ------------------------------------------------------------ reverse
+    f32x4 dacc[UPW];
+#pragma unroll
+    for (int v = 0; v < UPW; v++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int n = tile_n0(v) + 4 * lg + i, pp = tile_p0(v) + li;
+            dacc[v][i] = p.dh_out ? p.dh_out[sh * N * P + n * P + pp] : 0.f;
+        }
+    for (int e = tid; e < R * N; e += NT) dBcIn[e] = 0.f;
+    for (int e = tid; e < R * P; e += NT) dXcIn[e] = 0.f;
+    for (int e = tid; e < N; e += NT) BBA[e] = CBA[e] = 0.f;
+    for (int e = tid; e < R * N; e += NT) BpRaw[e] = 0.f;
+    for (int e = tid; e < R; e += NT) INVBP[e] = 1.f;
+    float dA_acc = 0.f, dD_acc = 0.f;
+    __syncthreads();
+    for (int64_t c = nch - 1; c >= 0; c--) {
+        const int64_t c0 = c * Q;
+        const int nq = (int)min((int64_t)Q, len - c0), e_ = nq - 1;
+        load_scalars(c0, nq);
+        load_prev(c0);
+        // G^ = R(-Phi_e) dH (registers, bf16 copy in Gb); H' entering the chunk from the workspace
+        f32x4 gacc[UPW], hcur[UPW];
+        const float *ws = wsS(c);
+#pragma unroll
+        for (int v = 0; v < UPW; v++) {
+            const int n0 = tile_n0(v), p0 = tile_p0(v);
+#pragma unroll
+            for (int m = 0; m < 2; m++) {
+                const int k = (n0 + 4 * lg) / 2 + m;
+                const float cs = CS[e_ * K + k], sn = SN[e_ * K + k];
+                const float g0 = dacc[v][2 * m], g1 = dacc[v][2 * m + 1];
+                gacc[v][2 * m] = cs * g0 + sn * g1;
+                gacc[v][2 * m + 1] = -sn * g0 + cs * g1;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int n = n0 + 4 * lg + i, pp = p0 + li;
+                hcur[v][i] = ws[n * P + pp];
+                Gb[n * PS + pp] = (bf16)gacc[v][i];
+                Hb[n * PS + pp] = (bf16)hcur[v][i];
+            }
+        }
+        stage_chunk(c0, nq, true);
+        for (int e = tid; e < Q * K; e += NT) DPHI[e] = 0.f;
+        for (int t = tid; t < Q; t += NT) DS[t] = DGM[t] = DDL[t] = 0.f;
+        // scores on every QR x QR tile (zero outside the causal part): S (fp32) and A = M o S (bf16)
+        for (int tile = wave; tile < TQ * TQ; tile += NW) {
+            const int tr = tile / TQ, tc = tile % TQ;
+            f32x4 acc = {};
+#pragma unroll
+            for (int k0 = 0; k0 < N; k0 += 32)
+                acc = mfma16(op_nat(Ct, NS, tr * 16 + li, k0, lg), op_nat(Bt, NS, tc * 16 + li, k0, lg), acc);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int r = tr * 16 + 4 * lg + i, q = tc * 16 + li, t = r / R, u = q / R;
+                const bool ok = u <= t && t < nq;
+                const float mw = ok ? EM[t * Q + u] * ((u < t) ? G1[u] : GM[u]) : 0.f;
+                Sf[r * SF + q] = ok ? acc[i] : 0.f;
+                Ab[r * QS + q] = (bf16)(mw * acc[i]);
+            }
+        }
+        __syncthreads();
+        if (p.z) {
+            // outputs before the gate, y0 = e^{S_t} C~ H' + A X + D X; dy0 = dy SiLU(z), dz
+            for (int tile = wave; tile < TQ * TP; tile += NW) {
+                const int tr = tile / TP, tp = tile % TP;
+                f32x4 yin = {}, yia = {};
+#pragma unroll
+                for (int k0 = 0; k0 < N; k0 += 32)
+                    yin = mfma16(op_split(Ct, NS, tr * 16 + li, k0, lg), op_tr(Hb, PS, k0, tp * 16, li, lg), yin);
+#pragma unroll
+                for (int k0 = 0; k0 < QR; k0 += 32)
+                    yia = mfma16(op_split(Ab, QS, tr * 16 + li, k0, lg), op_tr(Xb, PS, k0, tp * 16, li, lg), yia);
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int r = tr * 16 + 4 * lg + i, pp = tp * 16 + li, t = r / R, j = r % R;
+                    if (t >= nq) continue;
+                    const float y0 = ES[t] * yin[i] + yia[i] + Dh * (float)Xb[r * PS + pp];
+                    const float d = (float)dYb[r * PS + pp];
+                    const int64_t oz = tokX(c0 + t) + j * P + pp;
+                    const float zv = ldt<bf16>(p.z, oz), sg = 1.f / (1.f + expf(-zv));
+                    if (p.dz) stt<bf16>(p.dz, oz, d * y0 * (sg + zv * sg * (1.f - sg)));
+                    dYb[r * PS + pp] = (bf16)(d * zv * sg);
+                }
+            }
+            __syncthreads();
+        }
+        // e^{S} o dy0, and D's gradient
+        for (int e = tid; e < QR * P; e += NT) {
+            const int r = e / P, pp = e % P, t = r / R;
+            const float d = (float)dYb[r * PS + pp];
+            EdYb[r * PS + pp] = (bf16)(ES[t] * d);
+            dD_acc += d * (float)Xb[r * PS + pp];
+        }
+        __syncthreads();
+        // dP = dY X^T with the mask: dS' = M o dP (bf16); d(mask) = S o dP, summed per row and column
+        for (int tile = wave; tile < TQ * TQ; tile += NW) {
+            const int tr = tile / TQ, tc = tile % TQ;
+            f32x4 acc = {};
+#pragma unroll
+            for (int k0 = 0; k0 < P; k0 += 32)
+                acc = mfma16(op_nat(dYb, PS, tr * 16 + li, k0, lg), op_nat(Xb, PS, tc * 16 + li, k0, lg), acc);
+            float cm = 0.f, cg = 0.f, cd = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int r = tr * 16 + 4 * lg + i, q = tc * 16 + li, t = r / R, u = q / R;
+                const bool ok = u <= t && t < nq;
+                const float E = ok ? EM[t * Q + u] : 0.f, w = (u < t) ? G1[u] : GM[u];
+                const float dm = Sf[r * SF + q] * acc[i];
+                dSb[r * QS + q] = (bf16)(E * w * acc[i]);
+                const float rm = sum16(dm * E * w);   // row r's share of this tile
+                if (li == 0) RPM[r * TQ + tc] = rm;
+                cm += dm * E * w;
+                cg += dm * E;
+                cd += (u < t) ? dm * E : 0.f;
+            }
+            cm = sum_groups(cm);
+            cg = sum_groups(cg);
+            cd = sum_groups(cd);
+            if (lg == 0) {
+                const int q = tc * 16 + li;
+                CPM[q * TQ + tr] = cm;
+                CPG[q * TQ + tr] = cg;
+                CPD[q * TQ + tr] = cd;
+            }
+        }
+        __syncthreads();
+        // dX = A^T dy0 + c o (B~ G^) + D dy0 (+ the fold's carry into the last token); dc partials
+        for (int tile = wave; tile < TQ * TP; tile += NW) {
+            const int tq = tile / TP, tp = tile % TP;
+            f32x4 a1 = {}, a2 = {};
+#pragma unroll
+            for (int k0 = 0; k0 < QR; k0 += 32)
+                a1 = mfma16(op_tr(Ab, QS, k0, tq * 16, li, lg), op_tr(dYb, PS, k0, tp * 16, li, lg), a1);
+#pragma unroll
+            for (int k0 = 0; k0 < N; k0 += 32)
+                a2 = mfma16(op_split(Bt, NS, tq * 16 + li, k0, lg), op_tr(Gb, PS, k0, tp * 16, li, lg), a2);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int q = tq * 16 + 4 * lg + i, pp = tp * 16 + li, u = q / R, j = q % R;
+                const float xv = (float)Xb[q * PS + pp];
+                const float dc = sum16(a2[i] * xv);
+                if (li == 0) RPC[q * TP + tp] = dc;
+                if (u < nq) {
+                    float dx = a1[i] + CU[u] * a2[i] + Dh * (float)dYb[q * PS + pp];
+                    if (u == e_) dx += dXcIn[j * P + pp];
+                    stt<bf16>(p.dx, tokX(c0 + u) + j * P + pp, dx);
+                }
+            }
+        }
+        // dC~ = dS' B~ + e^{S_t} (dY H'^T); the inter part's share of dS
+        for (int tile = wave; tile < TQ * TN; tile += NW) {
+            const int tq = tile / TN, tn = tile % TN;
+            f32x4 a1 = {}, a2 = {};
+#pragma unroll
+            for (int k0 = 0; k0 < QR; k0 += 32)
+                a1 = mfma16(op_split(dSb, QS, tq * 16 + li, k0, lg), op_tr(Bt, NS, k0, tn * 16, li, lg), a1);
+#pragma unroll
+            for (int k0 = 0; k0 < P; k0 += 32)
+                a2 = mfma16(op_nat(dYb, PS, tq * 16 + li, k0, lg), op_nat(Hb, PS, tn * 16 + li, k0, lg), a2);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int r = tq * 16 + 4 * lg + i, n = tn * 16 + li, t = r / R;
+                const float inter = (t < nq) ? ES[t] * a2[i] : 0.f;
+                dCf[r * NF + n] = (t < nq) ? a1[i] + inter : 0.f;
+                const float di = sum16((float)Ct[r * NS + n] * inter);
+                if (li == 0) RPI[r * TN + tn] = di;
+            }
+        }
+        // dB~ = dS'^T C~ + c o (X G^^T)
+        for (int tile = wave; tile < TQ * TN; tile += NW) {
+            const int tq = tile / TN, tn = tile % TN;
+            f32x4 a1 = {}, a2 = {};
+#pragma unroll
+            for (int k0 = 0; k0 < QR; k0 += 32)
+                a1 = mfma16(op_tr(dSb, QS, k0, tq * 16, li, lg), op_tr(Ct, NS, k0, tn * 16, li, lg), a1);
+#pragma unroll
+            for (int k0 = 0; k0 < P; k0 += 32)
+                a2 = mfma16(op_nat(Xb, PS, tq * 16 + li, k0, lg), op_nat(Gb, PS, tn * 16 + li, k0, lg), a2);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int q = tq * 16 + 4 * lg + i, n = tn * 16 + li, u = q / R;
+                dBf[q * NF + n] = (u < nq) ? a1[i] + CU[u] * a2[i] : 0.f;
+            }
+        }
+        // dH' = e^{S_e} G^ + C~^T (e^{S} o dY), and the rotated state Inner = e^{S_e} H' + B~^T (c o X)
+        // for dPhi_e = sum_p G^^T J Inner; <G^, H'> for dS_e
+        float gh_acc = 0.f;
+#pragma unroll
+        for (int v = 0; v < UPW; v++) {
+            const int n0 = tile_n0(v), p0 = tile_p0(v);
+            f32x4 a1 = {}, a2 = {};
+#pragma unroll
+            for (int k0 = 0; k0 < QR; k0 += 32) {
+                a1 = mfma16(op_tr(Ct, NS, k0, n0, li, lg), op_tr(EdYb, PS, k0, p0, li, lg), a1);
+                a2 = mfma16(op_tr(Bt, NS, k0, n0, li, lg), op_tr(XcB, PS, k0, p0, li, lg), a2);
+            }
+#pragma unroll
+            for (int m = 0; m < 2; m++) {
+                const float in0 = ES[e_] * hcur[v][2 * m] + a2[2 * m], in1 = ES[e_] * hcur[v][2 * m + 1] + a2[2 * m + 1];
+                const float ph = sum16(gacc[v][2 * m + 1] * in0 - gacc[v][2 * m] * in1);
+                if (li == 0) PHE[((n0 + 4 * lg) / 2 + m) * TP + p0 / 16] = ph;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                gh_acc += gacc[v][i] * hcur[v][i];
+                dacc[v][i] = ES[e_] * gacc[v][i] + a1[i];
+            }
+        }
+        const float gh = block_sum(gh_acc, RED);   // (also orders every write above before the reads below)
+        // dH' in bf16 for the fold (G^ is no longer read)
+#pragma unroll
+        for (int v = 0; v < UPW; v++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) Gb[(tile_n0(v) + 4 * lg + i) * PS + tile_p0(v) + li] = (bf16)dacc[v][i];
+        // dPhi_e, and dPhi_t from C~ and B~ (thread per (t, k))
+        for (int k = tid; k < K; k += NT) {
+            float a = 0.f;
+            for (int tp = 0; tp < TP; tp++) a += PHE[k * TP + tp];
+            DPHI[e_ * K + k] += a;
+        }
+        __syncthreads();
+        for (int e = tid; e < nq * K; e += NT) {
+            const int t = e / K, k = e % K;
+            float a = 0.f;
+            for (int j = 0; j < R; j++) {
+                const int r = t * R + j;
+                a += dCf[r * NF + 2 * k] * (float)Ct[r * NS + 2 * k + 1] - dCf[r * NF + 2 * k + 1] * (float)Ct[r * NS + 2 * k];
+                a += dBf[r * NF + 2 * k] * (float)Bt[r * NS + 2 * k + 1] - dBf[r * NF + 2 * k + 1] * (float)Bt[r * NS + 2 * k];
+            }
+            DPHI[t * K + k] += a;
+        }
+        // per-token scalar gradients from the row / column partials (fixed order)
+        if (tid == 0) {
+            float dSe = ES[e_] * gh;
+            for (int u = 0; u < nq; u++) {
+                float rowA = 0.f, rowB = 0.f, colS = 0.f, colG = 0.f, colD = 0.f, dc = 0.f;
+                for (int j = 0; j < R; j++) {
+                    const int q = u * R + j;
+                    for (int x = 0; x < TN; x++) rowA += RPI[q * TN + x];
+                    for (int x = 0; x < TQ; x++) {
+                        rowB += RPM[q * TQ + x];
+                        colS += CPM[q * TQ + x];
+                        colG += CPG[q * TQ + x];
+                        colD += CPD[q * TQ + x];
+                    }
+                    for (int x = 0; x < TP; x++) dc += RPC[q * TP + x];
+                }
+                const float E = EM[e_ * Q + u];
+                const float cu = CU[u];
+                DS[u] += rowA + rowB - colS - dc * cu;
+                dSe += dc * cu;
+                DGM[u] += colG + dc * E;
+                if (u + 1 < nq) DDL[u + 1] += colD + dc * E;
+            }
+            DS[e_] += dSe;
+        }
+        // the fold at the chunk start: d delta_0 = <dH', Bp Xp^T>, carries for the previous token
+        float fold_acc = 0.f;
+        if (MISC[0] != 0.f) {
+            for (int e = tid; e < R * N; e += NT) {
+                const int j = e / N, n = e % N;
+                float a = 0.f;
+                for (int pp = 0; pp < P; pp++) a += (float)Gb[n * PS + pp] * Xp[j * P + pp];
+                dBcOut[e] = DL[0] * a;
+                fold_acc += Bp[e] * a;
+            }
+            for (int e = tid; e < R * P; e += NT) {
+                const int j = e / P, pp = e % P;
+                float a = 0.f;
+                for (int n = 0; n < N; n++) a += (float)Gb[n * PS + pp] * Bp[j * N + n];
+                dXcOut[e] = DL[0] * a;
+            }
+        } else {
+            for (int e = tid; e < R * N; e += NT) dBcOut[e] = 0.f;
+            for (int e = tid; e < R * P; e += NT) dXcOut[e] = 0.f;
+        }
+        const float fold = block_sum(fold_acc, RED);
+        if (tid == 0) DDL[0] += fold;
+        __syncthreads();
+        for (int k = tid; k < K; k += NT) {
+            float acc = 0.f;
+            for (int t = nq - 1; t >= 0; t--) {
+                acc += DPHI[t * K + k];
+                DPHI[t * K + k] = acc;
+            }
+        }
+        if (tid == 0) {
+            float acc = 0.f;
+            for (int t = nq - 1; t >= 0; t--) {
+                acc += DS[t];
+                DS[t] = acc;
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < nq * K; e += NT) {
+            const int t = e / K, k = e % K;
+            stt<bf16>(p.dtheta, ((start + c0 + t) * H + h) * K + k, DT[t] * DPHI[e]);
+        }
+        for (int t = tid; t < nq; t += NT) {
+            float ddt = Ah * DS[t] + (1.f - LM[t]) * DDL[t] + LM[t] * DGM[t];
+            for (int k = 0; k < K; k++) ddt += ldt<bf16>(p.theta, ((start + c0 + t) * H + h) * K + k) * DPHI[t * K + k];
+            stt<bf16>(p.ddt, (start + c0 + t) * H + h, ddt);
+            stt<bf16>(p.dlam, (start + c0 + t) * H + h, DT[t] * (DGM[t] - DDL[t]));
+            dA_acc += DT[t] * DS[t];
+        }
+        // dB, dC back to the physical frame (+ the carry into the last token), through the prologue
+        for (int e = tid; e < nq * K * R; e += NT) {
+            const int t = e / (K * R), k = (e / R) % K, j = e % R, r = t * R + j;
+            const float cs = CS[t * K + k], sn = SN[t * K + k];
+            float d0 = dBf[r * NF + 2 * k], d1 = dBf[r * NF + 2 * k + 1];
+            float b0 = cs * d0 - sn * d1, b1 = sn * d0 + cs * d1;
+            if (t == e_) {
+                b0 += dBcIn[j * N + 2 * k];
+                b1 += dBcIn[j * N + 2 * k + 1];
+            }
+            dBf[r * NF + 2 * k] = b0;
+            dBf[r * NF + 2 * k + 1] = b1;
+            d0 = dCf[r * NF + 2 * k];
+            d1 = dCf[r * NF + 2 * k + 1];
+            dCf[r * NF + 2 * k] = cs * d0 - sn * d1;
+            dCf[r * NF + 2 * k + 1] = sn * d0 + cs * d1;
+        }
+        __syncthreads();
+        for (int n = tid; n < N; n += NT) {
+            float a = 0.f, b = 0.f;
+            for (int r = 0; r < nq * R; r++) {
+                a += dBf[r * NF + n];
+                b += dCf[r * NF + n];
+            }
+            BBA[n] += a;
+            CBA[n] += b;
+        }
+        for (int r = tid; r < 2 * nq * R; r += NT) {
+            const bool isC = r >= nq * R;
+            const int rr = isC ? r - nq * R : r, t = rr / R, j = rr % R;
+            const float *gout = (isC ? dCf : dBf) + rr * NF;
+            const float inv = (isC ? INVC : INVB)[rr];
+            const bf16 *src = isC ? gC : gB;
+            const int64_t o = tokB(c0 + t) + j * N;
+            float dot = 0.f;
+            if (p.norm)
+                for (int n = 0; n < N; n++) dot += gout[n] * (float)src[o + n];
+            const float k3 = p.norm ? dot * inv * inv * inv / (float)N : 0.f;
+            float *part = isC ? p.p_dC : p.p_dB;
+            for (int n = 0; n < N; n++) {
+                const float v = p.norm ? gout[n] * inv - k3 * (float)src[o + n] : gout[n];
+                if (part) part[((start + c0 + t) * H + h) * (int64_t)R * N + j * N + n] = v;
+                else stt<bf16>(isC ? p.dC : p.dB, o + n, v);
+            }
+        }
+        for (int e = tid; e < R * N; e += NT) dBcIn[e] = dBcOut[e];
+        for (int e = tid; e < R * P; e += NT) dXcIn[e] = dXcOut[e];
+        __syncthreads();
+    }
+
+    // ------------------------------------------------------------ slab results
+    if (p.dh_in) {
+#pragma unroll
+        for (int v = 0; v < UPW; v++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                p.dh_in[sh * N * P + (tile_n0(v) + 4 * lg + i) * P + tile_p0(v) + li] = dacc[v][i];
+    }
+    if (has_prev) {
+        for (int j = tid; j < R; j += NT) {
+            const float *gout = dBcIn + j * N;
+            const float inv = INVBP[j];
+            const int64_t o = ((int64_t)s * G + g) * R * N + j * N;
+            float dot = 0.f;
+            if (p.norm)
+                for (int n = 0; n < N; n++) dot += gout[n] * BpRaw[j * N + n];
+            const float k3 = p.norm ? dot * inv * inv * inv / (float)N : 0.f;
+            for (int n = 0; n < N; n++) {
+                const float v = p.norm ? gout[n] * inv - k3 * BpRaw[j * N + n] : gout[n];
+                if (p.p_dBprev) p.p_dBprev[sh * (int64_t)R * N + j * N + n] = v;
+                else if (p.dBprev) stt<bf16>(p.dBprev, o + n, v);
+            }
+        }
+        for (int n = tid; n < N; n += NT)
+            for (int j = 0; j < R; j++) BBA[n] += dBcIn[j * N + n];
+        for (int e = tid; e < R * P; e += NT)
+            if (p.dxprev) stt<bf16>(p.dxprev, sh * R * P + e, dXcIn[e]);
+    }
+    const float dA_sum = block_sum(dA_acc, RED);
+    const float dD_sum = block_sum(dD_acc, RED);
+    if (tid == 0) {
+        p.p_dA[sh] = dA_sum;
+        p.p_dD[sh] = dD_sum;
+    }
+    for (int n = tid; n < N; n += NT) {
+        p.p_dBb[sh * N + n] = BBA[n];
+        p.p_dCb[sh * N + n] = CBA[n];
+    }
+}
+
+// (N, P, R) -> chunk length and waves of the MFMA backward
+#define M3_BWD_MFMA_SHAPES(X) \
+    X(128, 64, 1, 32, 8)      \
+    X(64, 64, 1, 32, 8)       \
+    X(64, 64, 4, 8, 8)        \
+    X(128, 64, 2, 16, 8)      \
+    X(128, 64, 4, 8, 8)       \
+    X(64, 64, 2, 16, 8)
+
+int scan_bwd_mfma_chunk(int N, int P, int R) {
+#define X(n, pp, r, q, w) if (N == n && P == pp && R == r) return q;
+    M3_BWD_MFMA_SHAPES(X)
+#undef X
+    return 0;
+}
+
+template <class CF>
+static mamba3_status launch_bwd_mfma_cfg(const BwdParams &p, int64_t nblk, hipStream_t st) {
+    if (hipFuncSetAttribute((const void *)k_scan_bwd_mfma<CF>, hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS) !=
+        hipSuccess)
+        return MAMBA3_EHIP;
+    if (nblk > 0) hipLaunchKernelGGL(k_scan_bwd_mfma<CF>, dim3((unsigned)nblk), dim3(CF::NT), CF::LDS, st, p);
+    return MAMBA3_OK;
+}
+
+static mamba3_status launch_bwd_mfma(const BwdParams &p, int64_t nblk, hipStream_t st) {
+#define X(n, pp, r, q, w) \
+    if (p.N == n && p.P == pp && p.R == r) return launch_bwd_mfma_cfg<BCfg<n, pp, r, q, w>>(p, nblk, st);
+    M3_BWD_MFMA_SHAPES(X)
+#undef X
+    return MAMBA3_EUNSUPPORTED;
 }
 
 // Fixed-order sums of the per-slab partials: dA, dD, the bias gradients over
@@ -790,15 +1570,24 @@ static BwdWs bwd_ws(const mamba3_scan_bwd_args *b, int Q) {
     return w;
 }
 
+// chunk length of the path that runs: the MFMA kernel's for bf16 inputs of its shapes, else the
+// VALU kernel's
+static int bwd_path_chunk(const mamba3_scan_args *a, bool *mfma) {
+    const int qm = a->dtype == MAMBA3_BF16 ? scan_bwd_mfma_chunk(a->dstate, a->headdim, a->rank) : 0;
+    if (mfma) *mfma = qm > 0;
+    return qm > 0 ? qm : scan_bwd_chunk(a->dstate, a->headdim, a->rank);
+}
+
 size_t scan_bwd_workspace_bytes(const mamba3_scan_bwd_args *b) {
-    const int Q = scan_bwd_chunk(b->fwd.dstate, b->fwd.headdim, b->fwd.rank);
+    const int Q = bwd_path_chunk(&b->fwd, nullptr);
     return Q ? bwd_ws(b, Q).total : 0;
 }
 
 template <typename T>
 static mamba3_status launch_bwd_t(const mamba3_scan_bwd_args *b, hipStream_t st) {
     const mamba3_scan_args *a = &b->fwd;
-    const int Q = scan_bwd_chunk(a->dstate, a->headdim, a->rank);
+    bool mfma = false;
+    const int Q = bwd_path_chunk(a, &mfma);
     const BwdWs w = bwd_ws(b, Q);
     char *ws = (char *)b->workspace;
     BwdParams p;
@@ -821,12 +1610,20 @@ static mamba3_status launch_bwd_t(const mamba3_scan_bwd_args *b, hipStream_t st)
     p.seqlen = a->seqlen; p.H = a->nheads; p.G = a->ngroups; p.P = a->headdim; p.N = a->dstate; p.R = a->rank;
     p.Q = Q; p.norm = a->bc_norm; p.eps = a->bc_eps;
     const int64_t S = p.nseq, T_tok = (int64_t)a->batch * a->seqlen;
-    const size_t lds = scan_bwd_lds_bytes(p.N, p.P, p.R, Q);
-    if (hipFuncSetAttribute((const void *)k_scan_bwd<T>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-        hipSuccess)
-        return MAMBA3_EHIP;
     const int64_t nblk = S * p.H;
-    if (nblk > 0) hipLaunchKernelGGL(k_scan_bwd<T>, dim3((unsigned)nblk), dim3(256), lds, st, p);
+    if constexpr (std::is_same<T, bf16>::value) {
+        if (mfma) {
+            const mamba3_status ms = launch_bwd_mfma(p, nblk, st);
+            if (ms != MAMBA3_OK) return ms;
+        }
+    }
+    if (!mfma) {
+        const size_t lds = scan_bwd_lds_bytes(p.N, p.P, p.R, Q);
+        if (hipFuncSetAttribute((const void *)k_scan_bwd<T>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+            hipSuccess)
+            return MAMBA3_EHIP;
+        if (nblk > 0) hipLaunchKernelGGL(k_scan_bwd<T>, dim3((unsigned)nblk), dim3(kBwdThreads), lds, st, p);
+    }
     int64_t nred = (int64_t)p.H * p.N;
     if (grouped) nred = std::max(nred, std::max(T_tok * p.G * p.R * p.N, S * p.G * p.R * p.N));
     if (nred > 0) hipLaunchKernelGGL(k_bwd_reduce<T>, dim3((unsigned)((nred + 255) / 256)), dim3(256), 0, st, p, T_tok, (int32_t)S);
