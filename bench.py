@@ -57,10 +57,17 @@ def scan_flops(c):
     return c["batch"] * L * H * (R * R * (N + P) * (Q + 1) + 4 * R * N * P)
 
 
+# (N, P, R) -> chunk length of the MFMA backward (bf16 token inputs); mirrors the library's table
+BWD_MFMA_CHUNK = {(128, 64, 1): 32, (64, 64, 1): 32, (64, 64, 4): 8, (128, 64, 2): 16, (128, 64, 4): 8, (64, 64, 2): 16}
+
+
 def bwd_chunk(c):
-    """Chunk length the backward kernel picks (largest power of two <= 64 whose
-    LDS layout fits 160 KB; mirrors the library's choice)."""
+    """Chunk length of the backward that runs: the MFMA kernel's for bf16 inputs
+    of its shapes, else the VALU kernel's (largest power of two <= 64 whose LDS
+    layout fits 160 KB). Mirrors the library's choice."""
     N, P, R = c["dstate"], c["headdim"], c["rank"]
+    if c.get("dtype") == "bf16" and (N, P, R) in BWD_MFMA_CHUNK:
+        return BWD_MFMA_CHUNK[(N, P, R)]
     for q in (64, 32, 16, 8, 4, 2, 1):
         QR, K = q * R, N // 2
         wk = max(max(QR, K) * (P + 1), 512)
@@ -178,11 +185,12 @@ def bench_bwd(cfg, steps, warmup, dev):
     ws = torch.empty((need,), dtype=torch.uint8, device=dev)
     ms, wall = timed(step, steps, warmup, stream)
     q = bwd_chunk(c)
+    mfma = c.get("dtype") == "bf16" and (c["dstate"], c["headdim"], c["rank"]) in BWD_MFMA_CHUNK
     nbytes, flops = bwd_bytes(c), bwd_flops(c, q)
     tokens = c["batch"] * c["seqlen"]
     out = dict(workload=c["name"] + " backward", ms=ms, tokens_per_s=tokens / (ms * 1e-3), bytes=nbytes, flops=flops,
                chunk=q, workspace_bytes=need, hbm_gbs=nbytes / (ms * 1e-3) / 1e9,
-               alu_tfs=flops / (ms * 1e-3) / 1e12, wall_s=wall)
+               alu_tfs=flops / (ms * 1e-3) / 1e12, wall_s=wall, mfma=mfma)
     del d, dy, ws
     torch.cuda.empty_cache()
     return out
@@ -475,7 +483,7 @@ def main():
         res["mimo_block"] = bench_scan(2, args.steps, args.warmup, dev, block=True)
         print(f"# mimo scan + block {res['mimo_block']['ms']:.3f} ms", file=sys.stderr, flush=True)
     if args.only in ("bwd", "all"):
-        # the backward (fp32 VALU kernel): a few steps, each is a whole backward of the batch
+        # the backward: a few steps, each is a whole backward of the batch
         res["siso_bwd"] = bench_bwd(1, 3, 1, dev)
         print(f"# siso backward {res['siso_bwd']['ms']:.2f} ms", file=sys.stderr, flush=True)
         res["mimo_bwd"] = bench_bwd(2, 3, 1, dev)
@@ -529,12 +537,14 @@ def main():
     for k in ("siso_bwd", "mimo_bwd"):
         if k in res:
             r = res[k]
-            # binding roofline: fp32 vector arithmetic (the kernel computes on VALU) or HBM bytes
-            alu_bound = r["flops"] / (VALU_F32_PEAK_TFS * 1e12) > r["bytes"] / (HBM_PEAK_GBS * 1e9)
-            roof = ({"bound": "alu", "achieved": r["alu_tfs"], "peak": VALU_F32_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": r["alu_tfs"] / VALU_F32_PEAK_TFS, "hbm_gbs": r["hbm_gbs"]} if alu_bound else
+            # binding roofline: the kernel's arithmetic (bf16 MFMA, or fp32 vector for the VALU
+            # kernel) or HBM bytes, whichever needs more time at peak
+            cpeak, cname = (MFMA_BF16_PEAK_TFS, "mfma") if r["mfma"] else (VALU_F32_PEAK_TFS, "alu")
+            c_bound = r["flops"] / (cpeak * 1e12) > r["bytes"] / (HBM_PEAK_GBS * 1e9)
+            roof = ({"bound": cname, "achieved": r["alu_tfs"], "peak": cpeak, "unit": "TFLOP/s",
+                     "frac": r["alu_tfs"] / cpeak, "hbm_gbs": r["hbm_gbs"]} if c_bound else
                     {"bound": "hbm", "achieved": r["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": r["hbm_gbs"] / HBM_PEAK_GBS, "alu_tflops": r["alu_tfs"]})
+                     "frac": r["hbm_gbs"] / HBM_PEAK_GBS, "tflops": r["alu_tfs"], "tflops_peak": cpeak})
             roof.update(bytes_per_launch=r["bytes"], flops_per_launch=r["flops"], chunk=r["chunk"])
             sec[k] = {"workload": r["workload"], "ms": r["ms"], "tokens_per_s": r["tokens_per_s"],
                       "workspace_bytes": r["workspace_bytes"], "roofline": roof}

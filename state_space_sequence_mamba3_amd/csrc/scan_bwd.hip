@@ -802,7 +802,8 @@ struct BCfg {
     static constexpr int O_RPI = O_CPM + al(3 * QR * TQ * 4);       // float [QR][TN] dS inter partials
     static constexpr int O_RPC = O_RPI + al(QR * TN * 4);           // float [QR][TP] dc partials
     static constexpr int O_PHE = O_RPC + al(QR * TP * 4);           // float [K2][TP] dPhi_e partials
-    static constexpr int O_SMALL = O_PHE + al(K2 * TP * 4);         // previous token, carries, biases
+    static constexpr int O_TH = O_PHE + al(K2 * TP * 4);            // bf16 [Q][K2] theta of the chunk
+    static constexpr int O_SMALL = O_TH + al(Q * K2 * 2);           // previous token, carries, biases
     static constexpr int SMALL = 6 * R * N + 4 * R * P + R + 2 * N + 16 + 64;
     static constexpr int O_DCF = O_SMALL + al(SMALL * 4);           // float [QR][NF] dC~ (raw C staging)
     static constexpr int O_DBF = O_DCF + al(QR * NF * 4);           // float [QR][NF] dB~ (raw B staging)
@@ -836,10 +837,11 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     float *RPM = (float *)(smem + CF::O_RPM), *CPM = (float *)(smem + CF::O_CPM);
     float *CPG = CPM + QR * TQ, *CPD = CPG + QR * TQ;
     float *RPI = (float *)(smem + CF::O_RPI), *RPC = (float *)(smem + CF::O_RPC), *PHE = (float *)(smem + CF::O_PHE);
+    bf16 *TH = (bf16 *)(smem + CF::O_TH);
     float *SMALLp = (float *)(smem + CF::O_SMALL);
     float *Bp = SMALLp, *BpRaw = Bp + R * N, *Xp = BpRaw + R * N, *dBcIn = Xp + R * P, *dBcOut = dBcIn + R * N;
     float *dXcIn = dBcOut + R * N, *dXcOut = dXcIn + R * P, *INVBP = dXcOut + R * P, *BBA = INVBP + R;
-    float *CBA = BBA + N, *MISC = CBA + N, *RED = MISC + 16;
+    float *CBA = BBA + N, *MISC = CBA + N, *RED = MISC + 16, *TMPC = RED + 16;   // RED: 8 floats, TMPC: [Q]
     float *dCf = (float *)(smem + CF::O_DCF), *dBf = (float *)(smem + CF::O_DBF), *Sf = (float *)(smem + CF::O_SF);
     bf16 *Ct = (bf16 *)(smem + CF::O_CT), *Bt = (bf16 *)(smem + CF::O_BT), *Xb = (bf16 *)(smem + CF::O_XB);
     bf16 *XcB = (bf16 *)(smem + CF::O_XC), *dYb = (bf16 *)(smem + CF::O_DY), *EdYb = (bf16 *)(smem + CF::O_EDY);
@@ -887,50 +889,64 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     auto tile_n0 = [&](int v) { return ((wave * UPW + v) / TP) * 16; };
     auto tile_p0 = [&](int v) { return ((wave * UPW + v) % TP) * 16; };
 
+    // Prologue of `nrows` LDS rows (raw values on entry): 16 lanes per row, N/16 columns each
     auto prologue_rows = [&](float *rows, int nrows, int stride, const float *bias, float *invs) {
-        for (int r = tid; r < nrows; r += NT) {
-            float *v = rows + (int64_t)r * stride;
+        for (int r0 = tid >> 4; r0 < (nrows + NT / 16 - 1) / (NT / 16) * (NT / 16); r0 += NT / 16) {
+            const bool ok = r0 < nrows;   // (every lane of a group reaches the shuffles)
+            float *v = rows + (int64_t)(ok ? r0 : 0) * stride;
             float inv = 1.f;
             if (p.norm) {
                 float ss = 0.f;
-                for (int n = 0; n < N; n++) ss += v[n] * v[n];
+                for (int n = li; n < N; n += 16) ss += v[n] * v[n];
+                ss = sum16(ss);
                 inv = 1.f / sqrtf(ss / (float)N + p.eps);
             }
-            invs[r] = inv;
-            if (pro)
-                for (int n = 0; n < N; n++) v[n] = v[n] * inv + (bias ? bias[n] : 0.f);
+            if (ok) {
+                if (li == 0) invs[r0] = inv;
+                if (pro)
+                    for (int n = li; n < N; n += 16) v[n] = v[n] * inv + (bias ? bias[n] : 0.f);
+            }
         }
     };
     auto load_scalars = [&](int64_t c0, int nq) {
-        for (int t = tid; t < Q; t += NT) {
+        static_assert(Q <= 64, "one wave scans the chunk");
+        if (wave == 0) {   // per-token scalars and the log-decay prefix (wave scan)
+            const int t = lane;
             float dtv = 0.f, lv = 0.f;
             if (t < nq) {
                 dtv = ldt<bf16>(p.dt, (start + c0 + t) * H + h);
                 lv = ldt<bf16>(p.lam, (start + c0 + t) * H + h);
             }
-            DT[t] = dtv;
-            LM[t] = lv;
-            GM[t] = lv * dtv;
-            DL[t] = (1.f - lv) * dtv;
+            float acc = dtv * Ah;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(acc, off, 64);
+                if (lane >= off) acc += o;
+            }
+            const float dln = __shfl_down((1.f - lv) * dtv, 1, 64);
+            if (t < Q) {
+                DT[t] = dtv;
+                LM[t] = lv;
+                GM[t] = lv * dtv;
+                DL[t] = (1.f - lv) * dtv;
+                S[t] = acc;
+                G1[t] = lv * dtv + ((t + 1 < nq) ? dln : 0.f);
+            }
+        }
+        for (int e = tid; e < Q * K / 8; e += NT) {   // theta of the chunk (zero past the end), 16-byte pieces
+            const int t = e / (K / 8), k = (e % (K / 8)) * 8;
+            *(bf16x8 *)(TH + t * K + k) =
+                (t < nq) ? *(const bf16x8 *)((const bf16 *)p.theta + ((start + c0 + t) * H + h) * K + k) : bf16x8{};
         }
         __syncthreads();
-        if (tid == 0) {
+        for (int e = tid; e < Q * K; e += NT) {   // cumulative angles, one (token, pair) per thread
+            const int t = e / K, k = e % K;
             float acc = 0.f;
-            for (int t = 0; t < Q; t++) {
-                acc += DT[t] * Ah;
-                S[t] = acc;
-                G1[t] = GM[t] + ((t + 1 < nq) ? DL[t + 1] : 0.f);
-            }
-        }
-        for (int k = tid; k < K; k += NT) {
-            float acc = 0.f;
-            for (int t = 0; t < Q; t++) {
-                if (t < nq) acc += DT[t] * ldt<bf16>(p.theta, ((start + c0 + t) * H + h) * K + k);
-                float sn, cs;
-                sincosf(acc, &sn, &cs);
-                CS[t * K + k] = cs;
-                SN[t * K + k] = sn;
-            }
+            for (int u = 0; u <= t; u++) acc += DT[u] * (float)TH[u * K + k];
+            float sn, cs;
+            __sincosf(acc, &sn, &cs);   // hardware sin / cos: operands of bf16 products
+            CS[e] = cs;
+            SN[e] = sn;
         }
         __syncthreads();
         for (int e = tid; e < Q * Q; e += NT) {
@@ -966,27 +982,33 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     // B~ (and C~, dy in the reverse pass) and X, c o X of the chunk in bf16; raw B and C rows go
     // through fp32 staging (dBf, dCf) for the prologue and the rotation
     auto stage_chunk = [&](int64_t c0, int nq, bool rev) {
-        for (int e = tid; e < QR * N; e += NT) {
-            const int r = e / N, n = e % N, t = r / R, j = r % R;
-            float bv = 0.f, cv = 0.f;
+        for (int e = tid; e < QR * N / 8; e += NT) {   // 16-byte pieces
+            const int r = e / (N / 8), n = (e % (N / 8)) * 8, t = r / R, j = r % R;
+            bf16x8 bv = {}, cv = {};
             if (t < nq) {
                 const int64_t o = tokB(c0 + t) + j * N + n;
-                bv = (float)gB[o];
-                if (rev) cv = (float)gC[o];
+                bv = *(const bf16x8 *)(gB + o);
+                if (rev) cv = *(const bf16x8 *)(gC + o);
             }
-            dBf[r * NF + n] = bv;
-            if (rev) dCf[r * NF + n] = cv;
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                dBf[r * NF + n + m] = (float)bv[m];
+                if (rev) dCf[r * NF + n + m] = (float)cv[m];
+            }
         }
-        for (int e = tid; e < QR * P; e += NT) {
-            const int r = e / P, pp = e % P, t = r / R, j = r % R;
-            float xv = 0.f, dv = 0.f;
+        for (int e = tid; e < QR * P / 8; e += NT) {
+            const int r = e / (P / 8), pp = (e % (P / 8)) * 8, t = r / R, j = r % R;
+            bf16x8 xv = {}, dv = {};
             if (t < nq) {
-                xv = (float)gx[tokX(c0 + t) + j * P + pp];
-                if (rev) dv = (float)gdy[tokX(c0 + t) + j * P + pp];
+                xv = *(const bf16x8 *)(gx + tokX(c0 + t) + j * P + pp);
+                if (rev) dv = *(const bf16x8 *)(gdy + tokX(c0 + t) + j * P + pp);
             }
-            Xb[r * PS + pp] = (bf16)xv;
-            XcB[r * PS + pp] = (bf16)(CU[t] * xv);
-            if (rev) dYb[r * PS + pp] = (bf16)dv;
+            bf16x8 xc;
+#pragma unroll
+            for (int m = 0; m < 8; m++) xc[m] = (bf16)(CU[t] * (float)xv[m]);
+            *(bf16x8 *)(Xb + r * PS + pp) = xv;
+            *(bf16x8 *)(XcB + r * PS + pp) = xc;
+            if (rev) *(bf16x8 *)(dYb + r * PS + pp) = dv;
         }
         __syncthreads();
         prologue_rows(dBf, nq * R, NF, Bbh, INVB);
@@ -1291,53 +1313,60 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             }
             DPHI[t * K + k] += a;
         }
-        // per-token scalar gradients from the row / column partials (fixed order)
-        if (tid == 0) {
-            float dSe = ES[e_] * gh;
-            for (int u = 0; u < nq; u++) {
-                float rowA = 0.f, rowB = 0.f, colS = 0.f, colG = 0.f, colD = 0.f, dc = 0.f;
-                for (int j = 0; j < R; j++) {
-                    const int q = u * R + j;
-                    for (int x = 0; x < TN; x++) rowA += RPI[q * TN + x];
-                    for (int x = 0; x < TQ; x++) {
-                        rowB += RPM[q * TQ + x];
-                        colS += CPM[q * TQ + x];
-                        colG += CPG[q * TQ + x];
-                        colD += CPD[q * TQ + x];
-                    }
-                    for (int x = 0; x < TP; x++) dc += RPC[q * TP + x];
+        // per-token scalar gradients from the row / column partials (fixed order), one token per
+        // thread; the state coefficient's share of dS_e is summed after the barrier below
+        for (int u = tid; u < nq; u += NT) {
+            float rowA = 0.f, rowB = 0.f, colS = 0.f, colG = 0.f, colD = 0.f, dc = 0.f;
+            for (int j = 0; j < R; j++) {
+                const int q = u * R + j;
+                for (int x = 0; x < TN; x++) rowA += RPI[q * TN + x];
+                for (int x = 0; x < TQ; x++) {
+                    rowB += RPM[q * TQ + x];
+                    colS += CPM[q * TQ + x];
+                    colG += CPG[q * TQ + x];
+                    colD += CPD[q * TQ + x];
                 }
-                const float E = EM[e_ * Q + u];
-                const float cu = CU[u];
-                DS[u] += rowA + rowB - colS - dc * cu;
-                dSe += dc * cu;
-                DGM[u] += colG + dc * E;
-                if (u + 1 < nq) DDL[u + 1] += colD + dc * E;
+                for (int x = 0; x < TP; x++) dc += RPC[q * TP + x];
             }
-            DS[e_] += dSe;
+            const float E = EM[e_ * Q + u];
+            const float cu = CU[u];
+            DS[u] += rowA + rowB - colS - dc * cu;
+            TMPC[u] = dc * cu;
+            DGM[u] += colG + dc * E;
+            if (u + 1 < nq) DDL[u + 1] += colD + dc * E;
         }
         // the fold at the chunk start: d delta_0 = <dH', Bp Xp^T>, carries for the previous token
         float fold_acc = 0.f;
-        if (MISC[0] != 0.f) {
-            for (int e = tid; e < R * N; e += NT) {
-                const int j = e / N, n = e % N;
+        if (MISC[0] != 0.f) {   // 16 lanes per output element
+            constexpr int NG = NT / 16;
+            for (int e0 = tid >> 4; e0 < (R * N + NG - 1) / NG * NG; e0 += NG) {
+                const int e = e0 < R * N ? e0 : 0, j = e / N, n = e % N;
                 float a = 0.f;
-                for (int pp = 0; pp < P; pp++) a += (float)Gb[n * PS + pp] * Xp[j * P + pp];
-                dBcOut[e] = DL[0] * a;
-                fold_acc += Bp[e] * a;
+                for (int pp = li; pp < P; pp += 16) a += (float)Gb[n * PS + pp] * Xp[j * P + pp];
+                a = sum16(a);
+                if (e0 < R * N && li == 0) {
+                    dBcOut[e] = DL[0] * a;
+                    fold_acc += Bp[e] * a;
+                }
             }
-            for (int e = tid; e < R * P; e += NT) {
-                const int j = e / P, pp = e % P;
+            for (int e0 = tid >> 4; e0 < (R * P + NG - 1) / NG * NG; e0 += NG) {
+                const int e = e0 < R * P ? e0 : 0, j = e / P, pp = e % P;
                 float a = 0.f;
-                for (int n = 0; n < N; n++) a += (float)Gb[n * PS + pp] * Bp[j * N + n];
-                dXcOut[e] = DL[0] * a;
+                for (int n = li; n < N; n += 16) a += (float)Gb[n * PS + pp] * Bp[j * N + n];
+                a = sum16(a);
+                if (e0 < R * P && li == 0) dXcOut[e] = DL[0] * a;
             }
         } else {
             for (int e = tid; e < R * N; e += NT) dBcOut[e] = 0.f;
             for (int e = tid; e < R * P; e += NT) dXcOut[e] = 0.f;
         }
         const float fold = block_sum(fold_acc, RED);
-        if (tid == 0) DDL[0] += fold;
+        if (tid == 0) {
+            DDL[0] += fold;
+            float dSe = ES[e_] * gh;
+            for (int u = 0; u < nq; u++) dSe += TMPC[u];
+            DS[e_] += dSe;
+        }
         __syncthreads();
         for (int k = tid; k < K; k += NT) {
             float acc = 0.f;
@@ -1358,12 +1387,31 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             const int t = e / K, k = e % K;
             stt<bf16>(p.dtheta, ((start + c0 + t) * H + h) * K + k, DT[t] * DPHI[e]);
         }
-        for (int t = tid; t < nq; t += NT) {
-            float ddt = Ah * DS[t] + (1.f - LM[t]) * DDL[t] + LM[t] * DGM[t];
-            for (int k = 0; k < K; k++) ddt += ldt<bf16>(p.theta, ((start + c0 + t) * H + h) * K + k) * DPHI[t * K + k];
-            stt<bf16>(p.ddt, (start + c0 + t) * H + h, ddt);
-            stt<bf16>(p.dlam, (start + c0 + t) * H + h, DT[t] * (DGM[t] - DDL[t]));
-            dA_acc += DT[t] * DS[t];
+        for (int t0 = tid >> 4; t0 < (nq + NT / 16 - 1) / (NT / 16) * (NT / 16); t0 += NT / 16) {
+            const int t = t0 < nq ? t0 : 0;   // (every lane of a group reaches the shuffles)
+            float a = 0.f;
+            for (int k = li; k < K; k += 16) a += (float)TH[t * K + k] * DPHI[t * K + k];
+            a = sum16(a);
+            if (t0 < nq && li == 0) {
+                const float ddt = Ah * DS[t] + (1.f - LM[t]) * DDL[t] + LM[t] * DGM[t] + a;
+                stt<bf16>(p.ddt, (start + c0 + t) * H + h, ddt);
+                stt<bf16>(p.dlam, (start + c0 + t) * H + h, DT[t] * (DGM[t] - DDL[t]));
+                dA_acc += DT[t] * DS[t];
+            }
+        }
+        // raw B and C rows of the chunk again (for the prologue's backward), over C~ and B~
+        if (pro) {
+            for (int e = tid; e < QR * (N / 8); e += NT) {
+                const int r = e / (N / 8), col = (e % (N / 8)) * 8, t = r / R, j = r % R;
+                bf16x8 bv = {}, cv = {};
+                if (t < nq) {
+                    const int64_t o = tokB(c0 + t) + j * N + col;
+                    bv = *(const bf16x8 *)(gB + o);
+                    cv = *(const bf16x8 *)(gC + o);
+                }
+                *(bf16x8 *)(Bt + r * NS + col) = bv;
+                *(bf16x8 *)(Ct + r * NS + col) = cv;
+            }
         }
         // dB, dC back to the physical frame (+ the carry into the last token), through the prologue
         for (int e = tid; e < nq * K * R; e += NT) {
@@ -1392,23 +1440,29 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             BBA[n] += a;
             CBA[n] += b;
         }
-        for (int r = tid; r < 2 * nq * R; r += NT) {
+        // back through the prologue to the raw columns (16 lanes per row; raw rows in Bt / Ct)
+        for (int r0 = tid >> 4; r0 < (2 * nq * R + NT / 16 - 1) / (NT / 16) * (NT / 16); r0 += NT / 16) {
+            const bool ok = r0 < 2 * nq * R;
+            const int r = ok ? r0 : 0;
             const bool isC = r >= nq * R;
             const int rr = isC ? r - nq * R : r, t = rr / R, j = rr % R;
             const float *gout = (isC ? dCf : dBf) + rr * NF;
             const float inv = (isC ? INVC : INVB)[rr];
-            const bf16 *src = isC ? gC : gB;
-            const int64_t o = tokB(c0 + t) + j * N;
+            const bf16 *raw = (isC ? Ct : Bt) + rr * NS;
             float dot = 0.f;
-            if (p.norm)
-                for (int n = 0; n < N; n++) dot += gout[n] * (float)src[o + n];
+            if (p.norm) {
+                for (int n = li; n < N; n += 16) dot += gout[n] * (float)raw[n];
+                dot = sum16(dot);
+            }
             const float k3 = p.norm ? dot * inv * inv * inv / (float)N : 0.f;
             float *part = isC ? p.p_dC : p.p_dB;
-            for (int n = 0; n < N; n++) {
-                const float v = p.norm ? gout[n] * inv - k3 * (float)src[o + n] : gout[n];
-                if (part) part[((start + c0 + t) * H + h) * (int64_t)R * N + j * N + n] = v;
-                else stt<bf16>(isC ? p.dC : p.dB, o + n, v);
-            }
+            const int64_t o = tokB(c0 + t) + j * N;
+            if (ok)
+                for (int n = li; n < N; n += 16) {
+                    const float v = p.norm ? gout[n] * inv - k3 * (float)raw[n] : gout[n];
+                    if (part) part[((start + c0 + t) * H + h) * (int64_t)R * N + j * N + n] = v;
+                    else stt<bf16>(isC ? p.dC : p.dB, o + n, v);
+                }
         }
         for (int e = tid; e < R * N; e += NT) dBcIn[e] = dBcOut[e];
         for (int e = tid; e < R * P; e += NT) dXcIn[e] = dXcOut[e];
