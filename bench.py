@@ -357,7 +357,7 @@ def summarize_stats(stats_dir, out_md, command):
              "```", command, "```", "", "| kernel | calls | average us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
     other, other_ms = 0, 0.0
     for r in rows:
-        if "k_scan" not in r["Name"] and "k_decode" not in r["Name"]:
+        if "k_scan" not in r["Name"] and "k_decode" not in r["Name"] and "k_bwd" not in r["Name"]:
             other += 1
             other_ms += float(r["TotalDurationNs"]) / 1e6
             continue
@@ -400,7 +400,8 @@ def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 3
     kernels = {"scan_bf16": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, false>",)),
                "scan_bf16_block": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, true>",)),
                "decode": ("decode.hip", ("k_decode_colIDF16bLi64ELi4ELb0E", "k_decode_col<__bf16, 64, 4, false>")),
-               "decode_block": ("decode.hip", ("k_decode_colIDF16bLi64ELi4ELb1E", "k_decode_col<__bf16, 64, 4, true>"))}
+               "decode_block": ("decode.hip", ("k_decode_colIDF16bLi64ELi4ELb1E", "k_decode_col<__bf16, 64, 4, true>")),
+               "scan_bwd": ("scan_bwd.hip", ("BCfg<128, 64, 1, 32, 8>",))}
     md = ["# HBM traffic per launch from rocprofv3 counters", "", "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):",
           "", "```", *commands, "```", "",
           f"Calibration: a plain 1 GiB device copy reads {sum(copy_f) / len(copy_f) / 2**30:.4f} GiB by FETCH_SIZE and writes "
@@ -546,6 +547,8 @@ def main():
                     {"bound": "hbm", "achieved": r["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["hbm_gbs"] / HBM_PEAK_GBS, "tflops": r["alu_tfs"], "tflops_peak": cpeak})
             roof.update(bytes_per_launch=r["bytes"], flops_per_launch=r["flops"], chunk=r["chunk"])
+            if k == "siso_bwd":
+                roof["traffic"] = traffic_record("scan_bwd")
             sec[k] = {"workload": r["workload"], "ms": r["ms"], "tokens_per_s": r["tokens_per_s"],
                       "workspace_bytes": r["workspace_bytes"], "roofline": roof}
     for k in ("decode", "decode_block"):
