@@ -52,6 +52,12 @@
  * normalizes each rank column of B_t, C_t separately; the bias is [H, N],
  * shared by the rank columns; the skip term D x is added before the gate.
  *
+ * Variants (section "The Complex-Valued A Parameterization", Remark 1; Table 8
+ * of the paper listing): a per-token decay rate A_t [T, H] replaces the head's
+ * A (alpha_t = exp(dt_t A_t)), and a fixed trapezoid weight replaces the
+ * per-token lam (lam = 1/2 is the classical trapezoid, lam = 1 exponential-
+ * Euler).
+ *
  * Inputs are read through a dtype tag (f64, f32, bf16 bits) and converted
  * exactly to double; all arithmetic is in double / double complex.
  */
@@ -91,6 +97,9 @@ typedef struct {
     const void *z;             /* [T, H, R, P] gate (dtype in_dtype), or NULL: y <- y * SiLU(z) */
     int32_t bc_norm;           /* 1: every B and C column (N values) is scaled to unit RMS */
     double bc_eps;             /* added to the mean square under the root */
+    /* Variants: */
+    const void *A_tok;         /* [T, H] per-token decay rate A_t (dtype in_dtype), or NULL: A[h] */
+    double lam_fixed;          /* the trapezoid weight of every token when lam is NULL */
 } m3o_args;
 
 static inline double ld(const void *p, int dt, int64_t i) {
@@ -119,6 +128,17 @@ static void bc_row(const m3o_args *a, const void *src, int64_t off, int h, const
     }
     if (bias)
         for (int n = 0; n < N; n++) out[n] += bias[(int64_t)h * N + n];
+}
+
+/* The token's trapezoid weight lam_t, or the fixed one when no lam array is given
+ * (the fixed-lambda variants, Table 8 of the paper listing: lam = 1/2, lam = 1). */
+static inline double lam_of(const m3o_args *a, int64_t i) {
+    return a->lam ? ld(a->lam, a->in_dtype, i) : a->lam_fixed;
+}
+/* The token's decay rate A_t (data-dependent A, Remark 1, section "The Complex-Valued A
+ * Parameterization"), or the head's A when no per-token array is given. i = t * H + h. */
+static inline double A_of(const m3o_args *a, int64_t i, int h) {
+    return a->A_tok ? ld(a->A_tok, a->in_dtype, i) : a->A[h];
 }
 
 /* Output gating: y * SiLU(z) with SiLU(v) = v / (1 + e^{-v}) (section
@@ -163,15 +183,14 @@ static void o1_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
         for (int p = 0; p < P; p++)
             for (int j = 0; j < R; j++) xp[p * R + j] = ld(a->xprev, dtp, ox + j * P + p);
     }
-    const double Ah = a->A[h];
     const double Dh = a->D ? a->D[h] : 0.0;
 
     for (int64_t tt = 0; tt < len; tt++) {
         const int64_t t = t0 + tt;
         const double dt = ld(a->dt, dtp, t * H + h);
-        const double lam = ld(a->lam, dtp, t * H + h);
+        const double lam = lam_of(a, t * H + h);
         const double delta = (1.0 - lam) * dt, gamma = lam * dt;
-        const double decay = exp(dt * Ah);
+        const double decay = exp(dt * A_of(a, t * H + h, h));
         for (int k = 0; k < K; k++) {
             double ang = dt * ld(a->theta, dtp, (t * H + h) * K + k);
             z[k] = decay * (cos(ang) + I * sin(ang));
@@ -265,14 +284,13 @@ static void o2_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
         for (int p = 0; p < P; p++)
             for (int j = 0; j < R; j++) xp[p * R + j] = ld(a->xprev, dtp, ox + j * P + p);
     }
-    const double Ah = a->A[h];
     const double Dh = a->D ? a->D[h] : 0.0;
 
     for (int64_t tt = 0; tt < len; tt++) {
         const int64_t t = t0 + tt;
         const double dt = ld(a->dt, dtp, t * H + h);
-        const double lam = ld(a->lam, dtp, t * H + h);
-        const double alpha = exp(dt * Ah);
+        const double lam = lam_of(a, t * H + h);
+        const double alpha = exp(dt * A_of(a, t * H + h, h));
         const double beta = (1.0 - lam) * dt * alpha, gamma = lam * dt;
         for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, (t * H + h) * K + k);
         const int64_t ob = (t * G + g) * N * R, ox = (t * H + h) * P * R;
@@ -340,12 +358,12 @@ static void o3_slab(const m3o_args *a, int s, int h, double *y_slab) {
     double *X = malloc(T * P * R * sizeof *X);
     double *psi = calloc(K, sizeof *psi), *tmp = malloc((size_t)N * R * sizeof *tmp);
     double *row = malloc((size_t)N * sizeof *row);
-    const double Ah = a->A[h], Dh = a->D ? a->D[h] : 0.0;
+    const double Dh = a->D ? a->D[h] : 0.0;
 
     for (int64_t t = 0; t < T; t++) {
         const int64_t tg = t0 + t;
-        double dt = ld(a->dt, dtp, tg * H + h), lam = ld(a->lam, dtp, tg * H + h);
-        alpha[t] = exp(dt * Ah);
+        double dt = ld(a->dt, dtp, tg * H + h), lam = lam_of(a, tg * H + h);
+        alpha[t] = exp(dt * A_of(a, tg * H + h, h));
         beta[t] = (1.0 - lam) * dt * alpha[t];
         gamma[t] = lam * dt;
         for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, (tg * H + h) * K + k);
@@ -430,6 +448,7 @@ typedef struct {
     double *dxprev;        /* [nseq, H, R, P] */
     double *dB_bias, *dC_bias;   /* [H, N] */
     double *dz;            /* [T, H, R, P] */
+    double *dA_tok;        /* [T, H] (with a per-token A) */
 } m3o_grads;
 
 /* Backward of bc_row: gout = dL/d(out) for the N outputs; adds dL/d(raw column)
@@ -464,7 +483,7 @@ static void ob_slab(const m3o_args *a, const m3o_grads *gr, int s, int h, double
     const int dtp = a->in_dtype;
     const int64_t t0 = a->seq_start[s], L = a->seq_len[s];
     const size_t NP = (size_t)N * P, RN = (size_t)R * N, RP = (size_t)R * P;
-    const double Ah = a->A[h], Dh = a->D ? a->D[h] : 0.0;
+    const double Dh = a->D ? a->D[h] : 0.0;
     const int has_prev = a->Bprev && a->xprev;
     const int64_t Lm = L > 0 ? L : 1;
 
@@ -489,7 +508,8 @@ static void ob_slab(const m3o_args *a, const m3o_grads *gr, int s, int h, double
     double *U = malloc(NP * sizeof *U);
     for (int64_t t = 0; t < L; t++) {
         const int64_t tg = t0 + t;
-        const double dt = ld(a->dt, dtp, tg * H + h), lam = ld(a->lam, dtp, tg * H + h);
+        const double dt = ld(a->dt, dtp, tg * H + h), lam = lam_of(a, tg * H + h);
+        const double Ah = A_of(a, tg * H + h, h);
         const double alpha = exp(dt * Ah), delta = (1.0 - lam) * dt, gamma = lam * dt;
         const double *Hp = Hall + t * NP;
         double *Hn = Hall + (t + 1) * NP;
@@ -526,7 +546,8 @@ static void ob_slab(const m3o_args *a, const m3o_grads *gr, int s, int h, double
         for (size_t e = 0; e < NP; e++) Gm[e] = gr->dh_out[((int64_t)s * H + h) * NP + e];
     for (int64_t t = L - 1; t >= 0; t--) {
         const int64_t tg = t0 + t;
-        const double dt = ld(a->dt, dtp, tg * H + h), lam = ld(a->lam, dtp, tg * H + h);
+        const double dt = ld(a->dt, dtp, tg * H + h), lam = lam_of(a, tg * H + h);
+        const double Ah = A_of(a, tg * H + h, h);
         const double alpha = exp(dt * Ah), delta = (1.0 - lam) * dt, gamma = lam * dt;
         const double *Ht = Hall + (t + 1) * NP, *Hp = Hall + t * NP;
         const double *Bt = Be + t * RN, *Ct = Ce + t * RN, *Xt = X + t * RP;
@@ -608,8 +629,12 @@ static void ob_slab(const m3o_args *a, const m3o_grads *gr, int s, int h, double
             if (gr->dtheta) gr->dtheta[(tg * H + h) * K + k] += dt * dphi[k];
         }
         if (gr->ddt) gr->ddt[tg * H + h] += ddt;
-        if (gr->dlam) gr->dlam[tg * H + h] += dt * (dgamma - ddelta);
-        *dA_h += dt * alpha * dalpha;
+        if (gr->dlam && a->lam) gr->dlam[tg * H + h] += dt * (dgamma - ddelta);
+        if (a->A_tok) {
+            if (gr->dA_tok) gr->dA_tok[tg * H + h] += dt * alpha * dalpha;
+        } else {
+            *dA_h += dt * alpha * dalpha;
+        }
     }
     if (gr->dh_in)
         for (size_t e = 0; e < NP; e++) gr->dh_in[((int64_t)s * H + h) * NP + e] += Gm[e];
@@ -638,7 +663,7 @@ static void ob_slab(const m3o_args *a, const m3o_grads *gr, int s, int h, double
 static int check(const m3o_args *a) {
     if (!a || a->nseq < 0 || a->H <= 0 || a->G <= 0 || a->P <= 0 || a->N <= 0 || a->R <= 0) return 1;
     if (a->N % 2 || a->H % a->G) return 1;
-    if (!a->x || !a->dt || !a->lam || !a->theta || !a->B || !a->C || !a->A) return 1;
+    if (!a->x || !a->dt || !a->theta || !a->B || !a->C || (!a->A && !a->A_tok)) return 1;
     if (a->bc_norm && !(a->bc_eps >= 0.0)) return 1;
     return 0;
 }

@@ -11,7 +11,8 @@ All arrays use the flat token axis (padded batches are flattened to
 ``A, D [H]``, ``h_in [S,H,N,P]``, ``Bprev [S,G,R,N]``, ``xprev [S,H,R,P]``
 (rank-major: the R columns of B_t, X_t are stored one after another), and the
 optional block prologue/epilogue: ``B_bias, C_bias [H,N]``, ``z`` (like x),
-``bc_norm`` (bool) and ``bc_eps``.
+``bc_norm`` (bool) and ``bc_eps``; and the variants: ``A_tok`` (like dt: a
+per-token decay rate replacing A) and ``lam`` = None with ``lam_fixed``.
 Token inputs may be float64, float32 or uint16 (bf16 bit patterns); they are
 converted exactly to double inside the oracle.
 """
@@ -53,13 +54,14 @@ class _Args(ctypes.Structure):
         ("Bprev", ctypes.c_void_p), ("xprev", ctypes.c_void_p),
         ("B_bias", ctypes.c_void_p), ("C_bias", ctypes.c_void_p), ("z", ctypes.c_void_p),
         ("bc_norm", ctypes.c_int32), ("bc_eps", ctypes.c_double),
+        ("A_tok", ctypes.c_void_p), ("lam_fixed", ctypes.c_double),
     ]
 
 
 class _Grads(ctypes.Structure):
     _fields_ = [(k, ctypes.c_void_p) for k in (
         "dy", "dh_out", "dx", "ddt", "dlam", "dtheta", "dB", "dC", "dA", "dD", "dh_in", "dBprev", "dxprev",
-        "dB_bias", "dC_bias", "dz")]
+        "dB_bias", "dC_bias", "dz", "dA_tok")]
 
 
 _lib = None
@@ -103,9 +105,8 @@ class _Pack:
 
     def __init__(self, inp: dict, seq_start, seq_len):
         keep = {}
-        tok = [inp[k] for k in ("x", "dt", "lam", "theta", "B", "C")]
-        tag = _tag(tok[0])
-        for k in ("x", "dt", "lam", "theta", "B", "C", "Bprev", "xprev", "z"):
+        tag = _tag(inp["x"])
+        for k in ("x", "dt", "lam", "theta", "B", "C", "Bprev", "xprev", "z", "A_tok"):
             v = inp.get(k)
             if v is not None:
                 v = np.ascontiguousarray(v)
@@ -130,7 +131,8 @@ class _Pack:
                           _ptr(keep["B"]), _ptr(keep["C"]), _ptr(keep["A"]), _ptr(keep["D"]),
                           _ptr(keep["h_in"]), _ptr(keep["Bprev"]), _ptr(keep["xprev"]),
                           _ptr(keep["B_bias"]), _ptr(keep["C_bias"]), _ptr(keep["z"]),
-                          1 if inp.get("bc_norm") else 0, float(inp.get("bc_eps", 0.0)))
+                          1 if inp.get("bc_norm") else 0, float(inp.get("bc_eps", 0.0)),
+                          _ptr(keep["A_tok"]), float(inp.get("lam_fixed", 0.0)))
 
 
 def flatten(inp: dict) -> tuple[dict, np.ndarray, np.ndarray]:
@@ -138,7 +140,7 @@ def flatten(inp: dict) -> tuple[dict, np.ndarray, np.ndarray]:
     inputs (key ``cu_seqlens``, batch 1) take their table from cu_seqlens."""
     out = dict(inp)
     b, L = inp["x"].shape[0], inp["x"].shape[1]
-    for k in ("x", "dt", "lam", "theta", "B", "C", "z"):
+    for k in ("x", "dt", "lam", "theta", "B", "C", "z", "A_tok"):
         if inp.get(k) is not None:
             out[k] = inp[k].reshape((b * L,) + inp[k].shape[2:])
     if inp.get("cu_seqlens") is not None:
@@ -199,9 +201,14 @@ def scan_bwd(inp: dict, dy: np.ndarray, dh_out: np.ndarray | None = None, nthrea
     H, G, P, N, R, S = pk.H, pk.G, pk.P, pk.N, pk.R, pk.nseq
     dyf = np.ascontiguousarray(np.asarray(dy, dtype=np.float64).reshape(T, H, R, P))
     dho = None if dh_out is None else np.ascontiguousarray(dh_out, dtype=np.float64)
-    out = dict(dx=np.zeros((T, H, R, P)), ddt=np.zeros((T, H)), dlam=np.zeros((T, H)), dtheta=np.zeros((T, H, N // 2)),
-               dB=np.zeros((T, G, R, N)), dC=np.zeros((T, G, R, N)), dA=np.zeros(H), dD=np.zeros(H),
-               dh_in=np.zeros((S, H, N, P)))
+    out = dict(dx=np.zeros((T, H, R, P)), ddt=np.zeros((T, H)), dtheta=np.zeros((T, H, N // 2)),
+               dB=np.zeros((T, G, R, N)), dC=np.zeros((T, G, R, N)), dD=np.zeros(H), dh_in=np.zeros((S, H, N, P)))
+    if inp.get("lam") is not None:
+        out["dlam"] = np.zeros((T, H))
+    if inp.get("A_tok") is not None:
+        out["dA_tok"] = np.zeros((T, H))
+    else:
+        out["dA"] = np.zeros(H)
     if inp.get("Bprev") is not None:
         out["dBprev"], out["dxprev"] = np.zeros((S, G, R, N)), np.zeros((S, H, R, P))
     if inp.get("B_bias") is not None:
@@ -211,12 +218,14 @@ def scan_bwd(inp: dict, dy: np.ndarray, dh_out: np.ndarray | None = None, nthrea
     if inp.get("z") is not None:
         out["dz"] = np.zeros((T, H, R, P))
     g = _Grads(dyf.ctypes.data, _ptr(dho), *[_ptr(out.get(k)) for k in (
-        "dx", "ddt", "dlam", "dtheta", "dB", "dC", "dA", "dD", "dh_in", "dBprev", "dxprev", "dB_bias", "dC_bias", "dz")])
+        "dx", "ddt", "dlam", "dtheta", "dB", "dC", "dA", "dD", "dh_in", "dBprev", "dxprev", "dB_bias", "dC_bias", "dz",
+        "dA_tok")])
     if lib().m3o_scan_bwd(ctypes.byref(pk.args), ctypes.byref(g), nthreads):
         raise ValueError("oracle rejected its arguments")
-    shp = {k: inp[k].shape for k in ("x", "dt", "lam", "theta", "B", "C")}
-    for k, src in (("dx", "x"), ("ddt", "dt"), ("dlam", "lam"), ("dtheta", "theta"), ("dB", "B"), ("dC", "C")):
-        out[k] = out[k].reshape(shp[src])
+    for k, src in (("dx", "x"), ("ddt", "dt"), ("dlam", "dt"), ("dtheta", "theta"), ("dB", "B"), ("dC", "C"),
+                   ("dA_tok", "dt")):
+        if k in out:
+            out[k] = out[k].reshape(inp[src].shape)
     if "dz" in out:
         out["dz"] = out["dz"].reshape(inp["z"].shape)
     return out

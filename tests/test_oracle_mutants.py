@@ -10,7 +10,8 @@ norm's eps added outside the root, every head taking head 0's bias; and in
 the gradient: the rotation's transpose taken the wrong way, the angle
 derivative's sign, the previous-token weight dropped from its gradient, the
 norm's Jacobian reduced to its diagonal, the gate's derivative without its
-input factor, and the decay's share of the step's gradient dropped."""
+input factor, and the decay's share of the step's gradient dropped; in the variants, a
+per-token decay rate halved and the fixed trapezoid weight ignored."""
 import os
 import shutil
 import subprocess
@@ -50,6 +51,10 @@ MUTATIONS = {
     "grad_gate_without_input": ("dy0[i * P + p] = d * v * sg;", "dy0[i * P + p] = d * sg;"),
     "grad_decay_chain_dropped": ("double ddt = Ah * alpha * dalpha + (1.0 - lam) * ddelta + lam * dgamma;",
                                  "double ddt = (1.0 - lam) * ddelta + lam * dgamma;"),
+    "per_token_decay_halved": ("return a->A_tok ? ld(a->A_tok, a->in_dtype, i) : a->A[h];",
+                               "return a->A_tok ? 0.5 * ld(a->A_tok, a->in_dtype, i) : a->A[h];"),
+    "fixed_lambda_ignored": ("return a->lam ? ld(a->lam, a->in_dtype, i) : a->lam_fixed;",
+                             "return a->lam ? ld(a->lam, a->in_dtype, i) : 0.5;"),
     "stale_previous": ("memcpy(bp, bc, (size_t)K * R * sizeof *bp);\n        memcpy(xp, xc, (size_t)P * R * sizeof *xp);\n",
                        ""),
 }

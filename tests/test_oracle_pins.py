@@ -77,9 +77,12 @@ def _real_trapezoid(inp, use_rotation):
     update h = a R h + b R B_{t-1}x_{t-1}^T + c B_t x_t^T with explicit 2x2
     rotation matrices on the state pairs (Proposition 2's block-diagonal R_t),
     written with numpy matrices rather than complex numbers."""
-    x, dt, lam, th, B, C, A, D = (inp[k] for k in ("x", "dt", "lam", "theta", "B", "C", "A", "D"))
+    x, dt, th, B, C, D = (inp[k] for k in ("x", "dt", "theta", "B", "C", "D"))
     b, L, H, R, P = x.shape
     G, N = B.shape[2], B.shape[4]
+    # the variants: a per-token decay rate, a fixed trapezoid weight
+    A = inp["A_tok"] if inp.get("A_tok") is not None else np.broadcast_to(inp["A"], dt.shape)
+    lam = inp["lam"] if inp.get("lam") is not None else np.full(dt.shape, inp["lam_fixed"])
     y = np.zeros_like(x)
     for s in range(b):
         for h in range(H):
@@ -87,7 +90,7 @@ def _real_trapezoid(inp, use_rotation):
             st = np.zeros((N, P))
             prev = np.zeros((N, P))
             for t in range(L):
-                alpha = math.exp(dt[s, t, h] * A[h])
+                alpha = math.exp(dt[s, t, h] * A[s, t, h])
                 beta = (1 - lam[s, t, h]) * dt[s, t, h] * alpha
                 gamma = lam[s, t, h] * dt[s, t, h]
                 Rt = np.zeros((N, N))
@@ -121,6 +124,35 @@ def test_rotation_with_block_diagonal_matrices(oracle):
     inp = rand_inputs(rng, b=1, L=15, H=2, G=2, P=3, N=6, R=2, scale_theta=2.0)
     y1, _ = oracle.scan(inp, form=1)
     assert relerr(y1, _real_trapezoid(inp, use_rotation=True)) < 1e-12
+
+
+@pytest.mark.parametrize("form", [1, 2])
+def test_per_token_decay(oracle, form):
+    """A data-dependent decay rate A_t (Remark 1: alpha_t = exp(dt_t A_t), with
+    A_t computed per token like dt) against the independent real recurrence,
+    rotation included; the SSD matrix form agrees too."""
+    rng = np.random.default_rng(9)
+    inp = rand_inputs(rng, b=2, L=13, H=2, G=1, P=3, N=4, R=2, scale_theta=1.5)
+    inp["A_tok"] = -np.exp(rng.normal(0, 0.7, inp["dt"].shape))
+    inp["A"] = None
+    y, _ = oracle.scan(inp, form=form)
+    assert relerr(y, _real_trapezoid(inp, use_rotation=True)) < 1e-12
+    y3, _ = oracle.scan_slab(inp, 1, 1, form=3, want_state=False)
+    assert relerr(y3, y[1, :, 1]) < 1e-12
+
+
+@pytest.mark.parametrize("lam_fixed", [0.5, 1.0, 0.3])
+def test_fixed_lambda(oracle, lam_fixed):
+    """No lam array: every token uses the fixed weight (Table 8 of the paper
+    listing: lam = 1/2, the classical trapezoid; lam = 1, exponential-Euler),
+    against the independent real recurrence, and against O2."""
+    rng = np.random.default_rng(10)
+    inp = rand_inputs(rng, b=1, L=11, H=2, G=2, P=2, N=4, R=1, scale_theta=1.5)
+    inp["lam"], inp["lam_fixed"] = None, lam_fixed
+    y1, h1 = oracle.scan(inp, form=1)
+    assert relerr(y1, _real_trapezoid(inp, use_rotation=True)) < 1e-12
+    y2, h2 = oracle.scan(inp, form=2)
+    assert relerr(y2, y1) < 1e-12 and relerr(h2, h1) < 1e-12
 
 
 def test_lambda_one_is_exponential_euler(oracle):
@@ -466,7 +498,7 @@ def test_prologue_and_gate_in_decode(oracle):
 # loss L = sum(dy * y) + sum(dh * h_out).
 GRAD_KEYS = (("x", "dx"), ("dt", "ddt"), ("lam", "dlam"), ("theta", "dtheta"), ("B", "dB"), ("C", "dC"),
              ("A", "dA"), ("D", "dD"), ("h_in", "dh_in"), ("Bprev", "dBprev"), ("xprev", "dxprev"),
-             ("B_bias", "dB_bias"), ("C_bias", "dC_bias"), ("z", "dz"))
+             ("B_bias", "dB_bias"), ("C_bias", "dC_bias"), ("z", "dz"), ("A_tok", "dA_tok"))
 
 
 def fd_check(oracle, inp, rng, with_dh=True, tol=2e-7):
@@ -524,6 +556,16 @@ def test_gradient_packed(oracle):
     inp["Bprev"] = rng.standard_normal((4, 2, 2, 4))
     inp["xprev"] = rng.standard_normal((4, 2, 2, 2))
     assert fd_check(oracle, inp, rng) == 11
+
+
+def test_gradient_variants(oracle):
+    """Per-token decay rate (dA_t per token) and a fixed trapezoid weight (no dlam)."""
+    rng = np.random.default_rng(85)
+    inp = rand_inputs(rng, b=1, L=7, H=2, G=1, P=2, N=4, R=2, state=True, prev=True)
+    inp["A_tok"] = -np.exp(rng.normal(0, 0.7, inp["dt"].shape))
+    inp["A"] = None
+    inp["lam"], inp["lam_fixed"] = None, 0.5
+    assert fd_check(oracle, inp, rng) == 10
 
 
 def test_gradient_norm_eps_zero(oracle):
