@@ -71,7 +71,7 @@ def bwd_chunk(c):
     for q in (64, 32, 16, 8, 4, 2, 1):
         QR, K = q * R, N // 2
         wk = max(max(QR, K) * (P + 1), 512)
-        o = 3 * q * K + 11 * q + q * q + 7 * QR
+        o = 3 * q * K + 12 * q + q * q + 7 * QR
         o = (o + 3) & ~3
         o += 4 * QR * (N + 1) + 2 * QR * (P + 1) + 2 * N * (P + 1) + 2 * QR * (QR + 1) + 2 * wk
         o += 4 * R * N + 3 * R * P + R + 2 * N + 16

@@ -68,6 +68,17 @@
  * The normalisation and biases act before the rotation; the recurrence is
  * otherwise unchanged. y must not alias z or a bias; the states must not
  * alias them either.
+ *
+ * Variants (ABI 1.3, fields A_tok and lam_fixed of both argument structs):
+ *   A_tok        per-token decay rate in the token dtype, layout of dt, or NULL.
+ *                When given, alpha_t = exp(dt_t A_tok_t) and A is not read (it
+ *                may be NULL): the data-dependent A of Remark 1 (section "The
+ *                Complex-Valued A Parameterization"), which the pages make the
+ *                default of Mamba-3.
+ *   lam == NULL  every token uses the trapezoid weight lam_fixed (finite): the
+ *                fixed-lambda variants of the pages' ablation (Table 8 of the
+ *                paper listing: 1/2 is the classical trapezoid rule, 1 the
+ *                exponential-Euler rule of Mamba-2).
  */
 #ifndef MAMBA3_H
 #define MAMBA3_H
@@ -128,6 +139,9 @@ typedef struct {
     const void *z;
     int32_t bc_norm;
     float bc_eps;
+    /* Variants (ABI 1.3; see below). */
+    const void *A_tok;
+    float lam_fixed;
 } mamba3_scan_args;
 
 /* Pure host check of every argument (no HIP call). */
@@ -152,8 +166,10 @@ mamba3_status mamba3_scan_fwd(const mamba3_scan_args *args, void *stream);
  * dy        dL/dy, layout and dtype of x (required when there are tokens).
  * dh_out    [S, H, N, P] fp32 dL/dh_out, or NULL (zero).
  * Outputs, overwritten, in the layout and dtype of the matching input:
- *   dx, ddt, dlam, dtheta, dB, dC (required when there are tokens);
- *   dA [H] fp32 (required); dD [H] fp32 or NULL;
+ *   dx, ddt, dtheta, dB, dC (required when there are tokens);
+ *   dA [H] fp32 (required unless fwd.A_tok is given: then dA_tok is, and
+ *   dA is not written); dD [H] fp32 or NULL;
+ *   dlam is required only when fwd.lam is given (a fixed weight has none);
  *   dh_in [S, H, N, P] fp32 or NULL;
  *   dBprev, dxprev: both or neither, and only with Bprev/xprev;
  *   dB_bias, dC_bias [H, N] fp32, each only with its bias (or NULL);
@@ -178,6 +194,7 @@ typedef struct {
     void *dz;
     void *workspace;
     size_t workspace_bytes;
+    void *dA_tok;    /* ABI 1.3: with fwd.A_tok, dL/dA_tok (layout and dtype of A_tok) */
 } mamba3_scan_bwd_args;
 
 mamba3_status mamba3_scan_bwd_validate(const mamba3_scan_bwd_args *args);
@@ -204,6 +221,9 @@ typedef struct {
     const void *z;
     int32_t bc_norm;
     float bc_eps;
+    /* Variants (ABI 1.3; see below). */
+    const void *A_tok;
+    float lam_fixed;
 } mamba3_decode_args;
 
 mamba3_status mamba3_decode_validate(const mamba3_decode_args *args);

@@ -31,6 +31,7 @@ class ScanArgs(ctypes.Structure):
         ("A", _vp), ("D", _vp), ("h_in", _vp), ("Bprev", _vp), ("xprev", _vp),
         ("y", _vp), ("h_out", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("B_bias", _vp), ("C_bias", _vp), ("z", _vp), ("bc_norm", _i32), ("bc_eps", ctypes.c_float),
+        ("A_tok", _vp), ("lam_fixed", ctypes.c_float),
     ]
 
 
@@ -42,6 +43,7 @@ class DecodeArgs(ctypes.Structure):
         ("x", _vp), ("dt", _vp), ("lam", _vp), ("theta", _vp), ("B", _vp), ("C", _vp),
         ("Bprev", _vp), ("xprev", _vp), ("A", _vp), ("D", _vp), ("h", _vp), ("y", _vp),
         ("B_bias", _vp), ("C_bias", _vp), ("z", _vp), ("bc_norm", _i32), ("bc_eps", ctypes.c_float),
+        ("A_tok", _vp), ("lam_fixed", ctypes.c_float),
     ]
 
 
@@ -52,6 +54,7 @@ class ScanBwdArgs(ctypes.Structure):
         ("dx", _vp), ("ddt", _vp), ("dlam", _vp), ("dtheta", _vp), ("dB", _vp), ("dC", _vp),
         ("dA", _vp), ("dD", _vp), ("dh_in", _vp), ("dBprev", _vp), ("dxprev", _vp),
         ("dB_bias", _vp), ("dC_bias", _vp), ("dz", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("dA_tok", _vp),
     ]
 
 
@@ -126,7 +129,7 @@ def _stream(stream):
 
 def scan_args(x, dt, lam, theta, B, C, A, D=None, *, y, h_in=None, h_out=None, Bprev=None, xprev=None,
               cu_seqlens=None, chunk=64, B_bias=None, C_bias=None, z=None, bc_norm=False,
-              bc_eps=1e-5) -> ScanArgs:
+              bc_eps=1e-5, A_tok=None, lam_fixed=0.5) -> ScanArgs:
     """Builds a ScanArgs from tensors in the library's layouts (see mamba3.h)."""
     b, L, H, R, P = x.shape
     G, N = B.shape[2], B.shape[4]
@@ -134,7 +137,8 @@ def scan_args(x, dt, lam, theta, B, C, A, D=None, *, y, h_in=None, h_out=None, B
     return ScanArgs(b, L, H, P, N, R, G, chunk, _dtype_code(x), _ptr(cu_seqlens), nseq,
                     _ptr(x), _ptr(dt), _ptr(lam), _ptr(theta), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
                     _ptr(h_in), _ptr(Bprev), _ptr(xprev), _ptr(y), _ptr(h_out), None, 0,
-                    _ptr(B_bias), _ptr(C_bias), _ptr(z), int(bool(bc_norm)), float(bc_eps))
+                    _ptr(B_bias), _ptr(C_bias), _ptr(z), int(bool(bc_norm)), float(bc_eps), _ptr(A_tok),
+                    float(lam_fixed))
 
 
 def mamba3_scan_validate(args: ScanArgs) -> int:
@@ -147,11 +151,13 @@ def mamba3_scan_workspace_size(args: ScanArgs) -> int:
 
 def mamba3_scan_fwd(x, dt, lam, theta, B, C, A, D=None, *, y=None, h_in=None, h_out=None, Bprev=None,
                     xprev=None, cu_seqlens=None, chunk=64, want_state=True, stream=None, B_bias=None,
-                    C_bias=None, z=None, bc_norm=False, bc_eps=1e-5):
+                    C_bias=None, z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5):
     """Chunked scan over whole sequences. Tensors are device tensors in the
     layouts of mamba3.h; y and h_out are allocated when not given. Returns
     (y, h_out). B_bias, C_bias ([H, N] fp32), z (layout of x) and bc_norm /
-    bc_eps switch on the fused B/C normalisation, B/C biases and output gate."""
+    bc_eps switch on the fused B/C normalisation, B/C biases and output gate;
+    A_tok (layout of dt) replaces A with a per-token decay rate, and lam=None
+    uses lam_fixed for every token."""
     import torch
     if y is None:
         y = torch.empty_like(x)
@@ -160,7 +166,7 @@ def mamba3_scan_fwd(x, dt, lam, theta, B, C, A, D=None, *, y=None, h_in=None, h_
         h_out = torch.empty((S, x.shape[2], B.shape[4], x.shape[4]), dtype=torch.float32, device=x.device)
     a = scan_args(x, dt, lam, theta, B, C, A, D, y=y, h_in=h_in, h_out=h_out, Bprev=Bprev, xprev=xprev,
                   cu_seqlens=cu_seqlens, chunk=chunk, B_bias=B_bias, C_bias=C_bias, z=z, bc_norm=bc_norm,
-                  bc_eps=bc_eps)
+                  bc_eps=bc_eps, A_tok=A_tok, lam_fixed=lam_fixed)
     st = lib().mamba3_scan_fwd(ctypes.byref(a), _stream(stream))
     if st != MAMBA3_OK:
         raise Mamba3Error(st, "mamba3_scan_fwd")
@@ -177,7 +183,7 @@ def mamba3_scan_bwd_workspace_size(args: ScanBwdArgs) -> int:
 
 def mamba3_scan_bwd(x, dt, lam, theta, B, C, A, D=None, *, dy, dh_out=None, h_in=None, Bprev=None, xprev=None,
                     cu_seqlens=None, chunk=64, B_bias=None, C_bias=None, z=None, bc_norm=False, bc_eps=1e-5,
-                    want_dD=True, want_dh_in=True, workspace=None, stream=None):
+                    A_tok=None, lam_fixed=0.5, want_dD=True, want_dh_in=True, workspace=None, stream=None):
     """Gradients of the scan. Takes the forward's inputs plus dy (layout of
     x) and dh_out ([S,H,N,P] fp32 or None); returns a dict of gradients shaped
     like the inputs (dx, ddt, dlam, dtheta, dB, dC; dA, dD fp32 [H]; dh_in;
@@ -186,13 +192,18 @@ def mamba3_scan_bwd(x, dt, lam, theta, B, C, A, D=None, *, dy, dh_out=None, h_in
     import torch
     fwd = scan_args(x, dt, lam, theta, B, C, A, D, y=None, h_in=h_in, h_out=None, Bprev=Bprev, xprev=xprev,
                     cu_seqlens=cu_seqlens, chunk=chunk, B_bias=B_bias, C_bias=C_bias, z=z, bc_norm=bc_norm,
-                    bc_eps=bc_eps)
+                    bc_eps=bc_eps, A_tok=A_tok, lam_fixed=lam_fixed)
     S = int(cu_seqlens.numel()) - 1 if cu_seqlens is not None else x.shape[0]
     H, N, P = x.shape[2], B.shape[4], x.shape[4]
     f32 = dict(dtype=torch.float32, device=x.device)
-    g = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt), dlam=torch.empty_like(lam),
-             dtheta=torch.empty_like(theta), dB=torch.empty_like(B), dC=torch.empty_like(C),
-             dA=torch.empty((H,), **f32))
+    g = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt), dtheta=torch.empty_like(theta),
+             dB=torch.empty_like(B), dC=torch.empty_like(C))
+    if lam is not None:
+        g["dlam"] = torch.empty_like(lam)
+    if A_tok is not None:
+        g["dA_tok"] = torch.empty_like(A_tok)
+    else:
+        g["dA"] = torch.empty((H,), **f32)
     if want_dD:
         g["dD"] = torch.empty((H,), **f32)
     if want_dh_in:
@@ -207,7 +218,7 @@ def mamba3_scan_bwd(x, dt, lam, theta, B, C, A, D=None, *, dy, dh_out=None, h_in
         g["dz"] = torch.empty_like(z)
     a = ScanBwdArgs(fwd, _ptr(dy), _ptr(dh_out), *[_ptr(g.get(k)) for k in (
         "dx", "ddt", "dlam", "dtheta", "dB", "dC", "dA", "dD", "dh_in", "dBprev", "dxprev", "dB_bias", "dC_bias",
-        "dz")], None, 0)
+        "dz")], None, 0, _ptr(g.get("dA_tok")))
     need = lib().mamba3_scan_bwd_workspace_size(ctypes.byref(a))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
@@ -219,12 +230,13 @@ def mamba3_scan_bwd(x, dt, lam, theta, B, C, A, D=None, *, dy, dh_out=None, h_in
 
 
 def decode_args(x, dt, lam, theta, B, C, A, D=None, *, h, y, Bprev=None, xprev=None, B_bias=None, C_bias=None,
-                z=None, bc_norm=False, bc_eps=1e-5) -> DecodeArgs:
+                z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5) -> DecodeArgs:
     b, H, R, P = x.shape
     G, N = B.shape[1], B.shape[3]
     return DecodeArgs(b, H, P, N, R, G, _dtype_code(x), _ptr(x), _ptr(dt), _ptr(lam), _ptr(theta), _ptr(B),
                       _ptr(C), _ptr(Bprev), _ptr(xprev), _ptr(A), _ptr(D), _ptr(h), _ptr(y),
-                      _ptr(B_bias), _ptr(C_bias), _ptr(z), int(bool(bc_norm)), float(bc_eps))
+                      _ptr(B_bias), _ptr(C_bias), _ptr(z), int(bool(bc_norm)), float(bc_eps), _ptr(A_tok),
+                      float(lam_fixed))
 
 
 def mamba3_decode_validate(args: DecodeArgs) -> int:
@@ -232,14 +244,14 @@ def mamba3_decode_validate(args: DecodeArgs) -> int:
 
 
 def mamba3_decode_step(x, dt, lam, theta, B, C, A, D=None, *, h, y=None, Bprev=None, xprev=None, stream=None,
-                       B_bias=None, C_bias=None, z=None, bc_norm=False, bc_eps=1e-5):
+                       B_bias=None, C_bias=None, z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5):
     """One decode step; h (fp32 [batch,H,N,P]) is updated in place. Returns y.
     The prologue / epilogue keywords are those of mamba3_scan_fwd."""
     import torch
     if y is None:
         y = torch.empty_like(x)
     a = decode_args(x, dt, lam, theta, B, C, A, D, h=h, y=y, Bprev=Bprev, xprev=xprev, B_bias=B_bias,
-                    C_bias=C_bias, z=z, bc_norm=bc_norm, bc_eps=bc_eps)
+                    C_bias=C_bias, z=z, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=A_tok, lam_fixed=lam_fixed)
     st = lib().mamba3_decode_step(ctypes.byref(a), _stream(stream))
     if st != MAMBA3_OK:
         raise Mamba3Error(st, "mamba3_decode_step")

@@ -19,6 +19,9 @@
 // "Architectural Integration"): each staged B, C and Bprev column is scaled to
 // unit RMS and gets the head's bias before the update, and y is multiplied by
 // SiLU(z) after the D term.
+//
+// Variants: a per-row decay rate A_t replaces the head's A, and without a lam
+// array every row uses the fixed trapezoid weight.
 #include "m3_common.h"
 
 namespace m3 {
@@ -33,6 +36,8 @@ struct DecodeParams {
     const void *z;          // output gate (token dtype), or NULL
     int32_t norm;           // 1: B, C, Bprev columns scaled to unit RMS
     float eps;
+    const void *A_tok;      // per-row decay rate [batch, H] (token dtype), or NULL: A per head
+    float lam_fixed;        // trapezoid weight of every row when lam is NULL
 };
 
 // Stand-in for an absent bias row or gate (read-only zeros), so that prologue loads are
@@ -94,10 +99,11 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
         stage_f32<T, TPB>(sXp, (const T *)pr.xprev + ox, P * R, tid, 3 * CB + CX + CT);
     }
     const float dt = to_f(((const T *)pr.dt)[bh]);
-    const float lam = to_f(((const T *)pr.lam)[bh]);
+    const float lam = pr.lam ? to_f(((const T *)pr.lam)[bh]) : pr.lam_fixed;
+    const float Ah = pr.A_tok ? to_f(((const T *)pr.A_tok)[bh]) : pr.A[hh];
     // fp32 inputs take the precise exp and sincos, bf16 inputs the hardware approximations
     constexpr bool FAST = sizeof(T) == 2;
-    const float alpha = FAST ? __expf(dt * pr.A[hh]) : expf(dt * pr.A[hh]);
+    const float alpha = FAST ? __expf(dt * Ah) : expf(dt * Ah);
     const float delta = (1.f - lam) * dt, gamma = lam * dt;
     const float Dh = pr.D ? pr.D[hh] : 0.f;
     const bool has_prev = pr.Bprev != nullptr;
@@ -253,8 +259,8 @@ __global__ __launch_bounds__(N / 16 * 64) __attribute__((amdgpu_waves_per_eu(8))
     }
     const T thr = ((const T *)pr.theta)[(int64_t)bh * (N / 2) + min(tid, N / 2 - 1)];
     const float dt = to_f(((const T *)pr.dt)[bh]);
-    const float lam = to_f(((const T *)pr.lam)[bh]);
-    const float Ah = pr.A[hh];
+    const float lam = pr.lam ? to_f(((const T *)pr.lam)[bh]) : pr.lam_fixed;
+    const float Ah = pr.A_tok ? to_f(((const T *)pr.A_tok)[bh]) : pr.A[hh];
     const float Dh = pr.D ? pr.D[hh] : 0.f;
 
     float st[ROWS];
@@ -379,7 +385,7 @@ static void launch_kernel(const DecodeParams &p, int64_t nblk, hipStream_t st) {
 template <typename T, int N, int P, int R>
 static mamba3_status launch_one(const mamba3_decode_args *a, hipStream_t st) {
     DecodeParams p{a->x, a->dt, a->lam, a->theta, a->B, a->C, a->Bprev, a->xprev, a->A, a->D, a->h, a->y,
-                   a->nheads, a->ngroups, a->B_bias, a->C_bias, a->z, a->bc_norm, a->bc_eps};
+                   a->nheads, a->ngroups, a->B_bias, a->C_bias, a->z, a->bc_norm, a->bc_eps, a->A_tok, a->lam_fixed};
     int64_t nblk = (int64_t)a->batch * a->nheads;
     if (nblk == 0) return MAMBA3_OK;
     if (a->bc_norm || a->B_bias || a->C_bias || a->z)

@@ -52,7 +52,7 @@ const char *mamba3_status_string(mamba3_status s) {
     return "unknown status";
 }
 
-int32_t mamba3_version(void) { return 10200; }
+int32_t mamba3_version(void) { return 10300; }
 
 // Every check of the scan arguments except the availability of a forward kernel.
 static mamba3_status scan_args_check(const mamba3_scan_args *a) {
@@ -68,14 +68,16 @@ static mamba3_status scan_args_check(const mamba3_scan_args *a) {
     const int64_t T = (int64_t)a->batch * a->seqlen;
     if (S * a->nheads > INT32_MAX) return MAMBA3_EINVAL;
     if ((a->Bprev == nullptr) != (a->xprev == nullptr)) return MAMBA3_EINVAL;
-    if (T > 0 && (!a->x || !a->dt || !a->lam || !a->theta || !a->B || !a->C || !a->y)) return MAMBA3_EINVAL;
-    if (!a->A) return MAMBA3_EINVAL;
+    if (T > 0 && (!a->x || !a->dt || !a->theta || !a->B || !a->C || !a->y)) return MAMBA3_EINVAL;
+    if (!a->A && !a->A_tok) return MAMBA3_EINVAL;
+    if (!a->lam && !std::isfinite(a->lam_fixed)) return MAMBA3_EINVAL;
+    if (a->A_tok && !aligned_elem(a->A_tok, a->dtype)) return MAMBA3_EALIGN;
     if (a->workspace_bytes > 0 && !a->workspace) return MAMBA3_EWORKSPACE;
     const void *al16[] = {a->x, a->theta, a->B, a->C, a->y, a->h_in, a->h_out, a->Bprev, a->xprev};
     for (const void *p : al16)
         if (p && !aligned16(p)) return MAMBA3_EALIGN;
     if (!aligned_elem(a->dt, a->dtype) || !aligned_elem(a->lam, a->dtype)) return MAMBA3_EALIGN;
-    if (!aligned4(a->A) || (a->D && !aligned4(a->D)) || (a->cu_seqlens && !aligned4(a->cu_seqlens)))
+    if ((a->A && !aligned4(a->A)) || (a->D && !aligned4(a->D)) || (a->cu_seqlens && !aligned4(a->cu_seqlens)))
         return MAMBA3_EALIGN;
     mamba3_status pst = check_prologue(a->bc_norm, a->bc_eps, a->B_bias, a->C_bias, a->z);
     if (pst != MAMBA3_OK) return pst;
@@ -88,12 +90,12 @@ static mamba3_status scan_args_check(const mamba3_scan_args *a) {
                    span(a->C, T * G * N * R, es), span(a->h_in, S * H * N * P, 4),
                    span(a->Bprev, S * G * N * R, es), span(a->xprev, S * H * P * R, es),
                    span(a->h_out, S * H * N * P, 4), span(a->B_bias, H * N, 4), span(a->C_bias, H * N, 4),
-                   span(a->z, T * H * P * R, es)};
+                   span(a->z, T * H * P * R, es), span(a->A_tok, T * H, es)};
     for (Range r : ins)
         if (overlaps(y, r)) return MAMBA3_EINVAL;
     // h_out may be h_in exactly, but no other overlap with an input
     Range ho = span(a->h_out, S * H * N * P, 4);
-    Range ins2[] = {ins[0], ins[1], ins[2], ins[3], ins[4], ins[5], ins[7], ins[8], ins[10], ins[11], ins[12]};
+    Range ins2[] = {ins[0], ins[1], ins[2], ins[3], ins[4], ins[5], ins[7], ins[8], ins[10], ins[11], ins[12], ins[13]};
     for (Range r : ins2)
         if (overlaps(ho, r)) return MAMBA3_EINVAL;
     if (a->h_in && a->h_out && a->h_in != a->h_out && overlaps(ins[6], ho)) return MAMBA3_EINVAL;
@@ -140,8 +142,12 @@ mamba3_status mamba3_scan_bwd_validate(const mamba3_scan_bwd_args *b) {
     const mamba3_scan_args *a = &b->fwd;
     const int64_t S = a->cu_seqlens ? a->nseq : a->batch, T = (int64_t)a->batch * a->seqlen;
     const int64_t H = a->nheads, G = a->ngroups, P = a->headdim, N = a->dstate, R = a->rank;
-    if (T > 0 && (!b->dx || !b->ddt || !b->dlam || !b->dtheta || !b->dB || !b->dC)) return MAMBA3_EINVAL;
-    if (!b->dA) return MAMBA3_EINVAL;
+    if (T > 0 && (!b->dx || !b->ddt || !b->dtheta || !b->dB || !b->dC)) return MAMBA3_EINVAL;
+    if (T > 0 && a->lam && !b->dlam) return MAMBA3_EINVAL;
+    if (!a->A_tok && !b->dA) return MAMBA3_EINVAL;
+    if (a->A_tok && T > 0 && !b->dA_tok) return MAMBA3_EINVAL;
+    if (b->dA_tok && !a->A_tok) return MAMBA3_EINVAL;
+    if (b->dA_tok && !aligned_elem(b->dA_tok, a->dtype)) return MAMBA3_EALIGN;
     if ((b->dBprev == nullptr) != (b->dxprev == nullptr)) return MAMBA3_EINVAL;
     if (b->dBprev && !a->Bprev) return MAMBA3_EINVAL;
     if ((b->dB_bias && !a->B_bias) || (b->dC_bias && !a->C_bias) || (b->dz && !a->z)) return MAMBA3_EINVAL;
@@ -150,7 +156,7 @@ mamba3_status mamba3_scan_bwd_validate(const mamba3_scan_bwd_args *b) {
     for (const void *q : al16)
         if (q && !aligned16(q)) return MAMBA3_EALIGN;
     if ((b->ddt && !aligned_elem(b->ddt, a->dtype)) || (b->dlam && !aligned_elem(b->dlam, a->dtype)) ||
-        !aligned4(b->dA) || (b->dD && !aligned4(b->dD)))
+        (b->dA && !aligned4(b->dA)) || (b->dD && !aligned4(b->dD)))
         return MAMBA3_EALIGN;
     const int64_t es = a->dtype == MAMBA3_BF16 ? 2 : 4;
     // every output against every input and every other output
@@ -159,13 +165,14 @@ mamba3_status mamba3_scan_bwd_validate(const mamba3_scan_bwd_args *b) {
                     span(b->dC, T * G * N * R, es), span(b->dA, H, 4), span(b->dD, H, 4),
                     span(b->dh_in, S * H * N * P, 4), span(b->dBprev, S * G * N * R, es),
                     span(b->dxprev, S * H * P * R, es), span(b->dB_bias, H * N, 4), span(b->dC_bias, H * N, 4),
-                    span(b->dz, T * H * P * R, es)};
+                    span(b->dz, T * H * P * R, es), span(b->dA_tok, T * H, es)};
     Range ins[] = {span(a->x, T * H * P * R, es), span(a->dt, T * H, es), span(a->lam, T * H, es),
                    span(a->theta, T * H * (N / 2), es), span(a->B, T * G * N * R, es),
                    span(a->C, T * G * N * R, es), span(a->h_in, S * H * N * P, 4),
                    span(a->Bprev, S * G * N * R, es), span(a->xprev, S * H * P * R, es), span(a->A, H, 4),
                    span(a->D, H, 4), span(a->B_bias, H * N, 4), span(a->C_bias, H * N, 4),
                    span(a->z, T * H * P * R, es), span(a->cu_seqlens, a->cu_seqlens ? a->nseq + 1 : 0, 4),
+                   span(a->A_tok, T * H, es),
                    span(b->dy, T * H * P * R, es), span(b->dh_out, S * H * N * P, 4)};
     const int nout = sizeof outs / sizeof outs[0];
     for (int i = 0; i < nout; i++) {
@@ -205,8 +212,10 @@ mamba3_status mamba3_decode_validate(const mamba3_decode_args *a) {
         return MAMBA3_EINVAL;
     if ((int64_t)a->batch * a->nheads > INT32_MAX) return MAMBA3_EINVAL;
     if ((a->Bprev == nullptr) != (a->xprev == nullptr)) return MAMBA3_EINVAL;
-    if (a->batch > 0 && (!a->x || !a->dt || !a->lam || !a->theta || !a->B || !a->C || !a->A || !a->h || !a->y))
-        return MAMBA3_EINVAL;
+    if (a->batch > 0 && (!a->x || !a->dt || !a->theta || !a->B || !a->C || !a->h || !a->y)) return MAMBA3_EINVAL;
+    if (a->batch > 0 && !a->A && !a->A_tok) return MAMBA3_EINVAL;
+    if (!a->lam && !std::isfinite(a->lam_fixed)) return MAMBA3_EINVAL;
+    if (a->A_tok && !aligned_elem(a->A_tok, a->dtype)) return MAMBA3_EALIGN;
     const void *al16[] = {a->x, a->theta, a->B, a->C, a->Bprev, a->xprev, a->h, a->y};
     for (const void *p : al16)
         if (p && !aligned16(p)) return MAMBA3_EALIGN;
@@ -222,10 +231,10 @@ mamba3_status mamba3_decode_validate(const mamba3_decode_args *a) {
                    span(a->theta, b * H * (N / 2), es), span(a->B, b * G * N * R, es),
                    span(a->C, b * G * N * R, es), span(a->Bprev, b * G * N * R, es),
                    span(a->xprev, b * H * P * R, es), span(a->B_bias, H * N, 4), span(a->C_bias, H * N, 4),
-                   span(a->z, b * H * P * R, es), hh};
+                   span(a->z, b * H * P * R, es), span(a->A_tok, b * H, es), hh};
     for (Range r : ins)
         if (overlaps(y, r)) return MAMBA3_EINVAL;
-    for (int i = 0; i < 11; i++)
+    for (int i = 0; i < 12; i++)
         if (overlaps(hh, ins[i])) return MAMBA3_EINVAL;
     if (!m3::decode_supported(a->dstate, a->headdim, a->rank, a->dtype)) return MAMBA3_EUNSUPPORTED;
     return MAMBA3_OK;

@@ -48,7 +48,8 @@
 // is multiplied by SiLU(z) after the D term, in fp32 before the single bf16
 // rounding. The RMS of a column is a butterfly of wave shuffles over the lanes
 // that hold its pieces: the 4 operand lanes of a C row, the N/8 consecutive
-// loading lanes of a staged B row.
+// loading lanes of a staged B row. They also carry the variants: a per-token
+// decay rate A_t (loaded with dt) and a fixed trapezoid weight.
 #include <type_traits>
 
 #include "m3_common.h"
@@ -153,6 +154,11 @@ struct BfParams {
     const bf16 *z;          // output gate, or NULL
     int32_t norm;           // 1: B, C, Bprev columns scaled to unit RMS
     float eps;
+    // variants (EPI instantiations): a per-token decay rate, a fixed trapezoid weight. Atk and
+    // lam always point at readable token data (dt stands in for an absent array).
+    const bf16 *Atk;
+    int32_t atok_on, lam_on;
+    float lam_fixed;
 };
 
 template <int N_, int P_, int R_, int Q_, int NW_, int UT_, int SBR_, bool EPI_>
@@ -272,7 +278,11 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         start = (int64_t)s * pr.seqlen;
         len = pr.seqlen;
     }
-    const float A2h = pr.A[h] * kLog2e;
+    const float A2h = (CF::EPI ? (pr.A ? pr.A[h] : 0.f) : pr.A[h]) * kLog2e;
+    // the trapezoid weight of a loaded lam value (the fixed one when there is no lam array)
+    auto lamv = [&](bf16 raw) { return (CF::EPI && !pr.lam_on) ? pr.lam_fixed : to_f(raw); };
+    // log2 decay rate of a token whose loaded A_t is raw (the head's without per-token A)
+    auto a2v = [&](bf16 raw) { return (CF::EPI && pr.atok_on) ? to_f(raw) * kLog2e : A2h; };
     const float Dh = pr.D ? pr.D[h] : 0.f;
     // per-(sequence, head) base pointers: add token * stride (+ rank * N or P)
     const bf16 *gB = pr.B + g * (int64_t)R * N;
@@ -314,7 +324,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         const int64_t so = ((int64_t)s * H + h) * N * P;
         float d0 = 0.f;
         if (pr.Bprev && len > 0) {
-            const float dt0 = to_f(pr.dt[start * H + h]), l0 = to_f(pr.lam[start * H + h]);
+            const float dt0 = to_f(pr.dt[start * H + h]), l0 = lamv(pr.lam[start * H + h]);
             d0 = (1.f - l0) * dt0;
         }
         // prologue of Bprev's columns: inverse RMS per column (every wave computes its own)
@@ -368,6 +378,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     // tokens past the end are masked; no select or conversion sits next to a
     // load, so nothing waits for a prefetch before its consumer needs it.
     bf16 h_dt = {}, h_lam = {};     // token tid of the chunk (tid < Q)
+    bf16 h_A = {};                  // its decay rate A_t (per-token variant)
     bf16 h_dtn = {}, h_lamn = {};   // the token after the chunk (same for every thread)
     bf16x2 h_th2[CF::TPL];          // theta of the lane's angle pair for its TPL tokens
     bf16x8 h_c[TPW][NKK];
@@ -394,6 +405,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             const int64_t tk = t0h + min((int64_t)min(tq, Q - 1), last);
             h_dt = pr.dt[tk * H + h];
             h_lam = pr.lam[tk * H + h];
+            if constexpr (CF::EPI) h_A = pr.Atk[tk * H + h];
             const int64_t tn = t0h + min((int64_t)nqh, last);
             h_dtn = pr.dt[tn * H + h];
             h_lamn = pr.lam[tn * H + h];
@@ -476,11 +488,11 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             if (wave == 0) {
                 const int t = lane;
                 const bool ok = (FULL || t < nq) && t < Q;
-                const float dt = ok ? to_f(h_dt) : 0.f, lm = ok ? to_f(h_lam) : 0.f;
+                const float dt = ok ? to_f(h_dt) : 0.f, lm = ok ? lamv(h_lam) : 0.f;
                 const float gm = lm * dt, dl = (1.f - lm) * dt;
-                const float s2 = wave_incl_scan(dt * A2h, lane);
+                const float s2 = wave_incl_scan(dt * a2v(h_A), lane);
                 const float s2e = __shfl(s2, nq - 1, 64);
-                const float dn = (c0 + nq < len) ? (1.f - to_f(h_lamn)) * to_f(h_dtn) : 0.f;
+                const float dn = (c0 + nq < len) ? (1.f - lamv(h_lamn)) * to_f(h_dtn) : 0.f;
                 const float dl1 = __shfl_down(dl, 1, 64);
                 const float g1 = gm + ((t + 1 < nq) ? dl1 : ((t + 1 == nq) ? dn : 0.f));
                 // mask factor relative to the first token of t's 32-row tile (>= 1)
@@ -504,13 +516,13 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         } else {
             if (tid < Q) {
                 const bool ok = FULL || tid < nq;
-                const float dt = ok ? to_f(h_dt) : 0.f, lm = ok ? to_f(h_lam) : 0.f;
+                const float dt = ok ? to_f(h_dt) : 0.f, lm = ok ? lamv(h_lam) : 0.f;
                 DT[tid] = dt;
-                A2[tid] = dt * A2h;
+                A2[tid] = dt * a2v(h_A);
                 GM[tid] = lm * dt;
                 DL[tid] = (1.f - lm) * dt;
             }
-            if (tid == 0) MISC[0] = (c0 + nq < len) ? (1.f - to_f(h_lamn)) * to_f(h_dtn) : 0.f;
+            if (tid == 0) MISC[0] = (c0 + nq < len) ? (1.f - lamv(h_lamn)) * to_f(h_dtn) : 0.f;
         }
         __syncthreads();
 
@@ -1073,6 +1085,8 @@ mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st) {
     p.cu = a->cu_seqlens; p.seqlen = a->seqlen; p.H = a->nheads; p.G = a->ngroups;
     p.nseq = a->cu_seqlens ? a->nseq : a->batch;
     p.Bb = a->B_bias; p.Cb = a->C_bias; p.z = (const bf16 *)a->z; p.norm = a->bc_norm; p.eps = a->bc_eps;
+    p.Atk = (const bf16 *)(a->A_tok ? a->A_tok : a->dt); p.atok_on = a->A_tok != nullptr;
+    p.lam = (const bf16 *)(a->lam ? a->lam : a->dt); p.lam_on = a->lam != nullptr; p.lam_fixed = a->lam_fixed;
     const int64_t nseq = a->cu_seqlens ? a->nseq : a->batch;
     const int64_t nblk = nseq * a->nheads;
     if (nblk == 0) return MAMBA3_OK;
@@ -1104,7 +1118,8 @@ bool scan_bf16_supported(int N, int P, int R, int Q) {
 
 mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st) {
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
-    const bool epi = a->bc_norm || a->B_bias || a->C_bias || a->z;
+    // the EPI instantiations also carry the variants (per-token A, fixed lambda)
+    const bool epi = a->bc_norm || a->B_bias || a->C_bias || a->z || a->A_tok || !a->lam;
 #define X(n, p, r, q, w, ut, sbr)                                                       \
     if (N == n && P == p && R == r && Q == q)                                           \
         return epi ? launch_cfg<Cfg<n, p, r, q, w, ut, sbr, true>>(a, st)               \

@@ -26,6 +26,9 @@
 // applied. Every sum runs in a fixed order (no atomics): per-slab partial sums
 // of dA, dD and the bias gradients, and (with G < H) per-head dB, dC, dBprev,
 // go to the workspace and a second kernel adds them up.
+//
+// Variants: a per-token decay rate A_t (its gradient is per token, dt_t dS_t),
+// and a fixed trapezoid weight (no lam gradient).
 #include <algorithm>
 #include <type_traits>
 
@@ -48,13 +51,16 @@ struct BwdParams {
     int32_t nseq, seqlen, H, G, P, N, R, Q;
     int32_t norm;
     float eps;
+    const void *A_tok;        // per-token decay rate (token dtype, layout of dt), or NULL
+    void *dA_tok;             // its gradient
+    float lam_fixed;          // trapezoid weight of every token when lam is NULL
 };
 
 constexpr int kBwdThreads = 512;
 
 // LDS layout of the backward (offsets in floats)
 struct BwdLayout {
-    int cs, sn, dphi, dts, lms, gms, dls, S, g1, dS, dgm, ddl, es, cu, em, scal_end;
+    int cs, sn, dphi, dts, lms, gms, dls, S, g1, dS, dgm, ddl, es, cu, at, em, scal_end;
     int invB, invC, rowA, rowB, colS, colG, colD, rows_end;
     int Bt, Ct, dBt, dCt, Xs, dY, Hs, dH, Sc, dPm, Wk, Wk2;
     int Bp, BpRaw, Xp, dBc_in, dXc_in, dBc_out, dXc_out, invBp, bba, cba, misc, total;
@@ -80,6 +86,7 @@ __host__ __device__ inline BwdLayout bwd_layout(int N, int P, int R, int Q) {
     L.ddl = o; o += Q;
     L.es = o; o += Q;
     L.cu = o; o += Q;
+    L.at = o; o += Q;
     L.em = o; o += Q * Q;
     L.scal_end = o;
     L.invB = o; o += QR;
@@ -156,6 +163,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_scan_bwd(BwdParams p) {
     float *DT = sm + L.dts, *LM = sm + L.lms, *GM = sm + L.gms, *DL = sm + L.dls, *S = sm + L.S, *G1 = sm + L.g1;
     float *DS = sm + L.dS, *DGM = sm + L.dgm, *DDL = sm + L.ddl;
     float *ES = sm + L.es, *CU = sm + L.cu, *EM = sm + L.em;   // e^{S_t}, c_t, e^{S_t - S_u}
+    float *AT = sm + L.at;                                       // A_t of each token
     float *INVB = sm + L.invB, *INVC = sm + L.invC, *ROWA = sm + L.rowA, *ROWB = sm + L.rowB;
     float *COLS = sm + L.colS, *COLG = sm + L.colG, *COLD = sm + L.colD;
     float *Bt = sm + L.Bt, *Ct = sm + L.Ct, *dBt = sm + L.dBt, *dCt = sm + L.dCt;
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_scan_bwd(BwdParams p) {
     // a sequence table that breaks its contract (decreasing offsets) could ask for more chunk
     // states than the workspace holds: such a slab writes nothing
     if (cbase + nch > p.ws_chunks) return;
-    const float Ah = p.A[h];
+    const float Ah = p.A ? p.A[h] : 0.f;
     const float Dh = p.D ? p.D[h] : 0.f;
     const bool pro = p.norm || p.Bb || p.Cb;
     const bool has_prev = p.Bprev != nullptr;
@@ -217,13 +225,15 @@ __global__ __launch_bounds__(kBwdThreads) void k_scan_bwd(BwdParams p) {
     // per-token scalars of the chunk at c0 with nq tokens, the decay prefix and the angle table
     auto load_scalars = [&](int64_t c0, int nq) {
         for (int t = tid; t < Q; t += nt) {
-            float dtv = 0.f, lv = 0.f;
+            float dtv = 0.f, lv = 0.f, av = Ah;
             if (t < nq) {
                 dtv = ldt<T>(p.dt, (start + c0 + t) * H + h);
-                lv = ldt<T>(p.lam, (start + c0 + t) * H + h);
+                lv = p.lam ? ldt<T>(p.lam, (start + c0 + t) * H + h) : p.lam_fixed;
+                if (p.A_tok) av = ldt<T>(p.A_tok, (start + c0 + t) * H + h);
             }
             DT[t] = dtv;
             LM[t] = lv;
+            AT[t] = av;
             GM[t] = lv * dtv;
             DL[t] = (1.f - lv) * dtv;
         }
@@ -231,7 +241,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_scan_bwd(BwdParams p) {
         if (tid == 0) {
             float acc = 0.f;
             for (int t = 0; t < Q; t++) {
-                acc += DT[t] * Ah;
+                acc += DT[t] * AT[t];
                 S[t] = acc;
                 G1[t] = GM[t] + ((t + 1 < nq) ? DL[t + 1] : 0.f);
             }
@@ -628,11 +638,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_scan_bwd(BwdParams p) {
             stt<T>(p.dtheta, ((start + c0 + t) * H + h) * K + k, DT[t] * DPHI[e]);
         }
         for (int t = tid; t < nq; t += nt) {
-            float ddt = Ah * DS[t] + (1.f - LM[t]) * DDL[t] + LM[t] * DGM[t];
+            float ddt = AT[t] * DS[t] + (1.f - LM[t]) * DDL[t] + LM[t] * DGM[t];
             for (int k = 0; k < K; k++) ddt += ldt<T>(p.theta, ((start + c0 + t) * H + h) * K + k) * DPHI[t * K + k];
             stt<T>(p.ddt, (start + c0 + t) * H + h, ddt);
-            stt<T>(p.dlam, (start + c0 + t) * H + h, DT[t] * (DGM[t] - DDL[t]));
-            dA_acc += DT[t] * DS[t];
+            if (p.dlam) stt<T>(p.dlam, (start + c0 + t) * H + h, DT[t] * (DGM[t] - DDL[t]));
+            if (p.A_tok) stt<T>(p.dA_tok, (start + c0 + t) * H + h, DT[t] * DS[t]);
+            else dA_acc += DT[t] * DS[t];
         }
         // dB, dC: rotate back to the physical frame (+ the carry into the last token), then back
         // through the prologue to the raw columns; bias gradients accumulate per slab
@@ -794,8 +805,8 @@ struct BCfg {
     // LDS layout (bytes; every region 16-byte aligned)
     static constexpr int al(int b) { return (b + 15) / 16 * 16; }
     static constexpr int O_CS = 0, O_SN = O_CS + al(Q * K2 * 4), O_DPHI = O_SN + al(Q * K2 * 4);
-    static constexpr int O_SC = O_DPHI + al(Q * K2 * 4);            // 11 float [Q] tables
-    static constexpr int O_EM = O_SC + al(11 * Q * 4);              // float [Q][Q]
+    static constexpr int O_SC = O_DPHI + al(Q * K2 * 4);            // 12 float [Q] tables
+    static constexpr int O_EM = O_SC + al(12 * Q * 4);              // float [Q][Q]
     static constexpr int O_INV = O_EM + al(Q * Q * 4);              // float [2][QR]
     static constexpr int O_RPM = O_INV + al(2 * QR * 4);            // float [QR][TQ] row partials of dM M
     static constexpr int O_CPM = O_RPM + al(QR * TQ * 4);           // float [3][QR][TQ] column partials
@@ -832,6 +843,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     float *SC = (float *)(smem + CF::O_SC);
     float *DT = SC, *LM = SC + Q, *GM = SC + 2 * Q, *DL = SC + 3 * Q, *S = SC + 4 * Q, *G1 = SC + 5 * Q;
     float *ES = SC + 6 * Q, *CU = SC + 7 * Q, *DS = SC + 8 * Q, *DGM = SC + 9 * Q, *DDL = SC + 10 * Q;
+    float *AT = SC + 11 * Q;   // A_t of each token
     float *EM = (float *)(smem + CF::O_EM);
     float *INVB = (float *)(smem + CF::O_INV), *INVC = INVB + QR;
     float *RPM = (float *)(smem + CF::O_RPM), *CPM = (float *)(smem + CF::O_CPM);
@@ -874,7 +886,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     }
     const int64_t nch = (len + Q - 1) / Q;
     if (cbase + nch > p.ws_chunks) return;   // a sequence table that breaks its contract
-    const float Ah = p.A[h];
+    const float Ah = p.A ? p.A[h] : 0.f;
     const float Dh = p.D ? p.D[h] : 0.f;
     const bool pro = p.norm || p.Bb || p.Cb;
     const bool has_prev = p.Bprev != nullptr;
@@ -912,12 +924,13 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         static_assert(Q <= 64, "one wave scans the chunk");
         if (wave == 0) {   // per-token scalars and the log-decay prefix (wave scan)
             const int t = lane;
-            float dtv = 0.f, lv = 0.f;
+            float dtv = 0.f, lv = 0.f, av = Ah;
             if (t < nq) {
                 dtv = ldt<bf16>(p.dt, (start + c0 + t) * H + h);
-                lv = ldt<bf16>(p.lam, (start + c0 + t) * H + h);
+                lv = p.lam ? ldt<bf16>(p.lam, (start + c0 + t) * H + h) : p.lam_fixed;
+                if (p.A_tok) av = ldt<bf16>(p.A_tok, (start + c0 + t) * H + h);
             }
-            float acc = dtv * Ah;
+            float acc = dtv * av;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float o = __shfl_up(acc, off, 64);
@@ -927,6 +940,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             if (t < Q) {
                 DT[t] = dtv;
                 LM[t] = lv;
+                AT[t] = av;
                 GM[t] = lv * dtv;
                 DL[t] = (1.f - lv) * dtv;
                 S[t] = acc;
@@ -1393,10 +1407,11 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             for (int k = li; k < K; k += 16) a += (float)TH[t * K + k] * DPHI[t * K + k];
             a = sum16(a);
             if (t0 < nq && li == 0) {
-                const float ddt = Ah * DS[t] + (1.f - LM[t]) * DDL[t] + LM[t] * DGM[t] + a;
+                const float ddt = AT[t] * DS[t] + (1.f - LM[t]) * DDL[t] + LM[t] * DGM[t] + a;
                 stt<bf16>(p.ddt, (start + c0 + t) * H + h, ddt);
-                stt<bf16>(p.dlam, (start + c0 + t) * H + h, DT[t] * (DGM[t] - DDL[t]));
-                dA_acc += DT[t] * DS[t];
+                if (p.dlam) stt<bf16>(p.dlam, (start + c0 + t) * H + h, DT[t] * (DGM[t] - DDL[t]));
+                if (p.A_tok) stt<bf16>(p.dA_tok, (start + c0 + t) * H + h, DT[t] * DS[t]);
+                else dA_acc += DT[t] * DS[t];
             }
         }
         // raw B and C rows of the chunk again (for the prologue's backward), over C~ and B~
@@ -1554,7 +1569,7 @@ __global__ void k_bwd_reduce(BwdParams p, int64_t T_tok, int32_t S) {
             a += p.p_dA[(int64_t)s * H + i];
             d += p.p_dD[(int64_t)s * H + i];
         }
-        p.dA[i] = a;
+        if (p.dA) p.dA[i] = a;
         if (p.dD) p.dD[i] = d;
     }
     if (i < (int64_t)H * N) {
@@ -1663,6 +1678,7 @@ static mamba3_status launch_bwd_t(const mamba3_scan_bwd_args *b, hipStream_t st)
     p.nseq = a->cu_seqlens ? a->nseq : a->batch;
     p.seqlen = a->seqlen; p.H = a->nheads; p.G = a->ngroups; p.P = a->headdim; p.N = a->dstate; p.R = a->rank;
     p.Q = Q; p.norm = a->bc_norm; p.eps = a->bc_eps;
+    p.A_tok = a->A_tok; p.dA_tok = b->dA_tok; p.lam_fixed = a->lam_fixed;
     const int64_t S = p.nseq, T_tok = (int64_t)a->batch * a->seqlen;
     const int64_t nblk = S * p.H;
     if constexpr (std::is_same<T, bf16>::value) {

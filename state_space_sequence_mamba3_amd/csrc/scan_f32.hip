@@ -19,6 +19,9 @@
 // Optional block prologue and epilogue (section "Architectural Integration"):
 // each B and C column is scaled to unit RMS and gets its head's bias before
 // the rotation, and y is multiplied by SiLU(z) after the D term.
+//
+// Variants: a per-token decay rate A_t replaces the head's A, and without a
+// lam array every token uses the fixed trapezoid weight.
 #include "m3_common.h"
 
 namespace m3 {
@@ -29,9 +32,11 @@ struct ValuParams {
     float *y, *h_out;
     const int32_t *cu;
     const float *Bb, *Cb, *z;   // prologue biases [H, N] and output gate, or NULL
+    const float *A_tok;         // per-token decay rate [T, H], or NULL (A per head)
     int32_t nseq, seqlen, H, G, P, N, R, Q;
     int32_t norm;               // 1: B and C columns scaled to unit RMS
     float eps;
+    float lam_fixed;            // trapezoid weight of every token when lam is NULL
 };
 
 // Block prologue on `nrows` LDS rows of N values: scale each row to unit RMS
@@ -52,7 +57,7 @@ __device__ void bc_prologue_rows(float *rows, int nrows, int N, const float *bia
 
 size_t scan_f32_lds_bytes(int N, int P, int R, int Q) {
     size_t QR = (size_t)Q * R, K = N / 2;
-    size_t floats = QR * N * 2 + QR * P + QR * QR + (size_t)N * P + (size_t)Q * (7 + K);
+    size_t floats = QR * N * 2 + QR * P + QR * QR + (size_t)N * P + (size_t)Q * (8 + K);
     return floats * sizeof(float);
 }
 
@@ -75,6 +80,7 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
     float *wU = dts + Q;           // [Q] chunk-state weights
     float *misc = wU + Q;          // [Q] (misc[0] = delta of the token after the chunk)
     float *phi = misc + Q;         // [Q][K]
+    float *dtA = phi + Q * K;      // [Q] dt_t A_t
 
     int64_t start, len;
     if (p.cu) {
@@ -86,7 +92,7 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
         start = (int64_t)s * p.seqlen;
         len = p.seqlen;
     }
-    const float Ah = p.A[h];
+    const float Ah = p.A ? p.A[h] : 0.f;
     const float Dh = p.D ? p.D[h] : 0.f;
     const bool pro = p.norm || p.Bb || p.Cb;
     const float *Bbh = p.Bb ? p.Bb + (int64_t)h * N : nullptr;
@@ -100,12 +106,14 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
         const int nq = (int)min((int64_t)Q, len - c0);
         // per-token scalars
         for (int t = tid; t < Q; t += nt) {
-            float dtv = 0.f, lv = 0.f;
+            float dtv = 0.f, lv = 0.f, av = 0.f;
             if (t < nq) {
                 int64_t tg = start + c0 + t;
                 dtv = p.dt[tg * H + h];
-                lv = p.lam[tg * H + h];
+                lv = p.lam ? p.lam[tg * H + h] : p.lam_fixed;
+                av = p.A_tok ? p.A_tok[tg * H + h] : Ah;
             }
+            dtA[t] = dtv * av;
             dts[t] = dtv;
             gm[t] = lv * dtv;
             dl[t] = (1.f - lv) * dtv;
@@ -114,7 +122,7 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
             float dnext = 0.f;
             if (c0 + nq < len) {
                 int64_t tg = start + c0 + nq;
-                float dtv = p.dt[tg * H + h], lv = p.lam[tg * H + h];
+                float dtv = p.dt[tg * H + h], lv = p.lam ? p.lam[tg * H + h] : p.lam_fixed;
                 dnext = (1.f - lv) * dtv;
             }
             misc[0] = dnext;
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
         if (tid == 0) {
             float acc = 0.f;
             for (int t = 0; t < Q; t++) {
-                if (t < nq) acc += dts[t] * Ah;
+                if (t < nq) acc += dtA[t];
                 S[t] = acc;
                 float dn = (t + 1 < nq) ? dl[t + 1] : (t + 1 == nq ? misc[0] : 0.f);
                 g1[t] = gm[t] + dn;
@@ -258,6 +266,7 @@ mamba3_status launch_scan_f32(const mamba3_scan_args *a, hipStream_t st) {
     p.R = a->rank; p.Q = a->chunk;
     p.Bb = a->B_bias; p.Cb = a->C_bias; p.z = (const float *)a->z;
     p.norm = a->bc_norm; p.eps = a->bc_eps;
+    p.A_tok = (const float *)a->A_tok; p.lam_fixed = a->lam_fixed;
     size_t lds = scan_f32_lds_bytes(p.N, p.P, p.R, p.Q);
     if (hipFuncSetAttribute((const void *)k_scan_f32, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return MAMBA3_EHIP;

@@ -157,6 +157,19 @@ def block_inputs(inp: dict, seed: int, norm: bool = True, B_bias: bool = True, C
     return out
 
 
+def variant_inputs(inp: dict, seed: int, A_tok: bool = True, lam_fixed: float | None = None) -> dict:
+    """The variants: a per-token decay rate A_t ~ -exp(N(0, 0.5)) shaped like
+    dt (token dtype), replacing A; and, with lam_fixed, no lam array."""
+    m = inp["meta"]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = dict(inp)
+    if A_tok:
+        out["A_tok"] = _tok(-np.exp(_normal(rng, inp["dt"].shape, 0.0, 0.5)), m["dtype"])
+    if lam_fixed is not None:
+        out["lam"], out["lam_fixed"] = None, float(lam_fixed)
+    return out
+
+
 def grad_inputs(inp: dict, seed: int, dh_out: bool = True) -> dict:
     """Output gradients for a backward test: dy ~ N(0, 1) shaped like x (token
     dtype) and, if asked, dh_out ~ N(0, 1) [S, H, N, P] fp32."""

@@ -37,7 +37,7 @@ def test_status_strings(lib):
     assert m3.status_string(m3.MAMBA3_OK) == "ok"
     for s in range(6):
         assert m3.status_string(s)
-    assert lib.mamba3_version() == 10200
+    assert lib.mamba3_version() == 10300
 
 
 BASE = 0x7F0000000000
@@ -112,6 +112,33 @@ def test_scan_validate_errors(lib, field, value, status):
 ])
 def test_scan_validate_prologue(lib, over, status):
     assert m3.mamba3_scan_validate(good_scan(**over)) == status
+
+
+def test_validate_variants(lib):
+    # per-token decay rate: A may then be absent; fixed trapezoid weight: lam may be absent
+    assert m3.mamba3_scan_validate(good_scan(A_tok=fake(17))) == m3.MAMBA3_OK
+    assert m3.mamba3_scan_validate(good_scan(A_tok=fake(17), A=None)) == m3.MAMBA3_OK
+    assert m3.mamba3_scan_validate(good_scan(A=None)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_scan_validate(good_scan(lam=None, lam_fixed=0.5)) == m3.MAMBA3_OK
+    assert m3.mamba3_scan_validate(good_scan(lam=None, lam_fixed=float("nan"))) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_scan_validate(good_scan(A_tok=fake(17) + 2)) == m3.MAMBA3_EALIGN    # fp32 element alignment
+    assert m3.mamba3_scan_validate(good_scan(A_tok=fake(9))) == m3.MAMBA3_EINVAL         # y aliases A_tok
+    assert m3.mamba3_decode_validate(good_decode(A_tok=fake(17), A=None)) == m3.MAMBA3_OK
+    assert m3.mamba3_decode_validate(good_decode(A=None)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_decode_validate(good_decode(lam=None, lam_fixed=1.0)) == m3.MAMBA3_OK
+    assert m3.mamba3_decode_validate(good_decode(lam=None, lam_fixed=float("inf"))) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_decode_validate(good_decode(A_tok=fake(11))) == m3.MAMBA3_EINVAL     # h aliases A_tok
+    # backward: dA_tok with a per-token A (and no dA), no dlam with a fixed weight
+    b = good_bwd(dA=None, dA_tok=fake(39))
+    b.fwd.A_tok = fake(17)
+    assert m3.mamba3_scan_bwd_validate(b) == m3.MAMBA3_OK
+    b.dA_tok = None
+    assert m3.mamba3_scan_bwd_validate(b) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_scan_bwd_validate(good_bwd(dA_tok=fake(39))) == m3.MAMBA3_EINVAL     # no A_tok in the forward
+    b = good_bwd(dlam=None)
+    assert m3.mamba3_scan_bwd_validate(b) == m3.MAMBA3_EINVAL
+    b.fwd.lam = None
+    assert m3.mamba3_scan_bwd_validate(b) == m3.MAMBA3_OK
 
 
 def test_decode_validate_prologue(lib):

@@ -19,11 +19,12 @@ pytestmark = pytest.mark.gpu
 
 def run(d, chunk, want_state=True):
     import torch
-    y, h = m3.mamba3_scan_fwd(d["x"], d["dt"], d["lam"], d["theta"], d["B"], d["C"], d["A"], d.get("D"),
+    y, h = m3.mamba3_scan_fwd(d["x"], d["dt"], d.get("lam"), d["theta"], d["B"], d["C"], d.get("A"), d.get("D"),
                               h_in=d.get("h_in"), Bprev=d.get("Bprev"), xprev=d.get("xprev"),
                               cu_seqlens=d.get("cu_seqlens"), chunk=chunk, want_state=want_state,
                               B_bias=d.get("B_bias"), C_bias=d.get("C_bias"), z=d.get("z"),
-                              bc_norm=d.get("bc_norm", False), bc_eps=d.get("bc_eps", 1e-5))
+                              bc_norm=d.get("bc_norm", False), bc_eps=d.get("bc_eps", 1e-5),
+                              A_tok=d.get("A_tok"), lam_fixed=d.get("lam_fixed", 0.5))
     torch.cuda.synchronize()
     return y, h
 
@@ -114,6 +115,27 @@ def test_block_packed_grouped(oracle):
     yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
     assert packed_relerr(from_dev(y), yo, inp["cu_seqlens"]) < TOL_BF16
     assert state_relerr(from_dev(h), ho) < TOL_BF16
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+@pytest.mark.parametrize("variant", [
+    dict(A_tok=True),
+    dict(A_tok=False, lam_fixed=0.5),
+    dict(A_tok=True, lam_fixed=1.0),
+])
+def test_variants(oracle, cfg, variant):
+    """Per-token decay rate A_t (A absent) and fixed trapezoid weights, with a resumed state."""
+    spec = dict(batch=2, seqlen=150, nheads=2) if cfg != 4 else dict(seqlen=300, nheads=2, packed=False)
+    inp = synth.resume_inputs(synth.scan_inputs(cfg, seed=71, **spec), seed=72)
+    inp = synth.variant_inputs(inp, seed=73, **variant)
+    if variant["A_tok"]:
+        inp["A"] = None
+    note(f"bf16 scan variant cfg{cfg} {variant}")
+    y, h = run(upload(inp, device()), inp["meta"]["chunk"])
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    ey, eh = slab_relerr(from_dev(y), yo), state_relerr(from_dev(h), ho)
+    note(f"  y relerr {ey:.2e}  h relerr {eh:.2e}")
+    assert ey < TOL_BF16 and eh < TOL_BF16
 
 
 @pytest.mark.parametrize("cfg", [1, 2])

@@ -15,18 +15,19 @@ from tests.gpu_util import TOL_BF16, TOL_F32, device, from_dev, note, upload
 
 pytestmark = pytest.mark.gpu
 
-KEYS = ("dx", "ddt", "dlam", "dtheta", "dB", "dC", "dA", "dD", "dh_in", "dBprev", "dxprev", "dB_bias", "dC_bias", "dz")
+KEYS = ("dx", "ddt", "dlam", "dtheta", "dB", "dC", "dA", "dD", "dh_in", "dBprev", "dxprev", "dB_bias", "dC_bias", "dz",
+        "dA_tok")
 
 
 def run_bwd(inp, gr):
     import torch
     d = upload(inp, device())
     dy = upload(gr, device())
-    g = m3.mamba3_scan_bwd(d["x"], d["dt"], d["lam"], d["theta"], d["B"], d["C"], d["A"], d.get("D"),
+    g = m3.mamba3_scan_bwd(d["x"], d["dt"], d.get("lam"), d["theta"], d["B"], d["C"], d.get("A"), d.get("D"),
                            dy=dy["dy"], dh_out=dy.get("dh_out"), h_in=d.get("h_in"), Bprev=d.get("Bprev"),
                            xprev=d.get("xprev"), cu_seqlens=d.get("cu_seqlens"), B_bias=d.get("B_bias"),
                            C_bias=d.get("C_bias"), z=d.get("z"), bc_norm=d.get("bc_norm", False),
-                           bc_eps=d.get("bc_eps", 1e-5))
+                           bc_eps=d.get("bc_eps", 1e-5), A_tok=d.get("A_tok"), lam_fixed=d.get("lam_fixed", 0.5))
     torch.cuda.synchronize()
     return {k: from_dev(v) for k, v in g.items()}
 
@@ -101,6 +102,19 @@ def test_bwd_bf16(oracle, name, spec, block):
         inp = synth.block_inputs(inp, seed=103)
     gr = synth.grad_inputs(inp, seed=104)
     compare(oracle, inp, gr, TOL_BF16, f"bwd bf16 {name} block={block}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", [dict(A_tok=True), dict(A_tok=True, lam_fixed=0.5), dict(A_tok=False, lam_fixed=1.0)])
+def test_bwd_variants(oracle, dtype, variant):
+    """Per-token decay rate (per-token dA) and fixed trapezoid weights (no dlam)."""
+    cfg = dict(synth.CONFIGS[1], dtype=dtype, batch=1, seqlen=70, nheads=2)
+    inp = synth.resume_inputs(synth.scan_inputs(cfg, seed=111), seed=112)
+    inp = synth.variant_inputs(inp, seed=113, **variant)
+    if variant["A_tok"]:
+        inp["A"] = None
+    gr = synth.grad_inputs(inp, seed=114)
+    compare(oracle, inp, gr, TOL_F32 if dtype == "f32" else TOL_BF16, f"bwd {dtype} variant {variant}")
 
 
 def test_bwd_deterministic():

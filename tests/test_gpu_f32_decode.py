@@ -15,11 +15,12 @@ def run_scan(inp, chunk, want_state=True):
     import torch
     dev = device()
     d = upload(inp, dev)
-    y, h = m3.mamba3_scan_fwd(d["x"], d["dt"], d["lam"], d["theta"], d["B"], d["C"], d["A"], d.get("D"),
+    y, h = m3.mamba3_scan_fwd(d["x"], d["dt"], d.get("lam"), d["theta"], d["B"], d["C"], d.get("A"), d.get("D"),
                               h_in=d.get("h_in"), Bprev=d.get("Bprev"), xprev=d.get("xprev"),
                               cu_seqlens=d.get("cu_seqlens"), chunk=chunk, want_state=want_state,
                               B_bias=d.get("B_bias"), C_bias=d.get("C_bias"), z=d.get("z"),
-                              bc_norm=d.get("bc_norm", False), bc_eps=d.get("bc_eps", 1e-5))
+                              bc_norm=d.get("bc_norm", False), bc_eps=d.get("bc_eps", 1e-5),
+                              A_tok=d.get("A_tok"), lam_fixed=d.get("lam_fixed", 0.5))
     torch.cuda.synchronize()
     return from_dev(y), (from_dev(h) if h is not None else None)
 
@@ -114,6 +115,20 @@ def test_scan_fp32_block_packed(oracle):
     assert state_relerr(h, ho) < TOL_F32
 
 
+@pytest.mark.parametrize("variant", [dict(A_tok=True), dict(A_tok=False, lam_fixed=0.5),
+                                     dict(A_tok=True, lam_fixed=1.0)])
+def test_scan_fp32_variants(oracle, variant):
+    cfg = dict(synth.CONFIGS[0], batch=2, seqlen=90, nheads=4, headdim=16, dstate=16, rank=2, chunk=32, ngroups=2)
+    inp = synth.resume_inputs(synth.scan_inputs(cfg, seed=75), seed=76)
+    inp = synth.variant_inputs(inp, seed=77, **variant)
+    if variant["A_tok"]:
+        inp["A"] = None
+    note(f"scan f32 variant {variant}")
+    y, h = run_scan(inp, chunk=32)
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    assert slab_relerr(y, yo) < TOL_F32 and state_relerr(h, ho) < TOL_F32
+
+
 def test_scan_fp32_chunk_size_invariance():
     cfg = dict(synth.CONFIGS[0], batch=1, seqlen=192, nheads=2, rank=2)
     inp = synth.scan_inputs(cfg, seed=12)
@@ -141,10 +156,13 @@ def run_decode(inp, steps, ring_index=None):
     Bprev, xprev = d["Bprev"], d["xprev"]
     for k in range(steps):
         i = k % d["x"].shape[0]
-        y = m3.mamba3_decode_step(d["x"][i], d["dt"][i], d["lam"][i], d["theta"][i], d["B"][i], d["C"][i],
-                                  d["A"], d["D"], h=h, Bprev=Bprev, xprev=xprev, B_bias=d.get("B_bias"),
+        lam = d["lam"][i] if d.get("lam") is not None else None
+        atok = d["A_tok"][i] if d.get("A_tok") is not None else None
+        y = m3.mamba3_decode_step(d["x"][i], d["dt"][i], lam, d["theta"][i], d["B"][i], d["C"][i],
+                                  d.get("A"), d["D"], h=h, Bprev=Bprev, xprev=xprev, B_bias=d.get("B_bias"),
                                   C_bias=d.get("C_bias"), z=d["z"][i] if d.get("z") is not None else None,
-                                  bc_norm=d.get("bc_norm", False), bc_eps=d.get("bc_eps", 1e-5))
+                                  bc_norm=d.get("bc_norm", False), bc_eps=d.get("bc_eps", 1e-5), A_tok=atok,
+                                  lam_fixed=d.get("lam_fixed", 0.5))
         ys.append(y)
         Bprev, xprev = d["B"][i], d["x"][i]
     torch.cuda.synchronize()
@@ -157,9 +175,12 @@ def oracle_decode(oracle, inp, steps):
     ys = []
     for k in range(steps):
         i = k % inp["x"].shape[0]
-        tok = {kk: inp[kk][i] for kk in ("x", "dt", "lam", "theta", "B", "C")}
-        tok.update(A=inp["A"], D=inp["D"], Bprev=Bprev, xprev=xprev)
-        for kk in ("B_bias", "C_bias", "bc_norm", "bc_eps"):
+        tok = {kk: inp[kk][i] for kk in ("x", "dt", "theta", "B", "C")}
+        tok["lam"] = inp["lam"][i] if inp.get("lam") is not None else None
+        if inp.get("A_tok") is not None:
+            tok["A_tok"] = inp["A_tok"][i]
+        tok.update(A=inp.get("A"), D=inp["D"], Bprev=Bprev, xprev=xprev)
+        for kk in ("B_bias", "C_bias", "bc_norm", "bc_eps", "lam_fixed"):
             if kk in inp:
                 tok[kk] = inp[kk]
         if inp.get("z") is not None:
@@ -230,6 +251,26 @@ def test_decode_block_feature_subsets(oracle, features):
         num = np.abs(a - b).max(axis=(2, 3))
         assert float(np.max(num / np.abs(b).max(axis=(2, 3)))) < TOL_BF16
     assert state_relerr(hg, ho) < 1e-5
+
+
+@pytest.mark.parametrize("dtype,tol", [("bf16", TOL_BF16), ("f32", TOL_F32)])
+@pytest.mark.parametrize("shape", [
+    dict(batch=4, nheads=4, headdim=64, dstate=64, rank=4),
+    dict(batch=4, nheads=2, headdim=64, dstate=128, rank=1),
+    dict(batch=5, nheads=4, headdim=16, dstate=16, rank=1, ngroups=2),
+])
+@pytest.mark.parametrize("variant", [dict(A_tok=True), dict(A_tok=True, lam_fixed=0.5)])
+def test_decode_variants(oracle, dtype, tol, shape, variant):
+    cfg = dict(synth.CONFIGS[3], dtype=dtype, **shape)
+    inp = synth.variant_inputs(synth.decode_inputs(cfg, seed=26, ring=3), seed=27, **variant)
+    inp["A"] = None
+    note(f"decode variant {dtype} {shape} {variant}")
+    yg, hg = run_decode(inp, steps=4)
+    yo, ho = oracle_decode(oracle, inp, steps=4)
+    for a, b in zip(yg, yo):
+        num = np.abs(a - b).max(axis=(2, 3))
+        assert float(np.max(num / np.abs(b).max(axis=(2, 3)))) < tol
+    assert state_relerr(hg, ho) < (tol if dtype == "f32" else 1e-5)
 
 
 def test_decode_config3_full_batch(oracle):
