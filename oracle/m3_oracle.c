@@ -56,7 +56,10 @@
  * of the paper listing): a per-token decay rate A_t [T, H] replaces the head's
  * A (alpha_t = exp(dt_t A_t)), and a fixed trapezoid weight replaces the
  * per-token lam (lam = 1/2 is the classical trapezoid, lam = 1 exponential-
- * Euler).
+ * Euler). The angle rows may also be shared by groups of heads (th_groups
+ * rows per token, head h reading row h / (H / th_groups), as B and C are
+ * shared by groups); the pages state no angle sharing, so this is a layout
+ * option only, and with one row per head it is the per-head form above.
  *
  * Inputs are read through a dtype tag (f64, f32, bf16 bits) and converted
  * exactly to double; all arithmetic is in double / double complex.
@@ -82,7 +85,7 @@ typedef struct {
     const void *x;             /* [T, H, R, P] */
     const void *dt;            /* [T, H] (post-softplus step) */
     const void *lam;           /* [T, H] (trapezoid weight in [0,1]) */
-    const void *theta;         /* [T, H, N/2] (rotation frequency) */
+    const void *theta;         /* [T, Gth, N/2] (rotation frequency; Gth = H unless th_groups says) */
     const void *B;             /* [T, G, R, N] */
     const void *C;             /* [T, G, R, N] */
     const double *A;           /* [H], negative */
@@ -100,6 +103,7 @@ typedef struct {
     /* Variants: */
     const void *A_tok;         /* [T, H] per-token decay rate A_t (dtype in_dtype), or NULL: A[h] */
     double lam_fixed;          /* the trapezoid weight of every token when lam is NULL */
+    int32_t th_groups;         /* angle rows per token, Gth (0 = H): heads h*Gth/H share one, as B/C groups do */
 } m3o_args;
 
 static inline double ld(const void *p, int dt, int64_t i) {
@@ -109,6 +113,13 @@ static inline double ld(const void *p, int dt, int64_t i) {
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/* Flat index of angle k of head h at token t: head h reads the angle row of
+ * its group h / (H / Gth), exactly as it reads the B/C row of group h / (H / G). */
+static inline int64_t th_at(const m3o_args *a, int64_t t, int h, int k) {
+    const int Gth = a->th_groups ? a->th_groups : a->H, K = a->N / 2;
+    return (t * Gth + h / (a->H / Gth)) * K + k;
 }
 
 /* One N-vector of B or C as the recurrence sees it: the raw column at src[off ..
@@ -192,7 +203,7 @@ static void o1_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
         const double delta = (1.0 - lam) * dt, gamma = lam * dt;
         const double decay = exp(dt * A_of(a, t * H + h, h));
         for (int k = 0; k < K; k++) {
-            double ang = dt * ld(a->theta, dtp, (t * H + h) * K + k);
+            double ang = dt * ld(a->theta, dtp, th_at(a, t, h, k));
             z[k] = decay * (cos(ang) + I * sin(ang));
         }
         const int64_t ob = (t * G + g) * N * R, ox = (t * H + h) * P * R;
@@ -292,7 +303,7 @@ static void o2_slab(const m3o_args *a, int s, int h, double *y_slab, double *h_s
         const double lam = lam_of(a, t * H + h);
         const double alpha = exp(dt * A_of(a, t * H + h, h));
         const double beta = (1.0 - lam) * dt * alpha, gamma = lam * dt;
-        for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, (t * H + h) * K + k);
+        for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, th_at(a, t, h, k));
         const int64_t ob = (t * G + g) * N * R, ox = (t * H + h) * P * R;
         for (int j = 0; j < R; j++) {
             bc_row(a, a->B, ob + j * N, h, a->B_bias, rowb);
@@ -366,7 +377,7 @@ static void o3_slab(const m3o_args *a, int s, int h, double *y_slab) {
         alpha[t] = exp(dt * A_of(a, tg * H + h, h));
         beta[t] = (1.0 - lam) * dt * alpha[t];
         gamma[t] = lam * dt;
-        for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, (tg * H + h) * K + k);
+        for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, th_at(a, tg, h, k));
         const int64_t ob = (tg * G + g) * N * R, ox = (tg * H + h) * P * R;
         for (int j = 0; j < R; j++) {
             bc_row(a, a->B, ob + j * N, h, a->B_bias, row);
@@ -523,7 +534,7 @@ static void ob_slab(const m3o_args *a, const m3o_grads *gr, int s, int h, double
                 U[n * P + p] = Hp[n * P + p] + delta * v;
             }
         for (int k = 0; k < K; k++) {
-            const double ang = dt * ld(a->theta, dtp, tg * H * K + (int64_t)h * K + k);
+            const double ang = dt * ld(a->theta, dtp, th_at(a, tg, h, k));
             const double c = cos(ang), sn = sin(ang);
             for (int p = 0; p < P; p++) {
                 const double u0 = U[(2 * k) * P + p], u1 = U[(2 * k + 1) * P + p];
@@ -596,7 +607,7 @@ static void ob_slab(const m3o_args *a, const m3o_grads *gr, int s, int h, double
                 U[n * P + p] = Hp[n * P + p] + delta * v;
             }
         for (int k = 0; k < K; k++) {
-            const double ang = dt * ld(a->theta, dtp, tg * H * K + (int64_t)h * K + k);
+            const double ang = dt * ld(a->theta, dtp, th_at(a, tg, h, k));
             const double c = cos(ang), sn = sin(ang);
             double acc = 0.0;
             for (int p = 0; p < P; p++) {
@@ -624,9 +635,9 @@ static void ob_slab(const m3o_args *a, const m3o_grads *gr, int s, int h, double
         /* scalars: alpha = e^{dt A}, delta = (1 - lam) dt, gamma = lam dt, phi_k = dt theta_k */
         double ddt = Ah * alpha * dalpha + (1.0 - lam) * ddelta + lam * dgamma;
         for (int k = 0; k < K; k++) {
-            const double th = ld(a->theta, dtp, tg * H * K + (int64_t)h * K + k);
+            const double th = ld(a->theta, dtp, th_at(a, tg, h, k));
             ddt += th * dphi[k];
-            if (gr->dtheta) gr->dtheta[(tg * H + h) * K + k] += dt * dphi[k];
+            if (gr->dtheta) gr->dtheta[th_at(a, tg, h, k)] += dt * dphi[k];
         }
         if (gr->ddt) gr->ddt[tg * H + h] += ddt;
         if (gr->dlam && a->lam) gr->dlam[tg * H + h] += dt * (dgamma - ddelta);
@@ -665,6 +676,7 @@ static int check(const m3o_args *a) {
     if (a->N % 2 || a->H % a->G) return 1;
     if (!a->x || !a->dt || !a->theta || !a->B || !a->C || (!a->A && !a->A_tok)) return 1;
     if (a->bc_norm && !(a->bc_eps >= 0.0)) return 1;
+    if (a->th_groups < 0 || (a->th_groups && a->H % a->th_groups)) return 1;
     return 0;
 }
 
@@ -731,8 +743,8 @@ int m3o_decode(const m3o_args *a_in, double *h_io, double *y, int nthreads) {
 }
 
 /* Gradient of the whole scan (OB). Sequences run in parallel; the heads of a
- * sequence run in order, so the heads of a group add into dB, dC, dBprev one
- * after another. The per-head sums dA, dD and the bias gradients are added
+ * sequence run in order, so the heads of a group add into dB, dC, dBprev (and
+ * the heads sharing an angle row into dtheta) one after another. The per-head sums dA, dD and the bias gradients are added
  * in sequence order. */
 int m3o_scan_bwd(const m3o_args *a, const m3o_grads *gr, int nthreads) {
     if (check(a) || !gr || !gr->dy) return 1;

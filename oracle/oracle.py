@@ -7,7 +7,7 @@ imports nothing from the product package.
 
 All arrays use the flat token axis (padded batches are flattened to
 ``batch*seqlen`` tokens, sequence ``s`` starting at ``s*seqlen``):
-``x [T,H,R,P]``, ``dt, lam [T,H]``, ``theta [T,H,N/2]``, ``B, C [T,G,R,N]``,
+``x [T,H,R,P]``, ``dt, lam [T,H]``, ``theta [T,H,N/2]`` (or ``[T,Gth,N/2]``, one angle row shared by each group of H/Gth heads), ``B, C [T,G,R,N]``,
 ``A, D [H]``, ``h_in [S,H,N,P]``, ``Bprev [S,G,R,N]``, ``xprev [S,H,R,P]``
 (rank-major: the R columns of B_t, X_t are stored one after another), and the
 optional block prologue/epilogue: ``B_bias, C_bias [H,N]``, ``z`` (like x),
@@ -54,7 +54,7 @@ class _Args(ctypes.Structure):
         ("Bprev", ctypes.c_void_p), ("xprev", ctypes.c_void_p),
         ("B_bias", ctypes.c_void_p), ("C_bias", ctypes.c_void_p), ("z", ctypes.c_void_p),
         ("bc_norm", ctypes.c_int32), ("bc_eps", ctypes.c_double),
-        ("A_tok", ctypes.c_void_p), ("lam_fixed", ctypes.c_double),
+        ("A_tok", ctypes.c_void_p), ("lam_fixed", ctypes.c_double), ("th_groups", ctypes.c_int32),
     ]
 
 
@@ -120,6 +120,7 @@ class _Pack:
         B = keep["B"]
         H, R, P = x.shape[-3], x.shape[-2], x.shape[-1]
         G, N = B.shape[-3], B.shape[-1]
+        self.Gth = keep["theta"].shape[-2]   # angle rows per token: H, or fewer shared by groups of heads
         keep["seq_start"] = np.ascontiguousarray(seq_start, dtype=np.int64)
         keep["seq_len"] = np.ascontiguousarray(seq_len, dtype=np.int64)
         self.keep = keep
@@ -132,7 +133,7 @@ class _Pack:
                           _ptr(keep["h_in"]), _ptr(keep["Bprev"]), _ptr(keep["xprev"]),
                           _ptr(keep["B_bias"]), _ptr(keep["C_bias"]), _ptr(keep["z"]),
                           1 if inp.get("bc_norm") else 0, float(inp.get("bc_eps", 0.0)),
-                          _ptr(keep["A_tok"]), float(inp.get("lam_fixed", 0.0)))
+                          _ptr(keep["A_tok"]), float(inp.get("lam_fixed", 0.0)), self.Gth)
 
 
 def flatten(inp: dict) -> tuple[dict, np.ndarray, np.ndarray]:
@@ -201,7 +202,7 @@ def scan_bwd(inp: dict, dy: np.ndarray, dh_out: np.ndarray | None = None, nthrea
     H, G, P, N, R, S = pk.H, pk.G, pk.P, pk.N, pk.R, pk.nseq
     dyf = np.ascontiguousarray(np.asarray(dy, dtype=np.float64).reshape(T, H, R, P))
     dho = None if dh_out is None else np.ascontiguousarray(dh_out, dtype=np.float64)
-    out = dict(dx=np.zeros((T, H, R, P)), ddt=np.zeros((T, H)), dtheta=np.zeros((T, H, N // 2)),
+    out = dict(dx=np.zeros((T, H, R, P)), ddt=np.zeros((T, H)), dtheta=np.zeros((T, pk.Gth, N // 2)),
                dB=np.zeros((T, G, R, N)), dC=np.zeros((T, G, R, N)), dD=np.zeros(H), dh_in=np.zeros((S, H, N, P)))
     if inp.get("lam") is not None:
         out["dlam"] = np.zeros((T, H))

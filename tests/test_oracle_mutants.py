@@ -11,7 +11,8 @@ the gradient: the rotation's transpose taken the wrong way, the angle
 derivative's sign, the previous-token weight dropped from its gradient, the
 norm's Jacobian reduced to its diagonal, the gate's derivative without its
 input factor, and the decay's share of the step's gradient dropped; in the variants, a
-per-token decay rate halved and the fixed trapezoid weight ignored."""
+per-token decay rate halved, the fixed trapezoid weight ignored and heads
+mapped to the wrong shared angle row."""
 import os
 import shutil
 import subprocess
@@ -55,6 +56,7 @@ MUTATIONS = {
                                "return a->A_tok ? 0.5 * ld(a->A_tok, a->in_dtype, i) : a->A[h];"),
     "fixed_lambda_ignored": ("return a->lam ? ld(a->lam, a->in_dtype, i) : a->lam_fixed;",
                              "return a->lam ? ld(a->lam, a->in_dtype, i) : 0.5;"),
+    "angle_group_of_head": ("return (t * Gth + h / (a->H / Gth)) * K + k;", "return (t * Gth + h % Gth) * K + k;"),
     "stale_previous": ("memcpy(bp, bc, (size_t)K * R * sizeof *bp);\n        memcpy(xp, xc, (size_t)P * R * sizeof *xp);\n",
                        ""),
 }

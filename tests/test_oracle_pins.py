@@ -155,6 +155,31 @@ def test_fixed_lambda(oracle, lam_fixed):
     assert relerr(y2, y1) < 1e-12 and relerr(h2, h1) < 1e-12
 
 
+@pytest.mark.parametrize("gth", [1, 2])
+def test_shared_angles(oracle, gth):
+    """Angle rows shared by groups of heads (head h reads row h / (H / Gth), as
+    it reads its B/C group) are the per-head form with each row repeated for
+    the heads of its group: against the independent real recurrence given the
+    repeated rows, for O1, O2 and decode."""
+    rng = np.random.default_rng(11)
+    inp = rand_inputs(rng, b=2, L=9, H=4, G=2, P=2, N=4, R=2, scale_theta=1.5)
+    inp["theta"] = inp["theta"][:, :, ::4 // gth].copy()     # [b, L, Gth, N/2]
+    full = dict(inp, theta=np.repeat(inp["theta"], 4 // gth, axis=2))
+    y1, _ = oracle.scan(inp, form=1)
+    assert relerr(y1, _real_trapezoid(full, use_rotation=True)) < 1e-12
+    # with a resumed state and previous token: O1 and O2 agree, and decode continues them
+    inp.update(h_in=rng.standard_normal((2, 4, 4, 2)), Bprev=rng.standard_normal((2, 2, 2, 4)) / 2,
+               xprev=rng.standard_normal((2, 4, 2, 2)))
+    y1, h1 = oracle.scan(inp, form=1)
+    y2, h2 = oracle.scan(inp, form=2)
+    assert relerr(y2, y1) < 1e-12 and relerr(h2, h1) < 1e-12
+    step = {k: (v[:, 0] if k in ("x", "dt", "lam", "theta", "B", "C") else v) for k, v in inp.items()
+            if k not in ("h_in",)}
+    yd, _ = oracle.decode(step, inp["h_in"])
+    yf, _ = oracle.scan(dict(inp, **{k: inp[k][:, :1] for k in ("x", "dt", "lam", "theta", "B", "C")}), form=1)
+    assert relerr(yd, yf[:, 0]) < 1e-12
+
+
 def test_lambda_one_is_exponential_euler(oracle):
     """lam = 1 removes the previous-token term: h_t = alpha_t R_t h_{t-1} +
     dt_t B_t x_t^T, Mamba-2's exponential-Euler rule with the complex
@@ -566,6 +591,14 @@ def test_gradient_variants(oracle):
     inp["A"] = None
     inp["lam"], inp["lam_fixed"] = None, 0.5
     assert fd_check(oracle, inp, rng) == 10
+
+
+def test_gradient_shared_angles(oracle):
+    """One angle row shared by all heads: its gradient sums every head's share."""
+    rng = np.random.default_rng(86)
+    inp = rand_inputs(rng, b=2, L=5, H=2, G=1, P=2, N=4, R=1, state=True, prev=True)
+    inp["theta"] = inp["theta"][:, :, :1].copy()
+    assert fd_check(oracle, inp, rng) == 11
 
 
 def test_gradient_norm_eps_zero(oracle):
