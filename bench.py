@@ -9,9 +9,11 @@ update, outputs). Inputs are synthetic (seeded, device-generated) and resident
 in HBM before timing starts. The same JSON line also carries the decode step
 (batch 256, 64 heads, N=64, R=4, fp32 state updated in place, 1000
 consecutive steps over a ring of 64 token-input sets) and the MIMO and packed
-MIMO scans as secondary figures, each with its roofline, and the SISO, MIMO
+MIMO scans as secondary figures, each with its roofline, the SISO, MIMO
 and decode workloads again with the fused block prologue / epilogue (B/C RMS
-norm, per-head B/C biases, SiLU(z) output gate).
+norm, per-head B/C biases, SiLU(z) output gate), the backward of the SISO and
+MIMO scans, the SISO decode shape (N=128, R=1) and the decode step with
+slot-indexed states (continuous batching).
 
 Timing: HIP events recorded on the stream the kernels are launched on (torch's
 current stream, which the binding passes to the library), W untimed warmup
@@ -196,11 +198,15 @@ def bench_bwd(cfg, steps, warmup, dev):
     return out
 
 
-def bench_decode(steps_per_rep, reps, dev, block=False):
+def bench_decode(steps_per_rep, reps, dev, block=False, siso=False, slots=False):
+    """The decode step over 1000 consecutive steps. siso: the SISO shape (N=128, R=1) instead of
+    MIMO; slots: the states live in a pool twice the batch, each row updating a scattered slot."""
     import torch
     import state_space_sequence_mamba3_amd as m3
     from state_space_sequence_mamba3_amd import synth
     c = synth.CONFIGS[3]
+    if siso:
+        c = dict(c, dstate=128, rank=1, name="SISO decode bf16 batch256 H64 P64 N128")
     ring = c["ring"]
     b, H, P, N, R = c["batch"], c["nheads"], c["headdim"], c["dstate"], c["rank"]
     g = torch.Generator(device=dev)
@@ -218,7 +224,11 @@ def bench_decode(steps_per_rep, reps, dev, block=False):
     C = nrm((ring, b, H, R, N), 0, 1 / math.sqrt(N)).bfloat16()
     A = -torch.exp(nrm((H,), 0, 0.5))
     D = nrm((H,))
-    h = nrm((b, H, N, P))
+    h = nrm((2 * b if slots else b, H, N, P))
+    sl = {}
+    if slots:   # rows take every other slot of the pool, in a shuffled order
+        perm = torch.randperm(2 * b, generator=torch.Generator().manual_seed(5))[:b]
+        sl = dict(slots=perm.to(torch.int32).to(dev))
     ys = torch.empty((ring, b, H, R, P), dtype=torch.bfloat16, device=dev)
     blk = {}
     if block:   # fused prologue / epilogue: BC norm, per-head biases ~ U(0.5, 1.5), gate z ~ N(0, 1)
@@ -230,7 +240,7 @@ def bench_decode(steps_per_rep, reps, dev, block=False):
     state = {"k": 0}
 
     def zarg(i):
-        return dict(blk, z=z[i]) if block else {}
+        return dict(blk, z=z[i], **sl) if block else dict(sl)
 
     def step():
         k = state["k"]
@@ -240,7 +250,7 @@ def bench_decode(steps_per_rep, reps, dev, block=False):
         state["k"] = k + 1
 
     ms, wall = timed(step, steps_per_rep, 10, stream)
-    nbytes = decode_bytes(c, block)
+    nbytes = decode_bytes(c, block) + (b * 4 if slots else 0)   # (+ the slot table)
     us = ms * 1e3
     # per-step event pairs (outside the timed region) for the median
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps_per_rep)]
@@ -278,7 +288,9 @@ def bench_decode(steps_per_rep, reps, dev, block=False):
         graph_us = (time.perf_counter() - w0) / (reps * ring) * 1e6
     except Exception as exc:  # graph capture unavailable: report the eager figures only
         print(f"# decode graph replay skipped: {exc}", file=sys.stderr)
-    return dict(workload=c["name"] + (" + BC norm, BC biases, SiLU gate" if block else ""), us_per_step=us, median_us=median, graph_wall_us=graph_us, steps=steps_per_rep,
+    name = c["name"] + (" + BC norm, BC biases, SiLU gate" if block else "") + (
+        f", slot-indexed states (pool of {2 * b})" if slots else "")
+    return dict(workload=name, us_per_step=us, median_us=median, graph_wall_us=graph_us, steps=steps_per_rep,
                 bytes_per_step=nbytes, hbm_gbs=nbytes / (us * 1e-6) / 1e9, wall_s=wall)
 
 
@@ -495,6 +507,11 @@ def main():
     if args.only == "all":
         res["decode_block"] = bench_decode(1000, 1, dev, block=True)
         print(f"# decode + block {res['decode_block']['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
+    if args.only in ("decode", "all"):
+        res["decode_siso"] = bench_decode(1000, 1, dev, siso=True)
+        print(f"# SISO decode {res['decode_siso']['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
+        res["decode_slots"] = bench_decode(1000, 1, dev, slots=True)
+        print(f"# decode with slots {res['decode_slots']['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline and args.only in ("scan", "all"):
@@ -551,7 +568,7 @@ def main():
                 roof["traffic"] = traffic_record("scan_bwd")
             sec[k] = {"workload": r["workload"], "ms": r["ms"], "tokens_per_s": r["tokens_per_s"],
                       "workspace_bytes": r["workspace_bytes"], "roofline": roof}
-    for k in ("decode", "decode_block"):
+    for k in ("decode", "decode_block", "decode_siso", "decode_slots"):
         if k in res:
             r = res[k]
             sec[k] = {"workload": r["workload"], "us_per_step": r["us_per_step"], "median_us": r["median_us"],

@@ -79,6 +79,17 @@
  *                fixed-lambda variants of the pages' ablation (Table 8 of the
  *                paper listing: 1/2 is the classical trapezoid rule, 1 the
  *                exponential-Euler rule of Mamba-2).
+ *
+ * Shared angle rows (ABI 1.4, field theta_groups of both argument structs):
+ *   theta_groups 0 (= nheads: one angle row per head, the layout above) or a
+ *                divisor Gth of nheads: theta is [batch, seqlen, Gth, N/2]
+ *                (decode: [batch, Gth, N/2]) and head h uses row
+ *                h / (nheads / Gth), the mapping of B/C groups. Gth = 1 shares
+ *                one set of angles across all heads, as B and C are shared
+ *                across heads (section "MIMO Formulation"; the pages do not say
+ *                whether the angles are shared, so both layouts are offered).
+ *                The backward's dtheta has theta's layout and sums the shares
+ *                of the heads that read a row.
  */
 #ifndef MAMBA3_H
 #define MAMBA3_H
@@ -142,6 +153,8 @@ typedef struct {
     /* Variants (ABI 1.3; see below). */
     const void *A_tok;
     float lam_fixed;
+    /* Shared angle rows (ABI 1.4; see below). */
+    int32_t theta_groups;
 } mamba3_scan_args;
 
 /* Pure host check of every argument (no HIP call). */
@@ -207,7 +220,17 @@ mamba3_status mamba3_scan_bwd(const mamba3_scan_bwd_args *args, void *stream);
  * the decode-time form H_t = alpha_t H_{t-1} + dt B_t x_t^T, y_t = H_t^T C_t).
  * Layouts: x, y [batch, H, R, P]; dt, lam [batch, H]; theta [batch, H, N/2];
  * B, C [batch, G, R, N]; Bprev [batch, G, R, N] and xprev [batch, H, R, P]
- * (both NULL = no previous-token term); h [batch, H, N, P] fp32 in/out. */
+ * (both NULL = no previous-token term); h [batch, H, N, P] fp32 in/out.
+ *
+ * Slot-indexed states for continuous batching (ABI 1.4, fields slots and
+ * nslots): with slots == NULL, batch row i updates h[i]. With slots given
+ * (device int32 [batch], 4-byte aligned), h is a pool of nslots states
+ * [nslots, H, N, P] and row i updates h[slots[i]] in place; a row whose slot
+ * is negative or >= nslots is inactive: its state and its y row are left
+ * untouched (a serving loop keeps one batch shape while sequences join and
+ * leave). Token inputs, y, Bprev and xprev stay indexed by batch row. Two
+ * active rows naming the same slot race (undefined result); slot values are
+ * device data and are not inspected on the host. */
 typedef struct {
     int32_t batch, nheads, headdim, dstate, rank, ngroups;
     int32_t dtype;
@@ -224,6 +247,10 @@ typedef struct {
     /* Variants (ABI 1.3; see below). */
     const void *A_tok;
     float lam_fixed;
+    /* ABI 1.4: shared angle rows (see the scan) and slot-indexed states. */
+    int32_t theta_groups;
+    const int32_t *slots;
+    int32_t nslots;
 } mamba3_decode_args;
 
 mamba3_status mamba3_decode_validate(const mamba3_decode_args *args);

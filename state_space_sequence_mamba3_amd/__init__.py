@@ -31,7 +31,7 @@ class ScanArgs(ctypes.Structure):
         ("A", _vp), ("D", _vp), ("h_in", _vp), ("Bprev", _vp), ("xprev", _vp),
         ("y", _vp), ("h_out", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("B_bias", _vp), ("C_bias", _vp), ("z", _vp), ("bc_norm", _i32), ("bc_eps", ctypes.c_float),
-        ("A_tok", _vp), ("lam_fixed", ctypes.c_float),
+        ("A_tok", _vp), ("lam_fixed", ctypes.c_float), ("theta_groups", _i32),
     ]
 
 
@@ -43,7 +43,7 @@ class DecodeArgs(ctypes.Structure):
         ("x", _vp), ("dt", _vp), ("lam", _vp), ("theta", _vp), ("B", _vp), ("C", _vp),
         ("Bprev", _vp), ("xprev", _vp), ("A", _vp), ("D", _vp), ("h", _vp), ("y", _vp),
         ("B_bias", _vp), ("C_bias", _vp), ("z", _vp), ("bc_norm", _i32), ("bc_eps", ctypes.c_float),
-        ("A_tok", _vp), ("lam_fixed", ctypes.c_float),
+        ("A_tok", _vp), ("lam_fixed", ctypes.c_float), ("theta_groups", _i32), ("slots", _vp), ("nslots", _i32),
     ]
 
 
@@ -138,7 +138,7 @@ def scan_args(x, dt, lam, theta, B, C, A, D=None, *, y, h_in=None, h_out=None, B
                     _ptr(x), _ptr(dt), _ptr(lam), _ptr(theta), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
                     _ptr(h_in), _ptr(Bprev), _ptr(xprev), _ptr(y), _ptr(h_out), None, 0,
                     _ptr(B_bias), _ptr(C_bias), _ptr(z), int(bool(bc_norm)), float(bc_eps), _ptr(A_tok),
-                    float(lam_fixed))
+                    float(lam_fixed), int(theta.shape[2]) if theta is not None else 0)
 
 
 def mamba3_scan_validate(args: ScanArgs) -> int:
@@ -156,8 +156,9 @@ def mamba3_scan_fwd(x, dt, lam, theta, B, C, A, D=None, *, y=None, h_in=None, h_
     layouts of mamba3.h; y and h_out are allocated when not given. Returns
     (y, h_out). B_bias, C_bias ([H, N] fp32), z (layout of x) and bc_norm /
     bc_eps switch on the fused B/C normalisation, B/C biases and output gate;
-    A_tok (layout of dt) replaces A with a per-token decay rate, and lam=None
-    uses lam_fixed for every token."""
+    A_tok (layout of dt) replaces A with a per-token decay rate, lam=None
+    uses lam_fixed for every token, and a theta of shape [b,L,Gth,N/2] with
+    Gth < H shares each angle row among H/Gth consecutive heads."""
     import torch
     if y is None:
         y = torch.empty_like(x)
@@ -230,13 +231,14 @@ def mamba3_scan_bwd(x, dt, lam, theta, B, C, A, D=None, *, dy, dh_out=None, h_in
 
 
 def decode_args(x, dt, lam, theta, B, C, A, D=None, *, h, y, Bprev=None, xprev=None, B_bias=None, C_bias=None,
-                z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5) -> DecodeArgs:
+                z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5, slots=None) -> DecodeArgs:
     b, H, R, P = x.shape
     G, N = B.shape[1], B.shape[3]
     return DecodeArgs(b, H, P, N, R, G, _dtype_code(x), _ptr(x), _ptr(dt), _ptr(lam), _ptr(theta), _ptr(B),
                       _ptr(C), _ptr(Bprev), _ptr(xprev), _ptr(A), _ptr(D), _ptr(h), _ptr(y),
                       _ptr(B_bias), _ptr(C_bias), _ptr(z), int(bool(bc_norm)), float(bc_eps), _ptr(A_tok),
-                      float(lam_fixed))
+                      float(lam_fixed), int(theta.shape[1]) if theta is not None else 0, _ptr(slots),
+                      int(h.shape[0]) if slots is not None else 0)
 
 
 def mamba3_decode_validate(args: DecodeArgs) -> int:
@@ -244,14 +246,20 @@ def mamba3_decode_validate(args: DecodeArgs) -> int:
 
 
 def mamba3_decode_step(x, dt, lam, theta, B, C, A, D=None, *, h, y=None, Bprev=None, xprev=None, stream=None,
-                       B_bias=None, C_bias=None, z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5):
+                       B_bias=None, C_bias=None, z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5,
+                       slots=None):
     """One decode step; h (fp32 [batch,H,N,P]) is updated in place. Returns y.
-    The prologue / epilogue keywords are those of mamba3_scan_fwd."""
+    The prologue / epilogue keywords are those of mamba3_scan_fwd. theta may
+    be [batch,Gth,N/2] (angle rows shared by groups of heads). With slots
+    (int32 [batch] on the device), h is a pool [nslots,H,N,P] and row i
+    updates h[slots[i]]; rows with an out-of-range slot are skipped (their y
+    rows are left as they were)."""
     import torch
     if y is None:
         y = torch.empty_like(x)
     a = decode_args(x, dt, lam, theta, B, C, A, D, h=h, y=y, Bprev=Bprev, xprev=xprev, B_bias=B_bias,
-                    C_bias=C_bias, z=z, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=A_tok, lam_fixed=lam_fixed)
+                    C_bias=C_bias, z=z, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=A_tok, lam_fixed=lam_fixed,
+                    slots=slots)
     st = lib().mamba3_decode_step(ctypes.byref(a), _stream(stream))
     if st != MAMBA3_OK:
         raise Mamba3Error(st, "mamba3_decode_step")

@@ -21,7 +21,12 @@
 // SiLU(z) after the D term.
 //
 // Variants: a per-row decay rate A_t replaces the head's A, and without a lam
-// array every row uses the fixed trapezoid weight.
+// array every row uses the fixed trapezoid weight. Angle rows may be shared by
+// groups of heads (head h reads row h / (H / Gth)).
+//
+// Slot-indexed states (continuous batching): row b updates state slots[b] of a
+// pool; a row whose slot is out of range is inactive and its workgroups return
+// before touching memory (the slot is uniform across the workgroup).
 #include "m3_common.h"
 
 namespace m3 {
@@ -38,7 +43,21 @@ struct DecodeParams {
     float eps;
     const void *A_tok;      // per-row decay rate [batch, H] (token dtype), or NULL: A per head
     float lam_fixed;        // trapezoid weight of every row when lam is NULL
+    int32_t Gth;            // angle rows per batch row (divides H)
+    const int32_t *slots;   // state slot of each batch row, or NULL: row b uses state b
+    int32_t nslots;
 };
+
+// The state slab of (row b, head hh), or NULL when the row is inactive.
+__device__ __forceinline__ float *state_slab(const DecodeParams &pr, int b, int hh, int NP) {
+    int64_t row = b;
+    if (pr.slots) {
+        const int s = pr.slots[b];
+        if (s < 0 || s >= pr.nslots) return nullptr;
+        row = s;
+    }
+    return pr.h + (row * pr.H + hh) * NP;
+}
 
 // Stand-in for an absent bias row or gate (read-only zeros), so that prologue loads are
 // unconditional.
@@ -81,7 +100,8 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
     const int bh = blockIdx.x;
     const int H = pr.H, G = pr.G;
     const int b = bh / H, hh = bh % H, g = hh / (H / G);
-    float *hs = pr.h + (int64_t)bh * N * P;
+    float *hs = state_slab(pr, b, hh, N * P);
+    if (!hs) return;   // inactive row (uniform across the workgroup)
 
     // state tile first: the bulk of the traffic, in flight while the token inputs are staged
     f32x4 st[ROWS];
@@ -93,7 +113,8 @@ __global__ __launch_bounds__(TPB) void k_decode(DecodeParams pr) {
     stage_f32<T, TPB>(sB, (const T *)pr.B + obc, N * R, tid, 0);
     stage_f32<T, TPB>(sC, (const T *)pr.C + obc, N * R, tid, CB);
     stage_f32<T, TPB>(sX, (const T *)pr.x + ox, P * R, tid, 2 * CB);
-    stage_f32<T, TPB>(sTh, (const T *)pr.theta + (int64_t)bh * (N / 2), N / 2, tid, 2 * CB + CX);
+    stage_f32<T, TPB>(sTh, (const T *)pr.theta + ((int64_t)b * pr.Gth + hh / (H / pr.Gth)) * (N / 2), N / 2, tid,
+                      2 * CB + CX);
     if (pr.Bprev) {
         stage_f32<T, TPB>(sBp, (const T *)pr.Bprev + obc, N * R, tid, 2 * CB + CX + CT);
         stage_f32<T, TPB>(sXp, (const T *)pr.xprev + ox, P * R, tid, 3 * CB + CX + CT);
@@ -228,7 +249,8 @@ __global__ __launch_bounds__(N / 16 * 64) __attribute__((amdgpu_waves_per_eu(8))
     const int bh = blockIdx.x;
     const int H = pr.H, G = pr.G;
     const int b = bh / H, hh = bh % H, g = hh / (H / G);
-    float *hs = pr.h + (int64_t)bh * N * P;
+    float *hs = state_slab(pr, b, hh, N * P);
+    if (!hs) return;   // inactive row (uniform across the workgroup)
 
     const int64_t obc = ((int64_t)b * G + g) * N * R, ox = (int64_t)bh * P * R;
     const bool has_prev = pr.Bprev != nullptr;
@@ -257,7 +279,7 @@ __global__ __launch_bounds__(N / 16 * 64) __attribute__((amdgpu_waves_per_eu(8))
         xr[j] = ((const T *)pr.x)[ox + j * P + p];
         xpr[j] = xp_src[ox + j * P + p];
     }
-    const T thr = ((const T *)pr.theta)[(int64_t)bh * (N / 2) + min(tid, N / 2 - 1)];
+    const T thr = ((const T *)pr.theta)[((int64_t)b * pr.Gth + hh / (H / pr.Gth)) * (N / 2) + min(tid, N / 2 - 1)];
     const float dt = to_f(((const T *)pr.dt)[bh]);
     const float lam = pr.lam ? to_f(((const T *)pr.lam)[bh]) : pr.lam_fixed;
     const float Ah = pr.A_tok ? to_f(((const T *)pr.A_tok)[bh]) : pr.A[hh];
@@ -385,7 +407,8 @@ static void launch_kernel(const DecodeParams &p, int64_t nblk, hipStream_t st) {
 template <typename T, int N, int P, int R>
 static mamba3_status launch_one(const mamba3_decode_args *a, hipStream_t st) {
     DecodeParams p{a->x, a->dt, a->lam, a->theta, a->B, a->C, a->Bprev, a->xprev, a->A, a->D, a->h, a->y,
-                   a->nheads, a->ngroups, a->B_bias, a->C_bias, a->z, a->bc_norm, a->bc_eps, a->A_tok, a->lam_fixed};
+                   a->nheads, a->ngroups, a->B_bias, a->C_bias, a->z, a->bc_norm, a->bc_eps, a->A_tok, a->lam_fixed,
+                   a->theta_groups ? a->theta_groups : a->nheads, a->slots, a->nslots};
     int64_t nblk = (int64_t)a->batch * a->nheads;
     if (nblk == 0) return MAMBA3_OK;
     if (a->bc_norm || a->B_bias || a->C_bias || a->z)

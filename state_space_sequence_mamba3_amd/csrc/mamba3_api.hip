@@ -52,7 +52,7 @@ const char *mamba3_status_string(mamba3_status s) {
     return "unknown status";
 }
 
-int32_t mamba3_version(void) { return 10300; }
+int32_t mamba3_version(void) { return 10400; }
 
 // Every check of the scan arguments except the availability of a forward kernel.
 static mamba3_status scan_args_check(const mamba3_scan_args *a) {
@@ -62,6 +62,7 @@ static mamba3_status scan_args_check(const mamba3_scan_args *a) {
         (a->dstate & 1) || a->rank < 1 || a->ngroups < 1 || a->chunk < 1)
         return MAMBA3_EINVAL;
     if (a->nheads % a->ngroups) return MAMBA3_EINVAL;
+    if (a->theta_groups < 0 || (a->theta_groups && a->nheads % a->theta_groups)) return MAMBA3_EINVAL;
     const bool packed = a->cu_seqlens != nullptr;
     if (packed && (a->batch != 1 || a->nseq < 1)) return MAMBA3_EINVAL;
     const int64_t S = packed ? a->nseq : a->batch;
@@ -84,9 +85,10 @@ static mamba3_status scan_args_check(const mamba3_scan_args *a) {
     // y must not overlap any input
     const int64_t es = a->dtype == MAMBA3_BF16 ? 2 : 4;
     const int64_t H = a->nheads, G = a->ngroups, P = a->headdim, N = a->dstate, R = a->rank;
+    const int64_t Gth = a->theta_groups ? a->theta_groups : H;
     Range y = span(a->y, T * H * P * R, es);
     Range ins[] = {span(a->x, T * H * P * R, es), span(a->dt, T * H, es), span(a->lam, T * H, es),
-                   span(a->theta, T * H * (N / 2), es), span(a->B, T * G * N * R, es),
+                   span(a->theta, T * Gth * (N / 2), es), span(a->B, T * G * N * R, es),
                    span(a->C, T * G * N * R, es), span(a->h_in, S * H * N * P, 4),
                    span(a->Bprev, S * G * N * R, es), span(a->xprev, S * H * P * R, es),
                    span(a->h_out, S * H * N * P, 4), span(a->B_bias, H * N, 4), span(a->C_bias, H * N, 4),
@@ -142,6 +144,7 @@ mamba3_status mamba3_scan_bwd_validate(const mamba3_scan_bwd_args *b) {
     const mamba3_scan_args *a = &b->fwd;
     const int64_t S = a->cu_seqlens ? a->nseq : a->batch, T = (int64_t)a->batch * a->seqlen;
     const int64_t H = a->nheads, G = a->ngroups, P = a->headdim, N = a->dstate, R = a->rank;
+    const int64_t Gth = a->theta_groups ? a->theta_groups : H;
     if (T > 0 && (!b->dx || !b->ddt || !b->dtheta || !b->dB || !b->dC)) return MAMBA3_EINVAL;
     if (T > 0 && a->lam && !b->dlam) return MAMBA3_EINVAL;
     if (!a->A_tok && !b->dA) return MAMBA3_EINVAL;
@@ -161,13 +164,13 @@ mamba3_status mamba3_scan_bwd_validate(const mamba3_scan_bwd_args *b) {
     const int64_t es = a->dtype == MAMBA3_BF16 ? 2 : 4;
     // every output against every input and every other output
     Range outs[] = {span(b->dx, T * H * P * R, es), span(b->ddt, T * H, es), span(b->dlam, T * H, es),
-                    span(b->dtheta, T * H * (N / 2), es), span(b->dB, T * G * N * R, es),
+                    span(b->dtheta, T * Gth * (N / 2), es), span(b->dB, T * G * N * R, es),
                     span(b->dC, T * G * N * R, es), span(b->dA, H, 4), span(b->dD, H, 4),
                     span(b->dh_in, S * H * N * P, 4), span(b->dBprev, S * G * N * R, es),
                     span(b->dxprev, S * H * P * R, es), span(b->dB_bias, H * N, 4), span(b->dC_bias, H * N, 4),
                     span(b->dz, T * H * P * R, es), span(b->dA_tok, T * H, es)};
     Range ins[] = {span(a->x, T * H * P * R, es), span(a->dt, T * H, es), span(a->lam, T * H, es),
-                   span(a->theta, T * H * (N / 2), es), span(a->B, T * G * N * R, es),
+                   span(a->theta, T * Gth * (N / 2), es), span(a->B, T * G * N * R, es),
                    span(a->C, T * G * N * R, es), span(a->h_in, S * H * N * P, 4),
                    span(a->Bprev, S * G * N * R, es), span(a->xprev, S * H * P * R, es), span(a->A, H, 4),
                    span(a->D, H, 4), span(a->B_bias, H * N, 4), span(a->C_bias, H * N, 4),
@@ -210,6 +213,9 @@ mamba3_status mamba3_decode_validate(const mamba3_decode_args *a) {
     if (a->batch < 0 || a->nheads < 1 || a->headdim < 1 || a->dstate < 2 || (a->dstate & 1) || a->rank < 1 ||
         a->ngroups < 1 || a->nheads % a->ngroups)
         return MAMBA3_EINVAL;
+    if (a->theta_groups < 0 || (a->theta_groups && a->nheads % a->theta_groups)) return MAMBA3_EINVAL;
+    if (a->nslots < 0 || (a->slots && (int64_t)a->nslots * a->nheads > INT32_MAX)) return MAMBA3_EINVAL;
+    if (a->slots && !aligned4(a->slots)) return MAMBA3_EALIGN;
     if ((int64_t)a->batch * a->nheads > INT32_MAX) return MAMBA3_EINVAL;
     if ((a->Bprev == nullptr) != (a->xprev == nullptr)) return MAMBA3_EINVAL;
     if (a->batch > 0 && (!a->x || !a->dt || !a->theta || !a->B || !a->C || !a->h || !a->y)) return MAMBA3_EINVAL;
@@ -225,16 +231,18 @@ mamba3_status mamba3_decode_validate(const mamba3_decode_args *a) {
     if (pst != MAMBA3_OK) return pst;
     const int64_t es = a->dtype == MAMBA3_BF16 ? 2 : 4;
     const int64_t b = a->batch, H = a->nheads, G = a->ngroups, P = a->headdim, N = a->dstate, R = a->rank;
+    const int64_t Gth = a->theta_groups ? a->theta_groups : H;
+    // with slots, h is the pool of nslots states; slots is an input like the token arrays
     Range y = span(a->y, b * H * P * R, es);
-    Range hh = span(a->h, b * H * N * P, 4);
+    Range hh = span(a->h, (a->slots ? a->nslots : b) * H * N * P, 4);
     Range ins[] = {span(a->x, b * H * P * R, es), span(a->dt, b * H, es), span(a->lam, b * H, es),
-                   span(a->theta, b * H * (N / 2), es), span(a->B, b * G * N * R, es),
+                   span(a->theta, b * Gth * (N / 2), es), span(a->B, b * G * N * R, es),
                    span(a->C, b * G * N * R, es), span(a->Bprev, b * G * N * R, es),
                    span(a->xprev, b * H * P * R, es), span(a->B_bias, H * N, 4), span(a->C_bias, H * N, 4),
-                   span(a->z, b * H * P * R, es), span(a->A_tok, b * H, es), hh};
+                   span(a->z, b * H * P * R, es), span(a->A_tok, b * H, es), span(a->slots, b, 4), hh};
     for (Range r : ins)
         if (overlaps(y, r)) return MAMBA3_EINVAL;
-    for (int i = 0; i < 12; i++)
+    for (int i = 0; i < 13; i++)
         if (overlaps(hh, ins[i])) return MAMBA3_EINVAL;
     if (!m3::decode_supported(a->dstate, a->headdim, a->rank, a->dtype)) return MAMBA3_EUNSUPPORTED;
     return MAMBA3_OK;

@@ -159,6 +159,7 @@ struct BfParams {
     const bf16 *Atk;
     int32_t atok_on, lam_on;
     float lam_fixed;
+    int32_t Gth;            // angle rows per token (divides H): head h reads row h / (H / Gth)
 };
 
 template <int N_, int P_, int R_, int Q_, int NW_, int UT_, int SBR_, bool EPI_>
@@ -289,8 +290,8 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     const bf16 *gC = pr.C + g * (int64_t)R * N;
     const bf16 *gX = pr.x + h * (int64_t)R * P;
     bf16 *gY = pr.y + h * (int64_t)R * P;
-    const bf16 *gTh = pr.theta + h * (int64_t)K;
-    const int64_t strBC = (int64_t)G * R * N, strX = (int64_t)H * R * P, strTh = (int64_t)H * K;
+    const bf16 *gTh = pr.theta + (h / (H / pr.Gth)) * (int64_t)K;
+    const int64_t strBC = (int64_t)G * R * N, strX = (int64_t)H * R * P, strTh = (int64_t)pr.Gth * K;
     // prologue bias rows of the head (zeros for an absent bias): [0, N) for B, [N, 2N) for C
     float *BIA = (float *)(smem + CF::OFF_BIA);
     if constexpr (CF::EPI) {
@@ -1087,6 +1088,7 @@ mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st) {
     p.Bb = a->B_bias; p.Cb = a->C_bias; p.z = (const bf16 *)a->z; p.norm = a->bc_norm; p.eps = a->bc_eps;
     p.Atk = (const bf16 *)(a->A_tok ? a->A_tok : a->dt); p.atok_on = a->A_tok != nullptr;
     p.lam = (const bf16 *)(a->lam ? a->lam : a->dt); p.lam_on = a->lam != nullptr; p.lam_fixed = a->lam_fixed;
+    p.Gth = a->theta_groups ? a->theta_groups : a->nheads;
     const int64_t nseq = a->cu_seqlens ? a->nseq : a->batch;
     const int64_t nblk = nseq * a->nheads;
     if (nblk == 0) return MAMBA3_OK;

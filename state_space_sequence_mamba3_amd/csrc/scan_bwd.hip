@@ -54,6 +54,8 @@ struct BwdParams {
     const void *A_tok;        // per-token decay rate (token dtype, layout of dt), or NULL
     void *dA_tok;             // its gradient
     float lam_fixed;          // trapezoid weight of every token when lam is NULL
+    int32_t Gth;              // angle rows per token (divides H): head h reads row h / (H / Gth)
+    float *p_dth;             // [T][H][K] per-head dtheta partials (Gth < H), else NULL
 };
 
 constexpr int kBwdThreads = 512;
@@ -134,6 +136,18 @@ __device__ __forceinline__ float ldt(const void *p, int64_t i) {
 template <typename T>
 __device__ __forceinline__ void stt(void *p, int64_t i, float v) {
     ((T *)p)[i] = from_f<T>(v);
+}
+// Offset of token tok's angle row for head h.
+__device__ __forceinline__ int64_t th_row(const BwdParams &p, int64_t tok, int h) {
+    return (tok * p.Gth + h / (p.H / p.Gth)) * (int64_t)(p.N / 2);
+}
+// Head h's share of dtheta at (token tok, pair k): the output itself with one angle row per
+// head, else the per-head partial that k_bwd_reduce sums over the heads sharing a row.
+template <typename T>
+__device__ __forceinline__ void st_dtheta(const BwdParams &p, int64_t tok, int h, int k, float v) {
+    const int64_t i = (tok * p.H + h) * (int64_t)(p.N / 2) + k;
+    if (p.p_dth) p.p_dth[i] = v;
+    else stt<T>(p.dtheta, i, v);
 }
 
 // Sum of one value per thread over the workgroup in a fixed order (wave butterflies, then the
@@ -249,7 +263,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_scan_bwd(BwdParams p) {
         for (int k = tid; k < K; k += nt) {
             float acc = 0.f;
             for (int t = 0; t < Q; t++) {
-                if (t < nq) acc += DT[t] * ldt<T>(p.theta, ((start + c0 + t) * H + h) * K + k);
+                if (t < nq) acc += DT[t] * ldt<T>(p.theta, th_row(p, start + c0 + t, h) + k);
                 float sn, cs;
                 sincosf(acc, &sn, &cs);
                 CS[t * K + k] = cs;
@@ -635,11 +649,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_scan_bwd(BwdParams p) {
         __syncthreads();
         for (int e = tid; e < nq * K; e += nt) {
             const int t = e / K, k = e % K;
-            stt<T>(p.dtheta, ((start + c0 + t) * H + h) * K + k, DT[t] * DPHI[e]);
+            st_dtheta<T>(p, start + c0 + t, h, k, DT[t] * DPHI[e]);
         }
         for (int t = tid; t < nq; t += nt) {
             float ddt = AT[t] * DS[t] + (1.f - LM[t]) * DDL[t] + LM[t] * DGM[t];
-            for (int k = 0; k < K; k++) ddt += ldt<T>(p.theta, ((start + c0 + t) * H + h) * K + k) * DPHI[t * K + k];
+            const int64_t tr = th_row(p, start + c0 + t, h);
+            for (int k = 0; k < K; k++) ddt += ldt<T>(p.theta, tr + k) * DPHI[t * K + k];
             stt<T>(p.ddt, (start + c0 + t) * H + h, ddt);
             if (p.dlam) stt<T>(p.dlam, (start + c0 + t) * H + h, DT[t] * (DGM[t] - DDL[t]));
             if (p.A_tok) stt<T>(p.dA_tok, (start + c0 + t) * H + h, DT[t] * DS[t]);
@@ -950,7 +965,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         for (int e = tid; e < Q * K / 8; e += NT) {   // theta of the chunk (zero past the end), 16-byte pieces
             const int t = e / (K / 8), k = (e % (K / 8)) * 8;
             *(bf16x8 *)(TH + t * K + k) =
-                (t < nq) ? *(const bf16x8 *)((const bf16 *)p.theta + ((start + c0 + t) * H + h) * K + k) : bf16x8{};
+                (t < nq) ? *(const bf16x8 *)((const bf16 *)p.theta + th_row(p, start + c0 + t, h) + k) : bf16x8{};
         }
         __syncthreads();
         for (int e = tid; e < Q * K; e += NT) {   // cumulative angles, one (token, pair) per thread
@@ -1399,7 +1414,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         __syncthreads();
         for (int e = tid; e < nq * K; e += NT) {
             const int t = e / K, k = e % K;
-            stt<bf16>(p.dtheta, ((start + c0 + t) * H + h) * K + k, DT[t] * DPHI[e]);
+            st_dtheta<bf16>(p, start + c0 + t, h, k, DT[t] * DPHI[e]);
         }
         for (int t0 = tid >> 4; t0 < (nq + NT / 16 - 1) / (NT / 16) * (NT / 16); t0 += NT / 16) {
             const int t = t0 < nq ? t0 : 0;   // (every lane of a group reaches the shuffles)
@@ -1558,7 +1573,8 @@ static mamba3_status launch_bwd_mfma(const BwdParams &p, int64_t nblk, hipStream
 }
 
 // Fixed-order sums of the per-slab partials: dA, dD, the bias gradients over
-// sequences; with G < H, dB, dC, dBprev over the heads of each group.
+// sequences; with G < H, dB, dC, dBprev over the heads of each group; with
+// Gth < H, dtheta over the heads sharing an angle row.
 template <typename T>
 __global__ void k_bwd_reduce(BwdParams p, int64_t T_tok, int32_t S) {
     const int H = p.H, G = p.G, N = p.N, R = p.R;
@@ -1603,6 +1619,15 @@ __global__ void k_bwd_reduce(BwdParams p, int64_t T_tok, int32_t S) {
             if (p.dBprev) ((T *)p.dBprev)[i] = from_f<T>(a);
         }
     }
+    if (p.p_dth) {
+        const int HT = H / p.Gth, K = N / 2;
+        if (i < T_tok * p.Gth * K) {
+            const int64_t t = i / ((int64_t)p.Gth * K), gq = (i / K) % p.Gth, k = i % K;
+            float a = 0.f;
+            for (int hh = 0; hh < HT; hh++) a += p.p_dth[(t * H + gq * HT + hh) * K + k];
+            ((T *)p.dtheta)[i] = from_f<T>(a);
+        }
+    }
 }
 
 // chunk length of the backward: the largest of 64, 32, ..., 1 whose LDS fits
@@ -1614,7 +1639,7 @@ int scan_bwd_chunk(int N, int P, int R) {
 
 // workspace: states, then the partial sums (each region 256-byte aligned)
 struct BwdWs {
-    size_t state, pA, pD, pBb, pCb, pB, pC, pBprev, total;
+    size_t state, pA, pD, pBb, pCb, pB, pC, pBprev, pth, total;
     int64_t chunks;
 };
 static BwdWs bwd_ws(const mamba3_scan_bwd_args *b, int Q) {
@@ -1635,6 +1660,8 @@ static BwdWs bwd_ws(const mamba3_scan_bwd_args *b, int Q) {
     w.pB = o; o += grouped ? al((size_t)T * H * R * N * 4) : 0;
     w.pC = o; o += grouped ? al((size_t)T * H * R * N * 4) : 0;
     w.pBprev = o; o += (grouped && a->Bprev) ? al((size_t)S * H * R * N * 4) : 0;
+    const bool th_shared = a->theta_groups && a->theta_groups < a->nheads;
+    w.pth = o; o += th_shared ? al((size_t)T * H * (N / 2) * 4) : 0;
     w.total = o;
     return w;
 }
@@ -1679,6 +1706,8 @@ static mamba3_status launch_bwd_t(const mamba3_scan_bwd_args *b, hipStream_t st)
     p.seqlen = a->seqlen; p.H = a->nheads; p.G = a->ngroups; p.P = a->headdim; p.N = a->dstate; p.R = a->rank;
     p.Q = Q; p.norm = a->bc_norm; p.eps = a->bc_eps;
     p.A_tok = a->A_tok; p.dA_tok = b->dA_tok; p.lam_fixed = a->lam_fixed;
+    p.Gth = a->theta_groups ? a->theta_groups : a->nheads;
+    p.p_dth = p.Gth < p.H ? (float *)(ws + w.pth) : nullptr;
     const int64_t S = p.nseq, T_tok = (int64_t)a->batch * a->seqlen;
     const int64_t nblk = S * p.H;
     if constexpr (std::is_same<T, bf16>::value) {
@@ -1696,6 +1725,7 @@ static mamba3_status launch_bwd_t(const mamba3_scan_bwd_args *b, hipStream_t st)
     }
     int64_t nred = (int64_t)p.H * p.N;
     if (grouped) nred = std::max(nred, std::max(T_tok * p.G * p.R * p.N, S * p.G * p.R * p.N));
+    if (p.p_dth) nred = std::max(nred, T_tok * p.Gth * (p.N / 2));
     if (nred > 0) hipLaunchKernelGGL(k_bwd_reduce<T>, dim3((unsigned)((nred + 255) / 256)), dim3(256), 0, st, p, T_tok, (int32_t)S);
     return hipGetLastError() == hipSuccess ? MAMBA3_OK : MAMBA3_EHIP;
 }

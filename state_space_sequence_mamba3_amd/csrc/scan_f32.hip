@@ -37,6 +37,7 @@ struct ValuParams {
     int32_t norm;               // 1: B and C columns scaled to unit RMS
     float eps;
     float lam_fixed;            // trapezoid weight of every token when lam is NULL
+    int32_t Gth;                // angle rows per token (divides H): head h reads row h / (H / Gth)
 };
 
 // Block prologue on `nrows` LDS rows of N values: scale each row to unit RMS
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
         for (int k = tid; k < K; k += nt) {
             float acc = 0.f;
             for (int t = 0; t < Q; t++) {
-                if (t < nq) acc += dts[t] * p.theta[((start + c0 + t) * H + h) * K + k];
+                if (t < nq) acc += dts[t] * p.theta[((start + c0 + t) * p.Gth + h / (H / p.Gth)) * K + k];
                 phi[t * K + k] = acc;
             }
         }
@@ -267,6 +268,7 @@ mamba3_status launch_scan_f32(const mamba3_scan_args *a, hipStream_t st) {
     p.Bb = a->B_bias; p.Cb = a->C_bias; p.z = (const float *)a->z;
     p.norm = a->bc_norm; p.eps = a->bc_eps;
     p.A_tok = (const float *)a->A_tok; p.lam_fixed = a->lam_fixed;
+    p.Gth = a->theta_groups ? a->theta_groups : a->nheads;
     size_t lds = scan_f32_lds_bytes(p.N, p.P, p.R, p.Q);
     if (hipFuncSetAttribute((const void *)k_scan_f32, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return MAMBA3_EHIP;

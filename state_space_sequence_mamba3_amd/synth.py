@@ -157,12 +157,18 @@ def block_inputs(inp: dict, seed: int, norm: bool = True, B_bias: bool = True, C
     return out
 
 
-def variant_inputs(inp: dict, seed: int, A_tok: bool = True, lam_fixed: float | None = None) -> dict:
+def variant_inputs(inp: dict, seed: int, A_tok: bool = True, lam_fixed: float | None = None,
+                   theta_groups: int | None = None) -> dict:
     """The variants: a per-token decay rate A_t ~ -exp(N(0, 0.5)) shaped like
-    dt (token dtype), replacing A; and, with lam_fixed, no lam array."""
+    dt (token dtype), replacing A; with lam_fixed, no lam array; with
+    theta_groups, Gth angle rows per token (the rows of heads 0, H/Gth, ...),
+    each shared by H/Gth consecutive heads."""
     m = inp["meta"]
     rng = np.random.Generator(np.random.PCG64(seed))
     out = dict(inp)
+    if theta_groups is not None:
+        H = inp["theta"].shape[-2]
+        out["theta"] = np.ascontiguousarray(inp["theta"][..., ::H // theta_groups, :])
     if A_tok:
         out["A_tok"] = _tok(-np.exp(_normal(rng, inp["dt"].shape, 0.0, 0.5)), m["dtype"])
     if lam_fixed is not None:

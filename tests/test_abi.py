@@ -37,7 +37,7 @@ def test_status_strings(lib):
     assert m3.status_string(m3.MAMBA3_OK) == "ok"
     for s in range(6):
         assert m3.status_string(s)
-    assert lib.mamba3_version() == 10300
+    assert lib.mamba3_version() == 10400
 
 
 BASE = 0x7F0000000000
@@ -139,6 +139,26 @@ def test_validate_variants(lib):
     assert m3.mamba3_scan_bwd_validate(b) == m3.MAMBA3_EINVAL
     b.fwd.lam = None
     assert m3.mamba3_scan_bwd_validate(b) == m3.MAMBA3_OK
+
+
+def test_validate_shared_angles_and_slots(lib):
+    # angle rows shared by groups of heads: theta_groups divides nheads (0 = one row per head)
+    for gth, st in ((0, m3.MAMBA3_OK), (1, m3.MAMBA3_OK), (2, m3.MAMBA3_OK), (3, m3.MAMBA3_EINVAL),
+                    (-1, m3.MAMBA3_EINVAL)):
+        assert m3.mamba3_scan_validate(good_scan(theta_groups=gth)) == st
+        assert m3.mamba3_decode_validate(good_decode(theta_groups=gth if gth != 3 else 3)) == st
+        b = good_bwd()
+        b.fwd.theta_groups = gth
+        assert m3.mamba3_scan_bwd_validate(b) == st
+    # slot-indexed states: the pool holds nslots states; slots is a 4-byte aligned int32 array
+    assert m3.mamba3_decode_validate(good_decode(slots=fake(13), nslots=16)) == m3.MAMBA3_OK
+    assert m3.mamba3_decode_validate(good_decode(slots=fake(13), nslots=0)) == m3.MAMBA3_OK
+    assert m3.mamba3_decode_validate(good_decode(slots=fake(13), nslots=-1)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_decode_validate(good_decode(slots=fake(13) + 2, nslots=16)) == m3.MAMBA3_EALIGN
+    assert m3.mamba3_decode_validate(good_decode(slots=fake(12), nslots=16)) == m3.MAMBA3_EINVAL   # y aliases slots
+    assert m3.mamba3_decode_validate(good_decode(slots=fake(11) + 64, nslots=16)) == m3.MAMBA3_EINVAL  # slots in h
+    # a pool of 10^6 states (8 heads of 64 x 64 fp32) reaches past y at the next fake address
+    assert m3.mamba3_decode_validate(good_decode(slots=fake(13), nslots=1_000_000)) == m3.MAMBA3_EINVAL
 
 
 def test_decode_validate_prologue(lib):

@@ -122,9 +122,11 @@ def test_block_packed_grouped(oracle):
     dict(A_tok=True),
     dict(A_tok=False, lam_fixed=0.5),
     dict(A_tok=True, lam_fixed=1.0),
+    dict(A_tok=False, theta_groups=1),
 ])
 def test_variants(oracle, cfg, variant):
-    """Per-token decay rate A_t (A absent) and fixed trapezoid weights, with a resumed state."""
+    """Per-token decay rate A_t (A absent), fixed trapezoid weights and one angle row shared by
+    all heads, with a resumed state."""
     spec = dict(batch=2, seqlen=150, nheads=2) if cfg != 4 else dict(seqlen=300, nheads=2, packed=False)
     inp = synth.resume_inputs(synth.scan_inputs(cfg, seed=71, **spec), seed=72)
     inp = synth.variant_inputs(inp, seed=73, **variant)

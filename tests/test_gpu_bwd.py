@@ -105,9 +105,11 @@ def test_bwd_bf16(oracle, name, spec, block):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("variant", [dict(A_tok=True), dict(A_tok=True, lam_fixed=0.5), dict(A_tok=False, lam_fixed=1.0)])
+@pytest.mark.parametrize("variant", [dict(A_tok=True), dict(A_tok=True, lam_fixed=0.5), dict(A_tok=False, lam_fixed=1.0),
+                                     dict(A_tok=False, theta_groups=1)])
 def test_bwd_variants(oracle, dtype, variant):
-    """Per-token decay rate (per-token dA) and fixed trapezoid weights (no dlam)."""
+    """Per-token decay rate (per-token dA), fixed trapezoid weights (no dlam) and one angle row
+    shared by the heads (dtheta sums their shares)."""
     cfg = dict(synth.CONFIGS[1], dtype=dtype, batch=1, seqlen=70, nheads=2)
     inp = synth.resume_inputs(synth.scan_inputs(cfg, seed=111), seed=112)
     inp = synth.variant_inputs(inp, seed=113, **variant)
@@ -115,6 +117,16 @@ def test_bwd_variants(oracle, dtype, variant):
         inp["A"] = None
     gr = synth.grad_inputs(inp, seed=114)
     compare(oracle, inp, gr, TOL_F32 if dtype == "f32" else TOL_BF16, f"bwd {dtype} variant {variant}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_shared_angles_grouped(oracle, dtype):
+    """Two angle rows shared by pairs of heads, with B/C groups and a resumed state."""
+    cfg = dict(synth.CONFIGS[1], dtype=dtype, batch=2, seqlen=45, nheads=4, ngroups=2)
+    inp = synth.resume_inputs(synth.scan_inputs(cfg, seed=115), seed=116)
+    inp = synth.variant_inputs(inp, seed=117, A_tok=False, theta_groups=2)
+    gr = synth.grad_inputs(inp, seed=118)
+    compare(oracle, inp, gr, TOL_F32 if dtype == "f32" else TOL_BF16, f"bwd {dtype} shared angles, G=2")
 
 
 def test_bwd_deterministic():

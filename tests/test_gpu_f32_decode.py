@@ -116,7 +116,8 @@ def test_scan_fp32_block_packed(oracle):
 
 
 @pytest.mark.parametrize("variant", [dict(A_tok=True), dict(A_tok=False, lam_fixed=0.5),
-                                     dict(A_tok=True, lam_fixed=1.0)])
+                                     dict(A_tok=True, lam_fixed=1.0), dict(A_tok=False, theta_groups=1),
+                                     dict(A_tok=True, theta_groups=2)])
 def test_scan_fp32_variants(oracle, variant):
     cfg = dict(synth.CONFIGS[0], batch=2, seqlen=90, nheads=4, headdim=16, dstate=16, rank=2, chunk=32, ngroups=2)
     inp = synth.resume_inputs(synth.scan_inputs(cfg, seed=75), seed=76)
@@ -259,11 +260,13 @@ def test_decode_block_feature_subsets(oracle, features):
     dict(batch=4, nheads=2, headdim=64, dstate=128, rank=1),
     dict(batch=5, nheads=4, headdim=16, dstate=16, rank=1, ngroups=2),
 ])
-@pytest.mark.parametrize("variant", [dict(A_tok=True), dict(A_tok=True, lam_fixed=0.5)])
+@pytest.mark.parametrize("variant", [dict(A_tok=True), dict(A_tok=True, lam_fixed=0.5),
+                                     dict(A_tok=False, theta_groups=1)])
 def test_decode_variants(oracle, dtype, tol, shape, variant):
     cfg = dict(synth.CONFIGS[3], dtype=dtype, **shape)
     inp = synth.variant_inputs(synth.decode_inputs(cfg, seed=26, ring=3), seed=27, **variant)
-    inp["A"] = None
+    if variant["A_tok"]:
+        inp["A"] = None
     note(f"decode variant {dtype} {shape} {variant}")
     yg, hg = run_decode(inp, steps=4)
     yo, ho = oracle_decode(oracle, inp, steps=4)
@@ -302,3 +305,42 @@ def test_decode_without_previous_token(oracle):
     assert state_relerr(from_dev(h), ho) < 1e-5
     num = np.abs(from_dev(y) - yo).max(axis=(2, 3))
     assert float(np.max(num / np.abs(yo).max(axis=(2, 3)))) < TOL_BF16
+
+
+def test_decode_slots(oracle):
+    """Slot-indexed states: batch rows update pool slots [3, -, 0, 6, -] (one row with a negative
+    slot, one past the pool); inactive rows leave their y rows and every other slot untouched,
+    bit for bit; active rows match the oracle from the gathered states and match, bit for bit,
+    the same step run on the gathered states without slots."""
+    import torch
+    dev = device()
+    cfg = dict(synth.CONFIGS[3], batch=5, nheads=4)
+    inp = synth.decode_inputs(cfg, seed=28, ring=1)
+    d = upload(inp, dev)
+    H, N, P = 4, cfg["dstate"], cfg["headdim"]
+    rng = np.random.default_rng(29)
+    pool0 = rng.standard_normal((7, H, N, P)).astype(np.float32)
+    slots = np.array([3, -1, 0, 6, 7], dtype=np.int32)
+    active = [i for i, s in enumerate(slots) if 0 <= s < 7]
+    pool = torch.from_numpy(pool0).to(dev)
+    sl = torch.from_numpy(slots).to(dev)
+    sentinel = torch.full_like(d["x"][0], 7.0)
+    note("decode with slots")
+    args = [d[k][0] for k in ("x", "dt", "lam", "theta", "B", "C")] + [d["A"], d["D"]]
+    m3.mamba3_decode_step(*args, h=pool, y=sentinel, Bprev=d["Bprev"], xprev=d["xprev"], slots=sl)
+    hg = torch.from_numpy(pool0[slots[active]]).to(dev).contiguous()
+    hfull = torch.zeros((5, H, N, P), dtype=torch.float32, device=dev)
+    hfull[active] = hg
+    y_ref = m3.mamba3_decode_step(*args, h=hfull, Bprev=d["Bprev"], xprev=d["xprev"])
+    torch.cuda.synchronize()
+    pool_g, y_g, y_r, h_r = from_dev(pool), from_dev(sentinel), from_dev(y_ref), from_dev(hfull)
+    untouched = [s for s in range(7) if s not in slots[active]]
+    assert np.array_equal(pool_g[untouched], pool0[untouched])
+    assert np.all(y_g[[1, 4]] == 7.0)
+    assert np.array_equal(y_g[active], y_r[active]) and np.array_equal(pool_g[slots[active]], h_r[active])
+    tok = {k: inp[k][0][active] for k in ("x", "dt", "lam", "theta", "B", "C")}
+    tok.update(A=inp["A"], D=inp["D"], Bprev=inp["Bprev"][active], xprev=inp["xprev"][active])
+    yo, ho = oracle.decode(tok, pool0[slots[active]].astype(np.float64))
+    num = np.abs(y_g[active] - yo).max(axis=(2, 3))
+    assert float(np.max(num / np.abs(yo).max(axis=(2, 3)))) < TOL_BF16
+    assert state_relerr(pool_g[slots[active]], ho) < 1e-5
