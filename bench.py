@@ -161,6 +161,38 @@ def bench_scan(cfg, steps, warmup, dev, block=False, **over):
     return out
 
 
+def bench_long(steps, warmup, dev, seqlen=32768, nseg=8):
+    """One long SISO sequence (batch 1): the plain scan (one workgroup per head walks every
+    token) against the segmented scan (nseg segments per sequence scanned as independent rows,
+    their entering states chained by mamba3_state_passing, then scanned again)."""
+    import torch
+    import state_space_sequence_mamba3_amd as m3
+    from state_space_sequence_mamba3_amd import synth
+    over = dict(batch=1, seqlen=seqlen)
+    c = dict(synth.CONFIGS[1], **over)
+    d = synth.torch_scan_inputs(1, dev, seed=11, **over)
+    y = torch.empty_like(d["x"])
+    h = torch.empty((1, c["nheads"], c["dstate"], c["headdim"]), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    args = [d[k] for k in ("x", "dt", "lam", "theta", "B", "C", "A", "D")]
+
+    def plain():
+        m3.mamba3_scan_fwd(*args, y=y, h_out=h, chunk=c["chunk"], stream=stream)
+
+    def segmented():
+        m3.mamba3_scan_segmented(*args, nseg=nseg, chunk=c["chunk"], stream=stream)
+
+    out = {}
+    for name, fn in (("plain", plain), ("segmented", segmented)):
+        ms, _ = timed(fn, steps, warmup, stream)
+        out[name] = dict(ms=ms, tokens_per_s=seqlen / (ms * 1e-3))
+    out["workload"] = f"SISO scan bf16 1x{seqlen} H64 P64 N128, plain vs {nseg} segments"
+    del d, y, h, args
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_bwd(cfg, steps, warmup, dev):
     import torch
     import state_space_sequence_mamba3_amd as m3
@@ -453,7 +485,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["scan", "decode", "bwd", "all"], default="all")
+    ap.add_argument("--only", choices=["scan", "decode", "bwd", "long", "all"], default="all")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -512,6 +544,11 @@ def main():
         print(f"# SISO decode {res['decode_siso']['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
         res["decode_slots"] = bench_decode(1000, 1, dev, slots=True)
         print(f"# decode with slots {res['decode_slots']['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
+
+    if args.only in ("long", "all"):
+        res["long"] = bench_long(max(3, args.steps // 5), max(1, args.warmup // 5), dev)
+        print(f"# long sequence: plain {res['long']['plain']['ms']:.3f} ms, segmented "
+              f"{res['long']['segmented']['ms']:.3f} ms", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline and args.only in ("scan", "all"):
@@ -577,6 +614,8 @@ def main():
                                    "unit": "GB/s", "frac": r["hbm_gbs"] / HBM_PEAK_GBS,
                                    "bytes_per_launch": r["bytes_per_step"],
                                    "traffic": traffic_record(k)}}
+    if "long" in res:
+        sec["long_sequence"] = res["long"]
     line["secondary"] = sec
     print(json.dumps(line), flush=True)
 

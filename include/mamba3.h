@@ -214,6 +214,61 @@ mamba3_status mamba3_scan_bwd_validate(const mamba3_scan_bwd_args *args);
 size_t mamba3_scan_bwd_workspace_size(const mamba3_scan_bwd_args *args);
 mamba3_status mamba3_scan_bwd(const mamba3_scan_bwd_args *args, void *stream);
 
+/* State passing between the segments of long sequences (ABI 1.4): the
+ * combine step of a context-parallel scan, and on one GPU a way to run a few
+ * long sequences as many independent segments.
+ *
+ * The chunked form hands each chunk the state that enters it (section
+ * "Parallel representation under SSD": chunk-local quadratic work plus a
+ * recurrence over chunk states). Across a segment of tokens t the recurrence
+ * is affine in its entering state: with the previous-token term of the
+ * segment's first token folded in, H_start = H_in + delta_0 Bprev xprev^T,
+ *   H_end = exp(S) R(Phi) H_start + U,   S = sum_t dt_t A_t,
+ *   Phi[k] = sum_t dt_t theta_t[k],
+ * where U is the segment's final state scanned from a zero state with no
+ * previous token (the rotations R_t are block-diagonal on the same pairs and
+ * commute, so their product is R(Phi)).
+ *
+ * Every sequence of fwd (padded mode; packed mode is not supported) is cut
+ * into nseg segments of seqlen / nseg tokens; segment k of sequence s is
+ * "segment row" s * nseg + k, which is how the token arrays [batch, seqlen,
+ * ...] read as [batch * nseg, seqlen / nseg, ...]. The intended use:
+ *   1. mamba3_scan_fwd on the segment rows with h_in, Bprev, xprev NULL:
+ *      its h_out is U [batch * nseg, H, N, P] (its y is not needed);
+ *   2. mamba3_state_passing: writes seg_h_in, seg_Bprev, seg_xprev;
+ *   3. mamba3_scan_fwd on the segment rows with h_in = seg_h_in,
+ *      Bprev = seg_Bprev, xprev = seg_xprev: y equals the whole-sequence
+ *      scan's y (up to rounding), and its h_out rows s * nseg + nseg - 1 are
+ *      the sequences' final states.
+ *
+ * fwd        the whole-sequence arguments as for mamba3_scan_fwd (batch
+ *            sequences of seqlen tokens; y, h_out, workspace, z and D are
+ *            not read; h_in, Bprev and xprev are those of the sequences).
+ * nseg       segments per sequence, >= 1, dividing seqlen.
+ * U          [batch * nseg, H, N, P] fp32, step 1's final states.
+ * seg_h_in   [batch * nseg, H, N, P] fp32 out: the state entering each
+ *            segment (fwd.h_in, or zero, for segment 0).
+ * seg_Bprev  [batch * nseg, G, R, N], seg_xprev [batch * nseg, H, R, P] out,
+ *            token dtype: the token before each segment (the last token of
+ *            the previous segment; fwd.Bprev/xprev, or zeros, for segment 0),
+ *            raw as read (the prologue, if any, is applied by the scan).
+ * h_out      [batch, H, N, P] fp32 out or NULL: the final state of every
+ *            sequence.
+ * The outputs must not overlap each other or any input. Alignment: 16 bytes
+ * for U and every output. The prologue settings of fwd (bc_norm, biases)
+ * apply to the folded previous token, as in the scan. Deterministic. */
+typedef struct {
+    mamba3_scan_args fwd;
+    int32_t nseg;
+    const float *U;
+    float *seg_h_in;
+    void *seg_Bprev, *seg_xprev;
+    float *h_out;
+} mamba3_state_passing_args;
+
+mamba3_status mamba3_state_passing_validate(const mamba3_state_passing_args *args);
+mamba3_status mamba3_state_passing(const mamba3_state_passing_args *args, void *stream);
+
 /* One decode step for a batch of independent sequences, state updated in
  * place: h <- alpha R (h + delta Bprev xprev^T) + gamma B x^T, y = h^T C + D x
  * (the same update as one token of the scan; section "MIMO Formulation" gives

@@ -58,9 +58,18 @@ class ScanBwdArgs(ctypes.Structure):
     ]
 
 
+class StatePassingArgs(ctypes.Structure):
+    """Mirror of ``mamba3_state_passing_args``."""
+    _fields_ = [
+        ("fwd", ScanArgs), ("nseg", _i32), ("U", _vp), ("seg_h_in", _vp), ("seg_Bprev", _vp), ("seg_xprev", _vp),
+        ("h_out", _vp),
+    ]
+
+
 EXPORTS = ("mamba3_scan_validate", "mamba3_scan_workspace_size", "mamba3_scan_fwd", "mamba3_scan_bwd_validate",
-           "mamba3_scan_bwd_workspace_size", "mamba3_scan_bwd", "mamba3_decode_validate",
-           "mamba3_decode_step", "mamba3_status_string", "mamba3_version")
+           "mamba3_scan_bwd_workspace_size", "mamba3_scan_bwd", "mamba3_state_passing_validate",
+           "mamba3_state_passing", "mamba3_decode_validate", "mamba3_decode_step", "mamba3_status_string",
+           "mamba3_version")
 
 _lib = None
 
@@ -228,6 +237,62 @@ def mamba3_scan_bwd(x, dt, lam, theta, B, C, A, D=None, *, dy, dh_out=None, h_in
     if st != MAMBA3_OK:
         raise Mamba3Error(st, "mamba3_scan_bwd")
     return g
+
+
+def mamba3_state_passing_validate(args: StatePassingArgs) -> int:
+    return lib().mamba3_state_passing_validate(ctypes.byref(args))
+
+
+def mamba3_state_passing(x, dt, lam, theta, B, C, A, *, nseg, U, h_in=None, Bprev=None, xprev=None, B_bias=None,
+                         C_bias=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5, want_state=True,
+                         stream=None):
+    """The state entering each of the nseg segments of every sequence, from U
+    ([batch*nseg,H,N,P], the segments scanned from a zero state with no
+    previous token). Returns (seg_h_in [batch*nseg,H,N,P] fp32, seg_Bprev,
+    seg_xprev (token before each segment), h_out [batch,H,N,P] or None)."""
+    import torch
+    b, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    SR = b * nseg
+    seg_h = torch.empty((SR, H, N, P), dtype=torch.float32, device=x.device)
+    seg_B = torch.empty((SR, G, R, N), dtype=x.dtype, device=x.device)
+    seg_x = torch.empty((SR, H, R, P), dtype=x.dtype, device=x.device)
+    h_out = torch.empty((b, H, N, P), dtype=torch.float32, device=x.device) if want_state else None
+    fwd = scan_args(x, dt, lam, theta, B, C, A, None, y=None, h_in=h_in, h_out=None, Bprev=Bprev, xprev=xprev,
+                    B_bias=B_bias, C_bias=C_bias, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=A_tok, lam_fixed=lam_fixed)
+    a = StatePassingArgs(fwd, int(nseg), _ptr(U), _ptr(seg_h), _ptr(seg_B), _ptr(seg_x), _ptr(h_out))
+    st = lib().mamba3_state_passing(ctypes.byref(a), _stream(stream))
+    if st != MAMBA3_OK:
+        raise Mamba3Error(st, "mamba3_state_passing")
+    return seg_h, seg_B, seg_x, h_out
+
+
+def mamba3_scan_segmented(x, dt, lam, theta, B, C, A, D=None, *, nseg, h_in=None, Bprev=None, xprev=None, chunk=64,
+                          want_state=True, stream=None, B_bias=None, C_bias=None, z=None, bc_norm=False, bc_eps=1e-5,
+                          A_tok=None, lam_fixed=0.5):
+    """The scan of whole sequences run as batch*nseg independent segments:
+    a scan of the segments from zero states, mamba3_state_passing, and a scan
+    of the segments from their entering states. Same results as
+    mamba3_scan_fwd up to rounding; more workgroups for few long sequences.
+    Returns (y, h_out)."""
+    b, L = x.shape[0], x.shape[1]
+    if L % nseg:
+        raise ValueError("nseg must divide seqlen")
+
+    def seg(t):
+        return None if t is None else t.reshape((b * nseg, L // nseg) + tuple(t.shape[2:]))
+
+    xs, dts, lams, ths, Bs, Cs, zs, ats = (seg(t) for t in (x, dt, lam, theta, B, C, z, A_tok))
+    kw = dict(chunk=chunk, stream=stream, B_bias=B_bias, C_bias=C_bias, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=ats,
+              lam_fixed=lam_fixed)
+    y, U = mamba3_scan_fwd(xs, dts, lams, ths, Bs, Cs, A, None, **kw)
+    seg_h, seg_B, seg_x, h_out = mamba3_state_passing(
+        x, dt, lam, theta, B, C, A, nseg=nseg, U=U, h_in=h_in, Bprev=Bprev, xprev=xprev, B_bias=B_bias,
+        C_bias=C_bias, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=A_tok, lam_fixed=lam_fixed, want_state=want_state,
+        stream=stream)
+    y, _ = mamba3_scan_fwd(xs, dts, lams, ths, Bs, Cs, A, D, y=y, h_in=seg_h, Bprev=seg_B, xprev=seg_x,
+                           want_state=False, z=zs, **kw)
+    return y.reshape(x.shape), h_out
 
 
 def decode_args(x, dt, lam, theta, B, C, A, D=None, *, h, y, Bprev=None, xprev=None, B_bias=None, C_bias=None,

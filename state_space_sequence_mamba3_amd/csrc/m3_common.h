@@ -43,5 +43,7 @@ mamba3_status launch_scan_bwd(const mamba3_scan_bwd_args *b, hipStream_t st);
 size_t scan_bwd_workspace_bytes(const mamba3_scan_bwd_args *b);
 int scan_bwd_chunk(int N, int P, int R);
 bool decode_supported(int N, int P, int R, int dtype);
+mamba3_status launch_state_passing(const mamba3_state_passing_args *a, hipStream_t st);
+size_t state_passing_lds_bytes(int N, int P, int R);
 
 }  // namespace m3

@@ -54,8 +54,9 @@ const char *mamba3_status_string(mamba3_status s) {
 
 int32_t mamba3_version(void) { return 10400; }
 
-// Every check of the scan arguments except the availability of a forward kernel.
-static mamba3_status scan_args_check(const mamba3_scan_args *a) {
+// Every check of the scan arguments except the availability of a forward kernel. need_y = false
+// for callers that do not write y (y must then be NULL).
+static mamba3_status scan_args_check(const mamba3_scan_args *a, bool need_y = true) {
     if (!a) return MAMBA3_EINVAL;
     if (a->dtype != MAMBA3_F32 && a->dtype != MAMBA3_BF16) return MAMBA3_EINVAL;
     if (a->batch < 0 || a->seqlen < 0 || a->nheads < 1 || a->headdim < 1 || a->dstate < 2 ||
@@ -69,7 +70,8 @@ static mamba3_status scan_args_check(const mamba3_scan_args *a) {
     const int64_t T = (int64_t)a->batch * a->seqlen;
     if (S * a->nheads > INT32_MAX) return MAMBA3_EINVAL;
     if ((a->Bprev == nullptr) != (a->xprev == nullptr)) return MAMBA3_EINVAL;
-    if (T > 0 && (!a->x || !a->dt || !a->theta || !a->B || !a->C || !a->y)) return MAMBA3_EINVAL;
+    if (T > 0 && (!a->x || !a->dt || !a->theta || !a->B || !a->C || (need_y && !a->y))) return MAMBA3_EINVAL;
+    if (!need_y && a->y) return MAMBA3_EINVAL;
     if (!a->A && !a->A_tok) return MAMBA3_EINVAL;
     if (!a->lam && !std::isfinite(a->lam_fixed)) return MAMBA3_EINVAL;
     if (a->A_tok && !aligned_elem(a->A_tok, a->dtype)) return MAMBA3_EALIGN;
@@ -205,6 +207,53 @@ mamba3_status mamba3_scan_bwd(const mamba3_scan_bwd_args *b, void *stream) {
     const mamba3_status st = mamba3_scan_bwd_validate(b);
     if (st != MAMBA3_OK) return st;
     return m3::launch_scan_bwd(b, (hipStream_t)stream);
+}
+
+mamba3_status mamba3_state_passing_validate(const mamba3_state_passing_args *sp) {
+    if (!sp) return MAMBA3_EINVAL;
+    // the sequences' arguments: y, h_out, workspace, z and D are not read
+    mamba3_scan_args f = sp->fwd;
+    f.y = nullptr;
+    f.h_out = nullptr;
+    f.workspace = nullptr;
+    f.workspace_bytes = 0;
+    f.z = nullptr;
+    f.D = nullptr;
+    mamba3_status st = scan_args_check(&f, false);
+    if (st != MAMBA3_OK) return st;
+    if (f.cu_seqlens) return MAMBA3_EUNSUPPORTED;   // padded sequences only
+    if (sp->nseg < 1 || f.seqlen < 1 || f.seqlen % sp->nseg) return MAMBA3_EINVAL;
+    const int64_t b = f.batch, T = b * f.seqlen, SR = b * sp->nseg;
+    if (SR * f.nheads > INT32_MAX) return MAMBA3_EINVAL;
+    if (b > 0 && (!sp->U || !sp->seg_h_in || !sp->seg_Bprev || !sp->seg_xprev)) return MAMBA3_EINVAL;
+    const void *al16[] = {sp->U, sp->seg_h_in, sp->seg_Bprev, sp->seg_xprev, sp->h_out};
+    for (const void *q : al16)
+        if (q && !aligned16(q)) return MAMBA3_EALIGN;
+    const int64_t es = f.dtype == MAMBA3_BF16 ? 2 : 4;
+    const int64_t H = f.nheads, G = f.ngroups, P = f.headdim, N = f.dstate, R = f.rank;
+    const int64_t Gth = f.theta_groups ? f.theta_groups : H;
+    Range outs[] = {span(sp->seg_h_in, SR * H * N * P, 4), span(sp->seg_Bprev, SR * G * N * R, es),
+                    span(sp->seg_xprev, SR * H * P * R, es), span(sp->h_out, b * H * N * P, 4)};
+    Range ins[] = {span(f.x, T * H * P * R, es), span(f.dt, T * H, es), span(f.lam, T * H, es),
+                   span(f.theta, T * Gth * (N / 2), es), span(f.B, T * G * N * R, es), span(f.A, H, 4),
+                   span(f.h_in, b * H * N * P, 4), span(f.Bprev, b * G * N * R, es),
+                   span(f.xprev, b * H * P * R, es), span(f.B_bias, H * N, 4), span(f.A_tok, T * H, es),
+                   span(sp->U, SR * H * N * P, 4)};
+    const int nout = sizeof outs / sizeof outs[0];
+    for (int i = 0; i < nout; i++) {
+        for (Range r : ins)
+            if (overlaps(outs[i], r)) return MAMBA3_EINVAL;
+        for (int j = i + 1; j < nout; j++)
+            if (overlaps(outs[i], outs[j])) return MAMBA3_EINVAL;
+    }
+    if (m3::state_passing_lds_bytes(f.dstate, f.headdim, f.rank) > kMaxLds) return MAMBA3_EUNSUPPORTED;
+    return MAMBA3_OK;
+}
+
+mamba3_status mamba3_state_passing(const mamba3_state_passing_args *sp, void *stream) {
+    const mamba3_status st = mamba3_state_passing_validate(sp);
+    if (st != MAMBA3_OK) return st;
+    return m3::launch_state_passing(sp, (hipStream_t)stream);
 }
 
 mamba3_status mamba3_decode_validate(const mamba3_decode_args *a) {

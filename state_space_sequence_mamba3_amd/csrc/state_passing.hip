@@ -1,0 +1,216 @@
+// State passing between the segments of long sequences.
+//
+// Across a segment the recurrence of Proposition 4 ("Complex-Valued State
+// Space Models") is affine in the state that enters it. Folding the segment's
+// first previous-token term into that state, H_start = H_in + delta_0 Bprev
+// xprev^T, the segment leaves
+//   H_end = exp(S) R(Phi) H_start + U,  S = sum_t dt_t A_t,  Phi[k] = sum_t dt_t theta_t[k],
+// where U is the segment scanned from a zero state with no previous token: the
+// per-token transitions alpha_t R_t are a scalar decay times rotations of the
+// same state pairs, so they commute and multiply to exp(S) R(Phi). This is the
+// chunk-state recurrence of the chunked form (section "Parallel
+// representation under SSD") taken over segments instead of chunks.
+//
+// Two kernels. k_segment_sums reduces dt A and dt theta over every segment's
+// tokens, all (segment, head) pairs in parallel (fixed order: strided
+// per-thread partial sums, then the partials in index order). k_state_passing
+// then walks each (sequence, head)'s segments in order with the fp32 state in
+// LDS: per segment it writes the entering state and the token before the
+// segment, and applies the affine map. The state update is elementwise
+// per (pair, column), one thread per element; U and the states are read and
+// written as whole rows of P consecutive floats.
+#include "m3_common.h"
+
+namespace m3 {
+
+struct SPParams {
+    const void *x, *dt, *lam, *theta, *B, *Bprev, *xprev, *A_tok;
+    const float *A, *h_in, *Bb, *U;
+    float *seg_h, *h_out;
+    void *seg_B, *seg_x;
+    int32_t seqlen, nseg, H, G, P, N, R, Gth;
+    int32_t norm;
+    float eps, lam_fixed;
+};
+
+constexpr int kSPThreads = 256;
+
+// LDS layout (floats)
+struct SPLayout {
+    int hs, phi, bl, xl, misc, total;
+};
+__host__ __device__ inline SPLayout sp_layout(int N, int P, int R) {
+    SPLayout L;
+    const int K = N / 2;
+    int o = 0;
+    L.hs = o; o += N * P;
+    L.phi = o; o += 2 * K;   // cos, sin of the segment's total angles
+    L.bl = o; o += R * N;
+    L.xl = o; o += R * P;
+    L.misc = o; o += 4;
+    L.total = o;
+    return L;
+}
+
+size_t state_passing_lds_bytes(int N, int P, int R) { return (size_t)sp_layout(N, P, R).total * sizeof(float); }
+
+// Per (segment row, head): S = sum_t dt_t A_t and Phi[k] = sum_t dt_t theta_t[k] over the
+// segment's tokens, staged in the first K + 1 floats of the segment's seg_h_in block (which
+// k_state_passing reads before it writes the entering state there). Every (row, head) runs in
+// parallel; each thread sums a strided set of tokens, then the partials are added in index order.
+template <typename T>
+__global__ __launch_bounds__(kSPThreads) void k_segment_sums(SPParams p) {
+    __shared__ float part[kSPThreads], spart[kSPThreads];
+    const int H = p.H, K = p.N / 2, tid = threadIdx.x, NT = kSPThreads;
+    const int TL = K >= NT ? 1 : NT / K;
+    const int64_t rh = blockIdx.x;                  // row * H + h
+    const int h = (int)(rh % H), gq = h / (H / p.Gth);
+    const int64_t row = rh / H, s = row / p.nseg, k = row % p.nseg;
+    const int Ls = p.seqlen / p.nseg;
+    const int64_t t0 = s * p.seqlen + k * Ls;
+    const T *dt = (const T *)p.dt, *th = (const T *)p.theta;
+    float *out = p.seg_h + rh * (int64_t)p.N * p.P;
+    float a = 0.f;
+#pragma unroll 8
+    for (int t = tid; t < Ls; t += NT) {
+        const int64_t i = (t0 + t) * H + h;
+        a += to_f(dt[i]) * (p.A_tok ? to_f(((const T *)p.A_tok)[i]) : p.A[h]);
+    }
+    spart[tid] = a;
+    for (int kk = 0; kk < K; kk += NT / TL) {   // pairs [kk, kk + NT / TL) per pass (K > NT only)
+        const int i = kk + tid % (NT / TL), j = tid / (NT / TL);
+        float b = 0.f;
+        if (i < K) {
+#pragma unroll 8
+            for (int t = j; t < Ls; t += TL) {
+                const int64_t tok = t0 + t;
+                b += to_f(dt[tok * H + h]) * to_f(th[(tok * p.Gth + gq) * K + i]);
+            }
+        }
+        part[tid] = b;
+        __syncthreads();
+        if (tid < NT / TL && kk + tid < K) {
+            float c = 0.f;
+            for (int jj = 0; jj < TL; jj++) c += part[jj * (NT / TL) + tid];
+            out[1 + kk + tid] = c;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        float c = 0.f;
+        for (int jj = 0; jj < NT; jj++) c += spart[jj];
+        out[0] = c;
+    }
+}
+
+// One workgroup per (sequence, head): the chain over the sequence's segments.
+template <typename T>
+__global__ __launch_bounds__(kSPThreads) void k_state_passing(SPParams p) {
+    extern __shared__ float smem[];
+    const int N = p.N, P = p.P, R = p.R, H = p.H, G = p.G, K = N / 2;
+    const SPLayout L = sp_layout(N, P, R);
+    float *Hs = smem + L.hs, *PHI = smem + L.phi, *BL = smem + L.bl, *XL = smem + L.xl, *MISC = smem + L.misc;
+    const int tid = threadIdx.x, NT = kSPThreads;
+    const int s = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
+    const int Ls = p.seqlen / p.nseg;
+    const int64_t NP = (int64_t)N * P;
+    const T *dt = (const T *)p.dt;
+
+    for (int64_t e = tid; e < NP; e += NT) Hs[e] = p.h_in ? p.h_in[((int64_t)s * H + h) * NP + e] : 0.f;
+
+    for (int k = 0; k < p.nseg; k++) {
+        const int64_t t0 = (int64_t)s * p.seqlen + (int64_t)k * Ls;   // first token of the segment
+        const int64_t row = (int64_t)s * p.nseg + k;                   // segment row
+        float *out = p.seg_h + (row * H + h) * NP;
+        // the segment's sums, staged by k_segment_sums in this block of seg_h_in
+        for (int i = tid; i < K; i += NT) sincosf(out[1 + i], &PHI[K + i], &PHI[i]);
+        // the token before the segment: the previous segment's last token, or the sequence's own
+        const bool has_prev = k > 0 || p.Bprev;
+        const T *bsrc = k > 0 ? (const T *)p.B + ((t0 - 1) * G + g) * R * N
+                              : (p.Bprev ? (const T *)p.Bprev + ((int64_t)s * G + g) * R * N : nullptr);
+        const T *xsrc = k > 0 ? (const T *)p.x + ((t0 - 1) * H + h) * R * P
+                              : (p.xprev ? (const T *)p.xprev + ((int64_t)s * H + h) * R * P : nullptr);
+        for (int e = tid; e < R * N; e += NT) {
+            const T v = has_prev ? bsrc[e] : from_f<T>(0.f);
+            BL[e] = to_f(v);
+            if (h % (H / G) == 0) ((T *)p.seg_B)[(row * G + g) * R * N + e] = v;   // one head per group writes
+        }
+        for (int e = tid; e < R * P; e += NT) {
+            const T v = has_prev ? xsrc[e] : from_f<T>(0.f);
+            XL[e] = to_f(v);
+            ((T *)p.seg_x)[(row * H + h) * R * P + e] = v;
+        }
+        if (tid == 0) {
+            MISC[0] = expf(out[0]);
+            const float lam = p.lam ? to_f(((const T *)p.lam)[t0 * H + h]) : p.lam_fixed;
+            MISC[1] = has_prev ? (1.f - lam) * to_f(dt[t0 * H + h]) : 0.f;   // delta of the first token
+        }
+        __syncthreads();   // the staged sums are read: the block may now be overwritten
+        // prologue on the folded previous token: unit-RMS columns and the head's bias, as the scan does
+        if (has_prev && (p.norm || p.Bb)) {
+            if (tid < R) {
+                float *col = BL + tid * N;
+                float inv = 1.f;
+                if (p.norm) {
+                    float ss = 0.f;
+                    for (int n = 0; n < N; n++) ss += col[n] * col[n];
+                    inv = 1.f / sqrtf(ss / N + p.eps);
+                }
+                for (int n = 0; n < N; n++) col[n] = col[n] * inv + (p.Bb ? p.Bb[(int64_t)h * N + n] : 0.f);
+            }
+            __syncthreads();
+        }
+        // entering state out, then H <- exp(S) R(Phi) (H + delta_0 Bprev xprev^T) + U
+        const float decay = MISC[0], d0 = MISC[1];
+        const float *Uk = p.U + (row * H + h) * NP;
+        for (int e = tid; e < K * P; e += NT) {
+            const int i = e / P, c = e % P;
+            const int64_t o0 = (int64_t)(2 * i) * P + c, o1 = o0 + P;
+            float u0 = Hs[o0], u1 = Hs[o1];
+            out[o0] = u0;
+            out[o1] = u1;
+            float f0 = 0.f, f1 = 0.f;
+            for (int r = 0; r < R; r++) {
+                f0 += BL[r * N + 2 * i] * XL[r * P + c];
+                f1 += BL[r * N + 2 * i + 1] * XL[r * P + c];
+            }
+            u0 += d0 * f0;
+            u1 += d0 * f1;
+            const float cs = PHI[i], sn = PHI[K + i];
+            Hs[o0] = decay * (cs * u0 - sn * u1) + Uk[o0];
+            Hs[o1] = decay * (sn * u0 + cs * u1) + Uk[o1];
+        }
+        __syncthreads();   // PHI, BL, XL, MISC are rewritten by the next segment
+    }
+    if (p.h_out)
+        for (int64_t e = tid; e < NP; e += NT) p.h_out[((int64_t)s * H + h) * NP + e] = Hs[e];
+}
+
+mamba3_status launch_state_passing(const mamba3_state_passing_args *a, hipStream_t st) {
+    const mamba3_scan_args *f = &a->fwd;
+    SPParams p;
+    p.x = f->x; p.dt = f->dt; p.lam = f->lam; p.theta = f->theta; p.B = f->B;
+    p.Bprev = f->Bprev; p.xprev = f->xprev; p.A_tok = f->A_tok;
+    p.A = f->A; p.h_in = f->h_in; p.Bb = f->B_bias; p.U = a->U;
+    p.seg_h = a->seg_h_in; p.h_out = a->h_out; p.seg_B = a->seg_Bprev; p.seg_x = a->seg_xprev;
+    p.seqlen = f->seqlen; p.nseg = a->nseg; p.H = f->nheads; p.G = f->ngroups; p.P = f->headdim;
+    p.N = f->dstate; p.R = f->rank; p.Gth = f->theta_groups ? f->theta_groups : f->nheads;
+    p.norm = f->bc_norm; p.eps = f->bc_eps; p.lam_fixed = f->lam_fixed;
+    const int64_t nblk = (int64_t)f->batch * f->nheads;
+    if (nblk == 0) return MAMBA3_OK;
+    const size_t lds = state_passing_lds_bytes(p.N, p.P, p.R);
+    const void *fn = f->dtype == MAMBA3_BF16 ? (const void *)k_state_passing<bf16> : (const void *)k_state_passing<float>;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return MAMBA3_EHIP;
+    const int64_t nrow = nblk * a->nseg;   // (segment row, head) pairs
+    if (f->dtype == MAMBA3_BF16) {
+        hipLaunchKernelGGL(k_segment_sums<bf16>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
+        hipLaunchKernelGGL(k_state_passing<bf16>, dim3((unsigned)nblk), dim3(kSPThreads), lds, st, p);
+    } else {
+        hipLaunchKernelGGL(k_segment_sums<float>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
+        hipLaunchKernelGGL(k_state_passing<float>, dim3((unsigned)nblk), dim3(kSPThreads), lds, st, p);
+    }
+    return hipGetLastError() == hipSuccess ? MAMBA3_OK : MAMBA3_EHIP;
+}
+
+}  // namespace m3

@@ -161,6 +161,37 @@ def test_validate_shared_angles_and_slots(lib):
     assert m3.mamba3_decode_validate(good_decode(slots=fake(13), nslots=1_000_000)) == m3.MAMBA3_EINVAL
 
 
+def good_sp(**over):
+    fwd = good_scan(y=None, h_out=None, h_in=fake(11), Bprev=fake(12), xprev=fake(13))
+    a = m3.StatePassingArgs(fwd=fwd, nseg=4, U=fake(20), seg_h_in=fake(21), seg_Bprev=fake(22), seg_xprev=fake(23),
+                            h_out=fake(24))
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_state_passing_validate(lib):
+    assert m3.mamba3_state_passing_validate(good_sp()) == m3.MAMBA3_OK
+    assert m3.mamba3_state_passing_validate(good_sp(h_out=None)) == m3.MAMBA3_OK
+    assert m3.mamba3_state_passing_validate(good_sp(nseg=3)) == m3.MAMBA3_EINVAL      # 100 tokens, 3 segments
+    assert m3.mamba3_state_passing_validate(good_sp(nseg=0)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_state_passing_validate(good_sp(U=None)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_state_passing_validate(good_sp(seg_xprev=None)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_state_passing_validate(good_sp(seg_h_in=fake(21) + 4)) == m3.MAMBA3_EALIGN
+    assert m3.mamba3_state_passing_validate(good_sp(seg_h_in=fake(20))) == m3.MAMBA3_EINVAL   # aliases U
+    assert m3.mamba3_state_passing_validate(good_sp(seg_Bprev=fake(5))) == m3.MAMBA3_EINVAL   # aliases B
+    assert m3.mamba3_state_passing_validate(good_sp(h_out=fake(23))) == m3.MAMBA3_EINVAL      # aliases seg_xprev
+    a = good_sp()
+    a.fwd.y, a.fwd.z = fake(9), fake(10)                                                       # ignored: not read
+    assert m3.mamba3_state_passing_validate(a) == m3.MAMBA3_OK
+    a = good_sp()
+    a.fwd.cu_seqlens, a.fwd.batch, a.fwd.nseq = fake(30), 1, 2                                 # packed: not supported
+    assert m3.mamba3_state_passing_validate(a) == m3.MAMBA3_EUNSUPPORTED
+    a = good_sp()
+    a.fwd.seqlen = 0
+    assert m3.mamba3_state_passing_validate(a) == m3.MAMBA3_EINVAL
+
+
 def test_decode_validate_prologue(lib):
     ok = dict(B_bias=fake(14), C_bias=fake(15), z=fake(16), bc_norm=1, bc_eps=1e-6)
     assert m3.mamba3_decode_validate(good_decode(**ok)) == m3.MAMBA3_OK
