@@ -99,6 +99,10 @@ def lib():
         l.mamba3_scan_bwd_workspace_size.restype = ctypes.c_size_t
         l.mamba3_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdArgs), _vp]
         l.mamba3_scan_bwd.restype = ctypes.c_int
+        l.mamba3_state_passing_validate.argtypes = [ctypes.POINTER(StatePassingArgs)]
+        l.mamba3_state_passing_validate.restype = ctypes.c_int
+        l.mamba3_state_passing.argtypes = [ctypes.POINTER(StatePassingArgs), _vp]
+        l.mamba3_state_passing.restype = ctypes.c_int
         l.mamba3_decode_validate.argtypes = [ctypes.POINTER(DecodeArgs)]
         l.mamba3_decode_validate.restype = ctypes.c_int
         l.mamba3_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]

@@ -33,6 +33,14 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(m3.EXPORTS)
 
 
+def test_binding_declares_every_signature(lib):
+    # a pointer argument passed without a declared signature would be truncated to a C int
+    l = m3.lib()
+    for name in m3.EXPORTS:
+        if name != "mamba3_version":
+            assert getattr(l, name).argtypes is not None, name
+
+
 def test_status_strings(lib):
     assert m3.status_string(m3.MAMBA3_OK) == "ok"
     for s in range(6):

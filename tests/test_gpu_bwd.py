@@ -137,3 +137,42 @@ def test_bwd_deterministic():
     a, b = run_bwd(inp, gr), run_bwd(inp, gr)
     for k in a:
         assert a[k].tobytes() == b[k].tobytes(), k
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_bwd_full_size_sampled_heads(oracle, cfg):
+    """The bf16 backward at the full layer workload (8 x 4096 tokens, 64 heads) in the bench's launch
+    configuration; for two sampled heads, every gradient of all 8 sequences (dA, dD of the head
+    included) against the oracle run on that head's inputs alone (G = H: a head reads only its own
+    B, C and angle rows)."""
+    import torch
+    c = synth.CONFIGS[cfg]
+    note(f"full-size bf16 backward config {cfg}: {c['name']}")
+    dev = device()
+    d = synth.torch_scan_inputs(cfg, dev, seed=cfg)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(100 + cfg)
+    dy = torch.randn(d["x"].shape, generator=gen, device=dev, dtype=torch.float32).to(d["x"].dtype)
+    g = m3.mamba3_scan_bwd(d["x"], d["dt"], d["lam"], d["theta"], d["B"], d["C"], d["A"], d["D"], dy=dy)
+    torch.cuda.synchronize()
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    rng = np.random.default_rng(cfg)
+    for hh in (0, int(rng.integers(1, c["nheads"]))):
+        one = {k: bits(d[k][:, :, hh:hh + 1]) for k in ("x", "dt", "lam", "theta", "B", "C")}
+        one.update(A=d["A"][hh:hh + 1].cpu().numpy(), D=d["D"][hh:hh + 1].cpu().numpy())
+        dy1 = synth.bits_to_f32(bits(dy[:, :, hh:hh + 1])).astype(np.float64)
+        go = oracle.scan_bwd(one, dy1, None)
+        worst = {}
+        for k in ("dx", "ddt", "dlam", "dtheta", "dB", "dC"):
+            a = from_dev(g[k][:, :, hh:hh + 1]).reshape(go[k].shape)
+            worst[k] = float(np.abs(a - go[k]).max() / np.abs(go[k]).max())
+        for k in ("dA", "dD"):
+            worst[k] = float(abs(from_dev(g[k][hh:hh + 1])[0] - go[k][0]) / abs(go[k][0]))
+        note(f"  head {hh}: " + " ".join(f"{k} {v:.1e}" for k, v in worst.items()))
+        bad = {k: v for k, v in worst.items() if not v < TOL_BF16}
+        assert not bad, bad
+    del d, dy, g
+    torch.cuda.empty_cache()
