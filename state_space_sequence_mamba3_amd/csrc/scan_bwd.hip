@@ -798,9 +798,16 @@ __device__ __forceinline__ bf16x8 op_tr(const bf16 *m, int ld, int k0, int c0, i
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 // sum over the 16 lanes of a lane group (i = l % 16), and over the 4 groups (g = l / 16)
+// (lane-to-lane moves within a row of 16 lanes: DPP, no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
+    v += dppf<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+    v += dppf<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+    v += dppf<0x141>(v);   // row_half_mirror: the other quad of the 8
+    v += dppf<0x140>(v);   // row_mirror: the other 8 lanes of the row
     return v;
 }
 __device__ __forceinline__ float sum_groups(float v) {
@@ -876,9 +883,19 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     bf16 *dSb = (bf16 *)(smem + CF::O_DSB);
 
     const int H = p.H, G = p.G;
-    const int tid = threadIdx.x, lane = tid & 63;
+    int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int li = lane & 15, lg = lane >> 4;
+    int li = lane & 15, lg = lane >> 4;
+    // With N = 128 the lane-derived values are made opaque once per chunk, so that address math is
+    // recomputed where it is used instead of being hoisted out of the chunk loops and spilled.
+    auto refresh = [&]() {
+        if constexpr (N == 128) {
+            asm volatile("" : "+v"(tid));
+            lane = tid & 63;
+            li = lane & 15;
+            lg = lane >> 4;
+        }
+    };
     const int s = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
     const bf16 *gx = (const bf16 *)p.x, *gB = (const bf16 *)p.B, *gC = (const bf16 *)p.C, *gdy = (const bf16 *)p.dy;
 
@@ -935,15 +952,74 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             }
         }
     };
+    // A chunk's raw token inputs are loaded into registers one chunk ahead (issued after the
+    // current chunk is staged, consumed when the next one is), so their latency overlaps the
+    // current chunk's work. Each thread loads the pieces it later stages; a token past the end
+    // reads the chunk's last token and is masked when consumed. The pieces: 16 bytes of B (and
+    // C), of x (and dy) and of theta; one element of the previous token's B and x; and, in wave 0,
+    // one token's dt, lam and A_t.
+    constexpr int PF_B = (QR * N / 8 + NT - 1) / NT, PF_X = (QR * P / 8 + NT - 1) / NT;
+    constexpr int PF_T = (Q * K / 8 + NT - 1) / NT, PF_V = (R * N + NT - 1) / NT, PF_U = (R * P + NT - 1) / NT;
+    bf16x8 pB[PF_B], pC[PF_B], pX[PF_X], pD[PF_X], pT[PF_T];
+    bf16 pBp[PF_V], pXp[PF_U], pdt = {}, plm = {}, pat = {};
+    auto prefetch = [&](int64_t c, bool rev) {
+        const int64_t c0 = c * Q;
+        const int last = (int)min((int64_t)Q, len - c0) - 1;
+#pragma unroll
+        for (int i = 0; i < PF_B; i++) {
+            const int e = tid + i * NT;
+            if (e < QR * N / 8) {
+                const int r = e / (N / 8), n = (e % (N / 8)) * 8;
+                const int64_t o = tokB(c0 + min(r / R, last)) + (r % R) * N + n;
+                pB[i] = *(const bf16x8 *)(gB + o);
+                if (rev) pC[i] = *(const bf16x8 *)(gC + o);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PF_X; i++) {
+            const int e = tid + i * NT;
+            if (e < QR * P / 8) {
+                const int r = e / (P / 8), pp = (e % (P / 8)) * 8;
+                const int64_t o = tokX(c0 + min(r / R, last)) + (r % R) * P + pp;
+                pX[i] = *(const bf16x8 *)(gx + o);
+                if (rev) pD[i] = *(const bf16x8 *)(gdy + o);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PF_T; i++) {
+            const int e = tid + i * NT;
+            if (e < Q * K / 8)
+                pT[i] = *(const bf16x8 *)((const bf16 *)p.theta + th_row(p, start + c0 + min(e / (K / 8), last), h) +
+                                          (e % (K / 8)) * 8);
+        }
+        const bf16 *srcB = c0 > 0 ? gB + tokB(c0 - 1) : has_prev ? (const bf16 *)p.Bprev + ((int64_t)s * G + g) * R * N : nullptr;
+        const bf16 *srcX = c0 > 0 ? gx + tokX(c0 - 1) : has_prev ? (const bf16 *)p.xprev + sh * R * P : nullptr;
+#pragma unroll
+        for (int i = 0; i < PF_V; i++) {
+            const int e = tid + i * NT;
+            if (srcB && e < R * N) pBp[i] = srcB[e];
+        }
+#pragma unroll
+        for (int i = 0; i < PF_U; i++) {
+            const int e = tid + i * NT;
+            if (srcX && e < R * P) pXp[i] = srcX[e];
+        }
+        if (wave == 0) {
+            const int64_t i = (start + c0 + min(lane, last)) * H + h;
+            pdt = ((const bf16 *)p.dt)[i];
+            if (p.lam) plm = ((const bf16 *)p.lam)[i];
+            if (p.A_tok) pat = ((const bf16 *)p.A_tok)[i];
+        }
+    };
     auto load_scalars = [&](int64_t c0, int nq) {
         static_assert(Q <= 64, "one wave scans the chunk");
         if (wave == 0) {   // per-token scalars and the log-decay prefix (wave scan)
             const int t = lane;
             float dtv = 0.f, lv = 0.f, av = Ah;
             if (t < nq) {
-                dtv = ldt<bf16>(p.dt, (start + c0 + t) * H + h);
-                lv = p.lam ? ldt<bf16>(p.lam, (start + c0 + t) * H + h) : p.lam_fixed;
-                if (p.A_tok) av = ldt<bf16>(p.A_tok, (start + c0 + t) * H + h);
+                dtv = (float)pdt;
+                lv = p.lam ? (float)plm : p.lam_fixed;
+                if (p.A_tok) av = (float)pat;
             }
             float acc = dtv * av;
 #pragma unroll
@@ -962,10 +1038,13 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
                 G1[t] = lv * dtv + ((t + 1 < nq) ? dln : 0.f);
             }
         }
-        for (int e = tid; e < Q * K / 8; e += NT) {   // theta of the chunk (zero past the end), 16-byte pieces
-            const int t = e / (K / 8), k = (e % (K / 8)) * 8;
-            *(bf16x8 *)(TH + t * K + k) =
-                (t < nq) ? *(const bf16x8 *)((const bf16 *)p.theta + th_row(p, start + c0 + t, h) + k) : bf16x8{};
+#pragma unroll
+        for (int i = 0; i < PF_T; i++) {   // theta of the chunk (zero past the end), 16-byte pieces
+            const int e = tid + i * NT;
+            if (e < Q * K / 8) {
+                const int t = e / (K / 8), k = (e % (K / 8)) * 8;
+                *(bf16x8 *)(TH + t * K + k) = (t < nq) ? pT[i] : bf16x8{};
+            }
         }
         __syncthreads();
         for (int e = tid; e < Q * K; e += NT) {   // cumulative angles, one (token, pair) per thread
@@ -990,18 +1069,19 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     };
     auto load_prev = [&](int64_t c0) {
         const bool ex = c0 > 0 || has_prev;
-        for (int e = tid; e < R * N; e += NT) {
-            float v = 0.f;
-            if (c0 > 0) v = ldt<bf16>(p.B, tokB(c0 - 1) + e);
-            else if (has_prev) v = ldt<bf16>(p.Bprev, ((int64_t)s * G + g) * R * N + e);
-            Bp[e] = v;
-            BpRaw[e] = v;
+#pragma unroll
+        for (int i = 0; i < PF_V; i++) {
+            const int e = tid + i * NT;
+            if (e < R * N) {
+                const float v = ex ? (float)pBp[i] : 0.f;
+                Bp[e] = v;
+                BpRaw[e] = v;
+            }
         }
-        for (int e = tid; e < R * P; e += NT) {
-            float v = 0.f;
-            if (c0 > 0) v = ldt<bf16>(p.x, tokX(c0 - 1) + e);
-            else if (has_prev) v = ldt<bf16>(p.xprev, ((int64_t)s * H + h) * R * P + e);
-            Xp[e] = v;
+#pragma unroll
+        for (int i = 0; i < PF_U; i++) {
+            const int e = tid + i * NT;
+            if (e < R * P) Xp[e] = ex ? (float)pXp[i] : 0.f;
         }
         if (tid == 0) MISC[0] = ex ? 1.f : 0.f;
         __syncthreads();
@@ -1011,27 +1091,24 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     // B~ (and C~, dy in the reverse pass) and X, c o X of the chunk in bf16; raw B and C rows go
     // through fp32 staging (dBf, dCf) for the prologue and the rotation
     auto stage_chunk = [&](int64_t c0, int nq, bool rev) {
-        for (int e = tid; e < QR * N / 8; e += NT) {   // 16-byte pieces
-            const int r = e / (N / 8), n = (e % (N / 8)) * 8, t = r / R, j = r % R;
-            bf16x8 bv = {}, cv = {};
-            if (t < nq) {
-                const int64_t o = tokB(c0 + t) + j * N + n;
-                bv = *(const bf16x8 *)(gB + o);
-                if (rev) cv = *(const bf16x8 *)(gC + o);
-            }
+#pragma unroll
+        for (int i = 0; i < PF_B; i++) {   // 16-byte pieces
+            const int e = tid + i * NT;
+            if (e >= QR * N / 8) break;
+            const int r = e / (N / 8), n = (e % (N / 8)) * 8, t = r / R;
+            const bf16x8 bv = (t < nq) ? pB[i] : bf16x8{}, cv = (rev && t < nq) ? pC[i] : bf16x8{};
 #pragma unroll
             for (int m = 0; m < 8; m++) {
                 dBf[r * NF + n + m] = (float)bv[m];
                 if (rev) dCf[r * NF + n + m] = (float)cv[m];
             }
         }
-        for (int e = tid; e < QR * P / 8; e += NT) {
-            const int r = e / (P / 8), pp = (e % (P / 8)) * 8, t = r / R, j = r % R;
-            bf16x8 xv = {}, dv = {};
-            if (t < nq) {
-                xv = *(const bf16x8 *)(gx + tokX(c0 + t) + j * P + pp);
-                if (rev) dv = *(const bf16x8 *)(gdy + tokX(c0 + t) + j * P + pp);
-            }
+#pragma unroll
+        for (int i = 0; i < PF_X; i++) {
+            const int e = tid + i * NT;
+            if (e >= QR * P / 8) break;
+            const int r = e / (P / 8), pp = (e % (P / 8)) * 8, t = r / R;
+            const bf16x8 xv = (t < nq) ? pX[i] : bf16x8{}, dv = (rev && t < nq) ? pD[i] : bf16x8{};
             bf16x8 xc;
 #pragma unroll
             for (int m = 0; m < 8; m++) xc[m] = (bf16)(CU[t] * (float)xv[m]);
@@ -1072,9 +1149,11 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             const int n = tile_n0(v) + 4 * lg + i, pp = tile_p0(v) + li;
             hacc[v][i] = p.h_in ? p.h_in[sh * N * P + n * P + pp] : 0.f;
         }
+    if (nch > 0) prefetch(0, false);
     for (int64_t c = 0; c < nch; c++) {
         const int64_t c0 = c * Q;
         const int nq = (int)min((int64_t)Q, len - c0), e_ = nq - 1;
+        refresh();
         load_scalars(c0, nq);
         load_prev(c0);
         float *ws = wsS(c);
@@ -1089,6 +1168,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
                 ws[n * P + pp] = hacc[v][i];
             }
         stage_chunk(c0, nq, false);
+        if (c + 1 < nch) prefetch(c + 1, false);
 #pragma unroll
         for (int v = 0; v < UPW; v++) {
             const int n0 = tile_n0(v), p0 = tile_p0(v);
@@ -1125,9 +1205,11 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     for (int e = tid; e < R; e += NT) INVBP[e] = 1.f;
     float dA_acc = 0.f, dD_acc = 0.f;
     __syncthreads();
+    if (nch > 0) prefetch(nch - 1, true);
     for (int64_t c = nch - 1; c >= 0; c--) {
         const int64_t c0 = c * Q;
         const int nq = (int)min((int64_t)Q, len - c0), e_ = nq - 1;
+        refresh();
         load_scalars(c0, nq);
         load_prev(c0);
         // G^ = R(-Phi_e) dH (registers, bf16 copy in Gb); H' entering the chunk from the workspace
@@ -1153,6 +1235,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             }
         }
         stage_chunk(c0, nq, true);
+        if (c > 0) prefetch(c - 1, true);
         for (int e = tid; e < Q * K; e += NT) DPHI[e] = 0.f;
         for (int t = tid; t < Q; t += NT) DS[t] = DGM[t] = DDL[t] = 0.f;
         // scores on every QR x QR tile (zero outside the causal part): S (fp32) and A = M o S (bf16)
