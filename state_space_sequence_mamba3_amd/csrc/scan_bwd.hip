@@ -962,6 +962,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     constexpr int PF_T = (Q * K / 8 + NT - 1) / NT, PF_V = (R * N + NT - 1) / NT, PF_U = (R * P + NT - 1) / NT;
     bf16x8 pB[PF_B], pC[PF_B], pX[PF_X], pD[PF_X], pT[PF_T];
     bf16 pBp[PF_V], pXp[PF_U], pdt = {}, plm = {}, pat = {};
+    f32x4 pH[UPW];   // reverse walk: the state entering the chunk, from the workspace
     auto prefetch = [&](int64_t c, bool rev) {
         const int64_t c0 = c * Q;
         const int last = (int)min((int64_t)Q, len - c0) - 1;
@@ -1004,6 +1005,13 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             const int e = tid + i * NT;
             if (srcX && e < R * P) pXp[i] = srcX[e];
         }
+        if (rev) {
+            const float *ws = wsS(c);
+#pragma unroll
+            for (int v = 0; v < UPW; v++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) pH[v][i] = ws[(tile_n0(v) + 4 * lg + i) * P + tile_p0(v) + li];
+        }
         if (wave == 0) {
             const int64_t i = (start + c0 + min(lane, last)) * H + h;
             pdt = ((const bf16 *)p.dt)[i];
@@ -1011,8 +1019,9 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             if (p.A_tok) pat = ((const bf16 *)p.A_tok)[i];
         }
     };
-    auto load_scalars = [&](int64_t c0, int nq) {
-        static_assert(Q <= 64, "one wave scans the chunk");
+    // em: also the decay table EM (the reverse walk's)
+    auto load_scalars = [&](int64_t c0, int nq, bool em) {
+        static_assert(Q <= 64 && K < NT, "one wave scans the chunk; spare threads for the exponentials");
         if (wave == 0) {   // per-token scalars and the log-decay prefix (wave scan)
             const int t = lane;
             float dtv = 0.f, lv = 0.f, av = Ah;
@@ -1047,23 +1056,25 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             }
         }
         __syncthreads();
-        for (int e = tid; e < Q * K; e += NT) {   // cumulative angles, one (token, pair) per thread
-            const int t = e / K, k = e % K;
+        if (tid < K) {   // cumulative angles: one thread per pair walks the chunk's tokens
             float acc = 0.f;
-            for (int u = 0; u <= t; u++) acc += DT[u] * (float)TH[u * K + k];
-            float sn, cs;
-            __sincosf(acc, &sn, &cs);   // hardware sin / cos: operands of bf16 products
-            CS[e] = cs;
-            SN[e] = sn;
-        }
-        __syncthreads();
-        for (int e = tid; e < Q * Q; e += NT) {
-            const int t = e / Q, u = e % Q;
-            EM[e] = (u <= t) ? expf(S[t] - S[u]) : 0.f;
-        }
-        for (int t = tid; t < Q; t += NT) {
-            ES[t] = expf(S[t]);
-            CU[t] = (t < nq) ? expf(S[nq - 1] - S[t]) * G1[t] : 0.f;
+            for (int t = 0; t < Q; t++) {
+                acc += DT[t] * (float)TH[t * K + tid];
+                float sn, cs;
+                __sincosf(acc, &sn, &cs);   // hardware sin / cos: operands of bf16 products
+                CS[t * K + tid] = cs;
+                SN[t * K + tid] = sn;
+            }
+        } else {         // meanwhile the other threads form the exponentials
+            if (em)
+                for (int e = tid - K; e < Q * Q; e += NT - K) {
+                    const int t = e / Q, u = e % Q;
+                    EM[e] = (u <= t) ? expf(S[t] - S[u]) : 0.f;
+                }
+            for (int t = tid - K; t < Q; t += NT - K) {
+                ES[t] = expf(S[t]);
+                CU[t] = (t < nq) ? expf(S[nq - 1] - S[t]) * G1[t] : 0.f;
+            }
         }
         __syncthreads();
     };
@@ -1154,7 +1165,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         const int64_t c0 = c * Q;
         const int nq = (int)min((int64_t)Q, len - c0), e_ = nq - 1;
         refresh();
-        load_scalars(c0, nq);
+        load_scalars(c0, nq, false);
         load_prev(c0);
         float *ws = wsS(c);
 #pragma unroll
@@ -1210,11 +1221,10 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         const int64_t c0 = c * Q;
         const int nq = (int)min((int64_t)Q, len - c0), e_ = nq - 1;
         refresh();
-        load_scalars(c0, nq);
+        load_scalars(c0, nq, true);
         load_prev(c0);
         // G^ = R(-Phi_e) dH (registers, bf16 copy in Gb); H' entering the chunk from the workspace
         f32x4 gacc[UPW], hcur[UPW];
-        const float *ws = wsS(c);
 #pragma unroll
         for (int v = 0; v < UPW; v++) {
             const int n0 = tile_n0(v), p0 = tile_p0(v);
@@ -1229,7 +1239,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int n = n0 + 4 * lg + i, pp = p0 + li;
-                hcur[v][i] = ws[n * P + pp];
+                hcur[v][i] = pH[v][i];
                 Gb[n * PS + pp] = (bf16)gacc[v][i];
                 Hb[n * PS + pp] = (bf16)hcur[v][i];
             }
@@ -1544,15 +1554,16 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             dCf[r * NF + 2 * k + 1] = sn * d0 + cs * d1;
         }
         __syncthreads();
-        for (int n = tid; n < N; n += NT) {
-            float a = 0.f, b = 0.f;
-            for (int r = 0; r < nq * R; r++) {
-                a += dBf[r * NF + n];
-                b += dCf[r * NF + n];
+        if (p.Bb || p.Cb)   // the bias gradients' per-slab sums
+            for (int n = tid; n < N; n += NT) {
+                float a = 0.f, b = 0.f;
+                for (int r = 0; r < nq * R; r++) {
+                    a += dBf[r * NF + n];
+                    b += dCf[r * NF + n];
+                }
+                BBA[n] += a;
+                CBA[n] += b;
             }
-            BBA[n] += a;
-            CBA[n] += b;
-        }
         // back through the prologue to the raw columns (16 lanes per row; raw rows in Bt / Ct)
         for (int r0 = tid >> 4; r0 < (2 * nq * R + NT / 16 - 1) / (NT / 16) * (NT / 16); r0 += NT / 16) {
             const bool ok = r0 < 2 * nq * R;
