@@ -886,15 +886,13 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int li = lane & 15, lg = lane >> 4;
-    // With N = 128 the lane-derived values are made opaque once per chunk, so that address math is
-    // recomputed where it is used instead of being hoisted out of the chunk loops and spilled.
+    // The lane-derived values are made opaque once per chunk, so that address math is recomputed
+    // where it is used instead of being hoisted out of the chunk loops and spilled.
     auto refresh = [&]() {
-        if constexpr (N == 128) {
-            asm volatile("" : "+v"(tid));
-            lane = tid & 63;
-            li = lane & 15;
-            lg = lane >> 4;
-        }
+        asm volatile("" : "+v"(tid));
+        lane = tid & 63;
+        li = lane & 15;
+        lg = lane >> 4;
     };
     const int s = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
     const bf16 *gx = (const bf16 *)p.x, *gB = (const bf16 *)p.B, *gC = (const bf16 *)p.C, *gdy = (const bf16 *)p.dy;
@@ -1413,11 +1411,31 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             }
         }
         const float gh = block_sum(gh_acc, RED);   // (also orders every write above before the reads below)
-        // dH' in bf16 for the fold (G^ is no longer read)
+        // The fold's products with dH' (in registers): dH' Xp^T and dH'^T Bp, as per-tile partial
+        // sums in LDS (Gb is free: G^ is no longer read), added up below in a fixed order.
+        float *FB = (float *)Gb, *FX = FB + R * N * TP;   // [R][N][TP], [R][P][TN]
+        static_assert(R * N * TP + R * P * TN <= N * PS / 2, "fold partials fit over G^");
+        const bool fold_on = MISC[0] != 0.f;
+        if (fold_on) {
 #pragma unroll
-        for (int v = 0; v < UPW; v++)
+            for (int v = 0; v < UPW; v++) {
+                const int n0 = tile_n0(v), p0 = tile_p0(v), pp = p0 + li;
 #pragma unroll
-            for (int i = 0; i < 4; i++) Gb[(tile_n0(v) + 4 * lg + i) * PS + tile_p0(v) + li] = (bf16)dacc[v][i];
+                for (int j = 0; j < R; j++) {
+                    const float xv = Xp[j * P + pp];
+                    float bx = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int n = n0 + 4 * lg + i;
+                        const float rb = sum16(dacc[v][i] * xv);   // over the tile's 16 columns
+                        if (li == 0) FB[(j * N + n) * TP + p0 / 16] = rb;
+                        bx += dacc[v][i] * Bp[j * N + n];
+                    }
+                    bx = sum_groups(bx);                           // over the tile's 16 rows
+                    if (lg == 0) FX[(j * P + pp) * TN + n0 / 16] = bx;
+                }
+            }
+        }
         // dPhi_e, and dPhi_t from C~ and B~ (thread per (t, k))
         for (int k = tid; k < K; k += NT) {
             float a = 0.f;
@@ -1459,24 +1477,17 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         }
         // the fold at the chunk start: d delta_0 = <dH', Bp Xp^T>, carries for the previous token
         float fold_acc = 0.f;
-        if (MISC[0] != 0.f) {   // 16 lanes per output element
-            constexpr int NG = NT / 16;
-            for (int e0 = tid >> 4; e0 < (R * N + NG - 1) / NG * NG; e0 += NG) {
-                const int e = e0 < R * N ? e0 : 0, j = e / N, n = e % N;
+        if (fold_on) {   // one output per thread, from the partials
+            for (int e = tid; e < R * N; e += NT) {
                 float a = 0.f;
-                for (int pp = li; pp < P; pp += 16) a += (float)Gb[n * PS + pp] * Xp[j * P + pp];
-                a = sum16(a);
-                if (e0 < R * N && li == 0) {
-                    dBcOut[e] = DL[0] * a;
-                    fold_acc += Bp[e] * a;
-                }
+                for (int q = 0; q < TP; q++) a += FB[e * TP + q];
+                dBcOut[e] = DL[0] * a;
+                fold_acc += Bp[e] * a;
             }
-            for (int e0 = tid >> 4; e0 < (R * P + NG - 1) / NG * NG; e0 += NG) {
-                const int e = e0 < R * P ? e0 : 0, j = e / P, pp = e % P;
+            for (int e = tid; e < R * P; e += NT) {
                 float a = 0.f;
-                for (int n = li; n < N; n += 16) a += (float)Gb[n * PS + pp] * Bp[j * N + n];
-                a = sum16(a);
-                if (e0 < R * P && li == 0) dXcOut[e] = DL[0] * a;
+                for (int q = 0; q < TN; q++) a += FX[e * TN + q];
+                dXcOut[e] = DL[0] * a;
             }
         } else {
             for (int e = tid; e < R * N; e += NT) dBcOut[e] = 0.f;
