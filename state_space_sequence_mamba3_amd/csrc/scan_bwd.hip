@@ -1413,26 +1413,35 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         const float gh = block_sum(gh_acc, RED);   // (also orders every write above before the reads below)
         // The fold's products with dH' (in registers): dH' Xp^T and dH'^T Bp, as per-tile partial
         // sums in LDS (Gb is free: G^ is no longer read), added up below in a fixed order.
-        float *FB = (float *)Gb, *FX = FB + R * N * TP;   // [R][N][TP], [R][P][TN]
-        static_assert(R * N * TP + R * P * TN <= N * PS / 2, "fold partials fit over G^");
+        // A wave's tiles share one row block and cover UPW consecutive column blocks, so dH' Xp^T
+        // is summed over them in registers first: TP / UPW partials per row.
+        constexpr int FBP = TP / UPW;
+        static_assert(TP % UPW == 0, "a wave's tiles share a row block");
+        float *FB = (float *)Gb, *FX = FB + R * N * FBP;   // [R][N][FBP], [R][P][TN]
+        static_assert(R * N * FBP + R * P * TN <= N * PS / 2, "fold partials fit over G^");
         const bool fold_on = MISC[0] != 0.f;
         if (fold_on) {
+            const int n0 = tile_n0(0), pb = tile_p0(0) / 16 / UPW;
 #pragma unroll
-            for (int v = 0; v < UPW; v++) {
-                const int n0 = tile_n0(v), p0 = tile_p0(v), pp = p0 + li;
+            for (int j = 0; j < R; j++) {
+                float rb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < R; j++) {
+                for (int v = 0; v < UPW; v++) {
+                    const int pp = tile_p0(v) + li;
                     const float xv = Xp[j * P + pp];
                     float bx = 0.f;
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
-                        const int n = n0 + 4 * lg + i;
-                        const float rb = sum16(dacc[v][i] * xv);   // over the tile's 16 columns
-                        if (li == 0) FB[(j * N + n) * TP + p0 / 16] = rb;
-                        bx += dacc[v][i] * Bp[j * N + n];
+                        rb[i] += dacc[v][i] * xv;
+                        bx += dacc[v][i] * Bp[j * N + n0 + 4 * lg + i];
                     }
                     bx = sum_groups(bx);                           // over the tile's 16 rows
                     if (lg == 0) FX[(j * P + pp) * TN + n0 / 16] = bx;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const float r = sum16(rb[i]);                  // over the wave's columns
+                    if (li == 0) FB[(j * N + n0 + 4 * lg + i) * FBP + pb] = r;
                 }
             }
         }
@@ -1480,7 +1489,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         if (fold_on) {   // one output per thread, from the partials
             for (int e = tid; e < R * N; e += NT) {
                 float a = 0.f;
-                for (int q = 0; q < TP; q++) a += FB[e * TP + q];
+                for (int q = 0; q < FBP; q++) a += FB[e * FBP + q];
                 dBcOut[e] = DL[0] * a;
                 fold_acc += Bp[e] * a;
             }
