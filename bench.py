@@ -60,7 +60,7 @@ def scan_flops(c):
 
 
 # (N, P, R) -> chunk length of the MFMA backward (bf16 token inputs); mirrors the library's table
-BWD_MFMA_CHUNK = {(128, 64, 1): 32, (64, 64, 1): 32, (64, 64, 4): 8, (128, 64, 2): 16, (128, 64, 4): 8, (64, 64, 2): 16}
+BWD_MFMA_CHUNK = {(128, 64, 1): 32, (64, 64, 1): 32, (64, 64, 4): 16, (128, 64, 2): 16, (128, 64, 4): 8, (64, 64, 2): 32}
 
 
 def bwd_chunk(c):

@@ -840,8 +840,12 @@ struct BCfg {
     static constexpr int SMALL = 6 * R * N + 4 * R * P + R + 2 * N + 16 + 64;
     static constexpr int O_DCF = O_SMALL + al(SMALL * 4);           // float [QR][NF] dC~ (raw C staging)
     static constexpr int O_DBF = O_DCF + al(QR * NF * 4);           // float [QR][NF] dB~ (raw B staging)
-    static constexpr int O_SF = O_DBF + al(QR * NF * 4);            // float [QR][SF] scores
-    static constexpr int O_CT = O_SF + al(QR * SF * 4);             // bf16 [QR][NS] C~
+    // float [QR][SF] scores: over the raw C staging when it fits (QR <= N). The staging is dead
+    // from the rotation into C~ until dC~ is written, and the scores live from the score tiles to
+    // dP, inside that window.
+    static constexpr bool SF_ALIAS = QR <= N;
+    static constexpr int O_SF = SF_ALIAS ? O_DCF : O_DBF + al(QR * NF * 4);
+    static constexpr int O_CT = SF_ALIAS ? O_DBF + al(QR * NF * 4) : O_SF + al(QR * SF * 4);   // bf16 [QR][NS] C~
     static constexpr int O_BT = O_CT + al(QR * NS * 2);             // bf16 [QR][NS] B~
     static constexpr int O_XB = O_BT + al(QR * NS * 2);             // bf16 [QR][PS] X
     static constexpr int O_XC = O_XB + al(QR * PS * 2);             // bf16 [QR][PS] c o X
@@ -1657,10 +1661,10 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
 #define M3_BWD_MFMA_SHAPES(X) \
     X(128, 64, 1, 32, 8)      \
     X(64, 64, 1, 32, 8)       \
-    X(64, 64, 4, 8, 8)        \
+    X(64, 64, 4, 16, 8)       \
     X(128, 64, 2, 16, 8)      \
     X(128, 64, 4, 8, 8)       \
-    X(64, 64, 2, 16, 8)
+    X(64, 64, 2, 32, 8)
 
 int scan_bwd_mfma_chunk(int N, int P, int R) {
 #define X(n, pp, r, q, w) if (N == n && P == pp && R == r) return q;

@@ -92,6 +92,9 @@ def test_bwd_fp32_packed(oracle):
     ("siso_n128", dict(cfg=1, batch=1, seqlen=90, nheads=2)),
     ("mimo_n64_r4", dict(cfg=2, batch=1, seqlen=70, nheads=2)),
     ("mimo_n128_r4_g1", dict(cfg=4, batch=1, seqlen=50, nheads=2, packed=False, ngroups=1)),
+    ("siso_n64", dict(cfg=1, batch=1, seqlen=75, nheads=2, dstate=64)),
+    ("r2_n128", dict(cfg=2, batch=1, seqlen=75, nheads=2, dstate=128, rank=2)),
+    ("r2_n64", dict(cfg=2, batch=2, seqlen=70, nheads=2, rank=2)),
 ])
 @pytest.mark.parametrize("block", [False, True])
 def test_bwd_bf16(oracle, name, spec, block):
