@@ -161,7 +161,7 @@ def bench_scan(cfg, steps, warmup, dev, block=False, **over):
     return out
 
 
-def bench_long(steps, warmup, dev, seqlen=32768, nseg=8):
+def bench_long(steps, warmup, dev, seqlen=65536, nseg=16):
     """One long SISO sequence (batch 1): the plain scan (one workgroup per head walks every
     token) against the segmented scan (nseg segments per sequence scanned as independent rows,
     their entering states chained by mamba3_state_passing, then scanned again)."""
@@ -232,7 +232,8 @@ def bench_bwd(cfg, steps, warmup, dev):
 
 def bench_decode(steps_per_rep, reps, dev, block=False, siso=False, slots=False):
     """The decode step over 1000 consecutive steps. siso: the SISO shape (N=128, R=1) instead of
-    MIMO; slots: the states live in a pool twice the batch, each row updating a scattered slot."""
+    MIMO; slots: the states live in a pool twice the batch, each row updating a scattered slot,
+    plus one inactive row (slot -1), which also gives this launch a grid of its own in profiles."""
     import torch
     import state_space_sequence_mamba3_amd as m3
     from state_space_sequence_mamba3_amd import synth
@@ -241,6 +242,9 @@ def bench_decode(steps_per_rep, reps, dev, block=False, siso=False, slots=False)
         c = dict(c, dstate=128, rank=1, name="SISO decode bf16 batch256 H64 P64 N128")
     ring = c["ring"]
     b, H, P, N, R = c["batch"], c["nheads"], c["headdim"], c["dstate"], c["rank"]
+    act = b          # active rows
+    if slots:
+        b += 1       # the inactive row
     g = torch.Generator(device=dev)
     g.manual_seed(3)
 
@@ -256,11 +260,11 @@ def bench_decode(steps_per_rep, reps, dev, block=False, siso=False, slots=False)
     C = nrm((ring, b, H, R, N), 0, 1 / math.sqrt(N)).bfloat16()
     A = -torch.exp(nrm((H,), 0, 0.5))
     D = nrm((H,))
-    h = nrm((2 * b if slots else b, H, N, P))
+    h = nrm((2 * act if slots else b, H, N, P))
     sl = {}
-    if slots:   # rows take every other slot of the pool, in a shuffled order
-        perm = torch.randperm(2 * b, generator=torch.Generator().manual_seed(5))[:b]
-        sl = dict(slots=perm.to(torch.int32).to(dev))
+    if slots:   # active rows take half the slots of the pool, in a shuffled order; the last row is inactive
+        perm = torch.randperm(2 * act, generator=torch.Generator().manual_seed(5))[:act]
+        sl = dict(slots=torch.cat([perm, torch.tensor([-1])]).to(torch.int32).to(dev))
     ys = torch.empty((ring, b, H, R, P), dtype=torch.bfloat16, device=dev)
     blk = {}
     if block:   # fused prologue / epilogue: BC norm, per-head biases ~ U(0.5, 1.5), gate z ~ N(0, 1)
@@ -282,7 +286,7 @@ def bench_decode(steps_per_rep, reps, dev, block=False, siso=False, slots=False)
         state["k"] = k + 1
 
     ms, wall = timed(step, steps_per_rep, 10, stream)
-    nbytes = decode_bytes(c, block) + (b * 4 if slots else 0)   # (+ the slot table)
+    nbytes = decode_bytes(c, block) + (b * 4 if slots else 0)   # active rows (+ the slot table)
     us = ms * 1e3
     # per-step event pairs (outside the timed region) for the median
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps_per_rep)]
@@ -321,7 +325,7 @@ def bench_decode(steps_per_rep, reps, dev, block=False, siso=False, slots=False)
     except Exception as exc:  # graph capture unavailable: report the eager figures only
         print(f"# decode graph replay skipped: {exc}", file=sys.stderr)
     name = c["name"] + (" + BC norm, BC biases, SiLU gate" if block else "") + (
-        f", slot-indexed states (pool of {2 * b})" if slots else "")
+        f", slot-indexed states (pool of {2 * act}, one more row inactive)" if slots else "")
     return dict(workload=name, us_per_step=us, median_us=median, graph_wall_us=graph_us, steps=steps_per_rep,
                 bytes_per_step=nbytes, hbm_gbs=nbytes / (us * 1e-6) / 1e9, wall_s=wall)
 
@@ -395,19 +399,28 @@ def _short(name):
 
 
 def summarize_stats(stats_dir, out_md, command):
-    """Writes a short text summary of a rocprofv3 --kernel-trace --stats run."""
-    rows = _csv_rows(os.path.join(stats_dir, "run_kernel_stats.csv"))
-    lines = ["# rocprofv3 kernel statistics", "", "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
-             "```", command, "```", "", "| kernel | calls | average us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
-    other, other_ms = 0, 0.0
-    for r in rows:
-        if "k_scan" not in r["Name"] and "k_decode" not in r["Name"] and "k_bwd" not in r["Name"]:
-            other += 1
-            other_ms += float(r["TotalDurationNs"]) / 1e6
+    """Writes a short text summary of a rocprofv3 --kernel-trace --stats run: the library's
+    kernels from the per-dispatch trace, one row per (kernel, workgroups), so that launches of
+    one kernel on different workloads are told apart."""
+    from collections import defaultdict
+    groups = defaultdict(list)
+    other, other_ms = set(), 0.0
+    for r in _csv_rows(os.path.join(stats_dir, "run_kernel_trace.csv")):
+        ns = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+        if not any(k in r["Kernel_Name"] for k in ("k_scan", "k_decode", "k_bwd", "k_segment_sums", "k_state_passing")):
+            other.add(r["Kernel_Name"])
+            other_ms += ns / 1e6
             continue
-        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['TotalDurationNs']) / 1e6:.3f} |")
-    lines += ["", f"Not listed: {other} other kernels (torch's input generation and copies), {other_ms:.3f} ms in total."]
+        wg = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        groups[(r["Kernel_Name"], wg)].append(ns)
+    lines = ["# rocprofv3 kernel statistics", "", "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+             "```", command, "```", "",
+             "Per (kernel, workgroups), from the run's kernel trace.", "",
+             "| kernel | workgroups | calls | average us | min us | max us | total ms |", "|---|---|---|---|---|---|---|"]
+    for (name, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{_short(name)}` | {wg} | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | {min(v) / 1e3:.2f} | "
+                     f"{max(v) / 1e3:.2f} | {sum(v) / 1e6:.3f} |")
+    lines += ["", f"Not listed: {len(other)} other kernels (torch's input generation and copies), {other_ms:.3f} ms in total."]
     open(out_md, "w").write("\n".join(lines) + "\n")
     print(f"wrote {out_md}")
 
@@ -422,11 +435,12 @@ def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 3
     from collections import defaultdict
 
     def per_dispatch(d, counter):
+        """{(kernel, workgroups): [bytes per dispatch]}"""
         agg, names = defaultdict(float), {}
         for r in _csv_rows(os.path.join(d, "run_counter_collection.csv")):
             if r["Counter_Name"] == counter:
                 agg[r["Dispatch_Id"]] += float(r["Counter_Value"])
-                names[r["Dispatch_Id"]] = r["Kernel_Name"]
+                names[r["Dispatch_Id"]] = (r["Kernel_Name"], int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
         by = defaultdict(list)
         for k, v in agg.items():
             by[names[k]].append(v * 1024.0)
@@ -434,38 +448,44 @@ def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 3
 
     fetch, write = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
     # the calibration copies: the device-to-device copy kernel's dispatches of about 1 GiB
-    copy_f = [v for n, vs in fetch.items() if "copyBuffer" in n for v in vs if v > copy_bytes / 2]
-    copy_w = [v for n, vs in write.items() if "copyBuffer" in n for v in vs if v > copy_bytes / 2]
+    copy_f = [v for (n, _), vs in fetch.items() if "copyBuffer" in n for v in vs if v > copy_bytes / 2]
+    copy_w = [v for (n, _), vs in write.items() if "copyBuffer" in n for v in vs if v > copy_bytes / 2]
     if not copy_f or not copy_w:
         raise SystemExit("no copy kernel found in the counter runs (run bench.py with --copy-calibration)")
     kf, kw = copy_bytes / (sum(copy_f) / len(copy_f)), copy_bytes / (sum(copy_w) / len(copy_w))
-    # the headline SISO scan, the decode step, and both again with the fused block prologue / epilogue
-    # (demangled or mangled names, as rocprofv3 prints them)
-    kernels = {"scan_bf16": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, false>",)),
-               "scan_bf16_block": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, true>",)),
-               "decode": ("decode.hip", ("k_decode_colIDF16bLi64ELi4ELb0E", "k_decode_col<__bf16, 64, 4, false>")),
-               "decode_block": ("decode.hip", ("k_decode_colIDF16bLi64ELi4ELb1E", "k_decode_col<__bf16, 64, 4, true>")),
-               "scan_bwd": ("scan_bwd.hip", ("BCfg<128, 64, 1, 32, 8>",))}
+    # the headline SISO scan, the decode steps, the SISO backward, and the fused block prologue /
+    # epilogue variants (demangled or mangled names, as rocprofv3 prints them; workgroups of the
+    # bench's launch: 8 x 64 (sequence, head) slabs, 256 x 64 decode rows, 257 x 64 with slots)
+    dec = ("k_decode_colIDF16bLi64ELi4ELb0E", "k_decode_col<__bf16, 64, 4, false>")
+    kernels = {"scan_bf16": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, false>",), 512),
+               "scan_bf16_block": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, true>",), 512),
+               "decode": ("decode.hip", dec, 16384),
+               "decode_slots": ("decode.hip", dec, 16448),
+               "decode_block": ("decode.hip", ("k_decode_colIDF16bLi64ELi4ELb1E", "k_decode_col<__bf16, 64, 4, true>"),
+                                16384),
+               "decode_siso": ("decode.hip", ("k_decode_colIDF16bLi128ELi1ELb0E", "k_decode_col<__bf16, 128, 1, false>"),
+                               16384),
+               "scan_bwd": ("scan_bwd.hip", ("BCfg<128, 64, 1, 32, 8>",), 512)}
     md = ["# HBM traffic per launch from rocprofv3 counters", "", "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):",
           "", "```", *commands, "```", "",
           f"Calibration: a plain 1 GiB device copy reads {sum(copy_f) / len(copy_f) / 2**30:.4f} GiB by FETCH_SIZE and writes "
           f"{sum(copy_w) / len(copy_w) / 2**30:.4f} GiB by WRITE_SIZE; scale factors {kf:.4f} (fetch), {kw:.4f} (write).", "",
-          "| kernel | dispatches | fetch MB | write MB | traffic MB per launch |", "|---|---|---|---|---|"]
-    for key, (src, pats) in kernels.items():
-        hit = lambda n: any(p in n for p in pats)
-        fs = [v for n, vs in fetch.items() if hit(n) for v in vs]
-        ws = [v for n, vs in write.items() if hit(n) for v in vs]
+          "| kernel | workgroups | dispatches | fetch MB | write MB | traffic MB per launch |", "|---|---|---|---|---|---|"]
+    for key, (src, pats, wg) in kernels.items():
+        hit = lambda nw: nw[1] == wg and any(p in nw[0] for p in pats)
+        fs = [v for nw, vs in fetch.items() if hit(nw) for v in vs]
+        ws = [v for nw, vs in write.items() if hit(nw) for v in vs]
         if not fs or not ws:
             continue
         fb, wb = kf * sum(fs) / len(fs), kw * sum(ws) / len(ws)
-        name = next(n for n in fetch if hit(n))
+        name = next(nw[0] for nw in fetch if hit(nw))
         srcp = os.path.join(ROOT, "state_space_sequence_mamba3_amd", "csrc", src)
         rec = {"kernel": _short(name), "source": src,
                "source_sha256": hashlib.sha256(open(srcp, "rb").read()).hexdigest(),
                "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb, "dispatches": len(fs),
-               "copy_scale_fetch": kf, "copy_scale_write": kw}
+               "copy_scale_fetch": kf, "copy_scale_write": kw, "workgroups": wg}
         json.dump(rec, open(os.path.join(out_dir, f"traffic_{key}.json"), "w"), indent=1)
-        md.append(f"| `{_short(name)}` | {len(fs)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} |")
+        md.append(f"| `{_short(name)}` | {wg} | {len(fs)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} |")
     out_md = os.path.join(out_dir, "traffic_scan_bf16_siso_8x4096_and_decode_b256.md")
     open(out_md, "w").write("\n".join(md) + "\n")
     print(f"wrote {out_md}")

@@ -103,8 +103,11 @@ __global__ __launch_bounds__(kSPThreads) void k_segment_sums(SPParams p) {
     }
 }
 
-// One workgroup per (sequence, head): the chain over the sequence's segments.
-template <typename T>
+// One workgroup per (sequence, head): the chain over the sequence's segments. With PREF (at most
+// PREF_MAX (pair, column) elements per thread) each thread loads its elements of U into registers
+// at the start of a segment, so that one memory latency per segment overlaps the staging.
+constexpr int PREF_MAX = 16;
+template <typename T, bool PREF>
 __global__ __launch_bounds__(kSPThreads) void k_state_passing(SPParams p) {
     extern __shared__ float smem[];
     const int N = p.N, P = p.P, R = p.R, H = p.H, G = p.G, K = N / 2;
@@ -122,6 +125,19 @@ __global__ __launch_bounds__(kSPThreads) void k_state_passing(SPParams p) {
         const int64_t t0 = (int64_t)s * p.seqlen + (int64_t)k * Ls;   // first token of the segment
         const int64_t row = (int64_t)s * p.nseg + k;                   // segment row
         float *out = p.seg_h + (row * H + h) * NP;
+        const float *Uk = p.U + (row * H + h) * NP;
+        float u0r[PREF ? PREF_MAX : 1], u1r[PREF ? PREF_MAX : 1];
+        if constexpr (PREF) {
+#pragma unroll
+            for (int j = 0; j < PREF_MAX; j++) {
+                const int e = tid + j * NT;
+                if (e < K * P) {
+                    const int64_t o0 = (int64_t)(2 * (e / P)) * P + e % P;
+                    u0r[j] = Uk[o0];
+                    u1r[j] = Uk[o0 + P];
+                }
+            }
+        }
         // the segment's sums, staged by k_segment_sums in this block of seg_h_in
         for (int i = tid; i < K; i += NT) sincosf(out[1 + i], &PHI[K + i], &PHI[i]);
         // the token before the segment: the previous segment's last token, or the sequence's own
@@ -162,8 +178,7 @@ __global__ __launch_bounds__(kSPThreads) void k_state_passing(SPParams p) {
         }
         // entering state out, then H <- exp(S) R(Phi) (H + delta_0 Bprev xprev^T) + U
         const float decay = MISC[0], d0 = MISC[1];
-        const float *Uk = p.U + (row * H + h) * NP;
-        for (int e = tid; e < K * P; e += NT) {
+        auto update = [&](int e, float U0, float U1) {
             const int i = e / P, c = e % P;
             const int64_t o0 = (int64_t)(2 * i) * P + c, o1 = o0 + P;
             float u0 = Hs[o0], u1 = Hs[o1];
@@ -177,8 +192,18 @@ __global__ __launch_bounds__(kSPThreads) void k_state_passing(SPParams p) {
             u0 += d0 * f0;
             u1 += d0 * f1;
             const float cs = PHI[i], sn = PHI[K + i];
-            Hs[o0] = decay * (cs * u0 - sn * u1) + Uk[o0];
-            Hs[o1] = decay * (sn * u0 + cs * u1) + Uk[o1];
+            Hs[o0] = decay * (cs * u0 - sn * u1) + U0;
+            Hs[o1] = decay * (sn * u0 + cs * u1) + U1;
+        };
+        if constexpr (PREF) {
+#pragma unroll
+            for (int j = 0; j < PREF_MAX; j++)
+                if (tid + j * NT < K * P) update(tid + j * NT, u0r[j], u1r[j]);
+        } else {
+            for (int e = tid; e < K * P; e += NT) {
+                const int64_t o0 = (int64_t)(2 * (e / P)) * P + e % P;
+                update(e, Uk[o0], Uk[o0 + P]);
+            }
         }
         __syncthreads();   // PHI, BL, XL, MISC are rewritten by the next segment
     }
@@ -199,17 +224,23 @@ mamba3_status launch_state_passing(const mamba3_state_passing_args *a, hipStream
     const int64_t nblk = (int64_t)f->batch * f->nheads;
     if (nblk == 0) return MAMBA3_OK;
     const size_t lds = state_passing_lds_bytes(p.N, p.P, p.R);
-    const void *fn = f->dtype == MAMBA3_BF16 ? (const void *)k_state_passing<bf16> : (const void *)k_state_passing<float>;
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return MAMBA3_EHIP;
+    const bool pref = (int64_t)(p.N / 2) * p.P <= (int64_t)PREF_MAX * kSPThreads;
     const int64_t nrow = nblk * a->nseg;   // (segment row, head) pairs
+    auto chain = [&](auto kern) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return false;
+        hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(kSPThreads), lds, st, p);
+        return true;
+    };
+    bool ok;
     if (f->dtype == MAMBA3_BF16) {
         hipLaunchKernelGGL(k_segment_sums<bf16>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
-        hipLaunchKernelGGL(k_state_passing<bf16>, dim3((unsigned)nblk), dim3(kSPThreads), lds, st, p);
+        ok = pref ? chain(k_state_passing<bf16, true>) : chain(k_state_passing<bf16, false>);
     } else {
         hipLaunchKernelGGL(k_segment_sums<float>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
-        hipLaunchKernelGGL(k_state_passing<float>, dim3((unsigned)nblk), dim3(kSPThreads), lds, st, p);
+        ok = pref ? chain(k_state_passing<float, true>) : chain(k_state_passing<float, false>);
     }
+    if (!ok) return MAMBA3_EHIP;
     return hipGetLastError() == hipSuccess ? MAMBA3_OK : MAMBA3_EHIP;
 }
 
