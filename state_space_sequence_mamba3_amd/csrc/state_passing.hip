@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kSPThreads) void k_segment_sums(SPParams p) {
 // PREF_MAX (pair, column) elements per thread) each thread loads its elements of U into registers
 // at the start of a segment, so that one memory latency per segment overlaps the staging.
 constexpr int PREF_MAX = 16;
-template <typename T, bool PREF>
+template <typename T, int PREF>
 __global__ __launch_bounds__(kSPThreads) void k_state_passing(SPParams p) {
     extern __shared__ float smem[];
     const int N = p.N, P = p.P, R = p.R, H = p.H, G = p.G, K = N / 2;
@@ -235,10 +235,10 @@ mamba3_status launch_state_passing(const mamba3_state_passing_args *a, hipStream
     bool ok;
     if (f->dtype == MAMBA3_BF16) {
         hipLaunchKernelGGL(k_segment_sums<bf16>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
-        ok = pref ? chain(k_state_passing<bf16, true>) : chain(k_state_passing<bf16, false>);
+        ok = pref ? chain(k_state_passing<bf16, 1>) : chain(k_state_passing<bf16, 0>);
     } else {
         hipLaunchKernelGGL(k_segment_sums<float>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
-        ok = pref ? chain(k_state_passing<float, true>) : chain(k_state_passing<float, false>);
+        ok = pref ? chain(k_state_passing<float, 1>) : chain(k_state_passing<float, 0>);
     }
     if (!ok) return MAMBA3_EHIP;
     return hipGetLastError() == hipSuccess ? MAMBA3_OK : MAMBA3_EHIP;
