@@ -161,6 +161,28 @@ def bench_scan(cfg, steps, warmup, dev, block=False, **over):
     return out
 
 
+def measured_peaks(dev):
+    """What this GPU reaches outside the library, as context for the published peaks: a plain
+    device copy of 1 GiB (bytes read + written per second) and a bf16 GEMM of 8192^3 through
+    torch (hipBLASLt)."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    ms, _ = timed(lambda: dst.copy_(src), 20, 3, stream)
+    copy_gbs = 2 * src.numel() * 4 / (ms * 1e-3) / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+    ms, _ = timed(lambda: torch.matmul(a, b, out=c), 20, 3, stream)
+    gemm_tfs = 2 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"device_copy_GBps": copy_gbs, "bf16_gemm_8192_TFLOPs": gemm_tfs}
+
+
 def bench_long(steps, warmup, dev, seqlen=65536, nseg=16):
     """One long SISO sequence (batch 1): the plain scan (one workgroup per head walks every
     token) against the segmented scan (nseg segments per sequence scanned as independent rows,
@@ -570,6 +592,8 @@ def main():
         print(f"# long sequence: plain {res['long']['plain']['ms']:.3f} ms, segmented "
               f"{res['long']['segmented']['ms']:.3f} ms", file=sys.stderr, flush=True)
 
+    peaks = measured_peaks(dev) if args.only == "all" else None
+
     cpu = None
     if not args.no_cpu_baseline and args.only in ("scan", "all"):
         cpu = cpu_baseline()
@@ -637,6 +661,8 @@ def main():
     if "long" in res:
         sec["long_sequence"] = res["long"]
     line["secondary"] = sec
+    if peaks:
+        line["measured_peaks"] = peaks
     print(json.dumps(line), flush=True)
 
 

@@ -1514,17 +1514,27 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             DS[e_] += dSe;
         }
         __syncthreads();
+        // reverse prefix sums over the chunk's tokens (past the end every term is zero): each pair's
+        // column read whole into registers, summed, written back
         for (int k = tid; k < K; k += NT) {
+            float v[Q];
+#pragma unroll
+            for (int t = 0; t < Q; t++) v[t] = DPHI[t * K + k];
             float acc = 0.f;
-            for (int t = nq - 1; t >= 0; t--) {
-                acc += DPHI[t * K + k];
+#pragma unroll
+            for (int t = Q - 1; t >= 0; t--) {
+                acc += v[t];
                 DPHI[t * K + k] = acc;
             }
         }
-        if (tid == 0) {
+        if (tid == NT - 1) {   // (a thread of the last wave, idle in the loop above)
+            float v[Q];
+#pragma unroll
+            for (int t = 0; t < Q; t++) v[t] = DS[t];
             float acc = 0.f;
-            for (int t = nq - 1; t >= 0; t--) {
-                acc += DS[t];
+#pragma unroll
+            for (int t = Q - 1; t >= 0; t--) {
+                acc += v[t];
                 DS[t] = acc;
             }
         }
@@ -1597,20 +1607,33 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             const float *gout = (isC ? dCf : dBf) + rr * NF;
             const float inv = (isC ? INVC : INVB)[rr];
             const bf16 *raw = (isC ? Ct : Bt) + rr * NS;
+            // lane li owns the NPL consecutive columns from li * NPL: one vector store each
+            constexpr int NPL = N / 16;
+            const int n0 = li * NPL;
             float dot = 0.f;
             if (p.norm) {
-                for (int n = li; n < N; n += 16) dot += gout[n] * (float)raw[n];
+#pragma unroll
+                for (int m = 0; m < NPL; m++) dot += gout[n0 + m] * (float)raw[n0 + m];
                 dot = sum16(dot);
             }
             const float k3 = p.norm ? dot * inv * inv * inv / (float)N : 0.f;
+            float v[NPL];
+#pragma unroll
+            for (int m = 0; m < NPL; m++)
+                v[m] = p.norm ? gout[n0 + m] * inv - k3 * (float)raw[n0 + m] : gout[n0 + m];
             float *part = isC ? p.p_dC : p.p_dB;
-            const int64_t o = tokB(c0 + t) + j * N;
-            if (ok)
-                for (int n = li; n < N; n += 16) {
-                    const float v = p.norm ? gout[n] * inv - k3 * (float)raw[n] : gout[n];
-                    if (part) part[((start + c0 + t) * H + h) * (int64_t)R * N + j * N + n] = v;
-                    else stt<bf16>(isC ? p.dC : p.dB, o + n, v);
+            if (ok) {
+                if (part) {
+                    float *dst = part + ((start + c0 + t) * H + h) * (int64_t)R * N + j * N + n0;
+#pragma unroll
+                    for (int m = 0; m < NPL; m += 4) *(f32x4 *)(dst + m) = f32x4{v[m], v[m + 1], v[m + 2], v[m + 3]};
+                } else {
+                    bf16 *dst = (bf16 *)(isC ? p.dC : p.dB) + tokB(c0 + t) + j * N + n0;
+#pragma unroll
+                    for (int m = 0; m < NPL; m += 4)
+                        *(bf16x4 *)(dst + m) = bf16x4{(bf16)v[m], (bf16)v[m + 1], (bf16)v[m + 2], (bf16)v[m + 3]};
                 }
+            }
         }
         for (int e = tid; e < R * N; e += NT) dBcIn[e] = dBcOut[e];
         for (int e = tid; e < R * P; e += NT) dXcIn[e] = dXcOut[e];
