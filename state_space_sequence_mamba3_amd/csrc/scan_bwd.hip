@@ -1251,7 +1251,10 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         for (int e = tid; e < Q * K; e += NT) DPHI[e] = 0.f;
         for (int t = tid; t < Q; t += NT) DS[t] = DGM[t] = DDL[t] = 0.f;
         // scores on every QR x QR tile (zero outside the causal part): S (fp32) and A = M o S (bf16)
-        for (int tile = wave; tile < TQ * TQ; tile += NW) {
+        #pragma unroll
+        for (int it_ = 0; it_ < (TQ * TQ + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
+            const int tile = wave + it_ * NW;
+            if ((TQ * TQ) % NW != 0 && tile >= TQ * TQ) break;
             const int tr = tile / TQ, tc = tile % TQ;
             f32x4 acc = {};
 #pragma unroll
@@ -1269,7 +1272,10 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         __syncthreads();
         if (p.z) {
             // outputs before the gate, y0 = e^{S_t} C~ H' + A X + D X; dy0 = dy SiLU(z), dz
-            for (int tile = wave; tile < TQ * TP; tile += NW) {
+            #pragma unroll
+            for (int it_ = 0; it_ < (TQ * TP + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
+                const int tile = wave + it_ * NW;
+                if ((TQ * TP) % NW != 0 && tile >= TQ * TP) break;
                 const int tr = tile / TP, tp = tile % TP;
                 f32x4 yin = {}, yia = {};
 #pragma unroll
@@ -1301,7 +1307,10 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         }
         __syncthreads();
         // dP = dY X^T with the mask: dS' = M o dP (bf16); d(mask) = S o dP, summed per row and column
-        for (int tile = wave; tile < TQ * TQ; tile += NW) {
+        #pragma unroll
+        for (int it_ = 0; it_ < (TQ * TQ + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
+            const int tile = wave + it_ * NW;
+            if ((TQ * TQ) % NW != 0 && tile >= TQ * TQ) break;
             const int tr = tile / TQ, tc = tile % TQ;
             f32x4 acc = {};
 #pragma unroll
@@ -1333,7 +1342,10 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         }
         __syncthreads();
         // dX = A^T dy0 + c o (B~ G^) + D dy0 (+ the fold's carry into the last token); dc partials
-        for (int tile = wave; tile < TQ * TP; tile += NW) {
+        #pragma unroll
+        for (int it_ = 0; it_ < (TQ * TP + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
+            const int tile = wave + it_ * NW;
+            if ((TQ * TP) % NW != 0 && tile >= TQ * TP) break;
             const int tq = tile / TP, tp = tile % TP;
             f32x4 a1 = {}, a2 = {};
 #pragma unroll
@@ -1356,7 +1368,10 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             }
         }
         // dC~ = dS' B~ + e^{S_t} (dY H'^T); the inter part's share of dS
-        for (int tile = wave; tile < TQ * TN; tile += NW) {
+        #pragma unroll
+        for (int it_ = 0; it_ < (TQ * TN + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
+            const int tile = wave + it_ * NW;
+            if ((TQ * TN) % NW != 0 && tile >= TQ * TN) break;
             const int tq = tile / TN, tn = tile % TN;
             f32x4 a1 = {}, a2 = {};
 #pragma unroll
@@ -1375,7 +1390,10 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             }
         }
         // dB~ = dS'^T C~ + c o (X G^^T)
-        for (int tile = wave; tile < TQ * TN; tile += NW) {
+        #pragma unroll
+        for (int it_ = 0; it_ < (TQ * TN + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
+            const int tile = wave + it_ * NW;
+            if ((TQ * TN) % NW != 0 && tile >= TQ * TN) break;
             const int tq = tile / TN, tn = tile % TN;
             f32x4 a1 = {}, a2 = {};
 #pragma unroll
