@@ -1080,7 +1080,8 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         }
         __syncthreads();
     };
-    auto load_prev = [&](int64_t c0) {
+    // the previous token into LDS (no barrier: load_scalars' first one orders it), then its prologue
+    auto stage_prev = [&](int64_t c0) {
         const bool ex = c0 > 0 || has_prev;
 #pragma unroll
         for (int i = 0; i < PF_V; i++) {
@@ -1097,9 +1098,12 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             if (e < R * P) Xp[e] = ex ? (float)pXp[i] : 0.f;
         }
         if (tid == 0) MISC[0] = ex ? 1.f : 0.f;
-        __syncthreads();
-        if (ex) prologue_rows(Bp, R, N, Bbh, INVBP);
-        __syncthreads();
+    };
+    auto prologue_prev = [&](int64_t c0) {
+        if (pro && (c0 > 0 || has_prev)) {
+            prologue_rows(Bp, R, N, Bbh, INVBP);
+            __syncthreads();
+        }
     };
     // B~ (and C~, dy in the reverse pass) and X, c o X of the chunk in bf16; raw B and C rows go
     // through fp32 staging (dBf, dCf) for the prologue and the rotation
@@ -1130,9 +1134,11 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             if (rev) *(bf16x8 *)(dYb + r * PS + pp) = dv;
         }
         __syncthreads();
-        prologue_rows(dBf, nq * R, NF, Bbh, INVB);
-        if (rev) prologue_rows(dCf, nq * R, NF, Cbh, INVC);
-        __syncthreads();
+        if (pro) {
+            prologue_rows(dBf, nq * R, NF, Bbh, INVB);
+            if (rev) prologue_rows(dCf, nq * R, NF, Cbh, INVC);
+            __syncthreads();
+        }
         for (int e = tid; e < QR * K; e += NT) {
             const int r = e / K, k = e % K, t = r / R;
             float b0 = 0.f, b1 = 0.f, q0 = 0.f, q1 = 0.f;
@@ -1167,8 +1173,9 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         const int64_t c0 = c * Q;
         const int nq = (int)min((int64_t)Q, len - c0), e_ = nq - 1;
         refresh();
+        stage_prev(c0);
         load_scalars(c0, nq, false);
-        load_prev(c0);
+        prologue_prev(c0);
         float *ws = wsS(c);
 #pragma unroll
         for (int v = 0; v < UPW; v++)
@@ -1223,8 +1230,9 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         const int64_t c0 = c * Q;
         const int nq = (int)min((int64_t)Q, len - c0), e_ = nq - 1;
         refresh();
+        stage_prev(c0);
         load_scalars(c0, nq, true);
-        load_prev(c0);
+        prologue_prev(c0);
         // G^ = R(-Phi_e) dH (registers, bf16 copy in Gb); H' entering the chunk from the workspace
         f32x4 gacc[UPW], hcur[UPW];
 #pragma unroll
