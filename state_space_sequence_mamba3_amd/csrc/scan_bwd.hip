@@ -815,6 +815,8 @@ __device__ __forceinline__ float sum_groups(float v) {
     v += __shfl_xor(v, 32, 64);
     return v;
 }
+// sum over the 64 lanes of a wave (the same pairing order as a xor butterfly 1, 2, ..., 32)
+__device__ __forceinline__ float wave_sum(float v) { return sum_groups(sum16(v)); }
 
 template <int N_, int P_, int R_, int Q_, int NW_>
 struct BCfg {
@@ -879,7 +881,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     float *SMALLp = (float *)(smem + CF::O_SMALL);
     float *Bp = SMALLp, *BpRaw = Bp + R * N, *Xp = BpRaw + R * N, *dBcIn = Xp + R * P, *dBcOut = dBcIn + R * N;
     float *dXcIn = dBcOut + R * N, *dXcOut = dXcIn + R * P, *INVBP = dXcOut + R * P, *BBA = INVBP + R;
-    float *CBA = BBA + N, *MISC = CBA + N, *RED = MISC + 16, *TMPC = RED + 16;   // RED: 8 floats, TMPC: [Q]
+    float *CBA = BBA + N, *MISC = CBA + N, *RED = MISC + 16, *TMPC = RED + 16;   // RED: 16 floats, TMPC: [Q]
     float *dCf = (float *)(smem + CF::O_DCF), *dBf = (float *)(smem + CF::O_DBF), *Sf = (float *)(smem + CF::O_SF);
     bf16 *Ct = (bf16 *)(smem + CF::O_CT), *Bt = (bf16 *)(smem + CF::O_BT), *Xb = (bf16 *)(smem + CF::O_XB);
     bf16 *XcB = (bf16 *)(smem + CF::O_XC), *dYb = (bf16 *)(smem + CF::O_DY), *EdYb = (bf16 *)(smem + CF::O_EDY);
@@ -1440,7 +1442,13 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
                 dacc[v][i] = ES[e_] * gacc[v][i] + a1[i];
             }
         }
-        const float gh = block_sum(gh_acc, RED);   // (also orders every write above before the reads below)
+        // <G^, H'>: per-wave sums in RED[0, NW), added in wave order by the scalar thread below
+        static_assert(NW <= 8, "per-wave partials");
+        {
+            const float w = wave_sum(gh_acc);
+            if (lane == 0) RED[wave] = w;
+        }
+        __syncthreads();   // (also orders every write above before the reads below)
         // The fold's products with dH' (in registers): dH' Xp^T and dH'^T Bp, as per-tile partial
         // sums in LDS (Gb is free: G^ is no longer read), added up below in a fixed order.
         // A wave's tiles share one row block and cover UPW consecutive column blocks, so dH' Xp^T
@@ -1532,12 +1540,9 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             for (int e = tid; e < R * N; e += NT) dBcOut[e] = 0.f;
             for (int e = tid; e < R * P; e += NT) dXcOut[e] = 0.f;
         }
-        const float fold = block_sum(fold_acc, RED);
-        if (tid == 0) {
-            DDL[0] += fold;
-            float dSe = ES[e_] * gh;
-            for (int u = 0; u < nq; u++) dSe += TMPC[u];
-            DS[e_] += dSe;
+        {
+            const float w = wave_sum(fold_acc);
+            if (lane == 0) RED[8 + wave] = w;
         }
         __syncthreads();
         // reverse prefix sums over the chunk's tokens (past the end every term is zero): each pair's
@@ -1554,6 +1559,16 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             }
         }
         if (tid == NT - 1) {   // (a thread of the last wave, idle in the loop above)
+            // the fold's d delta_0 and the state's share of dS_e, then dS's reverse prefix
+            float gh = 0.f, fold = 0.f;
+            for (int w = 0; w < NW; w++) {
+                gh += RED[w];
+                fold += RED[8 + w];
+            }
+            DDL[0] += fold;
+            float dSe = ES[e_] * gh;
+            for (int u = 0; u < nq; u++) dSe += TMPC[u];
+            DS[e_] += dSe;
             float v[Q];
 #pragma unroll
             for (int t = 0; t < Q; t++) v[t] = DS[t];
