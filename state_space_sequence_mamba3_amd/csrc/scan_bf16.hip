@@ -475,9 +475,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     auto chunk_body = [&](auto FULLC, int64_t c0) {
         constexpr bool FULL = decltype(FULLC)::value;
         const int nq = FULL ? Q : (int)(len - c0);
-        // with the fused prologue / epilogue the registers run short: the lane-derived address
-        // math of the prefetch, staging and output code is recomputed in every chunk
-        const int tq = opaque<CF::EPI>(tid);
+        // with the fused prologue / epilogue, and at N = 128, R = 4, the registers run short: the
+        // lane-derived address math of the prefetch, staging and output code is recomputed in
+        // every chunk (for the other plain shapes hoisting it is faster)
+        const int tq = opaque<CF::EPI || (CF::N == 128 && CF::R == 4)>(tid);
         const int64_t tok0 = start + c0;
         int task_tb[TPW];
 #pragma unroll
