@@ -307,17 +307,28 @@ def test_decode_without_previous_token(oracle):
     assert float(np.max(num / np.abs(yo).max(axis=(2, 3)))) < TOL_BF16
 
 
-def test_decode_slots(oracle):
+@pytest.mark.parametrize("shape,block", [
+    (dict(), False),                                          # column kernel (P = 64)
+    (dict(), True),                                           # column kernel, fused prologue / gate
+    (dict(headdim=16, dstate=16, rank=1, dtype="f32"), True),   # tile kernel (P = 16), fp32
+])
+def test_decode_slots(oracle, shape, block):
     """Slot-indexed states: batch rows update pool slots [3, -, 0, 6, -] (one row with a negative
     slot, one past the pool); inactive rows leave their y rows and every other slot untouched,
     bit for bit; active rows match the oracle from the gathered states and match, bit for bit,
     the same step run on the gathered states without slots."""
     import torch
     dev = device()
-    cfg = dict(synth.CONFIGS[3], batch=5, nheads=4)
+    cfg = dict(synth.CONFIGS[3], batch=5, nheads=4, **shape)
     inp = synth.decode_inputs(cfg, seed=28, ring=1)
+    if block:
+        inp = synth.block_inputs(inp, seed=30)
     d = upload(inp, dev)
     H, N, P = 4, cfg["dstate"], cfg["headdim"]
+    tol = TOL_F32 if cfg.get("dtype") == "f32" else TOL_BF16
+    blk = {}
+    if block:
+        blk = dict(B_bias=d["B_bias"], C_bias=d["C_bias"], z=d["z"][0], bc_norm=True, bc_eps=d["bc_eps"])
     rng = np.random.default_rng(29)
     pool0 = rng.standard_normal((7, H, N, P)).astype(np.float32)
     slots = np.array([3, -1, 0, 6, 7], dtype=np.int32)
@@ -327,11 +338,11 @@ def test_decode_slots(oracle):
     sentinel = torch.full_like(d["x"][0], 7.0)
     note("decode with slots")
     args = [d[k][0] for k in ("x", "dt", "lam", "theta", "B", "C")] + [d["A"], d["D"]]
-    m3.mamba3_decode_step(*args, h=pool, y=sentinel, Bprev=d["Bprev"], xprev=d["xprev"], slots=sl)
+    m3.mamba3_decode_step(*args, h=pool, y=sentinel, Bprev=d["Bprev"], xprev=d["xprev"], slots=sl, **blk)
     hg = torch.from_numpy(pool0[slots[active]]).to(dev).contiguous()
     hfull = torch.zeros((5, H, N, P), dtype=torch.float32, device=dev)
     hfull[active] = hg
-    y_ref = m3.mamba3_decode_step(*args, h=hfull, Bprev=d["Bprev"], xprev=d["xprev"])
+    y_ref = m3.mamba3_decode_step(*args, h=hfull, Bprev=d["Bprev"], xprev=d["xprev"], **blk)
     torch.cuda.synchronize()
     pool_g, y_g, y_r, h_r = from_dev(pool), from_dev(sentinel), from_dev(y_ref), from_dev(hfull)
     untouched = [s for s in range(7) if s not in slots[active]]
@@ -340,7 +351,10 @@ def test_decode_slots(oracle):
     assert np.array_equal(y_g[active], y_r[active]) and np.array_equal(pool_g[slots[active]], h_r[active])
     tok = {k: inp[k][0][active] for k in ("x", "dt", "lam", "theta", "B", "C")}
     tok.update(A=inp["A"], D=inp["D"], Bprev=inp["Bprev"][active], xprev=inp["xprev"][active])
+    if block:
+        tok.update(B_bias=inp["B_bias"], C_bias=inp["C_bias"], z=inp["z"][0][active], bc_norm=True,
+                   bc_eps=inp["bc_eps"])
     yo, ho = oracle.decode(tok, pool0[slots[active]].astype(np.float64))
     num = np.abs(y_g[active] - yo).max(axis=(2, 3))
-    assert float(np.max(num / np.abs(yo).max(axis=(2, 3)))) < TOL_BF16
-    assert state_relerr(pool_g[slots[active]], ho) < 1e-5
+    assert float(np.max(num / np.abs(yo).max(axis=(2, 3)))) < tol
+    assert state_relerr(pool_g[slots[active]], ho) < (tol if cfg.get("dtype") == "f32" else 1e-5)
