@@ -23,8 +23,10 @@
  *   x, y        [batch, seqlen, H, R, P]        token inputs / outputs
  *   dt, lam     [batch, seqlen, H]              step (post-softplus), trapezoid weight in [0,1]
  *   theta       [batch, seqlen, H, N/2]         rotation frequency; the angle is dt*theta
+ *                                               (or [batch, seqlen, Gth, N/2]: theta_groups)
  *   B, C        [batch, seqlen, G, R, N]
- *   A, D        [H] fp32                         decay (A < 0) and skip; D may be NULL (= 0)
+ *   A, D        [H] fp32                         decay (A < 0) and skip; D may be NULL (= 0);
+ *                                               A may be NULL with a per-token A_tok
  *   states      [S, H, N, P] fp32                S = batch (padded) or nseq (packed)
  *   Bprev       [S, G, R, N],  xprev [S, H, R, P]   token before position 0 of each sequence
  * Token inputs x, dt, lam, theta, B, C, Bprev, xprev and the output y share
@@ -193,8 +195,11 @@ mamba3_status mamba3_scan_fwd(const mamba3_scan_args *args, void *stream);
  * workspace: device memory of at least mamba3_scan_bwd_workspace_size(args)
  * bytes, owned by the caller, 256-byte aligned. It holds the state entering
  * every chunk (the backward walks the chunks in reverse) and per-(sequence,
- * head) partial sums, so that every sum is formed in a fixed order: the
- * results are bitwise reproducible. Its contents are scratch on return. */
+ * head) partial sums (per head also for dB, dC with G < H and for dtheta with
+ * theta_groups < H), so that every sum is formed in a fixed order: the
+ * results are bitwise reproducible. Its contents are scratch on return. The
+ * size depends on the shapes, the chunk the backward picks and which inputs
+ * are present, so query it for every distinct argument set. */
 typedef struct {
     mamba3_scan_args fwd;
     const void *dy;
