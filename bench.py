@@ -532,8 +532,9 @@ def main():
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the scan and decode shard over (sequence, head) with no communication", file=sys.stderr)
+        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}); the scan and decode shard over "
+              "(sequence, head) with no communication, so each GPU would run this same workload share",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
