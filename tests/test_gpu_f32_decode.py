@@ -358,3 +358,47 @@ def test_decode_slots(oracle, shape, block):
     num = np.abs(y_g[active] - yo).max(axis=(2, 3))
     assert float(np.max(num / np.abs(yo).max(axis=(2, 3)))) < tol
     assert state_relerr(pool_g[slots[active]], ho) < (tol if cfg.get("dtype") == "f32" else 1e-5)
+
+
+def test_decode_graph_replay():
+    """Three decode steps captured in a HIP graph and replayed several times, with the program's
+    own eager work and synchronisations between the replays: every replay equals the same three
+    steps run eagerly from the same starting state, bit for bit."""
+    import torch
+    dev = device()
+    cfg = dict(synth.CONFIGS[3], batch=8, nheads=4)
+    inp = synth.decode_inputs(cfg, seed=33, ring=3)
+    d = upload(inp, dev)
+    h0 = d["h"].clone()
+    h = h0.clone()
+    ys = [torch.empty_like(d["x"][0]) for _ in range(3)]
+
+    def steps():
+        Bprev, xprev = d["Bprev"], d["xprev"]
+        for i in range(3):
+            m3.mamba3_decode_step(d["x"][i], d["dt"][i], d["lam"][i], d["theta"][i], d["B"][i], d["C"][i], d["A"],
+                                  d["D"], h=h, y=ys[i], Bprev=Bprev, xprev=xprev,
+                                  stream=torch.cuda.current_stream())
+            Bprev, xprev = d["B"][i], d["x"][i]
+
+    note("decode graph replay")
+    steps()
+    torch.cuda.synchronize()
+    y_eager = [y.clone() for y in ys]
+    h_eager = h.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        h.copy_(h0)
+        with torch.cuda.graph(g):
+            steps()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        h.copy_(h0)                       # eager work between the replays
+        ys[0].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(ys, y_eager)), rep
+        assert torch.equal(h, h_eager), rep
