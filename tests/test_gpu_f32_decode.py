@@ -288,6 +288,19 @@ def test_decode_config3_full_batch(oracle):
     assert state_relerr(hg, ho) < 1e-5
 
 
+def test_decode_siso_full_batch(oracle):
+    """The SISO decode shape of the bench (batch 256, 64 heads, N = 128, R = 1), whole batch, 2 steps."""
+    inp = synth.decode_inputs(dict(synth.CONFIGS[3], dstate=128, rank=1), ring=2)
+    note("SISO decode full batch, 2 steps")
+    yg, hg = run_decode(inp, steps=2)
+    yo, ho = oracle_decode(oracle, inp, steps=2)
+    for a, b in zip(yg, yo):
+        num = np.abs(a - b).max(axis=(2, 3))
+        den = np.abs(b).max(axis=(2, 3))
+        assert float(np.max(num / den)) < TOL_BF16
+    assert state_relerr(hg, ho) < 1e-5
+
+
 def test_decode_without_previous_token(oracle):
     cfg = dict(synth.CONFIGS[3], batch=4, nheads=2)
     inp = synth.decode_inputs(cfg, seed=5, ring=1)

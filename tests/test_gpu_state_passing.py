@@ -129,3 +129,31 @@ def test_long_sequence_matches_unsplit():
     y2, h2 = segmented(d, 8, 64)
     torch.cuda.synchronize()
     assert slab_relerr(y2, from_dev(y1)) < TOL_BF16 and state_relerr(h2, from_dev(h1)) < TOL_BF16
+
+
+def test_long_sequence_full_size_sampled_heads(oracle):
+    """The bench's long-sequence workload (one 65536-token SISO sequence, 64 heads) in its launch
+    configuration (16 segments): two sampled heads' y and final state against the oracle's
+    whole-sequence scan of that head alone (G = H: a head reads only its own rows)."""
+    import torch
+    dev = device()
+    c = synth.CONFIGS[1]
+    d = synth.torch_scan_inputs(1, dev, seed=11, batch=1, seqlen=65536)
+    note("segmented scan, 1 x 65536 tokens, 16 segments")
+    y, h = m3.mamba3_scan_segmented(d["x"], d["dt"], d["lam"], d["theta"], d["B"], d["C"], d["A"], d["D"],
+                                    nseg=16, chunk=c["chunk"])
+    torch.cuda.synchronize()
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    for hh in (0, 37):
+        one = {k: bits(d[k][:, :, hh:hh + 1]) for k in ("x", "dt", "lam", "theta", "B", "C")}
+        one.update(A=d["A"][hh:hh + 1].cpu().numpy(), D=d["D"][hh:hh + 1].cpu().numpy())
+        yo, ho = oracle.scan_slab(one, 0, 0)
+        ey = float(np.abs(from_dev(y[0, :, hh]) - yo).max() / np.abs(yo).max())
+        eh = float(np.abs(from_dev(h[0, hh]) - ho).max() / np.abs(ho).max())
+        note(f"  head {hh}: y relerr {ey:.2e}  h relerr {eh:.2e}")
+        assert ey < TOL_BF16 and eh < TOL_BF16
+    del d, y, h
+    torch.cuda.empty_cache()
