@@ -258,7 +258,7 @@ mamba3_status mamba3_scan_bwd(const mamba3_scan_bwd_args *args, void *stream);
  *            the previous segment; fwd.Bprev/xprev, or zeros, for segment 0),
  *            raw as read (the prologue, if any, is applied by the scan).
  * h_out      [batch, H, N, P] fp32 out or NULL: the final state of every
- *            sequence.
+ *            sequence (it may be fwd.h_in exactly).
  * The outputs must not overlap each other or any input. Alignment: 16 bytes
  * for U and every output. The prologue settings of fwd (bc_norm, biases)
  * apply to the folded previous token, as in the scan. Deterministic. */
@@ -273,6 +273,33 @@ typedef struct {
 
 mamba3_status mamba3_state_passing_validate(const mamba3_state_passing_args *args);
 mamba3_status mamba3_state_passing(const mamba3_state_passing_args *args, void *stream);
+
+/* The whole-sequence scan run as batch * nseg independent segments (ABI
+ * 1.4): steps 1-3 above, enqueued in order on one stream. The result equals
+ * mamba3_scan_fwd's up to rounding; it does the scan's work twice but
+ * multiplies the workgroups by nseg, which pays for a few long sequences.
+ *
+ * fwd        as for mamba3_scan_fwd (padded mode only; fwd.workspace must be
+ *            NULL / 0). y and h_out (if given) are written as by
+ *            mamba3_scan_fwd; h_in, Bprev and xprev are honoured.
+ * nseg       segments per sequence, >= 1, dividing seqlen; seqlen >= 1.
+ * workspace  device memory of at least mamba3_scan_segmented_workspace_size
+ *            bytes, 256-byte aligned, owned by the caller: the segments' zero-
+ *            state final states and entering states (fp32) and their previous
+ *            tokens. Its contents are scratch on return. It must not overlap
+ *            any input or output.
+ * Errors as for mamba3_scan_fwd and mamba3_state_passing; MAMBA3_EUNSUPPORTED
+ * also when no kernel exists for the segments' shape (chunk as in fwd). */
+typedef struct {
+    mamba3_scan_args fwd;
+    int32_t nseg;
+    void *workspace;
+    size_t workspace_bytes;
+} mamba3_scan_segmented_args;
+
+size_t mamba3_scan_segmented_workspace_size(const mamba3_scan_segmented_args *args);
+mamba3_status mamba3_scan_segmented_validate(const mamba3_scan_segmented_args *args);
+mamba3_status mamba3_scan_segmented(const mamba3_scan_segmented_args *args, void *stream);
 
 /* One decode step for a batch of independent sequences, state updated in
  * place: h <- alpha R (h + delta Bprev xprev^T) + gamma B x^T, y = h^T C + D x

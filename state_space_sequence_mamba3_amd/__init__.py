@@ -66,9 +66,15 @@ class StatePassingArgs(ctypes.Structure):
     ]
 
 
+class ScanSegmentedArgs(ctypes.Structure):
+    """Mirror of ``mamba3_scan_segmented_args``."""
+    _fields_ = [("fwd", ScanArgs), ("nseg", _i32), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+
+
 EXPORTS = ("mamba3_scan_validate", "mamba3_scan_workspace_size", "mamba3_scan_fwd", "mamba3_scan_bwd_validate",
            "mamba3_scan_bwd_workspace_size", "mamba3_scan_bwd", "mamba3_state_passing_validate",
-           "mamba3_state_passing", "mamba3_decode_validate", "mamba3_decode_step", "mamba3_status_string",
+           "mamba3_state_passing", "mamba3_scan_segmented_workspace_size", "mamba3_scan_segmented_validate",
+           "mamba3_scan_segmented", "mamba3_decode_validate", "mamba3_decode_step", "mamba3_status_string",
            "mamba3_version")
 
 _lib = None
@@ -103,6 +109,12 @@ def lib():
         l.mamba3_state_passing_validate.restype = ctypes.c_int
         l.mamba3_state_passing.argtypes = [ctypes.POINTER(StatePassingArgs), _vp]
         l.mamba3_state_passing.restype = ctypes.c_int
+        l.mamba3_scan_segmented_workspace_size.argtypes = [ctypes.POINTER(ScanSegmentedArgs)]
+        l.mamba3_scan_segmented_workspace_size.restype = ctypes.c_size_t
+        l.mamba3_scan_segmented_validate.argtypes = [ctypes.POINTER(ScanSegmentedArgs)]
+        l.mamba3_scan_segmented_validate.restype = ctypes.c_int
+        l.mamba3_scan_segmented.argtypes = [ctypes.POINTER(ScanSegmentedArgs), _vp]
+        l.mamba3_scan_segmented.restype = ctypes.c_int
         l.mamba3_decode_validate.argtypes = [ctypes.POINTER(DecodeArgs)]
         l.mamba3_decode_validate.restype = ctypes.c_int
         l.mamba3_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
@@ -271,32 +283,34 @@ def mamba3_state_passing(x, dt, lam, theta, B, C, A, *, nseg, U, h_in=None, Bpre
     return seg_h, seg_B, seg_x, h_out
 
 
-def mamba3_scan_segmented(x, dt, lam, theta, B, C, A, D=None, *, nseg, h_in=None, Bprev=None, xprev=None, chunk=64,
-                          want_state=True, stream=None, B_bias=None, C_bias=None, z=None, bc_norm=False, bc_eps=1e-5,
-                          A_tok=None, lam_fixed=0.5):
-    """The scan of whole sequences run as batch*nseg independent segments:
-    a scan of the segments from zero states, mamba3_state_passing, and a scan
-    of the segments from their entering states. Same results as
-    mamba3_scan_fwd up to rounding; more workgroups for few long sequences.
-    Returns (y, h_out)."""
-    b, L = x.shape[0], x.shape[1]
-    if L % nseg:
-        raise ValueError("nseg must divide seqlen")
+def mamba3_scan_segmented_validate(args: ScanSegmentedArgs) -> int:
+    return lib().mamba3_scan_segmented_validate(ctypes.byref(args))
 
-    def seg(t):
-        return None if t is None else t.reshape((b * nseg, L // nseg) + tuple(t.shape[2:]))
 
-    xs, dts, lams, ths, Bs, Cs, zs, ats = (seg(t) for t in (x, dt, lam, theta, B, C, z, A_tok))
-    kw = dict(chunk=chunk, stream=stream, B_bias=B_bias, C_bias=C_bias, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=ats,
-              lam_fixed=lam_fixed)
-    y, U = mamba3_scan_fwd(xs, dts, lams, ths, Bs, Cs, A, None, **kw)
-    seg_h, seg_B, seg_x, h_out = mamba3_state_passing(
-        x, dt, lam, theta, B, C, A, nseg=nseg, U=U, h_in=h_in, Bprev=Bprev, xprev=xprev, B_bias=B_bias,
-        C_bias=C_bias, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=A_tok, lam_fixed=lam_fixed, want_state=want_state,
-        stream=stream)
-    y, _ = mamba3_scan_fwd(xs, dts, lams, ths, Bs, Cs, A, D, y=y, h_in=seg_h, Bprev=seg_B, xprev=seg_x,
-                           want_state=False, z=zs, **kw)
-    return y.reshape(x.shape), h_out
+def mamba3_scan_segmented(x, dt, lam, theta, B, C, A, D=None, *, nseg, y=None, h_in=None, h_out=None, Bprev=None,
+                          xprev=None, chunk=64, want_state=True, workspace=None, stream=None, B_bias=None,
+                          C_bias=None, z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5):
+    """mamba3_scan_segmented: the whole-sequence scan run as batch*nseg
+    independent segments (scan, state passing, scan, all in the library).
+    Same results as mamba3_scan_fwd up to rounding. The workspace is allocated
+    when not given. Returns (y, h_out)."""
+    import torch
+    if y is None:
+        y = torch.empty_like(x)
+    if h_out is None and want_state:
+        h_out = torch.empty((x.shape[0], x.shape[2], B.shape[4], x.shape[4]), dtype=torch.float32, device=x.device)
+    fwd = scan_args(x, dt, lam, theta, B, C, A, D, y=y, h_in=h_in, h_out=h_out, Bprev=Bprev, xprev=xprev,
+                    chunk=chunk, B_bias=B_bias, C_bias=C_bias, z=z, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=A_tok,
+                    lam_fixed=lam_fixed)
+    a = ScanSegmentedArgs(fwd, int(nseg), None, 0)
+    need = lib().mamba3_scan_segmented_workspace_size(ctypes.byref(a))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    st = lib().mamba3_scan_segmented(ctypes.byref(a), _stream(stream))
+    if st != MAMBA3_OK:
+        raise Mamba3Error(st, "mamba3_scan_segmented")
+    return y, h_out
 
 
 def decode_args(x, dt, lam, theta, B, C, A, D=None, *, h, y, Bprev=None, xprev=None, B_bias=None, C_bias=None,

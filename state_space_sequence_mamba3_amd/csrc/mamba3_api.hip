@@ -241,8 +241,11 @@ mamba3_status mamba3_state_passing_validate(const mamba3_state_passing_args *sp)
                    span(sp->U, SR * H * N * P, 4)};
     const int nout = sizeof outs / sizeof outs[0];
     for (int i = 0; i < nout; i++) {
-        for (Range r : ins)
+        for (Range r : ins) {
+            // h_out may be h_in exactly (each workgroup reads its slab's h_in before it writes h_out)
+            if (i == 3 && sp->h_out && sp->h_out == f.h_in && r.lo == (const char *)f.h_in) continue;
             if (overlaps(outs[i], r)) return MAMBA3_EINVAL;
+        }
         for (int j = i + 1; j < nout; j++)
             if (overlaps(outs[i], outs[j])) return MAMBA3_EINVAL;
     }
@@ -254,6 +257,119 @@ mamba3_status mamba3_state_passing(const mamba3_state_passing_args *sp, void *st
     const mamba3_status st = mamba3_state_passing_validate(sp);
     if (st != MAMBA3_OK) return st;
     return m3::launch_state_passing(sp, (hipStream_t)stream);
+}
+
+// Segmented scan: the workspace holds U and the entering states [b*nseg, H, N, P] fp32, then the
+// previous tokens [b*nseg, G, R, N] and [b*nseg, H, R, P] in the token dtype (each region
+// 256-byte aligned).
+namespace {
+struct SegWs {
+    size_t U, h, B, x, total;
+};
+SegWs seg_ws(const mamba3_scan_segmented_args *a) {
+    const mamba3_scan_args &f = a->fwd;
+    const int64_t SR = (int64_t)f.batch * (a->nseg > 0 ? a->nseg : 0);
+    const int64_t H = f.nheads, G = f.ngroups, P = f.headdim, N = f.dstate, R = f.rank;
+    const int64_t es = f.dtype == MAMBA3_BF16 ? 2 : 4;
+    auto al = [](int64_t v) { return (size_t)((v + 255) / 256 * 256); };
+    SegWs w;
+    size_t o = 0;
+    w.U = o; o += al(SR * H * N * P * 4);
+    w.h = o; o += al(SR * H * N * P * 4);
+    w.B = o; o += al(SR * G * R * N * es);
+    w.x = o; o += al(SR * H * R * P * es);
+    w.total = o;
+    return w;
+}
+// The three calls' arguments, built over the workspace.
+void seg_calls(const mamba3_scan_segmented_args *a, mamba3_scan_args *pass1, mamba3_state_passing_args *sp,
+               mamba3_scan_args *pass2) {
+    const mamba3_scan_args &f = a->fwd;
+    const SegWs w = seg_ws(a);
+    char *ws = (char *)a->workspace;
+    float *U = (float *)(ws + w.U), *segh = (float *)(ws + w.h);
+    void *segB = ws + w.B, *segx = ws + w.x;
+    mamba3_scan_args rows = f;   // the segments as independent rows of seqlen / nseg tokens
+    rows.batch = f.batch * a->nseg;
+    rows.seqlen = a->nseg > 0 ? f.seqlen / a->nseg : 0;
+    rows.workspace = nullptr;
+    rows.workspace_bytes = 0;
+    *pass1 = rows;                // from zero states, no previous token, no gate: U in h_out
+    pass1->h_in = nullptr;
+    pass1->Bprev = pass1->xprev = nullptr;
+    pass1->z = nullptr;
+    pass1->h_out = U;
+    *sp = mamba3_state_passing_args{};
+    sp->fwd = f;
+    sp->fwd.y = nullptr;
+    sp->fwd.h_out = nullptr;
+    sp->fwd.z = nullptr;
+    sp->fwd.D = nullptr;
+    sp->nseg = a->nseg;
+    sp->U = U;
+    sp->seg_h_in = segh;
+    sp->seg_Bprev = segB;
+    sp->seg_xprev = segx;
+    sp->h_out = f.h_out;
+    *pass2 = rows;                // from the entering states, with the previous tokens
+    pass2->h_in = segh;
+    pass2->Bprev = segB;
+    pass2->xprev = segx;
+    pass2->h_out = nullptr;
+}
+}  // namespace
+
+size_t mamba3_scan_segmented_workspace_size(const mamba3_scan_segmented_args *a) {
+    if (!a || a->nseg < 1 || a->fwd.batch < 0 || a->fwd.nheads < 1 || a->fwd.headdim < 1 || a->fwd.dstate < 2 ||
+        a->fwd.rank < 1 || a->fwd.ngroups < 1)
+        return 0;
+    return seg_ws(a).total;
+}
+
+mamba3_status mamba3_scan_segmented_validate(const mamba3_scan_segmented_args *a) {
+    if (!a) return MAMBA3_EINVAL;
+    const mamba3_scan_args &f = a->fwd;
+    if (f.workspace || f.workspace_bytes) return MAMBA3_EINVAL;
+    mamba3_status st = scan_args_check(&f);
+    if (st != MAMBA3_OK) return st;
+    if (f.cu_seqlens) return MAMBA3_EUNSUPPORTED;
+    if (a->nseg < 1 || f.seqlen < 1 || f.seqlen % a->nseg) return MAMBA3_EINVAL;
+    const size_t need = seg_ws(a).total;
+    if (a->workspace_bytes < need || !a->workspace) return MAMBA3_EWORKSPACE;
+    if ((uintptr_t)a->workspace & 255u) return MAMBA3_EALIGN;
+    // the workspace against every input and output of the whole-sequence call
+    const int64_t es = f.dtype == MAMBA3_BF16 ? 2 : 4;
+    const int64_t S = f.batch, T = (int64_t)f.batch * f.seqlen;
+    const int64_t H = f.nheads, G = f.ngroups, P = f.headdim, N = f.dstate, R = f.rank;
+    const int64_t Gth = f.theta_groups ? f.theta_groups : H;
+    const Range wsr = span(a->workspace, (int64_t)a->workspace_bytes, 1);
+    Range all[] = {span(f.x, T * H * P * R, es), span(f.dt, T * H, es), span(f.lam, T * H, es),
+                   span(f.theta, T * Gth * (N / 2), es), span(f.B, T * G * N * R, es), span(f.C, T * G * N * R, es),
+                   span(f.h_in, S * H * N * P, 4), span(f.Bprev, S * G * N * R, es), span(f.xprev, S * H * P * R, es),
+                   span(f.h_out, S * H * N * P, 4), span(f.B_bias, H * N, 4), span(f.C_bias, H * N, 4),
+                   span(f.z, T * H * P * R, es), span(f.A_tok, T * H, es), span(f.y, T * H * P * R, es),
+                   span(f.A, H, 4), span(f.D, H, 4)};
+    for (Range r : all)
+        if (overlaps(wsr, r)) return MAMBA3_EINVAL;
+    // each call's own checks (kernel availability for the segment rows included)
+    mamba3_scan_args p1, p2;
+    mamba3_state_passing_args sp;
+    seg_calls(a, &p1, &sp, &p2);
+    if ((st = mamba3_scan_validate(&p1)) != MAMBA3_OK) return st;
+    if ((st = mamba3_state_passing_validate(&sp)) != MAMBA3_OK) return st;
+    return mamba3_scan_validate(&p2);
+}
+
+mamba3_status mamba3_scan_segmented(const mamba3_scan_segmented_args *a, void *stream) {
+    mamba3_status st = mamba3_scan_segmented_validate(a);
+    if (st != MAMBA3_OK) return st;
+    if (a->fwd.batch == 0) return MAMBA3_OK;
+    mamba3_scan_args p1, p2;
+    mamba3_state_passing_args sp;
+    seg_calls(a, &p1, &sp, &p2);
+    if ((st = mamba3_scan_fwd(&p1, stream)) != MAMBA3_OK) return st;
+    if ((st = mamba3_state_passing(&sp, stream)) != MAMBA3_OK) return st;
+    return mamba3_scan_fwd(&p2, stream);
 }
 
 mamba3_status mamba3_decode_validate(const mamba3_decode_args *a) {

@@ -1,6 +1,7 @@
 """C ABI on the CPU: the library loads, exports every declared symbol, and its
 pure host-side validation returns the documented status codes. No compute
 call is made here (no GPU in this tier)."""
+import ctypes
 import os
 import re
 
@@ -198,6 +199,39 @@ def test_state_passing_validate(lib):
     a = good_sp()
     a.fwd.seqlen = 0
     assert m3.mamba3_state_passing_validate(a) == m3.MAMBA3_EINVAL
+
+
+def good_seg(**over):
+    fwd = good_scan(h_in=fake(11), Bprev=fake(12), xprev=fake(13))
+    a = m3.ScanSegmentedArgs(fwd=fwd, nseg=4, workspace=fake(30), workspace_bytes=1 << 32)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_scan_segmented_validate(lib):
+    need = m3.lib().mamba3_scan_segmented_workspace_size(ctypes.byref(good_seg()))
+    # U and the entering states (2 x 8 rows x 4 heads x 16 x 16 fp32) and the previous tokens
+    assert need == 2 * 8 * 4 * 16 * 16 * 4 + 8 * 4 * 16 * 4 + 8 * 4 * 16 * 4
+    assert m3.mamba3_scan_segmented_validate(good_seg()) == m3.MAMBA3_OK
+    assert m3.mamba3_scan_segmented_validate(good_seg(workspace_bytes=need)) == m3.MAMBA3_OK
+    assert m3.mamba3_scan_segmented_validate(good_seg(workspace_bytes=need - 1)) == m3.MAMBA3_EWORKSPACE
+    assert m3.mamba3_scan_segmented_validate(good_seg(workspace=None)) == m3.MAMBA3_EWORKSPACE
+    assert m3.mamba3_scan_segmented_validate(good_seg(workspace=fake(30) + 128)) == m3.MAMBA3_EALIGN
+    assert m3.mamba3_scan_segmented_validate(good_seg(workspace=fake(9) + 256)) == m3.MAMBA3_EINVAL   # inside y
+    assert m3.mamba3_scan_segmented_validate(good_seg(nseg=3)) == m3.MAMBA3_EINVAL          # 100 tokens
+    a = good_seg()
+    a.fwd.workspace, a.fwd.workspace_bytes = fake(31), 256
+    assert m3.mamba3_scan_segmented_validate(a) == m3.MAMBA3_EINVAL
+    a = good_seg()
+    a.fwd.cu_seqlens, a.fwd.batch, a.fwd.nseq = fake(32), 1, 2
+    assert m3.mamba3_scan_segmented_validate(a) == m3.MAMBA3_EUNSUPPORTED
+    a = good_seg()
+    a.fwd.h_out = fake(11)                                                          # h_out may be h_in
+    assert m3.mamba3_scan_segmented_validate(a) == m3.MAMBA3_OK
+    a = good_seg(nseg=2)
+    a.fwd.dtype, a.fwd.dstate, a.fwd.headdim, a.fwd.chunk = m3.MAMBA3_BF16, 48, 48, 64   # no bf16 kernel
+    assert m3.mamba3_scan_segmented_validate(a) == m3.MAMBA3_EUNSUPPORTED
 
 
 def test_decode_validate_prologue(lib):
