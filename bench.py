@@ -434,14 +434,18 @@ def summarize_stats(stats_dir, out_md, command):
             other_ms += ns / 1e6
             continue
         wg = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
-        groups[(r["Kernel_Name"], wg)].append(ns)
+        groups[(r["Kernel_Name"], wg)].append((float(r["Start_Timestamp"]), ns))
     lines = ["# rocprofv3 kernel statistics", "", "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
              "```", command, "```", "",
-             "Per (kernel, workgroups), from the run's kernel trace.", "",
-             "| kernel | workgroups | calls | average us | min us | max us | total ms |", "|---|---|---|---|---|---|---|"]
-    for (name, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+             "Per (kernel, workgroups), from the run's kernel trace. The bench times the last half of each "
+             "workload's launches (its warmup equals its timed steps by default): the last column averages those.", "",
+             "| kernel | workgroups | calls | average us | min us | max us | total ms | average of the last half us |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (name, wg), tv in sorted(groups.items(), key=lambda kv: -sum(n for _, n in kv[1])):
+        v = [n for _, n in sorted(tv)]
+        last = v[len(v) // 2:]
         lines.append(f"| `{_short(name)}` | {wg} | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | {min(v) / 1e3:.2f} | "
-                     f"{max(v) / 1e3:.2f} | {sum(v) / 1e6:.3f} |")
+                     f"{max(v) / 1e3:.2f} | {sum(v) / 1e6:.3f} | {sum(last) / len(last) / 1e3:.2f} |")
     lines += ["", f"Not listed: {len(other)} other kernels (torch's input generation and copies), {other_ms:.3f} ms in total."]
     open(out_md, "w").write("\n".join(lines) + "\n")
     print(f"wrote {out_md}")
