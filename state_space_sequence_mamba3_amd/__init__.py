@@ -131,9 +131,18 @@ def status_string(status: int) -> str:
 
 
 def _ptr(t):
+    """Device address of a tensor (or an int address as is). Every pointer of the ABI is a device
+    pointer into a dense row-major array, so a host tensor or a strided view is refused here
+    rather than read as if it were dense device memory."""
     if t is None:
         return None
-    return t.data_ptr() if hasattr(t, "data_ptr") else int(t)
+    if not hasattr(t, "data_ptr"):
+        return int(t)
+    if not t.is_cuda:
+        raise ValueError("mamba3: tensors must be in device memory")
+    if not t.is_contiguous():
+        raise ValueError("mamba3: tensors must be contiguous (dense row-major); call .contiguous()")
+    return t.data_ptr()
 
 
 def _dtype_code(t) -> int:

@@ -339,3 +339,14 @@ def test_decode_validate(lib):
     assert m3.mamba3_decode_validate(good_decode(dt=BASE + 0x200000002)) == m3.MAMBA3_OK
     assert m3.mamba3_decode_validate(good_decode(dt=BASE + 0x200000001)) == m3.MAMBA3_EALIGN
     assert m3.mamba3_decode_validate(good_decode(batch=0)) == m3.MAMBA3_OK
+
+
+def test_binding_refuses_host_and_strided_tensors():
+    # every ABI pointer is a dense device array: a host tensor or a strided view never reaches the library
+    import torch
+    x = torch.zeros((2, 8, 4, 1, 16))
+    with pytest.raises(ValueError, match="device memory"):
+        m3._ptr(x)
+    with pytest.raises(ValueError, match="device memory"):
+        m3.mamba3_scan_fwd(x, x[..., 0, 0], x[..., 0, 0], x[..., 0, :8], x, x, torch.zeros(4))
+    assert m3._ptr(None) is None and m3._ptr(fake(3)) == fake(3)
