@@ -24,8 +24,9 @@
 // The fold gives d delta_0 = <dH', Bp Xp^T> and the previous token's dB, dX.
 // The block prologue (BC norm, biases) and the gate are differentiated as
 // applied. Every sum runs in a fixed order (no atomics): per-slab partial sums
-// of dA, dD and the bias gradients, and (with G < H) per-head dB, dC, dBprev,
-// go to the workspace and a second kernel adds them up.
+// of dA, dD and the bias gradients, (with G < H) per-head dB, dC, dBprev, and
+// (with shared angle rows) per-head dtheta go to the workspace and a second
+// kernel adds them up.
 //
 // Variants: a per-token decay rate A_t (its gradient is per token, dt_t dS_t),
 // and a fixed trapezoid weight (no lam gradient).
@@ -764,7 +765,11 @@ __global__ __launch_bounds__(kBwdThreads) void k_scan_bwd(BwdParams p) {
 // (masked into A = M o S and dS' = M o dP), then dX = A^T dY + c o (B~ G^), dC~ = dS' B~ +
 // e^{S} o (dY H'^T), dB~ = dS'^T C~ + c o (X G^^T), dH' = e^{S_e} G^ + C~^T (e^{S} o dY) and the
 // rotated state Inner = e^{S_e} H' + B~^T (c o X). Row and column sums that the scalar
-// gradients need are formed per tile (wave shuffles) and added in a fixed order.
+// gradients need are formed per tile (DPP row sums, wave shuffles) and added in a fixed order.
+// Latency, not bandwidth, sets the time of a chunk, so: each chunk's token inputs (and, in the
+// reverse walk, its entering state) are loaded into registers one chunk ahead; the lane index is
+// made opaque per chunk so that address math is recomputed rather than spilled; block-wide sums
+// go through per-wave partials read after barriers the phases need anyway.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -854,7 +859,7 @@ struct BCfg {
     static constexpr int O_DY = O_XC + al(QR * PS * 2);             // bf16 [QR][PS] dy0
     static constexpr int O_EDY = O_DY + al(QR * PS * 2);            // bf16 [QR][PS] e^{S} o dy0
     static constexpr int O_HB = O_EDY + al(QR * PS * 2);            // bf16 [N][PS] H'
-    static constexpr int O_GB = O_HB + al(N * PS * 2);              // bf16 [N][PS] G^ (then dH')
+    static constexpr int O_GB = O_HB + al(N * PS * 2);              // bf16 [N][PS] G^ (then the fold's partials)
     static constexpr int O_AB = O_GB + al(N * PS * 2);              // bf16 [QR][QS] A = M o S
     static constexpr int O_DSB = O_AB + al(QR * QS * 2);            // bf16 [QR][QS] dS' = M o dP
     static constexpr int LDS = O_DSB + al(QR * QS * 2);
