@@ -607,3 +607,38 @@ def test_gradient_norm_eps_zero(oracle):
     inp = rand_inputs(rng, b=1, L=6, H=4, G=2, P=2, N=4, R=1, prev=True)
     inp.update(bc_norm=True, bc_eps=0.0, B_bias=rng.uniform(0, 1, (4, 4)), C_bias=rng.uniform(0, 1, (4, 4)))
     assert fd_check(oracle, inp, rng) == 12
+
+
+def test_segment_affine_map(oracle):
+    """What state passing between segments relies on: across a segment the recurrence is affine in
+    its entering state, H_end = exp(S) R(Phi) (H_in + delta_0 Bprev xprev^T) + U, with S and Phi the
+    segment's sums of dt A and dt theta and U the segment run from a zero state with no previous
+    token (the rotations of one step all act on the same pairs, so they commute). Checked on the
+    oracle's own scans of the segments against its scan of the whole sequence."""
+    rng = np.random.default_rng(12)
+    b, L, H, G, P, N, R, nseg = 2, 24, 2, 1, 3, 6, 2, 3
+    inp = rand_inputs(rng, b=b, L=L, H=H, G=G, P=P, N=N, R=R, state=True, prev=True, scale_theta=1.5)
+    Ls = L // nseg
+    tok = ("x", "dt", "lam", "theta", "B", "C")
+    h = inp["h_in"].copy()
+    Bp, xp = inp["Bprev"], inp["xprev"]
+    for k in range(nseg):
+        seg = {kk: inp[kk][:, k * Ls:(k + 1) * Ls] for kk in tok}
+        seg.update(A=inp["A"], D=inp["D"])
+        _, U = oracle.scan(seg)                                            # zero state, no previous token
+        dt, th = seg["dt"], seg["theta"]
+        S = (dt * inp["A"][None, None, :]).sum(axis=1)                     # [b, H]
+        Phi = (dt[..., None] * th).sum(axis=1)                             # [b, H, N/2]
+        d0 = (1 - seg["lam"][:, 0]) * dt[:, 0]                             # [b, H]
+        fold = np.einsum("bgrn,bhrp->bhnp", Bp, xp)                        # G = 1: every head reads group 0
+        Hs = h + d0[..., None, None] * fold
+        c, s_ = np.cos(Phi), np.sin(Phi)
+        rot = np.empty_like(Hs)
+        rot[:, :, 0::2] = c[..., None] * Hs[:, :, 0::2] - s_[..., None] * Hs[:, :, 1::2]
+        rot[:, :, 1::2] = s_[..., None] * Hs[:, :, 0::2] + c[..., None] * Hs[:, :, 1::2]
+        h = np.exp(S)[..., None, None] * rot + U
+        Bp, xp = seg["B"][:, -1], seg["x"][:, -1]
+        pre = {kk: inp[kk][:, :(k + 1) * Ls] for kk in tok}
+        pre.update(A=inp["A"], D=inp["D"], h_in=inp["h_in"], Bprev=inp["Bprev"], xprev=inp["xprev"])
+        _, href = oracle.scan(pre)
+        assert relerr(h, href) < 1e-12, k
