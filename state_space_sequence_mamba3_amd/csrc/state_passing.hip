@@ -77,6 +77,36 @@ __global__ __launch_bounds__(kSPThreads) void k_segment_sums(SPParams p) {
         a += to_f(dt[i]) * (p.A_tok ? to_f(((const T *)p.A_tok)[i]) : p.A[h]);
     }
     spart[tid] = a;
+    // angles: with K a multiple of the 16-byte vector (VW elements), thread (token lane j, group q)
+    // reads VW consecutive angles of a token per load and keeps VW partial sums
+    constexpr int VW = 16 / sizeof(T);
+    typedef T vec_t __attribute__((ext_vector_type(VW)));
+    __shared__ float vpart[kSPThreads * VW];
+    if (K % VW == 0 && K / VW <= NT) {
+        const int KG = K / VW, TLV = NT / KG, q = tid % KG, j = tid / KG;
+        float acc[VW];
+#pragma unroll
+        for (int m = 0; m < VW; m++) acc[m] = 0.f;
+        if (j < TLV) {
+#pragma unroll 4
+            for (int t = j; t < Ls; t += TLV) {
+                const int64_t tok = t0 + t;
+                const float d = to_f(dt[tok * H + h]);
+                const vec_t v = *(const vec_t *)(th + (tok * p.Gth + gq) * K + q * VW);
+#pragma unroll
+                for (int m = 0; m < VW; m++) acc[m] += d * to_f(v[m]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < VW; m++) vpart[tid * VW + m] = acc[m];   // [j][q][m] = [j][angle]
+        __syncthreads();
+        if (tid < K) {
+            float c = 0.f;
+            for (int jj = 0; jj < TLV; jj++) c += vpart[jj * K + tid];
+            out[1 + tid] = c;
+        }
+        __syncthreads();
+    } else
     for (int kk = 0; kk < K; kk += NT / TL) {   // pairs [kk, kk + NT / TL) per pass (K > NT only)
         const int i = kk + tid % (NT / TL), j = tid / (NT / TL);
         float b = 0.f;
