@@ -275,9 +275,11 @@ mamba3_status mamba3_state_passing_validate(const mamba3_state_passing_args *arg
 mamba3_status mamba3_state_passing(const mamba3_state_passing_args *args, void *stream);
 
 /* The whole-sequence scan run as batch * nseg independent segments (ABI
- * 1.4): steps 1-3 above, enqueued in order on one stream. The result equals
- * mamba3_scan_fwd's up to rounding; it does the scan's work twice but
- * multiplies the workgroups by nseg, which pays for a few long sequences.
+ * 1.4): steps 1-3 above, enqueued in order on one stream. Step 1 runs as a
+ * state-only scan (the chunk-state updates alone: no C rows read, no scores
+ * or y formed). The result equals mamba3_scan_fwd's up to rounding; it costs
+ * about one and a half scans but multiplies the workgroups by nseg, which
+ * pays for a few long sequences.
  *
  * fwd        as for mamba3_scan_fwd (padded mode only; fwd.workspace must be
  *            NULL / 0). y and h_out (if given) are written as by

@@ -34,6 +34,7 @@ struct ScanPlan {
     int32_t nseq;
 };
 
+// The scan launchers accept y == NULL: a state-only scan (final states alone).
 mamba3_status launch_scan_f32(const mamba3_scan_args *a, hipStream_t st);
 mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st);
 bool scan_bf16_supported(int N, int P, int R, int Q);

@@ -106,8 +106,10 @@ static mamba3_status scan_args_check(const mamba3_scan_args *a, bool need_y = tr
     return MAMBA3_OK;
 }
 
-mamba3_status mamba3_scan_validate(const mamba3_scan_args *a) {
-    const mamba3_status st = scan_args_check(a);
+// The scan's checks; need_y = false admits the state-only scan (y NULL, final states alone) that
+// the segmented scan runs as its first pass.
+static mamba3_status scan_validate_impl(const mamba3_scan_args *a, bool need_y) {
+    const mamba3_status st = scan_args_check(a, need_y);
     if (st != MAMBA3_OK) return st;
     // kernel availability
     if (a->dtype == MAMBA3_F32) {
@@ -118,13 +120,8 @@ mamba3_status mamba3_scan_validate(const mamba3_scan_args *a) {
     return MAMBA3_OK;
 }
 
-size_t mamba3_scan_workspace_size(const mamba3_scan_args *a) {
-    (void)a;
-    return 0;
-}
-
-mamba3_status mamba3_scan_fwd(const mamba3_scan_args *a, void *stream) {
-    mamba3_status st = mamba3_scan_validate(a);
+static mamba3_status scan_run(const mamba3_scan_args *a, void *stream, bool need_y) {
+    mamba3_status st = scan_validate_impl(a, need_y);
     if (st != MAMBA3_OK) return st;
     const int64_t S = a->cu_seqlens ? a->nseq : a->batch;
     if (S == 0) return MAMBA3_OK;
@@ -132,6 +129,15 @@ mamba3_status mamba3_scan_fwd(const mamba3_scan_args *a, void *stream) {
     hipStream_t hs = (hipStream_t)stream;
     return a->dtype == MAMBA3_F32 ? m3::launch_scan_f32(a, hs) : m3::launch_scan_bf16(a, hs);
 }
+
+mamba3_status mamba3_scan_validate(const mamba3_scan_args *a) { return scan_validate_impl(a, true); }
+
+size_t mamba3_scan_workspace_size(const mamba3_scan_args *a) {
+    (void)a;
+    return 0;
+}
+
+mamba3_status mamba3_scan_fwd(const mamba3_scan_args *a, void *stream) { return scan_run(a, stream, true); }
 
 mamba3_status mamba3_scan_bwd_validate(const mamba3_scan_bwd_args *b) {
     if (!b) return MAMBA3_EINVAL;
@@ -294,7 +300,8 @@ void seg_calls(const mamba3_scan_segmented_args *a, mamba3_scan_args *pass1, mam
     rows.seqlen = a->nseg > 0 ? f.seqlen / a->nseg : 0;
     rows.workspace = nullptr;
     rows.workspace_bytes = 0;
-    *pass1 = rows;                // from zero states, no previous token, no gate: U in h_out
+    *pass1 = rows;                // from zero states, no previous token, state only: U in h_out
+    pass1->y = nullptr;
     pass1->h_in = nullptr;
     pass1->Bprev = pass1->xprev = nullptr;
     pass1->z = nullptr;
@@ -355,7 +362,7 @@ mamba3_status mamba3_scan_segmented_validate(const mamba3_scan_segmented_args *a
     mamba3_scan_args p1, p2;
     mamba3_state_passing_args sp;
     seg_calls(a, &p1, &sp, &p2);
-    if ((st = mamba3_scan_validate(&p1)) != MAMBA3_OK) return st;
+    if ((st = scan_validate_impl(&p1, false)) != MAMBA3_OK) return st;
     if ((st = mamba3_state_passing_validate(&sp)) != MAMBA3_OK) return st;
     return mamba3_scan_validate(&p2);
 }
@@ -367,7 +374,7 @@ mamba3_status mamba3_scan_segmented(const mamba3_scan_segmented_args *a, void *s
     mamba3_scan_args p1, p2;
     mamba3_state_passing_args sp;
     seg_calls(a, &p1, &sp, &p2);
-    if ((st = mamba3_scan_fwd(&p1, stream)) != MAMBA3_OK) return st;
+    if ((st = scan_run(&p1, stream, false)) != MAMBA3_OK) return st;
     if ((st = mamba3_state_passing(&sp, stream)) != MAMBA3_OK) return st;
     return mamba3_scan_fwd(&p2, stream);
 }

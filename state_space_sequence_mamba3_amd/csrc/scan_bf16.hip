@@ -39,8 +39,9 @@
 //     stream through two register sets two blocks ahead, and the next chunk's
 //     dt, lam, theta and C rows are loaded while the current chunk computes.
 //   * Outputs leave through a per-wave LDS transpose as 16-byte row stores.
-//     The transpose buffers share LDS with the angle table, which is dead
-//     from the end of the sweep until the next chunk rebuilds it.
+//     With the fused epilogue the transpose buffers share LDS with the angle
+//     table, which is dead from the end of the sweep until the next chunk
+//     rebuilds it.
 //
 // The EPI instantiations fuse the block prologue and epilogue (section
 // "Architectural Integration"): every B, C and Bprev column is scaled to unit
@@ -162,10 +163,13 @@ struct BfParams {
     int32_t Gth;            // angle rows per token (divides H): head h reads row h / (H / Gth)
 };
 
-template <int N_, int P_, int R_, int Q_, int NW_, int UT_, int SBR_, bool EPI_>
+template <int N_, int P_, int R_, int Q_, int NW_, int UT_, int SBR_, bool EPI_, bool YO_ = true>
 struct Cfg {
     static constexpr int N = N_, P = P_, R = R_, Q = Q_, NW = NW_, UT = UT_, SBR = SBR_;
     static constexpr bool EPI = EPI_;                        // fused block prologue / epilogue
+    // outputs; without them (a state-only scan) a chunk is its chunk-state update alone: no C
+    // rows are read, no scores or y are formed
+    static constexpr bool YO = YO_;
     static constexpr int K = N / 2, QR = Q * R;
     static constexpr int NTB = QR / 16, NSB = QR / SBR;     // 16-row t-blocks, SBR-row s-blocks
     static constexpr int NSUB = SBR / 32;                    // 32-row score tiles per s-block
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 h_th2[j] = *(const bf16x2 *)(gTh + tk * strTh + k);
             }
         }
-        if constexpr (CF::PFC) load_crows(c0h, tq);
+        if constexpr (CF::PFC && CF::YO) load_crows(c0h, tq);
     };
 
     // ---- s-block stream: block j of the sequence lives in register set j % 2
@@ -613,9 +617,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         __syncthreads();
 
         // ---- rotated C~ rows of this wave's t-blocks, from the prefetched (or just loaded) raw rows
-        if constexpr (!CF::PFC) load_crows(c0, tq);
         bf16x8 creg[TPW][NKK];
         f32x4 yacc[TPW][NPT];
+        if constexpr (CF::YO) {
+        if constexpr (!CF::PFC) load_crows(c0, tq);
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
             const int tau = (task_tb[u] * 16 + l16) / R;
@@ -670,6 +675,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                 for (int i = 0; i < 4; i++) yacc[u][pt][i] *= sc[i];
         }
+        }   // CF::YO
         {
             const float eS = exp2_neg(MISC[1]);
 #pragma unroll
@@ -768,7 +774,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             // masks, and the masks before the output MFMAs, so their dependent chains overlap.
             constexpr int UG = TPW < 2 ? TPW : 2;
 #pragma unroll
-            for (int ug = 0; ug < TPW; ug += UG)
+            for (int ug = 0; ug < (CF::YO ? TPW : 0); ug += UG)
 #pragma unroll
             for (int j = 0; j < CF::NSUB; j++) {
                 const int sbj = sb * CF::NSUB + j;              // 32-row tile of the chunk
@@ -941,7 +947,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             // skip term D x_t, off the MFMA chains: the stage still holds the chunk's X rows
             const bf16 *xs = (const bf16 *)(UR + CF::SB_X);
 #pragma unroll
-            for (int u = 0; u < TPW; u++)
+            for (int u = 0; u < (CF::YO ? TPW : 0); u++)
 #pragma unroll
                 for (int pt = 0; pt < NPT; pt++) {
                     const bf16x4 xv = ds_read_tr(xs + (task_tb[u] * 16 + 4 * q4 + l16 / 4) * PS + pt * 16 + 4 * (l16 % 4));
@@ -974,7 +980,8 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         }
 
         // ---- epilogue: outputs through a per-wave LDS transpose, 16-byte row stores
-        if constexpr (CF::EPI) {
+        if constexpr (!CF::YO) {
+        } else if constexpr (CF::EPI) {
             // fp32 transpose, then y * SiLU(z) in fp32 and one rounding to bf16
             constexpr int NPC = 16 * P / 8 / 64;   // 16-byte pieces per lane and t-block
             static_assert((16 * P / 8) % 64 == 0, "output pieces");
@@ -1123,10 +1130,16 @@ mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st) {
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
     // the EPI instantiations also carry the variants (per-token A, fixed lambda)
     const bool epi = a->bc_norm || a->B_bias || a->C_bias || a->z || a->A_tok || !a->lam;
-#define X(n, p, r, q, w, ut, sbr)                                                       \
-    if (N == n && P == p && R == r && Q == q)                                           \
-        return epi ? launch_cfg<Cfg<n, p, r, q, w, ut, sbr, true>>(a, st)               \
-                   : launch_cfg<Cfg<n, p, r, q, w, ut, sbr, false>>(a, st);
+    // y NULL: a state-only scan (the first pass of a segmented scan)
+    const bool yo = a->y != nullptr;
+#define X(n, p, r, q, w, ut, sbr)                                                                     \
+    if (N == n && P == p && R == r && Q == q) {                                                       \
+        if (!yo)                                                                                      \
+            return epi ? launch_cfg<Cfg<n, p, r, q, w, ut, sbr, true, false>>(a, st)                  \
+                       : launch_cfg<Cfg<n, p, r, q, w, ut, sbr, false, false>>(a, st);                \
+        return epi ? launch_cfg<Cfg<n, p, r, q, w, ut, sbr, true>>(a, st)                             \
+                   : launch_cfg<Cfg<n, p, r, q, w, ut, sbr, false>>(a, st);                           \
+    }
     M3_BF16_SHAPES(X)
 #undef X
     return MAMBA3_EUNSUPPORTED;

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
         }
         __syncthreads();
         // masked score matrix M[(t,i)][(s,j)]
-        for (int e = tid; e < QR * QR; e += nt) {
+        for (int e = tid; p.y && e < QR * QR; e += nt) {
             int r = e / QR, q = e % QR, tt = r / R, ss = q / R;
             float v = 0.f;
             if (ss <= tt && tt < nq) {
@@ -215,8 +215,8 @@ __global__ __launch_bounds__(256) void k_scan_f32(ValuParams p) {
             M[e] = v;
         }
         __syncthreads();
-        // outputs
-        for (int e = tid; e < QR * P; e += nt) {
+        // outputs (none in a state-only scan: y NULL)
+        for (int e = tid; p.y && e < QR * P; e += nt) {
             int r = e / P, pp = e % P, tt = r / R, i = r % R;
             if (tt >= nq) continue;
             float inter = 0.f;
