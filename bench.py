@@ -483,8 +483,8 @@ def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 3
     # epilogue variants (demangled or mangled names, as rocprofv3 prints them; workgroups of the
     # bench's launch: 8 x 64 (sequence, head) slabs, 256 x 64 decode rows, 257 x 64 with slots)
     dec = ("k_decode_colIDF16bLi64ELi4ELb0E", "k_decode_col<__bf16, 64, 4, false>")
-    kernels = {"scan_bf16": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, false>",), 512),
-               "scan_bf16_block": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, true>",), 512),
+    kernels = {"scan_bf16": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, false, true>",), 512),
+               "scan_bf16_block": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, true, true>",), 512),
                "decode": ("decode.hip", dec, 16384),
                "decode_slots": ("decode.hip", dec, 16448),
                "decode_block": ("decode.hip", ("k_decode_colIDF16bLi64ELi4ELb1E", "k_decode_col<__bf16, 64, 4, true>"),
