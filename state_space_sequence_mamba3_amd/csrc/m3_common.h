@@ -38,6 +38,11 @@ struct ScanPlan {
 mamba3_status launch_scan_f32(const mamba3_scan_args *a, hipStream_t st);
 mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st);
 bool scan_bf16_supported(int N, int P, int R, int Q);
+// State-only bf16 scan (a->y NULL) that may also write the state entering every chunk into
+// ws_state ([S * ceil(seqlen / chunk)][H][N][P] fp32, padded batches only): the backward's
+// chunk states. scan_bf16_states_supported covers the scan's shapes and the backward's chunks.
+bool scan_bf16_states_supported(int N, int P, int R, int Q);
+mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, float *ws_state, hipStream_t st);
 size_t scan_f32_lds_bytes(int N, int P, int R, int Q);
 mamba3_status launch_decode(const mamba3_decode_args *a, hipStream_t st);
 mamba3_status launch_scan_bwd(const mamba3_scan_bwd_args *b, hipStream_t st);

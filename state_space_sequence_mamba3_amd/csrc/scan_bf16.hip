@@ -161,6 +161,9 @@ struct BfParams {
     int32_t atok_on, lam_on;
     float lam_fixed;
     int32_t Gth;            // angle rows per token (divides H): head h reads row h / (H / Gth)
+    // state-only scans: the state entering every chunk, [S * chunks][H][N][P] fp32 (the
+    // backward's chunk-state layout), or NULL
+    float *ws_state;
 };
 
 template <int N_, int P_, int R_, int Q_, int NW_, int UT_, int SBR_, bool EPI_, bool YO_ = true>
@@ -187,7 +190,8 @@ struct Cfg {
     static constexpr int KW = K / NW, KP = KW / 2, TG = 64 / KP, TPL = Q / TG;
     static_assert(K % NW == 0 && KW % 2 == 0 && 64 % KP == 0 && Q % TG == 0, "angle prefix split");
     static_assert(N % 32 == 0 && P % 32 == 0 && (R == 1 || R == 2 || R == 4) && QR % 32 == 0, "shape");
-    static_assert(NTB % NW == 0 && (TPW == 1 || TPW % 2 == 0), "t-block split");
+    // t-blocks exist only with outputs (a state-only scan may have fewer 16-row blocks than waves)
+    static_assert(!YO || (NTB % NW == 0 && (TPW == 1 || TPW % 2 == 0)), "t-block split");
     static_assert(NUT % NW == 0 && (UT == 16 || UT == 32), "state tile split");
     static_assert(K % 8 == 0 && Q % NW == 0 && Q <= 128 && Q < NTHR, "prologue");
     static_assert(SBR % 32 == 0 && QR % SBR == 0, "s-block size");
@@ -229,6 +233,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int N = CF::N, P = CF::P, R = CF::R, Q = CF::Q, NW = CF::NW, K = CF::K, UT = CF::UT;
     constexpr int TOKT = CF::TOKT, TOKS = CF::TOKS, TOKS32 = CF::TOKS32, NTHR = CF::NTHR, TPW = CF::TPW;
     constexpr int NKK = CF::NKK, NPT = CF::NPT, UPW = CF::UPW, NS = CF::NS, PS = CF::PS, UR_ = CF::UR_;
+    constexpr int TPA = TPW > 0 ? TPW : 1;   // extent of per-t-block arrays (a state-only scan may have none)
     using UAcc = std::conditional_t<UT == 32, f32x16, f32x4>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     f16x2 *cstw = (f16x2 *)(smem + CF::OFF_PHI);
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     bf16 h_A = {};                  // its decay rate A_t (per-token variant)
     bf16 h_dtn = {}, h_lamn = {};   // the token after the chunk (same for every thread)
     bf16x2 h_th2[CF::TPL];          // theta of the lane's angle pair for its TPL tokens
-    bf16x8 h_c[TPW][NKK];
+    bf16x8 h_c[TPA][NKK];
     // C rows of the own t-blocks in operand layout: row 16 tb + l16, columns 32 kk + 8 q4 ..
     // tq: the thread index the address math uses (tid, or an opaque copy inside the chunk loop)
     auto load_crows = [&](int64_t c0h, int tq) {
@@ -484,7 +489,19 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         // every chunk (for the other plain shapes hoisting it is faster)
         const int tq = opaque<CF::EPI || (CF::N == 128 && CF::R == 4)>(tid);
         const int64_t tok0 = start + c0;
-        int task_tb[TPW];
+        if constexpr (!CF::YO) {
+            // the state entering the chunk, with the previous-token term of its first token
+            // (folded into the previous chunk's last weight, or added from Bprev for chunk 0)
+            if (pr.ws_state) {
+                float *wsc = pr.ws_state + ((s * (((int64_t)pr.seqlen + Q - 1) / Q) + c0 / Q) * H + h) * (int64_t)N * P;
+#pragma unroll
+                for (int v = 0; v < UPW; v++)
+#pragma unroll
+                    for (int r = 0; r < UR_; r++)
+                        wsc[(int64_t)(ut_n0[v] + urow(r)) * P + ut_p0[v] + ucol] = hreg[v][r];
+            }
+        }
+        int task_tb[TPA];
 #pragma unroll
         for (int u = 0; u < TPW; u++) task_tb[u] = tb_of(u, c0);
 
@@ -617,8 +634,8 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         __syncthreads();
 
         // ---- rotated C~ rows of this wave's t-blocks, from the prefetched (or just loaded) raw rows
-        bf16x8 creg[TPW][NKK];
-        f32x4 yacc[TPW][NPT];
+        bf16x8 creg[TPA][NKK];
+        f32x4 yacc[TPA][NPT];
         if constexpr (CF::YO) {
         if constexpr (!CF::PFC) load_crows(c0, tq);
 #pragma unroll
@@ -692,7 +709,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         unsigned l16c = l16, q4c = q4;
         if constexpr (CF::NSB <= 8) asm volatile("" : "+v"(l16c), "+v"(q4c));   // fully unrolled sweeps
         const bool fastmask = __builtin_amdgcn_readfirstlane(__float_as_int(MISC[2])) != 0;
-        float S2t[TPW];
+        float S2t[TPA];
 #pragma unroll
         for (int u = 0; u < TPW; u++) S2t[u] = S2[(task_tb[u] * 16 + l16) / R];
         const int nbs = FULL ? CF::NSB : (nq + TOKS - 1) / TOKS;   // s-blocks holding valid tokens
@@ -772,7 +789,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             // Per 32-row tile, t-blocks in groups of (up to) two: the group's t-blocks that reach
             // the tile share its B~ and X operands; the score MFMAs of both are issued before their
             // masks, and the masks before the output MFMAs, so their dependent chains overlap.
-            constexpr int UG = TPW < 2 ? TPW : 2;
+            constexpr int UG = TPW < 2 ? TPA : 2;
 #pragma unroll
             for (int ug = 0; ug < (CF::YO ? TPW : 0); ug += UG)
 #pragma unroll
@@ -1085,8 +1102,9 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 template <class CF>
-mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st) {
+mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st, float *ws_state = nullptr) {
     BfParams p;
+    p.ws_state = ws_state;
     p.x = (const bf16 *)a->x; p.dt = (const bf16 *)a->dt; p.lam = (const bf16 *)a->lam;
     p.theta = (const bf16 *)a->theta; p.B = (const bf16 *)a->B; p.C = (const bf16 *)a->C;
     p.Bprev = (const bf16 *)a->Bprev; p.xprev = (const bf16 *)a->xprev;
@@ -1119,6 +1137,11 @@ mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st) {
     X(128, 64, 2, 64, 8, 32, 128)  \
     X(128, 64, 4, 64, 8, 32, 64)
 
+// state-only shapes at the backward's chunks (N, P, R, Q) -> waves, state tile, rows per s-block
+#define M3_BF16_STATE_SHAPES(X)    \
+    X(128, 64, 1, 32, 4, 32, 32)   \
+    X(64, 64, 4, 16, 4, 16, 64)
+
 bool scan_bf16_supported(int N, int P, int R, int Q) {
 #define X(n, p, r, q, w, ut, sbr) if (N == n && P == p && R == r && Q == q) return true;
     M3_BF16_SHAPES(X)
@@ -1126,20 +1149,41 @@ bool scan_bf16_supported(int N, int P, int R, int Q) {
     return false;
 }
 
+bool scan_bf16_states_supported(int N, int P, int R, int Q) {
+#define X(n, p, r, q, w, ut, sbr) if (N == n && P == p && R == r && Q == q) return true;
+    M3_BF16_SHAPES(X)
+    M3_BF16_STATE_SHAPES(X)
+#undef X
+    return false;
+}
+
+mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, float *ws_state, hipStream_t st) {
+    if (a->y) return MAMBA3_EINVAL;
+    if (ws_state && a->cu_seqlens) return MAMBA3_EUNSUPPORTED;
+    const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
+    // the EPI instantiations also carry the variants (per-token A, fixed lambda); the gate and
+    // the C bias act on outputs only
+    const bool epi = a->bc_norm || a->B_bias || a->A_tok || !a->lam;
+#define X(n, p, r, q, w, ut, sbr)                                                        \
+    if (N == n && P == p && R == r && Q == q)                                            \
+        return epi ? launch_cfg<Cfg<n, p, r, q, w, ut, sbr, true, false>>(a, st, ws_state) \
+                   : launch_cfg<Cfg<n, p, r, q, w, ut, sbr, false, false>>(a, st, ws_state);
+    M3_BF16_SHAPES(X)
+    M3_BF16_STATE_SHAPES(X)
+#undef X
+    return MAMBA3_EUNSUPPORTED;
+}
+
 mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st) {
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
+    // y NULL: a state-only scan (the first pass of a segmented scan)
+    if (!a->y) return launch_scan_bf16_states(a, nullptr, st);
     // the EPI instantiations also carry the variants (per-token A, fixed lambda)
     const bool epi = a->bc_norm || a->B_bias || a->C_bias || a->z || a->A_tok || !a->lam;
-    // y NULL: a state-only scan (the first pass of a segmented scan)
-    const bool yo = a->y != nullptr;
-#define X(n, p, r, q, w, ut, sbr)                                                                     \
-    if (N == n && P == p && R == r && Q == q) {                                                       \
-        if (!yo)                                                                                      \
-            return epi ? launch_cfg<Cfg<n, p, r, q, w, ut, sbr, true, false>>(a, st)                  \
-                       : launch_cfg<Cfg<n, p, r, q, w, ut, sbr, false, false>>(a, st);                \
-        return epi ? launch_cfg<Cfg<n, p, r, q, w, ut, sbr, true>>(a, st)                             \
-                   : launch_cfg<Cfg<n, p, r, q, w, ut, sbr, false>>(a, st);                           \
-    }
+#define X(n, p, r, q, w, ut, sbr)                                                       \
+    if (N == n && P == p && R == r && Q == q)                                           \
+        return epi ? launch_cfg<Cfg<n, p, r, q, w, ut, sbr, true>>(a, st)               \
+                   : launch_cfg<Cfg<n, p, r, q, w, ut, sbr, false>>(a, st);
     M3_BF16_SHAPES(X)
 #undef X
     return MAMBA3_EUNSUPPORTED;

@@ -56,6 +56,7 @@ struct BwdParams {
     void *dA_tok;             // its gradient
     float lam_fixed;          // trapezoid weight of every token when lam is NULL
     int32_t Gth;              // angle rows per token (divides H): head h reads row h / (H / Gth)
+    int32_t fwd_states;       // MFMA kernel: the chunk states are already in ws_state (no forward walk)
     float *p_dth;             // [T][H][K] per-head dtheta partials (Gth < H), else NULL
 };
 
@@ -1167,6 +1168,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     };
 
     // ------------------------------------------------------------ forward: chunk states
+    if (!p.fwd_states) {
     f32x4 hacc[UPW];
 #pragma unroll
     for (int v = 0; v < UPW; v++)
@@ -1214,6 +1216,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             }
         }
         __syncthreads();
+    }
     }
 
     // ------------------------------------------------------------ reverse
@@ -1874,6 +1877,7 @@ static mamba3_status launch_bwd_t(const mamba3_scan_bwd_args *b, hipStream_t st)
     const BwdWs w = bwd_ws(b, Q);
     char *ws = (char *)b->workspace;
     BwdParams p;
+    p.fwd_states = 0;
     p.x = a->x; p.dt = a->dt; p.lam = a->lam; p.theta = a->theta; p.B = a->B; p.C = a->C;
     p.Bprev = a->Bprev; p.xprev = a->xprev; p.z = a->z; p.dy = b->dy;
     p.A = a->A; p.D = a->D; p.h_in = a->h_in; p.dh_out = b->dh_out; p.Bb = a->B_bias; p.Cb = a->C_bias;
@@ -1899,6 +1903,23 @@ static mamba3_status launch_bwd_t(const mamba3_scan_bwd_args *b, hipStream_t st)
     const int64_t nblk = S * p.H;
     if constexpr (std::is_same<T, bf16>::value) {
         if (mfma) {
+            // padded batches at a chunk the forward kernel covers: the chunk states come from a
+            // state-only forward scan, and the backward kernel skips its own forward walk
+            p.fwd_states = 0;
+            if (!a->cu_seqlens && T_tok > 0 && scan_bf16_states_supported(p.N, p.P, p.R, Q)) {
+                mamba3_scan_args f = *a;
+                f.y = nullptr;
+                f.h_out = nullptr;
+                f.z = nullptr;
+                f.C_bias = nullptr;
+                f.D = nullptr;
+                f.chunk = Q;
+                f.workspace = nullptr;
+                f.workspace_bytes = 0;
+                const mamba3_status fs = launch_scan_bf16_states(&f, p.ws_state, st);
+                if (fs != MAMBA3_OK) return fs;
+                p.fwd_states = 1;
+            }
             const mamba3_status ms = launch_bwd_mfma(p, nblk, st);
             if (ms != MAMBA3_OK) return ms;
         }
