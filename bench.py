@@ -491,7 +491,9 @@ def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 3
                                 16384),
                "decode_siso": ("decode.hip", ("k_decode_colIDF16bLi128ELi1ELb0E", "k_decode_col<__bf16, 128, 1, false>"),
                                16384),
-               "scan_bwd": ("scan_bwd.hip", ("BCfg<128, 64, 1, 32, 8>",), 512)}
+               "scan_bwd": ("scan_bwd.hip", ("BCfg<128, 64, 1, 32, 8>",), 512),
+               # the backward's chunk states: the state-only forward scan at chunk 32
+               "scan_bwd_states": ("scan_bf16.hip", ("Cfg<128, 64, 1, 32, 4, 32, 32, false, false>",), 512)}
     md = ["# HBM traffic per launch from rocprofv3 counters", "", "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):",
           "", "```", *commands, "```", "",
           f"Calibration: a plain 1 GiB device copy reads {sum(copy_f) / len(copy_f) / 2**30:.4f} GiB by FETCH_SIZE and writes "
@@ -651,7 +653,10 @@ def main():
                      "frac": r["hbm_gbs"] / HBM_PEAK_GBS, "tflops": r["alu_tfs"], "tflops_peak": cpeak})
             roof.update(bytes_per_launch=r["bytes"], flops_per_launch=r["flops"], chunk=r["chunk"])
             if k == "siso_bwd":
-                roof["traffic"] = traffic_record("scan_bwd")
+                # the whole backward: the state-only forward scan that writes the chunk states,
+                # then the backward kernel
+                tb, ts = traffic_record("scan_bwd"), traffic_record("scan_bwd_states")
+                roof["traffic"] = tb + ts if tb is not None and ts is not None else None
             sec[k] = {"workload": r["workload"], "ms": r["ms"], "tokens_per_s": r["tokens_per_s"],
                       "workspace_bytes": r["workspace_bytes"], "roofline": roof}
     for k in ("decode", "decode_block", "decode_siso", "decode_slots"):
