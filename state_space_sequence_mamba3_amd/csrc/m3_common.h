@@ -38,18 +38,21 @@ struct ScanPlan {
 mamba3_status launch_scan_f32(const mamba3_scan_args *a, hipStream_t st);
 mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st);
 bool scan_bf16_supported(int N, int P, int R, int Q);
-// State-only bf16 scan (a->y NULL) that may also write the state entering every chunk into
-// ws_state ([S * ceil(seqlen / chunk)][H][N][P] fp32, padded batches only): the backward's
-// chunk states. scan_bf16_states_supported covers the scan's shapes and the backward's chunks.
+// State-only bf16 scan (a->y NULL) that may also write, for padded batches only, the state
+// entering every chunk into ws_state ([S * ceil(seqlen / chunk)][H][N][P] fp32: the backward's
+// chunk states) and each row's decay and angle sums into seg_sums (the first K + 1 floats of
+// each [S][H][N][P] block: the segment sums of state passing). scan_bf16_states_supported
+// covers the scan's shapes and the backward's chunks.
 bool scan_bf16_states_supported(int N, int P, int R, int Q);
-mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, float *ws_state, hipStream_t st);
+mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, float *ws_state, float *seg_sums, hipStream_t st);
 size_t scan_f32_lds_bytes(int N, int P, int R, int Q);
 mamba3_status launch_decode(const mamba3_decode_args *a, hipStream_t st);
 mamba3_status launch_scan_bwd(const mamba3_scan_bwd_args *b, hipStream_t st);
 size_t scan_bwd_workspace_bytes(const mamba3_scan_bwd_args *b);
 int scan_bwd_chunk(int N, int P, int R);
 bool decode_supported(int N, int P, int R, int dtype);
-mamba3_status launch_state_passing(const mamba3_state_passing_args *a, hipStream_t st);
+// sums_staged: the segment sums are already in seg_h_in (written by the state-only scan)
+mamba3_status launch_state_passing(const mamba3_state_passing_args *a, hipStream_t st, bool sums_staged = false);
 size_t state_passing_lds_bytes(int N, int P, int R);
 
 }  // namespace m3

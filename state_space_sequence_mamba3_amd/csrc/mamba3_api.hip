@@ -374,8 +374,17 @@ mamba3_status mamba3_scan_segmented(const mamba3_scan_segmented_args *a, void *s
     mamba3_scan_args p1, p2;
     mamba3_state_passing_args sp;
     seg_calls(a, &p1, &sp, &p2);
-    if ((st = scan_run(&p1, stream, false)) != MAMBA3_OK) return st;
-    if ((st = mamba3_state_passing(&sp, stream)) != MAMBA3_OK) return st;
+    // bf16: the state-only first pass also stages the segment sums that state passing reads
+    const bool staged = p1.dtype == MAMBA3_BF16;
+    if (staged) {
+        if ((st = scan_validate_impl(&p1, false)) != MAMBA3_OK) return st;
+        if ((st = m3::launch_scan_bf16_states(&p1, nullptr, sp.seg_h_in, (hipStream_t)stream)) != MAMBA3_OK)
+            return st;
+    } else if ((st = scan_run(&p1, stream, false)) != MAMBA3_OK) {
+        return st;
+    }
+    if ((st = mamba3_state_passing_validate(&sp)) != MAMBA3_OK) return st;
+    if ((st = m3::launch_state_passing(&sp, (hipStream_t)stream, staged)) != MAMBA3_OK) return st;
     return mamba3_scan_fwd(&p2, stream);
 }
 

@@ -164,6 +164,10 @@ struct BfParams {
     // state-only scans: the state entering every chunk, [S * chunks][H][N][P] fp32 (the
     // backward's chunk-state layout), or NULL
     float *ws_state;
+    // state-only scans of padded rows: sum_t dt_t A_t and sum_t dt_t theta_t[k] over each row,
+    // written to the first K + 1 floats of its [S][H][N][P] block (the segment sums that state
+    // passing reads), or NULL
+    float *seg_sums;
 };
 
 template <int N_, int P_, int R_, int Q_, int NW_, int UT_, int SBR_, bool EPI_, bool YO_ = true>
@@ -477,6 +481,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     __syncthreads();
 
+    // state-only scans: running sums over the chunks of the log2 decay (thread 0) and of the
+    // angles of the lane's pair (lanes of the last token group)
+    float sum_s2 = 0.f, sum_ph0 = 0.f, sum_ph1 = 0.f;
+
     // One chunk. Full chunks (Q tokens) have a compile-time number of s-blocks
     // (NSB, even), so block j of the sequence always sits in register set j % 2
     // and the sweep is fully unrolled; the final partial chunk runs the same
@@ -625,6 +633,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 __sincosf(x1, &s1, &c1v);
                 *(f16x4 *)(cstw + tau * K + k) = f16x4{(_Float16)c0v, (_Float16)s0, (_Float16)c1v, (_Float16)s1};
                 if (tau == Q - 1) {   // angles past the end are zero: Phi[Q-1] = Phi[nq-1]
+                    if constexpr (!CF::YO) {
+                        sum_ph0 += x0;
+                        sum_ph1 += x1;
+                    }
                     sincosf(x0, &s0, &c0v);
                     sincosf(x1, &s1, &c1v);
                     *(f32x4 *)(PHC + k) = f32x4{c0v, s0, c1v, s1};
@@ -632,6 +644,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
         __syncthreads();
+
+        if constexpr (!CF::YO) {
+            if (tid == 0) sum_s2 += MISC[1];
+        }
 
         // ---- rotated C~ rows of this wave's t-blocks, from the prefetched (or just loaded) raw rows
         bf16x8 creg[TPA][NKK];
@@ -1089,6 +1105,17 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     int64_t c0 = 0;
     for (; c0 + Q <= len; c0 += Q) chunk_body(std::true_type{}, c0);
     if (c0 < len) chunk_body(std::false_type{}, c0);
+    if constexpr (!CF::YO) {
+        if (pr.seg_sums) {
+            float *o = pr.seg_sums + ((int64_t)s * H + h) * (int64_t)N * P;
+            if (tid == 0) o[0] = sum_s2 / kLog2e;
+            if (lane / CF::KP == CF::TG - 1) {   // the lanes holding the chunks' last token
+                const int k = wave * CF::KW + 2 * (lane % CF::KP);
+                o[1 + k] = sum_ph0;
+                o[2 + k] = sum_ph1;
+            }
+        }
+    }
 
     if (pr.h_out) {
         const int64_t so = ((int64_t)s * H + h) * N * P;
@@ -1102,9 +1129,11 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 template <class CF>
-mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st, float *ws_state = nullptr) {
+mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st, float *ws_state = nullptr,
+                         float *seg_sums = nullptr) {
     BfParams p;
     p.ws_state = ws_state;
+    p.seg_sums = seg_sums;
     p.x = (const bf16 *)a->x; p.dt = (const bf16 *)a->dt; p.lam = (const bf16 *)a->lam;
     p.theta = (const bf16 *)a->theta; p.B = (const bf16 *)a->B; p.C = (const bf16 *)a->C;
     p.Bprev = (const bf16 *)a->Bprev; p.xprev = (const bf16 *)a->xprev;
@@ -1157,17 +1186,17 @@ bool scan_bf16_states_supported(int N, int P, int R, int Q) {
     return false;
 }
 
-mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, float *ws_state, hipStream_t st) {
+mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, float *ws_state, float *seg_sums, hipStream_t st) {
     if (a->y) return MAMBA3_EINVAL;
-    if (ws_state && a->cu_seqlens) return MAMBA3_EUNSUPPORTED;
+    if ((ws_state || seg_sums) && a->cu_seqlens) return MAMBA3_EUNSUPPORTED;
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
     // the EPI instantiations also carry the variants (per-token A, fixed lambda); the gate and
     // the C bias act on outputs only
     const bool epi = a->bc_norm || a->B_bias || a->A_tok || !a->lam;
 #define X(n, p, r, q, w, ut, sbr)                                                        \
     if (N == n && P == p && R == r && Q == q)                                            \
-        return epi ? launch_cfg<Cfg<n, p, r, q, w, ut, sbr, true, false>>(a, st, ws_state) \
-                   : launch_cfg<Cfg<n, p, r, q, w, ut, sbr, false, false>>(a, st, ws_state);
+        return epi ? launch_cfg<Cfg<n, p, r, q, w, ut, sbr, true, false>>(a, st, ws_state, seg_sums) \
+                   : launch_cfg<Cfg<n, p, r, q, w, ut, sbr, false, false>>(a, st, ws_state, seg_sums);
     M3_BF16_SHAPES(X)
     M3_BF16_STATE_SHAPES(X)
 #undef X
@@ -1177,7 +1206,7 @@ mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, float *ws_state
 mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st) {
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
     // y NULL: a state-only scan (the first pass of a segmented scan)
-    if (!a->y) return launch_scan_bf16_states(a, nullptr, st);
+    if (!a->y) return launch_scan_bf16_states(a, nullptr, nullptr, st);
     // the EPI instantiations also carry the variants (per-token A, fixed lambda)
     const bool epi = a->bc_norm || a->B_bias || a->C_bias || a->z || a->A_tok || !a->lam;
 #define X(n, p, r, q, w, ut, sbr)                                                       \

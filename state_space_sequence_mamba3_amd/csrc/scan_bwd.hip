@@ -1916,7 +1916,7 @@ static mamba3_status launch_bwd_t(const mamba3_scan_bwd_args *b, hipStream_t st)
                 f.chunk = Q;
                 f.workspace = nullptr;
                 f.workspace_bytes = 0;
-                const mamba3_status fs = launch_scan_bf16_states(&f, p.ws_state, st);
+                const mamba3_status fs = launch_scan_bf16_states(&f, p.ws_state, nullptr, st);
                 if (fs != MAMBA3_OK) return fs;
                 p.fwd_states = 1;
             }

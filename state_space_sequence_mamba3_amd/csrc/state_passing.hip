@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kSPThreads) void k_state_passing(SPParams p) {
         for (int64_t e = tid; e < NP; e += NT) p.h_out[((int64_t)s * H + h) * NP + e] = Hs[e];
 }
 
-mamba3_status launch_state_passing(const mamba3_state_passing_args *a, hipStream_t st) {
+mamba3_status launch_state_passing(const mamba3_state_passing_args *a, hipStream_t st, bool sums_staged) {
     const mamba3_scan_args *f = &a->fwd;
     SPParams p;
     p.x = f->x; p.dt = f->dt; p.lam = f->lam; p.theta = f->theta; p.B = f->B;
@@ -264,10 +264,10 @@ mamba3_status launch_state_passing(const mamba3_state_passing_args *a, hipStream
     };
     bool ok;
     if (f->dtype == MAMBA3_BF16) {
-        hipLaunchKernelGGL(k_segment_sums<bf16>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
+        if (!sums_staged) hipLaunchKernelGGL(k_segment_sums<bf16>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
         ok = pref ? chain(k_state_passing<bf16, 1>) : chain(k_state_passing<bf16, 0>);
     } else {
-        hipLaunchKernelGGL(k_segment_sums<float>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
+        if (!sums_staged) hipLaunchKernelGGL(k_segment_sums<float>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
         ok = pref ? chain(k_state_passing<float, 1>) : chain(k_state_passing<float, 0>);
     }
     if (!ok) return MAMBA3_EHIP;
