@@ -142,6 +142,40 @@ def test_bwd_deterministic():
         assert a[k].tobytes() == b[k].tobytes(), k
 
 
+def test_bwd_deterministic_bf16_state_pass():
+    """The bf16 MFMA backward of a padded SISO batch, whose chunk states come from the state-only
+    forward scan: bitwise equal gradients on two runs."""
+    cfg = dict(synth.CONFIGS[1], batch=2, seqlen=150, nheads=4)
+    inp = synth.resume_inputs(synth.scan_inputs(cfg, seed=121), seed=122)
+    gr = synth.grad_inputs(inp, seed=123)
+    note("bwd determinism, bf16 with the state pass")
+    a, b = run_bwd(inp, gr), run_bwd(inp, gr)
+    for k in a:
+        assert a[k].tobytes() == b[k].tobytes(), k
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_bwd_state_sources_agree(cfg):
+    """Chunk states from the state-only forward scan (a padded batch) and from the backward
+    kernel's own forward walk (the same two sequences as a packed batch) give the same gradients
+    up to rounding: within 2^-6 of the other path's largest magnitude, two bf16 steps (the paths
+    round the chunk states' bf16 operands differently, and most gradients are stored in bf16).
+    A misplaced or missing chunk state moves them by far more."""
+    c = dict(synth.CONFIGS[cfg], batch=2, seqlen=150, nheads=4)
+    inp = synth.scan_inputs(c, seed=126 + cfg)
+    gr = synth.grad_inputs(inp, seed=128 + cfg)
+    tok = ("x", "dt", "lam", "theta", "B", "C")
+    pk = {k: (v.reshape((1, 300) + v.shape[2:]) if k in tok else v) for k, v in inp.items()}
+    pk["cu_seqlens"] = np.array([0, 150, 300], dtype=np.int32)
+    gpk = dict(gr, dy=gr["dy"].reshape((1, 300) + gr["dy"].shape[2:]))
+    note(f"bwd state sources, config {cfg}: padded (state pass) against packed (forward walk)")
+    a, b = run_bwd(inp, gr), run_bwd(pk, gpk)
+    for k in a:
+        x, y = a[k].reshape(-1).astype(np.float64), b[k].reshape(-1).astype(np.float64)
+        scale = max(np.abs(y).max(), 1e-30)
+        assert np.abs(x - y).max() / scale < 2.0 ** -6, k
+
+
 @pytest.mark.parametrize("cfg", [1, 2])
 def test_bwd_full_size_sampled_heads(oracle, cfg):
     """The bf16 backward at the full layer workload (8 x 4096 tokens, 64 heads) in the bench's launch
