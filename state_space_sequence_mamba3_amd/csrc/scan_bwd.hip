@@ -1,9 +1,11 @@
 // Backward of the chunked scan: gradients of every input given dL/dy and
 // dL/dh_out (VALU, fp32 arithmetic, token inputs fp32 or bf16).
 //
-// One workgroup owns one (sequence, head) slab. It first walks the chunks
-// forward and stores the state entering each chunk in the workspace, then
-// walks them in reverse. Per chunk (tokens 0..e, chunk-local log decay S_t,
+// One workgroup owns one (sequence, head) slab. The state entering each chunk
+// is first stored in the workspace: by a state-only forward scan (the bf16
+// forward kernel without outputs, at this kernel's chunk) for padded bf16
+// batches of the shapes it covers, otherwise by a forward walk of this kernel.
+// The slab's chunks are then walked in reverse. Per chunk (tokens 0..e, chunk-local log decay S_t,
 // cumulative angle Phi_t, B~ = R(-Phi) B, C~ = R(-Phi) C, carried state H'
 // entering the chunk, physical frame) the forward is
 //   y_t  = e^{S_t} C~_t^T H' + sum_{s<=t} e^{S_t-S_s} w(t,s) (C~_t . B~_s) X_s + D X_t
