@@ -1,19 +1,25 @@
 #!/usr/bin/env python3
 """Bench of the Mamba-3 SSM recurrence on one MI355X.
 
-Headline: prefill throughput (tokens/s) of the bf16 chunked scan on the SISO
-layer workload (batch 8 x 4096 tokens, 64 heads, head dim 64, state 128,
-rank 1, chunk 64). One step = one whole scan of that batch (every step of the
-hot path: chunk-local prefixes and rotations, score and output MFMAs, state
-update, outputs). Inputs are synthetic (seeded, device-generated) and resident
-in HBM before timing starts. The same JSON line also carries the decode step
-(batch 256, 64 heads, N=64, R=4, fp32 state updated in place, 1000
-consecutive steps over a ring of 64 token-input sets) and the MIMO and packed
-MIMO scans as secondary figures, each with its roofline, the SISO, MIMO
-and decode workloads again with the fused block prologue / epilogue (B/C RMS
-norm, per-head B/C biases, SiLU(z) output gate), the backward of the SISO and
-MIMO scans, the SISO decode shape (N=128, R=1) and the decode step with
-slot-indexed states (continuous batching).
+Headline: prefill throughput (tokens/s) of the bf16 chunked MIMO scan on the
+packed long-context workload: 8 variable-length sequences totalling 65536
+tokens (state reset at each start), 64 heads, head dim 64, state 128, rank 4,
+chunk 128. One step = one whole scan of that batch (every step of the hot
+path: chunk-local prefixes and rotations, score and output MFMAs, the rank-4
+state update, the state pass across chunks, outputs). Inputs are synthetic
+(seeded, device-generated) and resident in HBM before timing starts. Its
+cpu_baseline is the fp64 oracle on whole slabs drawn like that workload.
+
+The same JSON line carries, under ``secondary``, each with its roofline and
+(where it is a forward scan or decode) the oracle timed on the host beside
+it: the SISO and MIMO layer scans (8 x 4096 tokens), the tiny fp32 scan, the
+MIMO and packed scans with B, C shared by all heads, the fused block
+prologue / epilogue (B/C RMS norm, per-head B/C biases, SiLU(z) gate), the
+backward of the SISO and MIMO scans, the decode step (batch 256, 64 heads,
+N=64, R=4, fp32 state updated in place, 1000 consecutive steps over a ring
+of 64 token-input sets), the SISO decode shape (N=128, R=1), decode with
+slot-indexed states (continuous batching) and one long sequence scanned
+plain and in segments.
 
 Timing: HIP events recorded on the stream the kernels are launched on (torch's
 current stream, which the binding passes to the library), W untimed warmup
@@ -43,7 +49,7 @@ def scan_bytes(c, block=False):
     G = c.get("ngroups", H)
     T = b * L
     S = c.get("nseq", b) if c.get("packed") else b
-    es = 2
+    es = 2 if c.get("dtype", "bf16") == "bf16" else 4
     tok = T * (H * P * R * es * (3 if block else 2)   # x, y (, z)
                + H * es * 2                          # dt, lam
                + H * (N // 2) * es                   # theta
@@ -129,6 +135,19 @@ def timed(fn, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps, wall
 
 
+def m3_config(cfg, **over):
+    from state_space_sequence_mamba3_amd import synth
+    return dict(synth.CONFIGS[cfg], **over)
+
+
+def scan_kernel_name(c):
+    """The forward kernel that runs a scan of these shapes (mirrors the library's dispatch)."""
+    N, P, R, Q = c["dstate"], c["headdim"], c["rank"], c["chunk"]
+    if c.get("dtype") != "bf16":
+        return f"k_scan_f32<N={N},P={P},R={R},Q={Q}>"
+    return f"k_scan_bf16<N={N},P={P},R={R},Q={Q}>"
+
+
 def bench_scan(cfg, steps, warmup, dev, block=False, **over):
     import torch
     import state_space_sequence_mamba3_amd as m3
@@ -154,7 +173,8 @@ def bench_scan(cfg, steps, warmup, dev, block=False, **over):
     nbytes, flops = scan_bytes(c, block), scan_flops(c)
     name = c["name"] + (f" (B, C shared: G={c['ngroups']})" if "ngroups" in over else "")
     name += " + BC norm, BC biases, SiLU gate" if block else ""
-    out = dict(workload=name, ms=ms, tokens_per_s=tokens / (ms * 1e-3), bytes=nbytes, flops=flops,
+    out = dict(workload=name, kernel=scan_kernel_name(c), ms=ms, tokens_per_s=tokens / (ms * 1e-3), bytes=nbytes,
+               flops=flops,
                hbm_gbs=nbytes / (ms * 1e-3) / 1e9, mfma_tfs=flops / (ms * 1e-3) / 1e12, wall_s=wall)
     del d, y, h
     torch.cuda.empty_cache()
@@ -352,39 +372,91 @@ def bench_decode(steps_per_rep, reps, dev, block=False, siso=False, slots=False)
                 bytes_per_step=nbytes, hbm_gbs=nbytes / (us * 1e-6) / 1e9, wall_s=wall)
 
 
-def cpu_baseline(target_s=12.0):
-    """The fp64 oracle (O1, C + OpenMP over (sequence, head) slabs) on whole
-    slabs of the headline workload (4096 tokens, N=128, P=64, R=1); its
-    throughput is scaled to the whole batch (8 sequences x 64 heads)."""
+_HOST_THREADS = None
+
+
+def host_threads():
+    """The oracle's OpenMP thread count, read once before any one-thread run (a run on fewer
+    threads changes what the OpenMP runtime reports afterwards)."""
+    global _HOST_THREADS
+    if _HOST_THREADS is None:
+        from oracle import oracle as o
+        _HOST_THREADS = o.max_threads()
+    return _HOST_THREADS
+
+
+def oracle_rate(cfg, threads, target_s, seqlen, nslab):
+    """Throughput of the fp64 oracle (O1, C + OpenMP over (sequence, head) slabs) in
+    token-heads/s: whole slabs drawn like config cfg (one sequence of seqlen tokens, nslab
+    heads), scanned repeatedly for about target_s seconds on `threads` threads. The oracle's
+    cost is linear in tokens, so the rate does not depend on the slab length."""
     from oracle import oracle as o
     from state_space_sequence_mamba3_amd import synth
-    import numpy as np
-    c = synth.CONFIGS[1]
-    threads = o.max_threads()
-    total_slabs = c["batch"] * c["nheads"]
-    nslab = min(total_slabs, 2 * threads)
-    inp = synth.scan_inputs(1, seed=500, batch=1, nheads=nslab)
+    inp = synth.scan_inputs(cfg, seed=500 + cfg, batch=1, seqlen=seqlen, nheads=nslab, packed=False)
     inp = {k: v for k, v in inp.items() if k != "meta"}
     done, spent = 0, 0.0
-    while spent < target_s and done < 8 * total_slabs:
+    while spent < target_s:
         t0 = time.perf_counter()
         o.scan(inp, form=1, nthreads=threads)
         spent += time.perf_counter() - t0
-        done += nslab
-    tokens = c["batch"] * c["seqlen"]
-    whole_job_s = spent * total_slabs / done
-    # the same oracle on one thread, on a few slabs
-    one = {k: (v[:, :, :2] if k in ("x", "dt", "lam", "theta", "B", "C") else (v[:2] if k in ("A", "D") else v))
-           for k, v in inp.items()}
-    t0 = time.perf_counter()
-    o.scan(one, form=1, nthreads=1)
-    one_s = (time.perf_counter() - t0) * total_slabs / 2
-    return dict(value=tokens / whole_job_s, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{done} (sequence, head) slabs of the 8x4096 SISO workload ({nslab} distinct, "
-                       f"4096 tokens each; the batch has {total_slabs}) in {spent:.1f} s; rate scaled to the "
-                       f"whole batch",
-                single_thread_value=tokens / one_s,
-                single_thread_sample="2 slabs on 1 thread, rate scaled to the whole batch")
+        done += nslab * seqlen
+    return done / spent, f"{done // seqlen} slabs of {seqlen} tokens ({nslab} distinct) in {spent:.1f} s"
+
+
+def cpu_baseline(cfg, target_s=10.0, seqlen=8192):
+    """The oracle on a bounded sample of config cfg's slabs, on every host thread and on one
+    thread; rates in tokens/s of the whole job (token-heads/s divided by the heads)."""
+    from oracle import oracle as o
+    from state_space_sequence_mamba3_amd import synth
+    c = synth.CONFIGS[cfg]
+    threads = host_threads()
+    rate, sample = oracle_rate(cfg, threads, target_s, seqlen, threads)
+    rate1, sample1 = oracle_rate(cfg, 1, max(1.0, target_s / 4), min(seqlen, 1024), 1)
+    H = c["nheads"]
+    return dict(value=rate / H, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{sample}, drawn like '{c['name']}'; token-heads/s divided by its {H} heads",
+                single_thread_value=rate1 / H, single_thread_sample=sample1)
+
+
+def cpu_baseline_tiny(target_s=1.0):
+    """The oracle on the whole tiny fp32 workload (1 x 256 tokens, 4 heads), repeated."""
+    from oracle import oracle as o
+    from state_space_sequence_mamba3_amd import synth
+    c = synth.CONFIGS[0]
+    threads = host_threads()
+    inp = {k: v for k, v in synth.scan_inputs(0).items() if k != "meta"}
+    n, spent = 0, 0.0
+    while spent < target_s:
+        t0 = time.perf_counter()
+        o.scan(inp, form=1, nthreads=threads)
+        spent += time.perf_counter() - t0
+        n += 1
+    return dict(value=n * c["batch"] * c["seqlen"] / spent, unit="tokens/s", ms_per_step=spent / n * 1e3,
+                cores=threads, kind="oracle", sample=f"the whole workload {n} times in {spent:.1f} s")
+
+
+def cpu_baseline_decode(target_s=4.0, rows=16):
+    """The oracle's decode step on `rows` batch rows of the decode workload (all 64 heads),
+    stepped repeatedly; the time per step is scaled to the batch of 256."""
+    import numpy as np
+    from oracle import oracle as o
+    from state_space_sequence_mamba3_amd import synth
+    c = synth.CONFIGS[3]
+    threads = host_threads()
+    inp = synth.decode_inputs(3, seed=503, batch=rows, ring=1)
+    tok = {k: inp[k][0] for k in ("x", "dt", "lam", "theta", "B", "C")}
+    tok.update(A=inp["A"], D=inp["D"], Bprev=inp["Bprev"], xprev=inp["xprev"])
+    h = inp["h"].astype(np.float64)
+    n, spent = 0, 0.0
+    while spent < target_s:
+        t0 = time.perf_counter()
+        _, h = o.decode(tok, h, nthreads=threads)
+        spent += time.perf_counter() - t0
+        n += 1
+    us = spent / n * 1e6 * c["batch"] / rows
+    return dict(value=us, unit="us/step", cores=threads, kind="oracle",
+                sample=f"{n} steps of {rows} batch rows x {c['nheads']} heads in {spent:.1f} s; "
+                       f"time scaled to the batch of {c['batch']}")
 
 
 def traffic_record(kernel):
@@ -484,6 +556,8 @@ def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 3
     # bench's launch: 8 x 64 (sequence, head) slabs, 256 x 64 decode rows, 257 x 64 with slots)
     dec = ("k_decode_colIDF16bLi64ELi4ELb0E", "k_decode_col<__bf16, 64, 4, false>")
     kernels = {"scan_bf16": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, false, true>",), 512),
+               "scan_bf16_mimo": ("scan_bf16.hip", ("Cfg<64, 64, 4, 64, 8, 16, 256, false, true>",), 512),
+               "scan_bf16_packed": ("scan_bf16.hip", ("Cfg<128, 64, 4, 128, 8, 16, 32, false, true>",), 512),
                "scan_bf16_block": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, true, true>",), 512),
                "decode": ("decode.hip", dec, 16384),
                "decode_slots": ("decode.hip", dec, 16448),
@@ -514,9 +588,96 @@ def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 3
                "copy_scale_fetch": kf, "copy_scale_write": kw, "workgroups": wg}
         json.dump(rec, open(os.path.join(out_dir, f"traffic_{key}.json"), "w"), indent=1)
         md.append(f"| `{_short(name)}` | {wg} | {len(fs)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} |")
-    out_md = os.path.join(out_dir, "traffic_scan_bf16_siso_8x4096_and_decode_b256.md")
+    out_md = os.path.join(out_dir, "traffic_scan_bf16_and_decode_bench_workloads.md")
     open(out_md, "w").write("\n".join(md) + "\n")
     print(f"wrote {out_md}")
+
+
+MFMA_KERNELS = {"scan_bf16_packed": ("scan_bf16.hip", ("Cfg<128, 64, 4, 128, 8, 16, 32, false, true>",), 512),
+                "scan_bf16_mimo": ("scan_bf16.hip", ("Cfg<64, 64, 4, 64, 8, 16, 256, false, true>",), 512),
+                "scan_bf16": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, false, true>",), 512)}
+CU_COUNT = 256
+XCD_COUNT = 8
+SIMDS_PER_CU = 4
+
+
+def summarize_mfma(pmc_dir, out_dir, command):
+    """Turns one rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16 and
+    GRBM_GUI_ACTIVE into per-launch MFMA records of the scan kernels: the MFMA busy share of the
+    CUs' active cycles (busy cycles / (GUI-active cycles x CUs), rocprof's MFMA utilisation) and the
+    bf16 MFMA work the counters saw (MOPS x 512 flops). Writes mfma_<kernel>.json records (read by
+    the bench while the kernel source is unchanged) and a text summary. On MI355X GRBM_GUI_ACTIVE
+    sums the 8 XCDs (a per-XCD share divided by the 2.4 GHz clock gives the kernel's duration), and
+    the MFMA busy cycles sum over the 1024 SIMDs (they equal the counted flops over the 1024 bf16
+    flops a SIMD retires per cycle), so the busy share is busy / (GUI / 8 x 1024)."""
+    import hashlib
+    from collections import defaultdict
+    agg, names = defaultdict(lambda: defaultdict(float)), {}
+    for r in _csv_rows(os.path.join(pmc_dir, "run_counter_collection.csv")):
+        agg[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[r["Dispatch_Id"]] = (r["Kernel_Name"], int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
+    md = ["# MFMA counters per launch from rocprofv3", "", "Command (run from /tmp with TMPDIR=/tmp; R = repository root):",
+          "", "```", command, "```", "",
+          f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCD_COUNT} XCDs x {CU_COUNT * SIMDS_PER_CU} SIMDs): "
+          "GRBM_GUI_ACTIVE sums the XCDs and the busy cycles sum the SIMDs. Counted bf16 work = "
+          "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops (it includes the masked halves of diagonal tiles).", "",
+          "| kernel | workgroups | dispatches | MFMA busy cycles | GUI active cycles | MFMA busy | counted bf16 GFLOP |",
+          "|---|---|---|---|---|---|---|"]
+    for key, (src, pats, wg) in MFMA_KERNELS.items():
+        ds = [d for d, nw in names.items() if nw[1] == wg and any(p in nw[0] for p in pats)]
+        if not ds:
+            continue
+        mean = lambda c: sum(agg[d][c] for d in ds) / len(ds)
+        busy, gui, mops = mean("SQ_VALU_MFMA_BUSY_CYCLES"), mean("GRBM_GUI_ACTIVE"), mean("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        srcp = os.path.join(ROOT, "state_space_sequence_mamba3_amd", "csrc", src)
+        rec = {"kernel": _short(names[ds[0]][0]), "source": src,
+               "source_sha256": hashlib.sha256(open(srcp, "rb").read()).hexdigest(), "dispatches": len(ds),
+               "workgroups": wg, "mfma_busy_cycles": busy, "gui_active_cycles": gui, "mops_bf16": mops,
+               "simds": CU_COUNT * SIMDS_PER_CU, "xcds": XCD_COUNT,
+               "busy_frac": busy / (gui / XCD_COUNT * CU_COUNT * SIMDS_PER_CU) if gui else None,
+               "counter_flops": mops * 512}
+        json.dump(rec, open(os.path.join(out_dir, f"mfma_{key}.json"), "w"), indent=1)
+        md.append(f"| `{rec['kernel']}` | {wg} | {len(ds)} | {busy:.4g} | {gui:.4g} | "
+                  f"{rec['busy_frac'] if rec['busy_frac'] is not None else float('nan'):.3f} | {mops * 512 / 1e9:.1f} |")
+    out_md = os.path.join(out_dir, "mfma_scan_bf16_bench_workloads.md")
+    open(out_md, "w").write("\n".join(md) + "\n")
+    print(f"wrote {out_md}")
+
+
+def counter_record(key):
+    """MFMA counters per launch from a committed rocprofv3 --pmc record (SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE), if taken on the current kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"mfma_{key}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "state_space_sequence_mamba3_amd", "csrc", rec.get("source", ""))
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec
+
+
+def scan_roofline(r, traffic_key=None, counter_key=None):
+    """Roofline entry of a scan line: the binding roofline (whichever of HBM bytes and MFMA flops
+    needs more time at peak), with the other figure beside it, and the counter records."""
+    mfma_bound = r["flops"] / (MFMA_BF16_PEAK_TFS * 1e12) > r["bytes"] / (HBM_PEAK_GBS * 1e9)
+    roof = ({"bound": "mfma", "achieved": r["mfma_tfs"], "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+             "frac": r["mfma_tfs"] / MFMA_BF16_PEAK_TFS, "hbm_gbs": r["hbm_gbs"],
+             "hbm_frac": r["hbm_gbs"] / HBM_PEAK_GBS} if mfma_bound else
+            {"bound": "hbm", "achieved": r["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": r["hbm_gbs"] / HBM_PEAK_GBS, "mfma_tflops": r["mfma_tfs"],
+             "mfma_frac": r["mfma_tfs"] / MFMA_BF16_PEAK_TFS})
+    roof["traffic"] = traffic_record(traffic_key) if traffic_key else None
+    roof.update(bytes_per_launch=r["bytes"], flops_per_launch=r["flops"], launch_ms=r["ms"])
+    cr = counter_record(counter_key) if counter_key else None
+    if cr:
+        # counter figures beside the algorithmic ones: MFMA busy share of the CUs' active cycles,
+        # and the bf16 MFMA work the counters saw (it includes masked tiles and padding)
+        roof["mfma_busy_counter"] = cr["busy_frac"]
+        roof["mfma_counter_tflops"] = cr["counter_flops"] / (r["ms"] * 1e-3) / 1e12
+        roof["mfma_counter_frac"] = roof["mfma_counter_tflops"] / MFMA_BF16_PEAK_TFS
+    return roof
 
 
 def main():
@@ -528,10 +689,14 @@ def main():
         # bench.py --summarize-traffic FETCH_DIR WRITE_DIR OUT_DIR COMMAND...
         summarize_traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
         return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-mfma":
+        # bench.py --summarize-mfma PMC_DIR OUT_DIR COMMAND
+        summarize_mfma(sys.argv[2], sys.argv[3], sys.argv[4])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["scan", "decode", "bwd", "long", "all"], default="all")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -557,24 +722,30 @@ def main():
         print(json.dumps({"copy_calibration_bytes_each_way": src.numel() * 4, "launches": 3}), flush=True)
         del src, dst
 
+    K, W = args.steps, args.warmup
     res = {}
     if args.only in ("scan", "all"):
-        res["siso"] = bench_scan(1, args.steps, args.warmup, dev)
+        res["packed"] = bench_scan(4, K, W, dev)
+        print(f"# packed MIMO scan {res['packed']['ms']:.3f} ms", file=sys.stderr, flush=True)
+    # the layer workloads take a fraction of a millisecond: more launches for a stable figure
+    KL, WL = max(K, 50), max(W, 20)
+    if args.only in ("scan", "all"):
+        res["siso"] = bench_scan(1, KL, WL, dev)
         print(f"# siso scan {res['siso']['ms']:.3f} ms", file=sys.stderr, flush=True)
-    if args.only == "all":
-        res["mimo"] = bench_scan(2, args.steps, args.warmup, dev)
+        res["mimo"] = bench_scan(2, KL, WL, dev)
         print(f"# mimo scan {res['mimo']['ms']:.3f} ms", file=sys.stderr, flush=True)
-        res["packed"] = bench_scan(4, max(2, args.steps // 2), max(1, args.warmup // 2), dev)
-        print(f"# packed scan {res['packed']['ms']:.3f} ms", file=sys.stderr, flush=True)
+        res["tiny"] = bench_scan(0, KL, WL, dev)
+        print(f"# tiny fp32 scan {res['tiny']['ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+    if args.only == "all":
         # B and C shared by all heads (one group), as the MIMO layer can be configured
-        res["mimo_g1"] = bench_scan(2, args.steps, args.warmup, dev, ngroups=1)
+        res["mimo_g1"] = bench_scan(2, KL, WL, dev, ngroups=1)
         print(f"# mimo scan G=1 {res['mimo_g1']['ms']:.3f} ms", file=sys.stderr, flush=True)
-        res["packed_g1"] = bench_scan(4, max(2, args.steps // 2), max(1, args.warmup // 2), dev, ngroups=1)
+        res["packed_g1"] = bench_scan(4, K, W, dev, ngroups=1)
         print(f"# packed scan G=1 {res['packed_g1']['ms']:.3f} ms", file=sys.stderr, flush=True)
         # the fused block prologue / epilogue on
-        res["siso_block"] = bench_scan(1, args.steps, args.warmup, dev, block=True)
+        res["siso_block"] = bench_scan(1, KL, WL, dev, block=True)
         print(f"# siso scan + block {res['siso_block']['ms']:.3f} ms", file=sys.stderr, flush=True)
-        res["mimo_block"] = bench_scan(2, args.steps, args.warmup, dev, block=True)
+        res["mimo_block"] = bench_scan(2, KL, WL, dev, block=True)
         print(f"# mimo scan + block {res['mimo_block']['ms']:.3f} ms", file=sys.stderr, flush=True)
     if args.only in ("bwd", "all"):
         # the backward: a few steps, each is a whole backward of the batch
@@ -595,51 +766,52 @@ def main():
         print(f"# decode with slots {res['decode_slots']['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
 
     if args.only in ("long", "all"):
-        res["long"] = bench_long(max(3, args.steps // 5), max(1, args.warmup // 5), dev)
+        res["long"] = bench_long(max(3, K // 4), max(1, W // 4), dev)
         print(f"# long sequence: plain {res['long']['plain']['ms']:.3f} ms, segmented "
               f"{res['long']['segmented']['ms']:.3f} ms", file=sys.stderr, flush=True)
 
     peaks = measured_peaks(dev) if args.only == "all" else None
 
-    cpu = None
-    if not args.no_cpu_baseline and args.only in ("scan", "all"):
-        cpu = cpu_baseline()
+    # the oracle on the host, beside each forward workload (a baseline, not a target)
+    cpu = {}
+    if not args.no_cpu_baseline:
+        if "packed" in res:
+            cpu["packed"] = cpu_baseline(4)
+        if "siso" in res:
+            cpu["siso"] = cpu_baseline(1, target_s=5.0, seqlen=4096)
+        if "mimo" in res:
+            cpu["mimo"] = cpu_baseline(2, target_s=5.0, seqlen=4096)
+        if "tiny" in res:
+            cpu["tiny"] = cpu_baseline_tiny()
+        if "decode" in res:
+            cpu["decode"] = cpu_baseline_decode()
+        print("# oracle timed", file=sys.stderr, flush=True)
 
-    if "siso" in res:
-        s = res["siso"]
-        tr = traffic_record("scan_bf16")
+    if "packed" in res:
+        r = res["packed"]
+        c = m3_config(4)
         line = {
             "metric": METRIC,
-            "value": s["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": s["ms"], "higher_is_better": True, "scaling": "weak",
+            "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": K,
+            "warmup": W, "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, device-generated)",
-            "config": {"workload": s["workload"], "batch": 8, "seqlen": 4096, "nheads": 64, "headdim": 64,
-                       "dstate": 128, "rank": 1, "chunk": 64, "parallelism": "single GPU"},
-            "roofline": {"bound": "hbm", "achieved": s["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": s["hbm_gbs"] / HBM_PEAK_GBS, "traffic": tr,
-                         "kernel": "k_scan_bf16<N=128,P=64,R=1,Q=64>", "bytes_per_launch": s["bytes"],
-                         "launch_ms": s["ms"], "mfma_tflops": s["mfma_tfs"],
-                         "mfma_frac": s["mfma_tfs"] / MFMA_BF16_PEAK_TFS},
-            "cpu_baseline": cpu,
+            "config": {"workload": r["workload"], "batch": 1, "seqlen": c["seqlen"], "nseq": c["nseq"],
+                       "nheads": c["nheads"], "headdim": c["headdim"], "dstate": c["dstate"], "rank": c["rank"],
+                       "ngroups": c["nheads"], "chunk": c["chunk"], "parallelism": "single GPU"},
+            "roofline": dict(scan_roofline(r, "scan_bf16_packed", "scan_bf16_packed"), kernel=r["kernel"]),
+            "cpu_baseline": cpu.get("packed"),
         }
     else:
         line = {"metric": METRIC, "value": None}
     sec = {}
-    for k in ("mimo", "packed", "mimo_g1", "packed_g1", "siso_block", "mimo_block"):
+    for k, tk in (("siso", "scan_bf16"), ("mimo", "scan_bf16_mimo"), ("tiny", None), ("mimo_g1", None),
+                  ("packed_g1", None), ("siso_block", "scan_bf16_block"), ("mimo_block", None)):
         if k in res:
             r = res[k]
-            # the binding roofline: whichever of HBM bytes and MFMA flops needs more time at peak
-            mfma_bound = r["flops"] / (MFMA_BF16_PEAK_TFS * 1e12) > r["bytes"] / (HBM_PEAK_GBS * 1e9)
-            roof = ({"bound": "mfma", "achieved": r["mfma_tfs"], "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": r["mfma_tfs"] / MFMA_BF16_PEAK_TFS, "hbm_gbs": r["hbm_gbs"],
-                     "hbm_frac": r["hbm_gbs"] / HBM_PEAK_GBS} if mfma_bound else
-                    {"bound": "hbm", "achieved": r["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": r["hbm_gbs"] / HBM_PEAK_GBS, "mfma_tflops": r["mfma_tfs"],
-                     "mfma_frac": r["mfma_tfs"] / MFMA_BF16_PEAK_TFS})
-            roof.update(bytes_per_launch=r["bytes"], flops_per_launch=r["flops"])
-            if k == "siso_block":
-                roof["traffic"] = traffic_record("scan_bf16_block")
-            sec[k] = {"workload": r["workload"], "ms": r["ms"], "tokens_per_s": r["tokens_per_s"], "roofline": roof}
+            sec[k] = {"workload": r["workload"], "ms": r["ms"], "tokens_per_s": r["tokens_per_s"],
+                      "kernel": r["kernel"], "roofline": scan_roofline(r, tk, tk)}
+            if k in cpu:
+                sec[k]["oracle"] = cpu[k]
     for k in ("siso_bwd", "mimo_bwd"):
         if k in res:
             r = res[k]
@@ -668,6 +840,8 @@ def main():
                                    "unit": "GB/s", "frac": r["hbm_gbs"] / HBM_PEAK_GBS,
                                    "bytes_per_launch": r["bytes_per_step"],
                                    "traffic": traffic_record(k)}}
+            if k in cpu:
+                sec[k]["oracle"] = cpu[k]
     if "long" in res:
         sec["long_sequence"] = res["long"]
     line["secondary"] = sec
