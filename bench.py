@@ -145,6 +145,8 @@ def scan_kernel_name(c):
     N, P, R, Q = c["dstate"], c["headdim"], c["rank"], c["chunk"]
     if c.get("dtype") != "bf16":
         return f"k_scan_f32<N={N},P={P},R={R},Q={Q}>"
+    if (N, P, R, Q) == (128, 64, 4, 128) and not c.get("block"):
+        return f"k_scan_mimo<N={N},P={P},R={R},Q={Q}>"
     return f"k_scan_bf16<N={N},P={P},R={R},Q={Q}>"
 
 
@@ -173,7 +175,7 @@ def bench_scan(cfg, steps, warmup, dev, block=False, **over):
     nbytes, flops = scan_bytes(c, block), scan_flops(c)
     name = c["name"] + (f" (B, C shared: G={c['ngroups']})" if "ngroups" in over else "")
     name += " + BC norm, BC biases, SiLU gate" if block else ""
-    out = dict(workload=name, kernel=scan_kernel_name(c), ms=ms, tokens_per_s=tokens / (ms * 1e-3), bytes=nbytes,
+    out = dict(workload=name, kernel=scan_kernel_name(dict(c, block=block)), ms=ms, tokens_per_s=tokens / (ms * 1e-3), bytes=nbytes,
                flops=flops,
                hbm_gbs=nbytes / (ms * 1e-3) / 1e9, mfma_tfs=flops / (ms * 1e-3) / 1e12, wall_s=wall)
     del d, y, h
@@ -557,7 +559,7 @@ def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 3
     dec = ("k_decode_colIDF16bLi64ELi4ELb0E", "k_decode_col<__bf16, 64, 4, false>")
     kernels = {"scan_bf16": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, false, true>",), 512),
                "scan_bf16_mimo": ("scan_bf16.hip", ("Cfg<64, 64, 4, 64, 8, 16, 256, false, true>",), 512),
-               "scan_bf16_packed": ("scan_bf16.hip", ("Cfg<128, 64, 4, 128, 8, 16, 32, false, true>",), 512),
+               "scan_bf16_packed": ("scan_mimo.hip", ("MCfg<128, 64, 4, 128>",), 512),
                "scan_bf16_block": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, true, true>",), 512),
                "decode": ("decode.hip", dec, 16384),
                "decode_slots": ("decode.hip", dec, 16448),
@@ -593,7 +595,7 @@ def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 3
     print(f"wrote {out_md}")
 
 
-MFMA_KERNELS = {"scan_bf16_packed": ("scan_bf16.hip", ("Cfg<128, 64, 4, 128, 8, 16, 32, false, true>",), 512),
+MFMA_KERNELS = {"scan_bf16_packed": ("scan_mimo.hip", ("MCfg<128, 64, 4, 128>",), 512),
                 "scan_bf16_mimo": ("scan_bf16.hip", ("Cfg<64, 64, 4, 64, 8, 16, 256, false, true>",), 512),
                 "scan_bf16": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, false, true>",), 512)}
 CU_COUNT = 256

@@ -38,6 +38,9 @@ struct ScanPlan {
 mamba3_status launch_scan_f32(const mamba3_scan_args *a, hipStream_t st);
 mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st);
 bool scan_bf16_supported(int N, int P, int R, int Q);
+// The panel kernel of the rank-4 shapes (plain path: no fused prologue / epilogue, no variants).
+bool scan_mimo_supported(const mamba3_scan_args *a);
+mamba3_status launch_scan_mimo(const mamba3_scan_args *a, hipStream_t st);
 // State-only bf16 scan (a->y NULL) that may also write, for padded batches only, the state
 // entering every chunk into ws_state ([S * ceil(seqlen / chunk)][H][N][P] fp32: the backward's
 // chunk states) and each row's decay and angle sums into seg_sums (the first K + 1 floats of

@@ -53,80 +53,12 @@
 // decay rate A_t (loaded with dt) and a fixed trapezoid weight.
 #include <type_traits>
 
-#include "m3_common.h"
+#include "mfma_ops.h"
 
 namespace m3 {
 
 namespace {
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// LDS transpose read (16-bit elements): within each group of 16 lanes, lane i
-// receives element i % 4 of the 4 elements read by lanes i/4 + 4k, k = 0..3.
-// With lane i of the group pointing at &M[r0 + i/4][c0 + 4*(i%4)] of a
-// row-major bf16 matrix M, lane i receives M[r0 + k][c0 + i] for k = 0..3.
-__device__ __forceinline__ bf16x4 ds_read_tr(const bf16 *p) {
-    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
-    return __builtin_bit_cast(bf16x4, v);
-}
-// 8 K-values (rows r0 .. r0+3 and r1 .. r1+3) of column c0 + (lane % 16) of a
-// row-major [rows][ld] bf16 matrix, as an MFMA operand.
-__device__ __forceinline__ bf16x8 tr_operand(const bf16 *m, int ld, int r0, int r1, int c0, int l16) {
-    const bf16x4 a = ds_read_tr(m + (r0 + l16 / 4) * ld + c0 + 4 * (l16 % 4));
-    const bf16x4 b = ds_read_tr(m + (r1 + l16 / 4) * ld + c0 + 4 * (l16 % 4));
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// The value, made opaque to the compiler when ON: address math derived from it is then
-// recomputed where it is used instead of being hoisted out of the chunk loop (and spilled).
-template <bool ON>
-__device__ __forceinline__ int opaque(int v) {
-    if constexpr (ON) asm volatile("" : "+v"(v));
-    return v;
-}
-
-// Wait for this wave's outstanding LDS operations (wave-private staging).
-__device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xc07f); }
-
-__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        float o = __shfl_up(v, off, 64);
-        if (lane >= off) v += o;
-    }
-    return v;
-}
-
-// 2^x for x <= 0 (hardware exp2; results below the fp32 normal range flush to 0)
-__device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Rotate the 4 pairs of an 8-element row piece by -Phi: (u, v) -> (c u + s v, -s u + c v),
-// with (cos, sin) of the 4 pairs packed as fp16 in cs.
-__device__ __forceinline__ void rot_piece_f(const float (&in)[8], const f16x8 cs, float (&o)[8]) {
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-        const float c = (float)cs[2 * m], sn = (float)cs[2 * m + 1];
-        const float u = in[2 * m], v = in[2 * m + 1];
-        o[2 * m] = c * u + sn * v;
-        o[2 * m + 1] = c * v - sn * u;
-    }
-}
-__device__ __forceinline__ void rot_piece(const bf16x8 raw, const f16x8 cs, float (&o)[8]) {
-    float in[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) in[e] = (float)raw[e];
-    rot_piece_f(in, cs, o);
-}
 // Prologue of one 8-element piece of a B or C column: scale by inv (the column's inverse RMS,
 // or 1) and add the bias slice b (8 fp32 values in LDS).
 __device__ __forceinline__ void prologue_piece(const bf16x8 raw, float inv, const float *b, float (&o)[8]) {
@@ -139,9 +71,6 @@ __device__ __forceinline__ float sumsq8(const bf16x8 v) {
 #pragma unroll
     for (int e = 0; e < 8; e++) ss += (float)v[e] * (float)v[e];
     return ss;
-}
-__device__ __forceinline__ bf16x8 pack8(const float (&o)[8]) {
-    return bf16x8{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3], (bf16)o[4], (bf16)o[5], (bf16)o[6], (bf16)o[7]};
 }
 
 struct BfParams {
@@ -1207,6 +1136,8 @@ mamba3_status launch_scan_bf16(const mamba3_scan_args *a, hipStream_t st) {
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
     // y NULL: a state-only scan (the first pass of a segmented scan)
     if (!a->y) return launch_scan_bf16_states(a, nullptr, nullptr, st);
+    // the rank-4 shapes of the plain path run in panels
+    if (scan_mimo_supported(a)) return launch_scan_mimo(a, st);
     // the EPI instantiations also carry the variants (per-token A, fixed lambda)
     const bool epi = a->bc_norm || a->B_bias || a->C_bias || a->z || a->A_tok || !a->lam;
 #define X(n, p, r, q, w, ut, sbr)                                                       \

@@ -140,12 +140,12 @@ def test_variants(oracle, cfg, variant):
     assert ey < TOL_BF16 and eh < TOL_BF16
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [1, 2, 4])
 def test_strong_decay(oracle, cfg):
     """Heads whose decay over a chunk spans from a few to hundreds of binary orders of
     magnitude: chunks beyond the factored mask's range take the per-element form, chunks
     near the threshold switch between the two."""
-    inp = synth.scan_inputs(cfg, seed=41, batch=2, seqlen=400, nheads=4)
+    inp = synth.scan_inputs(cfg, seed=41, batch=2, seqlen=400, nheads=4, packed=False)
     inp["A"] = np.array([-0.5, -9.0, -10.0, -40.0], dtype=np.float32)
     inp = synth.resume_inputs(inp, seed=42)
     note(f"bf16 strong decay cfg{cfg}")
@@ -163,6 +163,61 @@ def test_grouped_bc_and_no_skip(oracle):
     y, h = run(upload(inp, device()), 64)
     yo, ho = oracle.scan({k: v for k, v in inp.items() if k not in ("meta", "D")})
     assert slab_relerr(from_dev(y), yo) < TOL_BF16 and state_relerr(from_dev(h), ho) < TOL_BF16
+
+
+# The panel kernel of the packed workload's shape (N = 128, R = 4, chunk 128): a chunk is two
+# 64-token panels; a last chunk may end inside panel 0 or panel 1.
+@pytest.mark.parametrize("seqlen", [300, 333, 64, 1])
+def test_panel_partial_chunks(oracle, seqlen):
+    inp = synth.resume_inputs(synth.scan_inputs(4, seed=70 + seqlen, batch=2, seqlen=seqlen, nheads=2,
+                                                packed=False), seed=71)
+    note(f"bf16 panel scan, last chunk of {seqlen % 128 or 128} tokens")
+    y, h = run(upload(inp, device()), 128)
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    ey, eh = slab_relerr(from_dev(y), yo), state_relerr(from_dev(h), ho)
+    note(f"  y relerr {ey:.2e}  h relerr {eh:.2e}")
+    assert ey < TOL_BF16 and eh < TOL_BF16
+
+
+def test_panel_grouped_no_skip(oracle):
+    inp = synth.scan_inputs(dict(synth.CONFIGS[4], ngroups=1), seed=72, batch=1, seqlen=390, nheads=4, packed=False)
+    inp["D"] = None
+    note("bf16 panel scan G=1, D=NULL")
+    y, h = run(upload(inp, device()), 128)
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k not in ("meta", "D")})
+    assert slab_relerr(from_dev(y), yo) < TOL_BF16 and state_relerr(from_dev(h), ho) < TOL_BF16
+
+
+def test_panel_weight_guard(oracle):
+    """A trapezoid weight lam > 1 can make gamma_s + delta_{s+1} vanish while gamma_s does not (dt
+    and lam chosen exactly representable: gamma_10 = 0.5 * 0.125, delta_11 = (1 - 2) * 0.0625); the
+    chunk holding that token takes the unscaled per-element form."""
+    inp = synth.scan_inputs(4, seed=73, batch=1, seqlen=256, nheads=2, packed=False)
+    dt = np.full(inp["dt"].shape, 0.125, dtype=np.float32)
+    lam = np.full(inp["lam"].shape, 0.5, dtype=np.float32)
+    dt[:, 11], lam[:, 11] = 0.0625, 2.0
+    dt[:, 140], lam[:, 140] = 0.0625, 2.0          # the same in the second chunk (panel 0 of chunk 1)
+    inp["dt"], inp["lam"] = synth.bf16_bits(dt), synth.bf16_bits(lam)
+    note("bf16 panel scan, vanishing trapezoid weight")
+    y, h = run(upload(inp, device()), 128)
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    ey, eh = slab_relerr(from_dev(y), yo), state_relerr(from_dev(h), ho)
+    note(f"  y relerr {ey:.2e}  h relerr {eh:.2e}")
+    assert ey < TOL_BF16 and eh < TOL_BF16
+
+
+def test_panel_chunk_invariance_and_determinism():
+    """Chunk 128 (the panel kernel) against chunk 64 (the general kernel) on the same inputs, and
+    two runs of the panel kernel bitwise equal."""
+    inp = synth.scan_inputs(4, seed=74, batch=1, seqlen=512, nheads=2, packed=False)
+    note("bf16 panel scan: chunk 128 vs 64, determinism")
+    d = upload(inp, device())
+    y128, h128 = run(d, 128)
+    y64, h64 = run(d, 64)
+    assert slab_relerr(from_dev(y128), from_dev(y64)) < TOL_BF16
+    assert state_relerr(from_dev(h128), from_dev(h64)) < 1e-2
+    y2, h2 = run(d, 128)
+    assert from_dev(y128).tobytes() == from_dev(y2).tobytes() and np.array_equal(from_dev(h128), from_dev(h2))
 
 
 def test_packed_ragged_with_empty(oracle):
