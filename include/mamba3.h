@@ -303,6 +303,30 @@ size_t mamba3_scan_segmented_workspace_size(const mamba3_scan_segmented_args *ar
 mamba3_status mamba3_scan_segmented_validate(const mamba3_scan_segmented_args *args);
 mamba3_status mamba3_scan_segmented(const mamba3_scan_segmented_args *args, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): mamba3_scan_segmented
+ * with a library-owned workspace, so the call allocates nothing (no hipMalloc,
+ * no hipFree, no allocating library routine). Same kernels and results as
+ * mamba3_scan_segmented.
+ *
+ * args       as for mamba3_scan_segmented, with workspace NULL and
+ *            workspace_bytes 0 (MAMBA3_EINVAL otherwise).
+ * stream     a stream of the current device (MAMBA3_EINVAL for another's).
+ * Workspace  a device array of MAMBA3_NOALLOC_SCRATCH_BYTES (64 MiB), 256-byte
+ *            aligned, held by every GPU the library runs on from the loading of
+ *            its code until the process ends. MAMBA3_EWORKSPACE when
+ *            mamba3_scan_segmented_workspace_size(args) exceeds it (about
+ *            batch * nseg * H * N * P * 8 bytes).
+ * Races      every call on one GPU uses that GPU's one array: calls that may run
+ *            at the same time on one GPU (different streams, or the same stream
+ *            from host threads without ordering) race and give wrong results.
+ *            Calls enqueued in order on one stream are safe: the array holds the
+ *            last call's contents and each call writes all it reads.
+ * Errors     as for mamba3_scan_segmented (nothing is enqueued on any error);
+ *            MAMBA3_EHIP also when the array's device address cannot be taken. */
+#define MAMBA3_NOALLOC_SCRATCH_BYTES (64u << 20)
+mamba3_status mamba3_scan_segmented_noalloc(const mamba3_scan_segmented_args *args, void *stream);
+
 /* One decode step for a batch of independent sequences, state updated in
  * place: h <- alpha R (h + delta Bprev xprev^T) + gamma B x^T, y = h^T C + D x
  * (the same update as one token of the scan; section "MIMO Formulation" gives

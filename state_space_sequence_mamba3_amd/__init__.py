@@ -74,8 +74,11 @@ class ScanSegmentedArgs(ctypes.Structure):
 EXPORTS = ("mamba3_scan_validate", "mamba3_scan_workspace_size", "mamba3_scan_fwd", "mamba3_scan_bwd_validate",
            "mamba3_scan_bwd_workspace_size", "mamba3_scan_bwd", "mamba3_state_passing_validate",
            "mamba3_state_passing", "mamba3_scan_segmented_workspace_size", "mamba3_scan_segmented_validate",
-           "mamba3_scan_segmented", "mamba3_decode_validate", "mamba3_decode_step", "mamba3_status_string",
-           "mamba3_version")
+           "mamba3_scan_segmented", "mamba3_scan_segmented_noalloc", "mamba3_decode_validate", "mamba3_decode_step",
+           "mamba3_status_string", "mamba3_version")
+
+# Size of the library-owned workspace of mamba3_scan_segmented_noalloc (bytes, per GPU).
+MAMBA3_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -115,6 +118,8 @@ def lib():
         l.mamba3_scan_segmented_validate.restype = ctypes.c_int
         l.mamba3_scan_segmented.argtypes = [ctypes.POINTER(ScanSegmentedArgs), _vp]
         l.mamba3_scan_segmented.restype = ctypes.c_int
+        l.mamba3_scan_segmented_noalloc.argtypes = [ctypes.POINTER(ScanSegmentedArgs), _vp]
+        l.mamba3_scan_segmented_noalloc.restype = ctypes.c_int
         l.mamba3_decode_validate.argtypes = [ctypes.POINTER(DecodeArgs)]
         l.mamba3_decode_validate.restype = ctypes.c_int
         l.mamba3_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
@@ -319,6 +324,27 @@ def mamba3_scan_segmented(x, dt, lam, theta, B, C, A, D=None, *, nseg, y=None, h
     st = lib().mamba3_scan_segmented(ctypes.byref(a), _stream(stream))
     if st != MAMBA3_OK:
         raise Mamba3Error(st, "mamba3_scan_segmented")
+    return y, h_out
+
+
+def mamba3_scan_segmented_noalloc(x, dt, lam, theta, B, C, A, D=None, *, nseg, y=None, h_in=None, h_out=None,
+                                  Bprev=None, xprev=None, chunk=64, want_state=True, stream=None, B_bias=None,
+                                  C_bias=None, z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5):
+    """mamba3_scan_segmented_noalloc: the segmented scan with the library's own workspace (the
+    library allocates nothing; y and h_out are allocated here by torch when not given, as by the
+    other entry points). Returns (y, h_out)."""
+    import torch
+    if y is None:
+        y = torch.empty_like(x)
+    if h_out is None and want_state:
+        h_out = torch.empty((x.shape[0], x.shape[2], B.shape[4], x.shape[4]), dtype=torch.float32, device=x.device)
+    fwd = scan_args(x, dt, lam, theta, B, C, A, D, y=y, h_in=h_in, h_out=h_out, Bprev=Bprev, xprev=xprev,
+                    chunk=chunk, B_bias=B_bias, C_bias=C_bias, z=z, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=A_tok,
+                    lam_fixed=lam_fixed)
+    a = ScanSegmentedArgs(fwd, int(nseg), None, 0)
+    st = lib().mamba3_scan_segmented_noalloc(ctypes.byref(a), _stream(stream))
+    if st != MAMBA3_OK:
+        raise Mamba3Error(st, "mamba3_scan_segmented_noalloc")
     return y, h_out
 
 

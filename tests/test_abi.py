@@ -380,3 +380,18 @@ def test_no_device_returns_ehip(lib):
     sg = good_seg()
     assert m3.mamba3_scan_segmented_validate(sg) == m3.MAMBA3_OK
     assert lib.mamba3_scan_segmented(ctypes.byref(sg), None) == m3.MAMBA3_EHIP
+    sg.workspace, sg.workspace_bytes = None, 0
+    assert lib.mamba3_scan_segmented_noalloc(ctypes.byref(sg), None) == m3.MAMBA3_EHIP
+
+
+def test_scan_segmented_noalloc_limits(lib):
+    """The allocation-free segmented scan refuses a caller workspace and a problem whose
+    workspace exceeds its array; both before any HIP call (so this runs without a device)."""
+    a = good_seg()
+    assert lib.mamba3_scan_segmented_noalloc(ctypes.byref(a), None) == m3.MAMBA3_EINVAL   # caller workspace
+    big = good_seg(workspace=None, workspace_bytes=0, nseg=64)
+    big.fwd.seqlen, big.fwd.nheads, big.fwd.ngroups, big.fwd.dstate, big.fwd.headdim = 64 * 16, 64, 64, 128, 64
+    need = lib.mamba3_scan_segmented_workspace_size(ctypes.byref(big))
+    assert need > m3.MAMBA3_NOALLOC_SCRATCH_BYTES
+    assert lib.mamba3_scan_segmented_noalloc(ctypes.byref(big), None) == m3.MAMBA3_EWORKSPACE
+    assert lib.mamba3_scan_segmented_noalloc(None, None) == m3.MAMBA3_EINVAL
