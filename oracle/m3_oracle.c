@@ -33,6 +33,15 @@
  *                       L = L1 L2 materialised (1-semiseparable decay times
  *                       the 2-band trapezoid matrix), section "Parallel
  *                       representation under SSD", Figure 1.
+ *   O3C m3o_scan_chunked : the same matrix form inside chunks of Q tokens,
+ *                       with the state carried from chunk to chunk (the
+ *                       parallel-within, recurrent-across-chunks reading of
+ *                       that section): per chunk, B and C are rotated by the
+ *                       chunk-local cumulative angle, L = L1 L2 is the
+ *                       chunk's own, the state entering the chunk (with the
+ *                       previous token's term folded in) decays into every
+ *                       output and into the chunk's final state, which is
+ *                       rotated back to the physical frame.
  *
  * Readings taken where the pages leave a step open:
  *   - State pair k is rows (2k, 2k+1) of the real state; the complex value is
@@ -426,6 +435,144 @@ static void o3_slab(const m3o_args *a, int s, int h, double *y_slab) {
     free(Bt); free(Ct); free(X); free(psi); free(tmp); free(row);
 }
 
+/* --------------------------------------------------------------- O3C ---- */
+/* Chunked SSD form for one slab, chunk size Q >= 1. In a chunk of tokens c0 .. e, with
+ * Phi_t = sum_{k=c0..t} dt_k theta_k (chunk-local, the frame before c0 being the physical one),
+ * B~_t = R(-Phi_t) B_t, C~_t = R(-Phi_t) C_t and the chunk's own L = L1 L2 (L1[t][s] = prod_{k=s+1..t}
+ * alpha_k, L2 = diag(gamma) + subdiag(beta), both over the chunk's tokens only), Proposition 4
+ * unrolls to
+ *   H_start = H_{c0-1} + delta_{c0} B_{c0-1} X_{c0-1}^T      (the previous token, if any)
+ *   y_t     = C~_t^T (prod_{k=c0..t} alpha_k) H_start + sum_{s=c0..t} L[t][s] (C~_t . B~_s) X_s + D X_t
+ *   H_e     = R(Phi_e) [ (prod_{k=c0..e} alpha_k) H_start + sum_{s=c0..e} L[e][s] B~_s X_s^T ]
+ * H is the real physical-frame state [N][P]; the gate applies to y as in the other forms. */
+static void o3c_slab(const m3o_args *a, int Q, int s, int h, double *y_slab, double *h_slab) {
+    const int H = a->H, G = a->G, P = a->P, N = a->N, R = a->R, K = N / 2;
+    const int g = h / (H / G);
+    const int dtp = a->in_dtype;
+    const int64_t t0 = a->seq_start[s], len = a->seq_len[s];
+    double *Hs = calloc((size_t)N * P, sizeof *Hs);                      /* state entering the chunk */
+    double *Bprev = calloc((size_t)N * R, sizeof *Bprev), *Xprev = calloc((size_t)P * R, sizeof *Xprev);
+    double *alpha = malloc((size_t)Q * sizeof *alpha), *beta = malloc((size_t)Q * sizeof *beta);
+    double *gamma = malloc((size_t)Q * sizeof *gamma), *delta = malloc((size_t)Q * sizeof *delta);
+    double *L1 = malloc((size_t)Q * Q * sizeof *L1), *L2 = malloc((size_t)Q * Q * sizeof *L2), *L = malloc((size_t)Q * Q * sizeof *L);
+    double *Braw = malloc((size_t)Q * N * R * sizeof *Braw), *Bt = malloc((size_t)Q * N * R * sizeof *Bt);
+    double *Ct = malloc((size_t)Q * N * R * sizeof *Ct), *X = malloc((size_t)Q * P * R * sizeof *X);
+    double *psi = malloc((size_t)K * sizeof *psi), *tmp = malloc((size_t)N * R * sizeof *tmp);
+    double *row = malloc((size_t)N * sizeof *row), *Hn = malloc((size_t)N * P * sizeof *Hn);
+    int has_prev = 0;
+    const double Dh = a->D ? a->D[h] : 0.0;
+
+    if (a->h_in) memcpy(Hs, a->h_in + ((int64_t)s * H + h) * N * P, (size_t)N * P * sizeof *Hs);
+    if (a->Bprev && a->xprev) {
+        has_prev = 1;
+        const int64_t ob = ((int64_t)s * G + g) * N * R, ox = ((int64_t)s * H + h) * P * R;
+        for (int j = 0; j < R; j++) {
+            bc_row(a, a->Bprev, ob + j * N, h, a->B_bias, row);
+            for (int n = 0; n < N; n++) Bprev[n * R + j] = row[n];
+        }
+        for (int p = 0; p < P; p++)
+            for (int j = 0; j < R; j++) Xprev[p * R + j] = ld(a->xprev, dtp, ox + j * P + p);
+    }
+    for (int64_t c0 = 0; c0 < len; c0 += Q) {
+        const int nq = (int)((len - c0 < Q) ? len - c0 : Q);
+        for (int k = 0; k < K; k++) psi[k] = 0.0;
+        for (int t = 0; t < nq; t++) {
+            const int64_t tg = t0 + c0 + t;
+            const double dt = ld(a->dt, dtp, tg * H + h), lam = lam_of(a, tg * H + h);
+            alpha[t] = exp(dt * A_of(a, tg * H + h, h));
+            delta[t] = (1.0 - lam) * dt;
+            beta[t] = delta[t] * alpha[t];
+            gamma[t] = lam * dt;
+            for (int k = 0; k < K; k++) psi[k] += dt * ld(a->theta, dtp, th_at(a, tg, h, k));
+            const int64_t ob = (tg * G + g) * N * R, ox = (tg * H + h) * P * R;
+            for (int j = 0; j < R; j++) {
+                bc_row(a, a->B, ob + j * N, h, a->B_bias, row);
+                for (int n = 0; n < N; n++) Braw[t * N * R + n * R + j] = row[n];
+            }
+            rot_vec(Bt + t * N * R, Braw + t * N * R, psi, K, R, -1);
+            for (int j = 0; j < R; j++) {
+                bc_row(a, a->C, ob + j * N, h, a->C_bias, row);
+                for (int n = 0; n < N; n++) tmp[n * R + j] = row[n];
+            }
+            rot_vec(Ct + t * N * R, tmp, psi, K, R, -1);
+            for (int p = 0; p < P; p++)
+                for (int j = 0; j < R; j++) X[t * P * R + p * R + j] = ld(a->x, dtp, ox + j * P + p);
+        }
+        /* the previous token's term folded into the state entering the chunk */
+        if (has_prev)
+            for (int n = 0; n < N; n++)
+                for (int p = 0; p < P; p++) {
+                    double acc = 0;
+                    for (int j = 0; j < R; j++) acc += Bprev[n * R + j] * Xprev[p * R + j];
+                    Hs[n * P + p] += delta[0] * acc;
+                }
+        /* the chunk's own L = L1 L2 */
+        for (int t = 0; t < nq; t++)
+            for (int u = 0; u < nq; u++) {
+                double prod = 0.0;
+                if (u <= t) {
+                    prod = 1.0;
+                    for (int k = u + 1; k <= t; k++) prod *= alpha[k];
+                }
+                L1[t * Q + u] = prod;
+                L2[t * Q + u] = (u == t) ? gamma[t] : ((u == t - 1) ? beta[t] : 0.0);
+            }
+        for (int t = 0; t < nq; t++)
+            for (int u = 0; u < nq; u++) {
+                double acc = 0;
+                for (int k = 0; k < nq; k++) acc += L1[t * Q + k] * L2[k * Q + u];
+                L[t * Q + u] = acc;
+            }
+        /* outputs */
+        for (int t = 0; t < nq; t++) {
+            double decay = 1.0;
+            for (int k = 0; k <= t; k++) decay *= alpha[k];
+            const int64_t tg = t0 + c0 + t;
+            for (int p = 0; p < P; p++)
+                for (int i = 0; i < R; i++) {
+                    double acc = 0;
+                    for (int n = 0; n < N; n++) acc += Ct[t * N * R + n * R + i] * decay * Hs[n * P + p];
+                    for (int u = 0; u <= t; u++) {
+                        if (L[t * Q + u] == 0.0) continue;
+                        for (int j = 0; j < R; j++) {
+                            double cb = 0;
+                            for (int n = 0; n < N; n++) cb += Ct[t * N * R + n * R + i] * Bt[u * N * R + n * R + j];
+                            acc += L[t * Q + u] * cb * X[u * P * R + p * R + j];
+                        }
+                    }
+                    y_slab[(c0 + t) * P * R + i * P + p] =
+                        gate(a, acc + Dh * X[t * P * R + p * R + i], (tg * H + h) * P * R + i * P + p);
+                }
+        }
+        /* the chunk's final state, rotated back to the physical frame */
+        const int e = nq - 1;
+        double decay = 1.0;
+        for (int k = 0; k <= e; k++) decay *= alpha[k];
+        for (int n = 0; n < N; n++)
+            for (int p = 0; p < P; p++) {
+                double acc = decay * Hs[n * P + p];
+                for (int u = 0; u <= e; u++)
+                    for (int j = 0; j < R; j++) acc += L[e * Q + u] * Bt[u * N * R + n * R + j] * X[u * P * R + p * R + j];
+                Hn[n * P + p] = acc;
+            }
+        for (int k = 0; k < K; k++) {
+            const double c = cos(psi[k]), sn = sin(psi[k]);
+            for (int p = 0; p < P; p++) {
+                const double u = Hn[(2 * k) * P + p], v = Hn[(2 * k + 1) * P + p];
+                Hs[(2 * k) * P + p] = c * u - sn * v;
+                Hs[(2 * k + 1) * P + p] = sn * u + c * v;
+            }
+        }
+        /* the chunk's last token is the next chunk's previous token (raw, physical frame) */
+        memcpy(Bprev, Braw + e * N * R, (size_t)N * R * sizeof *Bprev);
+        memcpy(Xprev, X + e * P * R, (size_t)P * R * sizeof *Xprev);
+        has_prev = 1;
+    }
+    if (h_slab) memcpy(h_slab, Hs, (size_t)N * P * sizeof *Hs);
+    free(Hs); free(Bprev); free(Xprev); free(alpha); free(beta); free(gamma); free(delta);
+    free(L1); free(L2); free(L); free(Braw); free(Bt); free(Ct); free(X); free(psi); free(tmp); free(row); free(Hn);
+}
+
 /* ---------------------------------------------------------------- OB ---- */
 /* Gradient of the layer (reverse mode), one (sequence, head) slab at a time.
  *
@@ -698,6 +845,31 @@ int m3o_scan(const m3o_args *a, int form, double *y, double *h_out, int nthreads
         double *ys = malloc((size_t)(len > 0 ? len : 1) * P * R * sizeof *ys);
         double *hs = h_out ? h_out + ((int64_t)s * H + h) * N * P : NULL;
         if (form == 1) o1_slab(a, s, h, ys, hs); else o2_slab(a, s, h, ys, hs);
+        for (int64_t tt = 0; tt < len; tt++)
+            memcpy(y + ((a->seq_start[s] + tt) * H + h) * P * R, ys + tt * P * R, (size_t)P * R * sizeof *ys);
+        free(ys);
+    }
+    return 0;
+}
+
+/* The chunked SSD form (O3C) over every slab, chunk size Q >= 1. y: [T, H, R, P] on the flat
+ * token axis, h_out: [nseq, H, N, P] (may be NULL). OpenMP over slabs. */
+int m3o_scan_chunked(const m3o_args *a, int Q, double *y, double *h_out, int nthreads) {
+    if (check(a) || !y || Q < 1) return 1;
+    const int H = a->H, P = a->P, N = a->N, R = a->R;
+    const int64_t nslab = (int64_t)a->nseq * H;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t sl = 0; sl < nslab; sl++) {
+        int s = (int)(sl / H), h = (int)(sl % H);
+        int64_t len = a->seq_len[s];
+        double *ys = malloc((size_t)(len > 0 ? len : 1) * P * R * sizeof *ys);
+        double *hs = h_out ? h_out + ((int64_t)s * H + h) * N * P : NULL;
+        o3c_slab(a, Q, s, h, ys, hs);
         for (int64_t tt = 0; tt < len; tt++)
             memcpy(y + ((a->seq_start[s] + tt) * H + h) * P * R, ys + tt * P * R, (size_t)P * R * sizeof *ys);
         free(ys);

@@ -77,6 +77,7 @@ def lib():
                                     ctypes.c_void_p, ctypes.c_void_p]
         l.m3o_decode.argtypes = [ctypes.POINTER(_Args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         l.m3o_max_threads.restype = ctypes.c_int
+        l.m3o_scan_chunked.argtypes = [ctypes.POINTER(_Args), ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         l.m3o_scan_bwd.argtypes = [ctypes.POINTER(_Args), ctypes.POINTER(_Grads), ctypes.c_int]
         _lib = l
     return _lib
@@ -160,6 +161,20 @@ def scan(inp: dict, form: int = 1, nthreads: int = 0, want_state: bool = True):
     y = np.zeros((T, pk.H, pk.R, pk.P), dtype=np.float64)
     h = np.zeros((pk.nseq, pk.H, pk.N, pk.P), dtype=np.float64) if want_state else None
     rc = lib().m3o_scan(ctypes.byref(pk.args), form, y.ctypes.data, _ptr(h), nthreads)
+    if rc:
+        raise ValueError("oracle rejected its arguments")
+    return y.reshape(inp["x"].shape), h
+
+
+def scan_chunked(inp: dict, chunk: int, nthreads: int = 0, want_state: bool = True):
+    """Whole scan in the chunked SSD form (O3C) with chunks of `chunk` tokens.
+    Returns (y [same leading shape as x], h_out [S,H,N,P])."""
+    flat, st, ln = flatten(inp)
+    pk = _Pack(flat, st, ln)
+    T = flat["x"].shape[0]
+    y = np.zeros((T, pk.H, pk.R, pk.P), dtype=np.float64)
+    h = np.zeros((pk.nseq, pk.H, pk.N, pk.P), dtype=np.float64) if want_state else None
+    rc = lib().m3o_scan_chunked(ctypes.byref(pk.args), int(chunk), y.ctypes.data, _ptr(h), nthreads)
     if rc:
         raise ValueError("oracle rejected its arguments")
     return y.reshape(inp["x"].shape), h

@@ -328,7 +328,15 @@ def test_full_size_sampled_slabs(oracle, cfg, block):
     cu = d["cu_seqlens"].cpu().numpy() if "cu_seqlens" in d else None
     S = (len(cu) - 1) if cu is not None else c["batch"]
     rng = np.random.default_rng(cfg)
-    picks = [(0, 0), (S - 1, c["nheads"] - 1)] + [(int(rng.integers(S)), int(rng.integers(c["nheads"]))) for _ in range(3)]
+    H = c["nheads"]
+    picks = [(0, 0), (S - 1, H - 1)] + [(int(rng.integers(S)), int(rng.integers(H))) for _ in range(3)]
+    if cu is not None:
+        # packed: the longest sequence (the kernel's first workgroups, and its longest chain of
+        # chunks) and the last workgroup in the kernel's longest-first order (the shortest
+        # sequence, ties by index, last head)
+        ln = np.diff(cu)
+        order = sorted(range(S), key=lambda i: (-int(ln[i]), i))
+        picks += [(order[0], int(rng.integers(H))), (order[-1], H - 1)]
     for s, hh in picks:
         one = _slab_inputs(d, s, hh, cu)
         yo, ho = oracle.scan_slab(one, 0, 0)

@@ -1,11 +1,18 @@
 """GPU parity of the scan's backward (mamba3_scan_bwd) against the fp64
 gradient oracle OB, itself pinned by finite differences of the forward.
 
-Metric: per gradient array, max |gpu - oracle| / max |oracle| over the whole
-array (tokens, heads and columns together); fp32 token inputs within 1e-4,
-bf16 token inputs (gradients returned in bf16) within 2e-2. A gradient that
-vanishes exactly is held to max |gpu| < 1e-6. All calls go through the C
-ABI."""
+Metric: per gradient array and per slab, as for the forward: a slab is one
+(sequence, head) of a token-indexed gradient (one (sequence, group) for dB, dC
+and a shared angle row's dtheta; packed sequences are split at cu_seqlens) and
+one (sequence, head) or (sequence, group) of dh_in, dBprev, dxprev. Per slab
+max |gpu - oracle| / max |oracle|; the maximum over slabs is held to 1e-4 for
+fp32 token inputs and 2e-2 for bf16 ones (gradients returned in bf16). The
+per-head parameter gradients (dA, dD, the bias gradients) are each one sum over
+every sequence and token of a head, whose relative error is set by cancellation
+in that sum rather than by any slab of the kernel's work; they are held to the
+same bounds over the whole array (all heads). A slab whose oracle gradient
+vanishes (max below 1e-9) is held to max |gpu| < 1e-6. All calls go through the
+C ABI."""
 import numpy as np
 import pytest
 
@@ -32,22 +39,46 @@ def run_bwd(inp, gr):
     return {k: from_dev(v) for k, v in g.items()}
 
 
+TOKEN_KEYS = ("dx", "ddt", "dlam", "dtheta", "dB", "dC", "dz", "dA_tok")   # [batch, L, head or group, ...]
+STATE_KEYS = ("dh_in", "dBprev", "dxprev")                                    # [sequence, head or group, ...]
+
+
+def slabs(k, a, cu):
+    """The slabs of gradient k (array a in the oracle's shape), as a list of arrays."""
+    if k in TOKEN_KEYS:
+        seqs = ([a[0, int(cu[i]):int(cu[i + 1])] for i in range(len(cu) - 1)] if cu is not None
+                else [a[i] for i in range(a.shape[0])])
+        return [q[:, j] for q in seqs for j in range(a.shape[2]) if q.shape[0] > 0]
+    if k in STATE_KEYS:
+        return [a[i, j] for i in range(a.shape[0]) for j in range(a.shape[1])]
+    return [a]                                                                  # dA, dD, biases: whole array
+
+
+def slab_err(k, a, b, cu):
+    worst = 0.0
+    for ga, ob in zip(slabs(k, a, cu), slabs(k, b, cu)):
+        den = np.abs(ob).max()
+        if den < 1e-9:
+            # an exactly vanishing gradient (e.g. the angle's with a zero state): the kernel's
+            # value is rounding residue of terms that cancel, held to an absolute bound
+            e = 0.0 if np.abs(ga).max() < 1e-6 else float("inf")
+        else:
+            e = float(np.abs(ga - ob).max() / den)
+        worst = max(worst, e)
+    return worst
+
+
 def compare(oracle, inp, gr, tol, label):
     gg = run_bwd(inp, gr)
     go = oracle.scan_bwd({k: v for k, v in inp.items() if k != "meta"}, gr["dy"].astype(np.float64)
                          if gr["dy"].dtype != np.uint16 else synth.bits_to_f32(gr["dy"]).astype(np.float64),
                          gr.get("dh_out"))
     worst = {}
+    cu = inp.get("cu_seqlens")
     for k in KEYS:
         if k not in go:
             continue
-        a, b = gg[k].reshape(go[k].shape), go[k]
-        if np.abs(b).max() < 1e-9:
-            # an exactly vanishing gradient (e.g. the angle's with a zero state): the kernel's
-            # value is rounding residue of terms that cancel, held to an absolute bound
-            worst[k] = 0.0 if np.abs(a).max() < 1e-6 else float("inf")
-        else:
-            worst[k] = float(np.abs(a - b).max() / np.abs(b).max())
+        worst[k] = slab_err(k, gg[k].reshape(go[k].shape), go[k], cu)
     note(f"{label}: " + " ".join(f"{k} {v:.1e}" for k, v in worst.items()))
     bad = {k: v for k, v in worst.items() if not v < tol}
     assert not bad, bad
@@ -203,9 +234,9 @@ def test_bwd_full_size_sampled_heads(oracle, cfg):
         dy1 = synth.bits_to_f32(bits(dy[:, :, hh:hh + 1])).astype(np.float64)
         go = oracle.scan_bwd(one, dy1, None)
         worst = {}
-        for k in ("dx", "ddt", "dlam", "dtheta", "dB", "dC"):
+        for k in ("dx", "ddt", "dlam", "dtheta", "dB", "dC"):   # per (sequence, head) slab
             a = from_dev(g[k][:, :, hh:hh + 1]).reshape(go[k].shape)
-            worst[k] = float(np.abs(a - go[k]).max() / np.abs(go[k]).max())
+            worst[k] = slab_err(k, a, go[k], None)
         for k in ("dA", "dD"):
             worst[k] = float(abs(from_dev(g[k][hh:hh + 1])[0] - go[k][0]) / abs(go[k][0]))
         note(f"  head {hh}: " + " ".join(f"{k} {v:.1e}" for k, v in worst.items()))

@@ -288,6 +288,41 @@ def test_decode_config3_full_batch(oracle):
     assert state_relerr(hg, ho) < 1e-5
 
 
+def test_decode_config3_full_batch_64_steps(oracle):
+    """The decode workload at full batch (256 rows x 64 heads) for 64 consecutive steps on the
+    hardware exp / sincos of the bf16 path, over a ring of 16 token-input sets (the state evolves,
+    so no step repeats another). Rows are independent: every step's y and the final state of
+    sampled rows (the first, the last and two inside) are checked against the oracle stepping
+    those rows alone, per (row, head) slab."""
+    import torch
+    steps, rows = 64, [0, 37, 170, 255]
+    inp = synth.decode_inputs(3, seed=8, ring=16)
+    note(f"decode config3 full batch, {steps} steps, sampled rows {rows}")
+    dev = device()
+    d = upload(inp, dev)
+    h = d["h"].clone()
+    Bprev, xprev = d["Bprev"], d["xprev"]
+    yg = []
+    for k in range(steps):
+        i = k % d["x"].shape[0]
+        y = m3.mamba3_decode_step(d["x"][i], d["dt"][i], d["lam"][i], d["theta"][i], d["B"][i], d["C"][i],
+                                  d["A"], d["D"], h=h, Bprev=Bprev, xprev=xprev)
+        yg.append(from_dev(y[rows]))
+        Bprev, xprev = d["B"][i], d["x"][i]
+    torch.cuda.synchronize()
+    hg = from_dev(h[rows])
+    sub = {kk: inp[kk][:, rows] for kk in ("x", "dt", "lam", "theta", "B", "C")}
+    sub.update(A=inp["A"], D=inp["D"], h=inp["h"][rows], Bprev=inp["Bprev"][rows], xprev=inp["xprev"][rows])
+    yo, ho = oracle_decode(oracle, sub, steps=steps)
+    worst = 0.0
+    for a, b in zip(yg, yo):
+        num = np.abs(a - b).max(axis=(2, 3))
+        worst = max(worst, float(np.max(num / np.abs(b).max(axis=(2, 3)))))
+    note(f"  y relerr (max over steps and slabs) {worst:.2e}  h relerr {state_relerr(hg, ho):.2e}")
+    assert worst < TOL_BF16
+    assert state_relerr(hg, ho) < 1e-4
+
+
 def test_decode_siso_full_batch(oracle):
     """The SISO decode shape of the bench (batch 256, 64 heads, N = 128, R = 1), whole batch, 2 steps."""
     inp = synth.decode_inputs(dict(synth.CONFIGS[3], dstate=128, rank=1), ring=2)

@@ -12,7 +12,9 @@ derivative's sign, the previous-token weight dropped from its gradient, the
 norm's Jacobian reduced to its diagonal, the gate's derivative without its
 input factor, and the decay's share of the step's gradient dropped; in the variants, a
 per-token decay rate halved, the fixed trapezoid weight ignored and heads
-mapped to the wrong shared angle row."""
+mapped to the wrong shared angle row; in the chunked SSD form, the carried
+state's fold taking another token's weight, its final state rotated the wrong
+way and the in-chunk decay missing its first factor."""
 import os
 import shutil
 import subprocess
@@ -57,6 +59,12 @@ MUTATIONS = {
     "fixed_lambda_ignored": ("return a->lam ? ld(a->lam, a->in_dtype, i) : a->lam_fixed;",
                              "return a->lam ? ld(a->lam, a->in_dtype, i) : 0.5;"),
     "angle_group_of_head": ("return (t * Gth + h / (a->H / Gth)) * K + k;", "return (t * Gth + h % Gth) * K + k;"),
+    # the chunked SSD form: the carried state's fold taking the chunk's second token's weight, the
+    # final state rotated the wrong way, the in-chunk decay missing its first factor
+    "chunked_fold_wrong_token": ("Hs[n * P + p] += delta[0] * acc;", "Hs[n * P + p] += delta[nq > 1 ? 1 : 0] * acc;"),
+    "chunked_state_rotation_sign": ("Hs[(2 * k) * P + p] = c * u - sn * v;\n                Hs[(2 * k + 1) * P + p] = sn * u + c * v;",
+                                    "Hs[(2 * k) * P + p] = c * u + sn * v;\n                Hs[(2 * k + 1) * P + p] = -sn * u + c * v;"),
+    "chunked_decay_first_factor": ("for (int k = 0; k <= t; k++) decay *= alpha[k];", "for (int k = 1; k <= t; k++) decay *= alpha[k];"),
     "stale_previous": ("memcpy(bp, bc, (size_t)K * R * sizeof *bp);\n        memcpy(xp, xc, (size_t)P * R * sizeof *xp);\n",
                        ""),
 }

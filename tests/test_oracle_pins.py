@@ -70,6 +70,36 @@ def test_complex_form_equals_ssd_matrix_form(oracle, R):
         assert relerr(y3, y1[0, :, h]) < 1e-12
 
 
+@pytest.mark.parametrize("Q", [1, 2, 5, 64])
+@pytest.mark.parametrize("features", ["plain", "block", "variants"])
+def test_chunked_form_equals_sequential(oracle, Q, features):
+    """O3C == O1: the SSD matrix form inside chunks of Q tokens, the state carried from chunk to
+    chunk with the previous token's term folded in ("Parallel representation under SSD": parallel
+    within chunks, recurrent across them), equals the token-by-token recurrence for every chunk
+    size (Q = 1: every token its own chunk; Q = 64: one chunk per sequence). Packed sequences
+    with empty and one-token members, each resumed from a state and a previous token, rank 3 with
+    grouped B/C; with the block prologue and gate; with the variants (per-token decay rate, fixed
+    trapezoid weight, one angle row per B/C group)."""
+    rng = np.random.default_rng(60 + Q)
+    lens = [1, 0, 18, 21]
+    H, G, P, N, R = 4, 2, 3, 6, 3
+    inp = rand_inputs(rng, b=1, L=sum(lens), H=H, G=G, P=P, N=N, R=R, scale_theta=3.0)
+    inp["cu_seqlens"] = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    inp.update(h_in=rng.standard_normal((4, H, N, P)), Bprev=rng.standard_normal((4, G, R, N)) / 2,
+               xprev=rng.standard_normal((4, H, R, P)))
+    if features == "block":
+        inp.update(bc_norm=True, bc_eps=1e-3, B_bias=rng.uniform(0.5, 1.5, (H, N)),
+                   C_bias=rng.uniform(0.5, 1.5, (H, N)), z=rng.standard_normal(inp["x"].shape))
+    if features == "variants":
+        inp["A_tok"], inp["A"] = -np.exp(rng.normal(0, 0.7, inp["dt"].shape)), None
+        inp["lam"], inp["lam_fixed"] = None, 0.3
+        inp["theta"] = inp["theta"][:, :, ::2].copy()          # one angle row per 2 heads
+    y1, h1 = oracle.scan(inp, form=1)
+    yc, hc = oracle.scan_chunked(inp, Q)
+    assert relerr(yc, y1) < 1e-12
+    assert relerr(hc, h1) < 1e-12
+
+
 # --------------------------------------------------------------------------
 # Special cases that reduce to simpler textbook recurrences.
 def _real_trapezoid(inp, use_rotation):
@@ -329,12 +359,13 @@ def test_constant_inputs_closed_form(oracle):
         inp = dict(x=np.tile(xv, (1, L, 1, 1, 1)), dt=np.full((1, L, 1), dt), lam=np.full((1, L, 1), lam),
                    theta=np.tile(th, (1, L, 1, 1)), B=np.tile(Bv, (1, L, 1, 1, 1)), C=np.tile(Cv, (1, L, 1, 1, 1)),
                    A=np.array([A]), D=np.array([D]))
-        y, h = oracle.scan(inp, form=1)
         ht = hstar + (z ** (L - 1))[:, None] * (gamma * v - hstar)
-        hc = h[0, 0, 0::2] + 1j * h[0, 0, 1::2]
-        assert np.allclose(hc, ht, rtol=1e-12, atol=1e-12)
         yt = (c.T @ ht).real + D * xv                                       # [R,P]
-        assert np.allclose(y[0, -1, 0], yt, rtol=1e-12, atol=1e-12)
+        # the recurrence, and the chunked SSD form at chunk sizes that do and do not divide L
+        for y, h in (oracle.scan(inp, form=1), oracle.scan_chunked(inp, 4), oracle.scan_chunked(inp, 16)):
+            hc = h[0, 0, 0::2] + 1j * h[0, 0, 1::2]
+            assert np.allclose(hc, ht, rtol=1e-12, atol=1e-12)
+            assert np.allclose(y[0, -1, 0], yt, rtol=1e-12, atol=1e-12)
 
 
 # --------------------------------------------------------------------------
