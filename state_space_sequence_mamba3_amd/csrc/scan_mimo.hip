@@ -49,6 +49,16 @@ struct MimoParams {
     int32_t seqlen, H, G, nseq, Gth;
 };
 
+// A load / store at a wave-uniform base plus a 32-bit byte offset (the scalar-base addressing form).
+template <class T>
+__device__ __forceinline__ T ld_off(const void *base, uint32_t byte_off) {
+    return *(const T *)((const char *)base + byte_off);
+}
+template <class T>
+__device__ __forceinline__ void st_off(void *base, uint32_t byte_off, T v) {
+    *(T *)((char *)base + byte_off) = v;
+}
+
 template <int N_, int P_, int R_, int Q_>
 struct MCfg {
     static constexpr int N = N_, P = P_, R = R_, Q = Q_;
@@ -218,41 +228,50 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     bf16x2 h_th[NPAN][TPL];                                // theta of the lane's angle pair, per panel
     bf16x8 RB[NLB], RX[NLX];                               // raw B and X pieces of the next panel
     bf16x8 HC[TPW][NKK];                                   // raw C rows of the next round's t-blocks
-    auto clamp_tok = [&](int64_t c0h, int tau) __attribute__((always_inline)) {           // token index of chunk-local tau, in range
-        const int64_t c0c = c0h < len ? c0h : 0;
-        return start + c0c + min((int64_t)tau, len - c0c - 1);
+    // Addressing: every load of a chunk is a wave-uniform base (the chunk's first token; SGPRs)
+    // plus a 32-bit per-lane element offset (a chunk spans at most Q tokens, far below 2^31
+    // elements), so a lane holds one 32-bit offset per load instead of a 64-bit address, and the
+    // loads take the scalar-base form. c0c: the chunk's start (a chunk past the end reads the
+    // sequence start); ltok: the clamp of chunk-local token indices to the last valid one.
+    auto chunk_start = [&](int64_t c0h) __attribute__((always_inline)) { return c0h < len ? c0h : (int64_t)0; };
+    auto ltok = [&](int64_t c0c, int tau) __attribute__((always_inline)) {
+        return (uint32_t)min(tau, (int)min((int64_t)Q, len - c0c - 1));   // tau <= Q always
     };
-    // tq: the thread index the address math uses (tid, or an opaque copy inside the chunk loop, so
-    // that the per-thread address terms are recomputed at each load instead of being hoisted out of
-    // the loop and spilled)
+    // tq: the thread index the offset math uses (tid, or an opaque copy inside the chunk loop, so
+    // that the per-thread terms are recomputed at each load instead of being hoisted out of the
+    // loop and spilled)
     auto load_header = [&](int64_t c0h, int tq) __attribute__((always_inline)) {
-        const int64_t c0c = c0h < len ? c0h : 0;
+        const int64_t c0c = chunk_start(c0h);
         const int nqh = (int)min((int64_t)Q, len - c0c);
+        const bf16 *bdt = pr.dt + (start + c0c) * H + h, *blam = pr.lam + (start + c0c) * H + h;
         {
-            const int64_t tk = clamp_tok(c0h, min(tq, Q - 1));
-            h_dt = pr.dt[tk * H + h];
-            h_lam = pr.lam[tk * H + h];
-            const int64_t tn = clamp_tok(c0h, nqh);
-            h_dtn = pr.dt[tn * H + h];
-            h_lamn = pr.lam[tn * H + h];
+            const uint32_t tk = ltok(c0c, min(tq, Q - 1)), tn = ltok(c0c, nqh);
+            h_dt = ld_off<bf16>(bdt, tk * (uint32_t)H * 2u);
+            h_lam = ld_off<bf16>(blam, tk * (uint32_t)H * 2u);
+            h_dtn = ld_off<bf16>(bdt, tn * (uint32_t)H * 2u);
+            h_lamn = ld_off<bf16>(blam, tn * (uint32_t)H * 2u);
         }
         const int lq = tq & 63;
         const int k = wave * CF::KW + 2 * (lq % KP), g0 = (lq / KP) * TPL;
+        const bf16 *bth = gTh + (start + c0c) * strTh;
 #pragma unroll
         for (int p = 0; p < NPAN; p++)
 #pragma unroll
-            for (int j = 0; j < TPL; j++) h_th[p][j] = *(const bf16x2 *)(gTh + clamp_tok(c0h, p * PT + g0 + j) * strTh + k);
+            for (int j = 0; j < TPL; j++)
+                h_th[p][j] = ld_off<bf16x2>(bth, (ltok(c0c, p * PT + g0 + j) * (uint32_t)strTh + (uint32_t)k) * 2u);
     };
     auto load_panel = [&](int64_t c0h, int pan, int tq) __attribute__((always_inline)) {
+        const int64_t c0c = chunk_start(c0h);
+        const bf16 *bB = gB + (start + c0c) * strBC, *bX = gX + (start + c0c) * strX;
 #pragma unroll
         for (int i = 0; i < NLB; i++) {
             const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
-            RB[i] = *(const bf16x8 *)(gB + clamp_tok(c0h, pan * PT + row / R) * strBC + (row % R) * N + col);
+            RB[i] = ld_off<bf16x8>(bB, (ltok(c0c, pan * PT + row / R) * (uint32_t)strBC + (uint32_t)((row % R) * N + col)) * 2u);
         }
 #pragma unroll
         for (int i = 0; i < NLX; i++) {
             const int c = tq + i * NTHR, row = c / (P / 8), col = (c % (P / 8)) * 8;
-            RX[i] = *(const bf16x8 *)(gX + clamp_tok(c0h, pan * PT + row / R) * strX + (row % R) * P + col);
+            RX[i] = ld_off<bf16x8>(bX, (ltok(c0c, pan * PT + row / R) * (uint32_t)strX + (uint32_t)((row % R) * P + col)) * 2u);
         }
     };
     // t-blocks of a round: a balanced pair along the causal triangle of the panel, rotated by the
@@ -263,12 +282,14 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     };
     auto load_crows = [&](int64_t c0h, int pan, int tq) __attribute__((always_inline)) {
         const int l16q = tq & 15, q4q = (tq & 63) >> 4;
+        const int64_t c0c = chunk_start(c0h);
+        const bf16 *bC = gC + (start + c0c) * strBC;
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
             const int row = tb_of(u, c0h) * 16 + l16q;
+            const uint32_t o = ltok(c0c, pan * PT + row / R) * (uint32_t)strBC + (uint32_t)((row % R) * N + 8 * q4q);
 #pragma unroll
-            for (int kk = 0; kk < NKK; kk++)
-                HC[u][kk] = *(const bf16x8 *)(gC + clamp_tok(c0h, pan * PT + row / R) * strBC + (row % R) * N + 32 * kk + 8 * q4q);
+            for (int kk = 0; kk < NKK; kk++) HC[u][kk] = ld_off<bf16x8>(bC, (o + 32 * kk) * 2u);
         }
     };
     if (len > 0) {
@@ -628,6 +649,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         };
         // outputs of the round through a per-wave LDS transpose, 16-byte row stores
+        bf16 *yb = gY + tok0 * strX;   // the chunk's first output row (a uniform base)
         auto store_y = [&](int tpn) __attribute__((always_inline)) {
             // lane indices made opaque here: the phase's address math is recomputed in it rather
             // than precomputed for every phase of the chunk and held across them
@@ -645,7 +667,9 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 for (int c = lane; c < 16 * P / 8; c += 64) {
                     const int row = c / (P / 8), col = (c % (P / 8)) * 8;
                     const int rr = tbr[u] * 16 + row, tau = tpn * PT + rr / R;
-                    if (tau < nq) *(bf16x8 *)(gY + (tok0 + tau) * strX + (rr % R) * P + col) = *(const bf16x8 *)(ys + row * PS + col);
+                    if (tau < nq)
+                        st_off<bf16x8>(yb, ((uint32_t)tau * (uint32_t)strX + (uint32_t)((rr % R) * P + col)) * 2u,
+                                       *(const bf16x8 *)(ys + row * PS + col));
                 }
                 lds_wait();
             }
