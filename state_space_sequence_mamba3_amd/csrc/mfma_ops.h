@@ -75,6 +75,17 @@ __device__ __forceinline__ void rot_piece(const bf16x8 raw, const f16x8 cs, floa
     for (int e = 0; e < 8; e++) in[e] = (float)raw[e];
     rot_piece_f(in, cs, o);
 }
+// A load / store at a wave-uniform base plus a 32-bit per-lane byte offset: the loads take the
+// scalar-base addressing form, and a lane holds one 32-bit offset instead of a 64-bit address.
+template <class T>
+__device__ __forceinline__ T ld_off(const void *base, uint32_t byte_off) {
+    return *(const T *)((const char *)base + byte_off);
+}
+template <class T>
+__device__ __forceinline__ void st_off(void *base, uint32_t byte_off, T v) {
+    *(T *)((char *)base + byte_off) = v;
+}
+
 __device__ __forceinline__ bf16x8 pack8(const float (&o)[8]) {
     return bf16x8{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3], (bf16)o[4], (bf16)o[5], (bf16)o[6], (bf16)o[7]};
 }

@@ -327,40 +327,41 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     bf16x8 h_c[TPA][NKK];
     // C rows of the own t-blocks in operand layout: row 16 tb + l16, columns 32 kk + 8 q4 ..
     // tq: the thread index the address math uses (tid, or an opaque copy inside the chunk loop)
+    // Addressing: a chunk's loads are a wave-uniform base (the chunk's first token) plus a 32-bit
+    // per-lane byte offset (chunk-local token indices stay below Q), clamped to the sequence's last
+    // token; lanes hold 32-bit offsets, not 64-bit addresses.
+    auto ltok = [&](int64_t c0c, int tau) { return (uint32_t)min(tau, (int)min((int64_t)Q, len - c0c - 1)); };
     auto load_crows = [&](int64_t c0h, int tq) {
         const int64_t c0c = c0h < len ? c0h : 0;
-        const int64_t t0h = start + c0c, last = len - c0c - 1;
+        const bf16 *bC = gC + (start + c0c) * strBC;
         const int l16q = tq & 15, q4q = (tq & 63) >> 4;
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
             const int row = tb_of(u, c0h) * 16 + l16q;
-            const int tau = row / R, j = row % R;
-            const int64_t tk = t0h + min((int64_t)tau, last);
+            const uint32_t o = ltok(c0c, row / R) * (uint32_t)strBC + (uint32_t)((row % R) * N + 8 * q4q);
 #pragma unroll
-            for (int kk = 0; kk < NKK; kk++) h_c[u][kk] = *(const bf16x8 *)(gC + tk * strBC + j * N + 32 * kk + 8 * q4q);
+            for (int kk = 0; kk < NKK; kk++) h_c[u][kk] = ld_off<bf16x8>(bC, (o + 32 * kk) * 2u);
         }
     };
     auto load_header = [&](int64_t c0h, int tq) {
         const int64_t c0c = c0h < len ? c0h : 0;
         const int nqh = (int)min((int64_t)Q, len - c0c);
-        const int64_t t0h = start + c0c, last = len - c0c - 1;
         {
-            const int64_t tk = t0h + min((int64_t)min(tq, Q - 1), last);
-            h_dt = pr.dt[tk * H + h];
-            h_lam = pr.lam[tk * H + h];
-            if constexpr (CF::EPI) h_A = pr.Atk[tk * H + h];
-            const int64_t tn = t0h + min((int64_t)nqh, last);
-            h_dtn = pr.dt[tn * H + h];
-            h_lamn = pr.lam[tn * H + h];
+            const int64_t b = (start + c0c) * H + h;
+            const uint32_t tk = ltok(c0c, min(tq, Q - 1)) * (uint32_t)H * 2u, tn = ltok(c0c, nqh) * (uint32_t)H * 2u;
+            h_dt = ld_off<bf16>(pr.dt + b, tk);
+            h_lam = ld_off<bf16>(pr.lam + b, tk);
+            if constexpr (CF::EPI) h_A = ld_off<bf16>(pr.Atk + b, tk);
+            h_dtn = ld_off<bf16>(pr.dt + b, tn);
+            h_lamn = ld_off<bf16>(pr.lam + b, tn);
         }
         {
             const int lq = tq & 63;
             const int k = wave * CF::KW + 2 * (lq % CF::KP), g0 = (lq / CF::KP) * CF::TPL;
+            const bf16 *bth = gTh + (start + c0c) * strTh;
 #pragma unroll
-            for (int j = 0; j < CF::TPL; j++) {
-                const int64_t tk = t0h + min((int64_t)(g0 + j), last);
-                h_th2[j] = *(const bf16x2 *)(gTh + tk * strTh + k);
-            }
+            for (int j = 0; j < CF::TPL; j++)
+                h_th2[j] = ld_off<bf16x2>(bth, (ltok(c0c, g0 + j) * (uint32_t)strTh + (uint32_t)k) * 2u);
         }
         if constexpr (CF::PFC && CF::YO) load_crows(c0h, tq);
     };
@@ -369,22 +370,20 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     bf16x8 rb0[CF::NLB], rx0[CF::NLX], rb1[CF::NLB], rx1[CF::NLX];
     auto load_block_into = [&](bf16x8 (&rb)[CF::NLB], bf16x8 (&rx)[CF::NLX], int64_t c0b, int sb, int tq) {
         const int64_t c0c = c0b < len ? c0b : 0;                   // past the end: dummy loads, never used
-        const int64_t t0b = start + c0c, last = len - c0c - 1;
+        const bf16 *bB = gB + (start + c0c) * strBC, *bX = gX + (start + c0c) * strX;
 #pragma unroll
         for (int i = 0; i < CF::NLB; i++) {
             const int c = (tq + i * NTHR) % CF::BCH;
             const int row = c / (N / 8), col = (c % (N / 8)) * 8;
             const int tau = sb * TOKS + row / R;
-            const int64_t tk = t0b + min((int64_t)tau, last);
-            rb[i] = *(const bf16x8 *)(gB + tk * strBC + (row % R) * N + col);
+            rb[i] = ld_off<bf16x8>(bB, (ltok(c0c, tau) * (uint32_t)strBC + (uint32_t)((row % R) * N + col)) * 2u);
         }
 #pragma unroll
         for (int i = 0; i < CF::NLX; i++) {
             const int c = (tq + i * NTHR) % CF::XCH;
             const int row = c / (P / 8), col = (c % (P / 8)) * 8;
             const int tau = sb * TOKS + row / R;
-            const int64_t tk = t0b + min((int64_t)tau, last);
-            rx[i] = *(const bf16x8 *)(gX + tk * strX + (row % R) * P + col);
+            rx[i] = ld_off<bf16x8>(bX, (ltok(c0c, tau) * (uint32_t)strX + (uint32_t)((row % R) * P + col)) * 2u);
         }
     };
     auto advance = [&](int64_t &c0b, int &sb) {
@@ -959,7 +958,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                     for (int k = 0; k < NPC; k++) {
                         const int c = (tq & 63) + 64 * k, row = c / (P / 8), col = (c % (P / 8)) * 8;
                         const int rr = tb * 16 + row, tau = min(rr / R, nq - 1);   // in bounds; unused past the end
-                        zr[k] = *(const bf16x8 *)(gZ + (tok0 + tau) * strX + (rr % R) * P + col);
+                        zr[k] = ld_off<bf16x8>(gZ + tok0 * strX, ((uint32_t)tau * (uint32_t)strX + (uint32_t)((rr % R) * P + col)) * 2u);
                     }
                 }
 #pragma unroll
@@ -983,7 +982,8 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                             o[e] *= v / (1.f + __expf(-v));
                         }
                     }
-                    if (FULL || tau < nq) *(bf16x8 *)(gY + (tok0 + tau) * strX + (rr % R) * P + col) = pack8(o);
+                    if (FULL || tau < nq)
+                        st_off<bf16x8>(gY + tok0 * strX, ((uint32_t)tau * (uint32_t)strX + (uint32_t)((rr % R) * P + col)) * 2u, pack8(o));
                 }
                 lds_wait();
             }
@@ -1001,8 +1001,9 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 for (int c = lane; c < 16 * P / 8; c += 64) {
                     const int row = c / (P / 8), col = (c % (P / 8)) * 8;
                     const int rr = tb * 16 + row, tau = rr / R;
-                    if (FULL || tau < nq) *(bf16x8 *)(gY + (tok0 + tau) * strX + (rr % R) * P + col) =
-                        *(const bf16x8 *)(ys + row * PS + col);
+                    if (FULL || tau < nq)
+                        st_off<bf16x8>(gY + tok0 * strX, ((uint32_t)tau * (uint32_t)strX + (uint32_t)((rr % R) * P + col)) * 2u,
+                                       *(const bf16x8 *)(ys + row * PS + col));
                 }
                 lds_wait();
             }

@@ -49,16 +49,6 @@ struct MimoParams {
     int32_t seqlen, H, G, nseq, Gth;
 };
 
-// A load / store at a wave-uniform base plus a 32-bit byte offset (the scalar-base addressing form).
-template <class T>
-__device__ __forceinline__ T ld_off(const void *base, uint32_t byte_off) {
-    return *(const T *)((const char *)base + byte_off);
-}
-template <class T>
-__device__ __forceinline__ void st_off(void *base, uint32_t byte_off, T v) {
-    *(T *)((char *)base + byte_off) = v;
-}
-
 template <int N_, int P_, int R_, int Q_>
 struct MCfg {
     static constexpr int N = N_, P = P_, R = R_, Q = Q_;
