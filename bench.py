@@ -526,24 +526,25 @@ def summarize_stats(stats_dir, out_md, command):
 
 
 def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 30):
-    """Turns two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
-    dispatch) of `bench.py --copy-calibration` into HBM bytes per launch of the
-    scan and decode kernels, each counter scaled by its reading on the plain
-    1 GiB device copy. Writes traffic_<kernel>.json records (read by the bench
+    """Turns rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch; each
+    may be several runs, comma-separated) of `bench.py --copy-calibration` into
+    HBM bytes per launch of the scan and decode kernels, each counter scaled by
+    its reading on the plain 1 GiB device copy. Writes traffic_<kernel>.json records (read by the bench
     while the kernel source is unchanged) and a text summary."""
     import hashlib
     from collections import defaultdict
 
-    def per_dispatch(d, counter):
-        """{(kernel, workgroups): [bytes per dispatch]}"""
-        agg, names = defaultdict(float), {}
-        for r in _csv_rows(os.path.join(d, "run_counter_collection.csv")):
-            if r["Counter_Name"] == counter:
-                agg[r["Dispatch_Id"]] += float(r["Counter_Value"])
-                names[r["Dispatch_Id"]] = (r["Kernel_Name"], int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
+    def per_dispatch(dirs, counter):
+        """{(kernel, workgroups): [bytes per dispatch]} over one or more runs (comma-separated dirs)"""
         by = defaultdict(list)
-        for k, v in agg.items():
-            by[names[k]].append(v * 1024.0)
+        for d in dirs.split(","):
+            agg, names = defaultdict(float), {}
+            for r in _csv_rows(os.path.join(d, "run_counter_collection.csv")):
+                if r["Counter_Name"] == counter:
+                    agg[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                    names[r["Dispatch_Id"]] = (r["Kernel_Name"], int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
+            for k, v in agg.items():
+                by[names[k]].append(v * 1024.0)
         return by
 
     fetch, write = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
