@@ -34,6 +34,11 @@
 //   * Operand reads of a tile are all issued before its MFMAs (no per-MFMA
 //     conditions), and the next panel's raw B and X rows and the next round's
 //     raw C rows are loaded into registers one phase ahead.
+//   * Outputs accumulate transposed (the X / H' operand goes first into the
+//     MFMA), so each lane ends with four adjacent outputs of one row and stores
+//     them from registers; no LDS staging of y. The LDS row strides are padded
+//     so that every operand read of the score, output and inter-chunk products
+//     is free of bank conflicts.
 #include "mfma_ops.h"
 
 namespace m3 {
@@ -62,7 +67,11 @@ struct MCfg {
     static constexpr int TOKS32 = 32 / R;           // tokens per s-tile
     static constexpr int NKK = N / 32;              // K-steps over N (16x16x32)
     static constexpr int NPT = P / 16;              // 16-column tiles of P
-    static constexpr int NS = N + 8, PS = P + 8;    // padded bf16 row strides
+    // padded row strides (bf16, f16x2 elements). On gfx950's 64 four-byte LDS banks (16 lanes a
+    // cycle for 16-byte reads, 32 for the transposing 8-byte reads) they make the 16-byte reads
+    // of 16 consecutive rows (score operands, H', the angle table) and the transposing reads of 8
+    // consecutive X rows free of bank conflicts, with constant offsets between a lane's reads
+    static constexpr int NS = N + 16, PS = P + 16, KS = K + 8;
     // the N x P state: 32 x 32 tiles (32x32x16 MFMA) when every wave gets a whole one, else 16 x 16
     static constexpr int UT = ((N / 32) * (P / 32) % NW == 0) ? 32 : 16;
     static constexpr int NUT = (N / UT) * (P / UT), UPW = NUT / NW, URG = (UT == 32) ? 16 : 4;
@@ -81,9 +90,8 @@ struct MCfg {
     static constexpr int OFF_BS = 0;                              // bf16 [PR][NS]  B~' rows of the panel
     static constexpr int OFF_XS = OFF_BS + PR * NS * 2;           // bf16 [PR][PS]  X rows of the panel
     static constexpr int OFF_HB = OFF_XS + PR * PS * 2;           // bf16 [P][NS]   carried state H'
-    static constexpr int OFF_TAB = OFF_HB + P * NS * 2;           // f16x2 [PT][K]  (cos, sin) of the panel's Phi
-    static constexpr int OFF_YS = OFF_TAB + PT * K * 4;           // bf16 [NW][16][PS] output staging
-    static constexpr int OFF_PHC = OFF_YS + NW * 16 * PS * 2;     // float2 [K]     chunk total angle
+    static constexpr int OFF_TAB = OFF_HB + P * NS * 2;           // f16x2 [PT][KS] (cos, sin) of the panel's Phi
+    static constexpr int OFF_PHC = OFF_TAB + PT * KS * 4;         // float2 [K]     chunk total angle
     static constexpr int OFF_S2 = OFF_PHC + K * 8;                // float [Q] log2-decay prefix S2_t
     static constexpr int OFF_G1 = OFF_S2 + Q * 4;                 // float [Q] gamma_s + delta_{s+1}
     static constexpr int OFF_GM = OFF_G1 + Q * 4;                 // float [Q] gamma_s
@@ -103,7 +111,7 @@ template <class CF>
 __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) void k_scan_mimo(MimoParams pr) {
     constexpr int N = CF::N, P = CF::P, R = CF::R, Q = CF::Q, NW = CF::NW, K = CF::K, PT = CF::PT;
     constexpr int PR = CF::PR, NPAN = CF::NPAN, TPW = CF::TPW, NKK = CF::NKK, NPT = CF::NPT;
-    constexpr int NS = CF::NS, PS = CF::PS, UT = CF::UT, UPW = CF::UPW, URG = CF::URG, NTHR = CF::NTHR;
+    constexpr int NS = CF::NS, PS = CF::PS, KS = CF::KS, UT = CF::UT, UPW = CF::UPW, URG = CF::URG, NTHR = CF::NTHR;
     constexpr int KP = CF::KP, TG = CF::TG, TPL = CF::TPL, NLB = CF::NLB, NLX = CF::NLX;
     using UAcc = std::conditional_t<UT == 32, f32x16, f32x4>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -111,7 +119,6 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     bf16 *XS = (bf16 *)(smem + CF::OFF_XS);
     bf16 *HB = (bf16 *)(smem + CF::OFF_HB);
     f16x2 *TAB = (f16x2 *)(smem + CF::OFF_TAB);
-    bf16 *YS = (bf16 *)(smem + CF::OFF_YS);
     float2 *PHC = (float2 *)(smem + CF::OFF_PHC);
     float *S2 = (float *)(smem + CF::OFF_S2);
     float *G1 = (float *)(smem + CF::OFF_G1);
@@ -393,7 +400,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 float sn0, cs0, sn1, cs1;
                 __sincosf(x0, &sn0, &cs0);
                 __sincosf(x1, &sn1, &cs1);
-                *(f16x4 *)(TAB + tau * K + k) = f16x4{(_Float16)cs0, (_Float16)sn0, (_Float16)cs1, (_Float16)sn1};
+                *(f16x4 *)(TAB + tau * KS + k) = f16x4{(_Float16)cs0, (_Float16)sn0, (_Float16)cs1, (_Float16)sn1};
                 if (last && tau == PT - 1) {   // the chunk's last panel; angles past the end are zero
                     sincosf(x0, &sn0, &cs0);
                     sincosf(x1, &sn1, &cs1);
@@ -425,7 +432,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int i = 0; i < NLB; i++) {
                 const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
-                cs[i] = *(const f16x8 *)(TAB + (row / R) * K + col / 2);
+                cs[i] = *(const f16x8 *)(TAB + (row / R) * KS + col / 2);
                 eb[i] = EB[pan * PT + row / R];
             }
 #pragma unroll
@@ -459,7 +466,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 const bool ok = pan * PT + tau < nq;
 #pragma unroll
                 for (int kk = 0; kk < NKK; kk++) {
-                    const f16x8 cs = *(const f16x8 *)(TAB + tau * K + 16 * kk + 4 * q4);
+                    const f16x8 cs = *(const f16x8 *)(TAB + tau * KS + 16 * kk + 4 * q4);
                     float o[8];
                     rot_piece(HC[u][kk], cs, o);
 #pragma unroll
@@ -468,7 +475,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 }
             }
         };
-        // ---- output accumulators of the round: the inter-chunk term e^{S_t} C~_t^T H'
+        // ---- output accumulators of the round, transposed: yacc[u][pt] of lane (l16, q4) holds
+        // y at t-row 16 tbr[u] + l16, columns 16 pt + 4 q4 .. + 3 (the MFMAs take the X / H'
+        // operand first), so a lane stores four adjacent outputs of one row straight from its
+        // registers. Here the inter-chunk term e^{S_t} C~_t^T H'.
         f32x4 yacc[TPW][NPT];
         auto inter = [&](int pan) __attribute__((always_inline)) {
             // lane indices made opaque here: the phase's address math is recomputed in it rather
@@ -487,18 +497,16 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                 for (int kk = 0; kk < NKK; kk++)
 #pragma unroll
-                    for (int u = 0; u < TPW; u++) yacc[u][pt] = mfma16(creg[u][kk], hop[kk], yacc[u][pt]);
+                    for (int u = 0; u < TPW; u++) yacc[u][pt] = mfma16(hop[kk], creg[u][kk], yacc[u][pt]);
             }
-            if (!fast) {   // unscaled C~ rows: the decay factor per output row
+            if (!fast) {   // unscaled C~ rows: the decay factor of the lane's output row
 #pragma unroll
                 for (int u = 0; u < TPW; u++) {
-                    float sc[4];
-#pragma unroll
-                    for (int i = 0; i < 4; i++) sc[i] = exp2_neg(S2[pan * PT + (tbr[u] * 16 + 4 * q4 + i) / R]);
+                    const float sc = exp2_neg(S2[pan * PT + (tbr[u] * 16 + l16) / R]);
 #pragma unroll
                     for (int pt = 0; pt < NPT; pt++)
 #pragma unroll
-                        for (int i = 0; i < 4; i++) yacc[u][pt][i] *= sc[i];
+                        for (int i = 0; i < 4; i++) yacc[u][pt][i] *= sc;
                 }
             }
         };
@@ -572,7 +580,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             for (int pt = 0; pt < NPT; pt++) {
                 const bf16x8 xop = tr_operand(XS, PS, 32 * j + 4 * q4, 32 * j + 16 + 4 * q4, pt * 16, l16);
 #pragma unroll
-                for (int u = 0; u < NA; u++) yacc[u0 + u][pt] = mfma16(mop[u], xop, yacc[u0 + u][pt]);
+                for (int u = 0; u < NA; u++) yacc[u0 + u][pt] = mfma16(xop, mop[u], yacc[u0 + u][pt]);
             }
         };
         // every s-tile of the staged panel spn that holds valid tokens, against the round's t-blocks
@@ -591,7 +599,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 for (int u = 0; u < TPW; u++)
 #pragma unroll
                     for (int pt = 0; pt < NPT; pt++) {
-                        const bf16x4 xv = ds_read_tr(XS + (tbr[u] * 16 + 4 * q4 + l16 / 4) * PS + pt * 16 + 4 * (l16 % 4));
+                        const bf16x4 xv = *(const bf16x4 *)(XS + (tbr[u] * 16 + l16) * PS + pt * 16 + 4 * q4);
 #pragma unroll
                         for (int i = 0; i < 4; i++) yacc[u][pt][i] += Dh * (float)xv[i];
                     }
@@ -638,30 +646,24 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 *(bf16x8 *)(BS + row * NS + col) = pack8(o);
             }
         };
-        // outputs of the round through a per-wave LDS transpose, 16-byte row stores
+        // outputs of the round straight from the accumulators: four adjacent columns of one row
+        // per lane and store (a t-block's 16 rows are 4 tokens' rank rows, 2 KB in all)
         bf16 *yb = gY + tok0 * strX;   // the chunk's first output row (a uniform base)
         auto store_y = [&](int tpn) __attribute__((always_inline)) {
             // lane indices made opaque here: the phase's address math is recomputed in it rather
             // than precomputed for every phase of the chunk and held across them
             const int tqp = opaque<true>(tid);
             const int lane = tqp & 63, l16 = tqp & 15, q4 = lane >> 4;
-            bf16 *ys = YS + wave * 16 * PS;
 #pragma unroll
             for (int u = 0; u < TPW; u++) {
+                const int rr = tbr[u] * 16 + l16, tau = tpn * PT + rr / R;
+                if (tau < nq) {
+                    const uint32_t o = (uint32_t)tau * (uint32_t)strX + (uint32_t)((rr % R) * P + 4 * q4);
 #pragma unroll
-                for (int pt = 0; pt < NPT; pt++)
-#pragma unroll
-                    for (int i = 0; i < 4; i++) ys[(4 * q4 + i) * PS + pt * 16 + l16] = (bf16)yacc[u][pt][i];
-                lds_wait();
-#pragma unroll
-                for (int c = lane; c < 16 * P / 8; c += 64) {
-                    const int row = c / (P / 8), col = (c % (P / 8)) * 8;
-                    const int rr = tbr[u] * 16 + row, tau = tpn * PT + rr / R;
-                    if (tau < nq)
-                        st_off<bf16x8>(yb, ((uint32_t)tau * (uint32_t)strX + (uint32_t)((rr % R) * P + col)) * 2u,
-                                       *(const bf16x8 *)(ys + row * PS + col));
+                    for (int pt = 0; pt < NPT; pt++)
+                        st_off<bf16x4>(yb, (o + 16 * pt) * 2u,
+                                       bf16x4{(bf16)yacc[u][pt][0], (bf16)yacc[u][pt][1], (bf16)yacc[u][pt][2], (bf16)yacc[u][pt][3]});
                 }
-                lds_wait();
             }
         };
 
