@@ -26,6 +26,7 @@ current stream, which the binding passes to the library), W untimed warmup
 steps, then exactly K timed steps between device synchronisations.
 """
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -233,6 +234,36 @@ def bench_long(steps, warmup, dev, seqlen=65536, nseg=16):
         out[name] = dict(ms=ms, tokens_per_s=seqlen / (ms * 1e-3))
     out["workload"] = f"SISO scan bf16 1x{seqlen} H64 P64 N128, plain vs {nseg} segments"
     del d, y, h, args
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_packed_segmented(steps, warmup, dev, seg_tokens=(2048, 4096, 8192)):
+    """The packed workload (8 sequences, 65536 tokens, N = 128, R = 4) scanned in segments of
+    seg_tokens tokens (segment table, state-only scan, state passing, scan), beside the plain scan."""
+    import torch
+    import state_space_sequence_mamba3_amd as m3
+    from state_space_sequence_mamba3_amd import synth
+    c = dict(synth.CONFIGS[4])
+    d = synth.torch_scan_inputs(4, dev, seed=4)
+    y = torch.empty_like(d["x"])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    args = [d[k] for k in ("x", "dt", "lam", "theta", "B", "C", "A", "D")]
+    out = {}
+    fns = [("plain", lambda: m3.mamba3_scan_fwd(*args, y=y, cu_seqlens=d["cu_seqlens"], chunk=c["chunk"],
+                                                stream=stream))]
+    for L in seg_tokens:
+        nws = m3.lib().mamba3_scan_segmented_workspace_size(ctypes.byref(m3.ScanSegmentedArgs(
+            m3.scan_args(*args, y=y, cu_seqlens=d["cu_seqlens"], chunk=c["chunk"]), 0, None, 0, L)))
+        ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+        fns.append((f"segments_{L}", lambda L=L, ws=ws: m3.mamba3_scan_segmented(
+            *args, y=y, seg_tokens=L, cu_seqlens=d["cu_seqlens"], chunk=c["chunk"], workspace=ws, stream=stream)))
+    for name, fn in fns:
+        ms, _ = timed(fn, steps, warmup, stream)
+        out[name] = dict(ms=ms, tokens_per_s=c["seqlen"] / (ms * 1e-3))
+    out["workload"] = "packed MIMO scan bf16 65536 tok (8 sequences) H64 P64 N128 R4, plain vs segments"
+    del d, y, args, fns
     torch.cuda.empty_cache()
     return out
 
@@ -772,6 +803,9 @@ def main():
         res["long"] = bench_long(max(3, K // 4), max(1, W // 4), dev)
         print(f"# long sequence: plain {res['long']['plain']['ms']:.3f} ms, segmented "
               f"{res['long']['segmented']['ms']:.3f} ms", file=sys.stderr, flush=True)
+        res["packed_segmented"] = bench_packed_segmented(max(3, K // 4), max(1, W // 4), dev)
+        print("# packed segmented: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in res["packed_segmented"].items()
+                                                 if isinstance(v, dict)), file=sys.stderr, flush=True)
 
     peaks = measured_peaks(dev) if args.only == "all" else None
 
@@ -847,6 +881,8 @@ def main():
                 sec[k]["oracle"] = cpu[k]
     if "long" in res:
         sec["long_sequence"] = res["long"]
+    if "packed_segmented" in res:
+        sec["packed_segmented"] = res["packed_segmented"]
     line["secondary"] = sec
     if peaks:
         line["measured_peaks"] = peaks

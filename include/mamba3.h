@@ -234,31 +234,44 @@ mamba3_status mamba3_scan_bwd(const mamba3_scan_bwd_args *args, void *stream);
  * previous token (the rotations R_t are block-diagonal on the same pairs and
  * commute, so their product is R(Phi)).
  *
- * Every sequence of fwd (padded mode; packed mode is not supported) is cut
- * into nseg segments of seqlen / nseg tokens; segment k of sequence s is
- * "segment row" s * nseg + k, which is how the token arrays [batch, seqlen,
- * ...] read as [batch * nseg, seqlen / nseg, ...]. The intended use:
+ * Padded mode: every sequence of fwd is cut into nseg segments of seqlen /
+ * nseg tokens; segment k of sequence s is "segment row" s * nseg + k, which
+ * is how the token arrays [batch, seqlen, ...] read as [batch * nseg,
+ * seqlen / nseg, ...]. Packed mode (ABI 1.5; fwd.cu_seqlens set, nseg = 0):
+ * sequence s is cut into max(1, ceil(len_s / seg_tokens)) segments of
+ * seg_tokens tokens (the last one shorter; one empty segment for an empty
+ * sequence), numbered in sequence order: the segment rows, at most
+ * mamba3_segment_rows(fwd, 0, seg_tokens) of them. mamba3_segment_table
+ * writes their token ranges as a cu_seqlens table, which makes the segment
+ * rows a packed batch of their own (rows past the last segment are empty).
+ * The intended use:
+ *   0. packed mode: mamba3_segment_table, and the segment rows' scans below
+ *      take its table as cu_seqlens and its row count as nseq;
  *   1. mamba3_scan_fwd on the segment rows with h_in, Bprev, xprev NULL:
- *      its h_out is U [batch * nseg, H, N, P] (its y is not needed);
+ *      its h_out is U [rows, H, N, P] (its y is not needed);
  *   2. mamba3_state_passing: writes seg_h_in, seg_Bprev, seg_xprev;
  *   3. mamba3_scan_fwd on the segment rows with h_in = seg_h_in,
  *      Bprev = seg_Bprev, xprev = seg_xprev: y equals the whole-sequence
- *      scan's y (up to rounding), and its h_out rows s * nseg + nseg - 1 are
- *      the sequences' final states.
+ *      scan's y (up to rounding), and the h_out row of a sequence's last
+ *      segment is its final state.
+ * Here rows = batch * nseg (padded) or mamba3_segment_rows(fwd, 0,
+ * seg_tokens) (packed), and S = batch (padded) or nseq (packed).
  *
- * fwd        the whole-sequence arguments as for mamba3_scan_fwd (batch
- *            sequences of seqlen tokens; y, h_out, workspace, z and D are
- *            not read; h_in, Bprev and xprev are those of the sequences).
- * nseg       segments per sequence, >= 1, dividing seqlen.
- * U          [batch * nseg, H, N, P] fp32, step 1's final states.
- * seg_h_in   [batch * nseg, H, N, P] fp32 out: the state entering each
- *            segment (fwd.h_in, or zero, for segment 0).
- * seg_Bprev  [batch * nseg, G, R, N], seg_xprev [batch * nseg, H, R, P] out,
- *            token dtype: the token before each segment (the last token of
- *            the previous segment; fwd.Bprev/xprev, or zeros, for segment 0),
- *            raw as read (the prologue, if any, is applied by the scan).
- * h_out      [batch, H, N, P] fp32 out or NULL: the final state of every
+ * fwd        the whole-sequence arguments as for mamba3_scan_fwd (padded or
+ *            packed; y, h_out, workspace, z and D are not read; h_in, Bprev
+ *            and xprev are those of the sequences).
+ * nseg       padded: segments per sequence, >= 1, dividing seqlen; packed: 0.
+ * U          [rows, H, N, P] fp32, step 1's final states.
+ * seg_h_in   [rows, H, N, P] fp32 out: the state entering each segment
+ *            (fwd.h_in, or zero, for a sequence's first segment).
+ * seg_Bprev  [rows, G, R, N], seg_xprev [rows, H, R, P] out, token dtype: the
+ *            token before each segment (the last token of the previous
+ *            segment; fwd.Bprev/xprev, or zeros, for a first segment), raw as
+ *            read (the prologue, if any, is applied by the scan).
+ * h_out      [S, H, N, P] fp32 out or NULL: the final state of every
  *            sequence (it may be fwd.h_in exactly).
+ * seg_tokens packed: tokens per segment, >= 1; padded: 0.
+ * Rows past the packed batch's last segment are neither read nor written.
  * The outputs must not overlap each other or any input. Alignment: 16 bytes
  * for U and every output. The prologue settings of fwd (bc_norm, biases)
  * apply to the folded previous token, as in the scan. Deterministic. */
@@ -269,27 +282,48 @@ typedef struct {
     float *seg_h_in;
     void *seg_Bprev, *seg_xprev;
     float *h_out;
+    int32_t seg_tokens;   /* ABI 1.5 */
 } mamba3_state_passing_args;
 
 mamba3_status mamba3_state_passing_validate(const mamba3_state_passing_args *args);
 mamba3_status mamba3_state_passing(const mamba3_state_passing_args *args, void *stream);
 
-/* The whole-sequence scan run as batch * nseg independent segments (ABI
- * 1.4): steps 1-3 above, enqueued in order on one stream. Step 1 runs as a
- * state-only scan (the chunk-state updates alone: no C rows read, no scores
- * or y formed). The result equals mamba3_scan_fwd's up to rounding; it costs
- * about one and a half scans but multiplies the workgroups by nseg, which
- * pays for a few long sequences.
+/* Segment rows of a batch (ABI 1.5): batch * nseg in padded mode (nseg >= 1,
+ * seg_tokens = 0); in packed mode (nseg = 0, seg_tokens >= 1) the bound
+ * nseq + ceil(seqlen / seg_tokens) on the number of segments, the row count
+ * of the packed segment arrays. 0 for any other combination. */
+int64_t mamba3_segment_rows(const mamba3_scan_args *fwd, int32_t nseg, int32_t seg_tokens);
+
+/* Segment table of a packed batch (ABI 1.5): writes rows + 1 entries of
+ * seg_cu (device int32, rows = nseq + ceil(seqlen / seg_tokens)) such that
+ * segment row r holds tokens [seg_cu[r], seg_cu[r+1]): the segments of
+ * state passing's packed mode in order, then empty rows at the end of the
+ * last sequence. Entries of cu_seqlens are clamped as the scan clamps them.
+ * cu_seqlens [nseq + 1] and seg_cu are device arrays, 4-byte aligned, not
+ * overlapping; nseq >= 0, seqlen >= 0, seg_tokens >= 1, rows + 1 <=
+ * INT32_MAX (MAMBA3_EINVAL otherwise). One kernel of one workgroup. */
+mamba3_status mamba3_segment_table(const int32_t *cu_seqlens, int32_t nseq, int32_t seqlen, int32_t seg_tokens,
+                                   int32_t *seg_cu, void *stream);
+
+/* The whole-sequence scan run as independent segments (ABI 1.4; packed
+ * batches ABI 1.5): steps 0-3 above, enqueued in order on one stream. Step 1
+ * runs as a state-only scan (the chunk-state updates alone: no C rows read,
+ * no scores or y formed). The result equals mamba3_scan_fwd's up to
+ * rounding; it costs about one and a half scans but multiplies the
+ * workgroups, which pays for a few long sequences.
  *
- * fwd        as for mamba3_scan_fwd (padded mode only; fwd.workspace must be
+ * fwd        as for mamba3_scan_fwd, padded or packed (fwd.workspace must be
  *            NULL / 0). y and h_out (if given) are written as by
  *            mamba3_scan_fwd; h_in, Bprev and xprev are honoured.
- * nseg       segments per sequence, >= 1, dividing seqlen; seqlen >= 1.
+ * nseg       padded: segments per sequence, >= 1, dividing seqlen; seqlen
+ *            >= 1. Packed: 0.
+ * seg_tokens packed: tokens per segment, >= 1 (each sequence is cut as in
+ *            state passing's packed mode). Padded: 0.
  * workspace  device memory of at least mamba3_scan_segmented_workspace_size
  *            bytes, 256-byte aligned, owned by the caller: the segments' zero-
- *            state final states and entering states (fp32) and their previous
- *            tokens. Its contents are scratch on return. It must not overlap
- *            any input or output.
+ *            state final states and entering states (fp32), their previous
+ *            tokens and (packed) the segment table. Its contents are scratch
+ *            on return. It must not overlap any input or output.
  * Errors as for mamba3_scan_fwd and mamba3_state_passing; MAMBA3_EUNSUPPORTED
  * also when no kernel exists for the segments' shape (chunk as in fwd). */
 typedef struct {
@@ -297,6 +331,7 @@ typedef struct {
     int32_t nseg;
     void *workspace;
     size_t workspace_bytes;
+    int32_t seg_tokens;   /* ABI 1.5 */
 } mamba3_scan_segmented_args;
 
 size_t mamba3_scan_segmented_workspace_size(const mamba3_scan_segmented_args *args);
@@ -316,7 +351,7 @@ mamba3_status mamba3_scan_segmented(const mamba3_scan_segmented_args *args, void
  *            aligned, held by every GPU the library runs on from the loading of
  *            its code until the process ends. MAMBA3_EWORKSPACE when
  *            mamba3_scan_segmented_workspace_size(args) exceeds it (about
- *            batch * nseg * H * N * P * 8 bytes).
+ *            rows * H * N * P * 8 bytes).
  * Races      every call on one GPU uses that GPU's one array: calls that may run
  *            at the same time on one GPU (different streams, or the same stream
  *            from host threads without ordering) race and give wrong results.

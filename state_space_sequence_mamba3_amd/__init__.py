@@ -62,18 +62,20 @@ class StatePassingArgs(ctypes.Structure):
     """Mirror of ``mamba3_state_passing_args``."""
     _fields_ = [
         ("fwd", ScanArgs), ("nseg", _i32), ("U", _vp), ("seg_h_in", _vp), ("seg_Bprev", _vp), ("seg_xprev", _vp),
-        ("h_out", _vp),
+        ("h_out", _vp), ("seg_tokens", _i32),
     ]
 
 
 class ScanSegmentedArgs(ctypes.Structure):
     """Mirror of ``mamba3_scan_segmented_args``."""
-    _fields_ = [("fwd", ScanArgs), ("nseg", _i32), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+    _fields_ = [("fwd", ScanArgs), ("nseg", _i32), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+                ("seg_tokens", _i32)]
 
 
 EXPORTS = ("mamba3_scan_validate", "mamba3_scan_workspace_size", "mamba3_scan_fwd", "mamba3_scan_bwd_validate",
            "mamba3_scan_bwd_workspace_size", "mamba3_scan_bwd", "mamba3_state_passing_validate",
-           "mamba3_state_passing", "mamba3_scan_segmented_workspace_size", "mamba3_scan_segmented_validate",
+           "mamba3_state_passing", "mamba3_segment_rows", "mamba3_segment_table",
+           "mamba3_scan_segmented_workspace_size", "mamba3_scan_segmented_validate",
            "mamba3_scan_segmented", "mamba3_scan_segmented_noalloc", "mamba3_decode_validate", "mamba3_decode_step",
            "mamba3_status_string", "mamba3_version")
 
@@ -112,6 +114,10 @@ def lib():
         l.mamba3_state_passing_validate.restype = ctypes.c_int
         l.mamba3_state_passing.argtypes = [ctypes.POINTER(StatePassingArgs), _vp]
         l.mamba3_state_passing.restype = ctypes.c_int
+        l.mamba3_segment_rows.argtypes = [ctypes.POINTER(ScanArgs), _i32, _i32]
+        l.mamba3_segment_rows.restype = ctypes.c_int64
+        l.mamba3_segment_table.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp]
+        l.mamba3_segment_table.restype = ctypes.c_int
         l.mamba3_scan_segmented_workspace_size.argtypes = [ctypes.POINTER(ScanSegmentedArgs)]
         l.mamba3_scan_segmented_workspace_size.restype = ctypes.c_size_t
         l.mamba3_scan_segmented_validate.argtypes = [ctypes.POINTER(ScanSegmentedArgs)]
@@ -273,24 +279,48 @@ def mamba3_state_passing_validate(args: StatePassingArgs) -> int:
     return lib().mamba3_state_passing_validate(ctypes.byref(args))
 
 
-def mamba3_state_passing(x, dt, lam, theta, B, C, A, *, nseg, U, h_in=None, Bprev=None, xprev=None, B_bias=None,
+def mamba3_segment_rows(args: ScanArgs, nseg: int = 0, seg_tokens: int = 0) -> int:
+    return lib().mamba3_segment_rows(ctypes.byref(args), int(nseg), int(seg_tokens))
+
+
+def mamba3_segment_table(cu_seqlens, seqlen: int, seg_tokens: int, stream=None):
+    """The segment table of a packed batch (int32 device tensor of rows + 1
+    entries, rows = nseq + ceil(seqlen / seg_tokens)): segment row r holds
+    tokens [t[r], t[r+1])."""
+    import torch
+    nseq = int(cu_seqlens.numel()) - 1
+    rows = nseq + (int(seqlen) + int(seg_tokens) - 1) // int(seg_tokens) if seg_tokens >= 1 else 0
+    seg_cu = torch.empty((max(rows, 0) + 1,), dtype=torch.int32, device=cu_seqlens.device)
+    st = lib().mamba3_segment_table(_ptr(cu_seqlens), nseq, int(seqlen), int(seg_tokens), _ptr(seg_cu),
+                                    _stream(stream))
+    if st != MAMBA3_OK:
+        raise Mamba3Error(st, "mamba3_segment_table")
+    return seg_cu
+
+
+def mamba3_state_passing(x, dt, lam, theta, B, C, A, *, nseg=0, U, h_in=None, Bprev=None, xprev=None, B_bias=None,
                          C_bias=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5, want_state=True,
-                         stream=None):
-    """The state entering each of the nseg segments of every sequence, from U
-    ([batch*nseg,H,N,P], the segments scanned from a zero state with no
-    previous token). Returns (seg_h_in [batch*nseg,H,N,P] fp32, seg_Bprev,
-    seg_xprev (token before each segment), h_out [batch,H,N,P] or None)."""
+                         cu_seqlens=None, seg_tokens=0, stream=None):
+    """The state entering each segment row, from U ([rows,H,N,P], the
+    segments scanned from a zero state with no previous token). Padded
+    batches: nseg segments per sequence, rows = batch*nseg. Packed batches
+    (cu_seqlens): segments of seg_tokens tokens, rows as mamba3_segment_rows.
+    Returns (seg_h_in [rows,H,N,P] fp32, seg_Bprev, seg_xprev (token before
+    each segment), h_out [S,H,N,P] or None)."""
     import torch
     b, L, H, R, P = x.shape
     G, N = B.shape[2], B.shape[4]
-    SR = b * nseg
+    fwd = scan_args(x, dt, lam, theta, B, C, A, None, y=None, h_in=h_in, h_out=None, Bprev=Bprev, xprev=xprev,
+                    cu_seqlens=cu_seqlens, B_bias=B_bias, C_bias=C_bias, bc_norm=bc_norm, bc_eps=bc_eps,
+                    A_tok=A_tok, lam_fixed=lam_fixed)
+    SR = mamba3_segment_rows(fwd, nseg, seg_tokens)
+    S = int(cu_seqlens.numel()) - 1 if cu_seqlens is not None else b
     seg_h = torch.empty((SR, H, N, P), dtype=torch.float32, device=x.device)
     seg_B = torch.empty((SR, G, R, N), dtype=x.dtype, device=x.device)
     seg_x = torch.empty((SR, H, R, P), dtype=x.dtype, device=x.device)
-    h_out = torch.empty((b, H, N, P), dtype=torch.float32, device=x.device) if want_state else None
-    fwd = scan_args(x, dt, lam, theta, B, C, A, None, y=None, h_in=h_in, h_out=None, Bprev=Bprev, xprev=xprev,
-                    B_bias=B_bias, C_bias=C_bias, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=A_tok, lam_fixed=lam_fixed)
-    a = StatePassingArgs(fwd, int(nseg), _ptr(U), _ptr(seg_h), _ptr(seg_B), _ptr(seg_x), _ptr(h_out))
+    h_out = torch.empty((S, H, N, P), dtype=torch.float32, device=x.device) if want_state else None
+    a = StatePassingArgs(fwd, int(nseg), _ptr(U), _ptr(seg_h), _ptr(seg_B), _ptr(seg_x), _ptr(h_out),
+                         int(seg_tokens))
     st = lib().mamba3_state_passing(ctypes.byref(a), _stream(stream))
     if st != MAMBA3_OK:
         raise Mamba3Error(st, "mamba3_state_passing")
@@ -301,22 +331,25 @@ def mamba3_scan_segmented_validate(args: ScanSegmentedArgs) -> int:
     return lib().mamba3_scan_segmented_validate(ctypes.byref(args))
 
 
-def mamba3_scan_segmented(x, dt, lam, theta, B, C, A, D=None, *, nseg, y=None, h_in=None, h_out=None, Bprev=None,
+def mamba3_scan_segmented(x, dt, lam, theta, B, C, A, D=None, *, nseg=0, y=None, h_in=None, h_out=None, Bprev=None,
                           xprev=None, chunk=64, want_state=True, workspace=None, stream=None, B_bias=None,
-                          C_bias=None, z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5):
-    """mamba3_scan_segmented: the whole-sequence scan run as batch*nseg
-    independent segments (scan, state passing, scan, all in the library).
-    Same results as mamba3_scan_fwd up to rounding. The workspace is allocated
-    when not given. Returns (y, h_out)."""
+                          C_bias=None, z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5,
+                          cu_seqlens=None, seg_tokens=0):
+    """mamba3_scan_segmented: the whole-sequence scan run as independent
+    segments (scan, state passing, scan, all in the library): nseg segments
+    per sequence of a padded batch, or segments of seg_tokens tokens of a
+    packed batch (cu_seqlens). Same results as mamba3_scan_fwd up to rounding.
+    The workspace is allocated when not given. Returns (y, h_out)."""
     import torch
     if y is None:
         y = torch.empty_like(x)
     if h_out is None and want_state:
-        h_out = torch.empty((x.shape[0], x.shape[2], B.shape[4], x.shape[4]), dtype=torch.float32, device=x.device)
+        S = int(cu_seqlens.numel()) - 1 if cu_seqlens is not None else x.shape[0]
+        h_out = torch.empty((S, x.shape[2], B.shape[4], x.shape[4]), dtype=torch.float32, device=x.device)
     fwd = scan_args(x, dt, lam, theta, B, C, A, D, y=y, h_in=h_in, h_out=h_out, Bprev=Bprev, xprev=xprev,
-                    chunk=chunk, B_bias=B_bias, C_bias=C_bias, z=z, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=A_tok,
-                    lam_fixed=lam_fixed)
-    a = ScanSegmentedArgs(fwd, int(nseg), None, 0)
+                    cu_seqlens=cu_seqlens, chunk=chunk, B_bias=B_bias, C_bias=C_bias, z=z, bc_norm=bc_norm,
+                    bc_eps=bc_eps, A_tok=A_tok, lam_fixed=lam_fixed)
+    a = ScanSegmentedArgs(fwd, int(nseg), None, 0, int(seg_tokens))
     need = lib().mamba3_scan_segmented_workspace_size(ctypes.byref(a))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
@@ -327,9 +360,10 @@ def mamba3_scan_segmented(x, dt, lam, theta, B, C, A, D=None, *, nseg, y=None, h
     return y, h_out
 
 
-def mamba3_scan_segmented_noalloc(x, dt, lam, theta, B, C, A, D=None, *, nseg, y=None, h_in=None, h_out=None,
+def mamba3_scan_segmented_noalloc(x, dt, lam, theta, B, C, A, D=None, *, nseg=0, y=None, h_in=None, h_out=None,
                                   Bprev=None, xprev=None, chunk=64, want_state=True, stream=None, B_bias=None,
-                                  C_bias=None, z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5):
+                                  C_bias=None, z=None, bc_norm=False, bc_eps=1e-5, A_tok=None, lam_fixed=0.5,
+                                  cu_seqlens=None, seg_tokens=0):
     """mamba3_scan_segmented_noalloc: the segmented scan with the library's own workspace (the
     library allocates nothing; y and h_out are allocated here by torch when not given, as by the
     other entry points). Returns (y, h_out)."""
@@ -337,11 +371,12 @@ def mamba3_scan_segmented_noalloc(x, dt, lam, theta, B, C, A, D=None, *, nseg, y
     if y is None:
         y = torch.empty_like(x)
     if h_out is None and want_state:
-        h_out = torch.empty((x.shape[0], x.shape[2], B.shape[4], x.shape[4]), dtype=torch.float32, device=x.device)
+        S = int(cu_seqlens.numel()) - 1 if cu_seqlens is not None else x.shape[0]
+        h_out = torch.empty((S, x.shape[2], B.shape[4], x.shape[4]), dtype=torch.float32, device=x.device)
     fwd = scan_args(x, dt, lam, theta, B, C, A, D, y=y, h_in=h_in, h_out=h_out, Bprev=Bprev, xprev=xprev,
-                    chunk=chunk, B_bias=B_bias, C_bias=C_bias, z=z, bc_norm=bc_norm, bc_eps=bc_eps, A_tok=A_tok,
-                    lam_fixed=lam_fixed)
-    a = ScanSegmentedArgs(fwd, int(nseg), None, 0)
+                    cu_seqlens=cu_seqlens, chunk=chunk, B_bias=B_bias, C_bias=C_bias, z=z, bc_norm=bc_norm,
+                    bc_eps=bc_eps, A_tok=A_tok, lam_fixed=lam_fixed)
+    a = ScanSegmentedArgs(fwd, int(nseg), None, 0, int(seg_tokens))
     st = lib().mamba3_scan_segmented_noalloc(ctypes.byref(a), _stream(stream))
     if st != MAMBA3_OK:
         raise Mamba3Error(st, "mamba3_scan_segmented_noalloc")

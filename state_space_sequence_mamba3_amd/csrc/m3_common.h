@@ -41,10 +41,10 @@ bool scan_bf16_supported(int N, int P, int R, int Q);
 // The panel kernel of the rank-4 shapes (plain path: no fused prologue / epilogue, no variants).
 bool scan_mimo_supported(const mamba3_scan_args *a);
 mamba3_status launch_scan_mimo(const mamba3_scan_args *a, hipStream_t st);
-// State-only bf16 scan (a->y NULL) that may also write, for padded batches only, the state
-// entering every chunk into ws_state ([S * ceil(seqlen / chunk)][H][N][P] fp32: the backward's
-// chunk states) and each row's decay and angle sums into seg_sums (the first K + 1 floats of
-// each [S][H][N][P] block: the segment sums of state passing). scan_bf16_states_supported
+// State-only bf16 scan (a->y NULL) that may also write the state entering every chunk into
+// ws_state (padded batches only: [S * ceil(seqlen / chunk)][H][N][P] fp32, the backward's chunk
+// states) and each sequence's decay and angle sums into seg_sums (the first K + 1 floats of each
+// [S][H][N][P] block: the segment sums of state passing). scan_bf16_states_supported
 // covers the scan's shapes and the backward's chunks.
 bool scan_bf16_states_supported(int N, int P, int R, int Q);
 mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, float *ws_state, float *seg_sums, hipStream_t st);
@@ -57,5 +57,10 @@ bool decode_supported(int N, int P, int R, int dtype);
 // sums_staged: the segment sums are already in seg_h_in (written by the state-only scan)
 mamba3_status launch_state_passing(const mamba3_state_passing_args *a, hipStream_t st, bool sums_staged = false);
 size_t state_passing_lds_bytes(int N, int P, int R);
+// packed batches: the bound nseq + ceil(seqlen / seg_tokens) on their segment rows (0 for
+// seg_tokens < 1), and the kernel writing their segment table (rows + 1 entries)
+int64_t segment_rows_packed(int64_t nseq, int64_t seqlen, int64_t seg_tokens);
+mamba3_status launch_segment_table(const int32_t *cu, int32_t nseq, int32_t seqlen, int32_t seg_tokens,
+                                   int32_t *seg_cu, hipStream_t st);
 
 }  // namespace m3

@@ -52,7 +52,33 @@ const char *mamba3_status_string(mamba3_status s) {
     return "unknown status";
 }
 
-int32_t mamba3_version(void) { return 10400; }
+int32_t mamba3_version(void) { return 10500; }
+
+// Segment rows: batch * nseg (padded, nseg >= 1, seg_tokens = 0) or the packed bound (nseg = 0,
+// seg_tokens >= 1); 0 for anything else.
+static int64_t seg_rows(const mamba3_scan_args *f, int32_t nseg, int32_t seg_tokens) {
+    if (!f) return 0;
+    if (f->cu_seqlens) {
+        if (nseg != 0 || seg_tokens < 1 || f->nseq < 0 || f->seqlen < 0) return 0;
+        return m3::segment_rows_packed(f->nseq, f->seqlen, seg_tokens);
+    }
+    if (seg_tokens != 0 || nseg < 1 || f->batch < 0) return 0;
+    return (int64_t)f->batch * nseg;
+}
+
+int64_t mamba3_segment_rows(const mamba3_scan_args *fwd, int32_t nseg, int32_t seg_tokens) {
+    return seg_rows(fwd, nseg, seg_tokens);
+}
+
+mamba3_status mamba3_segment_table(const int32_t *cu_seqlens, int32_t nseq, int32_t seqlen, int32_t seg_tokens,
+                                   int32_t *seg_cu, void *stream) {
+    if (!cu_seqlens || !seg_cu || nseq < 0 || seqlen < 0 || seg_tokens < 1) return MAMBA3_EINVAL;
+    if (!aligned4(cu_seqlens) || !aligned4(seg_cu)) return MAMBA3_EALIGN;
+    const int64_t rows = m3::segment_rows_packed(nseq, seqlen, seg_tokens);
+    if (rows + 1 > INT32_MAX) return MAMBA3_EINVAL;
+    if (overlaps(span(cu_seqlens, (int64_t)nseq + 1, 4), span(seg_cu, rows + 1, 4))) return MAMBA3_EINVAL;
+    return m3::launch_segment_table(cu_seqlens, nseq, seqlen, seg_tokens, seg_cu, (hipStream_t)stream);
+}
 
 // Every check of the scan arguments except the availability of a forward kernel. need_y = false
 // for callers that do not write y (y must then be NULL).
@@ -227,10 +253,16 @@ mamba3_status mamba3_state_passing_validate(const mamba3_state_passing_args *sp)
     f.D = nullptr;
     mamba3_status st = scan_args_check(&f, false);
     if (st != MAMBA3_OK) return st;
-    if (f.cu_seqlens) return MAMBA3_EUNSUPPORTED;   // padded sequences only
-    if (sp->nseg < 1 || f.seqlen < 1 || f.seqlen % sp->nseg) return MAMBA3_EINVAL;
-    const int64_t b = f.batch, T = b * f.seqlen, SR = b * sp->nseg;
-    if (SR * f.nheads > INT32_MAX) return MAMBA3_EINVAL;
+    const bool packed = f.cu_seqlens != nullptr;
+    if (packed) {
+        if (sp->nseg != 0 || sp->seg_tokens < 1) return MAMBA3_EINVAL;
+    } else if (sp->seg_tokens != 0 || sp->nseg < 1 || f.seqlen < 1 || f.seqlen % sp->nseg) {
+        return MAMBA3_EINVAL;
+    }
+    // S: sequences; SR: segment rows
+    const int64_t b = packed ? f.nseq : f.batch, T = (int64_t)f.batch * f.seqlen;
+    const int64_t SR = seg_rows(&f, sp->nseg, sp->seg_tokens);
+    if (SR * f.nheads > INT32_MAX || SR + 1 > INT32_MAX) return MAMBA3_EINVAL;
     if (b > 0 && (!sp->U || !sp->seg_h_in || !sp->seg_Bprev || !sp->seg_xprev)) return MAMBA3_EINVAL;
     const void *al16[] = {sp->U, sp->seg_h_in, sp->seg_Bprev, sp->seg_xprev, sp->h_out};
     for (const void *q : al16)
@@ -244,7 +276,7 @@ mamba3_status mamba3_state_passing_validate(const mamba3_state_passing_args *sp)
                    span(f.theta, T * Gth * (N / 2), es), span(f.B, T * G * N * R, es), span(f.A, H, 4),
                    span(f.h_in, b * H * N * P, 4), span(f.Bprev, b * G * N * R, es),
                    span(f.xprev, b * H * P * R, es), span(f.B_bias, H * N, 4), span(f.A_tok, T * H, es),
-                   span(sp->U, SR * H * N * P, 4)};
+                   span(sp->U, SR * H * N * P, 4), span(f.cu_seqlens, packed ? f.nseq + 1 : 0, 4)};
     const int nout = sizeof outs / sizeof outs[0];
     for (int i = 0; i < nout; i++) {
         for (Range r : ins) {
@@ -265,16 +297,16 @@ mamba3_status mamba3_state_passing(const mamba3_state_passing_args *sp, void *st
     return m3::launch_state_passing(sp, (hipStream_t)stream);
 }
 
-// Segmented scan: the workspace holds U and the entering states [b*nseg, H, N, P] fp32, then the
-// previous tokens [b*nseg, G, R, N] and [b*nseg, H, R, P] in the token dtype (each region
-// 256-byte aligned).
+// Segmented scan: the workspace holds U and the entering states [rows, H, N, P] fp32, then the
+// previous tokens [rows, G, R, N] and [rows, H, R, P] in the token dtype, then (packed batches) the
+// segment table [rows + 1] int32 (each region 256-byte aligned).
 namespace {
 struct SegWs {
-    size_t U, h, B, x, total;
+    size_t U, h, B, x, cu, total;
 };
 SegWs seg_ws(const mamba3_scan_segmented_args *a) {
     const mamba3_scan_args &f = a->fwd;
-    const int64_t SR = (int64_t)f.batch * (a->nseg > 0 ? a->nseg : 0);
+    const int64_t SR = seg_rows(&f, a->nseg, a->seg_tokens);
     const int64_t H = f.nheads, G = f.ngroups, P = f.headdim, N = f.dstate, R = f.rank;
     const int64_t es = f.dtype == MAMBA3_BF16 ? 2 : 4;
     auto al = [](int64_t v) { return (size_t)((v + 255) / 256 * 256); };
@@ -284,6 +316,7 @@ SegWs seg_ws(const mamba3_scan_segmented_args *a) {
     w.h = o; o += al(SR * H * N * P * 4);
     w.B = o; o += al(SR * G * R * N * es);
     w.x = o; o += al(SR * H * R * P * es);
+    w.cu = o; o += f.cu_seqlens ? al((SR + 1) * 4) : 0;
     w.total = o;
     return w;
 }
@@ -295,9 +328,14 @@ void seg_calls(const mamba3_scan_segmented_args *a, mamba3_scan_args *pass1, mam
     char *ws = (char *)a->workspace;
     float *U = (float *)(ws + w.U), *segh = (float *)(ws + w.h);
     void *segB = ws + w.B, *segx = ws + w.x;
-    mamba3_scan_args rows = f;   // the segments as independent rows of seqlen / nseg tokens
-    rows.batch = f.batch * a->nseg;
-    rows.seqlen = a->nseg > 0 ? f.seqlen / a->nseg : 0;
+    mamba3_scan_args rows = f;
+    if (f.cu_seqlens) {           // the segments as a packed batch of their own (the segment table)
+        rows.cu_seqlens = (const int32_t *)(ws + w.cu);
+        rows.nseq = (int32_t)seg_rows(&f, a->nseg, a->seg_tokens);
+    } else {                      // the segments as independent rows of seqlen / nseg tokens
+        rows.batch = f.batch * a->nseg;
+        rows.seqlen = a->nseg > 0 ? f.seqlen / a->nseg : 0;
+    }
     rows.workspace = nullptr;
     rows.workspace_bytes = 0;
     *pass1 = rows;                // from zero states, no previous token, state only: U in h_out
@@ -313,6 +351,7 @@ void seg_calls(const mamba3_scan_segmented_args *a, mamba3_scan_args *pass1, mam
     sp->fwd.z = nullptr;
     sp->fwd.D = nullptr;
     sp->nseg = a->nseg;
+    sp->seg_tokens = a->seg_tokens;
     sp->U = U;
     sp->seg_h_in = segh;
     sp->seg_Bprev = segB;
@@ -327,9 +366,10 @@ void seg_calls(const mamba3_scan_segmented_args *a, mamba3_scan_args *pass1, mam
 }  // namespace
 
 size_t mamba3_scan_segmented_workspace_size(const mamba3_scan_segmented_args *a) {
-    if (!a || a->nseg < 1 || a->fwd.batch < 0 || a->fwd.nheads < 1 || a->fwd.headdim < 1 || a->fwd.dstate < 2 ||
+    if (!a || a->fwd.batch < 0 || a->fwd.nheads < 1 || a->fwd.headdim < 1 || a->fwd.dstate < 2 ||
         a->fwd.rank < 1 || a->fwd.ngroups < 1)
         return 0;
+    if (seg_rows(&a->fwd, a->nseg, a->seg_tokens) < 1) return 0;
     return seg_ws(a).total;
 }
 
@@ -339,14 +379,19 @@ mamba3_status mamba3_scan_segmented_validate(const mamba3_scan_segmented_args *a
     if (f.workspace || f.workspace_bytes) return MAMBA3_EINVAL;
     mamba3_status st = scan_args_check(&f);
     if (st != MAMBA3_OK) return st;
-    if (f.cu_seqlens) return MAMBA3_EUNSUPPORTED;
-    if (a->nseg < 1 || f.seqlen < 1 || f.seqlen % a->nseg) return MAMBA3_EINVAL;
+    if (f.cu_seqlens) {
+        if (a->nseg != 0 || a->seg_tokens < 1) return MAMBA3_EINVAL;
+        const int64_t SR = seg_rows(&f, 0, a->seg_tokens);
+        if (SR * f.nheads > INT32_MAX || SR + 1 > INT32_MAX) return MAMBA3_EINVAL;
+    } else if (a->seg_tokens != 0 || a->nseg < 1 || f.seqlen < 1 || f.seqlen % a->nseg) {
+        return MAMBA3_EINVAL;
+    }
     const size_t need = seg_ws(a).total;
     if (a->workspace_bytes < need || !a->workspace) return MAMBA3_EWORKSPACE;
     if ((uintptr_t)a->workspace & 255u) return MAMBA3_EALIGN;
     // the workspace against every input and output of the whole-sequence call
     const int64_t es = f.dtype == MAMBA3_BF16 ? 2 : 4;
-    const int64_t S = f.batch, T = (int64_t)f.batch * f.seqlen;
+    const int64_t S = f.cu_seqlens ? f.nseq : f.batch, T = (int64_t)f.batch * f.seqlen;
     const int64_t H = f.nheads, G = f.ngroups, P = f.headdim, N = f.dstate, R = f.rank;
     const int64_t Gth = f.theta_groups ? f.theta_groups : H;
     const Range wsr = span(a->workspace, (int64_t)a->workspace_bytes, 1);
@@ -355,7 +400,7 @@ mamba3_status mamba3_scan_segmented_validate(const mamba3_scan_segmented_args *a
                    span(f.h_in, S * H * N * P, 4), span(f.Bprev, S * G * N * R, es), span(f.xprev, S * H * P * R, es),
                    span(f.h_out, S * H * N * P, 4), span(f.B_bias, H * N, 4), span(f.C_bias, H * N, 4),
                    span(f.z, T * H * P * R, es), span(f.A_tok, T * H, es), span(f.y, T * H * P * R, es),
-                   span(f.A, H, 4), span(f.D, H, 4)};
+                   span(f.A, H, 4), span(f.D, H, 4), span(f.cu_seqlens, f.cu_seqlens ? f.nseq + 1 : 0, 4)};
     for (Range r : all)
         if (overlaps(wsr, r)) return MAMBA3_EINVAL;
     // each call's own checks (kernel availability for the segment rows included)
@@ -374,6 +419,11 @@ mamba3_status mamba3_scan_segmented(const mamba3_scan_segmented_args *a, void *s
     mamba3_scan_args p1, p2;
     mamba3_state_passing_args sp;
     seg_calls(a, &p1, &sp, &p2);
+    // packed: the segment rows' token ranges first
+    if (a->fwd.cu_seqlens &&
+        (st = m3::launch_segment_table(a->fwd.cu_seqlens, a->fwd.nseq, a->fwd.seqlen, a->seg_tokens,
+                                       (int32_t *)p1.cu_seqlens, (hipStream_t)stream)) != MAMBA3_OK)
+        return st;
     // bf16: the state-only first pass also stages the segment sums that state passing reads
     const bool staged = p1.dtype == MAMBA3_BF16;
     if (staged) {

@@ -93,9 +93,9 @@ struct BfParams {
     // state-only scans: the state entering every chunk, [S * chunks][H][N][P] fp32 (the
     // backward's chunk-state layout), or NULL
     float *ws_state;
-    // state-only scans of padded rows: sum_t dt_t A_t and sum_t dt_t theta_t[k] over each row,
-    // written to the first K + 1 floats of its [S][H][N][P] block (the segment sums that state
-    // passing reads), or NULL
+    // state-only scans: sum_t dt_t A_t and sum_t dt_t theta_t[k] over each sequence, written to
+    // the first K + 1 floats of its [S][H][N][P] block (the segment sums that state passing
+    // reads), or NULL
     float *seg_sums;
 };
 
@@ -1118,7 +1118,7 @@ bool scan_bf16_states_supported(int N, int P, int R, int Q) {
 
 mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, float *ws_state, float *seg_sums, hipStream_t st) {
     if (a->y) return MAMBA3_EINVAL;
-    if ((ws_state || seg_sums) && a->cu_seqlens) return MAMBA3_EUNSUPPORTED;
+    if (ws_state && a->cu_seqlens) return MAMBA3_EUNSUPPORTED;
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
     // the EPI instantiations also carry the variants (per-token A, fixed lambda); the gate and
     // the C bias act on outputs only

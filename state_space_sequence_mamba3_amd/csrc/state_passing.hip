@@ -19,6 +19,14 @@
 // segment, and applies the affine map. The state update is elementwise
 // per (pair, column), one thread per element; U and the states are read and
 // written as whole rows of P consecutive floats.
+//
+// Packed batches: sequence s (tokens [cu[s], cu[s+1])) is cut into
+// max(1, ceil(len / L)) segments of L tokens, and its segments are the rows
+// base_s .. base_s + n_s - 1, base_s counting the segments of the sequences
+// before it. k_segment_table writes the rows' token ranges as a cu table (so
+// the scans can take the rows as a packed batch); k_state_passing finds
+// base_s itself from cu and reduces each segment's sums in the walk unless
+// the state-only scan staged them.
 #include "m3_common.h"
 
 namespace m3 {
@@ -31,13 +39,17 @@ struct SPParams {
     int32_t seqlen, nseg, H, G, P, N, R, Gth;
     int32_t norm;
     float eps, lam_fixed;
+    // packed batches: the sequence table, its length, tokens per segment, the segment rows
+    const int32_t *cu;
+    int32_t nseq, seg_tokens, rows;
+    int32_t sums_inline;   // 1: k_state_passing reduces each segment's sums itself
 };
 
 constexpr int kSPThreads = 256;
 
 // LDS layout (floats)
 struct SPLayout {
-    int hs, phi, bl, xl, misc, total;
+    int hs, phi, bl, xl, misc, sums, total;
 };
 __host__ __device__ inline SPLayout sp_layout(int N, int P, int R) {
     SPLayout L;
@@ -48,28 +60,24 @@ __host__ __device__ inline SPLayout sp_layout(int N, int P, int R) {
     L.bl = o; o += R * N;
     L.xl = o; o += R * P;
     L.misc = o; o += 4;
+    L.sums = o; o += K + 1;   // the segment's sum of dt A, then its angle sums
     L.total = o;
     return L;
 }
 
 size_t state_passing_lds_bytes(int N, int P, int R) { return (size_t)sp_layout(N, P, R).total * sizeof(float); }
 
-// Per (segment row, head): S = sum_t dt_t A_t and Phi[k] = sum_t dt_t theta_t[k] over the
-// segment's tokens, staged in the first K + 1 floats of the segment's seg_h_in block (which
-// k_state_passing reads before it writes the entering state there). Every (row, head) runs in
-// parallel; each thread sums a strided set of tokens, then the partials are added in index order.
+// S = sum_t dt_t A_t and Phi[k] = sum_t dt_t theta_t[k] over tokens [t0, t0 + Ls) of head h, into
+// out[0] and out[1 + k] (global memory or LDS). The whole block of kSPThreads takes part and
+// every thread must call it: each thread sums a strided set of tokens, then the partials are
+// added in index order (a fixed order).
 template <typename T>
-__global__ __launch_bounds__(kSPThreads) void k_segment_sums(SPParams p) {
+__device__ void segment_sums_block(const SPParams &p, int64_t t0, int Ls, int h, float *out) {
     __shared__ float part[kSPThreads], spart[kSPThreads];
     const int H = p.H, K = p.N / 2, tid = threadIdx.x, NT = kSPThreads;
     const int TL = K >= NT ? 1 : NT / K;
-    const int64_t rh = blockIdx.x;                  // row * H + h
-    const int h = (int)(rh % H), gq = h / (H / p.Gth);
-    const int64_t row = rh / H, s = row / p.nseg, k = row % p.nseg;
-    const int Ls = p.seqlen / p.nseg;
-    const int64_t t0 = s * p.seqlen + k * Ls;
+    const int gq = h / (H / p.Gth);
     const T *dt = (const T *)p.dt, *th = (const T *)p.theta;
-    float *out = p.seg_h + rh * (int64_t)p.N * p.P;
     float a = 0.f;
 #pragma unroll 8
     for (int t = tid; t < Ls; t += NT) {
@@ -131,6 +139,73 @@ __global__ __launch_bounds__(kSPThreads) void k_segment_sums(SPParams p) {
         for (int jj = 0; jj < NT; jj++) c += spart[jj];
         out[0] = c;
     }
+    __syncthreads();   // the partial buffers may be reused at once
+}
+
+// Per (segment row, head) of a padded batch: the segment's sums, staged in the first K + 1 floats
+// of the segment's seg_h_in block (which k_state_passing reads before it writes the entering
+// state there). Every (row, head) runs in parallel.
+template <typename T>
+__global__ __launch_bounds__(kSPThreads) void k_segment_sums(SPParams p) {
+    const int64_t rh = blockIdx.x;                  // row * H + h
+    const int h = (int)(rh % p.H);
+    const int64_t row = rh / p.H, s = row / p.nseg, k = row % p.nseg;
+    const int Ls = p.seqlen / p.nseg;
+    segment_sums_block<T>(p, s * p.seqlen + k * Ls, Ls, h, p.seg_h + rh * (int64_t)p.N * p.P);
+}
+
+// Tokens [a, b) of packed sequence i, entries clamped to [0, seqlen] as the scans clamp them.
+__device__ __forceinline__ void seq_bounds(const int32_t *cu, int i, int seqlen, int &a, int &b) {
+    a = min(max(cu[i], 0), seqlen);
+    b = min(max(cu[i + 1], a), seqlen);
+}
+// Segments of a packed sequence of len tokens (one, empty, for an empty sequence).
+__device__ __forceinline__ int seq_segments(int len, int L) { return max(1, (int)(((int64_t)len + L - 1) / L)); }
+
+// The segment table of a packed batch: seg_cu[r] = first token of segment row r, for the rows of
+// every sequence in order, then the end of the last sequence up to seg_cu[rows] (empty rows). One
+// workgroup: the sequences in blocks of 1024, a block-wide scan of their segment counts, and a
+// running carry. A write is skipped past the rows' bound (reachable only with entries that are not
+// non-decreasing).
+constexpr int kTabThreads = 1024;
+__global__ __launch_bounds__(kTabThreads) void k_segment_table(const int32_t *cu, int nseq, int seqlen, int L,
+                                                               int32_t *seg_cu, int rows) {
+    __shared__ int wsum[kTabThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int carry = 0;
+    for (int i0 = 0; i0 < nseq; i0 += kTabThreads) {
+        const int i = i0 + tid;
+        int a = 0, b = 0, n = 0;
+        if (i < nseq) {
+            seq_bounds(cu, i, seqlen, a, b);
+            n = seq_segments(b - a, L);
+        }
+        int incl = n;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int woff = 0, tot = 0;
+        for (int w = 0; w < kTabThreads / 64; w++) {
+            woff += (w < wave) ? wsum[w] : 0;
+            tot += wsum[w];
+        }
+        const int64_t first = (int64_t)carry + woff + incl - n;
+        for (int k = 0; k < n; k++)
+            if (first + k < rows) seg_cu[first + k] = a + k * L;   // a + k L < b <= seqlen
+        carry = (int)min((int64_t)carry + tot, (int64_t)rows);
+        __syncthreads();   // wsum is rewritten by the next block
+    }
+    int endv = 0;
+    if (nseq > 0) {
+        int a, b;
+        seq_bounds(cu, nseq - 1, seqlen, a, b);
+        endv = b;
+    }
+    for (int r = carry + tid; r <= rows; r += kTabThreads) seg_cu[r] = endv;
 }
 
 // One workgroup per (sequence, head): the chain over the sequence's segments. With PREF (at most
@@ -143,17 +218,53 @@ __global__ __launch_bounds__(kSPThreads) void k_state_passing(SPParams p) {
     const int N = p.N, P = p.P, R = p.R, H = p.H, G = p.G, K = N / 2;
     const SPLayout L = sp_layout(N, P, R);
     float *Hs = smem + L.hs, *PHI = smem + L.phi, *BL = smem + L.bl, *XL = smem + L.xl, *MISC = smem + L.misc;
+    float *SUMS = smem + L.sums;
     const int tid = threadIdx.x, NT = kSPThreads;
     const int s = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
-    const int Ls = p.seqlen / p.nseg;
     const int64_t NP = (int64_t)N * P;
     const T *dt = (const T *)p.dt;
 
+    // the sequence's tokens, segment length and count, and first segment row
+    int64_t a0, len, base;
+    int Ls, nsg;
+    if (p.cu) {
+        int a, b;
+        seq_bounds(p.cu, s, p.seqlen, a, b);
+        a0 = a;
+        len = b - a;
+        Ls = p.seg_tokens;
+        nsg = seq_segments(b - a, Ls);
+        // base: the segments of the sequences before s (per-thread strided counts, then a
+        // block reduction)
+        __shared__ int cnt[kSPThreads];
+        int c = 0;
+        for (int j = tid; j < s; j += NT) {
+            int aj, bj;
+            seq_bounds(p.cu, j, p.seqlen, aj, bj);
+            c += seq_segments(bj - aj, Ls);
+        }
+        cnt[tid] = c;
+        __syncthreads();
+        int64_t tot = 0;
+        for (int j = 0; j < NT; j++) tot += cnt[j];
+        base = tot;
+    } else {
+        a0 = (int64_t)s * p.seqlen;
+        len = p.seqlen;
+        Ls = p.seqlen / p.nseg;
+        nsg = p.nseg;
+        base = (int64_t)s * p.nseg;
+    }
+    // rows past the bound (reachable only with a sequence table that is not non-decreasing) are
+    // neither read nor written
+    if (p.cu) nsg = (int)max((int64_t)0, min((int64_t)nsg, (int64_t)p.rows - base));
+
     for (int64_t e = tid; e < NP; e += NT) Hs[e] = p.h_in ? p.h_in[((int64_t)s * H + h) * NP + e] : 0.f;
 
-    for (int k = 0; k < p.nseg; k++) {
-        const int64_t t0 = (int64_t)s * p.seqlen + (int64_t)k * Ls;   // first token of the segment
-        const int64_t row = (int64_t)s * p.nseg + k;                   // segment row
+    for (int k = 0; k < nsg; k++) {
+        const int64_t t0 = a0 + (int64_t)k * Ls;                       // first token of the segment
+        const int tl = (int)min((int64_t)Ls, len - (int64_t)k * Ls);   // its tokens (0: empty sequence)
+        const int64_t row = base + k;                                  // segment row
         float *out = p.seg_h + (row * H + h) * NP;
         const float *Uk = p.U + (row * H + h) * NP;
         float u0r[PREF ? PREF_MAX : 1], u1r[PREF ? PREF_MAX : 1];
@@ -168,8 +279,15 @@ __global__ __launch_bounds__(kSPThreads) void k_state_passing(SPParams p) {
                 }
             }
         }
-        // the segment's sums, staged by k_segment_sums in this block of seg_h_in
-        for (int i = tid; i < K; i += NT) sincosf(out[1 + i], &PHI[K + i], &PHI[i]);
+        // the segment's sums: reduced here, or staged in this block of seg_h_in (by k_segment_sums
+        // or the state-only scan)
+        if (p.sums_inline) {
+            segment_sums_block<T>(p, t0, tl, h, SUMS);
+        } else {
+            for (int i = tid; i <= K; i += NT) SUMS[i] = out[i];
+            __syncthreads();
+        }
+        for (int i = tid; i < K; i += NT) sincosf(SUMS[1 + i], &PHI[K + i], &PHI[i]);
         // the token before the segment: the previous segment's last token, or the sequence's own
         const bool has_prev = k > 0 || p.Bprev;
         const T *bsrc = k > 0 ? (const T *)p.B + ((t0 - 1) * G + g) * R * N
@@ -187,11 +305,16 @@ __global__ __launch_bounds__(kSPThreads) void k_state_passing(SPParams p) {
             ((T *)p.seg_x)[(row * H + h) * R * P + e] = v;
         }
         if (tid == 0) {
-            MISC[0] = expf(out[0]);
-            const float lam = p.lam ? to_f(((const T *)p.lam)[t0 * H + h]) : p.lam_fixed;
-            MISC[1] = has_prev ? (1.f - lam) * to_f(dt[t0 * H + h]) : 0.f;   // delta of the first token
+            MISC[0] = expf(SUMS[0]);
+            // delta of the first token (none in an empty segment, which leaves the state as it is)
+            float d0 = 0.f;
+            if (has_prev && tl > 0) {
+                const float lam = p.lam ? to_f(((const T *)p.lam)[t0 * H + h]) : p.lam_fixed;
+                d0 = (1.f - lam) * to_f(dt[t0 * H + h]);
+            }
+            MISC[1] = d0;
         }
-        __syncthreads();   // the staged sums are read: the block may now be overwritten
+        __syncthreads();   // the sums are read: the block of seg_h_in may now be overwritten
         // prologue on the folded previous token: unit-RMS columns and the head's bias, as the scan does
         if (has_prev && (p.norm || p.Bb)) {
             if (tid < R) {
@@ -251,11 +374,16 @@ mamba3_status launch_state_passing(const mamba3_state_passing_args *a, hipStream
     p.seqlen = f->seqlen; p.nseg = a->nseg; p.H = f->nheads; p.G = f->ngroups; p.P = f->headdim;
     p.N = f->dstate; p.R = f->rank; p.Gth = f->theta_groups ? f->theta_groups : f->nheads;
     p.norm = f->bc_norm; p.eps = f->bc_eps; p.lam_fixed = f->lam_fixed;
-    const int64_t nblk = (int64_t)f->batch * f->nheads;
+    const bool packed = f->cu_seqlens != nullptr;
+    p.cu = f->cu_seqlens; p.nseq = packed ? f->nseq : 0; p.seg_tokens = packed ? a->seg_tokens : 0;
+    p.rows = packed ? (int32_t)segment_rows_packed(f->nseq, f->seqlen, a->seg_tokens) : f->batch * a->nseg;
+    // packed batches reduce the segment sums in the walk (their rows are not known on the host)
+    p.sums_inline = packed && !sums_staged;
+    const int64_t nblk = (int64_t)(packed ? f->nseq : f->batch) * f->nheads;
     if (nblk == 0) return MAMBA3_OK;
     const size_t lds = state_passing_lds_bytes(p.N, p.P, p.R);
     const bool pref = (int64_t)(p.N / 2) * p.P <= (int64_t)PREF_MAX * kSPThreads;
-    const int64_t nrow = nblk * a->nseg;   // (segment row, head) pairs
+    const int64_t nrow = packed ? 0 : nblk * a->nseg;   // (segment row, head) pairs of k_segment_sums
     auto chain = [&](auto kern) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return false;
@@ -264,13 +392,25 @@ mamba3_status launch_state_passing(const mamba3_state_passing_args *a, hipStream
     };
     bool ok;
     if (f->dtype == MAMBA3_BF16) {
-        if (!sums_staged) hipLaunchKernelGGL(k_segment_sums<bf16>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
+        if (nrow && !sums_staged) hipLaunchKernelGGL(k_segment_sums<bf16>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
         ok = pref ? chain(k_state_passing<bf16, 1>) : chain(k_state_passing<bf16, 0>);
     } else {
-        if (!sums_staged) hipLaunchKernelGGL(k_segment_sums<float>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
+        if (nrow && !sums_staged) hipLaunchKernelGGL(k_segment_sums<float>, dim3((unsigned)nrow), dim3(kSPThreads), 0, st, p);
         ok = pref ? chain(k_state_passing<float, 1>) : chain(k_state_passing<float, 0>);
     }
     if (!ok) return MAMBA3_EHIP;
+    return hipGetLastError() == hipSuccess ? MAMBA3_OK : MAMBA3_EHIP;
+}
+
+int64_t segment_rows_packed(int64_t nseq, int64_t seqlen, int64_t seg_tokens) {
+    return seg_tokens >= 1 ? nseq + (seqlen + seg_tokens - 1) / seg_tokens : 0;
+}
+
+mamba3_status launch_segment_table(const int32_t *cu, int32_t nseq, int32_t seqlen, int32_t seg_tokens,
+                                   int32_t *seg_cu, hipStream_t st) {
+    const int64_t rows = segment_rows_packed(nseq, seqlen, seg_tokens);
+    hipLaunchKernelGGL(k_segment_table, dim3(1), dim3(kTabThreads), 0, st, cu, nseq, seqlen, seg_tokens, seg_cu,
+                       (int)rows);
     return hipGetLastError() == hipSuccess ? MAMBA3_OK : MAMBA3_EHIP;
 }
 

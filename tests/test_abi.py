@@ -46,7 +46,7 @@ def test_status_strings(lib):
     assert m3.status_string(m3.MAMBA3_OK) == "ok"
     for s in range(6):
         assert m3.status_string(s)
-    assert lib.mamba3_version() == 10400
+    assert lib.mamba3_version() == 10500
 
 
 BASE = 0x7F0000000000
@@ -194,11 +194,49 @@ def test_state_passing_validate(lib):
     a.fwd.y, a.fwd.z = fake(9), fake(10)                                                       # ignored: not read
     assert m3.mamba3_state_passing_validate(a) == m3.MAMBA3_OK
     a = good_sp()
-    a.fwd.cu_seqlens, a.fwd.batch, a.fwd.nseq = fake(30), 1, 2                                 # packed: not supported
-    assert m3.mamba3_state_passing_validate(a) == m3.MAMBA3_EUNSUPPORTED
-    a = good_sp()
     a.fwd.seqlen = 0
     assert m3.mamba3_state_passing_validate(a) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_state_passing_validate(good_sp(seg_tokens=32)) == m3.MAMBA3_EINVAL   # padded: nseg alone
+
+
+def packed_sp(**over):
+    """Packed batch of 3 sequences, 100 tokens, segments of 32 tokens: at most 3 + 4 = 7 rows."""
+    a = good_sp(nseg=0, seg_tokens=32)
+    a.fwd.cu_seqlens, a.fwd.batch, a.fwd.nseq = fake(30), 1, 3
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_state_passing_validate_packed(lib):
+    a = packed_sp()
+    assert lib.mamba3_segment_rows(ctypes.byref(a.fwd), 0, 32) == 7
+    assert lib.mamba3_segment_rows(ctypes.byref(a.fwd), 0, 100) == 4
+    assert lib.mamba3_segment_rows(ctypes.byref(a.fwd), 4, 32) == 0          # packed: nseg must be 0
+    assert lib.mamba3_segment_rows(ctypes.byref(good_scan()), 4, 0) == 8     # padded: batch * nseg
+    assert lib.mamba3_segment_rows(ctypes.byref(good_scan()), 4, 32) == 0
+    assert m3.mamba3_state_passing_validate(a) == m3.MAMBA3_OK
+    assert m3.mamba3_state_passing_validate(packed_sp(nseg=4)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_state_passing_validate(packed_sp(seg_tokens=0)) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_state_passing_validate(packed_sp(seg_h_in=fake(30))) == m3.MAMBA3_EINVAL   # aliases cu_seqlens
+    # h_in / h_out are per sequence (3 rows), the segment arrays per segment row (7)
+    b = packed_sp()
+    b.fwd.h_in = fake(31)
+    assert m3.mamba3_state_passing_validate(b) == m3.MAMBA3_OK
+    b.fwd.h_in = fake(24) - 3 * 4 * 16 * 16 * 4 + 256                       # its 3 rows reach into h_out
+    assert m3.mamba3_state_passing_validate(b) == m3.MAMBA3_EINVAL
+
+
+def test_segment_table_validate(lib):
+    """The segment table's host checks (no launch: every case fails before one)."""
+    t = lib.mamba3_segment_table
+    assert t(None, 3, 100, 32, fake(2), None) == m3.MAMBA3_EINVAL
+    assert t(fake(1), 3, 100, 32, None, None) == m3.MAMBA3_EINVAL
+    assert t(fake(1), -1, 100, 32, fake(2), None) == m3.MAMBA3_EINVAL
+    assert t(fake(1), 3, 100, 0, fake(2), None) == m3.MAMBA3_EINVAL
+    assert t(fake(1) + 2, 3, 100, 32, fake(2), None) == m3.MAMBA3_EALIGN
+    assert t(fake(1), 3, 100, 32, fake(1) + 8, None) == m3.MAMBA3_EINVAL   # overlaps cu_seqlens
+    assert t(fake(1), 2 ** 31 - 2, 2 ** 31 - 1, 1, fake(2), None) == m3.MAMBA3_EINVAL   # rows + 1 > INT32_MAX
 
 
 def good_seg(**over):
@@ -225,7 +263,17 @@ def test_scan_segmented_validate(lib):
     assert m3.mamba3_scan_segmented_validate(a) == m3.MAMBA3_EINVAL
     a = good_seg()
     a.fwd.cu_seqlens, a.fwd.batch, a.fwd.nseq = fake(32), 1, 2
-    assert m3.mamba3_scan_segmented_validate(a) == m3.MAMBA3_EUNSUPPORTED
+    assert m3.mamba3_scan_segmented_validate(a) == m3.MAMBA3_EINVAL                # packed: nseg must be 0
+    a.nseg, a.seg_tokens = 0, 32
+    assert m3.mamba3_scan_segmented_validate(a) == m3.MAMBA3_OK
+    # packed: 2 + ceil(100 / 32) = 6 rows, and the segment table (7 int32) in its own region
+    need = m3.lib().mamba3_scan_segmented_workspace_size(ctypes.byref(a))
+    assert need == 2 * 6 * 4 * 16 * 16 * 4 + 6 * 4 * 16 * 4 + 6 * 4 * 16 * 4 + 256
+    a.workspace_bytes = need - 1
+    assert m3.mamba3_scan_segmented_validate(a) == m3.MAMBA3_EWORKSPACE
+    a.workspace, a.workspace_bytes = fake(32) - 256, need                          # overlaps cu_seqlens
+    assert m3.mamba3_scan_segmented_validate(a) == m3.MAMBA3_EINVAL
+    assert m3.mamba3_scan_segmented_validate(good_seg(seg_tokens=32)) == m3.MAMBA3_EINVAL   # padded: nseg alone
     a = good_seg()
     a.fwd.h_out = fake(11)                                                          # h_out may be h_in
     assert m3.mamba3_scan_segmented_validate(a) == m3.MAMBA3_OK

@@ -40,3 +40,24 @@ def test_noalloc_matches_workspace_entry_twice(cfg):
         (y0, h0), (y1, h1) = _both(inp, nseg, inp["meta"]["chunk"])
         assert np.array_equal(_bits(y0), _bits(y1))
         assert np.array_equal(_bits(h0), _bits(h1))
+
+
+def test_noalloc_packed_matches_workspace_entry_twice():
+    """Packed batches (segments of seg_tokens tokens, the segment table in the array too): two
+    calls in a row, the second smaller, each bitwise equal to the workspace entry point's."""
+    import torch
+    for i, (cu, L) in enumerate((([0, 1, 1, 129, 130, 400, 700, 700], 100), ([0, 37, 37, 250], 64))):
+        cu = np.array(cu, dtype=np.int32)
+        inp = synth.scan_inputs(4, seed=95 + i, seqlen=int(cu[-1]), nheads=2, packed=False)
+        inp["cu_seqlens"] = cu
+        inp = synth.resume_inputs(inp, seed=96 + i)
+        note(f"no-alloc packed segmented scan call {i}: {len(cu) - 1} sequences, {cu[-1]} tokens, segments of {L}")
+        d = upload(inp, device())
+        args = [d[k] for k in ("x", "dt", "lam", "theta", "B", "C", "A", "D")]
+        kw = dict(seg_tokens=L, cu_seqlens=d["cu_seqlens"], chunk=inp["meta"]["chunk"], h_in=d["h_in"],
+                  Bprev=d["Bprev"], xprev=d["xprev"])
+        y0, h0 = m3.mamba3_scan_segmented(*args, **kw)
+        y1, h1 = m3.mamba3_scan_segmented_noalloc(*args, **kw)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(y0), _bits(y1))
+        assert np.array_equal(_bits(h0), _bits(h1))
