@@ -1033,7 +1033,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     };
     // em: also the decay table EM (the reverse walk's)
     auto load_scalars = [&](int64_t c0, int nq, bool em) {
-        static_assert(Q <= 64 && K < NT, "one wave scans the chunk; spare threads for the exponentials");
+        static_assert(Q <= 64, "one wave scans the chunk");
         if (wave == 0) {   // per-token scalars and the log-decay prefix (wave scan)
             const int t = lane;
             float dtv = 0.f, lv = 0.f, av = Ah;
@@ -1068,25 +1068,43 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             }
         }
         __syncthreads();
-        if (tid < K) {   // cumulative angles: one thread per pair walks the chunk's tokens
-            float acc = 0.f;
-            for (int t = 0; t < Q; t++) {
-                acc += DT[t] * (float)TH[t * K + tid];
+        {   // cumulative angles: J consecutive lanes per pair, TPG tokens each; a lane's running sum
+            // over its tokens, then an exclusive scan of the lane totals across the pair's J lanes
+            constexpr int J = NT / K, TPG = Q / J;
+            static_assert(NT % K == 0 && Q % J == 0 && (J & (J - 1)) == 0 && J <= 64, "angle split");
+            const int k = tid / J, j = tid % J;
+            float a[TPG], run = 0.f;
+#pragma unroll
+            for (int i = 0; i < TPG; i++) {
+                const int t = j * TPG + i;
+                run += DT[t] * (float)TH[t * K + k];
+                a[i] = run;
+            }
+            float ex = run;
+#pragma unroll
+            for (int off = 1; off < J; off <<= 1) {
+                const float o = __shfl_up(ex, off, J);
+                if (j >= off) ex += o;
+            }
+            ex -= run;
+#pragma unroll
+            for (int i = 0; i < TPG; i++) {
+                const int t = j * TPG + i;
                 float sn, cs;
-                __sincosf(acc, &sn, &cs);   // hardware sin / cos: operands of bf16 products
-                CS[t * K + tid] = cs;
-                SN[t * K + tid] = sn;
+                __sincosf(a[i] + ex, &sn, &cs);   // hardware sin / cos: operands of bf16 products
+                CS[t * K + k] = cs;
+                SN[t * K + k] = sn;
             }
-        } else {         // meanwhile the other threads form the exponentials
-            if (em)
-                for (int e = tid - K; e < Q * Q; e += NT - K) {
-                    const int t = e / Q, u = e % Q;
-                    EM[e] = (u <= t) ? expf(S[t] - S[u]) : 0.f;
-                }
-            for (int t = tid - K; t < Q; t += NT - K) {
-                ES[t] = expf(S[t]);
-                CU[t] = (t < nq) ? expf(S[nq - 1] - S[t]) * G1[t] : 0.f;
+        }
+        // the exponentials
+        if (em)
+            for (int e = tid; e < Q * Q; e += NT) {
+                const int t = e / Q, u = e % Q;
+                EM[e] = (u <= t) ? expf(S[t] - S[u]) : 0.f;
             }
+        for (int t = tid; t < Q; t += NT) {
+            ES[t] = expf(S[t]);
+            CU[t] = (t < nq) ? expf(S[nq - 1] - S[t]) * G1[t] : 0.f;
         }
         __syncthreads();
     };
@@ -1115,20 +1133,56 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             __syncthreads();
         }
     };
-    // B~ (and C~, dy in the reverse pass) and X, c o X of the chunk in bf16; raw B and C rows go
-    // through fp32 staging (dBf, dCf) for the prologue and the rotation
-    auto stage_chunk = [&](int64_t c0, int nq, bool rev) {
+    // B~ (and C~, dy in the reverse pass) and X, c o X of the chunk in bf16. B and C go from the
+    // prefetched 16-byte pieces straight to their rotated bf16 rows: a row's pieces sit on the
+    // N / 8 consecutive lanes of one DPP row group, which form the row's sum of squares for the
+    // prologue; each lane then rotates its 4 pairs by R(-Phi_t) and writes one 16-byte piece.
+    static_assert(N / 8 == 8 || N / 8 == 16, "a row's pieces fill half or all of a 16-lane DPP row");
+    auto row_sum = [&](float v) {   // over the N / 8 lanes holding one row
+        v += dppf<0xB1>(v);
+        v += dppf<0x4E>(v);
+        v += dppf<0x141>(v);
+        if constexpr (N / 8 == 16) v += dppf<0x140>(v);
+        return v;
+    };
+    auto stage_rows = [&](const bf16x8 &raw, int r, int n, int nq_, const float *bias, float *invs, bf16 *dst) {
+        const int t = r / R;
+        float u[8];
 #pragma unroll
-        for (int i = 0; i < PF_B; i++) {   // 16-byte pieces
+        for (int m = 0; m < 8; m++) u[m] = (t < nq_) ? (float)raw[m] : 0.f;
+        if (pro) {
+            float inv = 1.f;
+            if (p.norm) {
+                float ss = 0.f;
+#pragma unroll
+                for (int m = 0; m < 8; m++) ss += u[m] * u[m];
+                inv = 1.f / sqrtf(row_sum(ss) / (float)N + p.eps);
+            }
+            if (n == 0) invs[r] = inv;
+            const f32x4 b0 = bias ? *(const f32x4 *)(bias + n) : f32x4{};
+            const f32x4 b1 = bias ? *(const f32x4 *)(bias + n + 4) : f32x4{};
+#pragma unroll
+            for (int m = 0; m < 8; m++) u[m] = (t < nq_) ? u[m] * inv + ((m < 4) ? b0[m] : b1[m - 4]) : 0.f;
+        }
+        const f32x4 cs = *(const f32x4 *)(CS + t * K + n / 2), sn = *(const f32x4 *)(SN + t * K + n / 2);
+        bf16x8 o;
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            o[2 * m] = (bf16)(cs[m] * u[2 * m] + sn[m] * u[2 * m + 1]);
+            o[2 * m + 1] = (bf16)(-sn[m] * u[2 * m] + cs[m] * u[2 * m + 1]);
+        }
+        *(bf16x8 *)(dst + r * NS + n) = o;
+    };
+    float dA_acc = 0.f, dD_acc = 0.f;   // thread partials (fixed order: reduced at the end)
+    auto stage_chunk = [&](int64_t c0, int nq, bool rev) {
+        (void)c0;
+#pragma unroll
+        for (int i = 0; i < PF_B; i++) {   // 16-byte pieces; whole rows are active or not
             const int e = tid + i * NT;
             if (e >= QR * N / 8) break;
-            const int r = e / (N / 8), n = (e % (N / 8)) * 8, t = r / R;
-            const bf16x8 bv = (t < nq) ? pB[i] : bf16x8{}, cv = (rev && t < nq) ? pC[i] : bf16x8{};
-#pragma unroll
-            for (int m = 0; m < 8; m++) {
-                dBf[r * NF + n + m] = (float)bv[m];
-                if (rev) dCf[r * NF + n + m] = (float)cv[m];
-            }
+            const int r = e / (N / 8), n = (e % (N / 8)) * 8;
+            stage_rows(pB[i], r, n, nq, Bbh, INVB, Bt);
+            if (rev) stage_rows(pC[i], r, n, nq, Cbh, INVC, Ct);
         }
 #pragma unroll
         for (int i = 0; i < PF_X; i++) {
@@ -1141,30 +1195,18 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             for (int m = 0; m < 8; m++) xc[m] = (bf16)(CU[t] * (float)xv[m]);
             *(bf16x8 *)(Xb + r * PS + pp) = xv;
             *(bf16x8 *)(XcB + r * PS + pp) = xc;
-            if (rev) *(bf16x8 *)(dYb + r * PS + pp) = dv;
-        }
-        __syncthreads();
-        if (pro) {
-            prologue_rows(dBf, nq * R, NF, Bbh, INVB);
-            if (rev) prologue_rows(dCf, nq * R, NF, Cbh, INVC);
-            __syncthreads();
-        }
-        for (int e = tid; e < QR * K; e += NT) {
-            const int r = e / K, k = e % K, t = r / R;
-            float b0 = 0.f, b1 = 0.f, q0 = 0.f, q1 = 0.f;
-            if (t < nq) {
-                const float cs = CS[t * K + k], sn = SN[t * K + k];
-                const float u0 = dBf[r * NF + 2 * k], u1 = dBf[r * NF + 2 * k + 1];
-                b0 = cs * u0 + sn * u1;
-                b1 = -sn * u0 + cs * u1;
-                if (rev) {
-                    const float v0 = dCf[r * NF + 2 * k], v1 = dCf[r * NF + 2 * k + 1];
-                    q0 = cs * v0 + sn * v1;
-                    q1 = -sn * v0 + cs * v1;
+            if (rev) {
+                *(bf16x8 *)(dYb + r * PS + pp) = dv;
+                if (!p.z) {   // e^{S} o dy and D's gradient (with the gate they wait for dy0)
+                    bf16x8 ed;
+#pragma unroll
+                    for (int m = 0; m < 8; m++) {
+                        ed[m] = (bf16)(ES[t] * (float)dv[m]);
+                        dD_acc += (float)dv[m] * (float)xv[m];
+                    }
+                    *(bf16x8 *)(EdYb + r * PS + pp) = ed;
                 }
             }
-            *(bf16x2 *)(Bt + r * NS + 2 * k) = bf16x2{(bf16)b0, (bf16)b1};
-            if (rev) *(bf16x2 *)(Ct + r * NS + 2 * k) = bf16x2{(bf16)q0, (bf16)q1};
         }
         __syncthreads();
     };
@@ -1235,7 +1277,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     for (int e = tid; e < N; e += NT) BBA[e] = CBA[e] = 0.f;
     for (int e = tid; e < R * N; e += NT) BpRaw[e] = 0.f;
     for (int e = tid; e < R; e += NT) INVBP[e] = 1.f;
-    float dA_acc = 0.f, dD_acc = 0.f;
+    float bbias[8] = {}, cbias[8] = {};   // this thread's columns of the bias gradients
     __syncthreads();
     if (nch > 0) prefetch(nch - 1, true);
     for (int64_t c = nch - 1; c >= 0; c--) {
@@ -1270,27 +1312,72 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         if (c > 0) prefetch(c - 1, true);
         for (int e = tid; e < Q * K; e += NT) DPHI[e] = 0.f;
         for (int t = tid; t < Q; t += NT) DS[t] = DGM[t] = DDL[t] = 0.f;
-        // scores on every QR x QR tile (zero outside the causal part): S (fp32) and A = M o S (bf16)
-        #pragma unroll
-        for (int it_ = 0; it_ < (TQ * TQ + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
-            const int tile = wave + it_ * NW;
-            if ((TQ * TQ) % NW != 0 && tile >= TQ * TQ) break;
-            const int tr = tile / TQ, tc = tile % TQ;
-            f32x4 acc = {};
-#pragma unroll
-            for (int k0 = 0; k0 < N; k0 += 32)
-                acc = mfma16(op_nat(Ct, NS, tr * 16 + li, k0, lg), op_nat(Bt, NS, tc * 16 + li, k0, lg), acc);
+        // scores S = C~ B~^T and dP = dY X^T on every QR x QR tile (zero outside the causal part):
+        // A = M o S and dS' = M o dP (bf16); d(mask) = S o dP, summed per row and column. Without
+        // the gate both run in one pass (the gated dy0 needs all of A first).
+        auto mask_tile = [&](int tr, int tc, const f32x4 &sacc, const f32x4 &pacc, bool write_a) {
+            float cm = 0.f, cg = 0.f, cd = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int r = tr * 16 + 4 * lg + i, q = tc * 16 + li, t = r / R, u = q / R;
                 const bool ok = u <= t && t < nq;
-                const float mw = ok ? EM[t * Q + u] * ((u < t) ? G1[u] : GM[u]) : 0.f;
-                Sf[r * SF + q] = ok ? acc[i] : 0.f;
-                Ab[r * QS + q] = (bf16)(mw * acc[i]);
+                const float E = ok ? EM[t * Q + u] : 0.f, w = (u < t) ? G1[u] : GM[u];
+                if (write_a) Ab[r * QS + q] = (bf16)(E * w * sacc[i]);
+                const float dm = sacc[i] * pacc[i];
+                dSb[r * QS + q] = (bf16)(E * w * pacc[i]);
+                const float rm = sum16(dm * E * w);   // row r's share of this tile
+                if (li == 0) RPM[r * TQ + tc] = rm;
+                cm += dm * E * w;
+                cg += dm * E;
+                cd += (u < t) ? dm * E : 0.f;
             }
-        }
-        __syncthreads();
-        if (p.z) {
+            cm = sum_groups(cm);
+            cg = sum_groups(cg);
+            cd = sum_groups(cd);
+            if (lg == 0) {
+                const int q = tc * 16 + li;
+                CPM[q * TQ + tr] = cm;
+                CPG[q * TQ + tr] = cg;
+                CPD[q * TQ + tr] = cd;
+            }
+        };
+        if (!p.z) {
+            #pragma unroll
+            for (int it_ = 0; it_ < (TQ * TQ + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
+                const int tile = wave + it_ * NW;
+                if ((TQ * TQ) % NW != 0 && tile >= TQ * TQ) break;
+                const int tr = tile / TQ, tc = tile % TQ;
+                f32x4 sacc = {}, pacc = {};
+#pragma unroll
+                for (int k0 = 0; k0 < N; k0 += 32)
+                    sacc = mfma16(op_nat(Ct, NS, tr * 16 + li, k0, lg), op_nat(Bt, NS, tc * 16 + li, k0, lg), sacc);
+#pragma unroll
+                for (int k0 = 0; k0 < P; k0 += 32)
+                    pacc = mfma16(op_nat(dYb, PS, tr * 16 + li, k0, lg), op_nat(Xb, PS, tc * 16 + li, k0, lg), pacc);
+                mask_tile(tr, tc, sacc, pacc, true);
+            }
+            __syncthreads();
+        } else {
+            // scores first: S (fp32, for the mask's gradient) and A
+            #pragma unroll
+            for (int it_ = 0; it_ < (TQ * TQ + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
+                const int tile = wave + it_ * NW;
+                if ((TQ * TQ) % NW != 0 && tile >= TQ * TQ) break;
+                const int tr = tile / TQ, tc = tile % TQ;
+                f32x4 acc = {};
+#pragma unroll
+                for (int k0 = 0; k0 < N; k0 += 32)
+                    acc = mfma16(op_nat(Ct, NS, tr * 16 + li, k0, lg), op_nat(Bt, NS, tc * 16 + li, k0, lg), acc);
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int r = tr * 16 + 4 * lg + i, q = tc * 16 + li, t = r / R, u = q / R;
+                    const bool ok = u <= t && t < nq;
+                    const float mw = ok ? EM[t * Q + u] * ((u < t) ? G1[u] : GM[u]) : 0.f;
+                    Sf[r * SF + q] = ok ? acc[i] : 0.f;
+                    Ab[r * QS + q] = (bf16)(mw * acc[i]);
+                }
+            }
+            __syncthreads();
             // outputs before the gate, y0 = e^{S_t} C~ H' + A X + D X; dy0 = dy SiLU(z), dz
             #pragma unroll
             for (int it_ = 0; it_ < (TQ * TP + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
@@ -1317,74 +1404,58 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
                 }
             }
             __syncthreads();
-        }
-        // e^{S} o dy0, and D's gradient
-        for (int e = tid; e < QR * P; e += NT) {
-            const int r = e / P, pp = e % P, t = r / R;
-            const float d = (float)dYb[r * PS + pp];
-            EdYb[r * PS + pp] = (bf16)(ES[t] * d);
-            dD_acc += d * (float)Xb[r * PS + pp];
-        }
-        __syncthreads();
-        // dP = dY X^T with the mask: dS' = M o dP (bf16); d(mask) = S o dP, summed per row and column
-        #pragma unroll
-        for (int it_ = 0; it_ < (TQ * TQ + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
-            const int tile = wave + it_ * NW;
-            if ((TQ * TQ) % NW != 0 && tile >= TQ * TQ) break;
-            const int tr = tile / TQ, tc = tile % TQ;
-            f32x4 acc = {};
-#pragma unroll
-            for (int k0 = 0; k0 < P; k0 += 32)
-                acc = mfma16(op_nat(dYb, PS, tr * 16 + li, k0, lg), op_nat(Xb, PS, tc * 16 + li, k0, lg), acc);
-            float cm = 0.f, cg = 0.f, cd = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int r = tr * 16 + 4 * lg + i, q = tc * 16 + li, t = r / R, u = q / R;
-                const bool ok = u <= t && t < nq;
-                const float E = ok ? EM[t * Q + u] : 0.f, w = (u < t) ? G1[u] : GM[u];
-                const float dm = Sf[r * SF + q] * acc[i];
-                dSb[r * QS + q] = (bf16)(E * w * acc[i]);
-                const float rm = sum16(dm * E * w);   // row r's share of this tile
-                if (li == 0) RPM[r * TQ + tc] = rm;
-                cm += dm * E * w;
-                cg += dm * E;
-                cd += (u < t) ? dm * E : 0.f;
+            // e^{S} o dy0, and D's gradient
+            for (int e = tid; e < QR * P; e += NT) {
+                const int r = e / P, pp = e % P, t = r / R;
+                const float d = (float)dYb[r * PS + pp];
+                EdYb[r * PS + pp] = (bf16)(ES[t] * d);
+                dD_acc += d * (float)Xb[r * PS + pp];
             }
-            cm = sum_groups(cm);
-            cg = sum_groups(cg);
-            cd = sum_groups(cd);
-            if (lg == 0) {
-                const int q = tc * 16 + li;
-                CPM[q * TQ + tr] = cm;
-                CPG[q * TQ + tr] = cg;
-                CPD[q * TQ + tr] = cd;
+            __syncthreads();
+            // dP with the gated dy0, and the mask's products with the stored scores
+            #pragma unroll
+            for (int it_ = 0; it_ < (TQ * TQ + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
+                const int tile = wave + it_ * NW;
+                if ((TQ * TQ) % NW != 0 && tile >= TQ * TQ) break;
+                const int tr = tile / TQ, tc = tile % TQ;
+                f32x4 pacc = {}, sacc;
+#pragma unroll
+                for (int k0 = 0; k0 < P; k0 += 32)
+                    pacc = mfma16(op_nat(dYb, PS, tr * 16 + li, k0, lg), op_nat(Xb, PS, tc * 16 + li, k0, lg), pacc);
+#pragma unroll
+                for (int i = 0; i < 4; i++) sacc[i] = Sf[(tr * 16 + 4 * lg + i) * SF + tc * 16 + li];
+                mask_tile(tr, tc, sacc, pacc, false);
             }
+            __syncthreads();
         }
-        __syncthreads();
         // dX = A^T dy0 + c o (B~ G^) + D dy0 (+ the fold's carry into the last token); dc partials
         #pragma unroll
         for (int it_ = 0; it_ < (TQ * TP + NW - 1) / NW; it_++) {   // a wave's tiles, unrolled
             const int tile = wave + it_ * NW;
             if ((TQ * TP) % NW != 0 && tile >= TQ * TP) break;
             const int tq = tile / TP, tp = tile % TP;
+            // transposed products (the dy / G^ operand first): the lane holds row q = 16 tq + li,
+            // columns pp .. pp + 3, and stores them as one 8-byte piece
             f32x4 a1 = {}, a2 = {};
 #pragma unroll
             for (int k0 = 0; k0 < QR; k0 += 32)
-                a1 = mfma16(op_tr(Ab, QS, k0, tq * 16, li, lg), op_tr(dYb, PS, k0, tp * 16, li, lg), a1);
+                a1 = mfma16(op_tr(dYb, PS, k0, tp * 16, li, lg), op_tr(Ab, QS, k0, tq * 16, li, lg), a1);
 #pragma unroll
             for (int k0 = 0; k0 < N; k0 += 32)
-                a2 = mfma16(op_split(Bt, NS, tq * 16 + li, k0, lg), op_tr(Gb, PS, k0, tp * 16, li, lg), a2);
+                a2 = mfma16(op_tr(Gb, PS, k0, tp * 16, li, lg), op_split(Bt, NS, tq * 16 + li, k0, lg), a2);
+            const int q = tq * 16 + li, pp = tp * 16 + 4 * lg, u = q / R, j = q % R;
+            const bf16x4 xv = *(const bf16x4 *)(Xb + q * PS + pp), dv = *(const bf16x4 *)(dYb + q * PS + pp);
+            float dc = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int q = tq * 16 + 4 * lg + i, pp = tp * 16 + li, u = q / R, j = q % R;
-                const float xv = (float)Xb[q * PS + pp];
-                const float dc = sum16(a2[i] * xv);
-                if (li == 0) RPC[q * TP + tp] = dc;
-                if (u < nq) {
-                    float dx = a1[i] + CU[u] * a2[i] + Dh * (float)dYb[q * PS + pp];
-                    if (u == e_) dx += dXcIn[j * P + pp];
-                    stt<bf16>(p.dx, tokX(c0 + u) + j * P + pp, dx);
-                }
+            for (int i = 0; i < 4; i++) dc += a2[i] * (float)xv[i];
+            dc = sum_groups(dc);   // row q's share over the tile's 16 columns
+            if (lg == 0) RPC[q * TP + tp] = dc;
+            if (u < nq) {
+                const f32x4 carry = (u == e_) ? *(const f32x4 *)(dXcIn + j * P + pp) : f32x4{};
+                float dx[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) dx[i] = a1[i] + CU[u] * a2[i] + Dh * (float)dv[i] + carry[i];
+                *(bf16x4 *)((bf16 *)p.dx + tokX(c0 + u) + j * P + pp) = bf16x4{(bf16)dx[0], (bf16)dx[1], (bf16)dx[2], (bf16)dx[3]};
             }
         }
         // dC~ = dS' B~ + e^{S_t} (dY H'^T); the inter part's share of dS
@@ -1590,103 +1661,107 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             }
         }
         __syncthreads();
-        for (int e = tid; e < nq * K; e += NT) {
-            const int t = e / K, k = e % K;
-            st_dtheta<bf16>(p, start + c0 + t, h, k, DT[t] * DPHI[e]);
-        }
-        for (int t0 = tid >> 4; t0 < (nq + NT / 16 - 1) / (NT / 16) * (NT / 16); t0 += NT / 16) {
-            const int t = t0 < nq ? t0 : 0;   // (every lane of a group reaches the shuffles)
-            float a = 0.f;
-            for (int k = li; k < K; k += 16) a += (float)TH[t * K + k] * DPHI[t * K + k];
-            a = sum16(a);
-            if (t0 < nq && li == 0) {
-                const float ddt = AT[t] * DS[t] + (1.f - LM[t]) * DDL[t] + LM[t] * DGM[t] + a;
-                stt<bf16>(p.ddt, (start + c0 + t) * H + h, ddt);
-                if (p.dlam) stt<bf16>(p.dlam, (start + c0 + t) * H + h, DT[t] * (DGM[t] - DDL[t]));
-                if (p.A_tok) stt<bf16>(p.dA_tok, (start + c0 + t) * H + h, DT[t] * DS[t]);
-                else dA_acc += DT[t] * DS[t];
-            }
-        }
-        // raw B and C rows of the chunk again (for the prologue's backward), over C~ and B~
-        if (pro) {
-            for (int e = tid; e < QR * (N / 8); e += NT) {
-                const int r = e / (N / 8), col = (e % (N / 8)) * 8, t = r / R, j = r % R;
-                bf16x8 bv = {}, cv = {};
-                if (t < nq) {
-                    const int64_t o = tokB(c0 + t) + j * N + col;
-                    bv = *(const bf16x8 *)(gB + o);
-                    cv = *(const bf16x8 *)(gC + o);
-                }
-                *(bf16x8 *)(Bt + r * NS + col) = bv;
-                *(bf16x8 *)(Ct + r * NS + col) = cv;
-            }
-        }
-        // dB, dC back to the physical frame (+ the carry into the last token), through the prologue
-        for (int e = tid; e < nq * K * R; e += NT) {
-            const int t = e / (K * R), k = (e / R) % K, j = e % R, r = t * R + j;
-            const float cs = CS[t * K + k], sn = SN[t * K + k];
-            float d0 = dBf[r * NF + 2 * k], d1 = dBf[r * NF + 2 * k + 1];
-            float b0 = cs * d0 - sn * d1, b1 = sn * d0 + cs * d1;
-            if (t == e_) {
-                b0 += dBcIn[j * N + 2 * k];
-                b1 += dBcIn[j * N + 2 * k + 1];
-            }
-            dBf[r * NF + 2 * k] = b0;
-            dBf[r * NF + 2 * k + 1] = b1;
-            d0 = dCf[r * NF + 2 * k];
-            d1 = dCf[r * NF + 2 * k + 1];
-            dCf[r * NF + 2 * k] = cs * d0 - sn * d1;
-            dCf[r * NF + 2 * k + 1] = sn * d0 + cs * d1;
-        }
-        __syncthreads();
-        if (p.Bb || p.Cb)   // the bias gradients' per-slab sums
-            for (int n = tid; n < N; n += NT) {
-                float a = 0.f, b = 0.f;
-                for (int r = 0; r < nq * R; r++) {
-                    a += dBf[r * NF + n];
-                    b += dCf[r * NF + n];
-                }
-                BBA[n] += a;
-                CBA[n] += b;
-            }
-        // back through the prologue to the raw columns (16 lanes per row; raw rows in Bt / Ct)
-        for (int r0 = tid >> 4; r0 < (2 * nq * R + NT / 16 - 1) / (NT / 16) * (NT / 16); r0 += NT / 16) {
-            const bool ok = r0 < 2 * nq * R;
-            const int r = ok ? r0 : 0;
-            const bool isC = r >= nq * R;
-            const int rr = isC ? r - nq * R : r, t = rr / R, j = rr % R;
-            const float *gout = (isC ? dCf : dBf) + rr * NF;
-            const float inv = (isC ? INVC : INVB)[rr];
-            const bf16 *raw = (isC ? Ct : Bt) + rr * NS;
-            // lane li owns the NPL consecutive columns from li * NPL: one vector store each
-            constexpr int NPL = N / 16;
-            const int n0 = li * NPL;
-            float dot = 0.f;
-            if (p.norm) {
+        {   // dtheta = dt dPhi, 8 pairs of a token per thread (one 16-byte store), and ddt: the
+            // token's K / 8 consecutive lanes add up its sum_k theta_k dPhi_k (DPP, within a row)
+            constexpr int KG = K / 8;
+            static_assert(KG == 4 || KG == 8, "a token's pairs on 4 or 8 lanes");
+            for (int e0 = tid; e0 < (Q * KG + NT - 1) / NT * NT; e0 += NT) {
+                const int t = e0 / KG, k0 = (e0 % KG) * 8;
+                const bool ok = t < nq;   // the same on every lane of the token
+                const int tt = ok ? t : 0;
+                const f32x4 d0 = *(const f32x4 *)(DPHI + tt * K + k0), d1 = *(const f32x4 *)(DPHI + tt * K + k0 + 4);
+                const bf16x8 th = *(const bf16x8 *)(TH + tt * K + k0);
+                float a = 0.f;
 #pragma unroll
-                for (int m = 0; m < NPL; m++) dot += gout[n0 + m] * (float)raw[n0 + m];
-                dot = sum16(dot);
-            }
-            const float k3 = p.norm ? dot * inv * inv * inv / (float)N : 0.f;
-            float v[NPL];
+                for (int m = 0; m < 8; m++) a += (float)th[m] * ((m < 4) ? d0[m] : d1[m - 4]);
+                a += dppf<0xB1>(a);
+                a += dppf<0x4E>(a);
+                if constexpr (KG == 8) a += dppf<0x141>(a);
+                if (ok) {
+                    const float dtv = DT[t];
+                    const int64_t tok = start + c0 + t;
+                    float o[8];
 #pragma unroll
-            for (int m = 0; m < NPL; m++)
-                v[m] = p.norm ? gout[n0 + m] * inv - k3 * (float)raw[n0 + m] : gout[n0 + m];
-            float *part = isC ? p.p_dC : p.p_dB;
-            if (ok) {
+                    for (int m = 0; m < 8; m++) o[m] = dtv * ((m < 4) ? d0[m] : d1[m - 4]);
+                    if (p.p_dth) {   // head h's share of a shared angle row
+                        float *dst = p.p_dth + (tok * H + h) * (int64_t)K + k0;
+                        *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};
+                        *(f32x4 *)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+                    } else {
+                        *(bf16x8 *)((bf16 *)p.dtheta + (tok * H + h) * (int64_t)K + k0) =
+                            bf16x8{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3], (bf16)o[4], (bf16)o[5], (bf16)o[6], (bf16)o[7]};
+                    }
+                    if (k0 == 0) {
+                        const float ddt = AT[t] * DS[t] + (1.f - LM[t]) * DDL[t] + LM[t] * DGM[t] + a;
+                        stt<bf16>(p.ddt, tok * H + h, ddt);
+                        if (p.dlam) stt<bf16>(p.dlam, tok * H + h, DT[t] * (DGM[t] - DDL[t]));
+                        if (p.A_tok) stt<bf16>(p.dA_tok, tok * H + h, DT[t] * DS[t]);
+                        else dA_acc += DT[t] * DS[t];
+                    }
+                }
+            }
+        }
+        // dB, dC of the chunk: back to the physical frame (+ the carry into the last token), through
+        // the prologue, stored. Thread e holds row r = e / (N / 8), columns n .. n + 7 of both: the
+        // rotation of its 4 pairs, the row's dot product over its N / 8 lanes (norm), one store each.
+        // The bias gradients accumulate per thread (its columns are the same in every chunk) and
+        // are summed over the threads at the end of the slab.
+        static_assert(PF_B == 1, "one 16-byte piece of B and of C per thread");
+        if (tid < QR * N / 8) {   // whole rows are active or not
+            const int r = tid / (N / 8), n = (tid % (N / 8)) * 8, t = r / R, j = r % R;
+            const bool live = t < nq;   // the same for every lane of the row
+            bf16x8 raw[2] = {bf16x8{}, bf16x8{}};
+            if (p.norm && live) {
+                const int64_t o = tokB(c0 + t) + j * N + n;
+                raw[0] = *(const bf16x8 *)(gB + o);
+                raw[1] = *(const bf16x8 *)(gC + o);
+            }
+            const f32x4 cs = *(const f32x4 *)(CS + t * K + n / 2), sn = *(const f32x4 *)(SN + t * K + n / 2);
+#pragma unroll
+            for (int isC = 0; isC < 2; isC++) {
+                const float *gsrc = (isC ? dCf : dBf) + r * NF + n;
+                float v[8];
+#pragma unroll
+                for (int m = 0; m < 4; m++) {
+                    const float d0 = gsrc[2 * m], d1 = gsrc[2 * m + 1];
+                    v[2 * m] = cs[m] * d0 - sn[m] * d1;
+                    v[2 * m + 1] = sn[m] * d0 + cs[m] * d1;
+                }
+                if (!isC && t == e_) {   // the carry; the rows of the last token then pass it on
+#pragma unroll
+                    for (int m = 0; m < 8; m++) {
+                        v[m] += dBcIn[j * N + n + m];
+                        dBcIn[j * N + n + m] = dBcOut[j * N + n + m];
+                    }
+                }
+                float dot = 0.f;
+                if (p.norm) {
+#pragma unroll
+                    for (int m = 0; m < 8; m++) dot += v[m] * (float)raw[isC][m];
+                    dot = row_sum(dot);
+                }
+                if (!live) continue;
+#pragma unroll
+                for (int m = 0; m < 8; m++) {
+                    if (isC) cbias[m] += v[m];
+                    else bbias[m] += v[m];
+                }
+                const float inv = (isC ? INVC : INVB)[r];
+                const float k3 = p.norm ? dot * inv * inv * inv / (float)N : 0.f;
+                float o[8];
+#pragma unroll
+                for (int m = 0; m < 8; m++) o[m] = p.norm ? v[m] * inv - k3 * (float)raw[isC][m] : v[m];
+                float *part = isC ? p.p_dC : p.p_dB;
                 if (part) {
-                    float *dst = part + ((start + c0 + t) * H + h) * (int64_t)R * N + j * N + n0;
-#pragma unroll
-                    for (int m = 0; m < NPL; m += 4) *(f32x4 *)(dst + m) = f32x4{v[m], v[m + 1], v[m + 2], v[m + 3]};
+                    float *dst = part + ((start + c0 + t) * H + h) * (int64_t)R * N + j * N + n;
+                    *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};
+                    *(f32x4 *)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
                 } else {
-                    bf16 *dst = (bf16 *)(isC ? p.dC : p.dB) + tokB(c0 + t) + j * N + n0;
-#pragma unroll
-                    for (int m = 0; m < NPL; m += 4)
-                        *(bf16x4 *)(dst + m) = bf16x4{(bf16)v[m], (bf16)v[m + 1], (bf16)v[m + 2], (bf16)v[m + 3]};
+                    *(bf16x8 *)((bf16 *)(isC ? p.dC : p.dB) + tokB(c0 + t) + j * N + n) =
+                        bf16x8{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3], (bf16)o[4], (bf16)o[5], (bf16)o[6], (bf16)o[7]};
                 }
             }
         }
-        for (int e = tid; e < R * N; e += NT) dBcIn[e] = dBcOut[e];
         for (int e = tid; e < R * P; e += NT) dXcIn[e] = dXcOut[e];
         __syncthreads();
     }
@@ -1718,6 +1793,21 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             for (int j = 0; j < R; j++) BBA[n] += dBcIn[j * N + n];
         for (int e = tid; e < R * P; e += NT)
             if (p.dxprev) stt<bf16>(p.dxprev, sh * R * P + e, dXcIn[e]);
+    }
+    if (p.Bb || p.Cb) {   // the per-thread bias partials, summed over the threads in thread order
+        float *scr = dBf;  // [QR * N / 8][8] (dB~'s staging is free after the last chunk)
+        for (int isC = 0; isC < 2; isC++) {
+            if (tid < QR * N / 8)
+#pragma unroll
+                for (int m = 0; m < 8; m++) scr[tid * 8 + m] = isC ? cbias[m] : bbias[m];
+            __syncthreads();
+            for (int n = tid; n < N; n += NT) {
+                float a = 0.f;
+                for (int q = n / 8; q < QR * N / 8; q += N / 8) a += scr[q * 8 + n % 8];
+                (isC ? CBA : BBA)[n] += a;
+            }
+            __syncthreads();
+        }
     }
     const float dA_sum = block_sum(dA_acc, RED);
     const float dD_sum = block_sum(dD_acc, RED);
