@@ -1316,30 +1316,30 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         // A = M o S and dS' = M o dP (bf16); d(mask) = S o dP, summed per row and column. Without
         // the gate both run in one pass (the gated dy0 needs all of A first).
         auto mask_tile = [&](int tr, int tc, const f32x4 &sacc, const f32x4 &pacc, bool write_a) {
+            // every table read first (indices stay below Q: no conditions), then the selects;
+            // the partial sums are stored by every lane holding them (the same value)
+            const int q = tc * 16 + li, u = q / R;
+            const float g1 = G1[u], gm = GM[u];
+            float em[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) em[i] = EM[((tr * 16 + 4 * lg + i) / R) * Q + u];
             float cm = 0.f, cg = 0.f, cd = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int r = tr * 16 + 4 * lg + i, q = tc * 16 + li, t = r / R, u = q / R;
+                const int r = tr * 16 + 4 * lg + i, t = r / R;
                 const bool ok = u <= t && t < nq;
-                const float E = ok ? EM[t * Q + u] : 0.f, w = (u < t) ? G1[u] : GM[u];
+                const float E = ok ? em[i] : 0.f, w = (u < t) ? g1 : gm;
                 if (write_a) Ab[r * QS + q] = (bf16)(E * w * sacc[i]);
                 const float dm = sacc[i] * pacc[i];
                 dSb[r * QS + q] = (bf16)(E * w * pacc[i]);
-                const float rm = sum16(dm * E * w);   // row r's share of this tile
-                if (li == 0) RPM[r * TQ + tc] = rm;
+                RPM[r * TQ + tc] = sum16(dm * E * w);   // row r's share of this tile
                 cm += dm * E * w;
                 cg += dm * E;
                 cd += (u < t) ? dm * E : 0.f;
             }
-            cm = sum_groups(cm);
-            cg = sum_groups(cg);
-            cd = sum_groups(cd);
-            if (lg == 0) {
-                const int q = tc * 16 + li;
-                CPM[q * TQ + tr] = cm;
-                CPG[q * TQ + tr] = cg;
-                CPD[q * TQ + tr] = cd;
-            }
+            CPM[q * TQ + tr] = sum_groups(cm);
+            CPG[q * TQ + tr] = sum_groups(cg);
+            CPD[q * TQ + tr] = sum_groups(cd);
         };
         if (!p.z) {
             #pragma unroll
@@ -1449,12 +1449,14 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; i++) dc += a2[i] * (float)xv[i];
             dc = sum_groups(dc);   // row q's share over the tile's 16 columns
-            if (lg == 0) RPC[q * TP + tp] = dc;
+            RPC[q * TP + tp] = dc;   // (every lane of the row's group: the same value)
+            const float cuu = CU[u];
+            const f32x4 cin = *(const f32x4 *)(dXcIn + j * P + pp);
             if (u < nq) {
-                const f32x4 carry = (u == e_) ? *(const f32x4 *)(dXcIn + j * P + pp) : f32x4{};
+                const f32x4 carry = (u == e_) ? cin : f32x4{};
                 float dx[4];
 #pragma unroll
-                for (int i = 0; i < 4; i++) dx[i] = a1[i] + CU[u] * a2[i] + Dh * (float)dv[i] + carry[i];
+                for (int i = 0; i < 4; i++) dx[i] = a1[i] + cuu * a2[i] + Dh * (float)dv[i] + carry[i];
                 *(bf16x4 *)((bf16 *)p.dx + tokX(c0 + u) + j * P + pp) = bf16x4{(bf16)dx[0], (bf16)dx[1], (bf16)dx[2], (bf16)dx[3]};
             }
         }
@@ -1471,13 +1473,19 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
 #pragma unroll
             for (int k0 = 0; k0 < P; k0 += 32)
                 a2 = mfma16(op_nat(dYb, PS, tq * 16 + li, k0, lg), op_nat(Hb, PS, tn * 16 + li, k0, lg), a2);
+            float es[4], cv[4];   // the epilogue's reads first (t < Q: no conditions)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int r = tq * 16 + 4 * lg + i;
+                es[i] = ES[r / R];
+                cv[i] = (float)Ct[r * NS + tn * 16 + li];
+            }
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int r = tq * 16 + 4 * lg + i, n = tn * 16 + li, t = r / R;
-                const float inter = (t < nq) ? ES[t] * a2[i] : 0.f;
+                const float inter = (t < nq) ? es[i] * a2[i] : 0.f;
                 dCf[r * NF + n] = (t < nq) ? a1[i] + inter : 0.f;
-                const float di = sum16((float)Ct[r * NS + n] * inter);
-                if (li == 0) RPI[r * TN + tn] = di;
+                RPI[r * TN + tn] = sum16(cv[i] * inter);   // (every lane of the row: the same value)
             }
         }
         // dB~ = dS'^T C~ + c o (X G^^T)
@@ -1493,10 +1501,13 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
 #pragma unroll
             for (int k0 = 0; k0 < P; k0 += 32)
                 a2 = mfma16(op_nat(Xb, PS, tq * 16 + li, k0, lg), op_nat(Gb, PS, tn * 16 + li, k0, lg), a2);
+            float cu4[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) cu4[i] = CU[(tq * 16 + 4 * lg + i) / R];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int q = tq * 16 + 4 * lg + i, n = tn * 16 + li, u = q / R;
-                dBf[q * NF + n] = (u < nq) ? a1[i] + CU[u] * a2[i] : 0.f;
+                dBf[q * NF + n] = (u < nq) ? a1[i] + cu4[i] * a2[i] : 0.f;
             }
         }
         // dH' = e^{S_e} G^ + C~^T (e^{S} o dY), and the rotated state Inner = e^{S_e} H' + B~^T (c o X)
@@ -1515,7 +1526,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
             for (int m = 0; m < 2; m++) {
                 const float in0 = ES[e_] * hcur[v][2 * m] + a2[2 * m], in1 = ES[e_] * hcur[v][2 * m + 1] + a2[2 * m + 1];
                 const float ph = sum16(gacc[v][2 * m + 1] * in0 - gacc[v][2 * m] * in1);
-                if (li == 0) PHE[((n0 + 4 * lg) / 2 + m) * TP + p0 / 16] = ph;
+                PHE[((n0 + 4 * lg) / 2 + m) * TP + p0 / 16] = ph;   // (every lane of the row: the same value)
             }
 #pragma unroll
             for (int i = 0; i < 4; i++) {
