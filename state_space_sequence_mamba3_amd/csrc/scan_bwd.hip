@@ -870,7 +870,15 @@ struct BCfg {
 };
 
 template <class CF>
-__global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
+__global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
+    // The arguments are read through the kernarg segment pointer (p below), which is made opaque
+    // at the start of every chunk: each chunk then re-reads the arguments it uses (scalar loads
+    // that hit the scalar cache) instead of holding every pointer in SGPRs across the kernel,
+    // which spilled them to VGPR lanes and reloaded them all over the chunk body.
+    (void)p_arg;
+    using KPtr = const __attribute__((address_space(4))) BwdParams *;
+    KPtr pk = (KPtr)__builtin_amdgcn_kernarg_segment_ptr();
+#define p (*pk)
     constexpr int N = CF::N, P = CF::P, R = CF::R, Q = CF::Q, NW = CF::NW, QR = CF::QR, K = CF::K2, NT = CF::NT;
     constexpr int NS = CF::NS, PS = CF::PS, QS = CF::QS, NF = CF::NF, SF = CF::SF;
     constexpr int TQ = CF::TQ, TN = CF::TN, TP = CF::TP, UPW = CF::UPW;
@@ -904,6 +912,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     // where it is used instead of being hoisted out of the chunk loops and spilled.
     auto refresh = [&]() {
         asm volatile("" : "+v"(tid));
+        asm volatile("" : "+s"(pk));
         lane = tid & 63;
         li = lane & 15;
         lg = lane >> 4;
@@ -975,60 +984,62 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
     bf16x8 pB[PF_B], pC[PF_B], pX[PF_X], pD[PF_X], pT[PF_T];
     bf16 pBp[PF_V], pXp[PF_U], pdt = {}, plm = {}, pat = {};
     f32x4 pH[UPW];   // reverse walk: the state entering the chunk, from the workspace
+    // Addressing: every prefetch load is a wave-uniform base (the chunk's first token; SGPRs) plus
+    // a 32-bit per-lane byte offset (a chunk spans at most Q tokens), so the loads take the
+    // scalar-base form and a lane holds no 64-bit address; a lane's condition is a clamped index
+    // rather than a branch.
+    const int hq = h / (H / p.Gth);   // head h's angle row
+    const uint32_t tsB = (uint32_t)G * R * N, tsX = (uint32_t)H * R * P, tsT = (uint32_t)p.Gth * K;   // per token
     auto prefetch = [&](int64_t c, bool rev) {
         const int64_t c0 = c * Q;
         const int last = (int)min((int64_t)Q, len - c0) - 1;
+        const char *bB = (const char *)(gB + tokB(c0)), *bC = (const char *)(gC + tokB(c0));
+        const char *bX = (const char *)(gx + tokX(c0)), *bD = (const char *)(gdy + tokX(c0));
+        const char *bT = (const char *)((const bf16 *)p.theta + ((start + c0) * p.Gth + hq) * (int64_t)K);
 #pragma unroll
         for (int i = 0; i < PF_B; i++) {
-            const int e = tid + i * NT;
-            if (e < QR * N / 8) {
-                const int r = e / (N / 8), n = (e % (N / 8)) * 8;
-                const int64_t o = tokB(c0 + min(r / R, last)) + (r % R) * N + n;
-                pB[i] = *(const bf16x8 *)(gB + o);
-                if (rev) pC[i] = *(const bf16x8 *)(gC + o);
-            }
+            const int e = min(tid + i * NT, QR * N / 8 - 1);   // (surplus threads repeat the last piece)
+            const int r = e / (N / 8), n = (e % (N / 8)) * 8;
+            const uint32_t o = ((uint32_t)min(r / R, last) * tsB + (uint32_t)((r % R) * N + n)) * 2u;
+            pB[i] = *(const bf16x8 *)(bB + o);
+            if (rev) pC[i] = *(const bf16x8 *)(bC + o);
         }
 #pragma unroll
         for (int i = 0; i < PF_X; i++) {
-            const int e = tid + i * NT;
-            if (e < QR * P / 8) {
-                const int r = e / (P / 8), pp = (e % (P / 8)) * 8;
-                const int64_t o = tokX(c0 + min(r / R, last)) + (r % R) * P + pp;
-                pX[i] = *(const bf16x8 *)(gx + o);
-                if (rev) pD[i] = *(const bf16x8 *)(gdy + o);
-            }
+            const int e = min(tid + i * NT, QR * P / 8 - 1);
+            const int r = e / (P / 8), pp = (e % (P / 8)) * 8;
+            const uint32_t o = ((uint32_t)min(r / R, last) * tsX + (uint32_t)((r % R) * P + pp)) * 2u;
+            pX[i] = *(const bf16x8 *)(bX + o);
+            if (rev) pD[i] = *(const bf16x8 *)(bD + o);
         }
 #pragma unroll
         for (int i = 0; i < PF_T; i++) {
-            const int e = tid + i * NT;
-            if (e < Q * K / 8)
-                pT[i] = *(const bf16x8 *)((const bf16 *)p.theta + th_row(p, start + c0 + min(e / (K / 8), last), h) +
-                                          (e % (K / 8)) * 8);
+            const int e = min(tid + i * NT, Q * K / 8 - 1);
+            const uint32_t o = ((uint32_t)min(e / (K / 8), last) * tsT + (uint32_t)((e % (K / 8)) * 8)) * 2u;
+            pT[i] = *(const bf16x8 *)(bT + o);
         }
         const bf16 *srcB = c0 > 0 ? gB + tokB(c0 - 1) : has_prev ? (const bf16 *)p.Bprev + ((int64_t)s * G + g) * R * N : nullptr;
         const bf16 *srcX = c0 > 0 ? gx + tokX(c0 - 1) : has_prev ? (const bf16 *)p.xprev + sh * R * P : nullptr;
+        if (srcB) {   // (uniform)
 #pragma unroll
-        for (int i = 0; i < PF_V; i++) {
-            const int e = tid + i * NT;
-            if (srcB && e < R * N) pBp[i] = srcB[e];
-        }
+            for (int i = 0; i < PF_V; i++) pBp[i] = srcB[min(tid + i * NT, R * N - 1)];
 #pragma unroll
-        for (int i = 0; i < PF_U; i++) {
-            const int e = tid + i * NT;
-            if (srcX && e < R * P) pXp[i] = srcX[e];
+            for (int i = 0; i < PF_U; i++) pXp[i] = srcX[min(tid + i * NT, R * P - 1)];
         }
         if (rev) {
-            const float *ws = wsS(c);
+            const char *ws = (const char *)wsS(c);
 #pragma unroll
             for (int v = 0; v < UPW; v++)
 #pragma unroll
-                for (int i = 0; i < 4; i++) pH[v][i] = ws[(tile_n0(v) + 4 * lg + i) * P + tile_p0(v) + li];
+                for (int i = 0; i < 4; i++)
+                    pH[v][i] = *(const float *)(ws + (uint32_t)((tile_n0(v) + 4 * lg + i) * P + tile_p0(v) + li) * 4u);
         }
         if (wave == 0) {
-            const int64_t i = (start + c0 + min(lane, last)) * H + h;
-            pdt = ((const bf16 *)p.dt)[i];
-            if (p.lam) plm = ((const bf16 *)p.lam)[i];
-            if (p.A_tok) pat = ((const bf16 *)p.A_tok)[i];
+            const int64_t t0 = (start + c0) * H + h;
+            const uint32_t o = (uint32_t)min(lane, last) * (uint32_t)H * 2u;
+            pdt = *(const bf16 *)((const char *)((const bf16 *)p.dt + t0) + o);
+            if (p.lam) plm = *(const bf16 *)((const char *)((const bf16 *)p.lam + t0) + o);
+            if (p.A_tok) pat = *(const bf16 *)((const char *)((const bf16 *)p.A_tok + t0) + o);
         }
     };
     // em: also the decay table EM (the reverse walk's)
@@ -1830,6 +1841,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p) {
         p.p_dBb[sh * N + n] = BBA[n];
         p.p_dCb[sh * N + n] = CBA[n];
     }
+#undef p
 }
 
 // (N, P, R) -> chunk length and waves of the MFMA backward
