@@ -27,6 +27,47 @@ template <> __device__ __forceinline__ float from_f<float>(float v) { return v; 
 // gfx950 converts with v_cvt_pk_bf16_f32 (round to nearest even).
 template <> __device__ __forceinline__ bf16 from_f<bf16>(float v) { return (bf16)v; }
 
+// Lane moves by DPP (within the VALU, no LDS round trip). dpp_move<CTRL, ROWS>(v): lane i gets the
+// value of the lane CTRL selects, or 0 where that lane does not exist or i's row is not in ROWS.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 within each 16-lane row,
+// then each row's total carried to the rows after it (row_bcast:15 into rows 1 and 3, row_bcast:31
+// into rows 2 and 3).
+__device__ __forceinline__ float wave_scan_dpp(float v) {
+    v += dpp_move<0x111>(v);
+    v += dpp_move<0x112>(v);
+    v += dpp_move<0x114>(v);
+    v += dpp_move<0x118>(v);
+    v += dpp_move<0x142, 0xA>(v);
+    v += dpp_move<0x143, 0xC>(v);
+    return v;
+}
+// Inclusive prefix sum within aligned groups of J consecutive lanes (J = 2, 4, 8 or 16; lane j of
+// its group, j = lane % J).
+template <int J>
+__device__ __forceinline__ float group_scan_dpp(float v, int j) {
+    static_assert(J == 2 || J == 4 || J == 8 || J == 16, "groups inside a 16-lane row");
+    float o;
+    o = dpp_move<0x111>(v);
+    if (j >= 1) v += o;
+    if constexpr (J > 2) {
+        o = dpp_move<0x112>(v);
+        if (j >= 2) v += o;
+    }
+    if constexpr (J > 4) {
+        o = dpp_move<0x114>(v);
+        if (j >= 4) v += o;
+    }
+    if constexpr (J > 8) {
+        o = dpp_move<0x118>(v);
+        if (j >= 8) v += o;
+    }
+    return v;
+}
+
 // Launch plumbing shared by the kernels' host-side entry points.
 struct ScanPlan {
     const mamba3_scan_args *a;

@@ -1053,13 +1053,8 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
                 lv = p.lam ? (float)plm : p.lam_fixed;
                 if (p.A_tok) av = (float)pat;
             }
-            float acc = dtv * av;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(acc, off, 64);
-                if (lane >= off) acc += o;
-            }
-            const float dln = __shfl_down((1.f - lv) * dtv, 1, 64);
+            const float acc = wave_scan_dpp(dtv * av);         // DPP lane moves
+            const float dln = dpp_move<0x130>((1.f - lv) * dtv);   // wave_shl:1, the next token's
             if (t < Q) {
                 DT[t] = dtv;
                 LM[t] = lv;
@@ -1082,7 +1077,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
         {   // cumulative angles: J consecutive lanes per pair, TPG tokens each; a lane's running sum
             // over its tokens, then an exclusive scan of the lane totals across the pair's J lanes
             constexpr int J = NT / K, TPG = Q / J;
-            static_assert(NT % K == 0 && Q % J == 0 && (J & (J - 1)) == 0 && J <= 64, "angle split");
+            static_assert(NT % K == 0 && Q % J == 0 && (J & (J - 1)) == 0 && J <= 16, "angle split");
             const int k = tid / J, j = tid % J;
             float a[TPG], run = 0.f;
 #pragma unroll
@@ -1091,13 +1086,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
                 run += DT[t] * (float)TH[t * K + k];
                 a[i] = run;
             }
-            float ex = run;
-#pragma unroll
-            for (int off = 1; off < J; off <<= 1) {
-                const float o = __shfl_up(ex, off, J);
-                if (j >= off) ex += o;
-            }
-            ex -= run;
+            const float ex = group_scan_dpp<J>(run, j) - run;
 #pragma unroll
             for (int i = 0; i < TPG; i++) {
                 const int t = j * TPG + i;
