@@ -47,12 +47,22 @@ __device__ __forceinline__ int opaque(int v) {
 __device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 __device__ __forceinline__ float wave_incl_scan(float v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        float o = __shfl_up(v, off, 64);
-        if (lane >= off) v += o;
-    }
-    return v;
+    (void)lane;
+    return wave_scan_dpp(v);   // DPP lane moves (no LDS round trip)
+}
+// The value of lane l (uniform l) in every lane.
+__device__ __forceinline__ float wave_bcast(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// Maximum over the 64 lanes of values >= 0, in every lane (a DPP max-scan, then lane 63's value).
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    v = fmaxf(v, dpp_move<0x111>(v));
+    v = fmaxf(v, dpp_move<0x112>(v));
+    v = fmaxf(v, dpp_move<0x114>(v));
+    v = fmaxf(v, dpp_move<0x118>(v));
+    v = fmaxf(v, dpp_move<0x142, 0xA>(v));
+    v = fmaxf(v, dpp_move<0x143, 0xC>(v));
+    return wave_bcast(v, 63);
 }
 
 // 2^x for x <= 0 (hardware exp2; results below the fp32 normal range flush to 0)

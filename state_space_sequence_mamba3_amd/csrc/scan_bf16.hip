@@ -450,13 +450,13 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 const float dt = ok ? to_f(h_dt) : 0.f, lm = ok ? lamv(h_lam) : 0.f;
                 const float gm = lm * dt, dl = (1.f - lm) * dt;
                 const float s2 = wave_incl_scan(dt * a2v(h_A), lane);
-                const float s2e = __shfl(s2, nq - 1, 64);
+                const float s2e = wave_bcast(s2, nq - 1);
                 const float dn = (c0 + nq < len) ? (1.f - lamv(h_lamn)) * to_f(h_dtn) : 0.f;
                 const float dl1 = __shfl_down(dl, 1, 64);
                 const float g1 = gm + ((t + 1 < nq) ? dl1 : ((t + 1 == nq) ? dn : 0.f));
                 // mask factor relative to the first token of t's 32-row tile (>= 1)
                 const float f = __builtin_amdgcn_exp2f(__shfl(s2, (t / TOKS32) * TOKS32, 64) - s2);
-                const float s2first = __shfl(s2, 0, 64), s2last = __shfl(s2, Q - 1, 64);
+                const float s2first = wave_bcast(s2, 0), s2last = wave_bcast(s2, Q - 1);
                 if (t < Q) {
                     DT[t] = dt;
                     S2[t] = s2;

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             float s2v[PER];
 #pragma unroll
             for (int i = 0; i < PER; i++) s2v[i] = excl + loc[i];
-            const float s2e = __shfl(s2v[PER - 1], 63, 64);   // S2 of the chunk's last token (dt = 0 past the end)
+            const float s2e = wave_bcast(s2v[PER - 1], 63);   // S2 of the chunk's last token (dt = 0 past the end)
             const float dn = MISC[0];
             // the fast form needs bounded scale factors and a finite gamma / (gamma + delta) ratio
             bool bad = false;
@@ -347,8 +347,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 bad |= g1v[i] == 0.f && GM[t] != 0.f;
                 mx = fmaxf(mx, fabsf(s2v[i]));
             }
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            mx = wave_max_nonneg(mx);
             const bool fast = __ballot(bad) == 0 && mx <= 100.f;
 #pragma unroll
             for (int i = 0; i < PER; i++) {
