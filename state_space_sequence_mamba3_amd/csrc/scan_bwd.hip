@@ -1026,14 +1026,6 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
 #pragma unroll
             for (int i = 0; i < PF_U; i++) pXp[i] = srcX[min(tid + i * NT, R * P - 1)];
         }
-        if (rev) {
-            const char *ws = (const char *)wsS(c);
-#pragma unroll
-            for (int v = 0; v < UPW; v++)
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    pH[v][i] = *(const float *)(ws + (uint32_t)((tile_n0(v) + 4 * lg + i) * P + tile_p0(v) + li) * 4u);
-        }
         if (wave == 0) {
             const int64_t t0 = (start + c0) * H + h;
             const uint32_t o = (uint32_t)min(lane, last) * (uint32_t)H * 2u;
@@ -1041,6 +1033,16 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
             if (p.lam) plm = *(const bf16 *)((const char *)((const bf16 *)p.lam + t0) + o);
             if (p.A_tok) pat = *(const bf16 *)((const char *)((const bf16 *)p.A_tok + t0) + o);
         }
+    };
+    // reverse walk: the state entering chunk c, issued in a phase of its own (the previous chunk's
+    // contractions are done by then), so its loads do not queue with the token inputs'
+    auto prefetch_state = [&](int64_t c) {
+        const char *ws = (const char *)wsS(c);
+#pragma unroll
+        for (int v = 0; v < UPW; v++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                pH[v][i] = *(const float *)(ws + (uint32_t)((tile_n0(v) + 4 * lg + i) * P + tile_p0(v) + li) * 4u);
     };
     // em: also the decay table EM (the reverse walk's)
     auto load_scalars = [&](int64_t c0, int nq, bool em) {
@@ -1279,7 +1281,10 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
     for (int e = tid; e < R; e += NT) INVBP[e] = 1.f;
     float bbias[8] = {}, cbias[8] = {};   // this thread's columns of the bias gradients
     __syncthreads();
-    if (nch > 0) prefetch(nch - 1, true);
+    if (nch > 0) {
+        prefetch(nch - 1, true);
+        prefetch_state(nch - 1);
+    }
     for (int64_t c = nch - 1; c >= 0; c--) {
         const int64_t c0 = c * Q;
         const int nq = (int)min((int64_t)Q, len - c0), e_ = nq - 1;
@@ -1541,6 +1546,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
             if (lane == 0) RED[wave] = w;
         }
         __syncthreads();   // (also orders every write above before the reads below)
+        if (c > 0) prefetch_state(c - 1);
         // The fold's products with dH' (in registers): dH' Xp^T and dH'^T Bp, as per-tile partial
         // sums in LDS (Gb is free: G^ is no longer read), added up below in a fixed order.
         // A wave's tiles share one row block and cover UPW consecutive column blocks, so dH' Xp^T
