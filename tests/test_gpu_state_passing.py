@@ -336,3 +336,31 @@ def test_packed_entering_states(oracle, dtype):
         for k in range(1, n):
             assert np.array_equal(xb[r + k], x_all[a + k * L - 1]) and np.array_equal(Bb[r + k], B_all[a + k * L - 1])
         r += n
+
+
+def test_packed_segmented_full_size_sampled(oracle):
+    """The packed workload (8 sequences, 65536 tokens, 64 heads, N = 128, R = 4, chunk 128) in the
+    bench's segmented launch configuration (segments of 4096 tokens): sampled (sequence, head)
+    slabs, including the longest sequence (five segments) and the shortest, against the oracle's
+    whole-sequence scan of each slab (G = H: a head reads only its own rows)."""
+    import torch
+    from tests.test_gpu_bf16_scan import _slab_inputs
+    c = synth.CONFIGS[4]
+    d = synth.torch_scan_inputs(4, device(), seed=4)
+    note("packed segmented scan, 65536 tokens, segments of 4096")
+    y, h = m3.mamba3_scan_segmented(d["x"], d["dt"], d["lam"], d["theta"], d["B"], d["C"], d["A"], d["D"],
+                                    seg_tokens=4096, cu_seqlens=d["cu_seqlens"], chunk=c["chunk"])
+    torch.cuda.synchronize()
+    cu = d["cu_seqlens"].cpu().numpy()
+    ln = np.diff(cu)
+    S, H = len(cu) - 1, c["nheads"]
+    picks = [(int(np.argmax(ln)), 5), (int(np.argmin(ln)), H - 1), (3, 40)]
+    for s, hh in picks:
+        yo, ho = oracle.scan_slab(_slab_inputs(d, s, hh, cu), 0, 0)
+        yg = y[0, int(cu[s]):int(cu[s + 1]), hh]
+        ey = float(np.abs(from_dev(yg) - yo).max() / np.abs(yo).max())
+        eh = float(np.abs(from_dev(h[s, hh]) - ho).max() / np.abs(ho).max())
+        note(f"  slab (s={s}, h={hh}) len={yo.shape[0]}: y relerr {ey:.2e}  h relerr {eh:.2e}")
+        assert ey < TOL_BF16 and eh < TOL_BF16
+    del d, y, h
+    torch.cuda.empty_cache()
