@@ -830,7 +830,9 @@ template <int N_, int P_, int R_, int Q_, int NW_>
 struct BCfg {
     static constexpr int N = N_, P = P_, R = R_, Q = Q_, NW = NW_;
     static constexpr int QR = Q * R, K2 = N / 2, NT = NW * 64;
-    static constexpr int NS = N + 8, PS = P + 8, QS = QR + 8, NF = N + 1, SF = QR + 1;
+    // NF: fp32 dC~ / dB~ rows, 16-byte aligned (their pieces are read as vectors; the tile
+    // epilogues' 4-byte writes of 16 columns by rows 4 apart still meet no bank conflict)
+    static constexpr int NS = N + 8, PS = P + 8, QS = QR + 8, NF = N + 4, SF = QR + 1;
     static constexpr int TQ = QR / 16, TN = N / 16, TP = P / 16, NPT = TN * TP, UPW = NPT / NW;
     static_assert(QR % 32 == 0 && N % 32 == 0 && P % 32 == 0 && NPT % NW == 0, "MFMA backward tiling");
     static_assert(R == 1 || R == 2 || R == 4, "rank");
@@ -1593,8 +1595,10 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
             float a = 0.f;
             for (int j = 0; j < R; j++) {
                 const int r = t * R + j;
-                a += dCf[r * NF + 2 * k] * (float)Ct[r * NS + 2 * k + 1] - dCf[r * NF + 2 * k + 1] * (float)Ct[r * NS + 2 * k];
-                a += dBf[r * NF + 2 * k] * (float)Bt[r * NS + 2 * k + 1] - dBf[r * NF + 2 * k + 1] * (float)Bt[r * NS + 2 * k];
+                const float2 dc = *(const float2 *)(dCf + r * NF + 2 * k), db = *(const float2 *)(dBf + r * NF + 2 * k);
+                const bf16x2 cc = *(const bf16x2 *)(Ct + r * NS + 2 * k), bb = *(const bf16x2 *)(Bt + r * NS + 2 * k);
+                a += dc.x * (float)cc[1] - dc.y * (float)cc[0];
+                a += db.x * (float)bb[1] - db.y * (float)bb[0];
             }
             DPHI[t * K + k] += a;
         }
@@ -1643,39 +1647,36 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
             if (lane == 0) RED[8 + wave] = w;
         }
         __syncthreads();
-        // reverse prefix sums over the chunk's tokens (past the end every term is zero): each pair's
-        // column read whole into registers, summed, written back
-        for (int k = tid; k < K; k += NT) {
-            float v[Q];
+        // reverse prefix sums over the chunk's tokens (past the end every term is zero). dPhi: J
+        // consecutive lanes per pair, lane j holding TPG tokens counted from the chunk's end; its
+        // own suffix sums, then the totals of the lanes holding later tokens (a DPP prefix sum over
+        // the J lanes) added to them.
+        {
+            constexpr int J = NT / K, TPG = Q / J;
+            const int k = tid / J, j = tid % J;
+            float v[TPG];
 #pragma unroll
-            for (int t = 0; t < Q; t++) v[t] = DPHI[t * K + k];
-            float acc = 0.f;
+            for (int i = 0; i < TPG; i++) v[i] = DPHI[((J - 1 - j) * TPG + i) * K + k];
 #pragma unroll
-            for (int t = Q - 1; t >= 0; t--) {
-                acc += v[t];
-                DPHI[t * K + k] = acc;
-            }
+            for (int i = TPG - 2; i >= 0; i--) v[i] += v[i + 1];
+            const float later = group_scan_dpp<J>(v[0], j) - v[0];
+#pragma unroll
+            for (int i = 0; i < TPG; i++) DPHI[((J - 1 - j) * TPG + i) * K + k] = v[i] + later;
         }
-        if (tid == NT - 1) {   // (a thread of the last wave, idle in the loop above)
-            // the fold's d delta_0 and the state's share of dS_e, then dS's reverse prefix
+        if (wave == NW - 1) {   // the last wave: the fold's d delta_0, the state's share of dS_e,
+            // then dS's reverse prefix (lane i holds token Q - 1 - i, so a prefix sum over the
+            // lanes is the suffix sum over the tokens)
             float gh = 0.f, fold = 0.f;
             for (int w = 0; w < NW; w++) {
                 gh += RED[w];
                 fold += RED[8 + w];
             }
-            DDL[0] += fold;
-            float dSe = ES[e_] * gh;
-            for (int u = 0; u < nq; u++) dSe += TMPC[u];
-            DS[e_] += dSe;
-            float v[Q];
-#pragma unroll
-            for (int t = 0; t < Q; t++) v[t] = DS[t];
-            float acc = 0.f;
-#pragma unroll
-            for (int t = Q - 1; t >= 0; t--) {
-                acc += v[t];
-                DS[t] = acc;
-            }
+            if (lane == 0) DDL[0] += fold;
+            const float dSe = ES[e_] * gh + wave_sum((lane < nq) ? TMPC[lane] : 0.f);
+            const int t = Q - 1 - lane;
+            float v = (t >= 0) ? DS[t] + ((t == e_) ? dSe : 0.f) : 0.f;
+            v = wave_scan_dpp(v);
+            if (t >= 0) DS[t] = v;
         }
         __syncthreads();
         {   // dtheta = dt dPhi, 8 pairs of a token per thread (one 16-byte store), and ddt: the
@@ -1737,10 +1738,11 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
 #pragma unroll
             for (int isC = 0; isC < 2; isC++) {
                 const float *gsrc = (isC ? dCf : dBf) + r * NF + n;
+                const f32x4 g0 = *(const f32x4 *)gsrc, g1 = *(const f32x4 *)(gsrc + 4);
                 float v[8];
 #pragma unroll
                 for (int m = 0; m < 4; m++) {
-                    const float d0 = gsrc[2 * m], d1 = gsrc[2 * m + 1];
+                    const float d0 = (m < 2) ? g0[2 * m] : g1[2 * m - 4], d1 = (m < 2) ? g0[2 * m + 1] : g1[2 * m - 3];
                     v[2 * m] = cs[m] * d0 - sn[m] * d1;
                     v[2 * m + 1] = sn[m] * d0 + cs[m] * d1;
                 }
