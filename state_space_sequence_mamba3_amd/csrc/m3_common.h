@@ -83,12 +83,12 @@ bool scan_bf16_supported(int N, int P, int R, int Q);
 bool scan_mimo_supported(const mamba3_scan_args *a);
 mamba3_status launch_scan_mimo(const mamba3_scan_args *a, hipStream_t st);
 // State-only bf16 scan (a->y NULL) that may also write the state entering every chunk into
-// ws_state (padded batches only: [S * ceil(seqlen / chunk)][H][N][P] fp32, the backward's chunk
-// states) and each sequence's decay and angle sums into seg_sums (the first K + 1 floats of each
+// ws_state (padded batches only: [S * ceil(seqlen / chunk)][H][P][N] bf16, the MFMA backward's
+// chunk states) and each sequence's decay and angle sums into seg_sums (the first K + 1 floats of each
 // [S][H][N][P] block: the segment sums of state passing). scan_bf16_states_supported
 // covers the scan's shapes and the backward's chunks.
 bool scan_bf16_states_supported(int N, int P, int R, int Q);
-mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, float *ws_state, float *seg_sums, hipStream_t st);
+mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, bf16 *ws_state, float *seg_sums, hipStream_t st);
 size_t scan_f32_lds_bytes(int N, int P, int R, int Q);
 mamba3_status launch_decode(const mamba3_decode_args *a, hipStream_t st);
 mamba3_status launch_scan_bwd(const mamba3_scan_bwd_args *b, hipStream_t st);

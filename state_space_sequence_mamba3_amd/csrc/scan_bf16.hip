@@ -90,9 +90,9 @@ struct BfParams {
     int32_t atok_on, lam_on;
     float lam_fixed;
     int32_t Gth;            // angle rows per token (divides H): head h reads row h / (H / Gth)
-    // state-only scans: the state entering every chunk, [S * chunks][H][N][P] fp32 (the
-    // backward's chunk-state layout), or NULL
-    float *ws_state;
+    // state-only scans: the state entering every chunk, [S * chunks][H][P][N] bf16 (the MFMA
+    // backward's chunk-state layout: a state column's N rows contiguous), or NULL
+    bf16 *ws_state;
     // state-only scans: sum_t dt_t A_t and sum_t dt_t theta_t[k] over each sequence, written to
     // the first K + 1 floats of its [S][H][N][P] block (the segment sums that state passing
     // reads), or NULL
@@ -428,13 +428,14 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         if constexpr (!CF::YO) {
             // the state entering the chunk, with the previous-token term of its first token
             // (folded into the previous chunk's last weight, or added from Bprev for chunk 0)
-            if (pr.ws_state) {
-                float *wsc = pr.ws_state + ((s * (((int64_t)pr.seqlen + Q - 1) / Q) + c0 / Q) * H + h) * (int64_t)N * P;
+            if (pr.ws_state) {   // registers 4j .. 4j + 3 hold four consecutive rows: one 8-byte piece
+                bf16 *wsc = pr.ws_state + ((s * (((int64_t)pr.seqlen + Q - 1) / Q) + c0 / Q) * H + h) * (int64_t)N * P;
 #pragma unroll
                 for (int v = 0; v < UPW; v++)
 #pragma unroll
-                    for (int r = 0; r < UR_; r++)
-                        wsc[(int64_t)(ut_n0[v] + urow(r)) * P + ut_p0[v] + ucol] = hreg[v][r];
+                    for (int r = 0; r < UR_; r += 4)
+                        *(bf16x4 *)(wsc + (ut_p0[v] + ucol) * N + ut_n0[v] + urow(r)) =
+                            bf16x4{(bf16)hreg[v][r], (bf16)hreg[v][r + 1], (bf16)hreg[v][r + 2], (bf16)hreg[v][r + 3]};
             }
         }
         int task_tb[TPA];
@@ -1059,7 +1060,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 template <class CF>
-mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st, float *ws_state = nullptr,
+mamba3_status launch_cfg(const mamba3_scan_args *a, hipStream_t st, bf16 *ws_state = nullptr,
                          float *seg_sums = nullptr) {
     BfParams p;
     p.ws_state = ws_state;
@@ -1116,7 +1117,7 @@ bool scan_bf16_states_supported(int N, int P, int R, int Q) {
     return false;
 }
 
-mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, float *ws_state, float *seg_sums, hipStream_t st) {
+mamba3_status launch_scan_bf16_states(const mamba3_scan_args *a, bf16 *ws_state, float *seg_sums, hipStream_t st) {
     if (a->y) return MAMBA3_EINVAL;
     if (ws_state && a->cu_seqlens) return MAMBA3_EUNSUPPORTED;
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;

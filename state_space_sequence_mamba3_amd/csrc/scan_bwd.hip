@@ -44,7 +44,8 @@ struct BwdParams {
     const float *A, *D, *h_in, *dh_out, *Bb, *Cb;
     void *dx, *ddt, *dlam, *dtheta, *dB, *dC, *dBprev, *dxprev, *dz;
     float *dh_in, *dA, *dD, *dB_bias, *dC_bias;
-    float *ws_state;          // [chunks][H][N][P] state entering each chunk
+    float *ws_state;          // VALU kernel: [chunks][H][N][P] fp32 state entering each chunk
+    bf16 *ws_hs;              // MFMA kernel: [chunks][H][P][N] bf16 state entering each chunk
     float *p_dA, *p_dD;       // [S][H]
     float *p_dBb, *p_dCb;     // [S][H][N]
     float *p_dB, *p_dC;       // [T][H][R][N] per-head partials (G < H), else NULL
@@ -58,7 +59,7 @@ struct BwdParams {
     void *dA_tok;             // its gradient
     float lam_fixed;          // trapezoid weight of every token when lam is NULL
     int32_t Gth;              // angle rows per token (divides H): head h reads row h / (H / Gth)
-    int32_t fwd_states;       // MFMA kernel: the chunk states are already in ws_state (no forward walk)
+    int32_t fwd_states;       // MFMA kernel: the chunk states are already in ws_hs (no forward walk)
     float *p_dth;             // [T][H][K] per-head dtheta partials (Gth < H), else NULL
 };
 
@@ -764,7 +765,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_scan_bwd(BwdParams p) {
 // The same chunked backward with every chunk contraction on v_mfma_f32_16x16x32_bf16: bf16
 // operands staged in LDS, fp32 accumulation. The state entering each chunk (forward pass) and
 // the carried gradient dH (reverse pass) live in fp32 accumulator registers; each wave owns
-// N x P tiles of both. Per chunk: scores S = C~ B~^T and dP = dY X^T on the causal tiles
+// N x P tiles of both. The chunk states go through the workspace in bf16, column-major per
+// chunk ([P][N]: a lane's four consecutive rows are one 8-byte piece): the state's bf16 copy is
+// what the contractions read anyway, and only the e^{S_e} H' terms of the rotated state and of
+// the chunk's decay gradient see the rounding, each once (the chain itself stays fp32). Per chunk: scores S = C~ B~^T and dP = dY X^T on the causal tiles
 // (masked into A = M o S and dS' = M o dP), then dX = A^T dY + c o (B~ G^), dC~ = dS' B~ +
 // e^{S} o (dY H'^T), dB~ = dS'^T C~ + c o (X G^^T), dH' = e^{S_e} G^ + C~^T (e^{S} o dY) and the
 // rotated state Inner = e^{S_e} H' + B~^T (c o X). Row and column sums that the scalar
@@ -948,7 +952,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
     const int64_t sh = (int64_t)s * H + h;
     const float *Bbh = p.Bb ? p.Bb + (int64_t)h * N : nullptr;
     const float *Cbh = p.Cb ? p.Cb + (int64_t)h * N : nullptr;
-    auto wsS = [&](int64_t c) { return p.ws_state + ((cbase + c) * H + h) * (int64_t)N * P; };
+    auto wsS = [&](int64_t c) { return p.ws_hs + ((cbase + c) * H + h) * (int64_t)N * P; };
     auto tokB = [&](int64_t t) { return ((start + t) * G + g) * (int64_t)R * N; };
     auto tokX = [&](int64_t t) { return ((start + t) * H + h) * (int64_t)R * P; };
     // this wave's N x P tiles: tile v covers rows n0 .. n0 + 15, columns p0 .. p0 + 15; the lane
@@ -985,7 +989,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
     constexpr int PF_T = (Q * K / 8 + NT - 1) / NT, PF_V = (R * N + NT - 1) / NT, PF_U = (R * P + NT - 1) / NT;
     bf16x8 pB[PF_B], pC[PF_B], pX[PF_X], pD[PF_X], pT[PF_T];
     bf16 pBp[PF_V], pXp[PF_U], pdt = {}, plm = {}, pat = {};
-    f32x4 pH[UPW];   // reverse walk: the state entering the chunk, from the workspace
+    bf16x4 pH[UPW];  // reverse walk: the state entering the chunk (rows 4 lg .. 4 lg + 3), from the workspace
     // Addressing: every prefetch load is a wave-uniform base (the chunk's first token; SGPRs) plus
     // a 32-bit per-lane byte offset (a chunk spans at most Q tokens), so the loads take the
     // scalar-base form and a lane holds no 64-bit address; a lane's condition is a clamped index
@@ -1042,9 +1046,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
         const char *ws = (const char *)wsS(c);
 #pragma unroll
         for (int v = 0; v < UPW; v++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                pH[v][i] = *(const float *)(ws + (uint32_t)((tile_n0(v) + 4 * lg + i) * P + tile_p0(v) + li) * 4u);
+            pH[v] = *(const bf16x4 *)(ws + (uint32_t)((tile_p0(v) + li) * N + tile_n0(v) + 4 * lg) * 2u);
     };
     // em: also the decay table EM (the reverse walk's)
     auto load_scalars = [&](int64_t c0, int nq, bool em) {
@@ -1233,17 +1235,19 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
         stage_prev(c0);
         load_scalars(c0, nq, false);
         prologue_prev(c0);
-        float *ws = wsS(c);
+        bf16 *ws = wsS(c);
 #pragma unroll
-        for (int v = 0; v < UPW; v++)
+        for (int v = 0; v < UPW; v++) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int n = tile_n0(v) + 4 * lg + i, pp = tile_p0(v) + li;
                 float acc = 0.f;
                 for (int j = 0; j < R; j++) acc += Bp[j * N + n] * Xp[j * P + pp];
                 hacc[v][i] += DL[0] * acc;
-                ws[n * P + pp] = hacc[v][i];
             }
+            *(bf16x4 *)(ws + (tile_p0(v) + li) * N + tile_n0(v) + 4 * lg) =
+                bf16x4{(bf16)hacc[v][0], (bf16)hacc[v][1], (bf16)hacc[v][2], (bf16)hacc[v][3]};
+        }
         stage_chunk(c0, nq, false);
         if (c + 1 < nch) prefetch(c + 1, false);
 #pragma unroll
@@ -1310,7 +1314,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int n = n0 + 4 * lg + i, pp = p0 + li;
-                hcur[v][i] = pH[v][i];
+                hcur[v][i] = (float)pH[v][i];
                 Gb[n * PS + pp] = (bf16)gacc[v][i];
                 Hb[n * PS + pp] = (bf16)hcur[v][i];
             }
@@ -1944,7 +1948,8 @@ struct BwdWs {
     size_t state, pA, pD, pBb, pCb, pB, pC, pBprev, pth, total;
     int64_t chunks;
 };
-static BwdWs bwd_ws(const mamba3_scan_bwd_args *b, int Q) {
+// mfma: the MFMA kernel's chunk states are bf16 (the VALU kernel's fp32)
+static BwdWs bwd_ws(const mamba3_scan_bwd_args *b, int Q, bool mfma) {
     const mamba3_scan_args *a = &b->fwd;
     const int64_t S = a->cu_seqlens ? a->nseq : a->batch, T = (int64_t)a->batch * a->seqlen;
     const int64_t H = a->nheads, N = a->dstate, P = a->headdim, R = a->rank;
@@ -1954,7 +1959,7 @@ static BwdWs bwd_ws(const mamba3_scan_bwd_args *b, int Q) {
     BwdWs w;
     size_t o = 0;
     w.chunks = chunks;
-    w.state = o; o += al((size_t)chunks * H * N * P * 4);
+    w.state = o; o += al((size_t)chunks * H * N * P * (mfma ? 2 : 4));
     w.pA = o; o += al((size_t)S * H * 4);
     w.pD = o; o += al((size_t)S * H * 4);
     w.pBb = o; o += al((size_t)S * H * N * 4);
@@ -1977,8 +1982,9 @@ static int bwd_path_chunk(const mamba3_scan_args *a, bool *mfma) {
 }
 
 size_t scan_bwd_workspace_bytes(const mamba3_scan_bwd_args *b) {
-    const int Q = bwd_path_chunk(&b->fwd, nullptr);
-    return Q ? bwd_ws(b, Q).total : 0;
+    bool mfma = false;
+    const int Q = bwd_path_chunk(&b->fwd, &mfma);
+    return Q ? bwd_ws(b, Q, mfma).total : 0;
 }
 
 template <typename T>
@@ -1986,7 +1992,7 @@ static mamba3_status launch_bwd_t(const mamba3_scan_bwd_args *b, hipStream_t st)
     const mamba3_scan_args *a = &b->fwd;
     bool mfma = false;
     const int Q = bwd_path_chunk(a, &mfma);
-    const BwdWs w = bwd_ws(b, Q);
+    const BwdWs w = bwd_ws(b, Q, mfma);
     char *ws = (char *)b->workspace;
     BwdParams p;
     p.fwd_states = 0;
@@ -1997,6 +2003,7 @@ static mamba3_status launch_bwd_t(const mamba3_scan_bwd_args *b, hipStream_t st)
     p.dBprev = b->dBprev; p.dxprev = b->dxprev; p.dz = b->dz; p.dh_in = b->dh_in;
     p.dA = b->dA; p.dD = b->dD; p.dB_bias = b->dB_bias; p.dC_bias = b->dC_bias;
     p.ws_state = (float *)(ws + w.state);
+    p.ws_hs = (bf16 *)(ws + w.state);
     p.p_dA = (float *)(ws + w.pA); p.p_dD = (float *)(ws + w.pD);
     p.p_dBb = (float *)(ws + w.pBb); p.p_dCb = (float *)(ws + w.pCb);
     const bool grouped = a->ngroups < a->nheads;
@@ -2028,7 +2035,7 @@ static mamba3_status launch_bwd_t(const mamba3_scan_bwd_args *b, hipStream_t st)
                 f.chunk = Q;
                 f.workspace = nullptr;
                 f.workspace_bytes = 0;
-                const mamba3_status fs = launch_scan_bf16_states(&f, p.ws_state, nullptr, st);
+                const mamba3_status fs = launch_scan_bf16_states(&f, p.ws_hs, nullptr, st);
                 if (fs != MAMBA3_OK) return fs;
                 p.fwd_states = 1;
             }
