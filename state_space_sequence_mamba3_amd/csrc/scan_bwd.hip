@@ -778,6 +778,28 @@ __global__ __launch_bounds__(kBwdThreads) void k_scan_bwd(BwdParams p) {
 // made opaque per chunk so that address math is recomputed rather than spilled; block-wide sums
 // go through per-wave partials read after barriers the phases need anyway.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// An empty asm that reads and rewrites v: the compiler's wait for a load into v falls here, and
+// later reads of v need none.
+template <class V>
+__device__ __forceinline__ void held(V &v) {
+    if constexpr (sizeof(V) == 16) {
+        u32x4 u = __builtin_bit_cast(u32x4, v);
+        asm volatile("" : "+v"(u));
+        v = __builtin_bit_cast(V, u);
+    } else if constexpr (sizeof(V) == 8) {
+        u32x2 u = __builtin_bit_cast(u32x2, v);
+        asm volatile("" : "+v"(u));
+        v = __builtin_bit_cast(V, u);
+    } else {
+        static_assert(sizeof(V) == 2, "16-bit element");
+        unsigned short u = __builtin_bit_cast(unsigned short, v);
+        asm volatile("" : "+v"(u));
+        v = __builtin_bit_cast(V, u);
+    }
+}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -852,8 +874,8 @@ struct BCfg {
     static constexpr int O_RPC = O_RPI + al(QR * TN * 4);           // float [QR][TP] dc partials
     static constexpr int O_PHE = O_RPC + al(QR * TP * 4);           // float [K2][TP] dPhi_e partials
     static constexpr int O_TH = O_PHE + al(K2 * TP * 4);            // bf16 [Q][K2] theta of the chunk
-    static constexpr int O_SMALL = O_TH + al(Q * K2 * 2);           // previous token, carries, biases
-    static constexpr int SMALL = 6 * R * N + 4 * R * P + R + 2 * N + 16 + 64;
+    static constexpr int O_SMALL = O_TH + al(Q * K2 * 2);           // biases, previous token, carries
+    static constexpr int SMALL = 2 * N + 6 * R * N + 4 * R * P + R + 2 * N + 16 + 64;
     static constexpr int O_DCF = O_SMALL + al(SMALL * 4);           // float [QR][NF] dC~ (raw C staging)
     static constexpr int O_DBF = O_DCF + al(QR * NF * 4);           // float [QR][NF] dB~ (raw B staging)
     // float [QR][SF] scores: over the raw C staging when it fits (QR <= N). The staging is dead
@@ -901,7 +923,8 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
     float *RPI = (float *)(smem + CF::O_RPI), *RPC = (float *)(smem + CF::O_RPC), *PHE = (float *)(smem + CF::O_PHE);
     bf16 *TH = (bf16 *)(smem + CF::O_TH);
     float *SMALLp = (float *)(smem + CF::O_SMALL);
-    float *Bp = SMALLp, *BpRaw = Bp + R * N, *Xp = BpRaw + R * N, *dBcIn = Xp + R * P, *dBcOut = dBcIn + R * N;
+    float *BBL = SMALLp, *CBL = BBL + N;   // the head's B and C biases (zero without them)
+    float *Bp = CBL + N, *BpRaw = Bp + R * N, *Xp = BpRaw + R * N, *dBcIn = Xp + R * P, *dBcOut = dBcIn + R * N;
     float *dXcIn = dBcOut + R * N, *dXcOut = dXcIn + R * P, *INVBP = dXcOut + R * P, *BBA = INVBP + R;
     float *CBA = BBA + N, *MISC = CBA + N, *RED = MISC + 16, *TMPC = RED + 16;   // RED: 16 floats, TMPC: [Q]
     float *dCf = (float *)(smem + CF::O_DCF), *dBf = (float *)(smem + CF::O_DBF), *Sf = (float *)(smem + CF::O_SF);
@@ -950,8 +973,12 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
     const bool pro = p.norm || p.Bb || p.Cb;
     const bool has_prev = p.Bprev != nullptr;
     const int64_t sh = (int64_t)s * H + h;
-    const float *Bbh = p.Bb ? p.Bb + (int64_t)h * N : nullptr;
-    const float *Cbh = p.Cb ? p.Cb + (int64_t)h * N : nullptr;
+    // the biases are read from LDS in every chunk (a global read there would wait for every
+    // memory access in flight); the first chunk's barriers order these writes
+    for (int e = tid; e < N; e += NT) {
+        BBL[e] = p.Bb ? p.Bb[(int64_t)h * N + e] : 0.f;
+        CBL[e] = p.Cb ? p.Cb[(int64_t)h * N + e] : 0.f;
+    }
     auto wsS = [&](int64_t c) { return p.ws_hs + ((cbase + c) * H + h) * (int64_t)N * P; };
     auto tokB = [&](int64_t t) { return ((start + t) * G + g) * (int64_t)R * N; };
     auto tokX = [&](int64_t t) { return ((start + t) * H + h) * (int64_t)R * P; };
@@ -961,7 +988,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
     auto tile_p0 = [&](int v) { return ((wave * UPW + v) % TP) * 16; };
 
     // Prologue of `nrows` LDS rows (raw values on entry): 16 lanes per row, N/16 columns each
-    auto prologue_rows = [&](float *rows, int nrows, int stride, const float *bias, float *invs) {
+    auto prologue_rows = [&](float *rows, int nrows, int stride, const float *bias, float *invs) {   // bias: LDS
         for (int r0 = tid >> 4; r0 < (nrows + NT / 16 - 1) / (NT / 16) * (NT / 16); r0 += NT / 16) {
             const bool ok = r0 < nrows;   // (every lane of a group reaches the shuffles)
             float *v = rows + (int64_t)(ok ? r0 : 0) * stride;
@@ -975,7 +1002,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
             if (ok) {
                 if (li == 0) invs[r0] = inv;
                 if (pro)
-                    for (int n = li; n < N; n += 16) v[n] = v[n] * inv + (bias ? bias[n] : 0.f);
+                    for (int n = li; n < N; n += 16) v[n] = v[n] * inv + bias[n];
             }
         }
     };
@@ -1047,6 +1074,33 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
 #pragma unroll
         for (int v = 0; v < UPW; v++)
             pH[v] = *(const bf16x4 *)(ws + (uint32_t)((tile_p0(v) + li) * N + tile_n0(v) + 4 * lg) * 2u);
+    };
+    // Every prefetched register taken as loaded (the reverse walk). The memory counter is in order
+    // and counts stores too, so a first read at the next chunk's start would also wait for every
+    // gradient store issued since; taken before the chunk's dtheta, dB and dC stores, the loads
+    // have long arrived and nothing is waited for.
+    auto settle = [&]() {
+#pragma unroll
+        for (int i = 0; i < PF_B; i++) {
+            held(pB[i]);
+            held(pC[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < PF_X; i++) {
+            held(pX[i]);
+            held(pD[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < PF_T; i++) held(pT[i]);
+#pragma unroll
+        for (int i = 0; i < PF_V; i++) held(pBp[i]);
+#pragma unroll
+        for (int i = 0; i < PF_U; i++) held(pXp[i]);
+        held(pdt);
+        held(plm);
+        held(pat);
+#pragma unroll
+        for (int v = 0; v < UPW; v++) held(pH[v]);
     };
     // em: also the decay table EM (the reverse walk's)
     auto load_scalars = [&](int64_t c0, int nq, bool em) {
@@ -1135,7 +1189,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
     };
     auto prologue_prev = [&](int64_t c0) {
         if (pro && (c0 > 0 || has_prev)) {
-            prologue_rows(Bp, R, N, Bbh, INVBP);
+            prologue_rows(Bp, R, N, BBL, INVBP);
             __syncthreads();
         }
     };
@@ -1165,8 +1219,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
                 inv = 1.f / sqrtf(row_sum(ss) / (float)N + p.eps);
             }
             if (n == 0) invs[r] = inv;
-            const f32x4 b0 = bias ? *(const f32x4 *)(bias + n) : f32x4{};
-            const f32x4 b1 = bias ? *(const f32x4 *)(bias + n + 4) : f32x4{};
+            const f32x4 b0 = *(const f32x4 *)(bias + n), b1 = *(const f32x4 *)(bias + n + 4);
 #pragma unroll
             for (int m = 0; m < 8; m++) u[m] = (t < nq_) ? u[m] * inv + ((m < 4) ? b0[m] : b1[m - 4]) : 0.f;
         }
@@ -1187,8 +1240,8 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
             const int e = tid + i * NT;
             if (e >= QR * N / 8) break;
             const int r = e / (N / 8), n = (e % (N / 8)) * 8;
-            stage_rows(pB[i], r, n, nq, Bbh, INVB, Bt);
-            if (rev) stage_rows(pC[i], r, n, nq, Cbh, INVC, Ct);
+            stage_rows(pB[i], r, n, nq, BBL, INVB, Bt);
+            if (rev) stage_rows(pC[i], r, n, nq, CBL, INVC, Ct);
         }
 #pragma unroll
         for (int i = 0; i < PF_X; i++) {
@@ -1227,6 +1280,8 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
             const int n = tile_n0(v) + 4 * lg + i, pp = tile_p0(v) + li;
             hacc[v][i] = p.h_in ? p.h_in[sh * N * P + n * P + pp] : 0.f;
         }
+#pragma unroll
+    for (int v = 0; v < UPW; v++) held(hacc[v]);
     if (nch > 0) prefetch(0, false);
     for (int64_t c = 0; c < nch; c++) {
         const int64_t c0 = c * Q;
@@ -1280,6 +1335,8 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
             const int n = tile_n0(v) + 4 * lg + i, pp = tile_p0(v) + li;
             dacc[v][i] = p.dh_out ? p.dh_out[sh * N * P + n * P + pp] : 0.f;
         }
+#pragma unroll
+    for (int v = 0; v < UPW; v++) held(dacc[v]);   // (else every chunk waits for memory at its first read)
     for (int e = tid; e < R * N; e += NT) dBcIn[e] = 0.f;
     for (int e = tid; e < R * P; e += NT) dXcIn[e] = 0.f;
     for (int e = tid; e < N; e += NT) BBA[e] = CBA[e] = 0.f;
@@ -1290,6 +1347,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
     if (nch > 0) {
         prefetch(nch - 1, true);
         prefetch_state(nch - 1);
+        settle();
     }
     for (int64_t c = nch - 1; c >= 0; c--) {
         const int64_t c0 = c * Q;
@@ -1683,6 +1741,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
             if (t >= 0) DS[t] = v;
         }
         __syncthreads();
+        settle();
         {   // dtheta = dt dPhi, 8 pairs of a token per thread (one 16-byte store), and ddt: the
             // token's K / 8 consecutive lanes add up its sum_k theta_k dPhi_k (DPP, within a row)
             constexpr int KG = K / 8;
@@ -1729,11 +1788,15 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
         // The bias gradients accumulate per thread (its columns are the same in every chunk) and
         // are summed over the threads at the end of the slab.
         static_assert(PF_B == 1, "one 16-byte piece of B and of C per thread");
+        // (instantiated with and without the norm, so that without it no instruction reads the
+        // raw rows' registers, which would wait for every memory access in flight)
+        auto tail = [&](auto NORMC) {
+        constexpr bool NORM = decltype(NORMC)::value;
         if (tid < QR * N / 8) {   // whole rows are active or not
             const int r = tid / (N / 8), n = (tid % (N / 8)) * 8, t = r / R, j = r % R;
             const bool live = t < nq;   // the same for every lane of the row
             bf16x8 raw[2] = {bf16x8{}, bf16x8{}};
-            if (p.norm && live) {
+            if (NORM && live) {
                 const int64_t o = tokB(c0 + t) + j * N + n;
                 raw[0] = *(const bf16x8 *)(gB + o);
                 raw[1] = *(const bf16x8 *)(gC + o);
@@ -1758,7 +1821,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
                     }
                 }
                 float dot = 0.f;
-                if (p.norm) {
+                if constexpr (NORM) {
 #pragma unroll
                     for (int m = 0; m < 8; m++) dot += v[m] * (float)raw[isC][m];
                     dot = row_sum(dot);
@@ -1769,11 +1832,16 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
                     if (isC) cbias[m] += v[m];
                     else bbias[m] += v[m];
                 }
-                const float inv = (isC ? INVC : INVB)[r];
-                const float k3 = p.norm ? dot * inv * inv * inv / (float)N : 0.f;
                 float o[8];
+                if constexpr (NORM) {
+                    const float inv = (isC ? INVC : INVB)[r];
+                    const float k3 = dot * inv * inv * inv / (float)N;
 #pragma unroll
-                for (int m = 0; m < 8; m++) o[m] = p.norm ? v[m] * inv - k3 * (float)raw[isC][m] : v[m];
+                    for (int m = 0; m < 8; m++) o[m] = v[m] * inv - k3 * (float)raw[isC][m];
+                } else {
+#pragma unroll
+                    for (int m = 0; m < 8; m++) o[m] = v[m];
+                }
                 float *part = isC ? p.p_dC : p.p_dB;
                 if (part) {
                     float *dst = part + ((start + c0 + t) * H + h) * (int64_t)R * N + j * N + n;
@@ -1785,6 +1853,9 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
                 }
             }
         }
+        };
+        if (p.norm) tail(std::true_type{});
+        else tail(std::false_type{});
         for (int e = tid; e < R * P; e += NT) dXcIn[e] = dXcOut[e];
         __syncthreads();
     }
