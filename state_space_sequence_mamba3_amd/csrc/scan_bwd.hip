@@ -1115,6 +1115,8 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
             }
             const float acc = wave_scan_dpp(dtv * av);         // DPP lane moves
             const float dln = dpp_move<0x130>((1.f - lv) * dtv);   // wave_shl:1, the next token's
+            const float g1 = lv * dtv + ((t + 1 < nq) ? dln : 0.f);
+            const float se = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), nq - 1));   // S_e
             if (t < Q) {
                 DT[t] = dtv;
                 LM[t] = lv;
@@ -1122,7 +1124,10 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
                 GM[t] = lv * dtv;
                 DL[t] = (1.f - lv) * dtv;
                 S[t] = acc;
-                G1[t] = lv * dtv + ((t + 1 < nq) ? dln : 0.f);
+                G1[t] = g1;
+                // the exponentials of the log decays here (S <= 0 and S_e - S_t <= 0), from registers
+                ES[t] = __expf(acc);
+                CU[t] = (t < nq) ? __expf(se - acc) * g1 : 0.f;
             }
         }
 #pragma unroll
@@ -1156,15 +1161,16 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
                 SN[t * K + k] = sn;
             }
         }
-        // the exponentials
-        if (em)
-            for (int e = tid; e < Q * Q; e += NT) {
+        // the decay table e^{S_t - S_u} (u <= t, else zero), branch-free
+        if (em) {
+#pragma unroll
+            for (int i = 0; i < (Q * Q + NT - 1) / NT; i++) {
+                const int e = tid + i * NT;
+                if ((Q * Q) % NT != 0 && e >= Q * Q) break;
                 const int t = e / Q, u = e % Q;
-                EM[e] = (u <= t) ? expf(S[t] - S[u]) : 0.f;
+                const float x = fminf(S[t] - S[u], 0.f);
+                EM[e] = (u <= t) ? __expf(x) : 0.f;
             }
-        for (int t = tid; t < Q; t += NT) {
-            ES[t] = expf(S[t]);
-            CU[t] = (t < nq) ? expf(S[nq - 1] - S[t]) * G1[t] : 0.f;
         }
         __syncthreads();
     };
