@@ -85,6 +85,24 @@ __device__ __forceinline__ void rot_piece(const bf16x8 raw, const f16x8 cs, floa
     for (int e = 0; e < 8; e++) in[e] = (float)raw[e];
     rot_piece_f(in, cs, o);
 }
+// The same rotation with (cos, sin) packed as bf16 pairs, on the bf16 dot-product unit: each
+// output is one v_dot2_f32_bf16 (two bf16 products summed in fp32) of the raw pair, so neither
+// the row nor the table is widened first. The first output takes (c, s).(u, v); the second takes
+// the pair swapped (a 16-bit funnel shift) against (c, -s) (the instruction's neg_hi modifier on
+// the table operand).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void rot_piece_bf(const bf16x8 raw, const bf16x8 cs, float (&o)[8]) {
+    const u32x4 x = __builtin_bit_cast(u32x4, raw), c = __builtin_bit_cast(u32x4, cs);
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const unsigned xs = __builtin_amdgcn_alignbit(x[m], x[m], 16);   // (v, u)
+        float a, b;
+        asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(a) : "v"(c[m]), "v"(x[m]));
+        asm("v_dot2_f32_bf16 %0, %1, %2, 0 neg_hi:[1,0,0]" : "=v"(b) : "v"(c[m]), "v"(xs));
+        o[2 * m] = a;
+        o[2 * m + 1] = b;
+    }
+}
 // A load / store at a wave-uniform base plus a 32-bit per-lane byte offset: the loads take the
 // scalar-base addressing form, and a lane holds one 32-bit offset instead of a 64-bit address.
 template <class T>
