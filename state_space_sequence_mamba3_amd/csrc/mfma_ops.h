@@ -79,29 +79,74 @@ __device__ __forceinline__ void rot_piece_f(const float (&in)[8], const f16x8 cs
         o[2 * m + 1] = c * v - sn * u;
     }
 }
-__device__ __forceinline__ void rot_piece(const bf16x8 raw, const f16x8 cs, float (&o)[8]) {
-    float in[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) in[e] = (float)raw[e];
-    rot_piece_f(in, cs, o);
-}
-// The same rotation with (cos, sin) packed as bf16 pairs, on the bf16 dot-product unit: each
-// output is one v_dot2_f32_bf16 (two bf16 products summed in fp32) of the raw pair, so neither
-// the row nor the table is widened first. The first output takes (c, s).(u, v); the second takes
-// the pair swapped (a 16-bit funnel shift) against (c, -s) (the instruction's neg_hi modifier on
-// the table operand).
+// The same rotation with (cos, sin) packed as bf16 pairs, on the bf16 dot-product instruction,
+// rounded to bf16: each output is one v_dot2_f32_bf16 (two bf16 products summed in fp32) of the
+// raw pair, so neither the row nor the table is widened. The first output of a pair takes
+// (c, s).(u, v); the second takes the pair swapped (a 16-bit funnel shift) against (c, -s) (the
+// instruction's neg_hi modifier on the table operand, which the builtin cannot express). One asm
+// block per 8-element piece, ordered for the hazards the compiler cannot see inside it: the
+// swaps come first, so every dot product reads registers written at least four instructions
+// earlier, and every dot product's result is read at least three instructions after it is
+// written (its required wait states) by the block's own multiplies or conversions, so the block
+// leaves only VALU-written registers behind. With scale: each result times s before rounding.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void rot_piece_bf(const bf16x8 raw, const bf16x8 cs, float (&o)[8]) {
+__device__ __forceinline__ bf16x8 rot_pack_bf(const bf16x8 raw, const bf16x8 cs) {
     const u32x4 x = __builtin_bit_cast(u32x4, raw), c = __builtin_bit_cast(u32x4, cs);
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-        const unsigned xs = __builtin_amdgcn_alignbit(x[m], x[m], 16);   // (v, u)
-        float a, b;
-        asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(a) : "v"(c[m]), "v"(x[m]));
-        asm("v_dot2_f32_bf16 %0, %1, %2, 0 neg_hi:[1,0,0]" : "=v"(b) : "v"(c[m]), "v"(xs));
-        o[2 * m] = a;
-        o[2 * m + 1] = b;
-    }
+    u32x4 r;
+    float t0, t1, t2, t3, t4, t5, t6, t7;
+    asm("v_alignbit_b32 %5, %16, %16, 16\n\t"
+        "v_alignbit_b32 %7, %17, %17, 16\n\t"
+        "v_alignbit_b32 %9, %18, %18, 16\n\t"
+        "v_alignbit_b32 %11, %19, %19, 16\n\t"
+        "v_dot2_f32_bf16 %4, %12, %16, 0\n\t"
+        "v_dot2_f32_bf16 %6, %13, %17, 0\n\t"
+        "v_dot2_f32_bf16 %8, %14, %18, 0\n\t"
+        "v_dot2_f32_bf16 %10, %15, %19, 0\n\t"
+        "v_dot2_f32_bf16 %5, %12, %5, 0 neg_hi:[1,0,0]\n\t"
+        "v_dot2_f32_bf16 %7, %13, %7, 0 neg_hi:[1,0,0]\n\t"
+        "v_dot2_f32_bf16 %9, %14, %9, 0 neg_hi:[1,0,0]\n\t"
+        "v_dot2_f32_bf16 %11, %15, %11, 0 neg_hi:[1,0,0]\n\t"
+        "v_cvt_pk_bf16_f32 %0, %4, %5\n\t"
+        "v_cvt_pk_bf16_f32 %1, %6, %7\n\t"
+        "v_cvt_pk_bf16_f32 %2, %8, %9\n\t"
+        "v_cvt_pk_bf16_f32 %3, %10, %11"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]),
+          "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+        : "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+    return __builtin_bit_cast(bf16x8, r);
+}
+__device__ __forceinline__ bf16x8 rot_scale_pack_bf(const bf16x8 raw, const bf16x8 cs, float sc) {
+    const u32x4 x = __builtin_bit_cast(u32x4, raw), c = __builtin_bit_cast(u32x4, cs);
+    u32x4 r;
+    float t0, t1, t2, t3, t4, t5, t6, t7;
+    asm("v_alignbit_b32 %5, %16, %16, 16\n\t"
+        "v_alignbit_b32 %7, %17, %17, 16\n\t"
+        "v_alignbit_b32 %9, %18, %18, 16\n\t"
+        "v_alignbit_b32 %11, %19, %19, 16\n\t"
+        "v_dot2_f32_bf16 %4, %12, %16, 0\n\t"
+        "v_dot2_f32_bf16 %6, %13, %17, 0\n\t"
+        "v_dot2_f32_bf16 %8, %14, %18, 0\n\t"
+        "v_dot2_f32_bf16 %10, %15, %19, 0\n\t"
+        "v_dot2_f32_bf16 %5, %12, %5, 0 neg_hi:[1,0,0]\n\t"
+        "v_dot2_f32_bf16 %7, %13, %7, 0 neg_hi:[1,0,0]\n\t"
+        "v_dot2_f32_bf16 %9, %14, %9, 0 neg_hi:[1,0,0]\n\t"
+        "v_dot2_f32_bf16 %11, %15, %11, 0 neg_hi:[1,0,0]\n\t"
+        "v_mul_f32 %4, %20, %4\n\t"
+        "v_mul_f32 %6, %20, %6\n\t"
+        "v_mul_f32 %8, %20, %8\n\t"
+        "v_mul_f32 %10, %20, %10\n\t"
+        "v_mul_f32 %5, %20, %5\n\t"
+        "v_mul_f32 %7, %20, %7\n\t"
+        "v_mul_f32 %9, %20, %9\n\t"
+        "v_mul_f32 %11, %20, %11\n\t"
+        "v_cvt_pk_bf16_f32 %0, %4, %5\n\t"
+        "v_cvt_pk_bf16_f32 %1, %6, %7\n\t"
+        "v_cvt_pk_bf16_f32 %2, %8, %9\n\t"
+        "v_cvt_pk_bf16_f32 %3, %10, %11"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]),
+          "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+        : "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(sc));
+    return __builtin_bit_cast(bf16x8, r);
 }
 // A load / store at a wave-uniform base plus a 32-bit per-lane byte offset: the loads take the
 // scalar-base addressing form, and a lane holds one 32-bit offset instead of a 64-bit address.

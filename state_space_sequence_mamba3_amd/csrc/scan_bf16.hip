@@ -17,8 +17,11 @@
 // layouts every such row of B, C, x and y is contiguous in memory. A chunk is
 // a (Q*R) x (Q*R) problem: outputs are cut into 16-row t-blocks, the sweep over
 // inputs into 32-row s-blocks.
-//   * Once per chunk the cumulative angles become an fp16 (cos, sin) table in
-//     LDS; every rotation of B, C reads it (one sincos per angle and chunk).
+//   * Once per chunk the cumulative angles become a (cos, sin) table in LDS;
+//     every rotation of B, C reads it (one sincos per angle and chunk). Raw
+//     rows are rotated on the bf16 dot-product instruction from bf16 pairs
+//     (one v_dot2_f32_bf16 per element, fp32 sums); with the fused prologue
+//     the rows are fp32 when rotated, and the table holds fp16 pairs.
 //   * Every wave owns t-blocks (balanced pairs along the causal triangle); it
 //     loads their C rows straight from memory in MFMA operand layout, rotates
 //     them in registers and keeps them, with the output accumulators, in
@@ -136,7 +139,7 @@ struct Cfg {
     // with EPI the output staging shares the angle table's bytes (the table is dead from the end of
     // the sweep to the next chunk's prologue); otherwise it has a region of its own
     static constexpr int REG0 = EPI ? ((Q * K * 4 > NW * YST) ? Q * K * 4 : NW * YST) : Q * K * 4;
-    static constexpr int OFF_PHI = 0;                                  // f16x2 [Q][K] (cos, sin) of Phi
+    static constexpr int OFF_PHI = 0;                                  // bf16x2 / f16x2 [Q][K] (cos, sin) of Phi
     static constexpr int OFF_PHC = REG0;                               // float2 [K] (cos, sin) of the chunk's total angle
     static constexpr int OFF_S2 = OFF_PHC + K * 8;                     // float [Q] log2 decay prefix
     static constexpr int OFF_A2 = OFF_S2 + Q * 4;                      // float [Q] per-token log2 decay
@@ -169,8 +172,14 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int TPA = TPW > 0 ? TPW : 1;   // extent of per-t-block arrays (a state-only scan may have none)
     using UAcc = std::conditional_t<UT == 32, f32x16, f32x4>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    f16x2 *cstw = (f16x2 *)(smem + CF::OFF_PHI);
-    const f16x2 *cst = cstw;                                   // (cos, sin) table of the chunk's angles
+    // (cos, sin) table of the chunk's angles: bf16 pairs for the dot-product rotation of raw rows,
+    // fp16 pairs with the fused prologue (whose rows are fp32 when rotated)
+    using TabEl = std::conditional_t<CF::EPI, _Float16, bf16>;
+    using Tab2 = std::conditional_t<CF::EPI, f16x2, bf16x2>;
+    using Tab4 = std::conditional_t<CF::EPI, f16x4, bf16x4>;
+    using Tab8 = std::conditional_t<CF::EPI, f16x8, bf16x8>;
+    Tab2 *cstw = (Tab2 *)(smem + CF::OFF_PHI);
+    const Tab2 *cst = cstw;
     float2 *PHC = (float2 *)(smem + CF::OFF_PHC);
     float *S2 = (float *)(smem + CF::OFF_S2);
     float *A2 = (float *)(smem + CF::OFF_A2);
@@ -560,7 +569,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 float s0, c0v, s1, c1v;
                 __sincosf(x0, &s0, &c0v);
                 __sincosf(x1, &s1, &c1v);
-                *(f16x4 *)(cstw + tau * K + k) = f16x4{(_Float16)c0v, (_Float16)s0, (_Float16)c1v, (_Float16)s1};
+                *(Tab4 *)(cstw + tau * K + k) = Tab4{(TabEl)c0v, (TabEl)s0, (TabEl)c1v, (TabEl)s1};
                 if (tau == Q - 1) {   // angles past the end are zero: Phi[Q-1] = Phi[nq-1]
                     if constexpr (!CF::YO) {
                         sum_ph0 += x0;
@@ -600,16 +609,17 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             }
 #pragma unroll
             for (int kk = 0; kk < NKK; kk++) {
-                const f16x8 cs = *(const f16x8 *)(cst + tau * K + 16 * kk + 4 * q4);
-                float o[8];
+                const Tab8 cs = *(const Tab8 *)(cst + tau * K + 16 * kk + 4 * q4);
+                bf16x8 o;
                 if constexpr (CF::EPI) {
-                    float in[8];
+                    float in[8], of[8];
                     prologue_piece(h_c[u][kk], cinv, BIA + N + 32 * kk + 8 * q4, in);
-                    rot_piece_f(in, cs, o);
+                    rot_piece_f(in, cs, of);
+                    o = pack8(of);
                 } else {
-                    rot_piece(h_c[u][kk], cs, o);
+                    o = rot_pack_bf(h_c[u][kk], cs);
                 }
-                creg[u][kk] = (FULL || tau < nq) ? pack8(o) : bf16x8{};
+                creg[u][kk] = (FULL || tau < nq) ? o : bf16x8{};
             }
         }
 
@@ -665,12 +675,12 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             bf16 *wx = (bf16 *)(stg + CF::SB_WX);   // [32 rows][PS]  wU * X
             // every LDS read of the block first, then the arithmetic and the stores: a read
             // issued after a store would also wait for that store
-            f16x8 csb[CF::NLB];
+            Tab8 csb[CF::NLB];
             float wxv[CF::NLX];
 #pragma unroll
             for (int i = 0; i < CF::NLB; i++) {
                 const int c = min(tq + i * NTHR, CF::BCH - 1);
-                csb[i] = *(const f16x8 *)(cst + (sb * TOKS + (c / (N / 8)) / R) * K + (c % (N / 8)) * 4);
+                csb[i] = *(const Tab8 *)(cst + (sb * TOKS + (c / (N / 8)) / R) * K + (c % (N / 8)) * 4);
             }
 #pragma unroll
             for (int i = 0; i < CF::NLX; i++) {
@@ -700,15 +710,16 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 if (c < CF::BCH) {
                     const int row = c / (N / 8), col = (c % (N / 8)) * 8;
                     const int tau = sb * TOKS + row / R;
-                    float o[8];
+                    bf16x8 o;
                     if constexpr (CF::EPI) {
-                        float in[8];
+                        float in[8], of[8];
                         prologue_piece(rawB[i], binv[i], bslice, in);
-                        rot_piece_f(in, csb[i], o);
+                        rot_piece_f(in, csb[i], of);
+                        o = pack8(of);
                     } else {
-                        rot_piece(rawB[i], csb[i], o);
+                        o = rot_pack_bf(rawB[i], csb[i]);
                     }
-                    *(bf16x8 *)(bt + row * NS + col) = (FULL || tau < nq) ? pack8(o) : bf16x8{};
+                    *(bf16x8 *)(bt + row * NS + col) = (FULL || tau < nq) ? o : bf16x8{};
                 }
             }
 #pragma unroll

@@ -444,11 +444,8 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int i = 0; i < NLB; i++) {
                 const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
-                float o[8];
-                rot_piece_bf(RB[i], cs[i], o);
-#pragma unroll
-                for (int e = 0; e < 8; e++) o[e] *= eb[i];
-                *(bf16x8 *)(BS + row * NS + col) = (pan * PT + row / R < nq) ? pack8(o) : bf16x8{};
+                const bf16x8 o = rot_scale_pack_bf(RB[i], cs[i], eb[i]);
+                *(bf16x8 *)(BS + row * NS + col) = (pan * PT + row / R < nq) ? o : bf16x8{};
             }
 #pragma unroll
             for (int i = 0; i < NLX; i++) {
@@ -473,11 +470,8 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                 for (int kk = 0; kk < NKK; kk++) {
                     const bf16x8 cs = *(const bf16x8 *)(TAB + tau * KS + 16 * kk + 4 * q4);
-                    float o[8];
-                    rot_piece_bf(HC[u][kk], cs, o);
-#pragma unroll
-                    for (int e = 0; e < 8; e++) o[e] *= ec;
-                    creg[u][kk] = ok ? pack8(o) : bf16x8{};
+                    const bf16x8 o = rot_scale_pack_bf(HC[u][kk], cs, ec);
+                    creg[u][kk] = ok ? o : bf16x8{};
                 }
             }
         };
