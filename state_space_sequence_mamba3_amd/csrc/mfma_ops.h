@@ -65,6 +65,18 @@ __device__ __forceinline__ float wave_max_nonneg(float v) {
     return wave_bcast(v, 63);
 }
 
+// (sin x, cos x) for the fp32 state rotation by a chunk's total angle: x reduced by 2 pi in three
+// fused steps (Cody-Waite: 2 pi = C1 + C2 + C3, C1 with 8 significant bits, so k C1 is exact for
+// |k| < 2^16), then the hardware sine and cosine of the remainder in [-pi, pi]. Absolute error
+// about 4e-7 for |x| up to 1e4, without the branches and the wide-argument path of sincosf (a
+// divergent branch that every wave holding one chunk-end lane would execute in full).
+__device__ __forceinline__ void sincos_state(float x, float *s, float *c) {
+    const float k = rintf(x * 0.15915494309189535f);
+    float r = fmaf(-k, 6.28125f, x);
+    r = fmaf(-k, 1.9353071693331003e-3f, r);
+    r = fmaf(-k, 1.0253131677018246e-11f, r);
+    __sincosf(r, s, c);
+}
 // 2^x for x <= 0 (hardware exp2; results below the fp32 normal range flush to 0)
 __device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -575,8 +575,8 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                         sum_ph0 += x0;
                         sum_ph1 += x1;
                     }
-                    sincosf(x0, &s0, &c0v);
-                    sincosf(x1, &s1, &c1v);
+                    sincos_state(x0, &s0, &c0v);
+                    sincos_state(x1, &s1, &c1v);
                     *(f32x4 *)(PHC + k) = f32x4{c0v, s0, c1v, s1};
                 }
             }

@@ -408,8 +408,8 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 __sincosf(x1, &sn1, &cs1);
                 *(bf16x4 *)(TAB + tau * KS + k) = bf16x4{(bf16)cs0, (bf16)sn0, (bf16)cs1, (bf16)sn1};
                 if (last && tau == PT - 1) {   // the chunk's last panel; angles past the end are zero
-                    sincosf(x0, &sn0, &cs0);
-                    sincosf(x1, &sn1, &cs1);
+                    sincos_state(x0, &sn0, &cs0);
+                    sincos_state(x1, &sn1, &cs1);
                     *(f32x4 *)(PHC + k) = f32x4{cs0, sn0, cs1, sn1};
                 }
             }
