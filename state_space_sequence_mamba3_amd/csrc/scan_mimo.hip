@@ -430,7 +430,9 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 for (int r = 0; r < URG; r++) hreg[v][r] *= eS;
         }
 
-        // ---- staging of panel pan from the prefetched raw rows: B~' = R(-Phi) B * EB, X as is
+        // ---- staging of panel pan from the prefetched raw rows: B~' = R(-Phi) B * EB, X as is.
+        // Rows past the end hold the last token's (finite) values: a zero scale clears their B~'
+        // rows, which zeroes every score and state term that would read their X rows.
         auto stage_panel = [&](int pan) __attribute__((always_inline)) {
             const int tq = opaque<true>(tid);
             bf16x8 cs[NLB];
@@ -439,18 +441,18 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             for (int i = 0; i < NLB; i++) {
                 const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
                 cs[i] = *(const bf16x8 *)(TAB + (row / R) * KS + col / 2);
-                eb[i] = EB[pan * PT + row / R];
+                const float e = EB[pan * PT + row / R];
+                eb[i] = (pan * PT + row / R < nq) ? e : 0.f;
             }
 #pragma unroll
             for (int i = 0; i < NLB; i++) {
                 const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
-                const bf16x8 o = rot_scale_pack_bf(RB[i], cs[i], eb[i]);
-                *(bf16x8 *)(BS + row * NS + col) = (pan * PT + row / R < nq) ? o : bf16x8{};
+                *(bf16x8 *)(BS + row * NS + col) = rot_scale_pack_bf(RB[i], cs[i], eb[i]);
             }
 #pragma unroll
             for (int i = 0; i < NLX; i++) {
                 const int c = tq + i * NTHR, row = c / (P / 8), col = (c % (P / 8)) * 8;
-                *(bf16x8 *)(XS + row * PS + col) = (pan * PT + row / R < nq) ? RX[i] : bf16x8{};
+                *(bf16x8 *)(XS + row * PS + col) = RX[i];
             }
         };
         // ---- C~' rows of the round's t-blocks from the prefetched raw rows: R(-Phi) C * EC
@@ -465,13 +467,12 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             for (int u = 0; u < TPW; u++) {
                 tbr[u] = tb_of(u, c0);
                 const int tau = (tbr[u] * 16 + l16) / R;
-                const float ec = EC[pan * PT + tau];
-                const bool ok = pan * PT + tau < nq;
+                const float e = EC[pan * PT + tau];
+                const float ec = (pan * PT + tau < nq) ? e : 0.f;   // (rows past the end: zero)
 #pragma unroll
                 for (int kk = 0; kk < NKK; kk++) {
                     const bf16x8 cs = *(const bf16x8 *)(TAB + tau * KS + 16 * kk + 4 * q4);
-                    const bf16x8 o = rot_scale_pack_bf(HC[u][kk], cs, ec);
-                    creg[u][kk] = ok ? o : bf16x8{};
+                    creg[u][kk] = rot_scale_pack_bf(HC[u][kk], cs, ec);
                 }
             }
         };
