@@ -156,6 +156,25 @@ def test_strong_decay(oracle, cfg):
     assert ey < TOL_BF16 and eh < TOL_BF16
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_large_angles(oracle, cfg):
+    """Angles 64 times the generator's (exact in bf16): a chunk's cumulative angles reach
+    hundreds to thousands of radians, so the state rotation by the chunk's total angle depends on
+    the kernels' 2 pi reduction before the hardware sine and cosine, and the per-token tables are
+    built far from the origin."""
+    inp = synth.scan_inputs(cfg, seed=43, batch=2, seqlen=300, nheads=4, packed=False)
+    th = inp["theta"]
+    f = (th.astype(np.uint32) << 16).view(np.float32) if th.dtype == np.uint16 else th
+    inp["theta"] = synth.bf16_bits(f * 64.0) if th.dtype == np.uint16 else f * 64.0
+    inp = synth.resume_inputs(inp, seed=44)
+    note(f"bf16 large angles cfg{cfg}")
+    y, h = run(upload(inp, device()), inp["meta"]["chunk"])
+    yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
+    ey, eh = slab_relerr(from_dev(y), yo), state_relerr(from_dev(h), ho)
+    note(f"  y relerr {ey:.2e}  h relerr {eh:.2e}")
+    assert ey < TOL_BF16 and eh < TOL_BF16
+
+
 def test_grouped_bc_and_no_skip(oracle):
     inp = synth.scan_inputs(dict(synth.CONFIGS[2], ngroups=1), seed=3, batch=1, seqlen=130, nheads=4)
     inp["D"] = None
