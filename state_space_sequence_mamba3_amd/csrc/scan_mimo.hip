@@ -109,7 +109,7 @@ struct MCfg {
     // the prologue's per-token log2 decay and delta share S2 and EB: wave 0 reads each entry
     // before it writes the entry's new value
     static constexpr int OFF_A2 = OFF_S2, OFF_DL = OFF_EB;
-    static constexpr int OFF_MISC = OFF_DT + Q * 4;               // float [4]
+    static constexpr int OFF_MISC = OFF_DT + Q * 4;               // float [4] (3: A log2 e of the head)
     static constexpr int LDS = OFF_MISC + 16;
     static_assert(LDS <= 160 * 1024, "LDS");
 };
@@ -301,6 +301,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         load_panel(0, 0, tid);
         load_crows(0, 0, tid);
     }
+    if (tid == 0) MISC[3] = A2h;
     __syncthreads();
 
     for (int64_t c0 = 0; c0 < len; c0 += Q) {
@@ -320,7 +321,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             const bool ok = tq < nq;
             const float dt = ok ? to_f(h_dt) : 0.f, lm = ok ? to_f(h_lam) : 0.f;
             DT[tq] = dt;
-            A2[tq] = dt * A2h;
+            // (A log2 e re-read from LDS in every chunk: a register copy held across the loop was
+            // spilled, and its reload here waited for every store and load in flight, since
+            // memory operations complete in order)
+            A2[tq] = dt * *(volatile __attribute__((address_space(3))) const float *)(MISC + 3);
             GM[tq] = lm * dt;
             DL[tq] = (1.f - lm) * dt;
         }
