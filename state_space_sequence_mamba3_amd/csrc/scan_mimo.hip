@@ -98,19 +98,21 @@ struct MCfg {
     static constexpr int OFF_XS = OFF_BS + PR * NS * 2;           // bf16 [PR][PS]  X rows of the panel
     static constexpr int OFF_HB = OFF_XS + PR * PS * 2;           // bf16 [P][NS]   carried state H'
     static constexpr int OFF_TAB = OFF_HB + P * NS * 2;           // bf16x2 [PT][KS] (cos, sin) of the panel's Phi
-    static constexpr int OFF_PHC = OFF_TAB + PT * KS * 4;         // float2 [K]     chunk total angle
-    static constexpr int OFF_S2 = OFF_PHC + K * 8;                // float [Q] log2-decay prefix S2_t
-    static constexpr int OFF_G1 = OFF_S2 + Q * 4;                 // float [Q] gamma_s + delta_{s+1}
-    static constexpr int OFF_GM = OFF_G1 + Q * 4;                 // float [Q] gamma_s
-    static constexpr int OFF_RR = OFF_GM + Q * 4;                 // float [Q] gamma_s / (gamma_s + delta_{s+1})
-    static constexpr int OFF_EB = OFF_RR + Q * 4;                 // float [Q] staged B row scale
+    static constexpr int OFF_PHC = OFF_TAB + PT * KS * 4;         // float2 [2][K] chunk total angle
+    // per-chunk tables in two copies, by chunk parity: the next chunk's prologue fills its copy
+    // during this chunk's last round, which still reads this chunk's
+    static constexpr int OFF_S2 = OFF_PHC + 2 * K * 8;            // float [2][Q] log2-decay prefix S2_t
+    static constexpr int OFF_G1 = OFF_S2 + 2 * Q * 4;             // float [2][Q] gamma_s + delta_{s+1}
+    static constexpr int OFF_GM = OFF_G1 + 2 * Q * 4;             // float [2][Q] gamma_s
+    static constexpr int OFF_RR = OFF_GM + 2 * Q * 4;             // float [2][Q] gamma_s / (gamma_s + delta_{s+1})
+    static constexpr int OFF_EB = OFF_RR + 2 * Q * 4;             // float [Q] staged B row scale
     static constexpr int OFF_EC = OFF_EB + Q * 4;                 // float [Q] C row scale
     static constexpr int OFF_DT = OFF_EC + Q * 4;                 // float [Q] dt (0 past the end)
-    // the prologue's per-token log2 decay and delta share S2 and EB: wave 0 reads each entry
+    static constexpr int OFF_DL = OFF_DT + Q * 4;                 // float [Q] (1 - lambda) dt
+    // the prologue's per-token log2 decay shares S2 (the chunk's copy): wave 0 reads each entry
     // before it writes the entry's new value
-    static constexpr int OFF_A2 = OFF_S2, OFF_DL = OFF_EB;
-    static constexpr int OFF_MISC = OFF_DT + Q * 4;               // float [4] (3: A log2 e of the head)
-    static constexpr int LDS = OFF_MISC + 16;
+    static constexpr int OFF_MISC = OFF_DL + Q * 4;               // float [2][4] per chunk, then A log2 e of the head
+    static constexpr int LDS = OFF_MISC + 48;
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -126,17 +128,16 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     bf16 *XS = (bf16 *)(smem + CF::OFF_XS);
     bf16 *HB = (bf16 *)(smem + CF::OFF_HB);
     bf16x2 *TAB = (bf16x2 *)(smem + CF::OFF_TAB);
-    float2 *PHC = (float2 *)(smem + CF::OFF_PHC);
-    float *S2 = (float *)(smem + CF::OFF_S2);
-    float *G1 = (float *)(smem + CF::OFF_G1);
-    float *GM = (float *)(smem + CF::OFF_GM);
-    float *RR = (float *)(smem + CF::OFF_RR);
+    float2 *const PHC0 = (float2 *)(smem + CF::OFF_PHC);   // copy of chunk parity q at + q K (S2 .. RR: + q Q)
+    float *const S20 = (float *)(smem + CF::OFF_S2);
+    float *const G10 = (float *)(smem + CF::OFF_G1);
+    float *const GM0 = (float *)(smem + CF::OFF_GM);
+    float *const RR0 = (float *)(smem + CF::OFF_RR);
     float *EB = (float *)(smem + CF::OFF_EB);
     float *EC = (float *)(smem + CF::OFF_EC);
     float *DT = (float *)(smem + CF::OFF_DT);
     float *DL = (float *)(smem + CF::OFF_DL);
-    float *A2 = (float *)(smem + CF::OFF_A2);
-    float *MISC = (float *)(smem + CF::OFF_MISC);
+    float *const MISC0 = (float *)(smem + CF::OFF_MISC);   // [4 q + 0..3] of chunk parity q; [8]: A log2 e
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -301,8 +302,134 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         load_panel(0, 0, tid);
         load_crows(0, 0, tid);
     }
-    if (tid == 0) MISC[3] = A2h;
+    // ---- a chunk's prologue, in two parts separated by a barrier: (a) its per-token scalars
+    // from the prefetched header, (b) the decay prefix, weights and operand scales (wave 0) and
+    // the angle table of panel 0 (every wave). Tables of chunk parity par.
+    float car0 = 0.f, car1 = 0.f;   // the angle sums of panel 0, carried into panel 1's table
+    // cumulative angles of the wave's angle pairs over panel pan, continuing from the carry
+    // (r0, r1: the lane's running sums; the lanes of the panel's last token group hold the
+    // panel totals afterwards); phc: the chunk's total-angle table
+    auto angle_table = [&](int pan, bool last, float2 *phc) __attribute__((always_inline)) {
+        const int lane = opaque<true>(tid) & 63;
+        const int k = wave * CF::KW + 2 * (lane % KP), g0 = (lane / KP) * TPL;
+        float a0[TPL], a1[TPL];
+        float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < TPL; j++) {
+            const float dt = DT[pan * PT + g0 + j];
+            r0 += dt * (float)h_th[pan][j][0];
+            r1 += dt * (float)h_th[pan][j][1];
+            a0[j] = r0;
+            a1[j] = r1;
+        }
+        float e0 = r0, e1 = r1;
+#pragma unroll
+        for (int off = KP; off < 64; off <<= 1) {
+            const float o0 = __shfl_up(e0, off, 64), o1 = __shfl_up(e1, off, 64);
+            if (lane >= off) {
+                e0 += o0;
+                e1 += o1;
+            }
+        }
+        // e0, e1: inclusive over the token groups; the panel total sits in the last group
+        const float tot0 = __shfl(e0, (TG - 1) * KP + lane % KP, 64), tot1 = __shfl(e1, (TG - 1) * KP + lane % KP, 64);
+        e0 += car0 - r0;
+        e1 += car1 - r1;
+#pragma unroll
+        for (int j = 0; j < TPL; j++) {
+            const int tau = g0 + j;
+            const float x0 = a0[j] + e0, x1 = a1[j] + e1;
+            float sn0, cs0, sn1, cs1;
+            __sincosf(x0, &sn0, &cs0);
+            __sincosf(x1, &sn1, &cs1);
+            *(bf16x4 *)(TAB + tau * KS + k) = bf16x4{(bf16)cs0, (bf16)sn0, (bf16)cs1, (bf16)sn1};
+            if (last && tau == PT - 1) {   // the chunk's last panel; angles past the end are zero
+                sincos_state(x0, &sn0, &cs0);
+                sincos_state(x1, &sn1, &cs1);
+                *(f32x4 *)(phc + k) = f32x4{cs0, sn0, cs1, sn1};
+            }
+        }
+        car0 += tot0;
+        car1 += tot1;
+    };
+    auto prologue_scalars = [&](int64_t c0x, int nqx, int par) __attribute__((always_inline)) {
+        const int tq = opaque<true>(tid);
+        float *A2 = S20 + par * Q, *GM = GM0 + par * Q, *MISC = MISC0 + 4 * par;
+        if (tq < Q) {
+            const bool ok = tq < nqx;
+            const float dt = ok ? to_f(h_dt) : 0.f, lm = ok ? to_f(h_lam) : 0.f;
+            DT[tq] = dt;
+            // (A log2 e re-read from LDS in every chunk: a register copy held across the loop was
+            // spilled, and its reload here waited for every store and load in flight, since
+            // memory operations complete in order)
+            A2[tq] = dt * *(volatile __attribute__((address_space(3))) const float *)(MISC0 + 8);
+            GM[tq] = lm * dt;
+            DL[tq] = (1.f - lm) * dt;
+        }
+        if (tq == 0) MISC[0] = (c0x + nqx < len) ? (1.f - to_f(h_lamn)) * to_f(h_dtn) : 0.f;
+    };
+    auto prologue_tables = [&](int nqx, int par) __attribute__((always_inline)) {
+        const int lane = opaque<true>(tid) & 63;
+        float *A2 = S20 + par * Q, *S2 = S20 + par * Q, *G1 = G10 + par * Q, *GM = GM0 + par * Q, *RR = RR0 + par * Q;
+        float *MISC = MISC0 + 4 * par;
+        const int nq = nqx;
+    if (wave == 0) {
+        // S2_t = sum_{tau <= t} dt A / ln 2 over the chunk; weights and operand scales
+        constexpr int PER = Q / 64;
+        float loc[PER];
+        float run = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            run += A2[lane * PER + i];
+            loc[i] = run;
+        }
+        const float excl = wave_incl_scan(run, lane) - run;
+        float s2v[PER];
+#pragma unroll
+        for (int i = 0; i < PER; i++) s2v[i] = excl + loc[i];
+        const float s2e = wave_bcast(s2v[PER - 1], 63);   // S2 of the chunk's last token (dt = 0 past the end)
+        const float dn = MISC[0];
+        // the fast form needs bounded scale factors and a finite gamma / (gamma + delta) ratio
+        bool bad = false;
+        float mx = 0.f;
+        float g1v[PER];
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int t = lane * PER + i;
+            const float next = (t + 1 < nq) ? DL[t + 1] : ((t + 1 == nq) ? dn : 0.f);
+            g1v[i] = (t < nq) ? GM[t] + next : 0.f;
+            bad |= g1v[i] == 0.f && GM[t] != 0.f;
+            mx = fmaxf(mx, fabsf(s2v[i]));
+        }
+        mx = wave_max_nonneg(mx);
+        const bool fast = __ballot(bad) == 0 && mx <= 100.f;
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int t = lane * PER + i;
+            S2[t] = s2v[i];
+            G1[t] = g1v[i];
+            RR[t] = (g1v[i] != 0.f) ? GM[t] / g1v[i] : 0.f;
+            EB[t] = fast ? exp2_neg(-s2v[i]) * g1v[i] : 1.f;
+            EC[t] = fast ? exp2_neg(s2v[i]) : 1.f;
+        }
+        if (lane == 0) {
+            MISC[1] = s2e;
+            MISC[2] = fast ? 1.f : 0.f;
+        }
+    }
+        car0 = car1 = 0.f;
+        angle_table(0, (nqx + PT - 1) / PT == 1, PHC0 + par * K);
+    };
+    if (tid == 0) MISC0[8] = A2h;
     __syncthreads();
+    if constexpr (NPAN == 2) {   // the first chunk's prologue; every later one runs in the chunk before
+        if (len > 0) {
+            prologue_scalars(0, (int)min((int64_t)Q, len), 0);
+            __syncthreads();
+            prologue_tables((int)min((int64_t)Q, len), 0);
+            __syncthreads();
+        }
+    }
 
     for (int64_t c0 = 0; c0 < len; c0 += Q) {
         const int nq = (int)min((int64_t)Q, len - c0);
@@ -316,112 +443,17 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         auto urow = [&](int r) __attribute__((always_inline)) { return (UT == 32) ? 8 * (r / 4) + 4 * hi + (r % 4) : 4 * q4 + r; };
         const int ucol = (UT == 32) ? l32 : l16;
 
-        // ---- prologue: per-token scalars, then the decay prefix and the angle table of panel 0
-        if (tq < Q) {
-            const bool ok = tq < nq;
-            const float dt = ok ? to_f(h_dt) : 0.f, lm = ok ? to_f(h_lam) : 0.f;
-            DT[tq] = dt;
-            // (A log2 e re-read from LDS in every chunk: a register copy held across the loop was
-            // spilled, and its reload here waited for every store and load in flight, since
-            // memory operations complete in order)
-            A2[tq] = dt * *(volatile __attribute__((address_space(3))) const float *)(MISC + 3);
-            GM[tq] = lm * dt;
-            DL[tq] = (1.f - lm) * dt;
+        // this chunk's copies of the per-chunk tables (the next chunk's prologue fills the others)
+        const int par = (int)((c0 / Q) & 1);
+        float2 *PHC = PHC0 + par * K;
+        float *S2 = S20 + par * Q, *G1 = G10 + par * Q, *GM = GM0 + par * Q, *RR = RR0 + par * Q;
+        float *MISC = MISC0 + 4 * par;
+        if constexpr (NPAN == 1) {   // one panel per chunk: the prologue at the chunk's start
+            prologue_scalars(c0, nq, par);
+            __syncthreads();
+            prologue_tables(nq, par);
+            __syncthreads();
         }
-        if (tq == 0) MISC[0] = (c0 + nq < len) ? (1.f - to_f(h_lamn)) * to_f(h_dtn) : 0.f;
-        __syncthreads();
-        if (wave == 0) {
-            // S2_t = sum_{tau <= t} dt A / ln 2 over the chunk; weights and operand scales
-            constexpr int PER = Q / 64;
-            float loc[PER];
-            float run = 0.f;
-#pragma unroll
-            for (int i = 0; i < PER; i++) {
-                run += A2[lane * PER + i];
-                loc[i] = run;
-            }
-            const float excl = wave_incl_scan(run, lane) - run;
-            float s2v[PER];
-#pragma unroll
-            for (int i = 0; i < PER; i++) s2v[i] = excl + loc[i];
-            const float s2e = wave_bcast(s2v[PER - 1], 63);   // S2 of the chunk's last token (dt = 0 past the end)
-            const float dn = MISC[0];
-            // the fast form needs bounded scale factors and a finite gamma / (gamma + delta) ratio
-            bool bad = false;
-            float mx = 0.f;
-            float g1v[PER];
-#pragma unroll
-            for (int i = 0; i < PER; i++) {
-                const int t = lane * PER + i;
-                const float next = (t + 1 < nq) ? DL[t + 1] : ((t + 1 == nq) ? dn : 0.f);
-                g1v[i] = (t < nq) ? GM[t] + next : 0.f;
-                bad |= g1v[i] == 0.f && GM[t] != 0.f;
-                mx = fmaxf(mx, fabsf(s2v[i]));
-            }
-            mx = wave_max_nonneg(mx);
-            const bool fast = __ballot(bad) == 0 && mx <= 100.f;
-#pragma unroll
-            for (int i = 0; i < PER; i++) {
-                const int t = lane * PER + i;
-                S2[t] = s2v[i];
-                G1[t] = g1v[i];
-                RR[t] = (g1v[i] != 0.f) ? GM[t] / g1v[i] : 0.f;
-                EB[t] = fast ? exp2_neg(-s2v[i]) * g1v[i] : 1.f;
-                EC[t] = fast ? exp2_neg(s2v[i]) : 1.f;
-            }
-            if (lane == 0) {
-                MISC[1] = s2e;
-                MISC[2] = fast ? 1.f : 0.f;
-            }
-        }
-        // cumulative angles of the wave's angle pairs over panel pan, continuing from carry
-        // (r0, r1: the lane's running sums; the lanes of the panel's last token group hold the
-        // panel totals afterwards)
-        float car0 = 0.f, car1 = 0.f;
-        auto angle_table = [&](int pan, bool last) __attribute__((always_inline)) {
-            const int k = wave * CF::KW + 2 * (lane % KP), g0 = (lane / KP) * TPL;
-            float a0[TPL], a1[TPL];
-            float r0 = 0.f, r1 = 0.f;
-#pragma unroll
-            for (int j = 0; j < TPL; j++) {
-                const float dt = DT[pan * PT + g0 + j];
-                r0 += dt * (float)h_th[pan][j][0];
-                r1 += dt * (float)h_th[pan][j][1];
-                a0[j] = r0;
-                a1[j] = r1;
-            }
-            float e0 = r0, e1 = r1;
-#pragma unroll
-            for (int off = KP; off < 64; off <<= 1) {
-                const float o0 = __shfl_up(e0, off, 64), o1 = __shfl_up(e1, off, 64);
-                if (lane >= off) {
-                    e0 += o0;
-                    e1 += o1;
-                }
-            }
-            // e0, e1: inclusive over the token groups; the panel total sits in the last group
-            const float tot0 = __shfl(e0, (TG - 1) * KP + lane % KP, 64), tot1 = __shfl(e1, (TG - 1) * KP + lane % KP, 64);
-            e0 += car0 - r0;
-            e1 += car1 - r1;
-#pragma unroll
-            for (int j = 0; j < TPL; j++) {
-                const int tau = g0 + j;
-                const float x0 = a0[j] + e0, x1 = a1[j] + e1;
-                float sn0, cs0, sn1, cs1;
-                __sincosf(x0, &sn0, &cs0);
-                __sincosf(x1, &sn1, &cs1);
-                *(bf16x4 *)(TAB + tau * KS + k) = bf16x4{(bf16)cs0, (bf16)sn0, (bf16)cs1, (bf16)sn1};
-                if (last && tau == PT - 1) {   // the chunk's last panel; angles past the end are zero
-                    sincos_state(x0, &sn0, &cs0);
-                    sincos_state(x1, &sn1, &cs1);
-                    *(f32x4 *)(PHC + k) = f32x4{cs0, sn0, cs1, sn1};
-                }
-            }
-            car0 += tot0;
-            car1 += tot1;
-        };
-        angle_table(0, npan == 1);
-        __syncthreads();
         const bool fast = __builtin_amdgcn_readfirstlane(__float_as_int(MISC[2])) != 0;
         const float s2e = MISC[1];
 
@@ -696,7 +728,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         if (fast) state_update(0);
         store_y(0);
         if constexpr (NPAN == 2) {
-            if (npan == 2) angle_table(1, true);
+            if (npan == 2) angle_table(1, true, PHC);
         }
         __syncthreads();
         if (NPAN == 2 && npan == 2) {
@@ -717,6 +749,11 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             stage_panel(1);
             __builtin_amdgcn_sched_barrier(0);
             load_panel(c0 + Q, 0, tq);
+            // the next chunk's prologue, part (a): its per-token scalars (this chunk no longer
+            // reads dt, DL or the other copy of the tables)
+            const bool has_next = c0 + Q < len;
+            const int nq_next = (int)min((int64_t)Q, len - c0 - Q);
+            if (has_next) prologue_scalars(c0 + Q, nq_next, par ^ 1);
             __syncthreads();
             sweep(1, 1);
             __builtin_amdgcn_sched_barrier(0);
@@ -729,6 +766,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 __syncthreads();
                 state_update(1);
             }
+            // part (b): the decay prefix, the weights and scales, the angle table of panel 0 (the
+            // angle table and the scales are no longer read by this chunk; the loop's last barrier
+            // orders them before the next chunk)
+            if (has_next) prologue_tables(nq_next, par ^ 1);
         } else {
             // one panel (or the sequence's last chunk ending inside panel 0)
             if (!fast) {
