@@ -844,10 +844,14 @@ __device__ __forceinline__ float sum16(float v) {
     v += dppf<0x140>(v);   // row_mirror: the other 8 lanes of the row
     return v;
 }
+// (the lane ^ 16 and lane ^ 32 partners through gfx950's row-swap instructions, VALU rather than
+// the LDS crossbar: v_permlane16_swap pairs rows 0-1 and 2-3, v_permlane32_swap the two halves;
+// each returns the lower and the upper partner, so both lanes of a pair add the same two values)
 __device__ __forceinline__ float sum_groups(float v) {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 // sum over the 64 lanes of a wave (the same pairing order as a xor butterfly 1, 2, ..., 32)
 __device__ __forceinline__ float wave_sum(float v) { return sum_groups(sum16(v)); }
