@@ -194,7 +194,8 @@ mamba3_status mamba3_scan_fwd(const mamba3_scan_args *args, void *stream);
  *
  * workspace: device memory of at least mamba3_scan_bwd_workspace_size(args)
  * bytes, owned by the caller, 256-byte aligned. It holds the state entering
- * every chunk (the backward walks the chunks in reverse) and per-(sequence,
+ * every chunk (the backward walks the chunks in reverse; a bf16 copy on the
+ * matrix-core path of bf16 inputs, fp32 otherwise) and per-(sequence,
  * head) partial sums (per head also for dB, dC with G < H and for dtheta with
  * theta_groups < H), so that every sum is formed in a fixed order: the
  * results are bitwise reproducible. Its contents are scratch on return. The
