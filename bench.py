@@ -58,12 +58,23 @@ def scan_bytes(c, block=False):
     return tok + S * H * N * P * 4 + 2 * H * 4 + (2 * H * N * 4 if block else 0)
 
 
+def score_span(c):
+    """Tokens over which the score and output contractions run causally: the chunk, except in
+    the panel kernel (plain bf16 (N, P, R, Q) = (128, 64, 4, 128)), whose two 64-token panels
+    of a chunk reach each other through the state."""
+    N, P, R, Q = c["dstate"], c["headdim"], c["rank"], c["chunk"]
+    if c.get("dtype") == "bf16" and (N, P, R, Q) == (128, 64, 4, 128) and not c.get("block"):
+        return 64
+    return Q
+
+
 def scan_flops(c):
-    """Algorithmic FLOPs of the chunked method per token-head (causal half of
-    the score and output contractions, inter-chunk output and chunk-state
-    update): R^2 (N + P)(Q + 1) + 4 R N P."""
-    L, H, P, N, R, Q = c["seqlen"], c["nheads"], c["headdim"], c["dstate"], c["rank"], c["chunk"]
-    return c["batch"] * L * H * (R * R * (N + P) * (Q + 1) + 4 * R * N * P)
+    """Algorithmic FLOPs of the chunked form the kernel runs, per token-head (causal half of
+    the score and output contractions over the span Qs, inter-chunk output and chunk-state
+    update): R^2 (N + P)(Qs + 1) + 4 R N P."""
+    L, H, P, N, R = c["seqlen"], c["nheads"], c["headdim"], c["dstate"], c["rank"]
+    Qs = score_span(c)
+    return c["batch"] * L * H * (R * R * (N + P) * (Qs + 1) + 4 * R * N * P)
 
 
 # (N, P, R) -> chunk length of the MFMA backward (bf16 token inputs); mirrors the library's table
@@ -173,7 +184,7 @@ def bench_scan(cfg, steps, warmup, dev, block=False, **over):
 
     ms, wall = timed(step, steps, warmup, stream)
     tokens = c["batch"] * c["seqlen"]
-    nbytes, flops = scan_bytes(c, block), scan_flops(c)
+    nbytes, flops = scan_bytes(c, block), scan_flops(dict(c, block=block))
     name = c["name"] + (f" (B, C shared: G={c['ngroups']})" if "ngroups" in over else "")
     name += " + BC norm, BC biases, SiLU gate" if block else ""
     out = dict(workload=name, kernel=scan_kernel_name(dict(c, block=block)), ms=ms, tokens_per_s=tokens / (ms * 1e-3), bytes=nbytes,

@@ -14,10 +14,21 @@
 //   * Panels. The chunk's rows are taken 64 tokens (256 rows) at a time. Only
 //     one panel of rotated B rows and X rows sits in LDS, and each wave holds
 //     the C~ rows and output accumulators of two 16-row t-blocks of one panel
-//     (a round): round 0 is panel 0 against itself; round 1 is panel 1 against
-//     panel 0 (a full block), then, after panel 1 is staged, against itself.
-//     Between the rounds and stagings a chunk passes six barriers; inside a
-//     round each wave runs its score, mask and output MFMAs straight through.
+//     (a round): round 0 is panel 0 against itself, round 1 panel 1 against
+//     itself. Panel 0's terms reach panel 1's tokens through the state: after
+//     round 0's state update the registers hold
+//       H' + sum_{s in panel 0} 2^{-S2_s} (gamma_s + delta_{s+1}) B~_s X_s^T,
+//     still in the chunk-start frame and decay reference, and since every s of
+//     panel 0 precedes every t of panel 1 (weight gamma_s + delta_{s+1}),
+//     panel 1's inter-chunk term 2^{S2_t} C~_t^T of that sum's bf16 copy is its
+//     carried term plus all of panel 0's. This is the same sum regrouped (the
+//     product C~_t^T B~_s X_s^T taken as C~_t^T (B~_s X_s^T)), exact up to the
+//     bf16 rounding of the summed state, like the carried state's own copy; it
+//     replaces the 256 x 256 score block of panel 1 against panel 0 (37 % of a
+//     chunk's matrix work) by nothing beyond the state update round 0 already
+//     does. A chunk passes four barriers; inside a round each wave runs its
+//     score, mask and output MFMAs straight through. The slow form below keeps
+//     the score block (round 1, part A) and its six barriers.
 //   * Decay folded into the operands. With the chunk-start reference,
 //     e^{S_t-S_s} = 2^{S2_t} 2^{-S2_s} (S2 = S / ln 2), so C~ rows are staged as
 //     2^{S2_t} C~_t and B~ rows as 2^{-S2_s} (gamma_s + delta_{s+1}) B~_s. A score
@@ -683,6 +694,18 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 *(bf16x8 *)(BS + row * NS + col) = pack8(o);
             }
         };
+        // bf16 copy of the registers' state for the inter-chunk products (each wave its tiles)
+        auto write_hb = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int v = 0; v < UPW; v++) {
+                const int p = ut_p0[v] + ucol;
+#pragma unroll
+                for (int r = 0; r < URG; r += 2) {
+                    const int n = ut_n0[v] + urow(r);
+                    *(bf16x2 *)(HB + p * NS + n) = bf16x2{(bf16)hreg[v][r], (bf16)hreg[v][r + 1]};
+                }
+            }
+        };
         // outputs of the round straight from the accumulators: four adjacent columns of one row
         // per lane and store (a t-block's 16 rows are 4 tokens' rank rows, 2 KB in all)
         bf16 *yb = gY + tok0 * strX;   // the chunk's first output row (a uniform base)
@@ -728,24 +751,34 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         if (fast) state_update(0);
         store_y(0);
         if constexpr (NPAN == 2) {
-            if (npan == 2) angle_table(1, true, PHC);
+            if (npan == 2) {
+                angle_table(1, true, PHC);
+                // the lane's angles of this chunk are consumed: the next chunk's header may load
+                __builtin_amdgcn_sched_barrier(0);
+                load_header(c0 + Q, tq);
+            }
         }
         __syncthreads();
         if (NPAN == 2 && npan == 2) {
-            // ---- round 1, part A: panel 1's t-blocks against panel 0 (a full block)
             rotate_crows(1);
             __builtin_amdgcn_sched_barrier(0);
-            load_header(c0 + Q, tq);
-            inter(1);
-            sweep(1, 0);
-            if (!fast) {
+            if (fast) {
+                // panel 0's terms for panel 1's tokens through the state: after round 0 the
+                // registers hold H' + sum_{s in panel 0} B~'_s X_s^T in the chunk-start frame and
+                // decay reference, so panel 1's inter-chunk term (2^{S2_t} C~_t)^T of its bf16 copy
+                // is the carried term plus every panel-0 term; no panel-1 x panel-0 score block
+                write_hb();
+            } else {
+                // ---- round 1, part A (slow form): panel 1's t-blocks against panel 0 (a full block)
+                inter(1);
+                sweep(1, 0);
                 __syncthreads();
                 slow_rescale(0);
                 __syncthreads();
                 state_update(0);
+                __syncthreads();
             }
-            __syncthreads();
-            // ---- panel 1 staged; round 1, part B: panel 1 against itself
+            // ---- panel 1 staged; round 1 (part B): panel 1 against itself
             stage_panel(1);
             __builtin_amdgcn_sched_barrier(0);
             load_panel(c0 + Q, 0, tq);
@@ -755,6 +788,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             const int nq_next = (int)min((int64_t)Q, len - c0 - Q);
             if (has_next) prologue_scalars(c0 + Q, nq_next, par ^ 1);
             __syncthreads();
+            if (fast) inter(1);
             sweep(1, 1);
             __builtin_amdgcn_sched_barrier(0);
             load_crows(c0 + Q, 0, tq);
