@@ -58,13 +58,16 @@ def scan_bytes(c, block=False):
     return tok + S * H * N * P * 4 + 2 * H * 4 + (2 * H * N * 4 if block else 0)
 
 
+# plain bf16 shapes (N, P, R, Q) the panel kernel runs -> tokens per panel; mirrors the library
+PANEL_SHAPES = {(128, 64, 4, 128): 64, (64, 64, 4, 64): 32}
+
+
 def score_span(c):
     """Tokens over which the score and output contractions run causally: the chunk, except in
-    the panel kernel (plain bf16 (N, P, R, Q) = (128, 64, 4, 128)), whose two 64-token panels
-    of a chunk reach each other through the state."""
+    the panel kernel, whose two panels of a chunk reach each other through the state."""
     N, P, R, Q = c["dstate"], c["headdim"], c["rank"], c["chunk"]
-    if c.get("dtype") == "bf16" and (N, P, R, Q) == (128, 64, 4, 128) and not c.get("block"):
-        return 64
+    if c.get("dtype") == "bf16" and (N, P, R, Q) in PANEL_SHAPES and not c.get("block"):
+        return PANEL_SHAPES[(N, P, R, Q)]
     return Q
 
 
@@ -157,7 +160,7 @@ def scan_kernel_name(c):
     N, P, R, Q = c["dstate"], c["headdim"], c["rank"], c["chunk"]
     if c.get("dtype") != "bf16":
         return f"k_scan_f32<N={N},P={P},R={R},Q={Q}>"
-    if (N, P, R, Q) == (128, 64, 4, 128) and not c.get("block"):
+    if (N, P, R, Q) in PANEL_SHAPES and not c.get("block"):
         return f"k_scan_mimo<N={N},P={P},R={R},Q={Q}>"
     return f"k_scan_bf16<N={N},P={P},R={R},Q={Q}>"
 

@@ -72,12 +72,13 @@ struct MimoParams {
     int32_t seqlen, H, G, nseq, Gth;
 };
 
-template <int N_, int P_, int R_, int Q_>
+// NW_ waves per workgroup, PT_ tokens per panel (PT_ R = 32 NW_ rows: two 16-row t-blocks a wave)
+template <int N_, int P_, int R_, int Q_, int NW_, int PT_>
 struct MCfg {
     static constexpr int N = N_, P = P_, R = R_, Q = Q_;
-    static constexpr int NW = 8, NTHR = 512;
+    static constexpr int NW = NW_, NTHR = 64 * NW_;
     static constexpr int K = N / 2;                 // angles per token (state pairs)
-    static constexpr int PT = 64, PR = PT * R;      // tokens and rank-expanded rows per panel
+    static constexpr int PT = PT_, PR = PT * R;     // tokens and rank-expanded rows per panel
     static constexpr int NPAN = Q / PT;             // panels per chunk
     static constexpr int NTBP = PR / 16;            // 16-row t-blocks per panel
     static constexpr int TPW = NTBP / NW;           // t-blocks per wave and round
@@ -879,11 +880,12 @@ bool scan_mimo_supported(const mamba3_scan_args *a) {
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
     if (a->dtype != MAMBA3_BF16 || !a->y || !a->A || a->A_tok || !a->lam) return false;
     if (a->bc_norm || a->B_bias || a->C_bias || a->z) return false;
-    return N == 128 && P == 64 && R == 4 && Q == 128;
+    return P == 64 && R == 4 && ((N == 128 && Q == 128) || (N == 64 && Q == 64));
 }
 
 mamba3_status launch_scan_mimo(const mamba3_scan_args *a, hipStream_t st) {
-    if (a->dstate == 128 && a->chunk == 128) return launch_mimo_cfg<MCfg<128, 64, 4, 128>>(a, st);
+    if (a->dstate == 128 && a->chunk == 128) return launch_mimo_cfg<MCfg<128, 64, 4, 128, 8, 64>>(a, st);
+    if (a->dstate == 64 && a->chunk == 64) return launch_mimo_cfg<MCfg<64, 64, 4, 64, 4, 32>>(a, st);
     return MAMBA3_EUNSUPPORTED;
 }
 
