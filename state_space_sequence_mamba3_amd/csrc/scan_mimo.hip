@@ -72,8 +72,9 @@ struct MimoParams {
     int32_t seqlen, H, G, nseq, Gth;
 };
 
-// NW_ waves per workgroup, PT_ tokens per panel (PT_ R = 32 NW_ rows: two 16-row t-blocks a wave)
-template <int N_, int P_, int R_, int Q_, int NW_, int PT_>
+// NW_ waves per workgroup, PT_ tokens per panel (PT_ R = 32 NW_ rows: two 16-row t-blocks a wave);
+// PAD_: LDS rows padded against bank conflicts (below)
+template <int N_, int P_, int R_, int Q_, int NW_, int PT_, bool PAD_ = true>
 struct MCfg {
     static constexpr int N = N_, P = P_, R = R_, Q = Q_;
     static constexpr int NW = NW_, NTHR = 64 * NW_;
@@ -90,7 +91,7 @@ struct MCfg {
     // cycle for 16-byte reads, 32 for the transposing 8-byte reads) they make the 16-byte reads
     // of 16 consecutive rows (score operands, H', the angle table) and the transposing reads of 8
     // consecutive X rows free of bank conflicts, with constant offsets between a lane's reads
-    static constexpr int NS = N + 16, PS = P + 16, KS = K + 8;
+    static constexpr int NS = N + (PAD_ ? 16 : 0), PS = P + (PAD_ ? 16 : 0), KS = K + (PAD_ ? 8 : 0);
     // the N x P state: 32 x 32 tiles (32x32x16 MFMA) when every wave gets a whole one, else 16 x 16
     static constexpr int UT = ((N / 32) * (P / 32) % NW == 0) ? 32 : 16;
     static constexpr int NUT = (N / UT) * (P / UT), UPW = NUT / NW, URG = (UT == 32) ? 16 : 4;
@@ -98,7 +99,7 @@ struct MCfg {
     static constexpr int KW = K / NW, KP = KW / 2, TG = 64 / KP, TPL = PT / TG;
     // raw 16-byte pieces of a panel per thread
     static constexpr int NLB = PR * N / 8 / NTHR, NLX = PR * P / 8 / NTHR;
-    static_assert(R == 4 && P % 32 == 0 && N % 32 == 0 && Q % PT == 0 && NPAN >= 1 && NPAN <= 2, "shape");
+    static_assert(R == 4 && P % 32 == 0 && N % 32 == 0 && Q % PT == 0 && NPAN >= 1, "shape");
     static_assert(NTBP == 2 * NW && TPW == 2, "a balanced pair of t-blocks per wave and round");
     static_assert(NUT % NW == 0, "state tiles");
     static_assert(K % NW == 0 && KW % 2 == 0 && 64 % KP == 0 && PT % TG == 0, "angle split");
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     };
     if (tid == 0) MISC0[8] = A2h;
     __syncthreads();
-    if constexpr (NPAN == 2) {   // the first chunk's prologue; every later one runs in the chunk before
+    if constexpr (NPAN >= 2) {   // the first chunk's prologue; every later one runs in the chunk before
         if (len > 0) {
             prologue_scalars(0, (int)min((int64_t)Q, len), 0);
             __syncthreads();
@@ -469,14 +470,11 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         const bool fast = __builtin_amdgcn_readfirstlane(__float_as_int(MISC[2])) != 0;
         const float s2e = MISC[1];
 
-        // the slow form scales the carried state first; the fast one at the end of the chunk
-        if (!fast) {
-            const float eS = exp2_neg(s2e);
-#pragma unroll
-            for (int v = 0; v < UPW; v++)
-#pragma unroll
-                for (int r = 0; r < URG; r++) hreg[v][r] *= eS;
-        }
+        // The slow form keeps the state referenced to the start of the panel in hand (S2 of the
+        // previous panel's last token; 0 at the chunk start) and moves it to the next panel's
+        // reference at each panel's state update; the fast one keeps the chunk-start reference
+        // and applies e^{S_e} at the end of the chunk.
+        auto s2ref = [&](int pan) __attribute__((always_inline)) { return pan == 0 ? 0.f : S2[pan * PT - 1]; };
 
         // ---- staging of panel pan from the prefetched raw rows: B~' = R(-Phi) B * EB, X as is.
         // Rows past the end hold the last token's (finite) values: a zero scale clears their B~'
@@ -548,10 +546,11 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                     for (int u = 0; u < TPW; u++) yacc[u][pt] = mfma16(hop[kk], creg[u][kk], yacc[u][pt]);
             }
-            if (!fast) {   // unscaled C~ rows: the decay factor of the lane's output row
+            if (!fast) {   // unscaled C~ rows: the decay of the lane's output row from the panel reference
+                const float ref = s2ref(pan);
 #pragma unroll
                 for (int u = 0; u < TPW; u++) {
-                    const float sc = exp2_neg(S2[pan * PT + (tbr[u] * 16 + l16) / R]);
+                    const float sc = exp2_neg(S2[pan * PT + (tbr[u] * 16 + l16) / R] - ref);
 #pragma unroll
                     for (int pt = 0; pt < NPT; pt++)
 #pragma unroll
@@ -680,14 +679,22 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 }
             }
         };
-        // the slow form: staged B~ rows scaled by e^{S_e - S_s} (gamma_s + delta_{s+1}) in place
+        // the slow form: staged B~ rows scaled in place by e^{S_ref - S_s} (gamma_s + delta_{s+1}),
+        // S_ref that of the panel's last token (the chunk's S_e for the last panel: dt is 0 past the
+        // end), and the state moved to that reference
         auto slow_rescale = [&](int spn) __attribute__((always_inline)) {
             const int tq = opaque<true>(tid);
+            const float ref = S2[spn * PT + PT - 1];
+            const float eS = exp2_neg(ref - s2ref(spn));
+#pragma unroll
+            for (int v = 0; v < UPW; v++)
+#pragma unroll
+                for (int r = 0; r < URG; r++) hreg[v][r] *= eS;
 #pragma unroll
             for (int i = 0; i < NLB; i++) {
                 const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
                 const int t = spn * PT + row / R;
-                const float f = exp2_neg(s2e - S2[t]) * G1[t];
+                const float f = exp2_neg(ref - S2[t]) * G1[t];
                 const bf16x8 v = *(const bf16x8 *)(BS + row * NS + col);
                 float o[8];
 #pragma unroll
@@ -728,93 +735,72 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         };
 
-        // ---- panel 0: staged from the prefetched rows, with round 0's C~' rows
-        stage_panel(0);
-        rotate_crows(0);
-        // the prefetch registers are consumed: no load that refills them may be scheduled into
-        // the staging above (old and new contents would be live together)
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (NPAN == 2) {
-            load_panel(c0, 1, tq);
-        } else {
-            load_header(c0 + Q, tq);
-            load_panel(c0 + Q, 0, tq);
-        }
-        __syncthreads();
-        // ---- round 0: panel 0 against itself; the angle table of panel 1 meanwhile. The next
-        // round's raw C rows are loaded once the sweep is done (no prefetch beyond the panel rows
-        // is live during tile work)
-        inter(0);
-        sweep(0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (NPAN == 2) load_crows(c0, 1, tq);
-        else load_crows(c0 + Q, 0, tq);
-        if (fast) state_update(0);
-        store_y(0);
-        if constexpr (NPAN == 2) {
-            if (npan == 2) {
-                angle_table(1, true, PHC);
-                // the lane's angles of this chunk are consumed: the next chunk's header may load
+        // ---- the panels of the chunk, one round each. Panel p is staged from the prefetched rows
+        // with its round's C~' rows, after the state in the registers is copied to HB for its
+        // inter-chunk term: the carried state at p = 0, plus every earlier panel's terms after
+        // (see above).
+        // Round p: panel p against itself; meanwhile the next panel's angle table, the next
+        // panel's (or chunk's) raw rows, and in the last round the next chunk's prologue.
+        const bool has_next = c0 + Q < len;
+        const int nq_next = (int)min((int64_t)Q, len - c0 - Q);
+#pragma unroll
+        for (int pan = 0; pan < NPAN; pan++) {
+            if (pan > 0 && pan >= npan) break;   // (uniform) panels past the sequence's end
+            if (pan > 0) {
+                rotate_crows(pan);
                 __builtin_amdgcn_sched_barrier(0);
-                load_header(c0 + Q, tq);
             }
-        }
-        __syncthreads();
-        if (NPAN == 2 && npan == 2) {
-            rotate_crows(1);
+            write_hb();
+            stage_panel(pan);
+            if (pan == 0) rotate_crows(0);
+            // the prefetch registers are consumed: no load that refills them may be scheduled into
+            // the staging above (old and new contents would be live together)
             __builtin_amdgcn_sched_barrier(0);
-            if (fast) {
-                // panel 0's terms for panel 1's tokens through the state: after round 0 the
-                // registers hold H' + sum_{s in panel 0} B~'_s X_s^T in the chunk-start frame and
-                // decay reference, so panel 1's inter-chunk term (2^{S2_t} C~_t)^T of its bf16 copy
-                // is the carried term plus every panel-0 term; no panel-1 x panel-0 score block
-                write_hb();
+            if (pan + 1 < NPAN) {
+                load_panel(c0, pan + 1, tq);
             } else {
-                // ---- round 1, part A (slow form): panel 1's t-blocks against panel 0 (a full block)
-                inter(1);
-                sweep(1, 0);
-                __syncthreads();
-                slow_rescale(0);
-                __syncthreads();
-                state_update(0);
-                __syncthreads();
+                if (NPAN == 1) load_header(c0 + Q, tq);
+                load_panel(c0 + Q, 0, tq);
+                // the next chunk's prologue, part (a): its per-token scalars (this chunk no longer
+                // reads dt, DL or the other copy of the tables)
+                if (NPAN > 1 && has_next) prologue_scalars(c0 + Q, nq_next, par ^ 1);
             }
-            // ---- panel 1 staged; round 1 (part B): panel 1 against itself
-            stage_panel(1);
-            __builtin_amdgcn_sched_barrier(0);
-            load_panel(c0 + Q, 0, tq);
-            // the next chunk's prologue, part (a): its per-token scalars (this chunk no longer
-            // reads dt, DL or the other copy of the tables)
-            const bool has_next = c0 + Q < len;
-            const int nq_next = (int)min((int64_t)Q, len - c0 - Q);
-            if (has_next) prologue_scalars(c0 + Q, nq_next, par ^ 1);
             __syncthreads();
-            if (fast) inter(1);
-            sweep(1, 1);
+            inter(pan);
+            sweep(pan, pan);
+            // the next round's raw C rows are loaded once the sweep is done (no prefetch beyond
+            // the panel rows is live during tile work)
             __builtin_amdgcn_sched_barrier(0);
-            load_crows(c0 + Q, 0, tq);
-            if (fast) state_update(1);
-            store_y(1);
-            if (!fast) {
-                __syncthreads();
-                slow_rescale(1);
-                __syncthreads();
-                state_update(1);
+            if (pan + 1 < NPAN) load_crows(c0, pan + 1, tq);
+            else load_crows(c0 + Q, 0, tq);
+            if (fast) state_update(pan);
+            store_y(pan);
+            if (pan + 1 < npan) {
+                angle_table(pan + 1, pan + 2 == npan, PHC);
+                if (pan + 2 == NPAN) {
+                    // the lane's angles of this chunk are consumed: the next chunk's header may load
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_header(c0 + Q, tq);
+                }
             }
-            // part (b): the decay prefix, the weights and scales, the angle table of panel 0 (the
-            // angle table and the scales are no longer read by this chunk; the loop's last barrier
-            // orders them before the next chunk)
-            if (has_next) prologue_tables(nq_next, par ^ 1);
-        } else {
-            // one panel (or the sequence's last chunk ending inside panel 0)
             if (!fast) {
-                slow_rescale(0);
                 __syncthreads();
-                state_update(0);
+                slow_rescale(pan);
+                __syncthreads();
+                state_update(pan);
+            }
+            if (pan + 1 == NPAN) {
+                // part (b): the decay prefix, the weights and scales, the angle table of panel 0
+                // (the angle table and the scales are no longer read by this chunk; the loop's last
+                // barrier orders them before the next chunk)
+                if (NPAN > 1 && has_next) prologue_tables(nq_next, par ^ 1);
+            } else if (pan + 1 < npan) {
+                __syncthreads();
             }
         }
-        // ---- state epilogue: e^{S_e} (fast form), the rotation by the chunk's total angle, and
-        // the bf16 copy for the next chunk's inter-chunk term
+        // ---- state epilogue: e^{S_e} (fast form) and the rotation by the chunk's total angle. Its
+        // bf16 copy is written at the next chunk's start: other waves may still be reading HB in
+        // the last round's inter-chunk product, and the loop's last barrier orders them first.
         {
             const float eS = fast ? exp2_neg(s2e) : 1.f;
             f32x4 rot4[UPW][URG / 4];
@@ -824,15 +810,12 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 for (int q = 0; q < URG / 4; q++) rot4[v][q] = *(const f32x4 *)(PHC + (ut_n0[v] + urow(4 * q)) / 2);
 #pragma unroll
             for (int v = 0; v < UPW; v++) {
-                const int p = ut_p0[v] + ucol;
 #pragma unroll
                 for (int r = 0; r < URG; r += 2) {
-                    const int n = ut_n0[v] + urow(r);
                     const float cs = rot4[v][r / 4][r % 4], sn = rot4[v][r / 4][r % 4 + 1];
                     const float u0 = hreg[v][r] * eS, u1 = hreg[v][r + 1] * eS;
                     hreg[v][r] = cs * u0 - sn * u1;
                     hreg[v][r + 1] = sn * u0 + cs * u1;
-                    *(bf16x2 *)(HB + p * NS + n) = bf16x2{(bf16)hreg[v][r], (bf16)hreg[v][r + 1]};
                 }
             }
         }
