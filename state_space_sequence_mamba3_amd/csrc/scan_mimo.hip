@@ -74,9 +74,10 @@ struct MimoParams {
 
 // NW_ waves per workgroup, PT_ tokens per panel (PT_ R = 32 NW_ rows: two 16-row t-blocks a wave);
 // PAD_: LDS rows padded against bank conflicts (below)
-template <int N_, int P_, int R_, int Q_, int NW_, int PT_, bool PAD_ = true>
+template <int N_, int P_, int R_, int Q_, int NW_, int PT_, bool PAD_ = true, int WPE_ = 2>
 struct MCfg {
     static constexpr int N = N_, P = P_, R = R_, Q = Q_;
+    static constexpr int WPE = WPE_;                // waves per SIMD the registers are sized for
     static constexpr int NW = NW_, NTHR = 64 * NW_;
     static constexpr int K = N / 2;                 // angles per token (state pairs)
     static constexpr int PT = PT_, PR = PT * R;     // tokens and rank-expanded rows per panel
@@ -130,7 +131,7 @@ struct MCfg {
 };
 
 template <class CF>
-__global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) void k_scan_mimo(MimoParams pr) {
+__global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WPE))) void k_scan_mimo(MimoParams pr) {
     constexpr int N = CF::N, P = CF::P, R = CF::R, Q = CF::Q, NW = CF::NW, K = CF::K, PT = CF::PT;
     constexpr int PR = CF::PR, NPAN = CF::NPAN, TPW = CF::TPW, NKK = CF::NKK, NPT = CF::NPT;
     constexpr int NS = CF::NS, PS = CF::PS, KS = CF::KS, UT = CF::UT, UPW = CF::UPW, URG = CF::URG, NTHR = CF::NTHR;

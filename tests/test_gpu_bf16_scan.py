@@ -207,18 +207,23 @@ def test_panel_grouped_no_skip(oracle):
     assert slab_relerr(from_dev(y), yo) < TOL_BF16 and state_relerr(from_dev(h), ho) < TOL_BF16
 
 
-def test_panel_weight_guard(oracle):
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_panel_weight_guard(oracle, cfg):
     """A trapezoid weight lam > 1 can make gamma_s + delta_{s+1} vanish while gamma_s does not (dt
     and lam chosen exactly representable: gamma_10 = 0.5 * 0.125, delta_11 = (1 - 2) * 0.0625); the
-    chunk holding that token takes the unscaled per-element form."""
-    inp = synth.scan_inputs(4, seed=73, batch=1, seqlen=256, nheads=2, packed=False)
+    chunk holding that token takes the unscaled per-element form, whose panels reach each other
+    through the state referenced to each panel's start. Both panel-kernel shapes (MIMO layer:
+    chunk 64 in 32-token panels; packed: chunk 128 in 64-token panels)."""
+    inp = synth.scan_inputs(cfg, seed=73, batch=1, seqlen=256, nheads=2, packed=False)
     dt = np.full(inp["dt"].shape, 0.125, dtype=np.float32)
     lam = np.full(inp["lam"].shape, 0.5, dtype=np.float32)
     dt[:, 11], lam[:, 11] = 0.0625, 2.0
-    dt[:, 140], lam[:, 140] = 0.0625, 2.0          # the same in the second chunk (panel 0 of chunk 1)
+    dt[:, 45], lam[:, 45] = 0.0625, 2.0            # in panel 1 of the first chunk (either shape)
+    dt[:, 75], lam[:, 75] = 0.0625, 2.0
+    dt[:, 140], lam[:, 140] = 0.0625, 2.0          # the same in a later chunk
     inp["dt"], inp["lam"] = synth.bf16_bits(dt), synth.bf16_bits(lam)
-    note("bf16 panel scan, vanishing trapezoid weight")
-    y, h = run(upload(inp, device()), 128)
+    note(f"bf16 panel scan cfg{cfg}, vanishing trapezoid weight")
+    y, h = run(upload(inp, device()), inp["meta"]["chunk"])
     yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
     ey, eh = slab_relerr(from_dev(y), yo), state_relerr(from_dev(h), ho)
     note(f"  y relerr {ey:.2e}  h relerr {eh:.2e}")
