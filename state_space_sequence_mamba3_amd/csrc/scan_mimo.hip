@@ -63,6 +63,10 @@ namespace m3 {
 
 namespace {
 
+// 24-bit unsigned product (full-rate v_mul_u32_u24; a 32-bit v_mul_lo_u32 is quarter rate): a
+// token index within a chunk (< 2^7) times a token stride, which the host keeps below 2^24
+__device__ __forceinline__ uint32_t mul24(uint32_t a, uint32_t b) { return __umul24(a, b); }
+
 struct MimoParams {
     const bf16 *x, *dt, *lam, *theta, *B, *C, *Bprev, *xprev;
     const float *A, *D, *h_in;
@@ -265,10 +269,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         const bf16 *bdt = pr.dt + (start + c0c) * H + h, *blam = pr.lam + (start + c0c) * H + h;
         {
             const uint32_t tk = ltok(c0c, min(tq, Q - 1)), tn = ltok(c0c, nqh);
-            h_dt = ld_off<bf16>(bdt, tk * (uint32_t)H * 2u);
-            h_lam = ld_off<bf16>(blam, tk * (uint32_t)H * 2u);
-            h_dtn = ld_off<bf16>(bdt, tn * (uint32_t)H * 2u);
-            h_lamn = ld_off<bf16>(blam, tn * (uint32_t)H * 2u);
+            h_dt = ld_off<bf16>(bdt, mul24(tk, (uint32_t)H) * 2u);
+            h_lam = ld_off<bf16>(blam, mul24(tk, (uint32_t)H) * 2u);
+            h_dtn = ld_off<bf16>(bdt, mul24(tn, (uint32_t)H) * 2u);
+            h_lamn = ld_off<bf16>(blam, mul24(tn, (uint32_t)H) * 2u);
         }
         const int lq = tq & 63;
         const int k = wave * CF::KW + 2 * (lq % KP), g0 = (lq / KP) * TPL;
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         for (int p = 0; p < NPAN; p++)
 #pragma unroll
             for (int j = 0; j < TPL; j++)
-                h_th[p][j] = ld_off<bf16x2>(bth, (ltok(c0c, p * PT + g0 + j) * (uint32_t)strTh + (uint32_t)k) * 2u);
+                h_th[p][j] = ld_off<bf16x2>(bth, (mul24(ltok(c0c, p * PT + g0 + j), (uint32_t)strTh) + (uint32_t)k) * 2u);
     };
     auto load_panel = [&](int64_t c0h, int pan, int tq) __attribute__((always_inline)) {
         const int64_t c0c = chunk_start(c0h);
@@ -285,12 +289,12 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
 #pragma unroll
         for (int i = 0; i < NLB; i++) {
             const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
-            RB[i] = ld_off<bf16x8>(bB, (ltok(c0c, pan * PT + row / R) * (uint32_t)strBC + (uint32_t)((row % R) * N + col)) * 2u);
+            RB[i] = ld_off<bf16x8>(bB, (mul24(ltok(c0c, pan * PT + row / R), (uint32_t)strBC) + (uint32_t)((row % R) * N + col)) * 2u);
         }
 #pragma unroll
         for (int i = 0; i < NLX; i++) {
             const int c = tq + i * NTHR, row = c / (P / 8), col = (c % (P / 8)) * 8;
-            RX[i] = ld_off<bf16x8>(bX, (ltok(c0c, pan * PT + row / R) * (uint32_t)strX + (uint32_t)((row % R) * P + col)) * 2u);
+            RX[i] = ld_off<bf16x8>(bX, (mul24(ltok(c0c, pan * PT + row / R), (uint32_t)strX) + (uint32_t)((row % R) * P + col)) * 2u);
         }
     };
     // t-blocks of a round: a balanced pair along the causal triangle of the panel, rotated by the
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
             const int row = tb_of(u, c0h) * 16 + l16q;
-            const uint32_t o = ltok(c0c, pan * PT + row / R) * (uint32_t)strBC + (uint32_t)((row % R) * N + 8 * q4q);
+            const uint32_t o = mul24(ltok(c0c, pan * PT + row / R), (uint32_t)strBC) + (uint32_t)((row % R) * N + 8 * q4q);
 #pragma unroll
             for (int kk = 0; kk < NKK; kk++) HC[u][kk] = ld_off<bf16x8>(bC, (o + 32 * kk) * 2u);
         }
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         car1 += tot1;
     };
     auto prologue_scalars = [&](int64_t c0x, int nqx, int par) __attribute__((always_inline)) {
-        const int tq = opaque<true>(tid);
+        const int tq = opaque<true>(tid) & (NTHR - 1);
         float *A2 = S20 + par * Q, *GM = GM0 + par * Q, *MISC = MISC0 + 4 * par;
         if (tq < Q) {
             const bool ok = tq < nqx;
@@ -452,7 +456,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         // Every lane-derived index inside the loop comes from an opaque copy of the thread index
         // (these names shadow the ones above), so none of it is hoisted out of the loop and held
         // (or spilled) across chunks; it is recomputed where it is used.
-        const int tq = opaque<true>(tid);
+        const int tq = opaque<true>(tid) & (NTHR - 1);
         const int lane = tq & 63, l16 = tq & 15, q4 = lane >> 4, l32 = tq & 31, hi = lane >> 5;
         auto urow = [&](int r) __attribute__((always_inline)) { return (UT == 32) ? 8 * (r / 4) + 4 * hi + (r % 4) : 4 * q4 + r; };
         const int ucol = (UT == 32) ? l32 : l16;
@@ -481,7 +485,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         // Rows past the end hold the last token's (finite) values: a zero scale clears their B~'
         // rows, which zeroes every score and state term that would read their X rows.
         auto stage_panel = [&](int pan) __attribute__((always_inline)) {
-            const int tq = opaque<true>(tid);
+            const int tq = opaque<true>(tid) & (NTHR - 1);
             bf16x8 cs[NLB];
             float eb[NLB];
 #pragma unroll
@@ -508,7 +512,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         auto rotate_crows = [&](int pan) __attribute__((always_inline)) {
             // lane indices made opaque here: the phase's address math is recomputed in it rather
             // than precomputed for every phase of the chunk and held across them
-            const int tqp = opaque<true>(tid);
+            const int tqp = opaque<true>(tid) & (NTHR - 1);
             const int lane = tqp & 63, l16 = tqp & 15, q4 = lane >> 4;
 #pragma unroll
             for (int u = 0; u < TPW; u++) {
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         auto inter = [&](int pan) __attribute__((always_inline)) {
             // lane indices made opaque here: the phase's address math is recomputed in it rather
             // than precomputed for every phase of the chunk and held across them
-            const int tqp = opaque<true>(tid);
+            const int tqp = opaque<true>(tid) & (NTHR - 1);
             const int lane = tqp & 63, l16 = tqp & 15, q4 = lane >> 4;
 #pragma unroll
             for (int u = 0; u < TPW; u++)
@@ -564,7 +568,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         auto tile = [&](auto NAC, int u0, int j, int tpn, int spn) __attribute__((always_inline)) {
             // lane indices made opaque here: the phase's address math is recomputed in it rather
             // than precomputed for every phase of the chunk and held across them
-            const int tqp = opaque<true>(tid);
+            const int tqp = opaque<true>(tid) & (NTHR - 1);
             const int lane = tqp & 63, l16 = tqp & 15, q4 = lane >> 4;
             constexpr int NA = decltype(NAC)::value;
             // score operands in two halves of the K steps (fewer registers live at once)
@@ -658,7 +662,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         auto state_update = [&](int spn) __attribute__((always_inline)) {
             // lane indices made opaque here: the phase's address math is recomputed in it rather
             // than precomputed for every phase of the chunk and held across them
-            const int tqp = opaque<true>(tid);
+            const int tqp = opaque<true>(tid) & (NTHR - 1);
             const int lane = tqp & 63, l16 = tqp & 15, q4 = lane >> 4;
             const int nrow = min(PR, (nq - spn * PT) * R);
             for (int rb = 0; rb < nrow; rb += 32) {
@@ -684,7 +688,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         // S_ref that of the panel's last token (the chunk's S_e for the last panel: dt is 0 past the
         // end), and the state moved to that reference
         auto slow_rescale = [&](int spn) __attribute__((always_inline)) {
-            const int tq = opaque<true>(tid);
+            const int tq = opaque<true>(tid) & (NTHR - 1);
             const float ref = S2[spn * PT + PT - 1];
             const float eS = exp2_neg(ref - s2ref(spn));
 #pragma unroll
@@ -721,13 +725,13 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         auto store_y = [&](int tpn) __attribute__((always_inline)) {
             // lane indices made opaque here: the phase's address math is recomputed in it rather
             // than precomputed for every phase of the chunk and held across them
-            const int tqp = opaque<true>(tid);
+            const int tqp = opaque<true>(tid) & (NTHR - 1);
             const int lane = tqp & 63, l16 = tqp & 15, q4 = lane >> 4;
 #pragma unroll
             for (int u = 0; u < TPW; u++) {
                 const int rr = tbr[u] * 16 + l16, tau = tpn * PT + rr / R;
                 if (tau < nq) {
-                    const uint32_t o = (uint32_t)tau * (uint32_t)strX + (uint32_t)((rr % R) * P + 4 * q4);
+                    const uint32_t o = mul24((uint32_t)tau, (uint32_t)strX) + (uint32_t)((rr % R) * P + 4 * q4);
 #pragma unroll
                     for (int pt = 0; pt < NPT; pt++)
                         st_off<bf16x4>(yb, (o + 16 * pt) * 2u,
@@ -865,7 +869,12 @@ bool scan_mimo_supported(const mamba3_scan_args *a) {
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
     if (a->dtype != MAMBA3_BF16 || !a->y || !a->A || a->A_tok || !a->lam) return false;
     if (a->bc_norm || a->B_bias || a->C_bias || a->z) return false;
-    return P == 64 && R == 4 && ((N == 128 && Q == 128) || (N == 64 && Q == 64));
+    if (!(P == 64 && R == 4 && ((N == 128 && Q == 128) || (N == 64 && Q == 64)))) return false;
+    // token strides (in elements) enter 24-bit products
+    const int64_t Gth = a->theta_groups ? a->theta_groups : a->nheads;
+    const int64_t lim = (int64_t)1 << 24;
+    return (int64_t)a->ngroups * R * N < lim && (int64_t)a->nheads * R * P < lim && Gth * (N / 2) < lim &&
+           a->nheads < lim;
 }
 
 mamba3_status launch_scan_mimo(const mamba3_scan_args *a, hipStream_t st) {
