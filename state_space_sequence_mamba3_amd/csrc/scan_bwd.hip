@@ -865,6 +865,7 @@ struct BCfg {
     static constexpr int NS = N + 8, PS = P + 8, QS = QR + 8, NF = N + 4, SF = QR + 1;
     static constexpr int TQ = QR / 16, TN = N / 16, TP = P / 16, NPT = TN * TP, UPW = NPT / NW;
     static_assert(QR % 32 == 0 && N % 32 == 0 && P % 32 == 0 && NPT % NW == 0, "MFMA backward tiling");
+    static_assert((NT & (NT - 1)) == 0, "the thread index is masked to the workgroup size");
     static_assert(R == 1 || R == 2 || R == 4, "rank");
     // LDS layout (bytes; every region 16-byte aligned)
     static constexpr int al(int b) { return (b + 15) / 16 * 16; }
@@ -946,6 +947,7 @@ __global__ __launch_bounds__(CF::NT) void k_scan_bwd_mfma(BwdParams p_arg) {
     auto refresh = [&]() {
         asm volatile("" : "+v"(tid));
         asm volatile("" : "+s"(pk));
+        tid &= NT - 1;   // (its range, for the address math: full-rate shifts and 24-bit products)
         lane = tid & 63;
         li = lane & 15;
         lg = lane >> 4;
