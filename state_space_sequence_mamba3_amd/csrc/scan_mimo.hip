@@ -642,11 +642,13 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
             if (tpn > spn) {
                 for (int j = 0; j < ntl; j++) tile(std::integral_constant<int, 2>{}, 0, j, tpn, spn);
             } else {
-                // t-blocks (tb_lo < tb_hi): a tile reaches both, or only the higher one
-                for (int j = 0; j < ntl; j++) {
-                    if (2 * j <= tbr[0]) tile(std::integral_constant<int, 2>{}, 0, j, tpn, spn);
-                    else if (2 * j <= tbr[1]) tile(std::integral_constant<int, 1>{}, 1, j, tpn, spn);
-                }
+                // t-blocks (tb_lo < tb_hi): the tiles j <= tb_lo / 2 reach both, those up to tb_hi / 2
+                // only the higher one. Two loops with one tile form each: in one loop with both forms
+                // the accumulators took different registers in the two branches and were copied
+                // back at every iteration.
+                const int j0 = min(ntl, tbr[0] / 2 + 1), j1 = min(ntl, tbr[1] / 2 + 1);
+                for (int j = 0; j < j0; j++) tile(std::integral_constant<int, 2>{}, 0, j, tpn, spn);
+                for (int j = j0; j < j1; j++) tile(std::integral_constant<int, 1>{}, 1, j, tpn, spn);
                 // skip term D x_t of the t-blocks' own rows (their X rows are in this panel)
 #pragma unroll
                 for (int u = 0; u < TPW; u++)
