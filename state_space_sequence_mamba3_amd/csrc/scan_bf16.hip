@@ -432,7 +432,9 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         // with the fused prologue / epilogue, and at N = 128, R = 4, the registers run short: the
         // lane-derived address math of the prefetch, staging and output code is recomputed in
         // every chunk (for the other plain shapes hoisting it is faster)
-        const int tq = opaque<CF::EPI || (CF::N == 128 && CF::R == 4)>(tid) & (NTHR - 1);
+        // (the plain kernels also re-mask it to its range, for cheaper address math; in the fused
+        // ones that let the compiler hold more derived values, and they spilled)
+        const int tq = CF::EPI ? opaque<true>(tid) : (opaque<(CF::N == 128 && CF::R == 4)>(tid) & (NTHR - 1));
         const int64_t tok0 = start + c0;
         if constexpr (!CF::YO) {
             // the state entering the chunk, with the previous-token term of its first token
@@ -663,8 +665,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         // recomputed in every chunk instead of being hoisted out of the chunk loop (and spilled)
         unsigned l16c = l16, q4c = q4;
         if constexpr (CF::NSB <= 8) asm volatile("" : "+v"(l16c), "+v"(q4c));   // fully unrolled sweeps
-        l16c &= 15;   // (their ranges, for the index math)
-        q4c &= 3;
+        if constexpr (!CF::EPI) {   // (their ranges, for the index math; see tq above)
+            l16c &= 15;
+            q4c &= 3;
+        }
         const bool fastmask = __builtin_amdgcn_readfirstlane(__float_as_int(MISC[2])) != 0;
         float S2t[TPA];
 #pragma unroll
