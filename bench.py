@@ -64,9 +64,10 @@ PANEL_SHAPES = {(128, 64, 4, 128): 64, (64, 64, 4, 64): 32}
 
 def score_span(c):
     """Tokens over which the score and output contractions run causally: the chunk, except in
-    the panel kernel, whose two panels of a chunk reach each other through the state."""
+    the panel kernel (plain or with the fused block prologue / epilogue), whose two panels of a
+    chunk reach each other through the state."""
     N, P, R, Q = c["dstate"], c["headdim"], c["rank"], c["chunk"]
-    if c.get("dtype") == "bf16" and (N, P, R, Q) in PANEL_SHAPES and not c.get("block"):
+    if c.get("dtype") == "bf16" and (N, P, R, Q) in PANEL_SHAPES:
         return PANEL_SHAPES[(N, P, R, Q)]
     return Q
 
@@ -160,8 +161,8 @@ def scan_kernel_name(c):
     N, P, R, Q = c["dstate"], c["headdim"], c["rank"], c["chunk"]
     if c.get("dtype") != "bf16":
         return f"k_scan_f32<N={N},P={P},R={R},Q={Q}>"
-    if (N, P, R, Q) in PANEL_SHAPES and not c.get("block"):
-        return f"k_scan_mimo<N={N},P={P},R={R},Q={Q}>"
+    if (N, P, R, Q) in PANEL_SHAPES:
+        return f"k_scan_mimo<N={N},P={P},R={R},Q={Q}" + (",EPI>" if c.get("block") else ">")
     return f"k_scan_bf16<N={N},P={P},R={R},Q={Q}>"
 
 

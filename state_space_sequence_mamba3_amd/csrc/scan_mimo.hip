@@ -74,13 +74,44 @@ struct MimoParams {
     float *h_out;
     const int32_t *cu;
     int32_t seqlen, H, G, nseq, Gth;
+    // fused block prologue / epilogue (EPI instantiations): B, C and Bprev columns scaled to unit
+    // RMS (norm) and given the head's bias rows [H, N] (or none), y multiplied by SiLU(z)
+    const float *Bb, *Cb;
+    const bf16 *z;
+    int32_t norm;
+    float eps;
 };
+
+// Prologue of an 8-element piece of a B or C column (scale by inv, add the bias slice b: 8 fp32 in
+// LDS), then the rotation by -Phi against the bf16 (cos, sin) pairs of the piece's 4 angle pairs,
+// in fp32, and the operand scale sc; rounded to bf16 once.
+__device__ __forceinline__ bf16x8 epi_rot_scale_pack(const bf16x8 raw, float inv, const float *b, const bf16x8 cs,
+                                                    float sc) {
+    const f32x4 b0 = *(const f32x4 *)b, b1 = *(const f32x4 *)(b + 4);
+    float o[8];
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const float u = (float)raw[2 * m] * inv + ((m < 2) ? b0[2 * m] : b1[2 * m - 4]);
+        const float v = (float)raw[2 * m + 1] * inv + ((m < 2) ? b0[2 * m + 1] : b1[2 * m - 3]);
+        const float c = (float)cs[2 * m], sn = (float)cs[2 * m + 1];
+        o[2 * m] = (c * u + sn * v) * sc;
+        o[2 * m + 1] = (c * v - sn * u) * sc;
+    }
+    return pack8(o);
+}
+__device__ __forceinline__ float epi_sumsq8(const bf16x8 v) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) ss += (float)v[e] * (float)v[e];
+    return ss;
+}
 
 // NW_ waves per workgroup, PT_ tokens per panel (PT_ R = 32 NW_ rows: two 16-row t-blocks a wave);
 // PAD_: LDS rows padded against bank conflicts (below)
-template <int N_, int P_, int R_, int Q_, int NW_, int PT_, bool PAD_ = true, int WPE_ = 2>
+template <int N_, int P_, int R_, int Q_, int NW_, int PT_, bool PAD_ = true, int WPE_ = 2, bool EPI_ = false>
 struct MCfg {
     static constexpr int N = N_, P = P_, R = R_, Q = Q_;
+    static constexpr bool EPI = EPI_;               // the fused block prologue / epilogue
     static constexpr int WPE = WPE_;                // waves per SIMD the registers are sized for
     static constexpr int NW = NW_, NTHR = 64 * NW_;
     static constexpr int K = N / 2;                 // angles per token (state pairs)
@@ -130,7 +161,8 @@ struct MCfg {
     // the prologue's per-token log2 decay shares S2 (the chunk's copy): wave 0 reads each entry
     // before it writes the entry's new value
     static constexpr int OFF_MISC = OFF_DL + Q * 4;               // float [2][4] per chunk, then A log2 e of the head
-    static constexpr int LDS = OFF_MISC + 48;
+    static constexpr int OFF_BIA = (OFF_MISC + 48 + 15) / 16 * 16;  // float [2][N] B, C bias rows (EPI)
+    static constexpr int LDS = OFF_BIA + (EPI ? 2 * N * 4 : 0);
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -210,6 +242,16 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
     auto urow = [&](int r) __attribute__((always_inline)) { return (UT == 32) ? 8 * (r / 4) + 4 * hi + (r % 4) : 4 * q4 + r; };
     const int ucol = (UT == 32) ? l32 : l16;
 
+    // prologue bias rows of the head (zeros for an absent bias): [0, N) for B, [N, 2N) for C
+    float *const BIA = (float *)(smem + CF::OFF_BIA);
+    if constexpr (CF::EPI) {
+        for (int e = tid; e < 2 * N; e += NTHR) {
+            const float *src = (e < N) ? pr.Bb : pr.Cb;
+            BIA[e] = src ? src[(int64_t)h * N + e % N] : 0.f;
+        }
+        __syncthreads();
+    }
+
     // ---- the state entering the slab: h_in (+ delta_0 Bprev xprev^T), and its bf16 copy
     UAcc hreg[UPW];
     {
@@ -218,6 +260,23 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         if (pr.Bprev && len > 0) {
             const float dt0 = to_f(pr.dt[start * H + h]), l0 = to_f(pr.lam[start * H + h]);
             d0 = (1.f - l0) * dt0;
+        }
+        // the prologue of Bprev's columns: inverse RMS per column (every wave computes its own)
+        float invp[R];
+#pragma unroll
+        for (int j = 0; j < R; j++) invp[j] = 1.f;
+        if constexpr (CF::EPI) {
+            if (pr.Bprev && pr.norm) {
+                const bf16 *bp0 = pr.Bprev + ((int64_t)s * G + g) * R * N;
+#pragma unroll
+                for (int j = 0; j < R; j++) {
+                    float ss = 0.f;
+                    for (int n = lane; n < N; n += 64) ss += to_f(bp0[j * N + n]) * to_f(bp0[j * N + n]);
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                    invp[j] = rsqrtf(ss * (1.f / N) + pr.eps);
+                }
+            }
         }
 #pragma unroll
         for (int v = 0; v < UPW; v++) {
@@ -231,7 +290,10 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
                     const bf16 *xp = pr.xprev + ((int64_t)s * H + h) * R * P + p;
                     float acc = 0.f;
 #pragma unroll
-                    for (int j = 0; j < R; j++) acc += to_f(bp[j * N]) * to_f(xp[j * P]);
+                    for (int j = 0; j < R; j++) {
+                        const float bv = CF::EPI ? to_f(bp[j * N]) * invp[j] + BIA[n] : to_f(bp[j * N]);
+                        acc += bv * to_f(xp[j * P]);
+                    }
                     val += d0 * acc;
                 }
                 hreg[v][r] = val;
@@ -495,10 +557,28 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
                 const float e = EB[pan * PT + row / R];
                 eb[i] = (pan * PT + row / R < nq) ? e : 0.f;
             }
+            if constexpr (CF::EPI) {
+                // the fused prologue: a row's N / 8 pieces sit in N / 8 consecutive lanes, whose
+                // butterfly sums its squares; every piece of a thread covers the same columns
+                const float *bslice = BIA + (tq % (N / 8)) * 8;
 #pragma unroll
-            for (int i = 0; i < NLB; i++) {
-                const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
-                *(bf16x8 *)(BS + row * NS + col) = rot_scale_pack_bf(RB[i], cs[i], eb[i]);
+                for (int i = 0; i < NLB; i++) {
+                    const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
+                    float inv = 1.f;
+                    if (pr.norm) {
+                        float ss = epi_sumsq8(RB[i]);
+#pragma unroll
+                        for (int off = 1; off < N / 8; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                        inv = rsqrtf(ss * (1.f / N) + pr.eps);
+                    }
+                    *(bf16x8 *)(BS + row * NS + col) = epi_rot_scale_pack(RB[i], inv, bslice, cs[i], eb[i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NLB; i++) {
+                    const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
+                    *(bf16x8 *)(BS + row * NS + col) = rot_scale_pack_bf(RB[i], cs[i], eb[i]);
+                }
             }
 #pragma unroll
             for (int i = 0; i < NLX; i++) {
@@ -520,10 +600,28 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
                 const int tau = (tbr[u] * 16 + l16) / R;
                 const float e = EC[pan * PT + tau];
                 const float ec = (pan * PT + tau < nq) ? e : 0.f;   // (rows past the end: zero)
+                if constexpr (CF::EPI) {
+                    // the fused prologue: the row's N values sit in lanes l16 + 16 q4, NKK pieces each
+                    float inv = 1.f;
+                    if (pr.norm) {
+                        float ss = 0.f;
 #pragma unroll
-                for (int kk = 0; kk < NKK; kk++) {
-                    const bf16x8 cs = *(const bf16x8 *)(TAB + tau * KS + 16 * kk + 4 * q4);
-                    creg[u][kk] = rot_scale_pack_bf(HC[u][kk], cs, ec);
+                        for (int kk = 0; kk < NKK; kk++) ss += epi_sumsq8(HC[u][kk]);
+                        ss += __shfl_xor(ss, 16, 64);
+                        ss += __shfl_xor(ss, 32, 64);
+                        inv = rsqrtf(ss * (1.f / N) + pr.eps);
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < NKK; kk++) {
+                        const bf16x8 cs = *(const bf16x8 *)(TAB + tau * KS + 16 * kk + 4 * q4);
+                        creg[u][kk] = epi_rot_scale_pack(HC[u][kk], inv, BIA + N + 32 * kk + 8 * q4, cs, ec);
+                    }
+                } else {
+#pragma unroll
+                    for (int kk = 0; kk < NKK; kk++) {
+                        const bf16x8 cs = *(const bf16x8 *)(TAB + tau * KS + 16 * kk + 4 * q4);
+                        creg[u][kk] = rot_scale_pack_bf(HC[u][kk], cs, ec);
+                    }
                 }
             }
         };
@@ -724,11 +822,42 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         // outputs of the round straight from the accumulators: four adjacent columns of one row
         // per lane and store (a t-block's 16 rows are 4 tokens' rank rows, 2 KB in all)
         bf16 *yb = gY + tok0 * strX;   // the chunk's first output row (a uniform base)
+        // the fused epilogue's gate z at the outputs' addresses (rows past the end read the last
+        // token's, unused), loaded once the round's tile work is done
+        bf16x4 zr[TPW][NPT];
+        const bool has_z = CF::EPI && pr.z != nullptr;
+        auto load_z = [&](int tpn) __attribute__((always_inline)) {
+            if constexpr (CF::EPI) {
+                if (has_z) {
+                    const int tqp = opaque<true>(tid) & (NTHR - 1);
+                    const int lane = tqp & 63, l16 = tqp & 15, q4 = lane >> 4;
+                    const bf16 *zb = pr.z + h * (int64_t)R * P + tok0 * strX;
+#pragma unroll
+                    for (int u = 0; u < TPW; u++) {
+                        const int rr = tbr[u] * 16 + l16, tau = min(tpn * PT + rr / R, nq - 1);
+                        const uint32_t o = mul24((uint32_t)tau, (uint32_t)strX) + (uint32_t)((rr % R) * P + 4 * q4);
+#pragma unroll
+                        for (int pt = 0; pt < NPT; pt++) zr[u][pt] = ld_off<bf16x4>(zb, (o + 16 * pt) * 2u);
+                    }
+                }
+            }
+        };
         auto store_y = [&](int tpn) __attribute__((always_inline)) {
             // lane indices made opaque here: the phase's address math is recomputed in it rather
             // than precomputed for every phase of the chunk and held across them
             const int tqp = opaque<true>(tid) & (NTHR - 1);
             const int lane = tqp & 63, l16 = tqp & 15, q4 = lane >> 4;
+            if (has_z) {   // y SiLU(z) in fp32, before the single rounding
+#pragma unroll
+                for (int u = 0; u < TPW; u++)
+#pragma unroll
+                    for (int pt = 0; pt < NPT; pt++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const float v = (float)zr[u][pt][i];
+                            yacc[u][pt][i] *= v / (1.f + __expf(-v));
+                        }
+            }
 #pragma unroll
             for (int u = 0; u < TPW; u++) {
                 const int rr = tbr[u] * 16 + l16, tau = tpn * PT + rr / R;
@@ -780,6 +909,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
             __builtin_amdgcn_sched_barrier(0);
             if (pan + 1 < NPAN) load_crows(c0, pan + 1, tq);
             else load_crows(c0 + Q, 0, tq);
+            load_z(pan);
             if (fast) state_update(pan);
             store_y(pan);
             if (pan + 1 < npan) {
@@ -850,6 +980,7 @@ mamba3_status launch_mimo_cfg(const mamba3_scan_args *a, hipStream_t st) {
     p.cu = a->cu_seqlens; p.seqlen = a->seqlen; p.H = a->nheads; p.G = a->ngroups;
     p.nseq = a->cu_seqlens ? a->nseq : a->batch;
     p.Gth = a->theta_groups ? a->theta_groups : a->nheads;
+    p.Bb = a->B_bias; p.Cb = a->C_bias; p.z = (const bf16 *)a->z; p.norm = a->bc_norm; p.eps = a->bc_eps;
     const int64_t nblk = (int64_t)p.nseq * a->nheads;
     if (nblk == 0) return MAMBA3_OK;
     if (hipFuncSetAttribute((const void *)k_scan_mimo<CF>, hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS) !=
@@ -870,7 +1001,6 @@ mamba3_status launch_mimo_cfg(const mamba3_scan_args *a, hipStream_t st) {
 bool scan_mimo_supported(const mamba3_scan_args *a) {
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
     if (a->dtype != MAMBA3_BF16 || !a->y || !a->A || a->A_tok || !a->lam) return false;
-    if (a->bc_norm || a->B_bias || a->C_bias || a->z) return false;
     if (!(P == 64 && R == 4 && ((N == 128 && Q == 128) || (N == 64 && Q == 64)))) return false;
     // token strides (in elements) enter 24-bit products
     const int64_t Gth = a->theta_groups ? a->theta_groups : a->nheads;
@@ -880,8 +1010,13 @@ bool scan_mimo_supported(const mamba3_scan_args *a) {
 }
 
 mamba3_status launch_scan_mimo(const mamba3_scan_args *a, hipStream_t st) {
-    if (a->dstate == 128 && a->chunk == 128) return launch_mimo_cfg<MCfg<128, 64, 4, 128, 8, 64>>(a, st);
-    if (a->dstate == 64 && a->chunk == 64) return launch_mimo_cfg<MCfg<64, 64, 4, 64, 4, 32>>(a, st);
+    const bool epi = a->bc_norm || a->B_bias || a->C_bias || a->z;
+    if (a->dstate == 128 && a->chunk == 128)
+        return epi ? launch_mimo_cfg<MCfg<128, 64, 4, 128, 8, 64, true, 2, true>>(a, st)
+                   : launch_mimo_cfg<MCfg<128, 64, 4, 128, 8, 64>>(a, st);
+    if (a->dstate == 64 && a->chunk == 64)
+        return epi ? launch_mimo_cfg<MCfg<64, 64, 4, 64, 4, 32, true, 2, true>>(a, st)
+                   : launch_mimo_cfg<MCfg<64, 64, 4, 64, 4, 32>>(a, st);
     return MAMBA3_EUNSUPPORTED;
 }
 
