@@ -992,12 +992,13 @@ mamba3_status launch_mimo_cfg(const mamba3_scan_args *a, hipStream_t st) {
 
 }  // namespace
 
-// The panel kernel serves two rank-4 shapes without the fused prologue / epilogue or the
-// variants (a per-token decay rate, a fixed trapezoid weight): (N, P, R, Q) = (128, 64, 4, 128),
-// whose chunk (512 rank-expanded rows) does not fit the general kernel's per-wave registers, in
-// 8-wave workgroups over two 64-token panels; and (64, 64, 4, 64) in 4-wave workgroups over two
-// 32-token panels (58.6 KB of LDS and 200 VGPRs: two workgroups per CU, where the general kernel
-// fits one). The general bf16 kernel runs everything else.
+// The panel kernel serves two rank-4 shapes, plain or with the fused block prologue / epilogue
+// (EPI), without the variants (a per-token decay rate, a fixed trapezoid weight):
+// (N, P, R, Q) = (128, 64, 4, 128), whose chunk (512 rank-expanded rows) does not fit the general
+// kernel's per-wave registers, in 8-wave workgroups over two 64-token panels; and (64, 64, 4, 64)
+// in 4-wave workgroups over two 32-token panels (58.6 KB of LDS and about 200 VGPRs: two
+// workgroups per CU, where the general kernel fits one). The general bf16 kernel runs everything
+// else.
 bool scan_mimo_supported(const mamba3_scan_args *a) {
     const int N = a->dstate, P = a->headdim, R = a->rank, Q = a->chunk;
     if (a->dtype != MAMBA3_BF16 || !a->y || !a->A || a->A_tok || !a->lam) return false;
