@@ -796,6 +796,8 @@ def main():
         print(f"# siso scan + block {res['siso_block']['ms']:.3f} ms", file=sys.stderr, flush=True)
         res["mimo_block"] = bench_scan(2, KL, WL, dev, block=True)
         print(f"# mimo scan + block {res['mimo_block']['ms']:.3f} ms", file=sys.stderr, flush=True)
+        res["packed_block"] = bench_scan(4, K, W, dev, block=True)
+        print(f"# packed scan + block {res['packed_block']['ms']:.3f} ms", file=sys.stderr, flush=True)
     if args.only in ("bwd", "all"):
         # the backward: a few steps, each is a whole backward of the batch
         res["siso_bwd"] = bench_bwd(1, 3, 1, dev)
@@ -857,7 +859,8 @@ def main():
         line = {"metric": METRIC, "value": None}
     sec = {}
     for k, tk in (("siso", "scan_bf16"), ("mimo", "scan_bf16_mimo"), ("tiny", None), ("mimo_g1", None),
-                  ("packed_g1", None), ("siso_block", "scan_bf16_block"), ("mimo_block", None)):
+                  ("packed_g1", None), ("siso_block", "scan_bf16_block"), ("mimo_block", None),
+                  ("packed_block", None)):
         if k in res:
             r = res[k]
             sec[k] = {"workload": r["workload"], "ms": r["ms"], "tokens_per_s": r["tokens_per_s"],

@@ -340,7 +340,7 @@ def _slab_inputs(d, s, h, cu=None):
     return out
 
 
-@pytest.mark.parametrize("cfg,block", [(1, False), (2, False), (4, False), (1, True), (2, True)])
+@pytest.mark.parametrize("cfg,block", [(1, False), (2, False), (4, False), (1, True), (2, True), (4, True)])
 def test_full_size_sampled_slabs(oracle, cfg, block):
     import torch
     c = synth.CONFIGS[cfg]
