@@ -605,8 +605,8 @@ def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 3
     # bench's launch: 8 x 64 (sequence, head) slabs, 256 x 64 decode rows, 257 x 64 with slots)
     dec = ("k_decode_colIDF16bLi64ELi4ELb0E", "k_decode_col<__bf16, 64, 4, false>")
     kernels = {"scan_bf16": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, false, true>",), 512),
-               "scan_bf16_mimo": ("scan_mimo.hip", ("MCfg<64, 64, 4, 64, 4, 32, true, 2>",), 512),
-               "scan_bf16_packed": ("scan_mimo.hip", ("MCfg<128, 64, 4, 128, 8, 64, true, 2>",), 512),
+               "scan_bf16_mimo": ("scan_mimo.hip", ("MCfg<64, 64, 4, 64, 4, 32, true, 2, false>",), 512),
+               "scan_bf16_packed": ("scan_mimo.hip", ("MCfg<128, 64, 4, 128, 8, 64, true, 2, false>",), 512),
                "scan_bf16_block": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, true, true>",), 512),
                "decode": ("decode.hip", dec, 16384),
                "decode_slots": ("decode.hip", dec, 16448),
@@ -642,8 +642,8 @@ def summarize_traffic(fetch_dir, write_dir, out_dir, commands, copy_bytes=1 << 3
     print(f"wrote {out_md}")
 
 
-MFMA_KERNELS = {"scan_bf16_packed": ("scan_mimo.hip", ("MCfg<128, 64, 4, 128, 8, 64, true, 2>",), 512),
-                "scan_bf16_mimo": ("scan_mimo.hip", ("MCfg<64, 64, 4, 64, 4, 32, true, 2>",), 512),
+MFMA_KERNELS = {"scan_bf16_packed": ("scan_mimo.hip", ("MCfg<128, 64, 4, 128, 8, 64, true, 2, false>",), 512),
+                "scan_bf16_mimo": ("scan_mimo.hip", ("MCfg<64, 64, 4, 64, 4, 32, true, 2, false>",), 512),
                 "scan_bf16": ("scan_bf16.hip", ("Cfg<128, 64, 1, 64, 4, 32, 64, false, true>",), 512)}
 CU_COUNT = 256
 XCD_COUNT = 8
