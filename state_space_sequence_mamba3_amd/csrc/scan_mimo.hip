@@ -1,34 +1,37 @@
-// bf16 chunked MIMO scan on gfx950 MFMA in 64-token panels, fp32 state.
+// bf16 chunked MIMO scan on gfx950 MFMA in token panels, fp32 state.
 //
-// One workgroup (8 waves) owns one (sequence, head) slab and walks it chunk by
-// chunk with the state in registers, like the general bf16 scan; the chunked
-// form is the same (the three-term update of Proposition 4, "Complex-Valued
-// State Space Models", in the matrix form of "Parallel representation under
-// SSD", with chunk-local decay S_t and angles Phi_t and the RoPE trick of
-// Proposition 3 inside a chunk; the rank-R update of "MIMO Formulation"):
+// One workgroup (NW waves) owns one (sequence, head) slab and walks it chunk
+// by chunk with the state in registers, like the general bf16 scan; the
+// chunked form is the same (the three-term update of Proposition 4,
+// "Complex-Valued State Space Models", in the matrix form of "Parallel
+// representation under SSD", with chunk-local decay S_t and angles Phi_t and
+// the RoPE trick of Proposition 3 inside a chunk; the rank-R update of "MIMO
+// Formulation"):
 //   y_t = e^{S_t} C~_t^T H' + sum_{s<=t} e^{S_t-S_s} w_ts (C~_t.B~_s) X_s + D X_t,
 //     w_ts = gamma_s + delta_{s+1} for s < t, gamma_s for s = t
 //   H'  <- R(Phi_e) ( e^{S_e} H' + sum_s e^{S_e-S_s} (gamma_s + delta_{s+1}) B~_s X_s^T )
 // What differs is how a chunk's work is laid out, for the rank-4 shapes whose
 // chunk has Q*R = 256 or 512 rank-expanded rows:
-//   * Panels. The chunk's rows are taken 64 tokens (256 rows) at a time. Only
-//     one panel of rotated B rows and X rows sits in LDS, and each wave holds
-//     the C~ rows and output accumulators of two 16-row t-blocks of one panel
-//     (a round): round 0 is panel 0 against itself, round 1 panel 1 against
-//     itself. Panel 0's terms reach panel 1's tokens through the state: after
-//     round 0's state update the registers hold
-//       H' + sum_{s in panel 0} 2^{-S2_s} (gamma_s + delta_{s+1}) B~_s X_s^T,
-//     still in the chunk-start frame and decay reference, and since every s of
-//     panel 0 precedes every t of panel 1 (weight gamma_s + delta_{s+1}),
-//     panel 1's inter-chunk term 2^{S2_t} C~_t^T of that sum's bf16 copy is its
-//     carried term plus all of panel 0's. This is the same sum regrouped (the
-//     product C~_t^T B~_s X_s^T taken as C~_t^T (B~_s X_s^T)), exact up to the
-//     bf16 rounding of the summed state, like the carried state's own copy; it
-//     replaces the 256 x 256 score block of panel 1 against panel 0 (37 % of a
-//     chunk's matrix work) by nothing beyond the state update round 0 already
-//     does. A chunk passes four barriers; inside a round each wave runs its
-//     score, mask and output MFMAs straight through. The slow form below keeps
-//     the score block (round 1, part A) and its six barriers.
+//   * Panels. The chunk's rows are taken PT tokens (32 NW rows) at a time.
+//     Only one panel of rotated B rows and X rows sits in LDS, and each wave
+//     holds the C~ rows and output accumulators of two 16-row t-blocks of one
+//     panel: round p is panel p against itself.
+//   * Earlier panels reach later ones through the state. After round p's state
+//     update the registers hold
+//       H' + sum_{s in panels 0..p} 2^{-S2_s} (gamma_s + delta_{s+1}) B~_s X_s^T,
+//     still in the chunk-start frame and decay reference; every s of those
+//     panels precedes every t of panel p+1 (weight gamma_s + delta_{s+1}), so
+//     panel p+1's inter-chunk term 2^{S2_t} C~_t^T of that sum's bf16 copy is its
+//     carried term plus all of the earlier panels'. This is the same sum
+//     regrouped (C~_t^T B~_s X_s^T taken as C~_t^T (B~_s X_s^T)), exact up to the
+//     bf16 rounding of the summed state, like the carried state's own copy; for
+//     two panels it replaces the 256 x 256 score block of panel 1 against panel
+//     0 (37 % of a chunk's matrix work at N = 128) by nothing beyond the state
+//     update the rounds already do. Each panel is staged behind one barrier and
+//     its round ends at another; inside a round each wave runs its score, mask
+//     and output MFMAs straight through. The state's bf16 copy is written at the
+//     start of the panel that reads it, behind the barrier that ends the
+//     previous round's reads of the old copy.
 //   * Decay folded into the operands. With the chunk-start reference,
 //     e^{S_t-S_s} = 2^{S2_t} 2^{-S2_s} (S2 = S / ln 2), so C~ rows are staged as
 //     2^{S2_t} C~_t and B~ rows as 2^{-S2_s} (gamma_s + delta_{s+1}) B~_s. A score
@@ -39,9 +42,11 @@
 //     2^{S2_e} (H' + sum_s B~'_s X_s^T). A chunk whose total log2 decay is
 //     beyond 100 (where the factors could leave the fp32 range), or whose
 //     trapezoid weights have gamma_s + delta_{s+1} = 0 with gamma_s != 0, runs
-//     unscaled operands with the per-element mask e^{S_t-S_s} w_ts and scales
-//     its staged B~ rows in LDS by e^{S_e-S_s} (gamma_s + delta_{s+1}) before the
-//     state update.
+//     unscaled operands with the per-element mask e^{S_t-S_s} w_ts, keeps its
+//     state referenced to the start of the current panel, and after each round
+//     scales its staged B~ rows in LDS by e^{S_ref'-S_s} (gamma_s + delta_{s+1})
+//     and the state by e^{S_ref'-S_ref} (S_ref' of the panel's last token)
+//     before the state update: every factor is at most 1.
 //   * Operand reads of a tile are all issued before its MFMAs (no per-MFMA
 //     conditions), and the next panel's raw B and X rows and the next round's
 //     raw C rows are loaded into registers one phase ahead.
@@ -57,6 +62,10 @@
 //     at most 2^-8 of |u| + |v| per element before the element's own bf16
 //     rounding; against the fp64 oracle the outputs moved by under 1e-3 of
 //     their slab maximum.
+//   * The EPI instantiations fuse the block prologue and epilogue ("Architectural
+//     Integration"): every B, C and Bprev column is scaled to unit RMS and gets
+//     the head's bias before its rotation (then in fp32), and y is multiplied by
+//     SiLU(z) in fp32 before its rounding.
 #include "mfma_ops.h"
 
 namespace m3 {
