@@ -184,25 +184,29 @@ def test_grouped_bc_and_no_skip(oracle):
     assert slab_relerr(from_dev(y), yo) < TOL_BF16 and state_relerr(from_dev(h), ho) < TOL_BF16
 
 
-# The panel kernel of the packed workload's shape (N = 128, R = 4, chunk 128): a chunk is two
-# 64-token panels; a last chunk may end inside panel 0 or panel 1.
-@pytest.mark.parametrize("seqlen", [300, 333, 64, 1])
-def test_panel_partial_chunks(oracle, seqlen):
-    inp = synth.resume_inputs(synth.scan_inputs(4, seed=70 + seqlen, batch=2, seqlen=seqlen, nheads=2,
+# The panel kernel: a chunk is two panels (64 tokens at the packed workload's shape, N = 128,
+# R = 4, chunk 128; 32 tokens at the MIMO layer's, N = 64, R = 4, chunk 64); a last chunk may end
+# inside panel 0 or panel 1, or on a panel boundary.
+@pytest.mark.parametrize("cfg,seqlen", [(4, 300), (4, 333), (4, 64), (4, 1), (2, 31), (2, 32), (2, 33),
+                                        (2, 95), (2, 128), (2, 161)])
+def test_panel_partial_chunks(oracle, cfg, seqlen):
+    inp = synth.resume_inputs(synth.scan_inputs(cfg, seed=70 + seqlen, batch=2, seqlen=seqlen, nheads=2,
                                                 packed=False), seed=71)
-    note(f"bf16 panel scan, last chunk of {seqlen % 128 or 128} tokens")
-    y, h = run(upload(inp, device()), 128)
+    Q = inp["meta"]["chunk"]
+    note(f"bf16 panel scan cfg{cfg}, last chunk of {seqlen % Q or Q} tokens")
+    y, h = run(upload(inp, device()), Q)
     yo, ho = oracle.scan({k: v for k, v in inp.items() if k != "meta"})
     ey, eh = slab_relerr(from_dev(y), yo), state_relerr(from_dev(h), ho)
     note(f"  y relerr {ey:.2e}  h relerr {eh:.2e}")
     assert ey < TOL_BF16 and eh < TOL_BF16
 
 
-def test_panel_grouped_no_skip(oracle):
-    inp = synth.scan_inputs(dict(synth.CONFIGS[4], ngroups=1), seed=72, batch=1, seqlen=390, nheads=4, packed=False)
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_panel_grouped_no_skip(oracle, cfg):
+    inp = synth.scan_inputs(dict(synth.CONFIGS[cfg], ngroups=1), seed=72, batch=1, seqlen=390, nheads=4, packed=False)
     inp["D"] = None
-    note("bf16 panel scan G=1, D=NULL")
-    y, h = run(upload(inp, device()), 128)
+    note(f"bf16 panel scan cfg{cfg} G=1, D=NULL")
+    y, h = run(upload(inp, device()), inp["meta"]["chunk"])
     yo, ho = oracle.scan({k: v for k, v in inp.items() if k not in ("meta", "D")})
     assert slab_relerr(from_dev(y), yo) < TOL_BF16 and state_relerr(from_dev(h), ho) < TOL_BF16
 
