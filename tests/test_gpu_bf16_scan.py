@@ -234,18 +234,19 @@ def test_panel_weight_guard(oracle, cfg):
     assert ey < TOL_BF16 and eh < TOL_BF16
 
 
-def test_panel_chunk_invariance_and_determinism():
-    """Chunk 128 (the panel kernel) against chunk 64 (the general kernel) on the same inputs, and
+@pytest.mark.parametrize("cfg,qp,qg", [(4, 128, 64), (2, 64, 32)])
+def test_panel_chunk_invariance_and_determinism(cfg, qp, qg):
+    """The panel kernel's chunk (qp) against a general-kernel chunk (qg) on the same inputs, and
     two runs of the panel kernel bitwise equal."""
-    inp = synth.scan_inputs(4, seed=74, batch=1, seqlen=512, nheads=2, packed=False)
-    note("bf16 panel scan: chunk 128 vs 64, determinism")
+    inp = synth.scan_inputs(cfg, seed=74, batch=1, seqlen=512, nheads=2, packed=False)
+    note(f"bf16 panel scan cfg{cfg}: chunk {qp} vs {qg}, determinism")
     d = upload(inp, device())
-    y128, h128 = run(d, 128)
-    y64, h64 = run(d, 64)
-    assert slab_relerr(from_dev(y128), from_dev(y64)) < TOL_BF16
-    assert state_relerr(from_dev(h128), from_dev(h64)) < 1e-2
-    y2, h2 = run(d, 128)
-    assert from_dev(y128).tobytes() == from_dev(y2).tobytes() and np.array_equal(from_dev(h128), from_dev(h2))
+    yp, hp = run(d, qp)
+    yg, hg = run(d, qg)
+    assert slab_relerr(from_dev(yp), from_dev(yg)) < TOL_BF16
+    assert state_relerr(from_dev(hp), from_dev(hg)) < 1e-2
+    y2, h2 = run(d, qp)
+    assert from_dev(yp).tobytes() == from_dev(y2).tobytes() and np.array_equal(from_dev(hp), from_dev(h2))
 
 
 def test_packed_ragged_with_empty(oracle):
