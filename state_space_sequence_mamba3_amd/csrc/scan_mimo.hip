@@ -557,32 +557,48 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
         // rows, which zeroes every score and state term that would read their X rows.
         auto stage_panel = [&](int pan) __attribute__((always_inline)) {
             const int tq = opaque<true>(tid) & (NTHR - 1);
-            bf16x8 cs[NLB];
-            float eb[NLB];
-#pragma unroll
-            for (int i = 0; i < NLB; i++) {
-                const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
-                cs[i] = *(const bf16x8 *)(TAB + (row / R) * KS + col / 2);
-                const float e = EB[pan * PT + row / R];
-                eb[i] = (pan * PT + row / R < nq) ? e : 0.f;
-            }
             if constexpr (CF::EPI) {
                 // the fused prologue: a row's N / 8 pieces sit in N / 8 consecutive lanes, whose
-                // butterfly sums its squares; every piece of a thread covers the same columns
+                // butterfly sums its squares; every piece of a thread covers the same columns. The
+                // pieces go two at a time (their table reads before their stores): fewer values live
+                // at once than with every piece's reads first (packed shape: 105 VGPRs spilled, not 158).
                 const float *bslice = BIA + (tq % (N / 8)) * 8;
+                constexpr int HB2 = (NLB >= 2) ? 2 : 1;
+#pragma unroll
+                for (int i0 = 0; i0 < NLB; i0 += HB2) {
+                    bf16x8 csh[HB2];
+                    float ebh[HB2];
+#pragma unroll
+                    for (int k = 0; k < HB2; k++) {
+                        const int c = tq + (i0 + k) * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
+                        csh[k] = *(const bf16x8 *)(TAB + (row / R) * KS + col / 2);
+                        const float e = EB[pan * PT + row / R];
+                        ebh[k] = (pan * PT + row / R < nq) ? e : 0.f;
+                    }
+#pragma unroll
+                    for (int k = 0; k < HB2; k++) {
+                        const int i = i0 + k;
+                        const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
+                        float inv = 1.f;
+                        if (pr.norm) {
+                            float ss = epi_sumsq8(RB[i]);
+#pragma unroll
+                            for (int off = 1; off < N / 8; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                            inv = rsqrtf(ss * (1.f / N) + pr.eps);
+                        }
+                        *(bf16x8 *)(BS + row * NS + col) = epi_rot_scale_pack(RB[i], inv, bslice, csh[k], ebh[k]);
+                    }
+                }
+            } else {
+                bf16x8 cs[NLB];
+                float eb[NLB];
 #pragma unroll
                 for (int i = 0; i < NLB; i++) {
                     const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
-                    float inv = 1.f;
-                    if (pr.norm) {
-                        float ss = epi_sumsq8(RB[i]);
-#pragma unroll
-                        for (int off = 1; off < N / 8; off <<= 1) ss += __shfl_xor(ss, off, 64);
-                        inv = rsqrtf(ss * (1.f / N) + pr.eps);
-                    }
-                    *(bf16x8 *)(BS + row * NS + col) = epi_rot_scale_pack(RB[i], inv, bslice, cs[i], eb[i]);
+                    cs[i] = *(const bf16x8 *)(TAB + (row / R) * KS + col / 2);
+                    const float e = EB[pan * PT + row / R];
+                    eb[i] = (pan * PT + row / R < nq) ? e : 0.f;
                 }
-            } else {
 #pragma unroll
                 for (int i = 0; i < NLB; i++) {
                     const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
