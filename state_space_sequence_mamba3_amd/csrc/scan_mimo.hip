@@ -581,9 +581,14 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
                         const int c = tq + i * NTHR, row = c / (N / 8), col = (c % (N / 8)) * 8;
                         float inv = 1.f;
                         if (pr.norm) {
+                            // the row's N / 8 lanes are one aligned group of 8 or 16 lanes: sums by
+                            // DPP (quad swaps, then the half-row and row mirrors), no LDS round trip
+                            static_assert(N / 8 == 8 || N / 8 == 16, "a B row's lanes form a DPP row or half");
                             float ss = epi_sumsq8(RB[i]);
-#pragma unroll
-                            for (int off = 1; off < N / 8; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                            ss += dpp_move<0xB1>(ss);   // quad_perm [1, 0, 3, 2]
+                            ss += dpp_move<0x4E>(ss);   // quad_perm [2, 3, 0, 1]
+                            ss += dpp_move<0x141>(ss);  // row_half_mirror
+                            if constexpr (N / 8 == 16) ss += dpp_move<0x140>(ss);   // row_mirror
                             inv = rsqrtf(ss * (1.f / N) + pr.eps);
                         }
                         *(bf16x8 *)(BS + row * NS + col) = epi_rot_scale_pack(RB[i], inv, bslice, csh[k], ebh[k]);
