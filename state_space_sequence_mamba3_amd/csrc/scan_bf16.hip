@@ -703,9 +703,14 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
                 if (pr.norm) {
 #pragma unroll
                     for (int i = 0; i < CF::NLB; i++) {
+                        // the row's N / 8 lanes are one aligned group of 8 or 16: sums by DPP lane
+                        // moves (quad swaps, then the half-row and row mirrors)
+                        static_assert(N / 8 == 8 || N / 8 == 16, "a B row's lanes form a DPP row or half");
                         float ss = sumsq8(rawB[i]);
-#pragma unroll
-                        for (int off = 1; off < N / 8; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                        ss += dpp_move<0xB1>(ss);   // quad_perm [1, 0, 3, 2]
+                        ss += dpp_move<0x4E>(ss);   // quad_perm [2, 3, 0, 1]
+                        ss += dpp_move<0x141>(ss);  // row_half_mirror
+                        if constexpr (N / 8 == 16) ss += dpp_move<0x140>(ss);   // row_mirror
                         binv[i] = rsqrtf(ss * (1.f / N) + pr.eps);
                     }
                 }
