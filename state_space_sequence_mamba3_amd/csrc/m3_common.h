@@ -33,6 +33,15 @@ template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ float dpp_move(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
 }
+// Sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48) by gfx950's row-swap
+// instructions, without the LDS crossbar: v_permlane16_swap pairs rows 0-1 and 2-3, then
+// v_permlane32_swap the two halves; every lane receives the sum.
+__device__ __forceinline__ float sum_across_rows(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 // Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 within each 16-lane row,
 // then each row's total carried to the rows after it (row_bcast:15 into rows 1 and 3, row_bcast:31
 // into rows 2 and 3).

@@ -637,8 +637,7 @@ __global__ __launch_bounds__(CF::NTHR) __attribute__((amdgpu_waves_per_eu(CF::WP
                         float ss = 0.f;
 #pragma unroll
                         for (int kk = 0; kk < NKK; kk++) ss += epi_sumsq8(HC[u][kk]);
-                        ss += __shfl_xor(ss, 16, 64);
-                        ss += __shfl_xor(ss, 32, 64);
+                        ss = sum_across_rows(ss);   // the row's 4 lanes l16 + 16 q4
                         inv = rsqrtf(ss * (1.f / N) + pr.eps);
                     }
 #pragma unroll
