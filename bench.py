@@ -693,6 +693,32 @@ def summarize_mfma(pmc_dir, out_dir, command):
     print(f"wrote {out_md}")
 
 
+def summarize_counters(pmc_dir, out_md, command, kernels=("k_scan_mimo", "k_scan_bf16", "k_scan_bwd_mfma")):
+    """Per-dispatch averages of every counter of one rocprofv3 --pmc run, per (kernel, workgroups),
+    for the library's kernels (instruction mixes, wait and busy cycles): a text summary."""
+    from collections import defaultdict
+    agg, names = defaultdict(lambda: defaultdict(float)), {}
+    for r in _csv_rows(os.path.join(pmc_dir, "run_counter_collection.csv")):
+        agg[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[r["Dispatch_Id"]] = (r["Kernel_Name"], int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
+    groups = defaultdict(list)
+    for d, nw in names.items():
+        if any(k in nw[0] for k in kernels):
+            groups[(_short(nw[0]), nw[1])].append(d)
+    counters = sorted({c for d in agg for c in agg[d]})
+    md = ["# rocprofv3 counters per dispatch", "", "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+          "```", command, "```", "",
+          "Per (kernel, workgroups): the average over its dispatches of each counter summed over the GPU "
+          "(SQ_*_CYCLES and SQ_WAIT_* count in units of 4 cycles).", "",
+          "| kernel | workgroups | dispatches | " + " | ".join(counters) + " |",
+          "|---|---|---|" + "---|" * len(counters)]
+    for (k, wg), ds in sorted(groups.items()):
+        md.append(f"| `{k}` | {wg} | {len(ds)} | " +
+                  " | ".join(f"{sum(agg[d][c] for d in ds) / len(ds):.4g}" for c in counters) + " |")
+    open(out_md, "w").write("\n".join(md) + "\n")
+    print(f"wrote {out_md}")
+
+
 def counter_record(key):
     """MFMA counters per launch from a committed rocprofv3 --pmc record (SQ_VALU_MFMA_BUSY_CYCLES,
     SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE), if taken on the current kernel source."""
@@ -737,6 +763,10 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-traffic":
         # bench.py --summarize-traffic FETCH_DIR WRITE_DIR OUT_DIR COMMAND...
         summarize_traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        # bench.py --summarize-counters PMC_DIR OUT_MD COMMAND
+        summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-mfma":
         # bench.py --summarize-mfma PMC_DIR OUT_DIR COMMAND
